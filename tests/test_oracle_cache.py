@@ -1,0 +1,242 @@
+"""Pins for the oracle's per-layer LRU slot cache and prefetch install.
+
+  * textbook LRU: for one id per call the miss count at every capacity S is
+    given by Mattson stack distances (Mattson, Gecsei, Slutz, Traiger, 1970),
+    and the resident set after every call equals an OrderedDict LRU;
+  * a brute-force re-statement of the batched rules (tie order, staging,
+    install) compared exactly on random traces;
+  * invariants after every call (maps inverse, D resident, misses = D \\ R,
+    free slots first, staging iff |D| > S, state untouched when staged);
+  * capacity >= distinct experts ever seen: only compulsory misses.
+"""
+from collections import OrderedDict
+
+import numpy as np
+import pytest
+
+
+def mattson_misses(trace, S):
+    stack, misses = [], 0
+    for e in trace:
+        if e in stack:
+            d = stack.index(e) + 1  # stack distance (1 = most recent)
+            stack.remove(e)
+        else:
+            d = None  # first reference: infinite distance
+        stack.insert(0, e)
+        if d is None or d > S:
+            misses += 1
+    return misses
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_single_id_calls_match_mattson_and_textbook_lru(orc, seed):
+    rng = np.random.default_rng(seed)
+    E = 16
+    p = 1.0 / np.arange(1, E + 1) ** 1.2
+    trace = rng.choice(E, size=400, p=p / p.sum()).astype(np.int32)
+    for S in range(1, E + 1):
+        c = orc.Cache(E, S)
+        lru = OrderedDict()
+        misses = 0
+        for e in trace:
+            _, mode, pairs = c.ensure(np.array([[e]], np.int32))
+            assert mode == orc.SLOTS
+            misses += len(pairs)
+            hit = e in lru
+            assert (len(pairs) == 0) == hit
+            if hit:
+                lru.move_to_end(e)
+            else:
+                if len(lru) == S:
+                    lru.popitem(last=False)
+                lru[e] = True
+            so, eo, _, _ = c.state()
+            assert set(int(v) for v in eo if v >= 0) == set(lru.keys())
+        assert misses == mattson_misses(list(trace), S)
+        assert c.counters()["misses"] == misses
+
+
+class BruteCache:
+    """The batched rules restated plainly (sorted(), dicts), independently of the C code."""
+
+    def __init__(self, E, S):
+        self.E, self.S = E, S
+        self.held = [None] * S
+        self.home = {}
+        self.used = [0] * S
+        self.clock = 0
+
+    def _victims(self, protect):
+        cands = [s for s in range(self.S) if self.held[s] is None or self.held[s] not in protect]
+        return sorted(cands, key=lambda s: (self.held[s] is not None, self.used[s], s))
+
+    def _put(self, e, s):
+        if self.held[s] is not None:
+            del self.home[self.held[s]]
+        self.held[s] = e
+        self.home[e] = s
+
+    def ensure(self, ids):
+        self.clock += 1
+        D = sorted(set(ids))
+        miss = [e for e in D if e not in self.home]
+        if len(D) > self.S:
+            return [self.home.get(e, self.S + e) for e in ids], 1, [(e, self.S + e) for e in miss]
+        pairs = list(zip(miss, self._victims(set(D))))
+        for e, s in pairs:
+            self._put(e, s)
+        for e in D:
+            self.used[self.home[e]] = self.clock
+        return [self.home[e] for e in ids], 0, pairs
+
+    def install(self, pred, n_max):
+        T, k = len(pred), len(pred[0])
+        count, best = {}, {}
+        for row in pred:
+            for j, e in enumerate(row):
+                count[e] = count.get(e, 0) + 1
+                best[e] = min(best.get(e, k), j)
+        cand = sorted((e for e in count if e not in self.home), key=lambda e: (-count[e], best[e], e))
+        vict = self._victims(set(count))
+        n = max(0, min(n_max, len(cand), len(vict)))
+        pairs = list(zip(cand[:n], vict[:n]))
+        for e, s in pairs:
+            self._put(e, s)
+            self.used[s] = 0
+        return pairs
+
+
+def _check_invariants(c, ids, slot_ids, mode, pairs, before):
+    so, eo, lu, tick = c.state()
+    S, E = c.S, c.E
+    for s in range(S):
+        if eo[s] >= 0:
+            assert so[eo[s]] == s
+    for e in range(E):
+        if so[e] >= 0:
+            assert eo[so[e]] == e
+    D = sorted(set(ids.reshape(-1).tolist()))
+    so0, eo0, lu0, tick0 = before
+    R0 = set(int(v) for v in eo0 if v >= 0)
+    assert tick == tick0 + 1
+    if len(D) > S:
+        assert mode == 1
+        assert np.array_equal(so, so0) and np.array_equal(eo, eo0) and np.array_equal(lu, lu0)
+        assert [int(p[0]) for p in pairs] == [e for e in D if e not in R0]
+        for i, e in np.ndenumerate(ids):
+            assert slot_ids[i] == (so0[e] if so0[e] >= 0 else S + e)
+        return
+    assert mode == 0
+    assert [int(p[0]) for p in pairs] == [e for e in D if e not in R0]  # misses ascending
+    for e in D:
+        assert so[e] >= 0 and lu[so[e]] == tick
+    for i, e in np.ndenumerate(ids):
+        assert slot_ids[i] == so[e]
+    # no expert of D was evicted; free slots were used before any eviction
+    free0 = [s for s in range(S) if eo0[s] < 0]
+    used = [int(p[1]) for p in pairs]
+    assert used[:len(free0)] == free0[:len(used)]
+    for s in used:
+        assert eo0[s] < 0 or eo0[s] not in D
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_batched_calls_match_brute_force(orc, seed):
+    rng = np.random.default_rng(100 + seed)
+    E = int(rng.choice([8, 16, 32]))
+    k = int(rng.choice([1, 2, 4]))
+    S = int(rng.integers(k, E + 1))
+    c = orc.Cache(E, S)
+    b = BruteCache(E, S)
+    p = 1.0 / np.arange(1, E + 1) ** rng.uniform(0.3, 1.5)
+    for step in range(200):
+        T = int(rng.integers(1, 6))
+        ids = np.stack([rng.choice(E, size=k, replace=False, p=p / p.sum()) for _ in range(T)]).astype(np.int32)
+        before = c.state()
+        if rng.random() < 0.2:
+            pred = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+            n = int(rng.integers(0, 5))
+            got = c.install(pred, n)
+            exp = b.install(pred.tolist(), n)
+            assert [tuple(map(int, r)) for r in got] == exp
+            before = c.state()
+        slot_ids, mode, pairs = c.ensure(ids)
+        es, em, ep = b.ensure(ids.reshape(-1).tolist())
+        assert slot_ids.reshape(-1).tolist() == es
+        assert mode == em
+        assert [tuple(map(int, r)) for r in pairs] == ep
+        _check_invariants(c, ids, slot_ids, mode, pairs, before)
+
+
+def test_enough_capacity_gives_only_compulsory_misses(orc):
+    rng = np.random.default_rng(9)
+    E, k = 32, 4
+    trace = [np.stack([rng.choice(12, size=k, replace=False) for _ in range(2)]).astype(np.int32) for _ in range(100)]
+    for S in (12, 20, 32):
+        c = orc.Cache(E, S)
+        total = sum(len(c.ensure(ids)[2]) for ids in trace)
+        assert total == len(set(np.concatenate([t.reshape(-1) for t in trace]).tolist()))
+
+
+def test_staging_threshold_and_free_first(orc):
+    c = orc.Cache(8, 3)
+    # three distinct experts fit
+    sid, mode, pairs = c.ensure(np.array([[5, 1], [1, 7]], np.int32))
+    assert mode == 0 and pairs.tolist() == [[1, 0], [5, 1], [7, 2]] and sid.tolist() == [[1, 0], [0, 2]]
+    # four distinct do not: staged, state untouched, residents read in place
+    before = c.state()
+    sid, mode, pairs = c.ensure(np.array([[5, 2], [3, 1]], np.int32))
+    assert mode == 1 and pairs.tolist() == [[2, 5], [3, 6]]
+    assert sid.tolist() == [[1, 5], [6, 0]]
+    after = c.state()
+    assert all(np.array_equal(a, b) for a, b in zip(before[:3], after[:3])) and after[3] == before[3] + 1
+    # LRU victim: expert 5 (slot 1) and 1 (slot 0) and 7 (slot 2) all last used at tick 1 -> lowest slot first
+    sid, mode, pairs = c.ensure(np.array([[4, 7]], np.int32))
+    assert pairs.tolist() == [[4, 0]]
+    sid, mode, pairs = c.ensure(np.array([[6, 4]], np.int32))
+    assert pairs.tolist() == [[6, 1]]  # slot 1 (tick 1) is older than slot 2 (tick 3)
+
+
+def test_invalid_id_leaves_state_untouched(orc):
+    c = orc.Cache(8, 4)
+    c.ensure(np.array([[1, 2]], np.int32))
+    before = c.state()
+    for bad in (8, -1, 1 << 20):
+        with pytest.raises(ValueError):
+            c.ensure(np.array([[1, bad]], np.int32))
+        after = c.state()
+        assert all(np.array_equal(a, b) for a, b in zip(before[:3], after[:3])) and after[3] == before[3]
+
+
+def test_perfect_prediction_turns_misses_into_prefetch_hits(orc):
+    rng = np.random.default_rng(3)
+    E, S, k = 32, 12, 4
+    with_pf, without = orc.Cache(E, S), orc.Cache(E, S)
+    demand_pf = demand_plain = 0
+    for step in range(100):
+        ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(2)]).astype(np.int32)
+        installed = with_pf.install(ids, 4)  # the predictor is exact
+        _, m1, p1 = with_pf.ensure(ids)
+        _, m0, p0 = without.ensure(ids)
+        if m1 == 0:
+            # every installed expert is a hit of the very next call
+            assert set(installed[:, 0].tolist()) <= set(ids.reshape(-1).tolist())
+            assert not (set(p1[:, 0].tolist()) & set(installed[:, 0].tolist()))
+            if step == 0:  # cold: the installs cover part of the compulsory misses
+                assert len(p1) == len(p0) - len(installed)
+        demand_pf += len(p1) if m1 == 0 else 0
+        demand_plain += len(p0) if m0 == 0 else 0
+    cnt = with_pf.counters()
+    assert cnt["prefetch_hits"] == cnt["prefetch_installs"]
+    assert demand_pf < demand_plain
+
+
+def test_install_budget_zero_changes_nothing(orc):
+    rng = np.random.default_rng(4)
+    a, b = orc.Cache(16, 6), orc.Cache(16, 6)
+    for _ in range(100):
+        ids = np.stack([rng.choice(16, size=2, replace=False) for _ in range(2)]).astype(np.int32)
+        assert len(a.install(ids[::-1], 0)) == 0
+        ra, rb = a.ensure(ids), b.ensure(ids)
+        assert np.array_equal(ra[0], rb[0]) and ra[1] == rb[1] and np.array_equal(ra[2], rb[2])

@@ -1,0 +1,146 @@
+"""Pins for the oracle's expert FFN and combine.
+
+  * numpy float64 matrix products on records decoded with torch's own
+    bf16 / float8_e4m3fn dtypes (the brute force; no cache involved) agree
+    with the oracle to 1e-12 relative;
+  * placement invariance: outputs through the oracle's own slot copies are
+    bitwise identical at every slot count S = k..E and with every call
+    staged, and equal the cache-free result (the pages' statement that
+    placement never changes routing or precision);
+  * special cases: x = 0 gives y = 0; k = 1 gives one expert's output;
+    zero down-projection gives 0.
+"""
+import numpy as np
+import pytest
+import torch
+
+
+def _decode(raw, wdt, n):
+    if wdt == 0:
+        return np.frombuffer(raw[:4 * n].tobytes(), np.float32).astype(np.float64)
+    if wdt == 1:
+        return torch.from_numpy(np.frombuffer(raw[:2 * n].tobytes(), np.int16).copy()).view(torch.bfloat16).double().numpy()
+    return torch.from_numpy(np.frombuffer(raw[:n].tobytes(), np.uint8).copy()).view(torch.float8_e4m3fn).double().numpy()
+
+
+def expert_mats(rec, wdt, H, F):
+    n = H * F
+    esz = {0: 4, 1: 2, 2: 1}[wdt]
+    g = _decode(rec[0:], wdt, n).reshape(F, H)
+    u = _decode(rec[esz * n:], wdt, n).reshape(F, H)
+    d = _decode(rec[2 * esz * n:], wdt, n).reshape(H, F)
+    if wdt == 2:
+        nb = (H // 128) * (F // 128)
+        sc = np.frombuffer(rec[3 * n:3 * n + 12 * nb].tobytes(), np.float32).astype(np.float64)
+        blk = np.ones((128, 128))
+        g = g * np.kron(sc[:nb].reshape(F // 128, H // 128), blk)
+        u = u * np.kron(sc[nb:2 * nb].reshape(F // 128, H // 128), blk)
+        d = d * np.kron(sc[2 * nb:].reshape(H // 128, F // 128), blk)
+    return g, u, d
+
+
+def act_f64(x, wdt):
+    if wdt == 0:
+        return x.astype(np.float64)
+    return torch.from_numpy(x.astype(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+def brute_layer(x, host, ids, w, wdt, H, F, shared=None):
+    xv = act_f64(x, wdt)
+    y = np.zeros((x.shape[0], H))
+    cache = {}
+    for t in range(x.shape[0]):
+        for j in range(ids.shape[1]):
+            e = int(ids[t, j])
+            if e not in cache:
+                cache[e] = expert_mats(host[e], wdt, H, F)
+            g, u, d = cache[e]
+            a, b = g @ xv[t], u @ xv[t]
+            y[t] += w[t, j] * (d @ (a / (1.0 + np.exp(-a)) * b))
+        if shared is not None:
+            g, u, d = expert_mats(shared, wdt, H, F)
+            a, b = g @ xv[t], u @ xv[t]
+            y[t] += d @ (a / (1.0 + np.exp(-a)) * b)
+    return y
+
+
+CASES = [  # wdt, E, k, H, F, T
+    (0, 8, 2, 64, 128, 4),
+    (1, 16, 4, 128, 64, 3),
+    (2, 6, 2, 256, 256, 2),
+]
+
+
+@pytest.mark.parametrize("wdt,E,k,H,F,T", CASES)
+def test_ffn_matches_numpy_brute_force(orc, syn, wdt, E, k, H, F, T):
+    host = syn.records(21, 0, E, H, F, wdt)
+    wr, b = syn.router(21, 0, E, H, wdt, zipf_s=0.0)
+    x = syn.tokens(21, 9, T, H, 1, 0.0, wdt)[0]
+    ids, w, _ = orc.route(x, wr, b, k, wdt)
+    shared = syn.records(21, 0, 1, H, F, wdt, shared=True)[0] if wdt == 2 else None
+    y, y64 = orc.ffn(x, wdt, H, F, orc.host_records(host, ids), w, shared, want_f64=True)
+    ref = brute_layer(x, host, ids, w, wdt, H, F, shared)
+    assert np.max(np.abs(y64 - ref)) <= 1e-12 * np.max(np.abs(ref))
+    # output is the double sum rounded once to the activation dtype
+    if wdt == 0:
+        assert np.array_equal(y, y64.astype(np.float32))
+    else:
+        assert np.array_equal(y, np.array([orc.f64_to_bf16(v) for v in y64.reshape(-1)], np.uint16).reshape(y.shape))
+
+
+@pytest.mark.parametrize("wdt,E,k,H,F,T", CASES[:2])
+def test_placement_invariance_in_the_oracle(orc, syn, wdt, E, k, H, F, T):
+    host = syn.records(5, 0, E, H, F, wdt)
+    wr, b = syn.router(5, 0, E, H, wdt, zipf_s=0.0)  # flat routing: many misses and evictions
+    xs = syn.tokens(5, 3, T, H, 12, 0.0, wdt)
+    ref = [orc.ffn(xs[s], wdt, H, F, orc.host_records(host, orc.route(xs[s], wr, b, k, wdt)[0]),
+                   orc.route(xs[s], wr, b, k, wdt)[1]) for s in range(len(xs))]
+    modes = set()
+    for S in list(range(k, E + 1)) + ["stage_all"]:
+        L = orc.Layer(E, E if S == "stage_all" else S, k, H, F, wdt, host, wr, b)
+        for s in range(len(xs)):
+            r = L.step(xs[s], stage_all=(S == "stage_all"))
+            modes.add(r["mode"])
+            assert np.array_equal(r["y"], ref[s]), (S, s)
+    assert modes == {0, 1, 2}  # slots, decode staging and whole-layer staging all exercised
+
+
+def test_wrong_slot_map_would_change_the_output(orc, syn):
+    # the oracle reads its own slot copies: pointing (t, j) at another slot changes y
+    E, k, H, F, wdt = 8, 2, 64, 128, 0
+    host = syn.records(6, 0, E, H, F, wdt)
+    wr, b = syn.router(6, 0, E, H, wdt, zipf_s=0.0)
+    x = syn.tokens(6, 1, 2, H, 1, 0.0, wdt)[0]
+    L = orc.Layer(E, 4, k, H, F, wdt, host, wr, b)
+    r = L.step(x)
+    bad = r["slot_ids"].copy()
+    bad[0, 0] = (bad[0, 0] + 1) % 4
+    y_bad = orc.ffn(x, wdt, H, F, L.cache.records(bad), r["w"])
+    assert not np.array_equal(y_bad[0], r["y"][0]) and np.array_equal(y_bad[1], r["y"][1])
+
+
+def test_special_cases(orc, syn):
+    E, k, H, F, wdt = 8, 2, 64, 128, 0
+    host = syn.records(8, 0, E, H, F, wdt)
+    w = np.array([[0.7, 0.3]])
+    ids = np.array([[3, 5]], np.int32)
+    # x = 0 -> y = 0 (silu(0) * 0 = 0)
+    y = orc.ffn(np.zeros((1, H), np.float32), wdt, H, F, orc.host_records(host, ids), w)
+    assert np.all(y == 0)
+    # k = 1, weight 1 -> the single expert's output
+    x = syn.tokens(8, 1, 1, H, 1, 0.0, wdt)[0]
+    y1, y64 = orc.ffn(x, wdt, H, F, orc.host_records(host, ids[:, :1]), np.ones((1, 1)), want_f64=True)
+    g, u, d = expert_mats(host[3], wdt, H, F)
+    a, bb = g @ x[0].astype(np.float64), u @ x[0].astype(np.float64)
+    assert np.allclose(y64[0], d @ (a / (1 + np.exp(-a)) * bb), rtol=1e-13, atol=0)
+    # zeroed down projection -> 0
+    h2 = host.copy()
+    h2[3, 2 * 4 * H * F:3 * 4 * H * F] = 0
+    h2[5, 2 * 4 * H * F:3 * 4 * H * F] = 0
+    assert np.all(orc.ffn(x, wdt, H, F, orc.host_records(h2, ids), w) == 0)
+
+
+def test_residual_rounds_once(orc):
+    x = np.array([0x3F80, 0x3F80], np.uint16)         # 1.0, 1.0
+    y = np.array([0x3B80, 0x3B81], np.uint16)         # 2^-8 (tie -> 1.0), 2^-8(1 + 2^-7) (-> 1 + 2^-7)
+    assert orc.residual(x, y, 1).tolist() == [0x3F80, 0x3F81]
