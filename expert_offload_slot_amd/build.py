@@ -1,0 +1,48 @@
+"""Builds libmoe_offload.so (gfx950 only) from csrc/*.hip with hipcc, in-tree."""
+import glob
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+OUT_DIR = os.path.join(HERE, "_build")
+LIB = os.path.join(OUT_DIR, "libmoe_offload.so")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
+    # no packed fp32 instructions anywhere
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the router's binary32 order is part of its definition: no contraction, no denormal flushing
+    "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def build(verbose=False):
+    os.makedirs(OUT_DIR, exist_ok=True)
+    objs = []
+    for src in SRC:
+        obj = os.path.join(OUT_DIR, os.path.basename(src).replace(".hip", ".o"))
+        cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l and l.strip())
+        if r.returncode != 0:
+            raise RuntimeError("hipcc failed for %s:\n%s" % (src, err))
+        if err and verbose:
+            print(err, file=sys.stderr)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n%s" % r.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

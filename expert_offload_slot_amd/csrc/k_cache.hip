@@ -1,0 +1,438 @@
+// Per-layer LRU slot table on the GPU: ensure (lookup, victims, id rewrite,
+// copy list, counters), prefetch install, whole-layer staging, reset, and the
+// copy kernel that moves records from device-mapped pinned host memory.
+//
+// xinfer-ai 0.14.6 docs/moe_offload.md, "How it works" (Decode, Prefill);
+// FreeToken issue #677, "Proposal" (Install, Correctness constraint).
+//
+// The table is only ever written by one workgroup of one kernel at a time,
+// on the caller's compute stream: no atomics on shared state, no races.
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kBlock = 1024;  // one workgroup, 16 wavefronts
+constexpr int kWaves = kBlock / 64;
+
+// Exclusive rank of `flag` among the block's threads in thread order, and the total.
+// All threads of the block must call it.  Uses s_wave[kWaves].
+__device__ __forceinline__ int block_rank(bool flag, int* s_wave, int* total) {
+  const unsigned long long m = __ballot(flag);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int below = __popcll(m & ((1ull << lane) - 1ull));
+  if (lane == 0) s_wave[wid] = __popcll(m);
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int c = s_wave[w];
+    base += w < wid ? c : 0;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + below;
+}
+
+// victim order key: (occupied, last_use, slot) ascending
+__device__ __forceinline__ bool key_before(bool occ_a, uint64_t lu_a, int a, bool occ_b, uint64_t lu_b, int b) {
+  if (occ_a != occ_b) return !occ_a;
+  if (lu_a != lu_b) return lu_a < lu_b;
+  return a < b;
+}
+
+struct SharedTable {
+  int slot_of[kMaxExperts];
+  int expert_of[kMaxExperts];
+  uint64_t last_use[kMaxExperts];
+  int flag[kMaxExperts];   // ensure: expert in D; install: tokens predicting it
+  int aux[kMaxExperts];    // install: best top-k position
+  int vic[kMaxExperts];    // victim slot by rank
+  int cand[kMaxExperts];   // install: candidate expert by rank
+  int wave[kWaves];
+  int bad;
+};
+
+// Loads the table into LDS.  Entries outside their range (only possible if
+// the table was overwritten from outside) are dropped and flagged, so every
+// later index stays in bounds.
+__device__ void load_table(const CacheDev& c, SharedTable& t) {
+  const int tid = threadIdx.x;
+  if (tid < c.E) {
+    int s = c.slot_of[tid];
+    if (s < -1 || s >= c.S) {
+      atomicOr(c.err, MOE_DEV_ERR_AUDIT);
+      s = -1;
+    }
+    t.slot_of[tid] = s;
+  }
+  if (tid < c.S) {
+    int e = c.expert_of[tid];
+    if (e < -1 || e >= c.E) {
+      atomicOr(c.err, MOE_DEV_ERR_AUDIT);
+      e = -1;
+    }
+    t.expert_of[tid] = e;
+    t.last_use[tid] = c.last_use[tid];
+  }
+}
+
+__device__ void store_table(const CacheDev& c, const SharedTable& t) {
+  const int tid = threadIdx.x;
+  if (tid < c.E) c.slot_of[tid] = t.slot_of[tid];
+  if (tid < c.S) {
+    c.expert_of[tid] = t.expert_of[tid];
+    c.last_use[tid] = t.last_use[tid];
+  }
+}
+
+// Audit: maps mutually inverse (and, for ensure, every expert of D resident).
+__device__ void audit_table(const CacheDev& c, const SharedTable& t, bool check_D) {
+  const int tid = threadIdx.x;
+  bool bad = false;
+  if (tid < c.S) {
+    const int e = t.expert_of[tid];
+    if (e >= c.E || (e >= 0 && t.slot_of[e] != tid)) bad = true;
+  }
+  if (tid < c.E) {
+    const int s = t.slot_of[tid];
+    if (s >= c.S || (s >= 0 && t.expert_of[s] != tid)) bad = true;
+    if (check_D && t.flag[tid] && s < 0) bad = true;
+  }
+  if (bad) atomicOr(c.err, MOE_DEV_ERR_AUDIT);
+}
+
+// ---------------------------------------------------------------- ensure
+__global__ __launch_bounds__(kBlock) void k_ensure(CacheDev c, const int32_t* __restrict__ ids, int n,
+                                                   int32_t* __restrict__ slot_ids, int audit) {
+  __shared__ SharedTable t;
+  const int tid = threadIdx.x;
+  const int E = c.E, S = c.S;
+  load_table(c, t);
+  if (tid < E) t.flag[tid] = 0;
+  if (tid == 0) t.bad = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += kBlock) {
+    const int e = ids[i];
+    if ((unsigned)e >= (unsigned)E) t.bad = 1;
+    else t.flag[e] = 1;
+  }
+  __syncthreads();
+  if (t.bad) {  // no-op call: table untouched, empty copy list, valid (0) slot ids
+    for (int i = tid; i < n; i += kBlock) slot_ids[i] = 0;
+    if (tid == 0) {
+      atomicOr(c.err, MOE_DEV_ERR_BAD_ID);
+      c.copy_list[0] = MOE_MODE_SLOTS;
+      c.copy_list[1] = 0;
+    }
+    return;
+  }
+  if (audit) audit_table(c, t, false);
+  const uint64_t tick = *c.tick + 1;
+  const bool inD = tid < E && t.flag[tid];
+  const int sl = tid < E ? t.slot_of[tid] : -1;
+  const bool miss = inD && sl < 0;
+  const bool hit = inD && sl >= 0;
+  const bool pf_hit = hit && t.last_use[sl] == 0;
+  int nd, nm, nh, npf;
+  (void)block_rank(inD, t.wave, &nd);
+  const int mrank = block_rank(miss, t.wave, &nm);
+  (void)block_rank(hit, t.wave, &nh);
+  (void)block_rank(pf_hit, t.wave, &npf);
+
+  if (nd > S) {  // staged: table untouched, residents read in place, misses staged at S + e
+    if (miss) {
+      c.copy_list[2 + 2 * mrank] = tid;
+      c.copy_list[3 + 2 * mrank] = S + tid;
+    }
+    for (int i = tid; i < n; i += kBlock) {
+      const int e = ids[i];
+      const int r = t.slot_of[e];
+      slot_ids[i] = r >= 0 ? r : S + e;
+    }
+    if (tid == 0) {
+      c.copy_list[0] = MOE_MODE_STAGED;
+      c.copy_list[1] = nm;
+      *c.tick = tick;
+      c.counters[C_CALLS] += 1;
+      c.counters[C_STAGED_CALLS] += 1;
+      c.counters[C_STAGED_COPIES] += (uint64_t)nm;
+      c.counters[C_BYTES] += (uint64_t)nm * c.record_bytes;
+    }
+    return;
+  }
+
+  // victim ranks among eligible slots (those not holding an expert of D)
+  if (tid < S) {
+    const int ex = t.expert_of[tid];
+    const bool occ = ex >= 0;
+    if (!occ || !t.flag[ex]) {
+      const uint64_t lu = t.last_use[tid];
+      int rank = 0;
+      for (int s2 = 0; s2 < S; ++s2) {
+        const int ex2 = t.expert_of[s2];
+        const bool occ2 = ex2 >= 0;
+        if (occ2 && t.flag[ex2]) continue;
+        rank += key_before(occ2, t.last_use[s2], s2, occ, lu, tid) ? 1 : 0;
+      }
+      if (rank < nm) t.vic[rank] = tid;
+    }
+  }
+  __syncthreads();
+  if (miss) {
+    const int v = t.vic[mrank];
+    const int old = t.expert_of[v];
+    if (old >= 0) t.slot_of[old] = -1;
+    t.expert_of[v] = tid;
+    t.slot_of[tid] = v;
+    c.copy_list[2 + 2 * mrank] = tid;
+    c.copy_list[3 + 2 * mrank] = v;
+  }
+  __syncthreads();
+  if (inD) t.last_use[t.slot_of[tid]] = tick;
+  __syncthreads();
+  for (int i = tid; i < n; i += kBlock) slot_ids[i] = t.slot_of[ids[i]];
+  store_table(c, t);
+  if (audit) audit_table(c, t, true);
+  if (tid == 0) {
+    c.copy_list[0] = MOE_MODE_SLOTS;
+    c.copy_list[1] = nm;
+    *c.tick = tick;
+    c.counters[C_CALLS] += 1;
+    c.counters[C_HITS] += (uint64_t)nh;
+    c.counters[C_MISSES] += (uint64_t)nm;
+    c.counters[C_PF_HITS] += (uint64_t)npf;
+    c.counters[C_BYTES] += (uint64_t)nm * c.record_bytes;
+  }
+}
+
+// ---------------------------------------------------------------- prefetch install
+__global__ __launch_bounds__(kBlock) void k_install(CacheDev c, const int32_t* __restrict__ pred, int n, int k,
+                                                    int max_n, int audit) {
+  __shared__ SharedTable t;
+  const int tid = threadIdx.x;
+  const int E = c.E, S = c.S;
+  load_table(c, t);
+  if (tid < E) {
+    t.flag[tid] = 0;  // tokens predicting the expert
+    t.aux[tid] = k;   // best top-k position
+  }
+  if (tid == 0) t.bad = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += kBlock) {
+    const int e = pred[i];
+    if ((unsigned)e >= (unsigned)E) {
+      t.bad = 1;
+    } else {
+      atomicAdd(&t.flag[e], 1);
+      atomicMin(&t.aux[e], i % k);
+    }
+  }
+  __syncthreads();
+  if (t.bad) {
+    if (tid == 0) {
+      atomicOr(c.err, MOE_DEV_ERR_BAD_ID);
+      c.pf_list[0] = MOE_MODE_SLOTS;
+      c.pf_list[1] = 0;
+    }
+    return;
+  }
+  // candidates: predicted and not resident, ordered by (count desc, best asc, id asc)
+  const bool cand = tid < E && t.flag[tid] > 0 && t.slot_of[tid] < 0;
+  int nc, nv;
+  (void)block_rank(cand, t.wave, &nc);
+  int crank = 0;
+  if (cand) {
+    const int cn = t.flag[tid], cb = t.aux[tid];
+    for (int e2 = 0; e2 < E; ++e2) {
+      if (!(t.flag[e2] > 0 && t.slot_of[e2] < 0)) continue;
+      const int n2 = t.flag[e2], b2 = t.aux[e2];
+      crank += (n2 > cn || (n2 == cn && (b2 < cb || (b2 == cb && e2 < tid)))) ? 1 : 0;
+    }
+  }
+  // victims: slots not holding a predicted expert, in ensure's order
+  bool elig = false;
+  int vrank = 0;
+  if (tid < S) {
+    const int ex = t.expert_of[tid];
+    const bool occ = ex >= 0;
+    elig = !occ || t.flag[ex] == 0;
+    if (elig) {
+      const uint64_t lu = t.last_use[tid];
+      for (int s2 = 0; s2 < S; ++s2) {
+        const int ex2 = t.expert_of[s2];
+        const bool occ2 = ex2 >= 0;
+        if (occ2 && t.flag[ex2] > 0) continue;
+        vrank += key_before(occ2, t.last_use[s2], s2, occ, lu, tid) ? 1 : 0;
+      }
+    }
+  }
+  (void)block_rank(elig, t.wave, &nv);
+  int m = max_n < nc ? max_n : nc;
+  m = m < nv ? m : nv;
+  if (cand && crank < m) t.cand[crank] = tid;
+  if (elig && vrank < m) t.vic[vrank] = tid;
+  __syncthreads();
+  if (tid < m) {
+    const int e = t.cand[tid], v = t.vic[tid];
+    const int old = t.expert_of[v];
+    if (old >= 0) t.slot_of[old] = -1;
+    t.expert_of[v] = e;
+    t.slot_of[e] = v;
+    t.last_use[v] = 0;
+    c.pf_list[2 + 2 * tid] = e;
+    c.pf_list[3 + 2 * tid] = v;
+  }
+  __syncthreads();
+  store_table(c, t);
+  if (audit) audit_table(c, t, false);
+  if (tid == 0) {
+    c.pf_list[0] = MOE_MODE_SLOTS;
+    c.pf_list[1] = m;
+    c.counters[C_PF_INSTALLS] += (uint64_t)m;
+    c.counters[C_BYTES] += (uint64_t)m * c.record_bytes;
+  }
+}
+
+// ---------------------------------------------------------------- prefill helpers
+// distinct ids of a call; -1 if any id is outside [0, E)
+__global__ __launch_bounds__(kBlock) void k_distinct(int E, const int32_t* __restrict__ ids, int n, int32_t* out) {
+  __shared__ int flag[kMaxExperts];
+  __shared__ int wave[kWaves];
+  __shared__ int bad;
+  const int tid = threadIdx.x;
+  if (tid < E) flag[tid] = 0;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += kBlock) {
+    const int e = ids[i];
+    if ((unsigned)e >= (unsigned)E) bad = 1;
+    else flag[e] = 1;
+  }
+  __syncthreads();
+  int nd;
+  (void)block_rank(tid < E && flag[tid], wave, &nd);
+  if (tid == 0) *out = bad ? -1 : nd;
+}
+
+// whole-layer staging: ids -> S + id, copy list {STAGED_ALL, E, (e, S+e)}, tick and counters
+__global__ void k_stage_all(CacheDev c, const int32_t* __restrict__ ids, int n, int32_t* __restrict__ slot_ids) {
+  const int i0 = blockIdx.x * blockDim.x + threadIdx.x, step = gridDim.x * blockDim.x;
+  for (int i = i0; i < n; i += step) slot_ids[i] = c.S + ids[i];
+  for (int e = i0; e < c.E; e += step) {
+    c.copy_list[2 + 2 * e] = e;
+    c.copy_list[3 + 2 * e] = c.S + e;
+  }
+  if (i0 == 0) {
+    c.copy_list[0] = MOE_MODE_STAGED_ALL;
+    c.copy_list[1] = c.E;
+    *c.tick += 1;
+    c.counters[C_CALLS] += 1;
+    c.counters[C_STAGED_CALLS] += 1;
+    c.counters[C_STAGED_COPIES] += (uint64_t)c.E;
+    c.counters[C_BYTES] += (uint64_t)c.E * c.record_bytes;
+  }
+}
+
+// empty cache, zero counters and error, empty lists, zero self-resetting counters
+__global__ void k_reset(CacheDev c, uint32_t* route_ctr, int n_route, uint32_t* comb_ctr, int n_comb) {
+  const int i0 = blockIdx.x * blockDim.x + threadIdx.x, step = gridDim.x * blockDim.x;
+  for (int e = i0; e < c.E; e += step) c.slot_of[e] = -1;
+  for (int s = i0; s < c.S; s += step) {
+    c.expert_of[s] = -1;
+    c.last_use[s] = 0;
+  }
+  for (int i = i0; i < n_route; i += step) route_ctr[i] = 0;
+  for (int i = i0; i < n_comb; i += step) comb_ctr[i] = 0;
+  for (int i = i0; i < C_N; i += step) c.counters[i] = 0;
+  if (i0 == 0) {
+    *c.tick = 0;
+    *c.err = 0;
+    c.copy_list[0] = MOE_MODE_SLOTS;
+    c.copy_list[1] = 0;
+    c.pf_list[0] = MOE_MODE_SLOTS;
+    c.pf_list[1] = 0;
+  }
+}
+
+// ---------------------------------------------------------------- copy
+// Fixed grid; the list (mode, count, pairs) is read on the device.  Each
+// workgroup moves 16 KiB chunks: 256 threads x 4 loads of 16 bytes in flight,
+// read from the device-mapped host store over the host link, written to HBM.
+__global__ __launch_bounds__(kCopyThreads) void k_copy(const int32_t* __restrict__ list,
+                                                      const uint8_t* __restrict__ host, uint8_t* __restrict__ slots,
+                                                      uint8_t* __restrict__ staging, uint64_t stride, uint64_t rb16,
+                                                      int S, int E, int32_t* err) {
+  const int mode = list[0];
+  const int count = list[1];
+  if (mode == MOE_MODE_STAGED_ALL || count <= 0) return;
+  constexpr uint64_t CH = (uint64_t)kCopyThreads * kCopyUnroll;
+  const uint64_t per = (rb16 + CH - 1) / CH;
+  const uint64_t total = (uint64_t)count * per;
+  for (uint64_t cidx = blockIdx.x; cidx < total; cidx += gridDim.x) {
+    const int m = (int)(cidx / per);
+    const uint64_t off = (cidx - (uint64_t)m * per) * CH;
+    const int e = list[2 + 2 * m], r = list[3 + 2 * m];
+    if ((unsigned)e >= (unsigned)E || (unsigned)r >= (unsigned)(S + E)) {
+      if (threadIdx.x == 0) atomicOr(err, MOE_DEV_ERR_AUDIT);
+      continue;
+    }
+    const uint4* src = reinterpret_cast<const uint4*>(host + (uint64_t)e * stride) + off;
+    uint8_t* dbase = r < S ? slots + (uint64_t)r * stride : staging + (uint64_t)(r - S) * stride;
+    uint4* dst = reinterpret_cast<uint4*>(dbase) + off;
+    const uint64_t lim = rb16 - off;
+    uint4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const uint64_t i = (uint64_t)u * kCopyThreads + threadIdx.x;
+      if (i < lim) v[u] = src[i];
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const uint64_t i = (uint64_t)u * kCopyThreads + threadIdx.x;
+      if (i < lim) dst[i] = v[u];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_ensure(moe_offload* h, const int32_t* ids, int n, int32_t* slot_ids, hipStream_t s) {
+  hipLaunchKernelGGL(k_ensure, dim3(1), dim3(kBlock), 0, s, h->cache, ids, n, slot_ids,
+                     (h->flags & MOE_FLAG_AUDIT) ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_install(moe_offload* h, const int32_t* pred, int T, int max_n, hipStream_t s) {
+  hipLaunchKernelGGL(k_install, dim3(1), dim3(kBlock), 0, s, h->cache, pred, T * h->k, h->k, max_n,
+                     (h->flags & MOE_FLAG_AUDIT) ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_distinct(moe_offload* h, const int32_t* ids, int n, int32_t* out_dev, hipStream_t s) {
+  hipLaunchKernelGGL(k_distinct, dim3(1), dim3(kBlock), 0, s, h->E, ids, n, out_dev);
+  return hipGetLastError();
+}
+
+hipError_t launch_stage_all(moe_offload* h, const int32_t* ids, int n, int32_t* slot_ids, hipStream_t s) {
+  hipLaunchKernelGGL(k_stage_all, dim3(64), dim3(256), 0, s, h->cache, ids, n, slot_ids);
+  return hipGetLastError();
+}
+
+hipError_t launch_reset(moe_offload* h, hipStream_t s) {
+  const int n_route = (h->max_tokens + kRouteTokens - 1) / kRouteTokens;
+  hipLaunchKernelGGL(k_reset, dim3(16), dim3(256), 0, s, h->cache, h->route_ctr, n_route, h->comb_ctr, h->H / 16);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy(moe_offload* h, const int32_t* list, hipStream_t s) {
+  hipLaunchKernelGGL(k_copy, dim3(kCopyGrid), dim3(kCopyThreads), 0, s, list, h->host_dev, h->slots, h->staging,
+                     // whole 16-byte units: the record stride is a multiple of 4096, so rounding
+                     // the record up stays inside its own stride on both sides
+                     (uint64_t)h->record_stride, (uint64_t)((h->record_bytes + 15) / 16), h->S, h->E,
+                     h->cache.err);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,371 @@
+// Handle lifetime, argument checks, error convention and the C entry points.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(e == hipErrorOutOfMemory ? MOE_ENOMEM : MOE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(call)                              \
+  do {                                             \
+    hipError_t e_ = (call);                        \
+    if (e_ != hipSuccess) return hip_fail(e_, #call); \
+  } while (0)
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+size_t record_bytes_of(int dtype, int H, int F) {
+  size_t n = 3 * (size_t)H * (size_t)F;
+  if (dtype == MOE_F32) return 4 * n;
+  if (dtype == MOE_BF16) return 2 * n;
+  return n + 3 * (size_t)(H / 128) * (size_t)(F / 128) * 4;
+}
+
+bool same_shape(const moe_offload* a, const moe_offload_desc* d) {
+  return a->E == d->num_experts && a->H == d->hidden && a->F == d->ffn && a->dtype == d->dtype;
+}
+
+// RAII device guard: every entry point runs on the handle's device.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) ok = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+void free_all(moe_offload* h) {
+  if (h->own_host && h->host) (void)hipHostFree(h->host);
+  if (h->slots) (void)hipFree(h->slots);
+  if (h->own_staging && h->staging) (void)hipFree(h->staging);
+  if (h->state_block) (void)hipFree(h->state_block);
+  if (h->pinned_i32) (void)hipHostFree(h->pinned_i32);
+}
+
+int check_handle(const moe_offload* h) {
+  if (!h) return fail(MOE_EINVAL, "null handle");
+  return MOE_OK;
+}
+
+int check_T(const moe_offload* h, int32_t T) {
+  if (T < 1 || T > h->max_tokens) return fail(MOE_EINVAL, "T=%d outside [1, max_tokens=%d]", T, h->max_tokens);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_offload_last_error(void) { return g_err; }
+
+int moe_offload_create(const moe_offload_desc* d, moe_offload** out) {
+  g_err[0] = 0;
+  if (!d || !out) return fail(MOE_EINVAL, "null argument");
+  *out = nullptr;
+  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16 && d->dtype != MOE_FP8_E4M3_B128)
+    return fail(MOE_EUNSUPPORTED, "unsupported dtype %d", d->dtype);
+  if (d->num_experts < 1 || d->num_experts > moe::kMaxExperts)
+    return fail(MOE_EINVAL, "num_experts=%d outside [1, %d]", d->num_experts, moe::kMaxExperts);
+  if (d->top_k < 1 || d->top_k > moe::kMaxTopK || d->top_k > d->num_experts)
+    return fail(MOE_EINVAL, "top_k=%d outside [1, min(%d, E)]", d->top_k, moe::kMaxTopK);
+  if (d->num_slots < d->top_k || d->num_slots > d->num_experts)
+    return fail(MOE_EINVAL, "num_slots=%d outside [top_k=%d, E=%d]", d->num_slots, d->top_k, d->num_experts);
+  int mult = d->dtype == MOE_F32 ? 64 : 128;
+  if (d->hidden < mult || d->hidden % mult || d->ffn < mult || d->ffn % mult)
+    return fail(MOE_EUNSUPPORTED, "hidden=%d / ffn=%d must be positive multiples of %d for this dtype", d->hidden,
+                d->ffn, mult);
+  if (d->hidden > 65536 || d->ffn > 65536) return fail(MOE_EINVAL, "hidden/ffn above 65536");
+  if (d->max_tokens < 1 || d->max_tokens > 65536) return fail(MOE_EINVAL, "max_tokens=%d outside [1, 65536]", d->max_tokens);
+  if (d->share_host && !same_shape(d->share_host, d)) return fail(MOE_EINVAL, "share_host handle has another shape");
+  if (d->share_staging && !same_shape(d->share_staging, d))
+    return fail(MOE_EINVAL, "share_staging handle has another shape");
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || d->device < 0 || d->device >= ndev)
+    return fail(MOE_EINVAL, "device %d not available (%d devices)", d->device, ndev);
+  DeviceGuard g(d->device);
+  if (!g.ok) return fail(MOE_EHIP, "hipSetDevice(%d) failed", d->device);
+
+  moe_offload* h = new (std::nothrow) moe_offload();
+  if (!h) return fail(MOE_ENOMEM, "host allocation of the handle failed");
+  memset(h, 0, sizeof *h);
+  h->E = d->num_experts;
+  h->S = d->num_slots;
+  h->H = d->hidden;
+  h->F = d->ffn;
+  h->k = d->top_k;
+  h->dtype = d->dtype;
+  h->max_tokens = d->max_tokens;
+  h->device = d->device;
+  h->flags = d->flags;
+  h->record_bytes = record_bytes_of(h->dtype, h->H, h->F);
+  h->record_stride = align_up(h->record_bytes, 4096);
+
+  int rc = MOE_OK;
+  auto bail = [&](int code) {
+    free_all(h);
+    delete h;
+    return code;
+  };
+  hipError_t e;
+  const size_t store = (size_t)h->E * h->record_stride;
+  if (d->share_host) {
+    h->host = d->share_host->host;
+    h->host_dev = d->share_host->host_dev;
+    h->own_host = false;
+  } else {
+    unsigned hf = hipHostMallocMapped | ((h->flags & MOE_FLAG_HOST_COHERENT) ? hipHostMallocCoherent
+                                                                               : hipHostMallocNonCoherent);
+    e = hipHostMalloc((void**)&h->host, store, hf);
+    if (e != hipSuccess) {
+      rc = fail(MOE_ENOMEM, "pinned host store of %zu bytes: %s", store, hipGetErrorString(e));
+      return bail(rc);
+    }
+    h->own_host = true;
+    e = hipHostGetDevicePointer((void**)&h->host_dev, h->host, 0);
+    if (e != hipSuccess) return bail(hip_fail(e, "hipHostGetDevicePointer"));
+  }
+  e = hipMalloc((void**)&h->slots, (size_t)h->S * h->record_stride);
+  if (e != hipSuccess) return bail(hip_fail(e, "slot tensor"));
+  if (d->share_staging) {
+    h->staging = d->share_staging->staging;
+    h->own_staging = false;
+  } else {
+    e = hipMalloc((void**)&h->staging, store);
+    if (e != hipSuccess) return bail(hip_fail(e, "staging buffer"));
+    h->own_staging = true;
+  }
+
+  // one allocation for the table, lists, counters and workspaces
+  const int maxSE = std::max(h->S, h->E);
+  const int max_pairs = h->max_tokens * h->k;
+  h->gl.max_pairs = max_pairs;
+  h->gl.max_recs = std::min(max_pairs, h->S + h->E) + 1;
+  const int rows = max_pairs + h->max_tokens;  // routed pairs + shared-expert rows
+  const int route_groups = (h->max_tokens + moe::kRouteTokens - 1) / moe::kRouteTokens;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  size_t o_slot_of = take(4 * (size_t)h->E), o_expert_of = take(4 * (size_t)h->S), o_last = take(8 * (size_t)h->S);
+  size_t o_tick = take(8), o_list = take(4 * (2 + 2 * (size_t)maxSE)), o_pf = take(4 * (2 + 2 * (size_t)h->S));
+  size_t o_cnt = take(8 * moe::C_N), o_err = take(4), o_logits = take(4 * (size_t)h->max_tokens * h->E);
+  size_t o_rctr = take(4 * (size_t)route_groups), o_grp = take(4 * (size_t)h->gl.words());
+  size_t o_h = take((h->dtype == MOE_F32 ? 4 : 2) * (size_t)rows * h->F), o_part = take(4 * (size_t)rows * h->H);
+  size_t o_cctr = take(4 * (size_t)(h->H / 16)), o_scr = take(64);
+  e = hipMalloc(&h->state_block, off);
+  if (e != hipSuccess) return bail(hip_fail(e, "state block"));
+  uint8_t* b = (uint8_t*)h->state_block;
+  h->cache.slot_of = (int32_t*)(b + o_slot_of);
+  h->cache.expert_of = (int32_t*)(b + o_expert_of);
+  h->cache.last_use = (uint64_t*)(b + o_last);
+  h->cache.tick = (uint64_t*)(b + o_tick);
+  h->cache.copy_list = (int32_t*)(b + o_list);
+  h->cache.pf_list = (int32_t*)(b + o_pf);
+  h->cache.counters = (uint64_t*)(b + o_cnt);
+  h->cache.err = (int32_t*)(b + o_err);
+  h->cache.E = h->E;
+  h->cache.S = h->S;
+  h->cache.record_bytes = h->record_bytes;
+  h->logits = (float*)(b + o_logits);
+  h->route_ctr = (uint32_t*)(b + o_rctr);
+  h->grp = (int32_t*)(b + o_grp);
+  h->hbuf = (void*)(b + o_h);
+  h->part = (float*)(b + o_part);
+  h->comb_ctr = (uint32_t*)(b + o_cctr);
+  h->scratch_i32 = (int32_t*)(b + o_scr);
+  e = hipHostMalloc((void**)&h->pinned_i32, 64, hipHostMallocDefault);
+  if (e != hipSuccess) return bail(hip_fail(e, "pinned scratch"));
+  // zero everything (counters, workspaces), then set the empty-cache state
+  e = hipMemset(h->state_block, 0, off);
+  if (e != hipSuccess) return bail(hip_fail(e, "hipMemset"));
+  e = moe::launch_reset(h, nullptr);
+  if (e != hipSuccess) return bail(hip_fail(e, "reset kernel"));
+  e = hipDeviceSynchronize();
+  if (e != hipSuccess) return bail(hip_fail(e, "hipDeviceSynchronize"));
+  *out = h;
+  return MOE_OK;
+}
+
+void moe_offload_destroy(moe_offload* h) {
+  if (!h) return;
+  DeviceGuard g(h->device);
+  (void)hipDeviceSynchronize();
+  free_all(h);
+  delete h;
+}
+
+int moe_offload_host_records(moe_offload* h, void** host, size_t* record_stride, size_t* record_bytes) {
+  if (int rc = check_handle(h)) return rc;
+  if (host) *host = h->host;
+  if (record_stride) *record_stride = h->record_stride;
+  if (record_bytes) *record_bytes = h->record_bytes;
+  return MOE_OK;
+}
+
+int moe_route_topk(moe_offload* h, const void* x, const void* w_router, const float* bias, int32_t T, int32_t* ids,
+                   float* w, void* stream) {
+  if (int rc = check_handle(h)) return rc;
+  if (int rc = check_T(h, T)) return rc;
+  if (!x || !w_router || !bias || !ids || !w) return fail(MOE_EINVAL, "moe_route_topk: null pointer");
+  DeviceGuard g(h->device);
+  HIP_TRY(moe::launch_route(h, x, w_router, bias, T, ids, w, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_slot_ensure(moe_offload* h, const int32_t* ids, int32_t T, int32_t* slot_ids, void* stream) {
+  if (int rc = check_handle(h)) return rc;
+  if (int rc = check_T(h, T)) return rc;
+  if (!ids || !slot_ids) return fail(MOE_EINVAL, "moe_slot_ensure: null pointer");
+  DeviceGuard g(h->device);
+  HIP_TRY(moe::launch_ensure(h, ids, T * h->k, slot_ids, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_copy_misses(moe_offload* h, void* stream) {
+  if (int rc = check_handle(h)) return rc;
+  DeviceGuard g(h->device);
+  HIP_TRY(moe::launch_copy(h, h->cache.copy_list, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_slot_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int32_t T,
+                 const void* shared_record, void* y, void* x_next, void* stream) {
+  if (int rc = check_handle(h)) return rc;
+  if (int rc = check_T(h, T)) return rc;
+  if (!x || !slot_ids || !w || !y) return fail(MOE_EINVAL, "moe_slot_ffn: null pointer");
+  DeviceGuard g(h->device);
+  HIP_TRY(moe::launch_ffn(h, x, slot_ids, w, T, shared_record, y, x_next, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_prefill_stage(moe_offload* h, const int32_t* ids, int32_t T, int32_t* slot_ids, int32_t* staged_out,
+                      void* stream) {
+  if (int rc = check_handle(h)) return rc;
+  if (int rc = check_T(h, T)) return rc;
+  if (!ids || !slot_ids) return fail(MOE_EINVAL, "moe_prefill_stage: null pointer");
+  DeviceGuard g(h->device);
+  hipStream_t s = (hipStream_t)stream;
+  const int n = T * h->k;
+  HIP_TRY(moe::launch_distinct(h, ids, n, h->scratch_i32, s));
+  HIP_TRY(hipMemcpyAsync(h->pinned_i32, h->scratch_i32, 4, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  const int nd = h->pinned_i32[0];
+  if (nd < 0) return fail(MOE_EDEVICE, "moe_prefill_stage: expert id outside [0, %d)", h->E);
+  if (nd > h->S) {
+    HIP_TRY(hipMemcpyAsync(h->staging, h->host, (size_t)h->E * h->record_stride, hipMemcpyHostToDevice, s));
+    HIP_TRY(moe::launch_stage_all(h, ids, n, slot_ids, s));
+    if (staged_out) *staged_out = 1;
+  } else {
+    HIP_TRY(moe::launch_ensure(h, ids, n, slot_ids, s));
+    HIP_TRY(moe::launch_copy(h, h->cache.copy_list, s));
+    if (staged_out) *staged_out = 0;
+  }
+  return MOE_OK;
+}
+
+int moe_prefetch_install(moe_offload* h, const int32_t* pred_ids, int32_t T, int32_t max_n, void* stream) {
+  if (int rc = check_handle(h)) return rc;
+  if (int rc = check_T(h, T)) return rc;
+  if (!pred_ids) return fail(MOE_EINVAL, "moe_prefetch_install: null pointer");
+  if (max_n < 0 || max_n > h->S) return fail(MOE_EINVAL, "max_n=%d outside [0, S=%d]", max_n, h->S);
+  DeviceGuard g(h->device);
+  HIP_TRY(moe::launch_install(h, pred_ids, T, max_n, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_copy_prefetch(moe_offload* h, void* stream) {
+  if (int rc = check_handle(h)) return rc;
+  DeviceGuard g(h->device);
+  HIP_TRY(moe::launch_copy(h, h->cache.pf_list, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_offload_stats(moe_offload* h, moe_stats* out) {
+  if (int rc = check_handle(h)) return rc;
+  if (!out) return fail(MOE_EINVAL, "null stats");
+  DeviceGuard g(h->device);
+  HIP_TRY(hipDeviceSynchronize());
+  uint64_t c[moe::C_N];
+  uint64_t tick = 0;
+  int32_t err = 0;
+  HIP_TRY(hipMemcpy(c, h->cache.counters, sizeof c, hipMemcpyDeviceToHost));
+  HIP_TRY(hipMemcpy(&tick, h->cache.tick, 8, hipMemcpyDeviceToHost));
+  HIP_TRY(hipMemcpy(&err, h->cache.err, 4, hipMemcpyDeviceToHost));
+  int32_t* eo = new (std::nothrow) int32_t[h->S];
+  if (!eo) return fail(MOE_ENOMEM, "stats scratch");
+  hipError_t e = hipMemcpy(eo, h->cache.expert_of, 4 * (size_t)h->S, hipMemcpyDeviceToHost);
+  int resident = 0;
+  for (int s = 0; s < h->S; ++s) resident += eo[s] >= 0;
+  delete[] eo;
+  if (e != hipSuccess) return hip_fail(e, "stats copy");
+  out->calls = c[moe::C_CALLS];
+  out->hits = c[moe::C_HITS];
+  out->misses = c[moe::C_MISSES];
+  out->staged_calls = c[moe::C_STAGED_CALLS];
+  out->staged_copies = c[moe::C_STAGED_COPIES];
+  out->prefetch_installs = c[moe::C_PF_INSTALLS];
+  out->prefetch_hits = c[moe::C_PF_HITS];
+  out->bytes_copied = c[moe::C_BYTES];
+  out->tick = tick;
+  out->error = err;
+  out->resident = resident;
+  return MOE_OK;
+}
+
+int moe_offload_reset(moe_offload* h, void* stream) {
+  if (int rc = check_handle(h)) return rc;
+  DeviceGuard g(h->device);
+  HIP_TRY(moe::launch_reset(h, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_offload_query(const moe_offload* h, moe_info* out) {
+  if (int rc = check_handle(h)) return rc;
+  if (!out) return fail(MOE_EINVAL, "null info");
+  out->slot_of = h->cache.slot_of;
+  out->expert_of = h->cache.expert_of;
+  out->last_use = h->cache.last_use;
+  out->copy_list = h->cache.copy_list;
+  out->prefetch_list = h->cache.pf_list;
+  out->slots = h->slots;
+  out->staging = h->staging;
+  out->host = h->host;
+  out->host_dev = h->host_dev;
+  out->record_bytes = h->record_bytes;
+  out->record_stride = h->record_stride;
+  out->E = h->E;
+  out->S = h->S;
+  out->H = h->H;
+  out->F = h->F;
+  out->k = h->k;
+  out->dtype = h->dtype;
+  out->max_tokens = h->max_tokens;
+  out->device = h->device;
+  return MOE_OK;
+}
+
+}  // extern "C"

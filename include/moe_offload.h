@@ -1,0 +1,258 @@
+/*
+ * moe_offload.h — C ABI of the offloaded Mixture-of-Experts layer step on
+ * one MI355X (gfx950).
+ *
+ * One handle = one MoE layer.  Every routed expert of the layer lives in a
+ * pinned, device-mapped host store; the layer keeps `num_slots` of them in a
+ * device slot tensor [num_slots, record] with a least-recently-used table.
+ * A decode call is:
+ *
+ *     moe_route_topk   -> ids[T,k], w[T,k]
+ *     moe_slot_ensure  -> slot_ids[T,k]    (LRU lookup, victim choice, id rewrite,
+ *                                           copy list and miss count in device memory)
+ *     moe_copy_misses  -> missing records copied from mapped host memory
+ *     moe_slot_ffn     -> y[T,H] (and optionally x + y)
+ *
+ * All four are asynchronous on the caller's stream, never synchronise the
+ * host and use launch shapes that depend only on the handle and T, so a
+ * whole decode step can be captured once in a HIP graph and replayed.
+ *
+ * Sources (cited by section):
+ *   xinfer-ai 0.14.6, docs/moe_offload.md (npm diff page on my.diffend.io):
+ *     "How it works" — Decode (per-layer LRU table on the GPU, least-recently-used
+ *     slots for misses, expert ids rewritten to slot ids, a second kernel copying
+ *     the missing experts from device-mapped pinned host memory, fixed launch
+ *     shapes with the miss count read from device memory, graph capture without
+ *     host sync), Prefill (whole-layer staging when a call touches more distinct
+ *     experts than slots), and the GEMM reading [num_slots, N, K] instead of
+ *     [num_experts, N, K]; "Supported" — every [E, ...] tensor (weights and scales)
+ *     in host RAM, unsupported inputs fail with a clear error; the opening
+ *     paragraph — placement never changes routing or precision.
+ *   FreeToken issue #677, "Proposal" — router lookahead, install of predicted
+ *     experts as low-priority slots (usage 0, first evicted), copy on a side
+ *     stream, every slot-map writer on the compute stream.
+ *
+ * Conventions
+ *   - Return value: 0 on success, a negative MOE_E* code on failure; the
+ *     message of the last failure on this host thread is moe_offload_last_error().
+ *     No call aborts or throws across the ABI.
+ *   - Errors found on the device (an expert id outside [0, E), a NaN router
+ *     logit, an audit failure) cannot be returned by asynchronous calls; they
+ *     set a sticky error word in the handle, reported by moe_offload_stats()
+ *     (which synchronises) and cleared by moe_offload_reset().  A call that
+ *     finds a bad id changes no slot state and writes an empty copy list.
+ *   - Pointers named `*_dev` or described as device pointers must be device
+ *     (or device-mapped) memory owned by the caller and valid until the work
+ *     queued on `stream` has finished.  `stream` is a hipStream_t passed as
+ *     void*; NULL means the null stream.
+ *   - One host thread at a time per handle.  Calls on one handle are ordered
+ *     by the caller's streams: the slot table has exactly one writer
+ *     (moe_slot_ensure, moe_prefill_stage, moe_prefetch_install), which must
+ *     all be issued on the same (compute) stream.
+ *
+ * Record layout (one expert, `record_bytes`, records `record_stride` apart):
+ *     gate [F][H] | up [F][H] | down [H][F] | (fp8 only) scales
+ *   rows are contiguous along the reduction dimension; elements are fp32,
+ *   bf16, or fp8 e4m3 (OCP "fn": bias 7, no infinities).  fp8 records end with
+ *   fp32 block scales, one per 128 x 128 block, row-major: gate [F/128][H/128],
+ *   up [F/128][H/128], down [H/128][F/128]; weight = decode(q) * scale.
+ *
+ * Record index ("slot id") space used by slot_ids:
+ *   r in [0, S)       slot r of the slot tensor
+ *   r in [S, S + E)   staging record r - S (expert r - S staged for this call)
+ */
+#ifndef MOE_OFFLOAD_H
+#define MOE_OFFLOAD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moe_offload moe_offload;
+
+/* weight/activation formats */
+enum moe_dtype {
+  MOE_F32 = 0,            /* fp32 weights, fp32 activations */
+  MOE_BF16 = 1,           /* bf16 weights, bf16 activations */
+  MOE_FP8_E4M3_B128 = 2   /* fp8 e4m3 weights + fp32 128x128 block scales, bf16 activations */
+};
+
+/* return codes */
+enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,        /* bad argument (shape, size, null pointer, S < k, ...) */
+  MOE_ENOMEM = -2,        /* device or pinned host allocation failed */
+  MOE_EHIP = -3,          /* a HIP runtime call failed */
+  MOE_EUNSUPPORTED = -4,  /* a dtype or shape this build does not handle */
+  MOE_EDEVICE = -5        /* a sticky device-side error is set (see stats.error) */
+};
+
+/* bits of moe_stats.error (sticky, device-side) */
+enum {
+  MOE_DEV_ERR_BAD_ID = 1,     /* a routed or predicted id outside [0, E) */
+  MOE_DEV_ERR_NAN = 2,        /* a NaN router logit (selection then treats it as -inf) */
+  MOE_DEV_ERR_AUDIT = 4,      /* audit mode: slot maps not mutually inverse, or a needed expert not resident */
+  MOE_DEV_ERR_TOO_MANY = 8    /* more (t, j) pairs than max_tokens * top_k */
+};
+
+/* creation flags */
+enum {
+  MOE_FLAG_AUDIT = 1,          /* check the slot table after every ensure/install (sets MOE_DEV_ERR_AUDIT) */
+  MOE_FLAG_HOST_COHERENT = 2   /* fine-grained (coherent) host store instead of coarse-grained */
+};
+
+typedef struct {
+  int32_t num_experts;   /* E, 1..1024 */
+  int32_t num_slots;     /* S, top_k <= S <= E ("at least one top-k decode step") */
+  int32_t hidden;        /* H, multiple of 64 for MOE_F32, of 128 otherwise */
+  int32_t ffn;           /* F, multiple of 64 for MOE_F32, of 128 otherwise */
+  int32_t top_k;         /* k, 1..16 */
+  int32_t dtype;         /* enum moe_dtype */
+  int32_t max_tokens;    /* largest T of any call, 1..65536 */
+  int32_t device;        /* HIP device ordinal */
+  uint32_t flags;        /* MOE_FLAG_* */
+  /* Optional sharing between the layers of one model (all calls of the
+   * sharing handles on one stream).  The owner must outlive every sharer.
+   *   share_host:    read this handle's host store instead of allocating one
+   *                  (same E, dtype, H, F).  Used when host RAM cannot hold
+   *                  every layer: layers then alias the same expert bytes.
+   *   share_staging: use this handle's staging buffer (same E, dtype, H, F). */
+  const moe_offload* share_host;
+  const moe_offload* share_staging;
+} moe_offload_desc;
+
+typedef struct {
+  uint64_t calls;             /* ensure + prefill-stage calls */
+  uint64_t hits;              /* distinct routed experts found resident (slot-mode calls) */
+  uint64_t misses;            /* demand misses: records copied into slots */
+  uint64_t staged_calls;      /* calls with more distinct experts than slots */
+  uint64_t staged_copies;     /* records copied into staging by those calls */
+  uint64_t prefetch_installs; /* experts installed by moe_prefetch_install */
+  uint64_t prefetch_hits;     /* installed experts found by a later ensure before any other use */
+  uint64_t bytes_copied;      /* bytes moved host -> device by this handle */
+  uint64_t tick;              /* LRU clock (ensure and stage calls) */
+  int32_t error;              /* sticky MOE_DEV_ERR_* bits */
+  int32_t resident;           /* experts currently resident in slots */
+} moe_stats;
+
+/* Device addresses and sizes of the handle's state, for inspection and tests.
+ * The arrays are owned by the handle; writing them is allowed only for
+ * fault-injection tests of the audit mode. */
+typedef struct {
+  int32_t* slot_of;       /* [E]  slot of each expert, -1 = not resident */
+  int32_t* expert_of;     /* [S]  expert in each slot, -1 = free */
+  uint64_t* last_use;     /* [S]  tick of last use; 0 = never used (free or prefetched) */
+  int32_t* copy_list;     /* [2 + 2*max(S,E)]  {mode, count, (expert, record index) x count} */
+  int32_t* prefetch_list; /* [2 + 2*S]         {0, count, (expert, slot) x count} */
+  void* slots;            /* device [S, record_stride] */
+  void* staging;          /* device [E, record_stride] */
+  void* host;             /* host store [E, record_stride] (host address) */
+  void* host_dev;         /* the same store as a device address */
+  size_t record_bytes;
+  size_t record_stride;
+  int32_t E, S, H, F, k, dtype, max_tokens, device;
+} moe_info;
+
+/* copy-list modes (copy_list[0]) */
+enum { MOE_MODE_SLOTS = 0, MOE_MODE_STAGED = 1, MOE_MODE_STAGED_ALL = 2 };
+
+/* Create one layer's handle: pinned mapped host store [E, record_stride]
+ * (contents undefined until the caller writes it), slot tensor, slot table
+ * (empty cache, tick 0), copy lists, staging buffer [E, record_stride],
+ * workspaces and counters.  Later calls never allocate.
+ * Errors: MOE_EINVAL (shape/limits), MOE_EUNSUPPORTED (dtype), MOE_ENOMEM, MOE_EHIP. */
+int moe_offload_create(const moe_offload_desc* desc, moe_offload** out);
+
+/* Synchronise the device, free everything the handle owns.  Null-safe. */
+void moe_offload_destroy(moe_offload* h);
+
+/* The host store, so the caller can write expert records in place
+ * (record e at host + e * record_stride).  Host address; pinned, mapped. */
+int moe_offload_host_records(moe_offload* h, void** host, size_t* record_stride, size_t* record_bytes);
+
+/* Router: logits l = x Wr^T + b (binary32, one fixed summation order: chunks
+ * of 8 elements, 64 lanes each owning every 64th chunk, an FMA chain per lane,
+ * an xor-butterfly over the lanes, then + b), top-k by (logit descending, id
+ * ascending), weights = softmax over the k chosen logits.
+ *   x:        device [T, H], fp32 (MOE_F32) or bf16
+ *   w_router: device [E, H], fp32 (MOE_F32) or bf16
+ *   bias:     device [E] fp32
+ *   ids:      device [T, k] int32 (out);  w: device [T, k] fp32 (out)
+ * 1 <= T <= max_tokens.  Asynchronous, capture-safe. */
+int moe_route_topk(moe_offload* h, const void* x, const void* w_router, const float* bias, int32_t T,
+                   int32_t* ids, float* w, void* stream);
+
+/* LRU slot table update for one call (single workgroup, fixed shape):
+ * D = distinct ids.  |D| <= S: misses (ascending id) take the free slots,
+ * then the least recently used (ties to the lower slot) among slots not
+ * holding an expert of D; ids are rewritten to slot ids; the copy list is
+ * {SLOTS, |misses|, (expert, slot)...}.  |D| > S: the table is left as is,
+ * resident experts are read in place, each missing expert e is staged and
+ * rewritten to S + e; copy list {STAGED, n, (e, S + e)...}.
+ *   ids: device [T, k] int32;  slot_ids: device [T, k] int32 (out).
+ * Asynchronous, capture-safe; the table's only writer besides install/stage. */
+int moe_slot_ensure(moe_offload* h, const int32_t* ids, int32_t T, int32_t* slot_ids, void* stream);
+
+/* Copy the current copy list's records from the mapped host store into slots
+ * or staging with 16-byte loads (fixed grid; the count is read on the device,
+ * an empty list costs one empty launch).  No-op for MOE_MODE_STAGED_ALL.
+ * Asynchronous, capture-safe. */
+int moe_copy_misses(moe_offload* h, void* stream);
+
+/* Expert FFN and combine over the slot tensor:
+ *   y_t = sum_j w[t][j] * Wd_r silu(Wg_r x_t) * (Wu_r x_t)   (j = 0..k-1 in order)
+ *         + the same FFN of shared_record on x_t (weight 1) if shared_record != NULL,
+ *   r = slot_ids[t][j] (slot or staging record), rounded once to the activation dtype.
+ *   x: device [T, H]; slot_ids: device [T, k]; w: device [T, k] fp32;
+ *   shared_record: NULL or a device record (same layout/dtype, caller-owned, always resident);
+ *   y: device [T, H] (out);  x_next: NULL or device [T, H] (out) = round(x + y).
+ * Results do not depend on which slot holds an expert or on S.
+ * Asynchronous, capture-safe. */
+int moe_slot_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int32_t T,
+                 const void* shared_record, void* y, void* x_next, void* stream);
+
+/* Prefill entry (host-synchronising, not capturable): count the distinct ids
+ * of the call.  More than S: copy the whole layer host -> staging with an
+ * asynchronous DMA copy, rewrite ids to S + id, copy list {STAGED_ALL, E, ...},
+ * slot table untouched (tick advances), *staged_out = 1.  Otherwise run
+ * moe_slot_ensure + moe_copy_misses, *staged_out = 0.
+ *   ids: device [T, k]; slot_ids: device [T, k] (out); staged_out: host int32 (may be NULL).
+ * Returns MOE_EDEVICE (nothing queued) if an id is out of range. */
+int moe_prefill_stage(moe_offload* h, const int32_t* ids, int32_t T, int32_t* slot_ids, int32_t* staged_out,
+                      void* stream);
+
+/* Router-lookahead prefetch, install half (FreeToken #677 "Install"): for
+ * the predicted ids of the *next* layer (this handle), take up to max_n
+ * predicted experts that are not resident, ordered by (number of tokens
+ * predicting them desc, best top-k position asc, id asc), and place them in
+ * victim slots (same order as ensure, never a slot holding a predicted
+ * expert) with last_use = 0, i.e. evicted first.  Writes the prefetch copy
+ * list.  Must be issued on the compute stream (single slot-table writer).
+ *   pred_ids: device [T, k] int32.  0 <= max_n <= S. */
+int moe_prefetch_install(moe_offload* h, const int32_t* pred_ids, int32_t T, int32_t max_n, void* stream);
+
+/* Copy the prefetch copy list's records (may run on a side stream after an
+ * event that follows the install; the demand copy of this layer must wait
+ * for it). */
+int moe_copy_prefetch(moe_offload* h, void* stream);
+
+/* Synchronise the device and read the counters and the sticky error word. */
+int moe_offload_stats(moe_offload* h, moe_stats* out);
+
+/* Empty the cache (all slots free, tick 0), zero the counters and the
+ * sticky error word, on `stream`. */
+int moe_offload_reset(moe_offload* h, void* stream);
+
+/* Fill `out` with the device addresses and sizes of the handle's state. */
+int moe_offload_query(const moe_offload* h, moe_info* out);
+
+/* Message of the last failing call on this host thread ("" if none). */
+const char* moe_offload_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_OFFLOAD_H */

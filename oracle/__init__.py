@@ -299,7 +299,7 @@ class Layer:
         else:
             slot_ids, mode, pairs = self.cache.ensure(ids)
         self.cache.copy(mode, pairs)
-        y = None
+        y = y64 = None
         if compute_ffn:
-            y = ffn(x, self.wdt, self.H, self.F, self.cache.records(slot_ids), w, self.shared)
-        return dict(ids=ids, w=w, slot_ids=slot_ids, mode=mode, pairs=pairs, y=y)
+            y, y64 = ffn(x, self.wdt, self.H, self.F, self.cache.records(slot_ids), w, self.shared, want_f64=True)
+        return dict(ids=ids, w=w, slot_ids=slot_ids, mode=mode, pairs=pairs, y=y, y64=y64)

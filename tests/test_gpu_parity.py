@@ -1,0 +1,261 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bit-exact: router ids, slot ids, copy lists, slot tables, slot bytes.
+Within tolerance: routing weights (1e-5) and layer outputs (per token row,
+||y - ref||_inf <= tol * ||ref||_inf with tol 1e-5 for fp32 and 2e-2 for
+bf16/fp8; ref = the oracle's double sums).
+Sizes span several MFMA tiles, ragged token counts, staging, and more than
+one 64-token pass per expert.
+"""
+import numpy as np
+import pytest
+import torch
+
+import expert_offload_slot_amd as m
+import oracle
+import synth
+from gpu_harness import (GpuLayer, compare_call, d2h, h2d, make_layer_inputs, row_rel_err, to_dev, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_sequence(E, S, k, H, F, wdt, zipf, seed, steps, Ts, shared=False, flags=m.FLAG_AUDIT):
+    print("case E=%d S=%d k=%d H=%d F=%d wdt=%d zipf=%s seed=%d Ts=%s shared=%s" %
+          (E, S, k, H, F, wdt, zipf, seed, Ts, shared), flush=True)
+    host, wr, b, sh = make_layer_inputs(seed, 0, E, H, F, wdt, zipf, shared)
+    maxT = max(Ts)
+    gl = GpuLayer(E, S, k, H, F, wdt, maxT, host, wr, b, flags=flags, shared=sh)
+    ol = oracle.Layer(E, S, k, H, F, wdt, host, wr, b, shared=sh)
+    xs = synth.tokens(seed, 7, maxT, H, steps, 0.0, wdt)
+    modes, errs = [], []
+    try:
+        for s in range(steps):
+            T = Ts[s % len(Ts)]
+            x = np.ascontiguousarray(xs[s][:T])
+            xd = to_dev(x)
+            gl.step(xd, T)
+            r = ol.step(x)
+            errs.append(compare_call(gl, r, T, r["y64"], oracle_cache=ol.cache))
+            modes.append(r["mode"])
+            # residual output: round(x + y) from the GPU's own y
+            xn = to_np(gl.xn[:T])
+            assert np.array_equal(xn, oracle.residual(x, to_np(gl.y[:T]), wdt))
+        st = gl.stats()
+        c = ol.cache.counters()
+        assert st["error"] == 0
+        for key in ("calls", "hits", "misses", "staged_calls", "staged_copies"):
+            assert st[key] == c[key], key
+        # every resident slot holds its expert's host bytes
+        so, eo, lu = gl.table()
+        rb = oracle.record_bytes(wdt, H, F)
+        for s_ in range(S):
+            if eo[s_] >= 0:
+                assert np.array_equal(gl.slot_bytes(s_, rb), host[eo[s_], :rb])
+    finally:
+        gl.close()
+    return modes, max(errs)
+
+
+def test_c1_tiny_fp32_config():
+    # 8 experts, top-2, hidden 64, ffn 128, 4 slots, 32 steps of batch 4, Zipf(1.2)-ranked bias
+    for seed in range(4):
+        run_sequence(8, 4, 2, 64, 128, 0, 1.2, seed, 32, [4])
+
+
+@pytest.mark.parametrize("S", [2, 3, 4, 8])
+def test_c1_variants_slots_and_batches(S):
+    modes, _ = run_sequence(8, S, 2, 64, 128, 0, 0.0, 11 + S, 24, [1, 2, 4, 8])
+    if S < 8:
+        assert 1 in modes and 0 in modes  # both slot calls and staged calls ran
+
+
+@pytest.mark.parametrize("S,zipf", [(4, 0.0), (6, 1.2), (16, 0.0)])
+def test_bf16_multi_tile(S, zipf):
+    run_sequence(16, S, 4, 256, 384, 1, zipf, 21, 20, [1, 3, 8, 17])
+
+
+def test_bf16_many_tokens_per_expert():
+    # > 64 tokens on an expert: several passes over each weight tile
+    run_sequence(8, 8, 2, 128, 256, 1, 1.2, 5, 4, [300, 77])
+
+
+@pytest.mark.parametrize("S", [4, 12])
+def test_fp8_block_scaled_with_shared_expert(S):
+    # 256 x 384 fp8 records are 294,984 bytes: not a multiple of 16 (the scales sit in the tail)
+    run_sequence(12, S, 3, 256, 384, 2, 0.0, 31, 12, [1, 5, 16], shared=True)
+
+
+def test_fp8_without_shared_expert():
+    run_sequence(10, 5, 2, 128, 256, 2, 1.2, 32, 10, [2, 7])
+
+
+def test_placement_invariance_bitwise():
+    """The same token stream at every slot count (slot calls, decode staging) and
+    with whole-layer staging on every overflowing call: identical y bits."""
+    E, k, H, F, wdt = 16, 4, 256, 256, 1
+    host, wr, b, _ = make_layer_inputs(41, 0, E, H, F, wdt, 0.0)
+    xs = synth.tokens(41, 3, 8, H, 12, 0.0, wdt)
+    outs = {}
+    staged_seen = set()
+    for S in [4, 5, 9, 16, "prefill"]:
+        gl = GpuLayer(E, 4 if S == "prefill" else S, k, H, F, wdt, 8, host, wr, b)
+        ys = []
+        for s in range(12):
+            T = [1, 8, 3, 5][s % 4]
+            xd = to_dev(np.ascontiguousarray(xs[s][:T]))
+            gl.route(xd, T)
+            if S == "prefill":
+                staged_seen.add(m.moe_prefill_stage(gl.h, gl.ids, T, gl.slot_ids, torch.cuda.current_stream()))
+            else:
+                gl.ensure(T)
+                gl.copy()
+                staged_seen.add(("mode", gl.copy_list()[0]))
+            gl.ffn(xd, T)
+            ys.append(to_np(gl.y[:T]).copy())
+        outs[S] = ys
+        gl.close()
+    assert {0, 1} <= staged_seen and ("mode", 0) in staged_seen and ("mode", 1) in staged_seen
+    for S in outs:
+        for a, b_ in zip(outs[S], outs[4]):
+            assert np.array_equal(a, b_), S
+
+
+def test_prefill_whole_layer_staging():
+    E, S, k, H, F, wdt = 16, 4, 4, 256, 256, 1
+    host, wr, b, _ = make_layer_inputs(51, 0, E, H, F, wdt, 0.0)
+    T = 40
+    gl = GpuLayer(E, S, k, H, F, wdt, T, host, wr, b)
+    ol = oracle.Layer(E, S, k, H, F, wdt, host, wr, b)
+    try:
+        x = synth.tokens(51, 1, T, H, 1, 0.0, wdt)[0]
+        xd = to_dev(x)
+        gl.route(xd, T)
+        staged = m.moe_prefill_stage(gl.h, gl.ids, T, gl.slot_ids)
+        assert staged == 1
+        gl.ffn(xd, T)
+        r = ol.step(x, stage_all=True)
+        compare_call(gl, r, T, r["y64"], oracle_cache=ol.cache)
+        for e in range(E):
+            assert np.array_equal(gl.staging_bytes(e, host.shape[1]), host[e])
+        # a small call afterwards takes the slot path
+        x1 = synth.tokens(51, 2, 1, H, 1, 0.0, wdt)[0]
+        x1d = to_dev(x1)
+        gl.route(x1d, 1)
+        assert m.moe_prefill_stage(gl.h, gl.ids, 1, gl.slot_ids) == 0
+        gl.ffn(x1d, 1)
+        r = ol.step(x1)
+        compare_call(gl, r, 1, r["y64"], oracle_cache=ol.cache)
+    finally:
+        gl.close()
+
+
+def test_bad_id_is_a_noop_with_sticky_error():
+    E, S, k, H, F = 8, 4, 2, 128, 128
+    host, wr, b, _ = make_layer_inputs(61, 0, E, H, F, 1, 1.2)
+    gl = GpuLayer(E, S, k, H, F, 1, 4, host, wr, b)
+    try:
+        x = to_dev(synth.tokens(61, 1, 2, H, 1, 0.0, 1)[0])
+        gl.step(x, 2)
+        before = gl.table()
+        bad = torch.tensor([[1, 2], [3, E]], dtype=torch.int32, device="cuda")
+        m.moe_slot_ensure(gl.h, bad, 2, gl.slot_ids)
+        gl.copy()
+        after = gl.table()
+        assert all(np.array_equal(p, q) for p, q in zip(before, after))
+        assert gl.copy_list()[1].shape[0] == 0
+        st = gl.stats()
+        assert st["error"] & m.DEV_ERR_BAD_ID
+        with pytest.raises(m.MoeError):
+            m.moe_prefill_stage(gl.h, bad, 2, gl.slot_ids)
+        m.moe_offload_reset(gl.h)
+        assert gl.stats()["error"] == 0 and gl.stats()["tick"] == 0
+    finally:
+        gl.close()
+
+
+def test_nan_logit_sets_error():
+    E, S, k, H, F = 8, 4, 2, 128, 128
+    host, wr, b, _ = make_layer_inputs(62, 0, E, H, F, 1, 1.2)
+    gl = GpuLayer(E, S, k, H, F, 1, 4, host, wr, b)
+    try:
+        x = synth.tokens(62, 1, 1, H, 1, 0.0, 1)[0].copy()
+        x[0, 5] = 0x7FC0
+        gl.route(to_dev(x), 1)
+        assert gl.stats()["error"] & m.DEV_ERR_NAN
+    finally:
+        gl.close()
+
+
+def test_audit_flags_a_corrupted_table():
+    E, S, k, H, F = 8, 4, 2, 128, 128
+    host, wr, b, _ = make_layer_inputs(63, 0, E, H, F, 1, 1.2)
+    gl = GpuLayer(E, S, k, H, F, 1, 4, host, wr, b)
+    try:
+        x = to_dev(synth.tokens(63, 1, 2, H, 1, 0.0, 1)[0])
+        gl.step(x, 2)
+        assert gl.stats()["error"] == 0
+        so, eo, lu = gl.table()
+        e = int(eo[0])
+        bad = so.copy()
+        bad[e] = 1 if so[e] != 1 else 2  # expert points at a slot that does not hold it
+        h2d(gl.info["slot_of"], bad)
+        gl.step(x, 2)
+        assert gl.stats()["error"] & m.DEV_ERR_AUDIT
+    finally:
+        gl.close()
+
+
+def test_create_rejects_bad_shapes():
+    with pytest.raises(m.MoeError) as ei:
+        m.moe_offload_create(8, 1, 128, 128, 2, 1, 4)  # S < k
+    assert ei.value.code == m.EINVAL
+    with pytest.raises(m.MoeError) as ei:
+        m.moe_offload_create(8, 4, 128, 128, 2, 7, 4)  # unknown dtype
+    assert ei.value.code == m.EUNSUPPORTED
+    with pytest.raises(m.MoeError) as ei:
+        m.moe_offload_create(8, 4, 100, 128, 2, 1, 4)  # hidden not a multiple of 128
+    assert ei.value.code == m.EUNSUPPORTED
+    with pytest.raises(m.MoeError) as ei:
+        m.moe_offload_create(8, 4, 128, 128, 2, 1, 4, device=99)
+    assert ei.value.code == m.EINVAL
+
+
+def test_graph_replay_matches_eager():
+    """Two layers captured once in a HIP graph (via torch.cuda.graph) and replayed."""
+    E, S, k, H, F, wdt, T = 16, 6, 4, 256, 256, 1, 3
+    L = 2
+    ins = [make_layer_inputs(71, l, E, H, F, wdt, 1.2) for l in range(L)]
+    xs = synth.tokens(71, 4, T, H, 6, 0.9, wdt)
+
+    def build():
+        return [GpuLayer(E, S, k, H, F, wdt, T, *ins[l][:3]) for l in range(L)]
+
+    def step(layers, x0):
+        x = x0
+        for gl in layers:
+            gl.step(x, T)
+            x = gl.xn
+        return x
+
+    eager = build()
+    ref = []
+    for s in range(6):
+        xo = step(eager, to_dev(xs[s]))
+        ref.append((to_np(xo[:T]).copy(), [gl.table() for gl in eager]))
+    graphed = build()
+    x_static = to_dev(xs[0])
+    # warm-up on a side stream is not needed: nothing here allocates
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        out = step(graphed, x_static)
+    # the capture did not execute: state is still empty
+    for s in range(6):
+        x_static.copy_(to_dev(xs[s]))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(out[:T]), ref[s][0]), s
+        for gl, tab in zip(graphed, ref[s][1]):
+            assert all(np.array_equal(p, q) for p, q in zip(gl.table(), tab))
+    for gl in eager + graphed:
+        gl.close()
