@@ -50,8 +50,14 @@ class Info(ctypes.Structure):
     _fields_ = [("slot_of", ctypes.c_void_p), ("expert_of", ctypes.c_void_p), ("last_use", ctypes.c_void_p),
                 ("copy_list", ctypes.c_void_p), ("prefetch_list", ctypes.c_void_p), ("slots", ctypes.c_void_p),
                 ("staging", ctypes.c_void_p), ("host", ctypes.c_void_p), ("host_dev", ctypes.c_void_p),
+                ("ffn_h", ctypes.c_void_p), ("ffn_part", ctypes.c_void_p), ("ffn_groups", ctypes.c_void_p),
                 ("record_bytes", ctypes.c_size_t), ("record_stride", ctypes.c_size_t)] + \
                [(n, ctypes.c_int32) for n in ("E", "S", "H", "F", "k", "dtype", "max_tokens", "device")]
+
+
+class ChainBuffers(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("x", "xn", "y", "ids", "w", "slot_ids", "pred")] + \
+               [("act_bytes", ctypes.c_size_t)]
 
 
 _lib = None
@@ -72,7 +78,8 @@ def lib():
             "moe_route_topk": ([vp, vp, vp, vp, i32, vp, vp, vp], i32),
             "moe_slot_ensure": ([vp, vp, i32, vp, vp], i32),
             "moe_copy_misses": ([vp, vp], i32),
-            "moe_slot_ffn": ([vp, vp, vp, vp, i32, vp, vp, vp, vp], i32),
+            "moe_slot_ffn": ([vp, vp, vp, vp, i32, vp, vp, vp, vp, vp], i32),
+            "moe_rmsnorm": ([vp, vp, i32, i32, i32, ctypes.c_float, vp], i32),
             "moe_prefill_stage": ([vp, vp, i32, vp, P(ctypes.c_int32), vp], i32),
             "moe_prefetch_install": ([vp, vp, i32, i32, vp], i32),
             "moe_copy_prefetch": ([vp, vp], i32),
@@ -80,6 +87,11 @@ def lib():
             "moe_offload_reset": ([vp, vp], i32),
             "moe_offload_query": ([vp, P(Info)], i32),
             "moe_offload_last_error": ([], ctypes.c_char_p),
+            "moe_chain_create": ([P(vp), i32, P(vp), P(vp), P(vp), i32, i32, P(vp)], i32),
+            "moe_chain_get_buffers": ([vp, P(ChainBuffers)], i32),
+            "moe_chain_run": ([vp, vp], i32),
+            "moe_chain_run_eager": ([vp, vp], i32),
+            "moe_chain_destroy": ([vp], None),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -154,9 +166,16 @@ def moe_copy_misses(h, stream=None):
     return _check(lib().moe_copy_misses(h, _stream(stream)))
 
 
-def moe_slot_ffn(h, x, slot_ids, w, T, shared_record, y, x_next=None, stream=None):
+def moe_slot_ffn(h, x, slot_ids, w, T, shared_record, y, residual=None, x_next=None, stream=None):
     return _check(lib().moe_slot_ffn(h, _addr(x), _addr(slot_ids), _addr(w), T, _addr(shared_record), _addr(y),
-                                     _addr(x_next), _stream(stream)))
+                                     _addr(residual), _addr(x_next), _stream(stream)))
+
+
+RMS_EPS = 1e-6
+
+
+def moe_rmsnorm(x, out, T, H, dtype, eps=RMS_EPS, stream=None):
+    return _check(lib().moe_rmsnorm(_addr(x), _addr(out), T, H, dtype, eps, _stream(stream)))
 
 
 def moe_prefill_stage(h, ids, T, slot_ids, stream=None):
@@ -195,3 +214,31 @@ def host_array(h, E):
     p, stride, _ = moe_offload_host_records(h)
     buf = (ctypes.c_uint8 * (E * stride)).from_address(p)
     return np.frombuffer(buf, dtype=np.uint8).reshape(E, stride)
+
+
+def moe_chain_create(layers, w_router, bias, T, prefetch_n=0, shared_records=None):
+    """layers: handles; w_router, bias, shared_records: per-layer tensors/addresses (shared entries may be None)."""
+    L = len(layers)
+    arr = lambda xs: (ctypes.c_void_p * L)(*[_addr(v) for v in xs])
+    out = ctypes.c_void_p()
+    sh = arr(shared_records) if shared_records is not None else None
+    _check(lib().moe_chain_create(arr(layers), L, arr(w_router), arr(bias), sh, T, prefetch_n, ctypes.byref(out)))
+    return out.value
+
+
+def moe_chain_get_buffers(c):
+    b = ChainBuffers()
+    _check(lib().moe_chain_get_buffers(c, ctypes.byref(b)))
+    return {n: getattr(b, n) for n, _ in ChainBuffers._fields_}
+
+
+def moe_chain_run(c, stream=None):
+    return _check(lib().moe_chain_run(c, _stream(stream)))
+
+
+def moe_chain_run_eager(c, stream=None):
+    return _check(lib().moe_chain_run_eager(c, _stream(stream)))
+
+
+def moe_chain_destroy(c):
+    lib().moe_chain_destroy(c)

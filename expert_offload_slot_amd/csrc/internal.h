@@ -17,7 +17,8 @@ constexpr int kCopyUnroll = 4;      // 16-byte loads in flight per thread
 constexpr int kRouteTokens = 4;     // tokens per router wave
 constexpr int kTile = 16;           // MFMA output rows per work item
 constexpr int kChunk = 128;         // K elements per MFMA group (4 x 32)
-constexpr int kTokGroup = 64;       // tokens per pass over a weight tile (4 MFMA column groups)
+constexpr int kTokGroup = 32;       // tokens per pass over a weight tile (MFMA column groups of 16)
+constexpr int kNG = kTokGroup / 16; // column groups per pass
 constexpr int kF32Rows = 64;        // rows per work item on the fp32 path
 
 // counters[] layout (device, uint64)
@@ -37,13 +38,20 @@ struct CacheDev {
   uint64_t record_bytes;
 };
 
-// FFN group descriptor offsets (int32 words) inside the FFN workspace
+// FFN group descriptor (int32 words) inside the FFN workspace:
+//   [0]                      number of distinct records nr
+//   record block r (32 words, 128-byte aligned) at kRecWords * (1 + r):
+//     [0] record index, [1] token count n, [2] offset of its pair ids in the
+//     pair array, [3 .. 3 + kInline) its first kInline pair ids (t*k + j)
+//   pair array at kRecWords * (1 + max_recs): all pair ids grouped by record
+// so a work item gets its record and (usually all) its tokens in one load trip.
+constexpr int kRecWords = 32;
+constexpr int kInline = kRecWords - 3;
 struct GroupLayout {
   int max_recs;   // distinct records a call can touch
   int max_pairs;  // max_tokens * k
-  int off_list() const { return 2; }
-  int off_start() const { return 2 + max_recs; }
-  int off_pairs() const { return 2 + max_recs + max_recs + 1; }
+  int off_rec(int r) const { return kRecWords * (1 + r); }
+  int off_pairs() const { return kRecWords * (1 + max_recs); }
   int words() const { return off_pairs() + max_pairs; }
 };
 
@@ -64,17 +72,18 @@ struct moe_offload {
   void* state_block;   // one allocation holding everything below
   moe::CacheDev cache;
   float* logits;       // [max_tokens, E]
-  uint32_t* route_ctr; // [ceil(max_tokens / kRouteTokens)]
   int32_t* grp;        // FFN group descriptor
   moe::GroupLayout gl;
   void* hbuf;          // [max_pairs + max_tokens, F] bf16 (fp32 for MOE_F32)
   float* part;         // [max_pairs + max_tokens, H] fp32 partial expert outputs
-  uint32_t* comb_ctr;  // [H / 16] combine counters
   int32_t* scratch_i32;      // small device scratch (distinct count etc.)
   int32_t* pinned_i32;       // small pinned host scratch
 };
 
 namespace moe {
+
+// records the message returned by moe_offload_last_error() on this thread; returns code
+int set_error(int code, const char* msg);
 
 // launchers (return hipError_t of the launch)
 hipError_t launch_reset(moe_offload* h, hipStream_t s);
@@ -85,7 +94,10 @@ hipError_t launch_install(moe_offload* h, const int32_t* pred, int T, int max_n,
 hipError_t launch_copy(moe_offload* h, const int32_t* list, hipStream_t s);
 hipError_t launch_distinct(moe_offload* h, const int32_t* ids, int n, int32_t* out_dev, hipStream_t s);
 hipError_t launch_stage_all(moe_offload* h, const int32_t* ids, int n, int32_t* slot_ids, hipStream_t s);
+// xn_next (optional, needs x_next): rmsnorm(x_next) with eps, for the next layer of a chain
 hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int T,
-                      const void* shared, void* y, void* x_next, hipStream_t s);
+                      const void* shared, void* y, const void* residual, void* x_next, void* xn_next, float eps,
+                      hipStream_t s);
+hipError_t launch_rmsnorm(const void* x, void* out, int T, int H, int dtype, float eps, hipStream_t s);
 
 }  // namespace moe

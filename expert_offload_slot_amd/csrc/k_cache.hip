@@ -335,16 +335,14 @@ __global__ void k_stage_all(CacheDev c, const int32_t* __restrict__ ids, int n, 
   }
 }
 
-// empty cache, zero counters and error, empty lists, zero self-resetting counters
-__global__ void k_reset(CacheDev c, uint32_t* route_ctr, int n_route, uint32_t* comb_ctr, int n_comb) {
+// empty cache, zero counters and error, empty lists
+__global__ void k_reset(CacheDev c) {
   const int i0 = blockIdx.x * blockDim.x + threadIdx.x, step = gridDim.x * blockDim.x;
   for (int e = i0; e < c.E; e += step) c.slot_of[e] = -1;
   for (int s = i0; s < c.S; s += step) {
     c.expert_of[s] = -1;
     c.last_use[s] = 0;
   }
-  for (int i = i0; i < n_route; i += step) route_ctr[i] = 0;
-  for (int i = i0; i < n_comb; i += step) comb_ctr[i] = 0;
   for (int i = i0; i < C_N; i += step) c.counters[i] = 0;
   if (i0 == 0) {
     *c.tick = 0;
@@ -421,8 +419,7 @@ hipError_t launch_stage_all(moe_offload* h, const int32_t* ids, int n, int32_t* 
 }
 
 hipError_t launch_reset(moe_offload* h, hipStream_t s) {
-  const int n_route = (h->max_tokens + kRouteTokens - 1) / kRouteTokens;
-  hipLaunchKernelGGL(k_reset, dim3(16), dim3(256), 0, s, h->cache, h->route_ctr, n_route, h->comb_ctr, h->H / 16);
+  hipLaunchKernelGGL(k_reset, dim3(16), dim3(256), 0, s, h->cache);
   return hipGetLastError();
 }
 

@@ -5,17 +5,18 @@
 // changes precision.  Per (token t, choice j) with record r = slot_ids[t][j]:
 //     h = silu(Wg x_t) * (Wu x_t),  o = Wd h,  y_t = sum_j w[t][j] o  (+ shared expert)
 //
-// Kernels (one launch each, fixed grids):
+// Kernels (one launch each, fixed grids, no communication between workgroups):
 //   k_group    one workgroup: counting sort of the T*k (t, j) pairs by record
-//              index -> list of distinct records, their token lists.
+//              index -> distinct records, each with its token list (the first
+//              kInline pair ids inline, so one load trip serves a work item).
 //   k_gateup   work item = (record, 16 rows of F): gate and up rows streamed
-//              once, bf16 MFMA 16x16x32 against up to 64 gathered tokens per
-//              pass, K split over the 4 wavefronts of the workgroup and reduced
-//              through LDS in a fixed order, SiLU * up fused, h stored in bf16.
-//   k_down     work item = (record, 16 rows of H): down rows against h, fp32
-//              partial outputs per (t, j).  The last work item of each 16-row
-//              tile to finish (device-scope counter) combines that tile for
-//              all tokens in j order, rounds to bf16, and adds the residual.
+//              once, bf16 MFMA 16x16x32 against up to 32 gathered tokens per
+//              pass, K split over the workgroup's wavefronts and reduced in
+//              LDS in wavefront order, SiLU * up fused, h stored in bf16.
+//   k_down     work item = (record, 16 rows of H): down rows against h; fp32
+//              partial outputs per (t, j) go to the workspace.
+//   k_combine  one workgroup per token: sum over j in order (+ shared), round,
+//              residual add, and optionally the next block's RMS norm.
 // fp8 records: e4m3 codes are widened exactly to bf16 by the hardware pair
 // converter and each 128-wide K block is scaled on the fp32 accumulator.
 // fp32 records use plain fp32 FMA kernels with the same structure.
@@ -27,12 +28,12 @@
 #include <algorithm>
 
 #include "internal.h"
+#include "rownorm.h"
 
 namespace moe {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct FfnArgs {
@@ -46,29 +47,21 @@ struct FfnArgs {
   int32_t* grp;
   void* hbuf;
   float* part;
-  uint32_t* comb_ctr;
   void* y;
+  const void* residual;  // stream the output is added to (x if none given)
   void* x_next;
   int32_t* err;
   int T, k, H, F, S, E;
-  int off_list, off_start, off_pairs;
+  int off_pairs;
 };
 
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu)) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)rn_to_bf16(f); }
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 // ------------------------------------------------------------------ grouping
 constexpr int kGrpBlock = 1024;
 
-// inclusive scan of v over the 1024 threads; returns exclusive prefix, *total = sum
+// exclusive prefix of v over the 1024 threads; *total = sum
 __device__ __forceinline__ int block_excl_sum(int v, int* s_wave, int* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   int inc = v;
@@ -94,6 +87,7 @@ __device__ __forceinline__ int block_excl_sum(int v, int* s_wave, int* total) {
 __global__ __launch_bounds__(kGrpBlock) void k_group(FfnArgs a) {
   __shared__ int cnt[2 * kMaxExperts];
   __shared__ int cur[2 * kMaxExperts];
+  __shared__ int rank_of[2 * kMaxExperts];
   __shared__ int wave[kGrpBlock / 64];
   const int tid = threadIdx.x;
   const int n = a.T * a.k, nb = a.S + a.E;
@@ -112,57 +106,70 @@ __global__ __launch_bounds__(kGrpBlock) void k_group(FfnArgs a) {
   int tot_pairs, nr;
   const int pre = block_excl_sum(c0 + c1, wave, &tot_pairs);
   const int pre_nz = block_excl_sum((c0 > 0) + (c1 > 0), wave, &nr);
-  int32_t* list = a.grp + a.off_list;
-  int32_t* start = a.grp + a.off_start;
   int32_t* pairs = a.grp + a.off_pairs;
   cur[2 * tid] = pre;
   cur[2 * tid + 1] = pre + c0;
+  rank_of[2 * tid] = pre_nz;
+  rank_of[2 * tid + 1] = pre_nz + (c0 > 0);
   if (c0 > 0) {
-    list[pre_nz] = 2 * tid;
-    start[pre_nz] = pre;
+    int32_t* blk = a.grp + kRecWords * (1 + pre_nz);
+    blk[0] = 2 * tid;
+    blk[1] = c0;
+    blk[2] = pre;
   }
   if (c1 > 0) {
-    list[pre_nz + (c0 > 0)] = 2 * tid + 1;
-    start[pre_nz + (c0 > 0)] = pre + c0;
+    int32_t* blk = a.grp + kRecWords * (1 + pre_nz + (c0 > 0));
+    blk[0] = 2 * tid + 1;
+    blk[1] = c1;
+    blk[2] = pre + c0;
   }
-  if (tid == 0) {
-    start[nr] = n;
-    a.grp[0] = nr;
-  }
+  if (tid == 0) a.grp[0] = nr;
   __syncthreads();
   for (int i = tid; i < n; i += kGrpBlock) {
     int r = a.slot_ids[i];
     if ((unsigned)r >= (unsigned)nb) r = 0;
     pairs[atomicAdd(&cur[r], 1)] = i;
   }
+  __syncthreads();
+  // inline copies of the first kInline pair ids of every record
+  for (int b = tid; b < nb; b += kGrpBlock) {
+    const int c = cnt[b];
+    if (c == 0) continue;
+    int32_t* blk = a.grp + kRecWords * (1 + rank_of[b]);
+    const int start = cur[b] - c;  // the cursor ended at start + c
+    for (int q = 0; q < c && q < kInline; ++q) blk[3 + q] = pairs[start + q];
+  }
 }
 
-// work item -> record bytes and its token list
+// A work item's record (pointer, token count); its pair ids come from the same
+// 128-byte record block, so one load trip serves the item.
 struct Item {
   const uint8_t* rec;
-  const int32_t* plist;  // pair ids (t*k + j); null for the shared expert
-  int n;                 // number of tokens
+  int n;    // tokens of the item
+  bool sh;  // the always-resident shared expert
 };
 
 __device__ __forceinline__ Item item_record(const FfnArgs& a, int nr, int r) {
   Item it;
   if (r < nr) {
-    const int ri = a.grp[a.off_list + r];
+    const int32_t* blk = a.grp + kRecWords * (1 + r);
+    const int ri = blk[0];
     it.rec = ri < a.S ? a.slots + (uint64_t)ri * a.stride : a.staging + (uint64_t)(ri - a.S) * a.stride;
-    const int s0 = a.grp[a.off_start + r];
-    it.n = a.grp[a.off_start + r + 1] - s0;
-    it.plist = a.grp + a.off_pairs + s0;
+    it.n = blk[1];
+    it.sh = false;
   } else {
     it.rec = a.shared;
     it.n = a.T;
-    it.plist = nullptr;
+    it.sh = true;
   }
   return it;
 }
 
-// pair id (row of h / part) and token of entry idx of an item
-__device__ __forceinline__ int item_pair(const FfnArgs& a, const Item& it, int idx) {
-  return it.plist ? it.plist[idx] : a.T * a.k + idx;
+// pair id (row of h / part) of entry idx of record r
+__device__ __forceinline__ int item_pair(const FfnArgs& a, const Item& it, int r, int idx) {
+  if (it.sh) return a.T * a.k + idx;
+  const int32_t* blk = a.grp + kRecWords * (1 + r);
+  return idx < kInline ? blk[3 + idx] : a.grp[a.off_pairs + blk[2] + idx];
 }
 __device__ __forceinline__ int pair_token(const FfnArgs& a, int p) {
   const int routed = a.T * a.k;
@@ -227,74 +234,99 @@ __device__ __forceinline__ f32x4 fma4(float s, f32x4 v, f32x4 acc) {
   return r;
 }
 
-// ------------------------------------------------------------------ gate/up (bf16, fp8)
 template <bool FP8>
-__global__ __launch_bounds__(256) void k_gateup(FfnArgs a) {
-  __shared__ float red[4][4][2][4][64];  // [wave][token group][gate/up][row][lane]
+__device__ __forceinline__ void load_chunk(const uint8_t* mat, int K, int row, int kc, int kq, bf16x8 a[4]) {
+  if (FP8)
+    load_a_fp8(mat + (uint64_t)row * K + kc + kq, a);
+  else
+    load_a_bf16(reinterpret_cast<const uint16_t*>(mat) + (uint64_t)row * K + kc + kq, a);
+}
+
+// ------------------------------------------------------------------ gate/up (bf16, fp8)
+// A work item is (record, 16 rows of F) for gate and up together.  Its K = H
+// reduction is split over the nw wavefronts of the workgroup (128-wide chunk c
+// goes to wavefront c % nw); each wavefront issues the loads of two of its
+// chunks before their MFMAs, and the partial sums are added in LDS in
+// wavefront order, so every output is one fixed-order sum.
+constexpr int kSplit = 8;
+
+template <bool FP8>
+__global__ __launch_bounds__(64 * kSplit) void k_gateup(FfnArgs a) {
+  __shared__ float red[kSplit][kNG][2][4][64];  // [wave][token group][gate/up][row][lane]
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
   const int nr = a.grp[0];
   const int nrt = nr + (a.shared ? 1 : 0);
   const int FT = a.F / kTile;
   const int H = a.H, F = a.F;
+  const int nchunk = H / kChunk;
   const uint64_t mat = (uint64_t)F * H * (FP8 ? 1 : 2);
   const int nsc = (F / 128) * (H / 128);
   const int kq = 32 * (lane >> 4);
-  const uint16_t* x = (const uint16_t*)a.x;
-  uint16_t* hb = (uint16_t*)a.hbuf;
+  const uint16_t* __restrict__ x = (const uint16_t*)a.x;
+  uint16_t* __restrict__ hb = (uint16_t*)a.hbuf;
   for (int item = blockIdx.x; item < nrt * FT; item += gridDim.x) {
     const int r = item / FT, f0 = (item % FT) * kTile;
     const Item it = item_record(a, nr, r);
     const int row = f0 + (lane & 15);
+    const float* sc = reinterpret_cast<const float*>(it.rec + 3 * mat);
+    const int sbase = (f0 / 128) * (H / 128);
     for (int tg0 = 0; tg0 < it.n; tg0 += kTokGroup) {
-      const int ng = min(4, (it.n - tg0 + 15) / 16);
-      int tok[4];
-      bool tv[4];
+      const int ng = min(kNG, (it.n - tg0 + 15) / 16);
+      int tok[kNG];
+      bool tv[kNG];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < kNG; ++g) {
         const int idx = tg0 + 16 * g + (lane & 15);
         tv[g] = g < ng && idx < it.n;
-        tok[g] = tv[g] ? pair_token(a, item_pair(a, it, idx)) : 0;
+        tok[g] = tv[g] ? pair_token(a, item_pair(a, it, r, idx)) : 0;
       }
-      f32x4 ag[4], au[4];
+      f32x4 ag[kNG], au[kNG];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < kNG; ++g) {
         ag[g] = f32x4{0.f, 0.f, 0.f, 0.f};
         au[g] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      for (int kc = wv * kChunk; kc < H; kc += 4 * kChunk) {
-        bf16x8 wg[4], wu[4];
-        float sg = 1.f, su = 1.f;
-        if (FP8) {
-          const uint8_t* pg = it.rec + (uint64_t)row * H + kc + kq;
-          load_a_fp8(pg, wg);
-          load_a_fp8(pg + mat, wu);
-          const float* sc = reinterpret_cast<const float*>(it.rec + 3 * mat);
-          const int si = (f0 / 128) * (H / 128) + kc / 128;
-          sg = sc[si];
-          su = sc[nsc + si];
-        } else {
-          const uint16_t* pg = reinterpret_cast<const uint16_t*>(it.rec) + (uint64_t)row * H + kc + kq;
-          load_a_bf16(pg, wg);
-          load_a_bf16(pg + (uint64_t)F * H, wu);
+      for (int c0 = wv; c0 < nchunk; c0 += 2 * nw) {
+        const int c1 = c0 + nw;
+        const bool two = c1 < nchunk;
+        bf16x8 wg0[4], wu0[4], wg1[4], wu1[4];
+        load_chunk<FP8>(it.rec, H, row, c0 * kChunk, kq, wg0);
+        load_chunk<FP8>(it.rec + mat, H, row, c0 * kChunk, kq, wu0);
+        if (two) {
+          load_chunk<FP8>(it.rec, H, row, c1 * kChunk, kq, wg1);
+          load_chunk<FP8>(it.rec + mat, H, row, c1 * kChunk, kq, wu1);
         }
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int g = 0; g < kNG; ++g) {
           if (g < ng) {
-            bf16x8 b[4];
-            load_b_bf16(x + (uint64_t)tok[g] * H + kc + kq, tv[g], b);
+            bf16x8 b0[4];
+            load_b_bf16(x + (uint64_t)tok[g] * H + c0 * kChunk + kq, tv[g], b0);
             if (FP8) {
               const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-              ag[g] = fma4(sg, mfma4(wg, b, z), ag[g]);
-              au[g] = fma4(su, mfma4(wu, b, z), au[g]);
+              ag[g] = fma4(sc[sbase + c0], mfma4(wg0, b0, z), ag[g]);
+              au[g] = fma4(sc[nsc + sbase + c0], mfma4(wu0, b0, z), au[g]);
             } else {
-              ag[g] = mfma4(wg, b, ag[g]);
-              au[g] = mfma4(wu, b, au[g]);
+              ag[g] = mfma4(wg0, b0, ag[g]);
+              au[g] = mfma4(wu0, b0, au[g]);
+            }
+            if (two) {
+              bf16x8 b1[4];
+              load_b_bf16(x + (uint64_t)tok[g] * H + c1 * kChunk + kq, tv[g], b1);
+              if (FP8) {
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                ag[g] = fma4(sc[sbase + c1], mfma4(wg1, b1, z), ag[g]);
+                au[g] = fma4(sc[nsc + sbase + c1], mfma4(wu1, b1, z), au[g]);
+              } else {
+                ag[g] = mfma4(wg1, b1, ag[g]);
+                au[g] = mfma4(wu1, b1, au[g]);
+              }
             }
           }
         }
       }
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < kNG; ++g) {
         if (g < ng) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -304,18 +336,18 @@ __global__ __launch_bounds__(256) void k_gateup(FfnArgs a) {
         }
       }
       __syncthreads();
-      if (wv < ng) {  // wavefront g finishes token group g
-        const int g = wv;
+      for (int g = wv; g < ng; g += nw) {  // wavefront wv finishes token groups wv, wv + nw, ...
         const int idx = tg0 + 16 * g + (lane & 15);
         if (idx < it.n) {
-          const int p = item_pair(a, it, idx);
+          const int p = item_pair(a, it, r, idx);
           uint16_t hv[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float gs = ((red[0][g][0][i][lane] + red[1][g][0][i][lane]) + red[2][g][0][i][lane]) +
-                             red[3][g][0][i][lane];
-            const float us = ((red[0][g][1][i][lane] + red[1][g][1][i][lane]) + red[2][g][1][i][lane]) +
-                             red[3][g][1][i][lane];
+            float gs = red[0][g][0][i][lane], us = red[0][g][1][i][lane];
+            for (int w = 1; w < nw; ++w) {
+              gs = gs + red[w][g][0][i][lane];
+              us = us + red[w][g][1][i][lane];
+            }
             hv[i] = f32_to_bf16(silu_mul(gs, us));
           }
           uint2 st;
@@ -329,123 +361,96 @@ __global__ __launch_bounds__(256) void k_gateup(FfnArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ combine
-// rows [r0, r0 + nrows) of y for all tokens, in j order, + shared, rounded once
-template <typename A>
-__device__ void combine_tile(const FfnArgs& a, int r0, int nrows) {
-  const int routed = a.T * a.k;
-  for (int q = threadIdx.x; q < a.T * nrows; q += blockDim.x) {
-    const int t = q / nrows, rr = r0 + q % nrows;
-    float acc = 0.f;
-    for (int j = 0; j < a.k; ++j)
-      acc = __builtin_fmaf(a.w[t * a.k + j], a.part[(uint64_t)(t * a.k + j) * a.H + rr], acc);
-    if (a.shared) acc = acc + a.part[(uint64_t)(routed + t) * a.H + rr];
-    const uint64_t o = (uint64_t)t * a.H + rr;
-    if (sizeof(A) == 2) {
-      const uint16_t yb = f32_to_bf16(acc);
-      ((uint16_t*)a.y)[o] = yb;
-      if (a.x_next)
-        ((uint16_t*)a.x_next)[o] = f32_to_bf16(bf16_to_f32(((const uint16_t*)a.x)[o]) + bf16_to_f32(yb));
-    } else {
-      ((float*)a.y)[o] = acc;
-      if (a.x_next) ((float*)a.x_next)[o] = ((const float*)a.x)[o] + acc;
-    }
-  }
-}
-
-// Counts a finished (record, tile) item; the last one for the tile combines it.
-template <typename A>
-__device__ void finish_tile(const FfnArgs& a, int nrt, int tile, int r0, int nrows) {
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(&a.comb_ctr[tile], 1u) == (uint32_t)(nrt - 1);
-  __syncthreads();
-  if (s_last) {
-    __threadfence();
-    if (threadIdx.x == 0) a.comb_ctr[tile] = 0;
-    combine_tile<A>(a, r0, nrows);
-  }
-  __syncthreads();
-}
-
 // ------------------------------------------------------------------ down (bf16, fp8)
+// A work item is (record, 16 rows of H); K = F split like gate/up; fp32
+// partial outputs per (t, j) go to the workspace for the combine kernel.
 template <bool FP8>
-__global__ __launch_bounds__(256) void k_down(FfnArgs a) {
-  __shared__ float red[4][4][4][64];  // [wave][token group][row][lane]
+__global__ __launch_bounds__(64 * kSplit) void k_down(FfnArgs a) {
+  __shared__ float red[kSplit][kNG][4][64];  // [wave][token group][row][lane]
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
   const int nr = a.grp[0];
   const int nrt = nr + (a.shared ? 1 : 0);
   const int HT = a.H / kTile;
   const int H = a.H, F = a.F;
+  const int nchunk = F / kChunk;
   const uint64_t mat = (uint64_t)F * H * (FP8 ? 1 : 2);
   const int nsc = (F / 128) * (H / 128);
   const int kq = 32 * (lane >> 4);
-  const uint16_t* hb = (const uint16_t*)a.hbuf;
+  const uint16_t* __restrict__ hb = (const uint16_t*)a.hbuf;
+  float* __restrict__ part = a.part;
   for (int item = blockIdx.x; item < nrt * HT; item += gridDim.x) {
     const int r = item / HT, ht = item % HT, h0 = ht * kTile;
     const Item it = item_record(a, nr, r);
     const int row = h0 + (lane & 15);
+    const float* sc = reinterpret_cast<const float*>(it.rec + 3 * mat) + 2 * nsc + (h0 / 128) * (F / 128);
     for (int tg0 = 0; tg0 < it.n; tg0 += kTokGroup) {
-      const int ng = min(4, (it.n - tg0 + 15) / 16);
-      int pr[4];
-      bool tv[4];
+      const int ng = min(kNG, (it.n - tg0 + 15) / 16);
+      int pr[kNG];
+      bool tv[kNG];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < kNG; ++g) {
         const int idx = tg0 + 16 * g + (lane & 15);
         tv[g] = g < ng && idx < it.n;
-        pr[g] = tv[g] ? item_pair(a, it, idx) : 0;
+        pr[g] = tv[g] ? item_pair(a, it, r, idx) : 0;
       }
-      f32x4 acc[4];
+      f32x4 acc[kNG];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int kc = wv * kChunk; kc < F; kc += 4 * kChunk) {
-        bf16x8 wd[4];
-        float sd = 1.f;
-        if (FP8) {
-          load_a_fp8(it.rec + 2 * mat + (uint64_t)row * F + kc + kq, wd);
-          const float* sc = reinterpret_cast<const float*>(it.rec + 3 * mat);
-          sd = sc[2 * nsc + (h0 / 128) * (F / 128) + kc / 128];
-        } else {
-          load_a_bf16(reinterpret_cast<const uint16_t*>(it.rec + 2 * mat) + (uint64_t)row * F + kc + kq, wd);
-        }
+      for (int g = 0; g < kNG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int c0 = wv; c0 < nchunk; c0 += 2 * nw) {
+        const int c1 = c0 + nw;
+        const bool two = c1 < nchunk;
+        bf16x8 wd0[4], wd1[4];
+        load_chunk<FP8>(it.rec + 2 * mat, F, row, c0 * kChunk, kq, wd0);
+        if (two) load_chunk<FP8>(it.rec + 2 * mat, F, row, c1 * kChunk, kq, wd1);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int g = 0; g < kNG; ++g) {
           if (g < ng) {
-            bf16x8 b[4];
-            load_b_bf16(hb + (uint64_t)pr[g] * F + kc + kq, tv[g], b);
+            bf16x8 b0[4];
+            load_b_bf16(hb + (uint64_t)pr[g] * F + c0 * kChunk + kq, tv[g], b0);
             if (FP8) {
               const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-              acc[g] = fma4(sd, mfma4(wd, b, z), acc[g]);
+              acc[g] = fma4(sc[c0], mfma4(wd0, b0, z), acc[g]);
             } else {
-              acc[g] = mfma4(wd, b, acc[g]);
+              acc[g] = mfma4(wd0, b0, acc[g]);
+            }
+            if (two) {
+              bf16x8 b1[4];
+              load_b_bf16(hb + (uint64_t)pr[g] * F + c1 * kChunk + kq, tv[g], b1);
+              if (FP8) {
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                acc[g] = fma4(sc[c1], mfma4(wd1, b1, z), acc[g]);
+              } else {
+                acc[g] = mfma4(wd1, b1, acc[g]);
+              }
             }
           }
         }
       }
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
+      for (int g = 0; g < kNG; ++g)
         if (g < ng) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) red[wv][g][i][lane] = acc[g][i];
         }
       __syncthreads();
-      if (wv < ng) {
-        const int g = wv;
+      for (int g = wv; g < ng; g += nw) {
         const int idx = tg0 + 16 * g + (lane & 15);
         if (idx < it.n) {
-          const int p = item_pair(a, it, idx);
+          const int p = item_pair(a, it, r, idx);
           float4 o;
           float* ov = reinterpret_cast<float*>(&o);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            ov[i] = ((red[0][g][i][lane] + red[1][g][i][lane]) + red[2][g][i][lane]) + red[3][g][i][lane];
-          *reinterpret_cast<float4*>(a.part + (uint64_t)p * H + h0 + 4 * (lane >> 4)) = o;
+          for (int i = 0; i < 4; ++i) {
+            float v = red[0][g][i][lane];
+            for (int w = 1; w < nw; ++w) v = v + red[w][g][i][lane];
+            ov[i] = v;
+          }
+          *reinterpret_cast<float4*>(part + (uint64_t)p * H + h0 + 4 * (lane >> 4)) = o;
         }
       }
       __syncthreads();
     }
-    finish_tile<uint16_t>(a, nrt, ht, h0, kTile);
   }
 }
 
@@ -455,15 +460,15 @@ __global__ __launch_bounds__(256) void k_gateup_f32(FfnArgs a) {
   const int nrt = nr + (a.shared ? 1 : 0);
   const int FT = a.F / kF32Rows;
   const int H = a.H, F = a.F;
-  const float* x = (const float*)a.x;
-  float* hb = (float*)a.hbuf;
+  const float* __restrict__ x = (const float*)a.x;
+  float* __restrict__ hb = (float*)a.hbuf;
   for (int item = blockIdx.x; item < nrt * FT; item += gridDim.x) {
     const int r = item / FT, f = (item % FT) * kF32Rows + (threadIdx.x & 63);
     const Item it = item_record(a, nr, r);
     const float* wg = reinterpret_cast<const float*>(it.rec) + (uint64_t)f * H;
     const float* wu = wg + (uint64_t)F * H;
     for (int idx = threadIdx.x >> 6; idx < it.n; idx += 4) {
-      const int p = item_pair(a, it, idx);
+      const int p = item_pair(a, it, r, idx);
       const float* xt = x + (uint64_t)pair_token(a, p) * H;
       float g = 0.f, u = 0.f;
       for (int i = 0; i < H; ++i) {
@@ -480,26 +485,78 @@ __global__ __launch_bounds__(256) void k_down_f32(FfnArgs a) {
   const int nrt = nr + (a.shared ? 1 : 0);
   const int HT = a.H / kF32Rows;
   const int H = a.H, F = a.F;
-  const float* hb = (const float*)a.hbuf;
+  const float* __restrict__ hb = (const float*)a.hbuf;
   for (int item = blockIdx.x; item < nrt * HT; item += gridDim.x) {
     const int r = item / HT, ht = item % HT, hr = ht * kF32Rows + (threadIdx.x & 63);
     const Item it = item_record(a, nr, r);
     const float* wd = reinterpret_cast<const float*>(it.rec) + 2ull * F * H + (uint64_t)hr * F;
     for (int idx = threadIdx.x >> 6; idx < it.n; idx += 4) {
-      const int p = item_pair(a, it, idx);
+      const int p = item_pair(a, it, r, idx);
       const float* hp = hb + (uint64_t)p * F;
       float o = 0.f;
       for (int f = 0; f < F; ++f) o = __builtin_fmaf(wd[f], hp[f], o);
       a.part[(uint64_t)p * H + hr] = o;
     }
-    finish_tile<float>(a, nrt, ht, ht * kF32Rows, kF32Rows);
+  }
+}
+
+// ------------------------------------------------------------------ combine
+// One 256-thread workgroup per token; thread i owns the chunks of 8 elements
+// c = i, i + 256, ...: y = sum_j w[t][j] * part[t*k + j] in j order (+ the
+// shared expert's row), rounded once; x_next = round(residual + y); and, for
+// the decode chain, xn_next = rmsnorm(x_next) in the order of rownorm.h (the
+// same bits as the norm kernel).  Each thread re-reads only what it wrote.
+template <bool F32>
+__global__ __launch_bounds__(kRowThreads) void k_combine(FfnArgs a, void* __restrict__ xn_next, float eps) {
+  __shared__ float s_wave[4];
+  const int t = blockIdx.x;
+  const int H = a.H, k = a.k, routed = a.T * a.k;
+  const float* __restrict__ part = a.part;
+  const float* __restrict__ wt = a.w + (size_t)t * k;
+  const size_t roff = (size_t)t * H * (F32 ? 4 : 2);
+  void* __restrict__ yrow = (uint8_t*)a.y + roff;
+  void* __restrict__ xrow = a.x_next ? (uint8_t*)a.x_next + roff : nullptr;
+  const void* __restrict__ rrow = (const uint8_t*)a.residual + roff;
+  float ss = 0.f;
+  for (int c = threadIdx.x; c * 8 < H; c += kRowThreads) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int j = 0; j < k; ++j) {
+      const float wj = wt[j];
+      const float4* pr = reinterpret_cast<const float4*>(part + (uint64_t)(t * k + j) * H + c * 8);
+      const float4 p0 = pr[0], p1 = pr[1];
+      acc[0] = __builtin_fmaf(wj, p0.x, acc[0]); acc[1] = __builtin_fmaf(wj, p0.y, acc[1]);
+      acc[2] = __builtin_fmaf(wj, p0.z, acc[2]); acc[3] = __builtin_fmaf(wj, p0.w, acc[3]);
+      acc[4] = __builtin_fmaf(wj, p1.x, acc[4]); acc[5] = __builtin_fmaf(wj, p1.y, acc[5]);
+      acc[6] = __builtin_fmaf(wj, p1.z, acc[6]); acc[7] = __builtin_fmaf(wj, p1.w, acc[7]);
+    }
+    if (a.shared) {
+      const float4* pr = reinterpret_cast<const float4*>(part + (uint64_t)(routed + t) * H + c * 8);
+      const float4 p0 = pr[0], p1 = pr[1];
+      acc[0] = acc[0] + p0.x; acc[1] = acc[1] + p0.y; acc[2] = acc[2] + p0.z; acc[3] = acc[3] + p0.w;
+      acc[4] = acc[4] + p1.x; acc[5] = acc[5] + p1.y; acc[6] = acc[6] + p1.z; acc[7] = acc[7] + p1.w;
+    }
+    chunk_store<F32>(yrow, c, acc);  // acc now holds y as stored
+    if (xrow) {
+      float res[8];
+      chunk_load<F32>(rrow, c, res);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) res[q] = res[q] + acc[q];
+      chunk_store<F32>(xrow, c, res);  // res now holds x_next as stored
+      ss = chunk_sumsq(res, ss);
+    }
+  }
+  if (xn_next && xrow) {
+    const float inv = row_inv_rms(row_block_sum(ss, s_wave), H, eps);
+    row_scale_chunks<F32>(xrow, (uint8_t*)xn_next + roff, H, inv);
   }
 }
 
 }  // namespace
 
 hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int T,
-                      const void* shared, void* y, void* x_next, hipStream_t s) {
+                      const void* shared, void* y, const void* residual, void* x_next, void* xn_next, float eps,
+                      hipStream_t s) {
   FfnArgs a;
   a.x = x;
   a.slot_ids = slot_ids;
@@ -511,8 +568,8 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
   a.grp = h->grp;
   a.hbuf = h->hbuf;
   a.part = h->part;
-  a.comb_ctr = h->comb_ctr;
   a.y = y;
+  a.residual = residual ? residual : x;
   a.x_next = x_next;
   a.err = h->cache.err;
   a.T = T;
@@ -521,8 +578,6 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
   a.F = h->F;
   a.S = h->S;
   a.E = h->E;
-  a.off_list = h->gl.off_list();
-  a.off_start = h->gl.off_start();
   a.off_pairs = h->gl.off_pairs();
   // distinct records a call can touch (+ the shared expert)
   const int max_items_r = std::min(T * h->k, h->E) + (shared ? 1 : 0);
@@ -532,16 +587,20 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
     const int g2 = std::min(max_items_r * (h->H / kF32Rows), 2048);
     hipLaunchKernelGGL(k_gateup_f32, dim3(g1), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_down_f32, dim3(g2), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_combine<true>, dim3(T), dim3(kRowThreads), 0, s, a, xn_next, eps);
   } else {
     const int g1 = std::min(max_items_r * (h->F / kTile), 4096);
     const int g2 = std::min(max_items_r * (h->H / kTile), 4096);
+    // wavefronts per work item: one per 128-wide K chunk, at most kSplit
+    const int w1 = std::min(kSplit, h->H / kChunk), w2 = std::min(kSplit, h->F / kChunk);
     if (h->dtype == MOE_FP8_E4M3_B128) {
-      hipLaunchKernelGGL(k_gateup<true>, dim3(g1), dim3(256), 0, s, a);
-      hipLaunchKernelGGL(k_down<true>, dim3(g2), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(k_gateup<true>, dim3(g1), dim3(64 * w1), 0, s, a);
+      hipLaunchKernelGGL(k_down<true>, dim3(g2), dim3(64 * w2), 0, s, a);
     } else {
-      hipLaunchKernelGGL(k_gateup<false>, dim3(g1), dim3(256), 0, s, a);
-      hipLaunchKernelGGL(k_down<false>, dim3(g2), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(k_gateup<false>, dim3(g1), dim3(64 * w1), 0, s, a);
+      hipLaunchKernelGGL(k_down<false>, dim3(g2), dim3(64 * w2), 0, s, a);
     }
+    hipLaunchKernelGGL(k_combine<false>, dim3(T), dim3(kRowThreads), 0, s, a, xn_next, eps);
   }
   return hipGetLastError();
 }

@@ -76,6 +76,8 @@ int check_T(const moe_offload* h, int32_t T) {
 
 }  // namespace
 
+int moe::set_error(int code, const char* msg) { return fail(code, "%s", msg); }
+
 extern "C" {
 
 const char* moe_offload_last_error(void) { return g_err; }
@@ -163,7 +165,6 @@ int moe_offload_create(const moe_offload_desc* d, moe_offload** out) {
   h->gl.max_pairs = max_pairs;
   h->gl.max_recs = std::min(max_pairs, h->S + h->E) + 1;
   const int rows = max_pairs + h->max_tokens;  // routed pairs + shared-expert rows
-  const int route_groups = (h->max_tokens + moe::kRouteTokens - 1) / moe::kRouteTokens;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -173,9 +174,9 @@ int moe_offload_create(const moe_offload_desc* d, moe_offload** out) {
   size_t o_slot_of = take(4 * (size_t)h->E), o_expert_of = take(4 * (size_t)h->S), o_last = take(8 * (size_t)h->S);
   size_t o_tick = take(8), o_list = take(4 * (2 + 2 * (size_t)maxSE)), o_pf = take(4 * (2 + 2 * (size_t)h->S));
   size_t o_cnt = take(8 * moe::C_N), o_err = take(4), o_logits = take(4 * (size_t)h->max_tokens * h->E);
-  size_t o_rctr = take(4 * (size_t)route_groups), o_grp = take(4 * (size_t)h->gl.words());
+  size_t o_grp = take(4 * (size_t)h->gl.words());
   size_t o_h = take((h->dtype == MOE_F32 ? 4 : 2) * (size_t)rows * h->F), o_part = take(4 * (size_t)rows * h->H);
-  size_t o_cctr = take(4 * (size_t)(h->H / 16)), o_scr = take(64);
+  size_t o_scr = take(64);
   e = hipMalloc(&h->state_block, off);
   if (e != hipSuccess) return bail(hip_fail(e, "state block"));
   uint8_t* b = (uint8_t*)h->state_block;
@@ -191,11 +192,9 @@ int moe_offload_create(const moe_offload_desc* d, moe_offload** out) {
   h->cache.S = h->S;
   h->cache.record_bytes = h->record_bytes;
   h->logits = (float*)(b + o_logits);
-  h->route_ctr = (uint32_t*)(b + o_rctr);
   h->grp = (int32_t*)(b + o_grp);
   h->hbuf = (void*)(b + o_h);
   h->part = (float*)(b + o_part);
-  h->comb_ctr = (uint32_t*)(b + o_cctr);
   h->scratch_i32 = (int32_t*)(b + o_scr);
   e = hipHostMalloc((void**)&h->pinned_i32, 64, hipHostMallocDefault);
   if (e != hipSuccess) return bail(hip_fail(e, "pinned scratch"));
@@ -253,12 +252,23 @@ int moe_copy_misses(moe_offload* h, void* stream) {
 }
 
 int moe_slot_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int32_t T,
-                 const void* shared_record, void* y, void* x_next, void* stream) {
+                 const void* shared_record, void* y, const void* residual, void* x_next, void* stream) {
   if (int rc = check_handle(h)) return rc;
   if (int rc = check_T(h, T)) return rc;
   if (!x || !slot_ids || !w || !y) return fail(MOE_EINVAL, "moe_slot_ffn: null pointer");
   DeviceGuard g(h->device);
-  HIP_TRY(moe::launch_ffn(h, x, slot_ids, w, T, shared_record, y, x_next, (hipStream_t)stream));
+  HIP_TRY(moe::launch_ffn(h, x, slot_ids, w, T, shared_record, y, residual, x_next, nullptr, 0.f,
+                          (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_rmsnorm(const void* x, void* out, int32_t T, int32_t H, int32_t dtype, float eps, void* stream) {
+  if (!x || !out) return fail(MOE_EINVAL, "moe_rmsnorm: null pointer");
+  if (T < 1 || H < 8 || H % 8) return fail(MOE_EINVAL, "moe_rmsnorm: T=%d, H=%d (H must be a multiple of 8)", T, H);
+  if (dtype != MOE_F32 && dtype != MOE_BF16 && dtype != MOE_FP8_E4M3_B128)
+    return fail(MOE_EUNSUPPORTED, "moe_rmsnorm: dtype %d", dtype);
+  if (!(eps > 0.0f)) return fail(MOE_EINVAL, "moe_rmsnorm: eps must be positive");
+  HIP_TRY(moe::launch_rmsnorm(x, out, T, H, dtype, eps, (hipStream_t)stream));
   return MOE_OK;
 }
 
@@ -355,6 +365,9 @@ int moe_offload_query(const moe_offload* h, moe_info* out) {
   out->staging = h->staging;
   out->host = h->host;
   out->host_dev = h->host_dev;
+  out->ffn_h = h->hbuf;
+  out->ffn_part = h->part;
+  out->ffn_groups = h->grp;
   out->record_bytes = h->record_bytes;
   out->record_stride = h->record_stride;
   out->E = h->E;

@@ -151,6 +151,9 @@ typedef struct {
   void* staging;          /* device [E, record_stride] */
   void* host;             /* host store [E, record_stride] (host address) */
   void* host_dev;         /* the same store as a device address */
+  void* ffn_h;            /* FFN workspace: h rows [max_tokens*(k+1)][F] (bf16, fp32 for MOE_F32) */
+  float* ffn_part;        /* FFN workspace: per-(t, j) expert outputs [max_tokens*(k+1)][H] fp32 */
+  int32_t* ffn_groups;    /* FFN workspace: {records, list, starts, pair ids} of the last call */
   size_t record_bytes;
   size_t record_stride;
   int32_t E, S, H, F, k, dtype, max_tokens, device;
@@ -208,11 +211,21 @@ int moe_copy_misses(moe_offload* h, void* stream);
  *   r = slot_ids[t][j] (slot or staging record), rounded once to the activation dtype.
  *   x: device [T, H]; slot_ids: device [T, k]; w: device [T, k] fp32;
  *   shared_record: NULL or a device record (same layout/dtype, caller-owned, always resident);
- *   y: device [T, H] (out);  x_next: NULL or device [T, H] (out) = round(x + y).
+ *   y: device [T, H] (out);
+ *   x_next: NULL or device [T, H] (out) = round(residual + y), the residual stream after
+ *           the block; residual: device [T, H], or NULL to add to x itself.
  * Results do not depend on which slot holds an expert or on S.
  * Asynchronous, capture-safe. */
 int moe_slot_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int32_t T,
-                 const void* shared_record, void* y, void* x_next, void* stream);
+                 const void* shared_record, void* y, const void* residual, void* x_next, void* stream);
+
+/* Per-token RMS normalisation, out = round(x / sqrt(mean(x^2) + eps)) (fp32 arithmetic,
+ * no learned scale): the input of each MoE block in the decode-step chain.  The pages
+ * describe no norm; it is this build's reading of the inter-layer glue (a 48-layer
+ * residual chain of gated FFNs without one overflows).
+ *   x, out: device [T, H], fp32 (MOE_F32) or bf16 (otherwise); H a multiple of 8.
+ * Asynchronous, capture-safe. */
+int moe_rmsnorm(const void* x, void* out, int32_t T, int32_t H, int32_t dtype, float eps, void* stream);
 
 /* Prefill entry (host-synchronising, not capturable): count the distinct ids
  * of the call.  More than S: copy the whole layer host -> staging with an
@@ -251,6 +264,64 @@ int moe_offload_query(const moe_offload* h, moe_info* out);
 
 /* Message of the last failing call on this host thread ("" if none). */
 const char* moe_offload_last_error(void);
+
+/* ------------------------------------------------------------------ */
+/* Decode-step chain: L layers captured once into one HIP graph.       */
+/* ------------------------------------------------------------------ */
+/* xinfer-ai 0.14.6 docs/moe_offload.md, "How it works", Decode: the offloaded
+ * decode step stays inside a captured graph with no host synchronisation.
+ * For l = 0 .. L-1 the chain issues, on one compute stream,
+ *     xn_l = rmsnorm(x_l) -> route(layer l, xn_l) -> ensure -> copy -> ffn(xn_l) -> y_l,
+ *     x_{l+1} = round(x_l + y_l)
+ * (a pre-norm residual stream between MoE layers; no other sublayer is modelled).
+ * prefetch_n > 0 builds the router-lookahead variant (FreeToken issue #677,
+ * "Proposal"): at the start of layer l-1 (l >= 1) a side stream runs layer l's
+ * router on layer l-1's router input xn_{l-1}; after ensure of layer l-1 the compute stream joins it
+ * and installs up to prefetch_n predicted experts into layer l (the only
+ * slot-table writers stay on the compute stream); a copy stream copies them
+ * after layer l-1's demand copy, and layer l's demand copy waits for it.
+ * All streams have the default priority.
+ *
+ * The chain owns its activation buffers (device):
+ *   x      [L+1][T][H]  x[0] is the step input (caller writes it before run), x[l+1] = x[l] + y[l]
+ *   xn     [L][T][H]    rmsnorm(x[l]) (eps 1e-6): layer l's router and expert input
+ *   y      [L][T][H]    layer outputs before the residual add
+ *   ids    [L][T][k] int32, w [L][T][k] fp32, slot_ids [L][T][k] int32
+ *   pred   [L][T][k] int32 lookahead predictions (prefetch variant; row l = prediction for layer l)
+ * Activations are fp32 for MOE_F32 layers, bf16 otherwise.
+ *   layers:        L handles (same H, k, dtype; T <= each max_tokens); not owned
+ *   w_router:      L device pointers [E][H]; bias: L device pointers [E] fp32 (caller-owned)
+ *   shared_records: NULL or L device pointers (each may be NULL)
+ * Errors: MOE_EINVAL, MOE_ENOMEM, MOE_EHIP. */
+typedef struct moe_chain moe_chain;
+
+typedef struct {
+  void* x;
+  void* xn;
+  void* y;
+  int32_t* ids;
+  float* w;
+  int32_t* slot_ids;
+  int32_t* pred;
+  size_t act_bytes;   /* bytes per activation element (4 or 2) */
+} moe_chain_buffers;
+
+int moe_chain_create(moe_offload* const* layers, int32_t L, const void* const* w_router, const float* const* bias,
+                     const void* const* shared_records, int32_t T, int32_t prefetch_n, moe_chain** out);
+
+/* Device addresses of the chain's buffers. */
+int moe_chain_get_buffers(const moe_chain* c, moe_chain_buffers* out);
+
+/* One decode step: launch the captured graph on `stream` (captured on the
+ * first call; later calls only launch).  Asynchronous. */
+int moe_chain_run(moe_chain* c, void* stream);
+
+/* The same step issued call by call on `stream` (no graph), for profiling
+ * and for checking the graph against eager execution. */
+int moe_chain_run_eager(moe_chain* c, void* stream);
+
+/* Synchronise and free the chain's graph, streams, events and buffers.  Null-safe. */
+void moe_chain_destroy(moe_chain* c);
 
 #ifdef __cplusplus
 }

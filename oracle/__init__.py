@@ -77,6 +77,7 @@ def lib():
         L.orc_ffn.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]
         L.orc_resolve.argtypes = [vp, i32, i32, vp, vp, sz, vp]
         L.orc_residual.argtypes = [vp, vp, i32, sz, vp]
+        L.orc_rmsnorm.argtypes = [vp, i32, i32, i32, f64, vp]
         _lib = L
     return _lib
 
@@ -279,6 +280,17 @@ def residual(x, y, wdt):
     y = np.ascontiguousarray(y)
     out = np.empty_like(x)
     lib().orc_residual(_p(x), _p(y), wdt, x.size, _p(out))
+    return out
+
+
+RMS_EPS = 1e-6
+
+
+def rmsnorm(x, wdt, eps=RMS_EPS):
+    """Per-token RMS normalisation of a [T, H] stream (the MoE block input)."""
+    x = np.ascontiguousarray(x)
+    out = np.empty_like(x)
+    lib().orc_rmsnorm(_p(x), wdt, x.shape[0], x.shape[1], eps, _p(out))
     return out
 
 

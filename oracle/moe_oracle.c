@@ -523,8 +523,27 @@ void orc_resolve(const int32_t* slot_ids, int n, int S, const uint8_t* slots, co
   }
 }
 
-/* Residual stream between layers (READING: no norm; x_next = x + y rounded
- * once to the activation dtype, with y already rounded). */
+/* Residual stream between layers (READING): the MoE block adds its output to
+ * the stream, x_next = x + y, rounded once to the activation dtype, with y
+ * already rounded. */
 void orc_residual(const void* x, const void* y, int wdt, size_t n, void* out) {
   for (size_t i = 0; i < n; ++i) store_act(out, wdt, i, load_act(x, wdt, i) + load_act(y, wdt, i));
+}
+
+/* Input of each MoE block (READING): the stream normalised to unit root mean
+ * square per token, xn = x / sqrt(mean(x^2) + eps), no learned scale, rounded
+ * once to the activation dtype.  The pages describe no norm; without one the
+ * residual stream of a 48-layer chain of gated FFNs with N(0, 0.02) weights
+ * grows until it overflows, while the pre-norm block of the model family the
+ * configurations are shaped after keeps it bounded. */
+void orc_rmsnorm(const void* x, int wdt, int T, int H, double eps, void* out) {
+  for (int t = 0; t < T; ++t) {
+    double ss = 0.0;
+    for (int i = 0; i < H; ++i) {
+      double v = load_act(x, wdt, (size_t)t * H + i);
+      ss += v * v;
+    }
+    double inv = 1.0 / sqrt(ss / H + eps);
+    for (int i = 0; i < H; ++i) store_act(out, wdt, (size_t)t * H + i, load_act(x, wdt, (size_t)t * H + i) * inv);
+  }
 }

@@ -108,9 +108,9 @@ class GpuLayer:
     def copy(self, stream=None):
         m.moe_copy_misses(self.h, stream or torch.cuda.current_stream())
 
-    def ffn(self, x, T, stream=None, x_next=True):
-        m.moe_slot_ffn(self.h, x, self.slot_ids, self.w, T, self.shared, self.y, self.xn if x_next else None,
-                       stream or torch.cuda.current_stream())
+    def ffn(self, x, T, stream=None, x_next=True, residual=None):
+        m.moe_slot_ffn(self.h, x, self.slot_ids, self.w, T, self.shared, self.y, residual,
+                       self.xn if x_next else None, stream or torch.cuda.current_stream())
 
     def step(self, x, T):
         self.route(x, T)

@@ -1,0 +1,164 @@
+"""GPU parity of the decode-step chain (norm, route, ensure, copy, FFN + residual
+per layer, captured in one HIP graph) and of its router-lookahead prefetch variant.
+
+Per step and layer the oracle is teacher-forced with the GPU's own block input
+xn_l (so the bit-exact routing comparison is on identical inputs), keeps its own
+cache per layer (with installs for the prefetch variant), and must match ids,
+slot ids, demand and prefetch copy lists, and slot tables bit for bit, and the
+outputs within 2e-2.
+"""
+import numpy as np
+import pytest
+import torch
+
+import expert_offload_slot_amd as m
+import oracle
+import synth
+from gpu_harness import act_f64, d2h, row_rel_err, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def test_rmsnorm_parity():
+    for wdt, H, T in [(1, 2048, 5), (1, 256, 33), (0, 64, 7)]:
+        x = synth.tokens(91, 1, T, H, 1, 0.0, wdt)[0] * (3 if wdt == 0 else 1)
+        x = np.ascontiguousarray(x)
+        xd = to_dev(x)
+        out = torch.empty_like(xd)
+        m.moe_rmsnorm(xd, out, T, H, wdt, stream=torch.cuda.current_stream())
+        got = to_np(out)
+        ref = oracle.rmsnorm(x, wdt)
+        if wdt == 0:
+            assert np.max(np.abs(got - ref) / np.abs(ref).max()) <= 1e-6
+        else:
+            # within one bf16 step of the exactly rounded result
+            diff = np.abs(got.astype(np.int32) - ref.astype(np.int32))
+            assert diff.max() <= 1, diff.max()
+
+
+class ChainModel:
+    def __init__(self, L, E, S, k, H, F, wdt, T, seed, prefetch_n=0, zipf=1.2, rho=0.9):
+        self.L, self.E, self.S, self.k, self.H, self.F, self.wdt, self.T = L, E, S, k, H, F, wdt, T
+        self.hosts, self.routers, self.handles = [], [], []
+        for l in range(L):
+            self.hosts.append(synth.records(seed, l, E, H, F, wdt))
+            self.routers.append(synth.router(seed, l, E, H, wdt, zipf_s=zipf))
+            h = m.moe_offload_create(E, S, H, F, k, wdt, T, 0, m.FLAG_AUDIT, None,
+                                     self.handles[0] if l else None)
+            m.host_array(h, E)[:, :self.hosts[l].shape[1]] = self.hosts[l]
+            self.handles.append(h)
+        self.wr = [to_dev(w) for w, _ in self.routers]
+        self.b = [to_dev(b) for _, b in self.routers]
+        self.chain = m.moe_chain_create(self.handles, self.wr, self.b, T, prefetch_n)
+        self.bufs = m.moe_chain_get_buffers(self.chain)
+        self.info = [m.moe_offload_query(h) for h in self.handles]
+        self.xs = synth.tokens(seed, 5, T, H, 64, rho, wdt)
+        self.act = 4 if wdt == 0 else 2
+
+    def run(self, s, graph=True):
+        xd = to_dev(np.ascontiguousarray(self.xs[s]))
+        torch.cuda.synchronize()
+        from gpu_harness import hip
+        hip().hipMemcpy(self.bufs["x"], xd.data_ptr(), self.T * self.H * self.act, 3)
+        (m.moe_chain_run if graph else m.moe_chain_run_eager)(self.chain, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+
+    def snapshot(self):
+        L, T, H, k = self.L, self.T, self.H, self.k
+        dt = np.float32 if self.wdt == 0 else np.uint16
+        return dict(
+            x=d2h(self.bufs["x"], (L + 1) * T * H * self.act, dt).reshape(L + 1, T, H),
+            xn=d2h(self.bufs["xn"], L * T * H * self.act, dt).reshape(L, T, H),
+            y=d2h(self.bufs["y"], L * T * H * self.act, dt).reshape(L, T, H),
+            ids=d2h(self.bufs["ids"], L * T * k * 4, np.int32).reshape(L, T, k),
+            sid=d2h(self.bufs["slot_ids"], L * T * k * 4, np.int32).reshape(L, T, k),
+        )
+
+    def lists(self, l):
+        i = self.info[l]
+        lst = d2h(i["copy_list"], 4 * (2 + 2 * max(self.S, self.E)), np.int32)
+        pf = d2h(i["prefetch_list"], 4 * (2 + 2 * self.S), np.int32)
+        so = d2h(i["slot_of"], 4 * self.E, np.int32)
+        eo = d2h(i["expert_of"], 4 * self.S, np.int32)
+        lu = d2h(i["last_use"], 8 * self.S, np.uint64)
+        return (int(lst[0]), lst[2:2 + 2 * lst[1]].reshape(-1, 2)), pf[2:2 + 2 * pf[1]].reshape(-1, 2), (so, eo, lu)
+
+    def close(self):
+        m.moe_chain_destroy(self.chain)
+        for h in reversed(self.handles):
+            m.moe_offload_destroy(h)
+
+
+def oracle_replay_step(cm, caches, snap, prefetch_n, check_ffn=True):
+    """Teacher-forced oracle for one chain step; asserts parity for every layer."""
+    L = cm.L
+    for l in range(L):
+        xn = snap["xn"][l]
+        # the block input itself: the GPU norm of the GPU stream, within one bf16 step
+        ref_xn = oracle.rmsnorm(snap["x"][l], cm.wdt)
+        if cm.wdt != 0:
+            assert np.abs(xn.astype(np.int32) - ref_xn.astype(np.int32)).max() <= 1
+        ids, w, _ = oracle.route(xn, cm.routers[l][0], cm.routers[l][1], cm.k, cm.wdt)
+        assert np.array_equal(ids, snap["ids"][l]), (l, ids, snap["ids"][l])
+        sid, mode, pairs = caches[l].ensure(ids)
+        caches[l].copy(mode, pairs)
+        assert np.array_equal(sid, snap["sid"][l]), l
+        if prefetch_n and l + 1 < L:
+            pred, _, _ = oracle.route(xn, cm.routers[l + 1][0], cm.routers[l + 1][1], cm.k, cm.wdt)
+            inst = caches[l + 1].install(pred, prefetch_n)
+            caches[l + 1].copy(0, inst)
+        if check_ffn:
+            y, y64 = oracle.ffn(xn, cm.wdt, cm.H, cm.F, caches[l].records(sid), w, want_f64=True)
+            assert row_rel_err(snap["y"][l], y64, cm.wdt) <= 2e-2, l
+            assert np.array_equal(snap["x"][l + 1], oracle.residual(snap["x"][l], snap["y"][l], cm.wdt))
+    # lists and tables of every layer after the step (each handle's last call)
+    for l in range(L):
+        (mode, pairs), pf, (so, eo, lu) = cm.lists(l)
+        oso, oeo, olu, _ = caches[l].state()
+        assert np.array_equal(so, oso) and np.array_equal(eo, oeo) and np.array_equal(lu, olu), l
+
+
+@pytest.mark.parametrize("prefetch_n", [0, 2])
+def test_chain_graph_matches_eager_and_oracle(prefetch_n):
+    L, E, S, k, H, F, T = 4, 16, 6, 4, 256, 256, 2
+    print("chain L=%d E=%d S=%d k=%d H=%d F=%d T=%d prefetch=%d" % (L, E, S, k, H, F, T, prefetch_n), flush=True)
+    cg = ChainModel(L, E, S, k, H, F, 1, T, 81, prefetch_n)
+    ce = ChainModel(L, E, S, k, H, F, 1, T, 81, prefetch_n)
+    caches = [oracle.Cache(E, S, cg.hosts[l], oracle.record_bytes(1, H, F)) for l in range(L)]
+    try:
+        for s in range(12):
+            cg.run(s, graph=True)
+            ce.run(s, graph=False)
+            sg, se = cg.snapshot(), ce.snapshot()
+            for key in sg:
+                assert np.array_equal(sg[key], se[key]), (s, key)
+            oracle_replay_step(cg, caches, sg, prefetch_n)
+        st = [m.moe_offload_stats(h) for h in cg.handles]
+        assert all(x["error"] == 0 for x in st)
+        if prefetch_n:
+            assert sum(x["prefetch_installs"] for x in st) > 0
+    finally:
+        cg.close()
+        ce.close()
+
+
+def test_prefetch_keeps_outputs_identical():
+    """Same token stream with and without lookahead prefetch: identical outputs, identical routing."""
+    L, E, S, k, H, F, T = 6, 32, 8, 4, 256, 256, 1
+    a = ChainModel(L, E, S, k, H, F, 1, T, 83, 0)
+    b = ChainModel(L, E, S, k, H, F, 1, T, 83, 4)
+    try:
+        for s in range(24):
+            a.run(s)
+            b.run(s)
+            sa, sb = a.snapshot(), b.snapshot()
+            assert np.array_equal(sa["x"], sb["x"]) and np.array_equal(sa["ids"], sb["ids"]), s
+        ma = sum(m.moe_offload_stats(h)["misses"] for h in a.handles)
+        stb = [m.moe_offload_stats(h) for h in b.handles]
+        mb = sum(x["misses"] for x in stb)
+        print("demand misses without / with prefetch: %d / %d, installs %d, prefetch hits %d" %
+              (ma, mb, sum(x["prefetch_installs"] for x in stb), sum(x["prefetch_hits"] for x in stb)), flush=True)
+        assert mb <= ma
+    finally:
+        a.close()
+        b.close()

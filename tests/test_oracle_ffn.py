@@ -144,3 +144,43 @@ def test_residual_rounds_once(orc):
     x = np.array([0x3F80, 0x3F80], np.uint16)         # 1.0, 1.0
     y = np.array([0x3B80, 0x3B81], np.uint16)         # 2^-8 (tie -> 1.0), 2^-8(1 + 2^-7) (-> 1 + 2^-7)
     assert orc.residual(x, y, 1).tolist() == [0x3F80, 0x3F81]
+
+
+def test_rmsnorm_matches_numpy(orc, syn):
+    x = syn.tokens(13, 2, 6, 256, 1, 0.0, 1)[0].copy()
+    x[0] = 0x3F80  # a constant row of 1.0 -> all ones
+    xv = act_f64(x, 1)
+    ref = xv / np.sqrt((xv ** 2).mean(axis=1, keepdims=True) + 1e-6)
+    got = orc.rmsnorm(x, 1)
+    exp = np.array([orc.f64_to_bf16(v) for v in ref.reshape(-1)], np.uint16).reshape(x.shape)
+    assert np.array_equal(got, exp)
+    assert np.all(got[0] == 0x3F80)
+    xf = syn.tokens(13, 3, 3, 64, 1, 0.0, 0)[0]
+    reff = xf.astype(np.float64) / np.sqrt((xf.astype(np.float64) ** 2).mean(axis=1, keepdims=True) + 1e-6)
+    assert np.array_equal(orc.rmsnorm(xf, 0), reff.astype(np.float32))
+
+
+def test_prenorm_chain_stays_bounded(orc, syn):
+    """48 chained blocks at hidden 2048 / ffn 768 with N(0, 0.02) experts: without a norm on the
+    block input the stream's RMS grows super-linearly (the reason for the pre-norm reading);
+    with x <- x + MoE(rmsnorm(x)) it stays O(1)."""
+    E, k, H, F, L = 8, 2, 2048, 768, 48
+    layers = []
+    for l in range(L):
+        host = syn.records(3, l, E, H, F, 1)
+        wr, b = syn.router(3, l, E, H, 1, zipf_s=1.2)
+        layers.append((host, wr, b))
+    rms = {}
+    for norm in (False, True):
+        x = syn.tokens(3, 1, 1, H, 1, 0.9, 1)[0]
+        try:
+            for host, wr, b in layers:
+                lay = orc.Layer(E, E, k, H, F, 1, host, wr, b)
+                r = lay.step(orc.rmsnorm(x, 1) if norm else x)
+                x = orc.residual(x, r["y"], 1)
+            xv = act_f64(x, 1)
+            rms[norm] = np.sqrt((xv ** 2).mean()) if np.all(np.isfinite(xv)) else np.inf
+        except ValueError:  # the stream overflowed and a router logit became NaN
+            rms[norm] = np.inf
+    assert rms[True] < 2.0
+    assert rms[False] > 2 * rms[True]
