@@ -1,6 +1,9 @@
 // Decode-step chain: L layers of (route, ensure, copy, ffn + residual) issued
 // on one compute stream and captured once into a HIP graph; optionally the
 // router-lookahead prefetch variant with a predictor stream and a copy stream.
+// Per layer on the compute stream: router logits; one control workgroup (top-k,
+// ensure, FFN grouping); the miss copy; the FFN kernels with the combine,
+// residual and the next layer's norm.
 //
 // xinfer-ai 0.14.6 docs/moe_offload.md, "How it works", Decode (the step stays
 // inside a captured graph, no host sync); FreeToken issue #677, "Proposal"
@@ -56,6 +59,7 @@ size_t R(moe_chain* c, int l) { return (size_t)l * c->T * c->k; }
 hipError_t issue(moe_chain* c, hipStream_t cs) {
   const int T = c->T, n = c->T * c->k;
   const bool pf = c->prefetch_n > 0;
+  const bool fused = n <= moe::kDecideMaxPairs;
   for (int l = 0; l < c->L; ++l) {
     moe_offload* h = c->layers[l];
     const bool look = pf && l + 1 < c->L;
@@ -69,8 +73,13 @@ hipError_t issue(moe_chain* c, hipStream_t cs) {
                             c->wpred + R(c, l + 1), c->sp));
       CHK(hipEventRecord(c->ev_pred[l + 1], c->sp));
     }
-    CHK(moe::launch_route(h, XN(c, l), c->wr[l], c->bias[l], T, c->ids + R(c, l), c->w + R(c, l), cs));
-    CHK(moe::launch_ensure(h, c->ids + R(c, l), n, c->sid + R(c, l), cs));
+    if (fused) {  // logits, then top-k + ensure + FFN grouping in one workgroup
+      CHK(moe::launch_logits(h, XN(c, l), c->wr[l], c->bias[l], T, cs));
+      CHK(moe::launch_decide(h, T, c->ids + R(c, l), c->w + R(c, l), c->sid + R(c, l), cs));
+    } else {
+      CHK(moe::launch_route(h, XN(c, l), c->wr[l], c->bias[l], T, c->ids + R(c, l), c->w + R(c, l), cs));
+      CHK(moe::launch_ensure(h, c->ids + R(c, l), n, c->sid + R(c, l), cs));
+    }
     if (look) {  // join, then install into layer l+1 on the compute stream
       CHK(hipStreamWaitEvent(cs, c->ev_pred[l + 1], 0));
       CHK(moe::launch_install(c->layers[l + 1], c->pred + R(c, l + 1), T, c->prefetch_n, cs));
@@ -85,7 +94,7 @@ hipError_t issue(moe_chain* c, hipStream_t cs) {
       CHK(hipEventRecord(c->ev_pf[l + 1], c->sf));
     }
     CHK(moe::launch_ffn(h, XN(c, l), c->sid + R(c, l), c->w + R(c, l), T, c->shared[l], Y(c, l), X(c, l), X(c, l + 1),
-                        l + 1 < c->L ? XN(c, l + 1) : nullptr, kRmsEps, cs));
+                        l + 1 < c->L ? XN(c, l + 1) : nullptr, kRmsEps, cs, fused));
   }
   if (pf && c->L > 1) {  // rejoin the side streams
     CHK(hipEventRecord(c->ev_sp_done, c->sp));

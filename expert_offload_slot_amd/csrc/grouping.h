@@ -1,0 +1,74 @@
+// Grouping of a call's (token, choice) pairs by record for the expert FFN:
+// one workgroup counting-sorts the n = T*k record indices into the group
+// descriptor (internal.h, GroupLayout) that the FFN work items read.
+#pragma once
+
+#include "blockops.h"
+
+namespace moe {
+
+struct GroupShared {
+  int cnt[2 * kMaxExperts];
+  int cur[2 * kMaxExperts];
+  int rank_of[2 * kMaxExperts];
+  int wave[kWaves];
+};
+
+// rec[i] (LDS or global) is the record index of pair i = t*k + j, in [0, nb).
+// An index outside that range is flagged (audit bit) and treated as record 0.
+// All threads of the block must call it.  The order of the pairs inside a
+// record's list is not fixed, and nothing downstream depends on it.
+__device__ __forceinline__ void group_body(const int32_t* rec, int n, int nb, int32_t* __restrict__ grp,
+                                           int off_pairs, int32_t* err, GroupShared& g) {
+  const int tid = threadIdx.x;
+  for (int b = tid; b < 2 * kMaxExperts; b += kBlock) g.cnt[b] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += kBlock) {
+    int r = rec[i];
+    if ((unsigned)r >= (unsigned)nb) {
+      atomicOr(err, MOE_DEV_ERR_AUDIT);
+      r = 0;
+    }
+    atomicAdd(&g.cnt[r], 1);
+  }
+  __syncthreads();
+  const int c0 = g.cnt[2 * tid], c1 = g.cnt[2 * tid + 1];
+  int tot_pairs, nr;
+  const int pre = block_excl_sum(c0 + c1, g.wave, &tot_pairs);
+  const int pre_nz = block_excl_sum((c0 > 0) + (c1 > 0), g.wave, &nr);
+  int32_t* pairs = grp + off_pairs;
+  g.cur[2 * tid] = pre;
+  g.cur[2 * tid + 1] = pre + c0;
+  g.rank_of[2 * tid] = pre_nz;
+  g.rank_of[2 * tid + 1] = pre_nz + (c0 > 0);
+  if (c0 > 0) {
+    int32_t* blk = grp + kRecWords * (1 + pre_nz);
+    blk[0] = 2 * tid;
+    blk[1] = c0;
+    blk[2] = pre;
+  }
+  if (c1 > 0) {
+    int32_t* blk = grp + kRecWords * (1 + pre_nz + (c0 > 0));
+    blk[0] = 2 * tid + 1;
+    blk[1] = c1;
+    blk[2] = pre + c0;
+  }
+  if (tid == 0) grp[0] = nr;
+  __syncthreads();
+  for (int i = tid; i < n; i += kBlock) {
+    int r = rec[i];
+    if ((unsigned)r >= (unsigned)nb) r = 0;
+    pairs[atomicAdd(&g.cur[r], 1)] = i;
+  }
+  __syncthreads();
+  // inline copies of the first kInline pair ids of every record
+  for (int b = tid; b < nb; b += kBlock) {
+    const int c = g.cnt[b];
+    if (c == 0) continue;
+    int32_t* blk = grp + kRecWords * (1 + g.rank_of[b]);
+    const int start = g.cur[b] - c;  // the cursor ended at start + c
+    for (int q = 0; q < c && q < kInline; ++q) blk[3 + q] = pairs[start + q];
+  }
+}
+
+}  // namespace moe

@@ -87,6 +87,7 @@ int set_error(int code, const char* msg);
 
 // launchers (return hipError_t of the launch)
 hipError_t launch_reset(moe_offload* h, hipStream_t s);
+hipError_t launch_logits(moe_offload* h, const void* x, const void* wr, const float* bias, int T, hipStream_t s);
 hipError_t launch_route(moe_offload* h, const void* x, const void* wr, const float* bias, int T, int32_t* ids,
                         float* w, hipStream_t s);
 hipError_t launch_ensure(moe_offload* h, const int32_t* ids, int n, int32_t* slot_ids, hipStream_t s);
@@ -94,10 +95,15 @@ hipError_t launch_install(moe_offload* h, const int32_t* pred, int T, int max_n,
 hipError_t launch_copy(moe_offload* h, const int32_t* list, hipStream_t s);
 hipError_t launch_distinct(moe_offload* h, const int32_t* ids, int n, int32_t* out_dev, hipStream_t s);
 hipError_t launch_stage_all(moe_offload* h, const int32_t* ids, int n, int32_t* slot_ids, hipStream_t s);
-// xn_next (optional, needs x_next): rmsnorm(x_next) with eps, for the next layer of a chain
+// xn_next (optional, needs x_next): rmsnorm(x_next) with eps, for the next layer of a chain;
+// grouped: the group descriptor for slot_ids was already built (launch_decide)
 hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int T,
                       const void* shared, void* y, const void* residual, void* x_next, void* xn_next, float eps,
-                      hipStream_t s);
+                      hipStream_t s, bool grouped = false);
+// Decode control step in one workgroup: top-k of h->logits (launch_logits first),
+// ensure, and the FFN grouping.  Needs T * k <= kDecideMaxPairs.
+constexpr int kDecideMaxPairs = 512;
+hipError_t launch_decide(moe_offload* h, int T, int32_t* ids, float* w, int32_t* slot_ids, hipStream_t s);
 hipError_t launch_rmsnorm(const void* x, void* out, int T, int H, int dtype, float eps, hipStream_t s);
 
 }  // namespace moe

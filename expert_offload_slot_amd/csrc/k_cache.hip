@@ -7,204 +7,17 @@
 //
 // The table is only ever written by one workgroup of one kernel at a time,
 // on the caller's compute stream: no atomics on shared state, no races.
-#include "internal.h"
+#include "table.h"
 
 namespace moe {
 namespace {
-
-constexpr int kBlock = 1024;  // one workgroup, 16 wavefronts
-constexpr int kWaves = kBlock / 64;
-
-// Exclusive rank of `flag` among the block's threads in thread order, and the total.
-// All threads of the block must call it.  Uses s_wave[kWaves].
-__device__ __forceinline__ int block_rank(bool flag, int* s_wave, int* total) {
-  const unsigned long long m = __ballot(flag);
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int below = __popcll(m & ((1ull << lane) - 1ull));
-  if (lane == 0) s_wave[wid] = __popcll(m);
-  __syncthreads();
-  int base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const int c = s_wave[w];
-    base += w < wid ? c : 0;
-    tot += c;
-  }
-  __syncthreads();
-  *total = tot;
-  return base + below;
-}
-
-// victim order key: (occupied, last_use, slot) ascending
-__device__ __forceinline__ bool key_before(bool occ_a, uint64_t lu_a, int a, bool occ_b, uint64_t lu_b, int b) {
-  if (occ_a != occ_b) return !occ_a;
-  if (lu_a != lu_b) return lu_a < lu_b;
-  return a < b;
-}
-
-struct SharedTable {
-  int slot_of[kMaxExperts];
-  int expert_of[kMaxExperts];
-  uint64_t last_use[kMaxExperts];
-  int flag[kMaxExperts];   // ensure: expert in D; install: tokens predicting it
-  int aux[kMaxExperts];    // install: best top-k position
-  int vic[kMaxExperts];    // victim slot by rank
-  int cand[kMaxExperts];   // install: candidate expert by rank
-  int wave[kWaves];
-  int bad;
-};
-
-// Loads the table into LDS.  Entries outside their range (only possible if
-// the table was overwritten from outside) are dropped and flagged, so every
-// later index stays in bounds.
-__device__ void load_table(const CacheDev& c, SharedTable& t) {
-  const int tid = threadIdx.x;
-  if (tid < c.E) {
-    int s = c.slot_of[tid];
-    if (s < -1 || s >= c.S) {
-      atomicOr(c.err, MOE_DEV_ERR_AUDIT);
-      s = -1;
-    }
-    t.slot_of[tid] = s;
-  }
-  if (tid < c.S) {
-    int e = c.expert_of[tid];
-    if (e < -1 || e >= c.E) {
-      atomicOr(c.err, MOE_DEV_ERR_AUDIT);
-      e = -1;
-    }
-    t.expert_of[tid] = e;
-    t.last_use[tid] = c.last_use[tid];
-  }
-}
-
-__device__ void store_table(const CacheDev& c, const SharedTable& t) {
-  const int tid = threadIdx.x;
-  if (tid < c.E) c.slot_of[tid] = t.slot_of[tid];
-  if (tid < c.S) {
-    c.expert_of[tid] = t.expert_of[tid];
-    c.last_use[tid] = t.last_use[tid];
-  }
-}
-
-// Audit: maps mutually inverse (and, for ensure, every expert of D resident).
-__device__ void audit_table(const CacheDev& c, const SharedTable& t, bool check_D) {
-  const int tid = threadIdx.x;
-  bool bad = false;
-  if (tid < c.S) {
-    const int e = t.expert_of[tid];
-    if (e >= c.E || (e >= 0 && t.slot_of[e] != tid)) bad = true;
-  }
-  if (tid < c.E) {
-    const int s = t.slot_of[tid];
-    if (s >= c.S || (s >= 0 && t.expert_of[s] != tid)) bad = true;
-    if (check_D && t.flag[tid] && s < 0) bad = true;
-  }
-  if (bad) atomicOr(c.err, MOE_DEV_ERR_AUDIT);
-}
 
 // ---------------------------------------------------------------- ensure
 __global__ __launch_bounds__(kBlock) void k_ensure(CacheDev c, const int32_t* __restrict__ ids, int n,
                                                    int32_t* __restrict__ slot_ids, int audit) {
   __shared__ SharedTable t;
-  const int tid = threadIdx.x;
-  const int E = c.E, S = c.S;
   load_table(c, t);
-  if (tid < E) t.flag[tid] = 0;
-  if (tid == 0) t.bad = 0;
-  __syncthreads();
-  for (int i = tid; i < n; i += kBlock) {
-    const int e = ids[i];
-    if ((unsigned)e >= (unsigned)E) t.bad = 1;
-    else t.flag[e] = 1;
-  }
-  __syncthreads();
-  if (t.bad) {  // no-op call: table untouched, empty copy list, valid (0) slot ids
-    for (int i = tid; i < n; i += kBlock) slot_ids[i] = 0;
-    if (tid == 0) {
-      atomicOr(c.err, MOE_DEV_ERR_BAD_ID);
-      c.copy_list[0] = MOE_MODE_SLOTS;
-      c.copy_list[1] = 0;
-    }
-    return;
-  }
-  if (audit) audit_table(c, t, false);
-  const uint64_t tick = *c.tick + 1;
-  const bool inD = tid < E && t.flag[tid];
-  const int sl = tid < E ? t.slot_of[tid] : -1;
-  const bool miss = inD && sl < 0;
-  const bool hit = inD && sl >= 0;
-  const bool pf_hit = hit && t.last_use[sl] == 0;
-  int nd, nm, nh, npf;
-  (void)block_rank(inD, t.wave, &nd);
-  const int mrank = block_rank(miss, t.wave, &nm);
-  (void)block_rank(hit, t.wave, &nh);
-  (void)block_rank(pf_hit, t.wave, &npf);
-
-  if (nd > S) {  // staged: table untouched, residents read in place, misses staged at S + e
-    if (miss) {
-      c.copy_list[2 + 2 * mrank] = tid;
-      c.copy_list[3 + 2 * mrank] = S + tid;
-    }
-    for (int i = tid; i < n; i += kBlock) {
-      const int e = ids[i];
-      const int r = t.slot_of[e];
-      slot_ids[i] = r >= 0 ? r : S + e;
-    }
-    if (tid == 0) {
-      c.copy_list[0] = MOE_MODE_STAGED;
-      c.copy_list[1] = nm;
-      *c.tick = tick;
-      c.counters[C_CALLS] += 1;
-      c.counters[C_STAGED_CALLS] += 1;
-      c.counters[C_STAGED_COPIES] += (uint64_t)nm;
-      c.counters[C_BYTES] += (uint64_t)nm * c.record_bytes;
-    }
-    return;
-  }
-
-  // victim ranks among eligible slots (those not holding an expert of D)
-  if (tid < S) {
-    const int ex = t.expert_of[tid];
-    const bool occ = ex >= 0;
-    if (!occ || !t.flag[ex]) {
-      const uint64_t lu = t.last_use[tid];
-      int rank = 0;
-      for (int s2 = 0; s2 < S; ++s2) {
-        const int ex2 = t.expert_of[s2];
-        const bool occ2 = ex2 >= 0;
-        if (occ2 && t.flag[ex2]) continue;
-        rank += key_before(occ2, t.last_use[s2], s2, occ, lu, tid) ? 1 : 0;
-      }
-      if (rank < nm) t.vic[rank] = tid;
-    }
-  }
-  __syncthreads();
-  if (miss) {
-    const int v = t.vic[mrank];
-    const int old = t.expert_of[v];
-    if (old >= 0) t.slot_of[old] = -1;
-    t.expert_of[v] = tid;
-    t.slot_of[tid] = v;
-    c.copy_list[2 + 2 * mrank] = tid;
-    c.copy_list[3 + 2 * mrank] = v;
-  }
-  __syncthreads();
-  if (inD) t.last_use[t.slot_of[tid]] = tick;
-  __syncthreads();
-  for (int i = tid; i < n; i += kBlock) slot_ids[i] = t.slot_of[ids[i]];
-  store_table(c, t);
-  if (audit) audit_table(c, t, true);
-  if (tid == 0) {
-    c.copy_list[0] = MOE_MODE_SLOTS;
-    c.copy_list[1] = nm;
-    *c.tick = tick;
-    c.counters[C_CALLS] += 1;
-    c.counters[C_HITS] += (uint64_t)nh;
-    c.counters[C_MISSES] += (uint64_t)nm;
-    c.counters[C_PF_HITS] += (uint64_t)npf;
-    c.counters[C_BYTES] += (uint64_t)nm * c.record_bytes;
-  }
+  ensure_body(c, t, ids, n, slot_ids, nullptr, audit);
 }
 
 // ---------------------------------------------------------------- prefetch install

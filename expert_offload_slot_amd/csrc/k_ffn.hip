@@ -27,7 +27,7 @@
 
 #include <algorithm>
 
-#include "internal.h"
+#include "grouping.h"
 #include "rownorm.h"
 
 namespace moe {
@@ -59,86 +59,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)rn_t
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 // ------------------------------------------------------------------ grouping
-constexpr int kGrpBlock = 1024;
-
-// exclusive prefix of v over the 1024 threads; *total = sum
-__device__ __forceinline__ int block_excl_sum(int v, int* s_wave, int* total) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int n = __shfl_up(inc, o);
-    if (lane >= o) inc += n;
-  }
-  if (lane == 63) s_wave[wid] = inc;
-  __syncthreads();
-  int base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kGrpBlock / 64; ++w) {
-    const int c = s_wave[w];
-    base += w < wid ? c : 0;
-    tot += c;
-  }
-  __syncthreads();
-  *total = tot;
-  return base + inc - v;
-}
-
-__global__ __launch_bounds__(kGrpBlock) void k_group(FfnArgs a) {
-  __shared__ int cnt[2 * kMaxExperts];
-  __shared__ int cur[2 * kMaxExperts];
-  __shared__ int rank_of[2 * kMaxExperts];
-  __shared__ int wave[kGrpBlock / 64];
-  const int tid = threadIdx.x;
-  const int n = a.T * a.k, nb = a.S + a.E;
-  for (int b = tid; b < 2 * kMaxExperts; b += kGrpBlock) cnt[b] = 0;
-  __syncthreads();
-  for (int i = tid; i < n; i += kGrpBlock) {
-    int r = a.slot_ids[i];
-    if ((unsigned)r >= (unsigned)nb) {
-      atomicOr(a.err, MOE_DEV_ERR_AUDIT);
-      r = 0;
-    }
-    atomicAdd(&cnt[r], 1);
-  }
-  __syncthreads();
-  const int c0 = cnt[2 * tid], c1 = cnt[2 * tid + 1];
-  int tot_pairs, nr;
-  const int pre = block_excl_sum(c0 + c1, wave, &tot_pairs);
-  const int pre_nz = block_excl_sum((c0 > 0) + (c1 > 0), wave, &nr);
-  int32_t* pairs = a.grp + a.off_pairs;
-  cur[2 * tid] = pre;
-  cur[2 * tid + 1] = pre + c0;
-  rank_of[2 * tid] = pre_nz;
-  rank_of[2 * tid + 1] = pre_nz + (c0 > 0);
-  if (c0 > 0) {
-    int32_t* blk = a.grp + kRecWords * (1 + pre_nz);
-    blk[0] = 2 * tid;
-    blk[1] = c0;
-    blk[2] = pre;
-  }
-  if (c1 > 0) {
-    int32_t* blk = a.grp + kRecWords * (1 + pre_nz + (c0 > 0));
-    blk[0] = 2 * tid + 1;
-    blk[1] = c1;
-    blk[2] = pre + c0;
-  }
-  if (tid == 0) a.grp[0] = nr;
-  __syncthreads();
-  for (int i = tid; i < n; i += kGrpBlock) {
-    int r = a.slot_ids[i];
-    if ((unsigned)r >= (unsigned)nb) r = 0;
-    pairs[atomicAdd(&cur[r], 1)] = i;
-  }
-  __syncthreads();
-  // inline copies of the first kInline pair ids of every record
-  for (int b = tid; b < nb; b += kGrpBlock) {
-    const int c = cnt[b];
-    if (c == 0) continue;
-    int32_t* blk = a.grp + kRecWords * (1 + rank_of[b]);
-    const int start = cur[b] - c;  // the cursor ended at start + c
-    for (int q = 0; q < c && q < kInline; ++q) blk[3 + q] = pairs[start + q];
-  }
+__global__ __launch_bounds__(kBlock) void k_group(FfnArgs a) {
+  __shared__ GroupShared g;
+  group_body(a.slot_ids, a.T * a.k, a.S + a.E, a.grp, a.off_pairs, a.err, g);
 }
 
 // A work item's record (pointer, token count); its pair ids come from the same
@@ -454,6 +377,219 @@ __global__ __launch_bounds__(64 * kSplit) void k_down(FfnArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ decode path (bf16, fp8)
+// Few tokens per record: the weights are streamed once and every byte meets all
+// of the record's tokens while it sits in registers.  A wavefront owns a work
+// item; each 16-lane quarter owns one weight row per stream and reads it in
+// coalesced 16-byte pieces (lane c takes the 8 K values at chunk 16*i + c), so
+// a quarter covers 256 contiguous bytes per load.  Products use the hardware
+// bf16 pair dot (fp32 accumulate); fp8 codes are widened exactly to bf16 pairs
+// first and each 128-wide K block is scaled on its fp32 partial sum.  The 16
+// lanes' partial sums of the (token, stream) pairs are reduced by a transposing
+// butterfly that leaves pair v's sum in lane v.  Fixed order throughout.
+constexpr int kVecK = 16;    // 128-wide K blocks held per stream (2048 K values)
+constexpr int kVecTok = 8;   // tokens per pass over the held weights (8 x 2 streams = 16 lanes)
+constexpr int kDecodeMaxT = 64;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// 8 bf16 weights (as 4 pairs) . 8 bf16 activations
+__device__ __forceinline__ float dot8(uint4 w, uint4 x, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.x), __builtin_bit_cast(bf16x2, x.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.y), __builtin_bit_cast(bf16x2, x.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.z), __builtin_bit_cast(bf16x2, x.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w), __builtin_bit_cast(bf16x2, x.w), acc, false);
+  return acc;
+}
+
+// 8 e4m3 weights widened to 4 bf16 pairs
+__device__ __forceinline__ uint4 widen8(uint2 d) {
+  uint4 u;
+  u.x = cvt2<false>(d.x);
+  u.y = cvt2<true>(d.x);
+  u.z = cvt2<false>(d.y);
+  u.w = cvt2<true>(d.y);
+  return u;
+}
+
+template <bool FP8>
+struct WChunk {
+  typedef uint4 T;
+};
+template <>
+struct WChunk<true> {
+  typedef uint2 T;
+};
+
+template <bool FP8>
+__device__ __forceinline__ typename WChunk<FP8>::T load_w(const uint8_t* row, int kb, int c) {
+  if (FP8)
+    return *reinterpret_cast<const typename WChunk<FP8>::T*>(row + (uint64_t)(16 * kb + c) * 8);
+  else
+    return *reinterpret_cast<const typename WChunk<FP8>::T*>(row + (uint64_t)(16 * kb + c) * 16);
+}
+
+template <bool FP8>
+__device__ __forceinline__ float wdot(typename WChunk<FP8>::T w, uint4 x, float acc, float scale) {
+  if constexpr (FP8) {
+    return __builtin_fmaf(scale, dot8(widen8(w), x, 0.f), acc);
+  } else {
+    return dot8(w, x, acc);
+  }
+}
+
+// v[16] summed over the 16 lanes of a quarter; lane c returns the sum of v[c]
+__device__ __forceinline__ float reduce16_scatter(const float v[16], int c) {
+  float w8[8], w4[4], w2[2];
+  const bool b3 = c & 8, b2 = c & 4, b1 = c & 2, b0 = c & 1;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float mine = b3 ? v[8 + i] : v[i], give = b3 ? v[i] : v[8 + i];
+    w8[i] = mine + __shfl_xor(give, 8);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float mine = b2 ? w8[4 + i] : w8[i], give = b2 ? w8[i] : w8[4 + i];
+    w4[i] = mine + __shfl_xor(give, 4);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float mine = b1 ? w4[2 + i] : w4[i], give = b1 ? w4[i] : w4[2 + i];
+    w2[i] = mine + __shfl_xor(give, 2);
+  }
+  const float mine = b0 ? w2[1] : w2[0], give = b0 ? w2[0] : w2[1];
+  return mine + __shfl_xor(give, 1);
+}
+
+// Two weight rows (stream 0, stream 1) of length K against up to kVecTok
+// activation rows act[t] (bf16, length K); acc[t][s] gets the lane's partial sums.
+template <bool FP8>
+__device__ __forceinline__ void vec_pass(const uint8_t* row0, const uint8_t* row1, const float* sc0,
+                                         const float* sc1, int nk, int c, const uint16_t* const act[kVecTok],
+                                         int nt, float acc[kVecTok][2]) {
+  for (int k0 = 0; k0 < nk; k0 += kVecK) {
+    typename WChunk<FP8>::T w0[kVecK], w1[kVecK];
+    float s0[kVecK], s1[kVecK];
+#pragma unroll
+    for (int i = 0; i < kVecK; ++i) {
+      if (k0 + i < nk) {
+        w0[i] = load_w<FP8>(row0, k0 + i, c);
+        w1[i] = load_w<FP8>(row1, k0 + i, c);
+        s0[i] = FP8 ? sc0[k0 + i] : 1.f;
+        s1[i] = FP8 ? sc1[k0 + i] : 1.f;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kVecTok; ++t) {
+      if (t < nt) {
+        const uint4* xr = reinterpret_cast<const uint4*>(act[t]);
+#pragma unroll
+        for (int i = 0; i < kVecK; ++i) {
+          if (k0 + i < nk) {
+            const uint4 xv = xr[16 * (k0 + i) + c];
+            acc[t][0] = wdot<FP8>(w0[i], xv, acc[t][0], s0[i]);
+            acc[t][1] = wdot<FP8>(w1[i], xv, acc[t][1], s1[i]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// gate/up: work item = (record, 4 rows of F); quarter q takes row f = 4*g + q of
+// gate (stream 0) and up (stream 1); h = silu(gate) * up stored in bf16.
+template <bool FP8>
+__global__ __launch_bounds__(256) void k_gateup_vec(FfnArgs a) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
+  const int nr = a.grp[0];
+  const int nrt = nr + (a.shared ? 1 : 0);
+  const int RG = a.F / 4;
+  const int H = a.H, F = a.F;
+  const int nk = H / 128;
+  const uint64_t esz = FP8 ? 1 : 2;
+  const uint64_t mat = (uint64_t)F * H * esz;
+  const int nsc = (F / 128) * (H / 128);
+  const uint16_t* __restrict__ x = (const uint16_t*)a.x;
+  uint16_t* __restrict__ hb = (uint16_t*)a.hbuf;
+  const int nwave = gridDim.x * 4;
+  for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < nrt * RG; item += nwave) {
+    const int r = item / RG, fg = (item % RG) * 4, f = fg + q;
+    const Item it = item_record(a, nr, r);
+    const uint8_t* wg = it.rec + (uint64_t)f * H * esz;
+    const float* sc = reinterpret_cast<const float*>(it.rec + 3 * mat) + (fg / 128) * (H / 128);
+    for (int tg = 0; tg < it.n; tg += kVecTok) {
+      const int nt = min(kVecTok, it.n - tg);
+      const uint16_t* act[kVecTok];
+#pragma unroll
+      for (int t = 0; t < kVecTok; ++t)
+        act[t] = x + (uint64_t)(t < nt ? pair_token(a, item_pair(a, it, r, tg + t)) : 0) * H;
+      float acc[kVecTok][2];
+#pragma unroll
+      for (int t = 0; t < kVecTok; ++t) acc[t][0] = acc[t][1] = 0.f;
+      vec_pass<FP8>(wg, wg + mat, sc, sc + nsc, nk, c, act, nt, acc);
+      float v[16];
+#pragma unroll
+      for (int t = 0; t < kVecTok; ++t) {
+        v[2 * t] = acc[t][0];
+        v[2 * t + 1] = acc[t][1];
+      }
+      const float mine = reduce16_scatter(v, c);  // token c / 2, stream c % 2
+      const float up = __shfl_xor(mine, 1);
+      const int t = c >> 1;
+      if ((c & 1) == 0 && t < nt) {
+        const int p = item_pair(a, it, r, tg + t);
+        hb[(uint64_t)p * F + f] = f32_to_bf16(silu_mul(mine, up));
+      }
+    }
+  }
+}
+
+// down: work item = (record, 8 rows of H); quarter q takes rows 8*g + q (stream 0)
+// and 8*g + 4 + q (stream 1) against h of the record's pairs; fp32 partial outputs.
+template <bool FP8>
+__global__ __launch_bounds__(256) void k_down_vec(FfnArgs a) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
+  const int nr = a.grp[0];
+  const int nrt = nr + (a.shared ? 1 : 0);
+  const int RG = a.H / 8;
+  const int H = a.H, F = a.F;
+  const int nk = F / 128;
+  const uint64_t esz = FP8 ? 1 : 2;
+  const uint64_t mat = (uint64_t)F * H * esz;
+  const int nsc = (F / 128) * (H / 128);
+  const uint16_t* __restrict__ hb = (const uint16_t*)a.hbuf;
+  float* __restrict__ part = a.part;
+  const int nwave = gridDim.x * 4;
+  for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < nrt * RG; item += nwave) {
+    const int r = item / RG, hg = (item % RG) * 8, h0 = hg + q;
+    const Item it = item_record(a, nr, r);
+    const uint8_t* wd = it.rec + 2 * mat + (uint64_t)h0 * F * esz;
+    const float* sc = reinterpret_cast<const float*>(it.rec + 3 * mat) + 2 * nsc + (hg / 128) * (F / 128);
+    for (int tg = 0; tg < it.n; tg += kVecTok) {
+      const int nt = min(kVecTok, it.n - tg);
+      const uint16_t* act[kVecTok];
+#pragma unroll
+      for (int t = 0; t < kVecTok; ++t) act[t] = hb + (uint64_t)(t < nt ? item_pair(a, it, r, tg + t) : 0) * F;
+      float acc[kVecTok][2];
+#pragma unroll
+      for (int t = 0; t < kVecTok; ++t) acc[t][0] = acc[t][1] = 0.f;
+      vec_pass<FP8>(wd, wd + 4ull * F * esz, sc, sc, nk, c, act, nt, acc);
+      float v[16];
+#pragma unroll
+      for (int t = 0; t < kVecTok; ++t) {
+        v[2 * t] = acc[t][0];
+        v[2 * t + 1] = acc[t][1];
+      }
+      const float mine = reduce16_scatter(v, c);  // token c / 2, stream c % 2
+      const int t = c >> 1;
+      if (t < nt) {
+        const int p = item_pair(a, it, r, tg + t);
+        part[(uint64_t)p * H + h0 + 4 * (c & 1)] = mine;
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ fp32 path
 __global__ __launch_bounds__(256) void k_gateup_f32(FfnArgs a) {
   const int nr = a.grp[0];
@@ -556,7 +692,7 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(FfnArgs a, void* __rest
 
 hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int T,
                       const void* shared, void* y, const void* residual, void* x_next, void* xn_next, float eps,
-                      hipStream_t s) {
+                      hipStream_t s, bool grouped) {
   FfnArgs a;
   a.x = x;
   a.slot_ids = slot_ids;
@@ -581,13 +717,25 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
   a.off_pairs = h->gl.off_pairs();
   // distinct records a call can touch (+ the shared expert)
   const int max_items_r = std::min(T * h->k, h->E) + (shared ? 1 : 0);
-  hipLaunchKernelGGL(k_group, dim3(1), dim3(kGrpBlock), 0, s, a);
+  if (!grouped) hipLaunchKernelGGL(k_group, dim3(1), dim3(kBlock), 0, s, a);
   if (h->dtype == MOE_F32) {
     const int g1 = std::min(max_items_r * (h->F / kF32Rows), 2048);
     const int g2 = std::min(max_items_r * (h->H / kF32Rows), 2048);
     hipLaunchKernelGGL(k_gateup_f32, dim3(g1), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_down_f32, dim3(g2), dim3(256), 0, s, a);
     hipLaunchKernelGGL(k_combine<true>, dim3(T), dim3(kRowThreads), 0, s, a, xn_next, eps);
+  } else if (T <= kDecodeMaxT) {
+    // decode: one wavefront per work item, 4 per workgroup
+    const int g1 = std::min((max_items_r * (h->F / 4) + 3) / 4, 8192);
+    const int g2 = std::min((max_items_r * (h->H / 8) + 3) / 4, 8192);
+    if (h->dtype == MOE_FP8_E4M3_B128) {
+      hipLaunchKernelGGL(k_gateup_vec<true>, dim3(g1), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(k_down_vec<true>, dim3(g2), dim3(256), 0, s, a);
+    } else {
+      hipLaunchKernelGGL(k_gateup_vec<false>, dim3(g1), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(k_down_vec<false>, dim3(g2), dim3(256), 0, s, a);
+    }
+    hipLaunchKernelGGL(k_combine<false>, dim3(T), dim3(kRowThreads), 0, s, a, xn_next, eps);
   } else {
     const int g1 = std::min(max_items_r * (h->F / kTile), 4096);
     const int g2 = std::min(max_items_r * (h->H / kTile), 4096);

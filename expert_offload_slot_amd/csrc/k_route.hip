@@ -12,10 +12,12 @@
 //   k_logits  grid (ceil(E/4), ceil(T/4)); a wavefront owns one expert and up
 //             to 4 tokens, so the router row is loaded once for them.
 //   k_topk    one wavefront per token: k rounds of a (logit desc, id asc)
-//             arg-max, then the softmax over the k chosen logits.
+//             arg-max over register-held logits, then the softmax over the k
+//             chosen logits (wave_topk.h; the fused decode control kernel runs
+//             the same code).
 #include <math.h>
 
-#include "internal.h"
+#include "wave_topk.h"
 
 namespace moe {
 namespace {
@@ -70,52 +72,25 @@ __global__ __launch_bounds__(256) void k_logits(const A* __restrict__ x, const A
   }
 }
 
-// Top-k of one token's E logits by one wavefront, by rank: the position of
-// expert e is the number of experts ordered before it by (logit desc, id asc);
-// the k experts of rank < k are selected.  No serial rounds.  NaN is reported
-// and ranked as -inf.
+// Top-k of one token by one wavefront (wave_topk.h).
+template <int J>
 __global__ __launch_bounds__(64) void k_topk(const float* __restrict__ logits, int T, int E, int k,
                                              int32_t* __restrict__ ids, float* __restrict__ w, int32_t* err) {
-  __shared__ float sl[kMaxExperts];
-  __shared__ float s_sel[kMaxTopK];
   const int lane = threadIdx.x;
-  const int t = blockIdx.x;  // one wavefront per token (workgroup-uniform)
-  const float* l = logits + (size_t)t * E;
-  bool nan = false;
-  for (int e = lane; e < E; e += 64) {
-    float v = l[e];
-    if (v != v) {
-      nan = true;
-      v = -INFINITY;
-    }
-    sl[e] = v;
+  const int t = blockIdx.x;
+  int id;
+  float wt;
+  const bool nan = wave_topk<J>(logits + (size_t)t * E, E, k, &id, &wt);
+  if (nan && lane == 0) atomicOr(err, MOE_DEV_ERR_NAN);
+  if (lane < k) {
+    ids[(size_t)t * k + lane] = id;
+    w[(size_t)t * k + lane] = wt;
   }
-  if (__any(nan) && lane == 0) atomicOr(err, MOE_DEV_ERR_NAN);
-  __syncthreads();
-  for (int e = lane; e < E; e += 64) {
-    const float v = sl[e];
-    int rank = 0;
-    for (int e2 = 0; e2 < E; ++e2) {
-      const float v2 = sl[e2];
-      rank += (v2 > v || (v2 == v && e2 < e)) ? 1 : 0;
-    }
-    if (rank < k) {
-      ids[(size_t)t * k + rank] = e;
-      s_sel[rank] = v;
-    }
-  }
-  __syncthreads();
-  const float ex = lane < k ? expf(s_sel[lane] - s_sel[0]) : 0.f;
-  float sum = ex;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
-  if (lane < k) w[(size_t)t * k + lane] = ex / sum;
 }
 
 }  // namespace
 
-hipError_t launch_route(moe_offload* h, const void* x, const void* wr, const float* bias, int T, int32_t* ids,
-                        float* w, hipStream_t s) {
+hipError_t launch_logits(moe_offload* h, const void* x, const void* wr, const float* bias, int T, hipStream_t s) {
   dim3 grid((h->E + 3) / 4, (T + kRouteTokens - 1) / kRouteTokens);
   if (h->dtype == MOE_F32)
     hipLaunchKernelGGL(k_logits<float>, grid, dim3(256), 0, s, (const float*)x, (const float*)wr, bias, T, h->E,
@@ -123,7 +98,16 @@ hipError_t launch_route(moe_offload* h, const void* x, const void* wr, const flo
   else
     hipLaunchKernelGGL(k_logits<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)x, (const uint16_t*)wr, bias, T,
                        h->E, h->H, h->logits);
-  hipLaunchKernelGGL(k_topk, dim3(T), dim3(64), 0, s, h->logits, T, h->E, h->k, ids, w, h->cache.err);
+  return hipGetLastError();
+}
+
+hipError_t launch_route(moe_offload* h, const void* x, const void* wr, const float* bias, int T, int32_t* ids,
+                        float* w, hipStream_t s) {
+  hipError_t e = launch_logits(h, x, wr, bias, T, s);
+  if (e != hipSuccess) return e;
+  const int J = topk_lanes(h->E);
+  auto kt = J == 1 ? k_topk<1> : J == 2 ? k_topk<2> : J == 4 ? k_topk<4> : J == 8 ? k_topk<8> : k_topk<16>;
+  hipLaunchKernelGGL(kt, dim3(T), dim3(64), 0, s, h->logits, T, h->E, h->k, ids, w, h->cache.err);
   return hipGetLastError();
 }
 

@@ -1,0 +1,62 @@
+// Decode control step in one workgroup: top-k, slot ensure and FFN grouping.
+//
+// xinfer-ai 0.14.6 docs/moe_offload.md, "How it works" (Decode): between the
+// router and the expert GEMMs a decode step looks up the chosen experts in the
+// layer's slot table, assigns LRU slots to the misses, rewrites ids to slot ids
+// and leaves the miss list on the device, all without a host round trip.
+//
+// The three steps are the ones the separate entry points run (wave_topk.h,
+// table.h, grouping.h); here they share one 1024-thread workgroup so a decode
+// layer pays one launch and no global round trip between them: each wavefront
+// takes tokens w, w + 16, ... for the top-k, the ids stay in LDS for the
+// ensure, and the record indices stay in LDS for the counting sort.  The slot
+// table load is issued first and overlaps the top-k.
+#include "grouping.h"
+#include "table.h"
+#include "wave_topk.h"
+
+namespace moe {
+namespace {
+
+template <int J>
+__global__ __launch_bounds__(kBlock) void k_decide(CacheDev c, const float* __restrict__ logits, int T, int k,
+                                                   int32_t* __restrict__ ids, float* __restrict__ w,
+                                                   int32_t* __restrict__ slot_ids, int32_t* __restrict__ grp,
+                                                   int off_pairs, int audit) {
+  __shared__ SharedTable t;
+  __shared__ GroupShared g;
+  __shared__ int ids_l[kDecideMaxPairs];
+  __shared__ int rec_l[kDecideMaxPairs];
+  load_table(c, t);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int E = c.E;
+  bool nan = false;
+  for (int tk = wv; tk < T; tk += kWaves) {
+    int id;
+    float wt;
+    nan = wave_topk<J>(logits + (size_t)tk * E, E, k, &id, &wt) || nan;
+    if (lane < k) {
+      ids[(size_t)tk * k + lane] = id;
+      w[(size_t)tk * k + lane] = wt;
+      ids_l[tk * k + lane] = id;
+    }
+  }
+  if (nan && lane == 0) atomicOr(c.err, MOE_DEV_ERR_NAN);
+  __syncthreads();
+  ensure_body(c, t, ids_l, T * k, slot_ids, rec_l, audit);
+  __syncthreads();
+  group_body(rec_l, T * k, c.S + c.E, grp, off_pairs, c.err, g);
+}
+
+}  // namespace
+
+hipError_t launch_decide(moe_offload* h, int T, int32_t* ids, float* w, int32_t* slot_ids, hipStream_t s) {
+  if (T * h->k > kDecideMaxPairs) return hipErrorInvalidValue;
+  const int J = topk_lanes(h->E);
+  auto kd = J == 1 ? k_decide<1> : J == 2 ? k_decide<2> : J == 4 ? k_decide<4> : J == 8 ? k_decide<8> : k_decide<16>;
+  hipLaunchKernelGGL(kd, dim3(1), dim3(kBlock), 0, s, h->cache, h->logits, T, h->k, ids, w, slot_ids, h->grp,
+                     h->gl.off_pairs(), (h->flags & MOE_FLAG_AUDIT) ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace moe
