@@ -37,6 +37,9 @@ __device__ __forceinline__ void group_body(const int32_t* rec, int n, int nb, in
   const int pre = block_excl_sum(c0 + c1, g.wave, &tot_pairs);
   const int pre_nz = block_excl_sum((c0 > 0) + (c1 > 0), g.wave, &nr);
   int32_t* pairs = grp + off_pairs;
+  // cnt now holds each record's start in the pair array, cur its cursor
+  g.cnt[2 * tid] = pre;
+  g.cnt[2 * tid + 1] = pre + c0;
   g.cur[2 * tid] = pre;
   g.cur[2 * tid + 1] = pre + c0;
   g.rank_of[2 * tid] = pre_nz;
@@ -55,19 +58,15 @@ __device__ __forceinline__ void group_body(const int32_t* rec, int n, int nb, in
   }
   if (tid == 0) grp[0] = nr;
   __syncthreads();
+  // each pair goes to its record's list, and the first kInline of a list also
+  // into the record block
   for (int i = tid; i < n; i += kBlock) {
     int r = rec[i];
     if ((unsigned)r >= (unsigned)nb) r = 0;
-    pairs[atomicAdd(&g.cur[r], 1)] = i;
-  }
-  __syncthreads();
-  // inline copies of the first kInline pair ids of every record
-  for (int b = tid; b < nb; b += kBlock) {
-    const int c = g.cnt[b];
-    if (c == 0) continue;
-    int32_t* blk = grp + kRecWords * (1 + g.rank_of[b]);
-    const int start = g.cur[b] - c;  // the cursor ended at start + c
-    for (int q = 0; q < c && q < kInline; ++q) blk[3 + q] = pairs[start + q];
+    const int pos = atomicAdd(&g.cur[r], 1);
+    pairs[pos] = i;
+    const int q = pos - g.cnt[r];
+    if (q < kInline) grp[kRecWords * (1 + g.rank_of[r]) + 3 + q] = i;
   }
 }
 

@@ -11,13 +11,12 @@
 // Two kernels, no communication between workgroups inside a kernel:
 //   k_logits  grid (ceil(E/4), ceil(T/4)); a wavefront owns one expert and up
 //             to 4 tokens, so the router row is loaded once for them.
-//   k_topk    one wavefront per token: k rounds of a (logit desc, id asc)
-//             arg-max over register-held logits, then the softmax over the k
-//             chosen logits (wave_topk.h; the fused decode control kernel runs
-//             the same code).
+//   k_topk    one wavefront per token: radix select of the k largest keys,
+//             then the softmax over the k chosen logits (topk.h; the fused
+//             decode control kernel runs the same code).
 #include <math.h>
 
-#include "wave_topk.h"
+#include "topk.h"
 
 namespace moe {
 namespace {
@@ -72,15 +71,17 @@ __global__ __launch_bounds__(256) void k_logits(const A* __restrict__ x, const A
   }
 }
 
-// Top-k of one token by one wavefront (wave_topk.h).
+// Top-k (topk.h): one wavefront per token, 4 tokens per workgroup.
 template <int J>
-__global__ __launch_bounds__(64) void k_topk(const float* __restrict__ logits, int T, int E, int k,
-                                             int32_t* __restrict__ ids, float* __restrict__ w, int32_t* err) {
-  const int lane = threadIdx.x;
-  const int t = blockIdx.x;
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
+                                              int32_t* __restrict__ ids, float* __restrict__ w, int32_t* err) {
+  __shared__ TopkScratch s[4];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wv;
+  if (t >= T) return;  // wave-uniform; no workgroup barrier below
   int id;
   float wt;
-  const bool nan = wave_topk<J>(logits + (size_t)t * E, E, k, &id, &wt);
+  const bool nan = wave_topk<J>(logits + (size_t)t * E, E, k, s[wv], &id, &wt);
   if (nan && lane == 0) atomicOr(err, MOE_DEV_ERR_NAN);
   if (lane < k) {
     ids[(size_t)t * k + lane] = id;
@@ -107,7 +108,7 @@ hipError_t launch_route(moe_offload* h, const void* x, const void* wr, const flo
   if (e != hipSuccess) return e;
   const int J = topk_lanes(h->E);
   auto kt = J == 1 ? k_topk<1> : J == 2 ? k_topk<2> : J == 4 ? k_topk<4> : J == 8 ? k_topk<8> : k_topk<16>;
-  hipLaunchKernelGGL(kt, dim3(T), dim3(64), 0, s, h->logits, T, h->E, h->k, ids, w, h->cache.err);
+  hipLaunchKernelGGL(kt, dim3((T + 3) / 4), dim3(256), 0, s, h->logits, T, h->E, h->k, ids, w, h->cache.err);
   return hipGetLastError();
 }
 

@@ -5,15 +5,15 @@
 // layer's slot table, assigns LRU slots to the misses, rewrites ids to slot ids
 // and leaves the miss list on the device, all without a host round trip.
 //
-// The three steps are the ones the separate entry points run (wave_topk.h,
+// The three steps are the ones the separate entry points run (topk.h,
 // table.h, grouping.h); here they share one 1024-thread workgroup so a decode
-// layer pays one launch and no global round trip between them: each wavefront
-// takes tokens w, w + 16, ... for the top-k, the ids stay in LDS for the
-// ensure, and the record indices stay in LDS for the counting sort.  The slot
-// table load is issued first and overlaps the top-k.
+// layer pays one launch and no global round trip between them: wavefront w
+// selects for tokens w, w + 16, ..., the ids stay in LDS for the ensure, and
+// the record indices stay in LDS for the counting sort.  The slot table load
+// is issued first and is in flight during the top-k.
 #include "grouping.h"
 #include "table.h"
-#include "wave_topk.h"
+#include "topk.h"
 
 namespace moe {
 namespace {
@@ -24,28 +24,29 @@ __global__ __launch_bounds__(kBlock) void k_decide(CacheDev c, const float* __re
                                                    int32_t* __restrict__ slot_ids, int32_t* __restrict__ grp,
                                                    int off_pairs, int audit) {
   __shared__ SharedTable t;
-  __shared__ GroupShared g;
+  __shared__ union {
+    GroupShared g;
+    TopkScratch tk[kWaves];
+  } u;
   __shared__ int ids_l[kDecideMaxPairs];
   __shared__ int rec_l[kDecideMaxPairs];
-  load_table(c, t);
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int E = c.E;
-  bool nan = false;
-  for (int tk = wv; tk < T; tk += kWaves) {
+  load_table(c, t);  // its loads are in flight while the top-k reads the logits
+  for (int tok = wv; tok < T; tok += kWaves) {
     int id;
     float wt;
-    nan = wave_topk<J>(logits + (size_t)tk * E, E, k, &id, &wt) || nan;
+    const bool nan = wave_topk<J>(logits + (size_t)tok * c.E, c.E, k, u.tk[wv], &id, &wt);
+    if (nan && lane == 0) atomicOr(c.err, MOE_DEV_ERR_NAN);
     if (lane < k) {
-      ids[(size_t)tk * k + lane] = id;
-      w[(size_t)tk * k + lane] = wt;
-      ids_l[tk * k + lane] = id;
+      ids[(size_t)tok * k + lane] = id;
+      w[(size_t)tok * k + lane] = wt;
+      ids_l[tok * k + lane] = id;
     }
   }
-  if (nan && lane == 0) atomicOr(c.err, MOE_DEV_ERR_NAN);
   __syncthreads();
   ensure_body(c, t, ids_l, T * k, slot_ids, rec_l, audit);
   __syncthreads();
-  group_body(rec_l, T * k, c.S + c.E, grp, off_pairs, c.err, g);
+  group_body(rec_l, T * k, c.S + c.E, grp, off_pairs, c.err, u.g);
 }
 
 }  // namespace

@@ -18,16 +18,29 @@ __device__ __forceinline__ bool key_before(bool occ_a, uint64_t lu_a, int a, boo
   return a < b;
 }
 
+// victim order as one integer: (occupied, last_use, slot) ascending.  last_use
+// is a call count, far below 2^53.
+__device__ __forceinline__ uint64_t victim_key(bool occ, uint64_t lu, int slot) {
+  return (occ ? (1ull << 63) : 0ull) | ((lu & ((1ull << 53) - 1)) << 10) | (uint64_t)slot;
+}
+
 struct SharedTable {
   int slot_of[kMaxExperts];
   int expert_of[kMaxExperts];
   uint64_t last_use[kMaxExperts];
   int flag[kMaxExperts];   // ensure: expert in D; install: tokens predicting it
-  int aux[kMaxExperts];    // install: best top-k position
+  union {
+    struct {
+      int aux[kMaxExperts];    // install: best top-k position
+      int cand[kMaxExperts];   // install: candidate expert by rank
+    };
+    uint64_t vkey[kMaxExperts];  // ensure: victim key of each slot (~0 if not eligible)
+  };
   int vic[kMaxExperts];    // victim slot by rank
-  int cand[kMaxExperts];   // install: candidate expert by rank
-  int wave[kWaves];
+  int wave[4 * kWaves];
   int bad;
+  uint64_t tick;           // the table's call counter as loaded
+  uint64_t cnt[C_N];       // the counters as loaded
 };
 
 // Loads the table into LDS.  Entries outside their range (only possible if
@@ -52,6 +65,10 @@ __device__ __forceinline__ void load_table(const CacheDev& c, SharedTable& t) {
     t.expert_of[tid] = e;
     t.last_use[tid] = c.last_use[tid];
   }
+  // the call counter and the statistics, from another wavefront
+  const int u = tid - 64 * (kWaves - 1);
+  if (u == 0) t.tick = *c.tick;
+  if (u >= 1 && u <= C_N) t.cnt[u - 1] = c.counters[u - 1];
 }
 
 __device__ __forceinline__ void store_table(const CacheDev& c, const SharedTable& t) {
@@ -116,17 +133,14 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
     return;  // block-uniform
   }
   if (audit) audit_table(c, t, false);
-  const uint64_t tick = *c.tick + 1;
+  const uint64_t tick = t.tick + 1;
   const bool inD = tid < E && t.flag[tid];
   const int sl = tid < E ? t.slot_of[tid] : -1;
-  const bool miss = inD && sl < 0;
-  const bool hit = inD && sl >= 0;
-  const bool pf_hit = hit && t.last_use[sl] == 0;
-  int nd, nm, nh, npf;
-  (void)block_rank(inD, t.wave, &nd);
-  const int mrank = block_rank(miss, t.wave, &nm);
-  (void)block_rank(hit, t.wave, &nh);
-  (void)block_rank(pf_hit, t.wave, &npf);
+  const bool f[4] = {inD, inD && sl < 0, inD && sl >= 0, inD && sl >= 0 && t.last_use[sl] == 0};
+  const bool miss = f[1];
+  int rk[4], tot[4];
+  block_rank4(f, t.wave, rk, tot);
+  const int nd = tot[0], mrank = rk[1], nm = tot[1], nh = tot[2], npf = tot[3];
 
   if (nd > S) {  // staged: table untouched, residents read in place, misses staged at S + e
     if (miss) {
@@ -144,41 +158,43 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
       c.copy_list[0] = MOE_MODE_STAGED;
       c.copy_list[1] = nm;
       *c.tick = tick;
-      c.counters[C_CALLS] += 1;
-      c.counters[C_STAGED_CALLS] += 1;
-      c.counters[C_STAGED_COPIES] += (uint64_t)nm;
-      c.counters[C_BYTES] += (uint64_t)nm * c.record_bytes;
+      c.counters[C_CALLS] = t.cnt[C_CALLS] + 1;
+      c.counters[C_STAGED_CALLS] = t.cnt[C_STAGED_CALLS] + 1;
+      c.counters[C_STAGED_COPIES] = t.cnt[C_STAGED_COPIES] + (uint64_t)nm;
+      c.counters[C_BYTES] = t.cnt[C_BYTES] + (uint64_t)nm * c.record_bytes;
     }
     return;  // block-uniform
   }
 
-  // victim ranks among eligible slots (those not holding an expert of D)
-  if (tid < S) {
-    const int ex = t.expert_of[tid];
-    const bool occ = ex >= 0;
-    if (!occ || !t.flag[ex]) {
-      const uint64_t lu = t.last_use[tid];
-      int rank = 0;
-      for (int s2 = 0; s2 < S; ++s2) {
-        const int ex2 = t.expert_of[s2];
-        const bool occ2 = ex2 >= 0;
-        if (occ2 && t.flag[ex2]) continue;
-        rank += key_before(occ2, t.last_use[s2], s2, occ, lu, tid) ? 1 : 0;
-      }
-      if (rank < nm) t.vic[rank] = tid;
+  // victims: the nm eligible slots (not holding an expert of D) of smallest key
+  if (nm > 0) {
+    if (tid < S) {
+      const int ex = t.expert_of[tid];
+      const bool occ = ex >= 0;
+      t.vkey[tid] = (!occ || !t.flag[ex]) ? victim_key(occ, t.last_use[tid], tid) : ~0ull;
     }
+    __syncthreads();
+    if (tid < S) {
+      const uint64_t mine = t.vkey[tid];
+      if (mine != ~0ull) {
+        int rank = 0;
+#pragma unroll 8
+        for (int s2 = 0; s2 < S; ++s2) rank += t.vkey[s2] < mine ? 1 : 0;
+        if (rank < nm) t.vic[rank] = tid;
+      }
+    }
+    __syncthreads();
+    if (miss) {
+      const int v = t.vic[mrank];
+      const int old = t.expert_of[v];
+      if (old >= 0) t.slot_of[old] = -1;
+      t.expert_of[v] = tid;
+      t.slot_of[tid] = v;
+      c.copy_list[2 + 2 * mrank] = tid;
+      c.copy_list[3 + 2 * mrank] = v;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (miss) {
-    const int v = t.vic[mrank];
-    const int old = t.expert_of[v];
-    if (old >= 0) t.slot_of[old] = -1;
-    t.expert_of[v] = tid;
-    t.slot_of[tid] = v;
-    c.copy_list[2 + 2 * mrank] = tid;
-    c.copy_list[3 + 2 * mrank] = v;
-  }
-  __syncthreads();
   if (inD) t.last_use[t.slot_of[tid]] = tick;
   __syncthreads();
   for (int i = tid; i < n; i += kBlock) {
@@ -192,11 +208,11 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
     c.copy_list[0] = MOE_MODE_SLOTS;
     c.copy_list[1] = nm;
     *c.tick = tick;
-    c.counters[C_CALLS] += 1;
-    c.counters[C_HITS] += (uint64_t)nh;
-    c.counters[C_MISSES] += (uint64_t)nm;
-    c.counters[C_PF_HITS] += (uint64_t)npf;
-    c.counters[C_BYTES] += (uint64_t)nm * c.record_bytes;
+    c.counters[C_CALLS] = t.cnt[C_CALLS] + 1;
+    c.counters[C_HITS] = t.cnt[C_HITS] + (uint64_t)nh;
+    c.counters[C_MISSES] = t.cnt[C_MISSES] + (uint64_t)nm;
+    c.counters[C_PF_HITS] = t.cnt[C_PF_HITS] + (uint64_t)npf;
+    c.counters[C_BYTES] = t.cnt[C_BYTES] + (uint64_t)nm * c.record_bytes;
   }
 }
 
