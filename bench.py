@@ -1,24 +1,33 @@
 #!/usr/bin/env python3
 """MoE-layer decode throughput of the offloaded MoE layer step on one MI355X.
 
-Default workload (one JSON line on stdout): Qwen3-30B-A3B-shaped decode in
-bf16 — 48 MoE layers, each 128 experts, top-8 with renormalised softmax,
-hidden 2048, moe ffn 768, 26 GPU slots per layer (20 %), batch 1, token hidden
-states from an AR(1) process (rho 0.9) per sequence, router bias ranked by a
-seeded Zipf(1.2) permutation.  Every expert of every layer (58 GB) sits in
-pinned, device-mapped host memory; a decode step = for each layer: router
-top-k, LRU slot ensure, miss copy from host memory, expert FFN + residual,
-all 48 layers replayed as one captured HIP graph.
+Workload (one JSON line on stdout): Qwen3-30B-A3B-shaped decode in bf16 -- 48
+MoE layers, each 128 experts, top-8 with renormalised softmax, hidden 2048,
+moe ffn 768, 26 GPU slots per layer (20 %), batch 1, token hidden states from
+an AR(1) process (rho 0.9), router bias ranked by a seeded Zipf(1.2)
+permutation.  Every expert of every layer (58 GB) sits in pinned,
+device-mapped host memory.  A step = for each layer: router logits, one
+control workgroup (top-k, LRU slot ensure, grouping), the miss copy from host
+memory, the expert FFN with combine and residual; all 48 layers replayed as
+one captured HIP graph.  Inputs are resident in HBM before the timed region.
 
-Measured: tokens/s over the timed steps; the dominant kernel's roofline (miss
-copy against the host link, HIP events around each copy launch in an eager
-pass over the same stream); the FFN against HBM; batch 8 and 32 runs; the CPU
-oracle on a bounded sample of the same workload.
+Also measured in the same run:
+  * per-kernel average durations from HIP events on the launch stream
+    (library profiling switch) over an eager pass of the same chain; the
+    gate/up kernel's HBM roofline and the miss copy's host-link fraction;
+  * a 256 MiB device-to-device copy (HBM reference, and the known-size kernel
+    that scales the rocprofv3 FETCH_SIZE / WRITE_SIZE counters);
+  * the host link: SDMA copy of 1 GiB pinned memory and the copy kernel over
+    128 records;
+  * the CPU oracle on a bounded sample of the same workload.
+--extra adds batch 8 and 32 and the router-lookahead prefetch comparison.
 """
 import argparse
 import ctypes
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -28,10 +37,27 @@ sys.path.insert(0, ROOT)
 E, K_TOP, H, F, SLOTS, LAYERS = 128, 8, 2048, 768, 26, 48
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 LINK_PEAK_GBPS = 64.0           # PCIe 5.0 x16, one direction, published
+COUNTERS = os.path.join(ROOT, "profiles", "k_gateup_vec_decode_b1_counters.md")
+FFN_SRC = os.path.join(ROOT, "expert_offload_slot_amd", "csrc", "k_ffn.hip")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def measured_traffic():
+    """HBM bytes per gate/up launch from the committed counter summary, if taken on the current kernel source."""
+    if not os.path.exists(COUNTERS):
+        return None
+    text = open(COUNTERS).read()
+    sha = hashlib.sha256(open(FFN_SRC, "rb").read()).hexdigest()
+    got = dict(re.findall(r"^(\w+):\s*(\S+)\s*$", text, re.M))
+    if got.get("source_sha256") != sha:
+        return None
+    try:
+        return int(got["fetch_bytes_per_launch"]) + int(got["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def main():
@@ -42,8 +68,9 @@ def main():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--layers", type=int, default=LAYERS)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--prof-steps", type=int, default=16)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-extra", action="store_true", help="skip the batch 8/32 runs and the link/FFN rooflines")
+    ap.add_argument("--extra", action="store_true", help="also batch 8/32 and the lookahead-prefetch comparison")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -64,6 +91,10 @@ def main():
     hip = ctypes.CDLL("libamdhip64.so")
     hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
     hip.hipMemcpyAsync.restype = ctypes.c_int
+    hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    hip.hipMemcpy.restype = ctypes.c_int
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
 
     # ---------------- layers: pinned host stores, slots, routers
     t0 = time.time()
@@ -83,20 +114,38 @@ def main():
     b_d = [torch.from_numpy(b).to(dev) for _, b in routers]
     log("setup %.0f s: %d layers, %.1f GB pinned host store" % (time.time() - t0, L, L * E * stride / 1e9))
 
-    stream = torch.cuda.current_stream()
+    # ---------------- known-size device copy: HBM reference and counter scale
+    n_cal = 256 << 20
+    a_cal = torch.empty(n_cal, dtype=torch.uint8, device=dev)
+    b_cal = torch.empty(n_cal, dtype=torch.uint8, device=dev)
+    b_cal.copy_(a_cal)
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    e0.record(stream)
+    for _ in range(3):
+        b_cal.copy_(a_cal)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    hbm_copy_gbps = 3 * 2 * n_cal / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a_cal, b_cal
+    log("device copy 256 MiB: %.0f GB/s (read + write)" % hbm_copy_gbps)
 
-    def stats_sum():
+    def stats_sum(hs=None):
         tot = {}
-        for h in handles:
+        for h in hs or handles:
             for kk, v in m.moe_offload_stats(h).items():
                 tot[kk] = tot.get(kk, 0) + v
         return tot
 
-    def run_decode(T, warm, steps, tag):
-        """graph replays of the whole step; returns (tok/s, ms/step, stats delta, chain, token stream)"""
-        xs = synth.tokens(args.seed, 100 + T, T, H, warm + steps + 24, 0.9, synth.BF16)
-        xs_d = torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16).to(dev)
-        c = m.moe_chain_create(handles, wr_d, b_d, T)
+    def token_stream(T, n):
+        xs = synth.tokens(args.seed, 100 + T, T, H, n, 0.9, synth.BF16)
+        return torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def run_decode(T, warm, steps, tag, prefetch_n=0, xs_d=None):
+        """graph replays of the whole step; returns (tok/s, ms/step, stats delta, chain, buffers, tokens)"""
+        if xs_d is None:
+            xs_d = token_stream(T, warm + steps + args.prof_steps)
+        c = m.moe_chain_create(handles, wr_d, b_d, T, prefetch_n)
         bufs = m.moe_chain_get_buffers(c)
         nbytes = T * H * 2
 
@@ -109,14 +158,14 @@ def main():
             step(s)
         torch.cuda.synchronize()
         before = stats_sum()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b_ = ev(), ev()
         torch.cuda.synchronize()
-        e0.record(stream)
+        a.record(stream)
         for s in range(warm, warm + steps):
             step(s)
-        e1.record(stream)
+        b_.record(stream)
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1)
+        ms = a.elapsed_time(b_)
         after = stats_sum()
         delta = {kk: after[kk] - before[kk] for kk in after}
         assert after["error"] == 0, "device error %d" % after["error"]
@@ -127,51 +176,43 @@ def main():
 
     tok_s, ms_step, delta, chain, bufs, xs_d = run_decode(T0, args.warmup, args.steps, "decode")
 
-    # ---------------- eager profile pass on the same stream: HIP events around every call
+    # ---------------- eager pass of the same chain with per-kernel HIP events on the launch stream
     T = T0
-    n_prof = 16
-    act = 2
-    xb, xnb, yb = bufs["x"], bufs["xn"], bufs["y"]
-    ev = lambda: torch.cuda.Event(enable_timing=True)
-    copy_ms = ffn_ms = other_ms = 0.0
-    copy_launches = ffn_launches = 0
+    for h in handles:
+        m.moe_offload_profile(h, 1)
     before = stats_sum()
-    pairs = []
     s0 = args.warmup + args.steps
-    for s in range(s0, s0 + n_prof):
-        hip.hipMemcpyAsync(xb, xs_d[s].data_ptr(), T * H * act, 3, stream.cuda_stream)
-        for l, h in enumerate(handles):
-            xl = xb + l * T * H * act
-            xnl = xnb + l * T * H * act
-            off = l * T * K_TOP * 4
-            a, b_, c_, d_ = ev(), ev(), ev(), ev()
-            a.record(stream)
-            m.moe_rmsnorm(xl, xnl, T, H, m.BF16, m.RMS_EPS, stream)
-            m.moe_route_topk(h, xnl, wr_d[l], b_d[l], T, bufs["ids"] + off, bufs["w"] + off, stream)
-            m.moe_slot_ensure(h, bufs["ids"] + off, T, bufs["slot_ids"] + off, stream)
-            b_.record(stream)
-            m.moe_copy_misses(h, stream)
-            c_.record(stream)
-            m.moe_slot_ffn(h, xnl, bufs["slot_ids"] + off, bufs["w"] + off, T, None, yb + l * T * H * act,
-                           xl, xl + T * H * act, stream)
-            d_.record(stream)
-            pairs.append((a, b_, c_, d_))
-    torch.cuda.synchronize()
-    for a, b_, c_, d_ in pairs:
-        other_ms += a.elapsed_time(b_)
-        copy_ms += b_.elapsed_time(c_)
-        ffn_ms += c_.elapsed_time(d_)
-        copy_launches += 1
-        ffn_launches += 1
+    gu_bytes = dn_bytes = 0
+    sid_host = np.empty((L, T, K_TOP), dtype=np.int32)
+    for s in range(s0, s0 + args.prof_steps):
+        hip.hipMemcpyAsync(bufs["x"], xs_d[s].data_ptr(), T * H * 2, 3, stream.cuda_stream)
+        m.moe_chain_run_eager(chain, stream)
+        torch.cuda.synchronize()
+        # algorithmic bytes of this step's FFN launches: distinct records of each call
+        assert hip.hipMemcpy(sid_host.ctypes.data, bufs["slot_ids"], sid_host.nbytes, 2) == 0
+        for l in range(L):
+            nrec = len(np.unique(sid_host[l]))
+            gu_bytes += nrec * 2 * F * H * 2 + T * H * 2 + T * K_TOP * F * 2
+            dn_bytes += nrec * F * H * 2 + T * K_TOP * F * 2 + T * K_TOP * H * 4
+    kt = {}
+    for h in handles:
+        for kind, (ms_, n_) in m.moe_offload_kernel_times(h).items():
+            a_ms, a_n = kt.get(kind, (0.0, 0))
+            kt[kind] = (a_ms + ms_, a_n + n_)
+        m.moe_offload_profile(h, 0)
     after = stats_sum()
-    prof_bytes = after["bytes_copied"] - before["bytes_copied"]
-    prof_misses = after["misses"] - before["misses"] + after["staged_copies"] - before["staged_copies"]
-    copy_avg_us = copy_ms * 1e3 / copy_launches
-    copy_gbps = prof_bytes / (copy_ms * 1e-3) / 1e9 if copy_ms > 0 else 0.0
-    ffn_avg_us = ffn_ms * 1e3 / ffn_launches
-    log("eager profile (%d steps): copy %.1f ms (%d launches, avg %.1f us, %.2f GB/s over %.1f MB), ffn %.1f ms "
-        "(avg %.1f us), route+ensure %.1f ms" % (n_prof, copy_ms, copy_launches, copy_avg_us, copy_gbps,
-                                                  prof_bytes / 1e6, ffn_ms, ffn_avg_us, other_ms))
+    copy_bytes = after["bytes_copied"] - before["bytes_copied"]
+    kernels = {kind: {"avg_us": round(ms_ * 1e3 / n_, 3), "launches": n_, "total_ms": round(ms_, 3)}
+               for kind, (ms_, n_) in kt.items() if n_}
+    log("eager profile (%d steps): " % args.prof_steps +
+        ", ".join("%s %.2f us" % (k_, v["avg_us"]) for k_, v in kernels.items()))
+    gu_ms, gu_n = kt["gateup"]
+    dn_ms, dn_n = kt["down"]
+    cp_ms, cp_n = kt["copy"]
+    gu_gbps = gu_bytes / (gu_ms * 1e-3) / 1e9
+    dn_gbps = dn_bytes / (dn_ms * 1e-3) / 1e9
+    cp_gbps = copy_bytes / (cp_ms * 1e-3) / 1e9 if cp_ms > 0 else 0.0
+    traffic = measured_traffic()
 
     result = {
         "metric": "MoE-layer decode tokens/s at 20% slots (Qwen3-30B-A3B-shaped, 48 layers, bf16)",
@@ -194,62 +235,61 @@ def main():
                          "staged_calls": delta["staged_calls"], "calls": delta["calls"],
                          "staged_copies_per_token": round(delta["staged_copies"] / (T0 * args.steps), 4),
                          "hit_rate": round(delta["hits"] / max(1, delta["hits"] + delta["misses"]), 4)},
-        "eager_profile": {"steps": n_prof, "copy_ms": round(copy_ms, 3), "ffn_ms": round(ffn_ms, 3),
-                          "route_ensure_ms": round(other_ms, 3), "copy_bytes": prof_bytes,
-                          "copied_records": prof_misses},
+        "roofline": {"bound": "hbm", "kernel": "k_gateup_vec (gate/up + SiLU, decode)",
+                     "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None if traffic is None else traffic,
+                     "avg_launch_us": round(gu_ms * 1e3 / gu_n, 3), "launches": gu_n,
+                     "algorithmic_bytes_per_launch": int(gu_bytes // gu_n)},
+        "roofline_down": {"bound": "hbm", "kernel": "k_down_vec", "achieved": round(dn_gbps, 1),
+                          "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dn_gbps / HBM_PEAK_GBPS, 4),
+                          "avg_launch_us": round(dn_ms * 1e3 / dn_n, 3),
+                          "algorithmic_bytes_per_launch": int(dn_bytes // dn_n)},
+        "roofline_copy": {"bound": "host_link", "kernel": "k_copy (demand misses)", "achieved": round(cp_gbps, 2),
+                          "peak": LINK_PEAK_GBPS, "unit": "GB/s", "frac": round(cp_gbps / LINK_PEAK_GBPS, 4),
+                          "avg_launch_us": round(cp_ms * 1e3 / max(1, cp_n), 3), "launches": cp_n,
+                          "bytes": copy_bytes},
+        "kernels_us": kernels,
+        "hbm_copy_256MiB_GBps": round(hbm_copy_gbps, 1),
     }
-    copy_roof = {"bound": "host_link", "kernel": "k_copy (moe_copy_misses)", "achieved": round(copy_gbps, 2),
-                 "peak": LINK_PEAK_GBPS, "unit": "GB/s", "frac": round(copy_gbps / LINK_PEAK_GBPS, 4),
-                 "traffic": None, "avg_launch_us": round(copy_avg_us, 2), "launches": copy_launches,
-                 "bytes": prof_bytes}
-    result["roofline"] = copy_roof
 
-    if not args.no_extra:
-        # FFN against HBM: 8 distinct resident records per call at batch 1
-        ffn_bytes_per_call = None
-        if T0 == 1:
-            ffn_bytes_per_call = K_TOP * rb + 3 * H * 2
-            gbps = ffn_bytes_per_call / (ffn_avg_us * 1e-6) / 1e9
-            result["roofline_ffn"] = {"bound": "hbm", "kernel": "moe_slot_ffn (group + gate/up + down)",
-                                      "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "avg_call_us": round(ffn_avg_us, 2),
-                                      "bytes_per_call": ffn_bytes_per_call, "traffic": None}
-        # host link: SDMA copy of 1 GiB pinned -> device, and the copy kernel moving 128 records (1.2 GB)
-        n = 1 << 30
-        src = torch.empty(n, dtype=torch.uint8, pin_memory=True)
-        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    # ---------------- host link: SDMA copy of 1 GiB pinned -> device, and the copy kernel moving 128 records
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    a, b_ = ev(), ev()
+    a.record(stream)
+    for _ in range(3):
         dst.copy_(src, non_blocking=True)
-        torch.cuda.synchronize()
+    b_.record(stream)
+    torch.cuda.synchronize()
+    sdma = 3 * n / (a.elapsed_time(b_) * 1e-3) / 1e9
+    del src, dst
+    hl = m.moe_offload_create(E, SLOTS, H, F, K_TOP, m.BF16, 16, 0, 0, handles[0], handles[0])
+    ids_all = torch.arange(E, dtype=torch.int32, device=dev).reshape(16, K_TOP)
+    sid = torch.empty_like(ids_all)
+    kern = []
+    for r in range(4):
+        m.moe_offload_reset(hl, stream)
+        m.moe_slot_ensure(hl, ids_all, 16, sid, stream)  # 128 distinct > 26 slots: all 128 staged
         a, b_ = ev(), ev()
         a.record(stream)
-        for _ in range(3):
-            dst.copy_(src, non_blocking=True)
+        m.moe_copy_misses(hl, stream)
         b_.record(stream)
         torch.cuda.synchronize()
-        sdma = 3 * n / (a.elapsed_time(b_) * 1e-3) / 1e9
-        del src, dst
-        hl = m.moe_offload_create(E, SLOTS, H, F, K_TOP, m.BF16, 16, 0, 0, handles[0], handles[0])
-        ids_all = torch.arange(E, dtype=torch.int32, device=dev).reshape(16, K_TOP)
-        sid = torch.empty_like(ids_all)
-        kern = []
-        for r in range(4):
-            m.moe_offload_reset(hl, stream)
-            m.moe_slot_ensure(hl, ids_all, 16, sid, stream)  # 128 distinct > 26 slots: all 128 staged
-            a, b_ = ev(), ev()
-            a.record(stream)
-            m.moe_copy_misses(hl, stream)
-            b_.record(stream)
-            torch.cuda.synchronize()
-            kern.append(E * rb / (a.elapsed_time(b_) * 1e-3) / 1e9)
-        m.moe_offload_destroy(hl)
-        kernel_link = max(kern[1:])
-        link = max(sdma, kernel_link)
-        result["host_link"] = {"sdma_GBps": round(sdma, 2), "copy_kernel_1p2GB_GBps": round(kernel_link, 2),
-                               "measured_link_GBps": round(link, 2),
-                               "decode_copy_frac_of_measured_link": round(copy_gbps / link, 4)}
-        log("host link: SDMA %.2f GB/s, copy kernel %.2f GB/s; decode copies at %.1f %% of measured link" %
-            (sdma, kernel_link, 100 * copy_gbps / link))
-        # other batch sizes (same layers, caches carry over)
+        kern.append(E * rb / (a.elapsed_time(b_) * 1e-3) / 1e9)
+    m.moe_offload_destroy(hl)
+    kernel_link = max(kern[1:])
+    link = max(sdma, kernel_link)
+    result["host_link"] = {"sdma_GBps": round(sdma, 2), "copy_kernel_1p2GB_GBps": round(kernel_link, 2),
+                           "measured_link_GBps": round(link, 2),
+                           "decode_copy_frac_of_measured_link": round(cp_gbps / link, 4)}
+    log("host link: SDMA %.2f GB/s, copy kernel %.2f GB/s; decode copies at %.1f %% of measured link" %
+        (sdma, kernel_link, 100 * cp_gbps / link))
+
+    if args.extra:
         for T in (8, 32):
             if T == T0:
                 continue
@@ -260,9 +300,10 @@ def main():
                                      "staged_calls": d["staged_calls"], "calls": d["calls"],
                                      "staged_copies_per_token": round(d["staged_copies"] / (T * steps), 4)}
             m.moe_chain_destroy(c2)
+        result["prefetch"] = prefetch_compare(args, m, hip, handles, run_decode, token_stream)
 
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(args, handles, routers, stride, rb, T0)
+        result["cpu_baseline"] = cpu_baseline(args, handles, routers, stride, T0)
 
     print(json.dumps(result), flush=True)
     m.moe_chain_destroy(chain)
@@ -270,7 +311,30 @@ def main():
         m.moe_offload_destroy(h)
 
 
-def cpu_baseline(args, handles, routers, stride, rb, T):
+def prefetch_compare(args, m, hip, handles, run_decode, token_stream):
+    """Router-lookahead prefetch (up to 4 experts per layer) against none, each from an empty cache on the
+    same token stream; the last step's output stream must be bitwise identical."""
+    import numpy as np
+    T, warm, steps = 1, 16, 128
+    xs_d = token_stream(T, warm + steps + args.prof_steps)
+    out, last = {}, {}
+    for n in (0, 4):
+        for h in handles:
+            m.moe_offload_reset(h)
+        ts, msps, d, c, bufs, _ = run_decode(T, warm, steps, "prefetch-%d" % n, prefetch_n=n, xs_d=xs_d)
+        xl = np.empty((T, H), dtype=np.uint16)  # the last layer's output stream x[L] of the last step
+        assert hip.hipMemcpy(xl.ctypes.data, bufs["x"] + len(handles) * T * H * 2, xl.nbytes, 2) == 0
+        last[n] = xl
+        out["prefetch_%d" % n] = {"tokens_per_s": round(ts, 2), "ms_per_step": round(msps, 3),
+                                  "demand_misses_per_token": round(d["misses"] / (T * steps), 4),
+                                  "prefetch_installs_per_token": round(d["prefetch_installs"] / (T * steps), 4),
+                                  "prefetch_hits_per_token": round(d["prefetch_hits"] / (T * steps), 4)}
+        m.moe_chain_destroy(c)
+    out["outputs_identical"] = bool(np.array_equal(last[0], last[4]))
+    return out
+
+
+def cpu_baseline(args, handles, routers, stride, T):
     """The CPU oracle, as it stands, on the first decode steps of the same token stream (all layers)."""
     import numpy as np
 

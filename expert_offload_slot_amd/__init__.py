@@ -46,6 +46,14 @@ class Stats(ctypes.Structure):
         return {n: getattr(self, n) for n, _ in self._fields_}
 
 
+KERNEL_KINDS = ("logits", "topk", "decide", "ensure", "install", "copy", "prefetch_copy", "group", "gateup",
+                "down", "combine", "stage")
+
+
+class KernelTimes(ctypes.Structure):
+    _fields_ = [("ms", ctypes.c_double * len(KERNEL_KINDS)), ("launches", ctypes.c_uint64 * len(KERNEL_KINDS))]
+
+
 class Info(ctypes.Structure):
     _fields_ = [("slot_of", ctypes.c_void_p), ("expert_of", ctypes.c_void_p), ("last_use", ctypes.c_void_p),
                 ("copy_list", ctypes.c_void_p), ("prefetch_list", ctypes.c_void_p), ("slots", ctypes.c_void_p),
@@ -87,6 +95,8 @@ def lib():
             "moe_offload_reset": ([vp, vp], i32),
             "moe_offload_query": ([vp, P(Info)], i32),
             "moe_offload_last_error": ([], ctypes.c_char_p),
+            "moe_offload_profile": ([vp, i32], i32),
+            "moe_offload_kernel_times": ([vp, P(KernelTimes)], i32),
             "moe_chain_create": ([P(vp), i32, P(vp), P(vp), P(vp), i32, i32, P(vp)], i32),
             "moe_chain_get_buffers": ([vp, P(ChainBuffers)], i32),
             "moe_chain_run": ([vp, vp], i32),
@@ -191,6 +201,17 @@ def moe_prefetch_install(h, pred_ids, T, max_n, stream=None):
 
 def moe_copy_prefetch(h, stream=None):
     return _check(lib().moe_copy_prefetch(h, _stream(stream)))
+
+
+def moe_offload_profile(h, enable):
+    return _check(lib().moe_offload_profile(h, int(bool(enable))))
+
+
+def moe_offload_kernel_times(h):
+    """{kind: (summed ms, timed launches)} for the kinds of KERNEL_KINDS."""
+    t = KernelTimes()
+    _check(lib().moe_offload_kernel_times(h, ctypes.byref(t)))
+    return {k: (t.ms[i], t.launches[i]) for i, k in enumerate(KERNEL_KINDS)}
 
 
 def moe_offload_stats(h):

@@ -55,6 +55,8 @@ struct GroupLayout {
   int words() const { return off_pairs() + max_pairs; }
 };
 
+struct Prof;  // prof.h
+
 }  // namespace moe
 
 struct moe_offload {
@@ -78,6 +80,7 @@ struct moe_offload {
   float* part;         // [max_pairs + max_tokens, H] fp32 partial expert outputs
   int32_t* scratch_i32;      // small device scratch (distinct count etc.)
   int32_t* pinned_i32;       // small pinned host scratch
+  moe::Prof* prof;           // per-kernel timing, created on first enable
 };
 
 namespace moe {

@@ -7,6 +7,7 @@
 //
 // The table is only ever written by one workgroup of one kernel at a time,
 // on the caller's compute stream: no atomics on shared state, no races.
+#include "prof.h"
 #include "table.h"
 
 namespace moe {
@@ -210,24 +211,24 @@ __global__ __launch_bounds__(kCopyThreads) void k_copy(const int32_t* __restrict
 }  // namespace
 
 hipError_t launch_ensure(moe_offload* h, const int32_t* ids, int n, int32_t* slot_ids, hipStream_t s) {
-  hipLaunchKernelGGL(k_ensure, dim3(1), dim3(kBlock), 0, s, h->cache, ids, n, slot_ids,
+  launch_k(h, MOE_K_ENSURE, k_ensure, dim3(1), dim3(kBlock), 0, s, h->cache, ids, n, slot_ids,
                      (h->flags & MOE_FLAG_AUDIT) ? 1 : 0);
   return hipGetLastError();
 }
 
 hipError_t launch_install(moe_offload* h, const int32_t* pred, int T, int max_n, hipStream_t s) {
-  hipLaunchKernelGGL(k_install, dim3(1), dim3(kBlock), 0, s, h->cache, pred, T * h->k, h->k, max_n,
+  launch_k(h, MOE_K_INSTALL, k_install, dim3(1), dim3(kBlock), 0, s, h->cache, pred, T * h->k, h->k, max_n,
                      (h->flags & MOE_FLAG_AUDIT) ? 1 : 0);
   return hipGetLastError();
 }
 
 hipError_t launch_distinct(moe_offload* h, const int32_t* ids, int n, int32_t* out_dev, hipStream_t s) {
-  hipLaunchKernelGGL(k_distinct, dim3(1), dim3(kBlock), 0, s, h->E, ids, n, out_dev);
+  launch_k(h, MOE_K_STAGE, k_distinct, dim3(1), dim3(kBlock), 0, s, h->E, ids, n, out_dev);
   return hipGetLastError();
 }
 
 hipError_t launch_stage_all(moe_offload* h, const int32_t* ids, int n, int32_t* slot_ids, hipStream_t s) {
-  hipLaunchKernelGGL(k_stage_all, dim3(64), dim3(256), 0, s, h->cache, ids, n, slot_ids);
+  launch_k(h, MOE_K_STAGE, k_stage_all, dim3(64), dim3(256), 0, s, h->cache, ids, n, slot_ids);
   return hipGetLastError();
 }
 
@@ -237,11 +238,11 @@ hipError_t launch_reset(moe_offload* h, hipStream_t s) {
 }
 
 hipError_t launch_copy(moe_offload* h, const int32_t* list, hipStream_t s) {
-  hipLaunchKernelGGL(k_copy, dim3(kCopyGrid), dim3(kCopyThreads), 0, s, list, h->host_dev, h->slots, h->staging,
-                     // whole 16-byte units: the record stride is a multiple of 4096, so rounding
-                     // the record up stays inside its own stride on both sides
-                     (uint64_t)h->record_stride, (uint64_t)((h->record_bytes + 15) / 16), h->S, h->E,
-                     h->cache.err);
+  launch_k(h, list == h->cache.pf_list ? MOE_K_PF_COPY : MOE_K_COPY, k_copy, dim3(kCopyGrid), dim3(kCopyThreads), 0,
+           s, list, h->host_dev, h->slots, h->staging,
+           // whole 16-byte units: the record stride is a multiple of 4096, so rounding
+           // the record up stays inside its own stride on both sides
+           (uint64_t)h->record_stride, (uint64_t)((h->record_bytes + 15) / 16), h->S, h->E, h->cache.err);
   return hipGetLastError();
 }
 

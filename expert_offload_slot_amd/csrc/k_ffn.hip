@@ -9,17 +9,24 @@
 //   k_group    one workgroup: counting sort of the T*k (t, j) pairs by record
 //              index -> distinct records, each with its token list (the first
 //              kInline pair ids inline, so one load trip serves a work item).
-//   k_gateup   work item = (record, 16 rows of F): gate and up rows streamed
-//              once, bf16 MFMA 16x16x32 against up to 32 gathered tokens per
-//              pass, K split over the workgroup's wavefronts and reduced in
-//              LDS in wavefront order, SiLU * up fused, h stored in bf16.
-//   k_down     work item = (record, 16 rows of H): down rows against h; fp32
-//              partial outputs per (t, j) go to the workspace.
+//              The decode chain builds the same descriptor in its control
+//              workgroup instead.
+//   gate/up + SiLU and down, one of three kernel pairs by call size:
+//     T <= kDecodeMaxT (decode): k_gateup_vec / k_down_vec, one wavefront per
+//              (record, 4 or 8 weight rows); the rows are loaded once, held in
+//              registers and met by every token of the record with the bf16
+//              pair-dot instruction.  Few tokens per record make this a
+//              weight-streaming (HBM) problem, not a matrix-core one.
+//     larger T: k_gateup / k_down, bf16 MFMA 16x16x32 tiles, work item =
+//              (record, 16 rows), K split over the workgroup's wavefronts and
+//              reduced in LDS in wavefront order, up to 32 tokens per pass.
+//     fp32 records: plain fp32 FMA kernels with the same work split.
+//   h is stored in bf16 (fp32 for fp32 records); down writes fp32 partial
+//   outputs per (t, j) to the workspace.
 //   k_combine  one workgroup per token: sum over j in order (+ shared), round,
 //              residual add, and optionally the next block's RMS norm.
 // fp8 records: e4m3 codes are widened exactly to bf16 by the hardware pair
-// converter and each 128-wide K block is scaled on the fp32 accumulator.
-// fp32 records use plain fp32 FMA kernels with the same structure.
+// converter and each 128-wide K block is scaled on its fp32 partial sum.
 //
 // Nothing depends on which slot holds an expert, on S, or on the order of the
 // tokens inside a record's list: every output element is one fixed-order sum.
@@ -28,6 +35,7 @@
 #include <algorithm>
 
 #include "grouping.h"
+#include "prof.h"
 #include "rownorm.h"
 
 namespace moe {
@@ -717,38 +725,45 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
   a.off_pairs = h->gl.off_pairs();
   // distinct records a call can touch (+ the shared expert)
   const int max_items_r = std::min(T * h->k, h->E) + (shared ? 1 : 0);
-  if (!grouped) hipLaunchKernelGGL(k_group, dim3(1), dim3(kBlock), 0, s, a);
+  if (!grouped) {
+    launch_k(h, MOE_K_GROUP, k_group, dim3(1), dim3(kBlock), 0, s, a);
+  }
+  const bool fp8 = h->dtype == MOE_FP8_E4M3_B128;
+  // gate/up and down: fp32 FMA kernels, the decode kernels (T <= kDecodeMaxT), or the MFMA kernels
+  void (*gu)(FfnArgs) = nullptr;
+  void (*dn)(FfnArgs) = nullptr;
+  dim3 g1, g2, b1, b2;
   if (h->dtype == MOE_F32) {
-    const int g1 = std::min(max_items_r * (h->F / kF32Rows), 2048);
-    const int g2 = std::min(max_items_r * (h->H / kF32Rows), 2048);
-    hipLaunchKernelGGL(k_gateup_f32, dim3(g1), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(k_down_f32, dim3(g2), dim3(256), 0, s, a);
-    hipLaunchKernelGGL(k_combine<true>, dim3(T), dim3(kRowThreads), 0, s, a, xn_next, eps);
-  } else if (T <= kDecodeMaxT) {
-    // decode: one wavefront per work item, 4 per workgroup
-    const int g1 = std::min((max_items_r * (h->F / 4) + 3) / 4, 8192);
-    const int g2 = std::min((max_items_r * (h->H / 8) + 3) / 4, 8192);
-    if (h->dtype == MOE_FP8_E4M3_B128) {
-      hipLaunchKernelGGL(k_gateup_vec<true>, dim3(g1), dim3(256), 0, s, a);
-      hipLaunchKernelGGL(k_down_vec<true>, dim3(g2), dim3(256), 0, s, a);
-    } else {
-      hipLaunchKernelGGL(k_gateup_vec<false>, dim3(g1), dim3(256), 0, s, a);
-      hipLaunchKernelGGL(k_down_vec<false>, dim3(g2), dim3(256), 0, s, a);
-    }
-    hipLaunchKernelGGL(k_combine<false>, dim3(T), dim3(kRowThreads), 0, s, a, xn_next, eps);
-  } else {
-    const int g1 = std::min(max_items_r * (h->F / kTile), 4096);
-    const int g2 = std::min(max_items_r * (h->H / kTile), 4096);
-    // wavefronts per work item: one per 128-wide K chunk, at most kSplit
-    const int w1 = std::min(kSplit, h->H / kChunk), w2 = std::min(kSplit, h->F / kChunk);
-    if (h->dtype == MOE_FP8_E4M3_B128) {
-      hipLaunchKernelGGL(k_gateup<true>, dim3(g1), dim3(64 * w1), 0, s, a);
-      hipLaunchKernelGGL(k_down<true>, dim3(g2), dim3(64 * w2), 0, s, a);
-    } else {
-      hipLaunchKernelGGL(k_gateup<false>, dim3(g1), dim3(64 * w1), 0, s, a);
-      hipLaunchKernelGGL(k_down<false>, dim3(g2), dim3(64 * w2), 0, s, a);
-    }
-    hipLaunchKernelGGL(k_combine<false>, dim3(T), dim3(kRowThreads), 0, s, a, xn_next, eps);
+    gu = k_gateup_f32;
+    dn = k_down_f32;
+    g1 = dim3(std::min(max_items_r * (h->F / kF32Rows), 2048));
+    g2 = dim3(std::min(max_items_r * (h->H / kF32Rows), 2048));
+    b1 = b2 = dim3(256);
+  } else if (T <= kDecodeMaxT) {  // one wavefront per work item, 4 per workgroup
+    gu = fp8 ? k_gateup_vec<true> : k_gateup_vec<false>;
+    dn = fp8 ? k_down_vec<true> : k_down_vec<false>;
+    g1 = dim3(std::min((max_items_r * (h->F / 4) + 3) / 4, 8192));
+    g2 = dim3(std::min((max_items_r * (h->H / 8) + 3) / 4, 8192));
+    b1 = b2 = dim3(256);
+  } else {  // wavefronts per work item: one per 128-wide K chunk, at most kSplit
+    gu = fp8 ? k_gateup<true> : k_gateup<false>;
+    dn = fp8 ? k_down<true> : k_down<false>;
+    g1 = dim3(std::min(max_items_r * (h->F / kTile), 4096));
+    g2 = dim3(std::min(max_items_r * (h->H / kTile), 4096));
+    b1 = dim3(64 * std::min(kSplit, h->H / kChunk));
+    b2 = dim3(64 * std::min(kSplit, h->F / kChunk));
+  }
+  {
+    launch_k(h, MOE_K_GATEUP, gu, g1, b1, 0, s, a);
+  }
+  {
+    launch_k(h, MOE_K_DOWN, dn, g2, b2, 0, s, a);
+  }
+  {
+    if (h->dtype == MOE_F32)
+      launch_k(h, MOE_K_COMBINE, k_combine<true>, dim3(T), dim3(kRowThreads), 0, s, a, xn_next, eps);
+    else
+      launch_k(h, MOE_K_COMBINE, k_combine<false>, dim3(T), dim3(kRowThreads), 0, s, a, xn_next, eps);
   }
   return hipGetLastError();
 }

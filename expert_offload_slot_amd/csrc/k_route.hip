@@ -16,6 +16,7 @@
 //             decode control kernel runs the same code).
 #include <math.h>
 
+#include "prof.h"
 #include "topk.h"
 
 namespace moe {
@@ -94,10 +95,10 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
 hipError_t launch_logits(moe_offload* h, const void* x, const void* wr, const float* bias, int T, hipStream_t s) {
   dim3 grid((h->E + 3) / 4, (T + kRouteTokens - 1) / kRouteTokens);
   if (h->dtype == MOE_F32)
-    hipLaunchKernelGGL(k_logits<float>, grid, dim3(256), 0, s, (const float*)x, (const float*)wr, bias, T, h->E,
+    launch_k(h, MOE_K_LOGITS, k_logits<float>, grid, dim3(256), 0, s, (const float*)x, (const float*)wr, bias, T, h->E,
                        h->H, h->logits);
   else
-    hipLaunchKernelGGL(k_logits<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)x, (const uint16_t*)wr, bias, T,
+    launch_k(h, MOE_K_LOGITS, k_logits<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)x, (const uint16_t*)wr, bias, T,
                        h->E, h->H, h->logits);
   return hipGetLastError();
 }
@@ -108,7 +109,7 @@ hipError_t launch_route(moe_offload* h, const void* x, const void* wr, const flo
   if (e != hipSuccess) return e;
   const int J = topk_lanes(h->E);
   auto kt = J == 1 ? k_topk<1> : J == 2 ? k_topk<2> : J == 4 ? k_topk<4> : J == 8 ? k_topk<8> : k_topk<16>;
-  hipLaunchKernelGGL(kt, dim3((T + 3) / 4), dim3(256), 0, s, h->logits, T, h->E, h->k, ids, w, h->cache.err);
+  launch_k(h, MOE_K_TOPK, kt, dim3((T + 3) / 4), dim3(256), 0, s, h->logits, T, h->E, h->k, ids, w, h->cache.err);
   return hipGetLastError();
 }
 

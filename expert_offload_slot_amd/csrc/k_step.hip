@@ -12,6 +12,7 @@
 // the record indices stay in LDS for the counting sort.  The slot table load
 // is issued first and is in flight during the top-k.
 #include "grouping.h"
+#include "prof.h"
 #include "table.h"
 #include "topk.h"
 
@@ -55,7 +56,7 @@ hipError_t launch_decide(moe_offload* h, int T, int32_t* ids, float* w, int32_t*
   if (T * h->k > kDecideMaxPairs) return hipErrorInvalidValue;
   const int J = topk_lanes(h->E);
   auto kd = J == 1 ? k_decide<1> : J == 2 ? k_decide<2> : J == 4 ? k_decide<4> : J == 8 ? k_decide<8> : k_decide<16>;
-  hipLaunchKernelGGL(kd, dim3(1), dim3(kBlock), 0, s, h->cache, h->logits, T, h->k, ids, w, slot_ids, h->grp,
+  launch_k(h, MOE_K_DECIDE, kd, dim3(1), dim3(kBlock), 0, s, h->cache, h->logits, T, h->k, ids, w, slot_ids, h->grp,
                      h->gl.off_pairs(), (h->flags & MOE_FLAG_AUDIT) ? 1 : 0);
   return hipGetLastError();
 }

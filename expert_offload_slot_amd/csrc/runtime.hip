@@ -6,7 +6,7 @@
 #include <algorithm>
 #include <new>
 
-#include "internal.h"
+#include "prof.h"
 
 namespace {
 
@@ -62,6 +62,13 @@ void free_all(moe_offload* h) {
   if (h->own_staging && h->staging) (void)hipFree(h->staging);
   if (h->state_block) (void)hipFree(h->state_block);
   if (h->pinned_i32) (void)hipHostFree(h->pinned_i32);
+  if (h->prof) {
+    for (auto& pair : h->prof->ev)
+      for (hipEvent_t e : pair)
+        if (e) (void)hipEventDestroy(e);
+    delete h->prof;
+    h->prof = nullptr;
+  }
 }
 
 int check_handle(const moe_offload* h) {
@@ -350,6 +357,45 @@ int moe_offload_reset(moe_offload* h, void* stream) {
   if (int rc = check_handle(h)) return rc;
   DeviceGuard g(h->device);
   HIP_TRY(moe::launch_reset(h, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_offload_profile(moe_offload* h, int32_t enable) {
+  if (int rc = check_handle(h)) return rc;
+  DeviceGuard g(h->device);
+  if (!h->prof) {
+    if (!enable) return MOE_OK;
+    h->prof = new (std::nothrow) moe::Prof();
+    if (!h->prof) return fail(MOE_ENOMEM, "moe_offload_profile: host allocation");
+    for (auto& pair : h->prof->ev)
+      for (hipEvent_t& e : pair) HIP_TRY(hipEventCreate(&e));
+  }
+  moe::Prof* p = h->prof;
+  for (int kd = 0; kd < MOE_K_N; ++kd) HIP_TRY(moe::prof_collect(p, kd));
+  if (enable) {
+    for (int kd = 0; kd < MOE_K_N; ++kd) {
+      p->ms[kd] = 0.0;
+      p->n[kd] = 0;
+    }
+  }
+  p->on = enable != 0;
+  return MOE_OK;
+}
+
+int moe_offload_kernel_times(moe_offload* h, moe_kernel_times* out) {
+  if (int rc = check_handle(h)) return rc;
+  if (!out) return fail(MOE_EINVAL, "moe_offload_kernel_times: null output");
+  DeviceGuard g(h->device);
+  for (int kd = 0; kd < MOE_K_N; ++kd) {
+    out->ms[kd] = 0.0;
+    out->launches[kd] = 0;
+  }
+  if (!h->prof) return MOE_OK;
+  for (int kd = 0; kd < MOE_K_N; ++kd) {
+    HIP_TRY(moe::prof_collect(h->prof, kd));
+    out->ms[kd] = h->prof->ms[kd];
+    out->launches[kd] = h->prof->n[kd];
+  }
   return MOE_OK;
 }
 

@@ -266,6 +266,44 @@ int moe_offload_query(const moe_offload* h, moe_info* out);
 const char* moe_offload_last_error(void);
 
 /* ------------------------------------------------------------------ */
+/* Per-kernel timing (opt-in, for measurement).                        */
+/* ------------------------------------------------------------------ */
+/* Not from the pages: a measurement aid.  While profiling is on, every
+ * kernel the handle launches on a stream that is not being captured is
+ * bracketed by two HIP events recorded on that same stream; the elapsed times
+ * accumulate per kernel kind.  The host waits for a kind's previous pair only
+ * when it records the next pair of that kind (or when the times are read).
+ * Launches inside graph capture are not timed. */
+enum moe_kernel_kind {
+  MOE_K_LOGITS = 0,   /* router logits */
+  MOE_K_TOPK = 1,     /* top-k + weights (moe_route_topk) */
+  MOE_K_DECIDE = 2,   /* fused decode control: top-k + ensure + grouping (chain) */
+  MOE_K_ENSURE = 3,   /* moe_slot_ensure */
+  MOE_K_INSTALL = 4,  /* moe_prefetch_install */
+  MOE_K_COPY = 5,     /* demand / staging copy (moe_copy_misses, prefill) */
+  MOE_K_PF_COPY = 6,  /* prefetch copy (moe_copy_prefetch) */
+  MOE_K_GROUP = 7,    /* FFN grouping by record */
+  MOE_K_GATEUP = 8,   /* FFN gate/up + SiLU */
+  MOE_K_DOWN = 9,     /* FFN down projection */
+  MOE_K_COMBINE = 10, /* top-k weighted combine (+ residual, + next norm) */
+  MOE_K_STAGE = 11,   /* prefill: distinct count, whole-layer id rewrite */
+  MOE_K_N = 12
+};
+
+typedef struct {
+  double ms[MOE_K_N];          /* summed event time per kind, milliseconds */
+  uint64_t launches[MOE_K_N];  /* timed launches per kind */
+} moe_kernel_times;
+
+/* enable != 0: start (or restart) timing with zeroed sums; 0: stop.  The
+ * first call with enable != 0 creates the handle's events.
+ * Errors: MOE_EINVAL, MOE_EHIP. */
+int moe_offload_profile(moe_offload* h, int32_t enable);
+
+/* Wait for the pending event pairs and read the sums. */
+int moe_offload_kernel_times(moe_offload* h, moe_kernel_times* out);
+
+/* ------------------------------------------------------------------ */
 /* Decode-step chain: L layers captured once into one HIP graph.       */
 /* ------------------------------------------------------------------ */
 /* xinfer-ai 0.14.6 docs/moe_offload.md, "How it works", Decode: the offloaded

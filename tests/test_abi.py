@@ -25,6 +25,16 @@ def test_struct_sizes_match_the_header_layout():
     # moe_offload_desc: 9 x 32-bit fields + 2 pointers; moe_stats: 9 x u64 + 2 x i32
     assert ctypes.sizeof(m.Desc) == 9 * 4 + 4 + 2 * 8
     assert ctypes.sizeof(m.Stats) == 9 * 8 + 2 * 4
+    # moe_kernel_times: MOE_K_N doubles + MOE_K_N u64
+    assert ctypes.sizeof(m.KernelTimes) == 2 * 8 * len(m.KERNEL_KINDS)
+
+
+def test_kernel_kinds_match_the_header_enum():
+    import re
+    text = open(m.HEADER).read()
+    kinds = dict((n, int(v)) for n, v in re.findall(r"MOE_K_(\w+)\s*=\s*(\d+)", text))
+    assert kinds.pop("N") == len(m.KERNEL_KINDS)
+    assert sorted(kinds.values()) == list(range(len(m.KERNEL_KINDS)))
 
 
 def test_last_error_is_empty_string_initially():
