@@ -123,6 +123,8 @@ size_t orc_record_bytes(int wdt, int H, int F) {
  * Inputs (bf16 or fp32) are widened exactly.  H must be a multiple of 8. */
 void orc_router_logits(const void* x, const void* wr, int wdt, const float* bias, int T, int E, int H,
                        float* logits) {
+  /* tokens are independent; threads only split them (each logit's arithmetic is unchanged) */
+#pragma omp parallel for schedule(static)
   for (int t = 0; t < T; ++t)
     for (int e = 0; e < E; ++e) {
       float p[64];

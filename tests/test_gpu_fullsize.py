@@ -1,0 +1,220 @@
+"""GPU parity of the Qwen3-30B-A3B-shaped decode chain at full size, in the
+launch configuration the benchmark times: 48 layers x 128 experts, top-8,
+hidden 2048, moe ffn 768, 26 slots per layer, bf16, every layer's 128 records
+(58 GB) in pinned host memory, the whole decode step replayed as one HIP graph
+at batch 1, 8 and 32, and the router-lookahead prefetch variant (4 installs
+per layer).
+
+Every call is teacher-forced (the oracle routes the GPU's own block input) and
+checked bit for bit on ids, slot ids, copy lists, prefetch lists, slot tables
+and counters; weights within 1e-5.  Expert outputs are sampled (a few token
+rows of a few calls, computed one by one by the oracle straight from the host
+records of the routed experts, independent of any slot map) and must be within
+2e-2 of the oracle's double sums; the residual stream is checked bitwise on
+every layer, and the slot bytes of two layers against the host records.
+"""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import expert_offload_slot_amd as m
+import oracle
+import synth
+from gpu_harness import d2h, hip, row_rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+BF16, FP8 = 1, 2
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+# ---------------------------------------------------------------------------------------------- Qwen3-30B chain
+
+class Qwen3Model:
+    L, E, k, H, F, S, MAX_T = 48, 128, 8, 2048, 768, 26, 32
+
+    def __init__(self, seed=0):
+        t0 = time.time()
+        self.seed = seed
+        self.handles = []
+        for l in range(self.L):
+            self.handles.append(m.moe_offload_create(self.E, self.S, self.H, self.F, self.k, BF16, self.MAX_T, 0,
+                                                     m.FLAG_AUDIT, None, self.handles[0] if l else None))
+        self.info = [m.moe_offload_query(h) for h in self.handles]
+        self.stride = self.info[0]["record_stride"]
+        self.rb = self.info[0]["record_bytes"]
+        for l, h in enumerate(self.handles):
+            p, _, _ = m.moe_offload_host_records(h)
+            synth.fill_records(seed, l, 0, self.E, self.H, self.F, BF16, p, self.stride)
+        self.hosts = [m.host_array(h, self.E) for h in self.handles]
+        self.routers = [synth.router(seed, l, self.E, self.H, BF16, zipf_s=1.2) for l in range(self.L)]
+        self.wr = [to_dev(w) for w, _ in self.routers]
+        self.b = [to_dev(b) for _, b in self.routers]
+        log("qwen3 model: %d layers, %.1f GB host store, %.0f s" % (self.L, self.L * self.E * self.stride / 1e9,
+                                                                     time.time() - t0))
+
+    def reset(self):
+        for h in self.handles:
+            m.moe_offload_reset(h)
+        torch.cuda.synchronize()
+        return [oracle.Cache(self.E, self.S) for _ in range(self.L)]
+
+    def close(self):
+        for h in reversed(self.handles):
+            m.moe_offload_destroy(h)
+
+
+class Chain:
+    def __init__(self, model, T, prefetch_n, tag):
+        self.mo, self.T, self.pf = model, T, prefetch_n
+        self.c = m.moe_chain_create(model.handles, model.wr, model.b, T, prefetch_n)
+        self.bufs = m.moe_chain_get_buffers(self.c)
+        self.xs = synth.tokens(model.seed, tag, T, model.H, 64, 0.9, BF16)
+
+    def run(self, s):
+        xd = to_dev(np.ascontiguousarray(self.xs[s]))
+        torch.cuda.synchronize()
+        assert hip().hipMemcpy(self.bufs["x"], xd.data_ptr(), xd.numel() * 2, 3) == 0
+        m.moe_chain_run(self.c, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+
+    def snapshot(self):
+        L, T, H, k = self.mo.L, self.T, self.mo.H, self.mo.k
+        return dict(
+            x=d2h(self.bufs["x"], (L + 1) * T * H * 2, np.uint16).reshape(L + 1, T, H),
+            xn=d2h(self.bufs["xn"], L * T * H * 2, np.uint16).reshape(L, T, H),
+            y=d2h(self.bufs["y"], L * T * H * 2, np.uint16).reshape(L, T, H),
+            ids=d2h(self.bufs["ids"], L * T * k * 4, np.int32).reshape(L, T, k),
+            w=d2h(self.bufs["w"], L * T * k * 4, np.float32).reshape(L, T, k),
+            sid=d2h(self.bufs["slot_ids"], L * T * k * 4, np.int32).reshape(L, T, k),
+        )
+
+    def close(self):
+        m.moe_chain_destroy(self.c)
+
+
+def layer_lists(mo, l):
+    i = mo.info[l]
+    lst = d2h(i["copy_list"], 4 * (2 + 2 * max(mo.S, mo.E)), np.int32)
+    pf = d2h(i["prefetch_list"], 4 * (2 + 2 * mo.S), np.int32)
+    so = d2h(i["slot_of"], 4 * mo.E, np.int32)
+    eo = d2h(i["expert_of"], 4 * mo.S, np.int32)
+    lu = d2h(i["last_use"], 8 * mo.S, np.uint64)
+    return (int(lst[0]), lst[2:2 + 2 * lst[1]].reshape(-1, 2)), pf[2:2 + 2 * pf[1]].reshape(-1, 2), (so, eo, lu)
+
+
+def replay_step(mo, caches, snap, T, prefetch_n, ffn_layers=(), ffn_tokens=()):
+    """Teacher-forced oracle for one chain step over all layers; returns the largest sampled row error."""
+    worst = 0.0
+    installs = {}
+    for l in range(mo.L):
+        xn = snap["xn"][l]
+        ref_xn = oracle.rmsnorm(snap["x"][l], BF16)
+        assert np.abs(xn.astype(np.int32) - ref_xn.astype(np.int32)).max() <= 1, l
+        wr, b = mo.routers[l]
+        ids, w, _ = oracle.route(xn, wr, b, mo.k, BF16)
+        assert np.array_equal(ids, snap["ids"][l]), (l, ids, snap["ids"][l])
+        assert np.abs(snap["w"][l] - w).max() <= 1e-5, l
+        sid, mode, pairs = caches[l].ensure(ids)
+        assert np.array_equal(sid, snap["sid"][l]), l
+        (gmode, gpairs), gpf, (so, eo, lu) = layer_lists(mo, l)
+        assert gmode == mode and np.array_equal(gpairs, pairs), (l, gmode, gpairs, mode, pairs)
+        if l in installs:
+            assert np.array_equal(gpf, installs[l]), (l, gpf, installs[l])
+        if prefetch_n and l + 1 < mo.L:
+            pred, _, _ = oracle.route(xn, mo.routers[l + 1][0], mo.routers[l + 1][1], mo.k, BF16)
+            installs[l + 1] = caches[l + 1].install(pred, prefetch_n)
+        oso, oeo, olu, _ = caches[l].state()
+        assert np.array_equal(so, oso) and np.array_equal(eo, oeo) and np.array_equal(lu, olu), l
+        if l in ffn_layers:
+            toks = [t for t in ffn_tokens if t < T]
+            _, y64 = oracle.ffn(xn[toks], BF16, mo.H, mo.F, oracle.host_records(mo.hosts[l], ids[toks]), w[toks],
+                                want_f64=True)
+            err = row_rel_err(snap["y"][l][toks], y64, BF16)
+            assert err <= 2e-2, (l, err)
+            worst = max(worst, err)
+        assert np.array_equal(snap["x"][l + 1], oracle.residual(snap["x"][l], snap["y"][l], BF16)), l
+    return worst
+
+
+def check_counters(mo, caches):
+    for l, h in enumerate(mo.handles):
+        st = m.moe_offload_stats(h)
+        c = caches[l].counters()
+        assert st["error"] == 0, (l, st["error"])
+        for key in ("calls", "hits", "misses", "staged_calls", "staged_copies", "prefetch_installs", "prefetch_hits"):
+            assert st[key] == c[key], (l, key, st[key], c[key])
+
+
+def check_slot_bytes(mo, layers):
+    for l in layers:
+        eo = d2h(mo.info[l]["expert_of"], 4 * mo.S, np.int32)
+        for s in range(mo.S):
+            if eo[s] >= 0:
+                got = d2h(mo.info[l]["slots"] + s * mo.stride, mo.rb)
+                assert np.array_equal(got, mo.hosts[l][eo[s], :mo.rb]), (l, s, eo[s])
+
+
+@pytest.fixture(scope="module")
+def qwen3():
+    mo = Qwen3Model()
+    yield mo
+    mo.close()
+
+
+def test_qwen3_chain_full_size_batches_1_8_32(qwen3):
+    mo = qwen3
+    caches = mo.reset()
+    plan = [(1, 20, {0, 9, 19}, (0, 1, 23, 47), (0,)),
+            (8, 6, {0, 5}, (0, 47), (0, 7)),
+            (32, 3, {2}, (0, 31), (0, 13, 31))]
+    for T, steps, ffn_steps, ffn_layers, toks in plan:
+        ch = Chain(mo, T, 0, 200 + T)
+        try:
+            worst = 0.0
+            for s in range(steps):
+                log("qwen3 chain T=%d step %d" % (T, s))
+                ch.run(s)
+                snap = ch.snapshot()
+                sample = s in ffn_steps
+                worst = max(worst, replay_step(mo, caches, snap, T, 0, ffn_layers if sample else (), toks))
+            log("qwen3 chain T=%d: %d steps bit-exact, sampled rows within %.2e" % (T, steps, worst))
+        finally:
+            ch.close()
+    check_counters(mo, caches)
+    check_slot_bytes(mo, (0, 47))
+
+
+def test_qwen3_lookahead_prefetch_full_size(qwen3):
+    mo = qwen3
+    T, steps = 1, 16
+    outs, misses = {}, {}
+    for n in (4, 0):
+        caches = mo.reset()
+        ch = Chain(mo, T, n, 300)
+        try:
+            xs_out = []
+            for s in range(steps):
+                log("qwen3 prefetch=%d step %d" % (n, s))
+                ch.run(s)
+                snap = ch.snapshot()
+                replay_step(mo, caches, snap, T, n, (0, 47) if s in (0, steps - 1) else (), (0,))
+                xs_out.append(snap["x"].copy())
+            outs[n] = xs_out
+        finally:
+            ch.close()
+        check_counters(mo, caches)
+        misses[n] = sum(m.moe_offload_stats(h)["misses"] for h in mo.handles)
+        if n:
+            st = [m.moe_offload_stats(h) for h in mo.handles]
+            log("prefetch: installs %d, prefetch hits %d" % (sum(x["prefetch_installs"] for x in st),
+                                                            sum(x["prefetch_hits"] for x in st)))
+    for a, b in zip(outs[4], outs[0]):
+        assert np.array_equal(a, b)
+    log("demand misses over %d steps: %d without prefetch, %d with" % (steps, misses[0], misses[4]))
+    assert misses[4] <= misses[0]
