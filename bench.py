@@ -20,7 +20,9 @@ Also measured in the same run:
   * the host link: SDMA copy of 1 GiB pinned memory and the copy kernel over
     128 records;
   * the CPU oracle on a bounded sample of the same workload.
---extra adds batch 8 and 32 and the router-lookahead prefetch comparison.
+--extra adds batch 8 and 32, the router-lookahead prefetch comparison, the
+Mixtral-8x7B-shaped layer at 2/4/6 slots and the DeepSeek-V3-shaped fp8 layer
+(decode at batch 16, the 2048-token prefill: staging copy and FFN TFLOP/s).
 """
 import argparse
 import ctypes
@@ -305,10 +307,149 @@ def main():
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args, handles, routers, stride, T0)
 
-    print(json.dumps(result), flush=True)
     m.moe_chain_destroy(chain)
     for h in reversed(handles):
         m.moe_offload_destroy(h)
+    if args.extra:  # single-layer workloads, after the 48 layers' host stores are released
+        result["mixtral_8x7b_layer"] = mixtral_layer(args, m, torch)
+        result["deepseek_v3_layer"] = deepseek_layer(args, m, torch)
+    print(json.dumps(result), flush=True)
+
+
+def layer_steps(m, torch, h, wr, b, shared, xs, T, steps, warm):
+    """Entry-point decode calls (route, ensure, copy, FFN) of one layer: tok/s over the timed calls, and the
+    per-kernel event averages of the same calls."""
+    dev = torch.device("cuda", 0)
+    st = torch.cuda.current_stream()
+    H = xs.shape[-1]
+    k = m.moe_offload_query(h)["k"]
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    sid = torch.empty_like(ids)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    def call(s):
+        x = xs[s]
+        m.moe_route_topk(h, x, wr, b, T, ids, w, st)
+        m.moe_slot_ensure(h, ids, T, sid, st)
+        m.moe_copy_misses(h, st)
+        m.moe_slot_ffn(h, x, sid, w, T, shared, y, None, None, st)
+
+    for s in range(warm):
+        call(s)
+    torch.cuda.synchronize()
+    before = m.moe_offload_stats(h)
+    m.moe_offload_profile(h, 1)
+    a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(st)
+    for s in range(warm, warm + steps):
+        call(s)
+    b_.record(st)
+    torch.cuda.synchronize()
+    kt = m.moe_offload_kernel_times(h)
+    m.moe_offload_profile(h, 0)
+    after = m.moe_offload_stats(h)
+    ms = a.elapsed_time(b_)
+    d = {kk: after[kk] - before[kk] for kk in after}
+    return {"tokens_per_s": round(T * steps * 1e3 / ms, 2), "ms_per_call": round(ms / steps, 3), "calls": steps,
+            "misses_per_call": round(d["misses"] / steps, 3), "staged_calls": d["staged_calls"],
+            "staged_copies_per_call": round(d["staged_copies"] / steps, 3),
+            "copy_GBps": round(d["bytes_copied"] / (kt["copy"][0] * 1e-3) / 1e9, 2) if kt["copy"][0] > 0 else None,
+            "kernels_us": {kind: round(v[0] * 1e3 / v[1], 2) for kind, v in kt.items() if v[1]}}
+
+
+def mixtral_layer(args, m, torch):
+    """Mixtral-8x7B-shaped layer (8 experts, top-2, hidden 4096, ffn 14336, bf16, uniform router): decode at
+    2, 4 and 6 slots."""
+    import numpy as np
+    import synth
+    E, k, H, F, seed = 8, 2, 4096, 14336, args.seed + 7
+    dev = torch.device("cuda", 0)
+    wr, b = synth.router(seed, 0, E, H, synth.BF16, zipf_s=0.0)
+    wr_d = torch.from_numpy(wr.view(np.int16)).view(torch.bfloat16).to(dev)
+    b_d = torch.from_numpy(b).to(dev)
+    out = {}
+    for S in (2, 4, 6):
+        h = m.moe_offload_create(E, S, H, F, k, m.BF16, 64, 0, 0)
+        p, stride, rb = m.moe_offload_host_records(h)
+        synth.fill_records(seed, 0, 0, E, H, F, synth.BF16, p, stride)
+        for T in (1, 8, 64):
+            xs = synth.tokens(seed, 50 + T, T, H, 24, 0.9, synth.BF16)
+            xs_d = torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16).to(dev)
+            r = layer_steps(m, torch, h, wr_d, b_d, None, xs_d, T, 16, 8)
+            out["S%d_T%d" % (S, T)] = r
+            log("mixtral S=%d T=%d: %.1f tok/s, %.3f misses/call, copy %s GB/s" %
+                (S, T, r["tokens_per_s"], r["misses_per_call"], r["copy_GBps"]))
+        m.moe_offload_destroy(h)
+    return out
+
+
+def deepseek_layer(args, m, torch):
+    """DeepSeek-V3-shaped layer (fp8 e4m3 + 128x128 scales, 256 experts + shared, top-8, hidden 7168, ffn 2048,
+    26 slots): decode at batch 16, and a 2048-token prefill that stages the whole layer."""
+    import numpy as np
+    import synth
+    E, k, H, F, S, seed = 256, 8, 7168, 2048, 26, args.seed + 9
+    dev = torch.device("cuda", 0)
+    st = torch.cuda.current_stream()
+    h = m.moe_offload_create(E, S, H, F, k, m.FP8, 2048, 0, 0)
+    p, stride, rb = m.moe_offload_host_records(h)
+    synth.fill_records(seed, 0, 0, E, H, F, synth.FP8, p, stride)
+    wr, b = synth.router(seed, 0, E, H, synth.BF16, zipf_s=1.2)
+    wr_d = torch.from_numpy(wr.view(np.int16)).view(torch.bfloat16).to(dev)
+    b_d = torch.from_numpy(b).to(dev)
+    sh_d = torch.from_numpy(synth.records(seed, 0, 1, H, F, synth.FP8, shared=True)[0]).to(dev)
+    out = {}
+    xs = synth.tokens(seed, 60, 16, H, 24, 0.0, synth.BF16)
+    xs_d = torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16).to(dev)
+    out["decode_T16"] = layer_steps(m, torch, h, wr_d, b_d, sh_d, xs_d, 16, 8, 4)
+    log("deepseek decode T=16: %.1f tok/s, %d/%d calls staged" % (out["decode_T16"]["tokens_per_s"],
+                                                                  out["decode_T16"]["staged_calls"], 8))
+    T = 2048
+    x = synth.tokens(seed, 70, T, H, 1, 0.0, synth.BF16)[0]
+    xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    sid = torch.empty_like(ids)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    m.moe_route_topk(h, xd, wr_d, b_d, T, ids, w, st)
+    a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(st)
+    staged = m.moe_prefill_stage(h, ids, T, sid, st)
+    b_.record(st)
+    torch.cuda.synchronize()
+    stage_ms = a.elapsed_time(b_)
+    m.moe_slot_ffn(h, xd, sid, w, T, sh_d, y, None, None, st)  # warm
+    torch.cuda.synchronize()
+    reps = 5
+    m.moe_offload_profile(h, 1)
+    a.record(st)
+    for _ in range(reps):
+        m.moe_slot_ffn(h, xd, sid, w, T, sh_d, y, None, None, st)
+    b_.record(st)
+    torch.cuda.synchronize()
+    kt = m.moe_offload_kernel_times(h)
+    m.moe_offload_profile(h, 0)
+    ffn_ms = a.elapsed_time(b_) / reps
+    flop_gu = 2 * (T * k + T) * 2 * F * H
+    flop_dn = 2 * (T * k + T) * F * H
+    cnt = np.bincount(ids.cpu().numpy().reshape(-1), minlength=E)
+    wbytes = (int((cnt > 0).sum()) + 1) * rb
+    gu_us = kt["gateup"][0] * 1e3 / kt["gateup"][1]
+    dn_us = kt["down"][0] * 1e3 / kt["down"][1]
+    out["prefill_T2048"] = {
+        "staged": staged, "stage_ms": round(stage_ms, 2), "stage_GBps": round(E * rb / (stage_ms * 1e-3) / 1e9, 2),
+        "ffn_ms": round(ffn_ms, 3), "ffn_TFLOPs": round((flop_gu + flop_dn) / (ffn_ms * 1e-3) / 1e12, 1),
+        "gateup_us": round(gu_us, 1), "gateup_TFLOPs": round(flop_gu / (gu_us * 1e-6) / 1e12, 1),
+        "down_us": round(dn_us, 1), "down_TFLOPs": round(flop_dn / (dn_us * 1e-6) / 1e12, 1),
+        "mfma_peak_TFLOPs": 2500.0, "mfma_dtype": "bf16 (fp8 codes widened exactly)",
+        "frac_of_mfma_peak": round((flop_gu + flop_dn) / (ffn_ms * 1e-3) / 1e12 / 2500.0, 4),
+        "hbm_bound_ms": round(wbytes / 8e12 * 1e3, 3), "tokens_per_expert_max": int(cnt.max()),
+        "experts_used": int((cnt > 0).sum())}
+    log("deepseek prefill T=2048: stage %.1f ms (%.1f GB/s), ffn %.2f ms = %.1f TFLOP/s" %
+        (stage_ms, E * rb / (stage_ms * 1e-3) / 1e9, ffn_ms, (flop_gu + flop_dn) / (ffn_ms * 1e-3) / 1e12))
+    m.moe_offload_destroy(h)
+    return out
 
 
 def prefetch_compare(args, m, hip, handles, run_decode, token_stream):

@@ -3,7 +3,11 @@
 // router-lookahead prefetch variant with a predictor stream and a copy stream.
 // Per layer on the compute stream: router logits; one control workgroup (top-k,
 // ensure, FFN grouping); the miss copy; the FFN kernels with the combine,
-// residual and the next layer's norm.
+// residual and the next layer's norm.  In the lookahead variant the logits
+// launch also runs the next layer's router on this layer's input, and the
+// control workgroup also installs the predicted experts into the next layer;
+// only the prefetch copy runs on a side stream.  (Calls with more than
+// kDecideMaxPairs (t, j) pairs use the separate kernels and a predictor stream.)
 //
 // xinfer-ai 0.14.6 docs/moe_offload.md, "How it works", Decode (the step stays
 // inside a captured graph, no host sync); FreeToken issue #677, "Proposal"
@@ -66,40 +70,47 @@ hipError_t issue(moe_chain* c, hipStream_t cs) {
     // layer 0 normalises the step input; every later input is normalised by the
     // previous layer's combine, in the same order (identical bits)
     if (l == 0) CHK(moe::launch_rmsnorm(X(c, 0), XN(c, 0), T, c->H, h->dtype, kRmsEps, cs));
-    if (look) {  // fork: layer l+1's router on layer l's router input
-      CHK(hipEventRecord(c->ev_x[l], cs));
-      CHK(hipStreamWaitEvent(c->sp, c->ev_x[l], 0));
-      CHK(moe::launch_route(c->layers[l + 1], XN(c, l), c->wr[l + 1], c->bias[l + 1], T, c->pred + R(c, l + 1),
-                            c->wpred + R(c, l + 1), c->sp));
-      CHK(hipEventRecord(c->ev_pred[l + 1], c->sp));
-    }
-    if (fused) {  // logits, then top-k + ensure + FFN grouping in one workgroup
-      CHK(moe::launch_logits(h, XN(c, l), c->wr[l], c->bias[l], T, cs));
-      CHK(moe::launch_decide(h, T, c->ids + R(c, l), c->w + R(c, l), c->sid + R(c, l), cs));
+    moe_offload* hn = look ? c->layers[l + 1] : nullptr;
+    if (fused) {
+      // router logits (and, for the lookahead, the next layer's router on the same
+      // input in the same launch), then one control workgroup: top-k, ensure, FFN
+      // grouping (and the next layer's prediction and install)
+      CHK(moe::launch_logits(h, XN(c, l), c->wr[l], c->bias[l], T, cs, hn, look ? c->wr[l + 1] : nullptr,
+                             look ? c->bias[l + 1] : nullptr));
+      CHK(moe::launch_decide(h, T, c->ids + R(c, l), c->w + R(c, l), c->sid + R(c, l), cs, hn,
+                             look ? c->pred + R(c, l + 1) : nullptr, look ? c->prefetch_n : 0));
     } else {
+      if (look) {  // fork: layer l+1's router on layer l's router input
+        CHK(hipEventRecord(c->ev_x[l], cs));
+        CHK(hipStreamWaitEvent(c->sp, c->ev_x[l], 0));
+        CHK(moe::launch_route(hn, XN(c, l), c->wr[l + 1], c->bias[l + 1], T, c->pred + R(c, l + 1),
+                              c->wpred + R(c, l + 1), c->sp));
+        CHK(hipEventRecord(c->ev_pred[l + 1], c->sp));
+      }
       CHK(moe::launch_route(h, XN(c, l), c->wr[l], c->bias[l], T, c->ids + R(c, l), c->w + R(c, l), cs));
       CHK(moe::launch_ensure(h, c->ids + R(c, l), n, c->sid + R(c, l), cs));
-    }
-    if (look) {  // join, then install into layer l+1 on the compute stream
-      CHK(hipStreamWaitEvent(cs, c->ev_pred[l + 1], 0));
-      CHK(moe::launch_install(c->layers[l + 1], c->pred + R(c, l + 1), T, c->prefetch_n, cs));
+      if (look) {  // join, then install into layer l+1 on the compute stream
+        CHK(hipStreamWaitEvent(cs, c->ev_pred[l + 1], 0));
+        CHK(moe::launch_install(hn, c->pred + R(c, l + 1), T, c->prefetch_n, cs));
+      }
     }
     if (pf && l >= 1) CHK(hipStreamWaitEvent(cs, c->ev_pf[l], 0));  // this layer's prefetch copy first
     CHK(moe::launch_copy(h, h->cache.copy_list, cs));
     if (look) {  // prefetch copy for layer l+1 behind layer l's demand copy
       CHK(hipEventRecord(c->ev_demand[l], cs));
       CHK(hipStreamWaitEvent(c->sf, c->ev_demand[l], 0));
-      moe_offload* hn = c->layers[l + 1];
       CHK(moe::launch_copy(hn, hn->cache.pf_list, c->sf));
       CHK(hipEventRecord(c->ev_pf[l + 1], c->sf));
     }
     CHK(moe::launch_ffn(h, XN(c, l), c->sid + R(c, l), c->w + R(c, l), T, c->shared[l], Y(c, l), X(c, l), X(c, l + 1),
                         l + 1 < c->L ? XN(c, l + 1) : nullptr, kRmsEps, cs, fused));
   }
-  if (pf && c->L > 1) {  // rejoin the side streams
-    CHK(hipEventRecord(c->ev_sp_done, c->sp));
+  if (pf && c->L > 1) {  // rejoin the side streams (the predictor stream is used only without fusion)
+    if (!fused) {
+      CHK(hipEventRecord(c->ev_sp_done, c->sp));
+      CHK(hipStreamWaitEvent(cs, c->ev_sp_done, 0));
+    }
     CHK(hipEventRecord(c->ev_sf_done, c->sf));
-    CHK(hipStreamWaitEvent(cs, c->ev_sp_done, 0));
     CHK(hipStreamWaitEvent(cs, c->ev_sf_done, 0));
   }
   return hipSuccess;

@@ -11,7 +11,7 @@ namespace moe {
 
 constexpr int kMaxExperts = 1024;   // one ensure thread per expert
 constexpr int kMaxTopK = 16;
-constexpr int kCopyGrid = 256;      // copy kernel: fixed grid (one workgroup per CU)
+constexpr int kCopyGrid = 64;       // copy kernel: fixed grid; 48+ workgroups already fill the host link
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 4;      // 16-byte loads in flight per thread
 constexpr int kRouteTokens = 4;     // tokens per router wave
@@ -90,7 +90,9 @@ int set_error(int code, const char* msg);
 
 // launchers (return hipError_t of the launch)
 hipError_t launch_reset(moe_offload* h, hipStream_t s);
-hipError_t launch_logits(moe_offload* h, const void* x, const void* wr, const float* bias, int T, hipStream_t s);
+// h->logits = x . wr^T + bias; with hn, also hn->logits = x . wrn^T + biasn in the same launch
+hipError_t launch_logits(moe_offload* h, const void* x, const void* wr, const float* bias, int T, hipStream_t s,
+                         moe_offload* hn = nullptr, const void* wrn = nullptr, const float* biasn = nullptr);
 hipError_t launch_route(moe_offload* h, const void* x, const void* wr, const float* bias, int T, int32_t* ids,
                         float* w, hipStream_t s);
 hipError_t launch_ensure(moe_offload* h, const int32_t* ids, int n, int32_t* slot_ids, hipStream_t s);
@@ -104,9 +106,12 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
                       const void* shared, void* y, const void* residual, void* x_next, void* xn_next, float eps,
                       hipStream_t s, bool grouped = false);
 // Decode control step in one workgroup: top-k of h->logits (launch_logits first),
-// ensure, and the FFN grouping.  Needs T * k <= kDecideMaxPairs.
+// ensure, and the FFN grouping.  With hn (max_n > 0): also the top-k of
+// hn->logits (the lookahead prediction, ids to pred) and the prefetch install
+// of up to max_n experts into hn.  Needs T * k <= kDecideMaxPairs.
 constexpr int kDecideMaxPairs = 512;
-hipError_t launch_decide(moe_offload* h, int T, int32_t* ids, float* w, int32_t* slot_ids, hipStream_t s);
+hipError_t launch_decide(moe_offload* h, int T, int32_t* ids, float* w, int32_t* slot_ids, hipStream_t s,
+                         moe_offload* hn = nullptr, int32_t* pred = nullptr, int max_n = 0);
 hipError_t launch_rmsnorm(const void* x, void* out, int T, int H, int dtype, float eps, hipStream_t s);
 
 }  // namespace moe

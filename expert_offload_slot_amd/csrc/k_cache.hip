@@ -17,96 +17,19 @@ namespace {
 __global__ __launch_bounds__(kBlock) void k_ensure(CacheDev c, const int32_t* __restrict__ ids, int n,
                                                    int32_t* __restrict__ slot_ids, int audit) {
   __shared__ SharedTable t;
+  __shared__ uint64_t vkey[kMaxExperts];
   load_table(c, t);
-  ensure_body(c, t, ids, n, slot_ids, nullptr, audit);
+  ensure_body(c, t, ids, n, slot_ids, nullptr, audit, vkey);
 }
 
 // ---------------------------------------------------------------- prefetch install
 __global__ __launch_bounds__(kBlock) void k_install(CacheDev c, const int32_t* __restrict__ pred, int n, int k,
                                                     int max_n, int audit) {
   __shared__ SharedTable t;
-  const int tid = threadIdx.x;
-  const int E = c.E, S = c.S;
+  __shared__ uint64_t ckey[kMaxExperts];
+  __shared__ uint64_t vkey[kMaxExperts];
   load_table(c, t);
-  if (tid < E) {
-    t.flag[tid] = 0;  // tokens predicting the expert
-    t.aux[tid] = k;   // best top-k position
-  }
-  if (tid == 0) t.bad = 0;
-  __syncthreads();
-  for (int i = tid; i < n; i += kBlock) {
-    const int e = pred[i];
-    if ((unsigned)e >= (unsigned)E) {
-      t.bad = 1;
-    } else {
-      atomicAdd(&t.flag[e], 1);
-      atomicMin(&t.aux[e], i % k);
-    }
-  }
-  __syncthreads();
-  if (t.bad) {
-    if (tid == 0) {
-      atomicOr(c.err, MOE_DEV_ERR_BAD_ID);
-      c.pf_list[0] = MOE_MODE_SLOTS;
-      c.pf_list[1] = 0;
-    }
-    return;
-  }
-  // candidates: predicted and not resident, ordered by (count desc, best asc, id asc)
-  const bool cand = tid < E && t.flag[tid] > 0 && t.slot_of[tid] < 0;
-  int nc, nv;
-  (void)block_rank(cand, t.wave, &nc);
-  int crank = 0;
-  if (cand) {
-    const int cn = t.flag[tid], cb = t.aux[tid];
-    for (int e2 = 0; e2 < E; ++e2) {
-      if (!(t.flag[e2] > 0 && t.slot_of[e2] < 0)) continue;
-      const int n2 = t.flag[e2], b2 = t.aux[e2];
-      crank += (n2 > cn || (n2 == cn && (b2 < cb || (b2 == cb && e2 < tid)))) ? 1 : 0;
-    }
-  }
-  // victims: slots not holding a predicted expert, in ensure's order
-  bool elig = false;
-  int vrank = 0;
-  if (tid < S) {
-    const int ex = t.expert_of[tid];
-    const bool occ = ex >= 0;
-    elig = !occ || t.flag[ex] == 0;
-    if (elig) {
-      const uint64_t lu = t.last_use[tid];
-      for (int s2 = 0; s2 < S; ++s2) {
-        const int ex2 = t.expert_of[s2];
-        const bool occ2 = ex2 >= 0;
-        if (occ2 && t.flag[ex2] > 0) continue;
-        vrank += key_before(occ2, t.last_use[s2], s2, occ, lu, tid) ? 1 : 0;
-      }
-    }
-  }
-  (void)block_rank(elig, t.wave, &nv);
-  int m = max_n < nc ? max_n : nc;
-  m = m < nv ? m : nv;
-  if (cand && crank < m) t.cand[crank] = tid;
-  if (elig && vrank < m) t.vic[vrank] = tid;
-  __syncthreads();
-  if (tid < m) {
-    const int e = t.cand[tid], v = t.vic[tid];
-    const int old = t.expert_of[v];
-    if (old >= 0) t.slot_of[old] = -1;
-    t.expert_of[v] = e;
-    t.slot_of[e] = v;
-    t.last_use[v] = 0;
-    c.pf_list[2 + 2 * tid] = e;
-    c.pf_list[3 + 2 * tid] = v;
-  }
-  __syncthreads();
-  store_table(c, t);
-  if (audit) audit_table(c, t, false);
-  if (tid == 0) {
-    c.pf_list[0] = MOE_MODE_SLOTS;
-    c.pf_list[1] = m;
-    c.counters[C_PF_INSTALLS] += (uint64_t)m;
-    c.counters[C_BYTES] += (uint64_t)m * c.record_bytes;
-  }
+  install_body(c, t, pred, n, k, max_n, audit, ckey, vkey);
 }
 
 // ---------------------------------------------------------------- prefill helpers

@@ -9,12 +9,16 @@
 // wavefront with 16-byte loads.
 //
 // Two kernels, no communication between workgroups inside a kernel:
-//   k_logits  grid (ceil(E/4), ceil(T/4)); a wavefront owns one expert and up
-//             to 4 tokens, so the router row is loaded once for them.
+//   k_logits  grid (ceil(E/4), ceil(T/4), routers); a wavefront owns one expert
+//             and up to 4 tokens, so the router row is loaded once for them.
+//             A second router (the next layer's, for the lookahead) can ride
+//             in the same launch.
 //   k_topk    one wavefront per token: radix select of the k largest keys,
 //             then the softmax over the k chosen logits (topk.h; the fused
 //             decode control kernel runs the same code).
 #include <math.h>
+
+#include <algorithm>
 
 #include "prof.h"
 #include "topk.h"
@@ -38,17 +42,28 @@ __device__ __forceinline__ void load8(const uint16_t* p, float v[8]) {
   v[4] = bf16_lo(a.z); v[5] = bf16_hi(a.z); v[6] = bf16_lo(a.w); v[7] = bf16_hi(a.w);
 }
 
+// One router's logits: weights [E][H], bias [E], output [T][E].
 template <typename A>
-__global__ __launch_bounds__(256) void k_logits(const A* __restrict__ x, const A* __restrict__ wr,
-                                                const float* __restrict__ bias, int T, int E, int H,
-                                                float* __restrict__ logits) {
+struct RouterJob {
+  const A* wr;
+  const float* bias;
+  float* logits;
+  int E;
+};
+
+// blockIdx.z picks the router (a layer's own, or the next layer's for the
+// lookahead prediction on the same input).
+template <typename A>
+__global__ __launch_bounds__(256) void k_logits(const A* __restrict__ x, RouterJob<A> j0, RouterJob<A> j1, int T,
+                                                int H) {
+  const RouterJob<A> j = blockIdx.z == 0 ? j0 : j1;
   const int lane = threadIdx.x & 63;
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int t0 = blockIdx.y * kRouteTokens;
   const int nt = min(kRouteTokens, T - t0);
-  if (e >= E) return;
+  if (e >= j.E) return;
   float acc[kRouteTokens] = {0.f, 0.f, 0.f, 0.f};
-  const A* wrow = wr + (size_t)e * H;
+  const A* wrow = j.wr + (size_t)e * H;
 #pragma unroll 4
   for (int c = lane; c * 8 < H; c += 64) {
     float wv8[8];
@@ -68,7 +83,7 @@ __global__ __launch_bounds__(256) void k_logits(const A* __restrict__ x, const A
     float p = acc[tt];
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) p = p + __shfl_xor(p, o);
-    if (lane == 0 && tt < nt) logits[(size_t)(t0 + tt) * E + e] = p + bias[e];
+    if (lane == 0 && tt < nt) j.logits[(size_t)(t0 + tt) * j.E + e] = p + j.bias[e];
   }
 }
 
@@ -92,14 +107,24 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
 
 }  // namespace
 
-hipError_t launch_logits(moe_offload* h, const void* x, const void* wr, const float* bias, int T, hipStream_t s) {
-  dim3 grid((h->E + 3) / 4, (T + kRouteTokens - 1) / kRouteTokens);
+namespace {
+template <typename A>
+void logits_jobs(moe_offload* h, const void* x, const void* wr, const float* bias, moe_offload* hn,
+                 const void* wrn, const float* biasn, int T, hipStream_t s) {
+  RouterJob<A> j0{(const A*)wr, bias, h->logits, h->E};
+  RouterJob<A> j1 = hn ? RouterJob<A>{(const A*)wrn, biasn, hn->logits, hn->E} : j0;
+  const int E = hn ? std::max(h->E, hn->E) : h->E;
+  dim3 grid((E + 3) / 4, (T + kRouteTokens - 1) / kRouteTokens, hn ? 2 : 1);
+  launch_k(h, MOE_K_LOGITS, k_logits<A>, grid, dim3(256), 0, s, (const A*)x, j0, j1, T, h->H);
+}
+}  // namespace
+
+hipError_t launch_logits(moe_offload* h, const void* x, const void* wr, const float* bias, int T, hipStream_t s,
+                         moe_offload* hn, const void* wrn, const float* biasn) {
   if (h->dtype == MOE_F32)
-    launch_k(h, MOE_K_LOGITS, k_logits<float>, grid, dim3(256), 0, s, (const float*)x, (const float*)wr, bias, T, h->E,
-                       h->H, h->logits);
+    logits_jobs<float>(h, x, wr, bias, hn, wrn, biasn, T, s);
   else
-    launch_k(h, MOE_K_LOGITS, k_logits<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)x, (const uint16_t*)wr, bias, T,
-                       h->E, h->H, h->logits);
+    logits_jobs<uint16_t>(h, x, wr, bias, hn, wrn, biasn, T, s);
   return hipGetLastError();
 }
 

@@ -11,13 +11,6 @@
 
 namespace moe {
 
-// victim order key: (occupied, last_use, slot) ascending
-__device__ __forceinline__ bool key_before(bool occ_a, uint64_t lu_a, int a, bool occ_b, uint64_t lu_b, int b) {
-  if (occ_a != occ_b) return !occ_a;
-  if (lu_a != lu_b) return lu_a < lu_b;
-  return a < b;
-}
-
 // victim order as one integer: (occupied, last_use, slot) ascending.  last_use
 // is a call count, far below 2^53.
 __device__ __forceinline__ uint64_t victim_key(bool occ, uint64_t lu, int slot) {
@@ -29,13 +22,8 @@ struct SharedTable {
   int expert_of[kMaxExperts];
   uint64_t last_use[kMaxExperts];
   int flag[kMaxExperts];   // ensure: expert in D; install: tokens predicting it
-  union {
-    struct {
-      int aux[kMaxExperts];    // install: best top-k position
-      int cand[kMaxExperts];   // install: candidate expert by rank
-    };
-    uint64_t vkey[kMaxExperts];  // ensure: victim key of each slot (~0 if not eligible)
-  };
+  int aux[kMaxExperts];    // install: best top-k position
+  int cand[kMaxExperts];   // install: candidate expert by rank
   int vic[kMaxExperts];    // victim slot by rank
   int wave[4 * kWaves];
   int bad;
@@ -106,9 +94,11 @@ __device__ __forceinline__ void audit_table(const CacheDev& c, const SharedTable
 //   |D| >  S: staged call; the table is untouched, residents are read in place
 //             and each missing expert e is copied to staging record S + e.
 //   an id outside [0, E): nothing changes, slot ids are 0, error bit set.
-// All threads of the block must call it; it ends with the table stored back.
+// vkey: LDS scratch of S entries.  All threads of the block must call it; it
+// ends with the table stored back.
 __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, const int32_t* ids, int n,
-                                            int32_t* __restrict__ slot_ids, int32_t* slot_lds, int audit) {
+                                            int32_t* __restrict__ slot_ids, int32_t* slot_lds, int audit,
+                                            uint64_t* vkey) {
   const int tid = threadIdx.x;
   const int E = c.E, S = c.S;
   if (tid < E) t.flag[tid] = 0;
@@ -171,15 +161,15 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
     if (tid < S) {
       const int ex = t.expert_of[tid];
       const bool occ = ex >= 0;
-      t.vkey[tid] = (!occ || !t.flag[ex]) ? victim_key(occ, t.last_use[tid], tid) : ~0ull;
+      vkey[tid] = (!occ || !t.flag[ex]) ? victim_key(occ, t.last_use[tid], tid) : ~0ull;
     }
     __syncthreads();
     if (tid < S) {
-      const uint64_t mine = t.vkey[tid];
+      const uint64_t mine = vkey[tid];
       if (mine != ~0ull) {
         int rank = 0;
 #pragma unroll 8
-        for (int s2 = 0; s2 < S; ++s2) rank += t.vkey[s2] < mine ? 1 : 0;
+        for (int s2 = 0; s2 < S; ++s2) rank += vkey[s2] < mine ? 1 : 0;
         if (rank < nm) t.vic[rank] = tid;
       }
     }
@@ -213,6 +203,98 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
     c.counters[C_MISSES] = t.cnt[C_MISSES] + (uint64_t)nm;
     c.counters[C_PF_HITS] = t.cnt[C_PF_HITS] + (uint64_t)npf;
     c.counters[C_BYTES] = t.cnt[C_BYTES] + (uint64_t)nm * c.record_bytes;
+  }
+}
+
+// Prefetch install (FreeToken issue #677, "Proposal", Install) for the n = T*k
+// predicted ids of a call (pred may live in LDS or global memory).  The table
+// must already be in `t` (load_table, then a barrier).
+//   candidates: predicted experts that are not resident, in (tokens predicting
+//               it desc, best top-k position asc, id asc) order;
+//   victims:    slots not holding a predicted expert, in ensure's order;
+//   the first min(max_n, candidates, victims) pairs are installed with
+//   last_use = 0 (evicted first) and written to the prefetch copy list.
+// ckey: LDS scratch of E entries, vkey: of S entries.  All threads of the block
+// must call it; it ends with the table stored back.
+__device__ __forceinline__ void install_body(const CacheDev& c, SharedTable& t, const int32_t* pred, int n, int k,
+                                             int max_n, int audit, uint64_t* ckey, uint64_t* vkey) {
+  const int tid = threadIdx.x;
+  const int E = c.E, S = c.S;
+  if (tid < E) {
+    t.flag[tid] = 0;  // tokens predicting the expert
+    t.aux[tid] = k;   // best top-k position
+  }
+  if (tid == 0) t.bad = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += kBlock) {
+    const int e = pred[i];
+    if ((unsigned)e >= (unsigned)E) {
+      t.bad = 1;
+    } else {
+      atomicAdd(&t.flag[e], 1);
+      atomicMin(&t.aux[e], i % k);
+    }
+  }
+  __syncthreads();
+  if (t.bad) {
+    if (tid == 0) {
+      atomicOr(c.err, MOE_DEV_ERR_BAD_ID);
+      c.pf_list[0] = MOE_MODE_SLOTS;
+      c.pf_list[1] = 0;
+    }
+    return;  // block-uniform
+  }
+  // candidate key, ascending = install order (count < 2^20, position < 16, id < 1024)
+  const bool cand = tid < E && t.flag[tid] > 0 && t.slot_of[tid] < 0;
+  if (tid < E)
+    ckey[tid] = cand ? ((uint64_t)(0xfffffu - (uint32_t)t.flag[tid]) << 40) | ((uint64_t)t.aux[tid] << 20) |
+                           (uint64_t)tid
+                     : ~0ull;
+  bool elig = false;
+  if (tid < S) {
+    const int ex = t.expert_of[tid];
+    const bool occ = ex >= 0;
+    elig = !occ || t.flag[ex] == 0;
+    vkey[tid] = elig ? victim_key(occ, t.last_use[tid], tid) : ~0ull;
+  }
+  int nc, nv;
+  (void)block_rank(cand, t.wave, &nc);  // its barriers also publish ckey / vkey
+  (void)block_rank(elig, t.wave, &nv);
+  int m = max_n < nc ? max_n : nc;
+  m = m < nv ? m : nv;
+  if (cand) {
+    const uint64_t mine = ckey[tid];
+    int crank = 0;
+#pragma unroll 8
+    for (int e2 = 0; e2 < E; ++e2) crank += ckey[e2] < mine ? 1 : 0;
+    if (crank < m) t.cand[crank] = tid;
+  }
+  if (elig) {
+    const uint64_t mine = vkey[tid];
+    int vrank = 0;
+#pragma unroll 8
+    for (int s2 = 0; s2 < S; ++s2) vrank += vkey[s2] < mine ? 1 : 0;
+    if (vrank < m) t.vic[vrank] = tid;
+  }
+  __syncthreads();
+  if (tid < m) {
+    const int e = t.cand[tid], v = t.vic[tid];
+    const int old = t.expert_of[v];
+    if (old >= 0) t.slot_of[old] = -1;
+    t.expert_of[v] = e;
+    t.slot_of[e] = v;
+    t.last_use[v] = 0;
+    c.pf_list[2 + 2 * tid] = e;
+    c.pf_list[3 + 2 * tid] = v;
+  }
+  __syncthreads();
+  store_table(c, t);
+  if (audit) audit_table(c, t, false);
+  if (tid == 0) {
+    c.pf_list[0] = MOE_MODE_SLOTS;
+    c.pf_list[1] = m;
+    c.counters[C_PF_INSTALLS] = t.cnt[C_PF_INSTALLS] + (uint64_t)m;
+    c.counters[C_BYTES] = t.cnt[C_BYTES] + (uint64_t)m * c.record_bytes;
   }
 }
 
