@@ -1,6 +1,7 @@
 // Grouping of a call's (token, choice) pairs by record for the expert FFN:
 // one workgroup counting-sorts the n = T*k record indices into the group
-// descriptor (internal.h, GroupLayout) that the FFN work items read.
+// descriptor (internal.h, GroupLayout) that the FFN work items read, with each
+// record's first prefill-GEMM tile (a prefix sum of ceil(count / kGemmTok)).
 #pragma once
 
 #include "blockops.h"
@@ -19,7 +20,7 @@ struct GroupShared {
 // All threads of the block must call it.  The order of the pairs inside a
 // record's list is not fixed, and nothing downstream depends on it.
 __device__ __forceinline__ void group_body(const int32_t* rec, int n, int nb, int32_t* __restrict__ grp,
-                                           int off_pairs, int32_t* err, GroupShared& g) {
+                                           int off_pairs, int off_tiles, int32_t* err, GroupShared& g) {
   const int tid = threadIdx.x;
   for (int b = tid; b < 2 * kMaxExperts; b += kBlock) g.cnt[b] = 0;
   __syncthreads();
@@ -36,6 +37,13 @@ __device__ __forceinline__ void group_body(const int32_t* rec, int n, int nb, in
   int tot_pairs, nr;
   const int pre = block_excl_sum(c0 + c1, g.wave, &tot_pairs);
   const int pre_nz = block_excl_sum((c0 > 0) + (c1 > 0), g.wave, &nr);
+  const int t0 = (c0 + kGemmTok - 1) / kGemmTok, t1 = (c1 + kGemmTok - 1) / kGemmTok;
+  int tot_tiles;
+  const int pre_t = block_excl_sum(t0 + t1, g.wave, &tot_tiles);
+  int32_t* tiles = grp + off_tiles;
+  if (c0 > 0) tiles[pre_nz] = pre_t;
+  if (c1 > 0) tiles[pre_nz + (c0 > 0)] = pre_t + t0;
+  if (tid == 0) tiles[nr] = tot_tiles;
   int32_t* pairs = grp + off_pairs;
   // cnt now holds each record's start in the pair array, cur its cursor
   g.cnt[2 * tid] = pre;

@@ -15,10 +15,6 @@ constexpr int kCopyGrid = 64;       // copy kernel: fixed grid; 48+ workgroups a
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 4;      // 16-byte loads in flight per thread
 constexpr int kRouteTokens = 4;     // tokens per router wave
-constexpr int kTile = 16;           // MFMA output rows per work item
-constexpr int kChunk = 128;         // K elements per MFMA group (4 x 32)
-constexpr int kTokGroup = 32;       // tokens per pass over a weight tile (MFMA column groups of 16)
-constexpr int kNG = kTokGroup / 16; // column groups per pass
 constexpr int kF32Rows = 64;        // rows per work item on the fp32 path
 
 // counters[] layout (device, uint64)
@@ -44,15 +40,19 @@ struct CacheDev {
 //     [0] record index, [1] token count n, [2] offset of its pair ids in the
 //     pair array, [3 .. 3 + kInline) its first kInline pair ids (t*k + j)
 //   pair array at kRecWords * (1 + max_recs): all pair ids grouped by record
+//   tile starts at off_tiles(): record r's first kGemmTok-pair tile, and the
+//     total at index nr (the prefill GEMM's work list)
 // so a work item gets its record and (usually all) its tokens in one load trip.
 constexpr int kRecWords = 32;
 constexpr int kInline = kRecWords - 3;
+constexpr int kGemmTok = 64;  // pairs per prefill GEMM tile
 struct GroupLayout {
   int max_recs;   // distinct records a call can touch
   int max_pairs;  // max_tokens * k
   int off_rec(int r) const { return kRecWords * (1 + r); }
   int off_pairs() const { return kRecWords * (1 + max_recs); }
-  int words() const { return off_pairs() + max_pairs; }
+  int off_tiles() const { return off_pairs() + max_pairs; }
+  int words() const { return off_tiles() + max_recs + 1; }
 };
 
 struct Prof;  // prof.h

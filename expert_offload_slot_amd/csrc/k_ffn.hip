@@ -60,7 +60,7 @@ struct FfnArgs {
   void* x_next;
   int32_t* err;
   int T, k, H, F, S, E;
-  int off_pairs;
+  int off_pairs, off_tiles;
 };
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)rn_to_bf16(f); }
@@ -69,7 +69,7 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 // ------------------------------------------------------------------ grouping
 __global__ __launch_bounds__(kBlock) void k_group(FfnArgs a) {
   __shared__ GroupShared g;
-  group_body(a.slot_ids, a.T * a.k, a.S + a.E, a.grp, a.off_pairs, a.err, g);
+  group_body(a.slot_ids, a.T * a.k, a.S + a.E, a.grp, a.off_pairs, a.off_tiles, a.err, g);
 }
 
 // A work item's record (pointer, token count); its pair ids come from the same
@@ -107,53 +107,21 @@ __device__ __forceinline__ int pair_token(const FfnArgs& a, int p) {
   return p < routed ? p / a.k : p - routed;
 }
 
-// ------------------------------------------------------------------ MFMA operand loads
-// Lane l of a 16x16x32 MFMA supplies row (l & 15) and 8 consecutive K values of
-// one of 4 K slices.  Over a 128-wide K chunk lane l reads 32 contiguous values
-// at K offset 32*(l >> 4) of its row and feeds values [8i, 8i+8) to MFMA i; the
-// B operand uses the same mapping, so the 4 MFMAs together cover the chunk.
-
-__device__ __forceinline__ void load_a_bf16(const uint16_t* p, bf16x8 a[4]) {
-  const uint4* q = reinterpret_cast<const uint4*>(p);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) a[i] = __builtin_bit_cast(bf16x8, q[i]);
-}
-
 template <bool HI>
 __device__ __forceinline__ uint32_t cvt2(uint32_t d) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)d, 1.0f, HI));
 }
 
-__device__ __forceinline__ void load_a_fp8(const uint8_t* p, bf16x8 a[4]) {
-  const uint4 q0 = reinterpret_cast<const uint4*>(p)[0];
-  const uint4 q1 = reinterpret_cast<const uint4*>(p)[1];
-  const uint32_t d[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint4 u;
-    u.x = cvt2<false>(d[2 * i]);
-    u.y = cvt2<true>(d[2 * i]);
-    u.z = cvt2<false>(d[2 * i + 1]);
-    u.w = cvt2<true>(d[2 * i + 1]);
-    a[i] = __builtin_bit_cast(bf16x8, u);
-  }
-}
-
-__device__ __forceinline__ void load_b_bf16(const uint16_t* p, bool valid, bf16x8 b[4]) {
-  if (valid) {
-    const uint4* q = reinterpret_cast<const uint4*>(p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) b[i] = __builtin_bit_cast(bf16x8, q[i]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) b[i] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-  }
-}
-
-__device__ __forceinline__ f32x4 mfma4(const bf16x8 a[4], const bf16x8 b[4], f32x4 acc) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[i], acc, 0, 0, 0);
-  return acc;
+// 16 e4m3 codes widened exactly to 16 bf16
+__device__ __forceinline__ void widen16(uint4 q, uint4& lo, uint4& hi) {
+  lo.x = cvt2<false>(q.x);
+  lo.y = cvt2<true>(q.x);
+  lo.z = cvt2<false>(q.y);
+  lo.w = cvt2<true>(q.y);
+  hi.x = cvt2<false>(q.z);
+  hi.y = cvt2<true>(q.z);
+  hi.z = cvt2<false>(q.w);
+  hi.w = cvt2<true>(q.w);
 }
 
 __device__ __forceinline__ f32x4 fma4(float s, f32x4 v, f32x4 acc) {
@@ -165,222 +133,262 @@ __device__ __forceinline__ f32x4 fma4(float s, f32x4 v, f32x4 acc) {
   return r;
 }
 
-template <bool FP8>
-__device__ __forceinline__ void load_chunk(const uint8_t* mat, int K, int row, int kc, int kq, bf16x8 a[4]) {
-  if (FP8)
-    load_a_fp8(mat + (uint64_t)row * K + kc + kq, a);
-  else
-    load_a_bf16(reinterpret_cast<const uint16_t*>(mat) + (uint64_t)row * K + kc + kq, a);
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// ------------------------------------------------------------------ gate/up (bf16, fp8)
-// A work item is (record, 16 rows of F) for gate and up together.  Its K = H
-// reduction is split over the nw wavefronts of the workgroup (128-wide chunk c
-// goes to wavefront c % nw); each wavefront issues the loads of two of its
-// chunks before their MFMAs, and the partial sums are added in LDS in
-// wavefront order, so every output is one fixed-order sum.
-constexpr int kSplit = 8;
+// ------------------------------------------------------------------ prefill GEMMs (bf16, fp8)
+// Many tokens per record: a call becomes a grouped GEMM over record tiles.
+// Work item = (tile of kGemmTok pairs of one record, kGemmRows weight rows);
+// the items of a call follow the tile starts of the group descriptor (routed
+// records, then the shared expert's ceil(T / kGemmTok) tiles).  A 256-thread
+// workgroup stages kGemmK-wide K slices of its weight rows and of its gathered
+// token rows through LDS with coalesced 16-byte loads (fp8 codes widened
+// exactly to bf16 on the way in), loads the next slice into registers while
+// the current one feeds bf16 MFMA 16x16x32 tiles, and each wavefront owns a
+// 32 x 32 corner of the 64 x 64 output tile.  fp8: one scale per 128 x 128
+// block, so one per K slice and matrix, multiplies the slice's partial sum.
+// MFMA operands: lane l supplies row (l & 15) and the 8 K values at
+// 8 * (l >> 4) of a 32-wide K step, for A (weight rows) and B (tokens) alike;
+// the result holds rows 4 * (l >> 4) + i and token column (l & 15).
+constexpr int kGemmRows = 64;         // weight rows per tile
+constexpr int kGemmK = 64;            // K per LDS slice
+constexpr int kLdsRow = kGemmK + 8;   // LDS row stride in bf16: rows start on different banks
 
-template <bool FP8>
-__global__ __launch_bounds__(64 * kSplit) void k_gateup(FfnArgs a) {
-  __shared__ float red[kSplit][kNG][2][4][64];  // [wave][token group][gate/up][row][lane]
+struct GemmItem {
+  Item it;
+  int r;   // record block (nr = the shared expert)
+  int n0;  // first pair of the tile within the record
+  int rt;  // row tile
+};
+
+__device__ __forceinline__ GemmItem gemm_item(const FfnArgs& a, int nr, int routed_tiles, int row_tiles, int item) {
+  GemmItem g;
+  const int ti = item / row_tiles;
+  g.rt = item - ti * row_tiles;
+  if (ti < routed_tiles) {
+    const int32_t* tiles = a.grp + a.off_tiles;  // strictly increasing: every record has a pair
+    int lo = 0, hi = nr - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tiles[mid] <= ti) lo = mid;
+      else hi = mid - 1;
+    }
+    g.r = lo;
+    g.n0 = (ti - tiles[lo]) * kGemmTok;
+  } else {
+    g.r = nr;
+    g.n0 = (ti - routed_tiles) * kGemmTok;
+  }
+  g.it = item_record(a, nr, g.r);
+  return g;
+}
+
+__device__ __forceinline__ int gemm_tiles(const FfnArgs& a, int nr, int* routed) {
+  *routed = a.grp[a.off_tiles + nr];
+  return *routed + (a.shared ? (a.T + kGemmTok - 1) / kGemmTok : 0);
+}
+
+// one K slice of NM weight matrices (kGemmRows rows each, row stride K elements)
+// and of the tile's token rows, from memory into registers
+template <bool FP8, int NM>
+struct Slice {
+  uint4 a[FP8 ? NM : 2 * NM];  // bf16: 2 per matrix (rows tid/8 and tid/8 + 32); fp8: 1 (row tid/4)
+  uint4 b[2];                  // token rows tid/8 and tid/8 + 32
+
+  __device__ __forceinline__ void load(const uint8_t* w0, uint64_t mat, int K, int k0,
+                                       const uint16_t* const bp[2]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      if (FP8) {
+        a[m] = *reinterpret_cast<const uint4*>(w0 + m * mat + (uint64_t)(tid >> 2) * K + k0 + (tid & 3) * 16);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          a[2 * m + q] = *reinterpret_cast<const uint4*>(
+              w0 + m * mat + ((uint64_t)((tid >> 3) + 32 * q) * K + k0 + (tid & 7) * 8) * 2);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) b[q] = bp[q] ? *reinterpret_cast<const uint4*>(bp[q] + k0) : make_uint4(0, 0, 0, 0);
+  }
+
+  __device__ __forceinline__ void store(uint16_t (*As)[kGemmRows][kLdsRow], uint16_t (*Bs)[kLdsRow]) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      if (FP8) {
+        uint4 lo, hi;
+        widen16(a[m], lo, hi);
+        uint4* d = reinterpret_cast<uint4*>(&As[m][tid >> 2][(tid & 3) * 16]);
+        d[0] = lo;
+        d[1] = hi;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          *reinterpret_cast<uint4*>(&As[m][(tid >> 3) + 32 * q][(tid & 7) * 8]) = a[2 * m + q];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) *reinterpret_cast<uint4*>(&Bs[(tid >> 3) + 32 * q][(tid & 7) * 8]) = b[q];
+  }
+};
+
+// acc[m][i][j] += the wavefront's 32 x 32 corner (row tiles i, token tiles j) of
+// matrix m over the LDS slice; fp8: the slice's sum is scaled by sc[m] first
+template <bool FP8, int NM>
+__device__ __forceinline__ void gemm_slice(const uint16_t (*As)[kGemmRows][kLdsRow], const uint16_t (*Bs)[kLdsRow],
+                                           const float* sc, f32x4 acc[NM][2][2]) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
+  const int r0 = 32 * (wv >> 1) + (lane & 15), c0 = 32 * (wv & 1) + (lane & 15), kq = 8 * (lane >> 4);
+  f32x4 part[NM][2][2];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) part[m][i][j] = FP8 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[m][i][j];
+#pragma unroll
+  for (int ks = 0; ks < kGemmK; ks += 32) {
+    bf16x8 bf[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) bf[j] = *reinterpret_cast<const bf16x8*>(&Bs[c0 + 16 * j][ks + kq]);
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[m][r0 + 16 * i][ks + kq]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) part[m][i][j] = mfma(af, bf[j], part[m][i][j]);
+      }
+  }
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[m][i][j] = FP8 ? fma4(sc[m], part[m][i][j], acc[m][i][j]) : part[m][i][j];
+}
+
+// gate/up: C[f][p] = W[f] . x[token(p)] for gate and up, h = silu(gate) * up in bf16
+template <bool FP8>
+__global__ __launch_bounds__(256) void k_gemm_gu(FfnArgs a) {
+  __shared__ uint16_t As[2][kGemmRows][kLdsRow];
+  __shared__ uint16_t Bs[kGemmTok][kLdsRow];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nr = a.grp[0];
-  const int nrt = nr + (a.shared ? 1 : 0);
-  const int FT = a.F / kTile;
-  const int H = a.H, F = a.F;
-  const int nchunk = H / kChunk;
-  const uint64_t mat = (uint64_t)F * H * (FP8 ? 1 : 2);
+  int routed;
+  const int ntiles = gemm_tiles(a, nr, &routed);
+  const int H = a.H, F = a.F, RT = F / kGemmRows, nk = H / kGemmK;
+  const uint64_t esz = FP8 ? 1 : 2;
+  const uint64_t mat = (uint64_t)F * H * esz;
   const int nsc = (F / 128) * (H / 128);
-  const int kq = 32 * (lane >> 4);
   const uint16_t* __restrict__ x = (const uint16_t*)a.x;
   uint16_t* __restrict__ hb = (uint16_t*)a.hbuf;
-  for (int item = blockIdx.x; item < nrt * FT; item += gridDim.x) {
-    const int r = item / FT, f0 = (item % FT) * kTile;
-    const Item it = item_record(a, nr, r);
-    const int row = f0 + (lane & 15);
-    const float* sc = reinterpret_cast<const float*>(it.rec + 3 * mat);
-    const int sbase = (f0 / 128) * (H / 128);
-    for (int tg0 = 0; tg0 < it.n; tg0 += kTokGroup) {
-      const int ng = min(kNG, (it.n - tg0 + 15) / 16);
-      int tok[kNG];
-      bool tv[kNG];
+  for (int item = blockIdx.x; item < ntiles * RT; item += gridDim.x) {
+    const GemmItem g = gemm_item(a, nr, routed, RT, item);
+    const int m0 = g.rt * kGemmRows, n_here = min(kGemmTok, g.it.n - g.n0);
+    const uint16_t* bp[2];
 #pragma unroll
-      for (int g = 0; g < kNG; ++g) {
-        const int idx = tg0 + 16 * g + (lane & 15);
-        tv[g] = g < ng && idx < it.n;
-        tok[g] = tv[g] ? pair_token(a, item_pair(a, it, r, idx)) : 0;
-      }
-      f32x4 ag[kNG], au[kNG];
+    for (int q = 0; q < 2; ++q) {
+      const int idx = (tid >> 3) + 32 * q;
+      bp[q] = idx < n_here ? x + (uint64_t)pair_token(a, item_pair(a, g.it, g.r, g.n0 + idx)) * H + (tid & 7) * 8
+                           : nullptr;
+    }
+    const uint8_t* w0 = g.it.rec + (uint64_t)m0 * H * esz;
+    const float* sc = reinterpret_cast<const float*>(g.it.rec + 3 * mat) + (m0 / 128) * (H / 128);
+    f32x4 acc[2][2][2];
 #pragma unroll
-      for (int g = 0; g < kNG; ++g) {
-        ag[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-        au[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-      for (int c0 = wv; c0 < nchunk; c0 += 2 * nw) {
-        const int c1 = c0 + nw;
-        const bool two = c1 < nchunk;
-        bf16x8 wg0[4], wu0[4], wg1[4], wu1[4];
-        load_chunk<FP8>(it.rec, H, row, c0 * kChunk, kq, wg0);
-        load_chunk<FP8>(it.rec + mat, H, row, c0 * kChunk, kq, wu0);
-        if (two) {
-          load_chunk<FP8>(it.rec, H, row, c1 * kChunk, kq, wg1);
-          load_chunk<FP8>(it.rec + mat, H, row, c1 * kChunk, kq, wu1);
-        }
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int g = 0; g < kNG; ++g) {
-          if (g < ng) {
-            bf16x8 b0[4];
-            load_b_bf16(x + (uint64_t)tok[g] * H + c0 * kChunk + kq, tv[g], b0);
-            if (FP8) {
-              const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-              ag[g] = fma4(sc[sbase + c0], mfma4(wg0, b0, z), ag[g]);
-              au[g] = fma4(sc[nsc + sbase + c0], mfma4(wu0, b0, z), au[g]);
-            } else {
-              ag[g] = mfma4(wg0, b0, ag[g]);
-              au[g] = mfma4(wu0, b0, au[g]);
-            }
-            if (two) {
-              bf16x8 b1[4];
-              load_b_bf16(x + (uint64_t)tok[g] * H + c1 * kChunk + kq, tv[g], b1);
-              if (FP8) {
-                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                ag[g] = fma4(sc[sbase + c1], mfma4(wg1, b1, z), ag[g]);
-                au[g] = fma4(sc[nsc + sbase + c1], mfma4(wu1, b1, z), au[g]);
-              } else {
-                ag[g] = mfma4(wg1, b1, ag[g]);
-                au[g] = mfma4(wu1, b1, au[g]);
-              }
-            }
-          }
-        }
-      }
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int g = 0; g < kNG; ++g) {
-        if (g < ng) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            red[wv][g][0][i][lane] = ag[g][i];
-            red[wv][g][1][i][lane] = au[g][i];
-          }
-        }
-      }
+        for (int j = 0; j < 2; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    Slice<FP8, 2> sl;
+    sl.load(w0, mat, H, 0, bp);
+    for (int kb = 0; kb < nk; ++kb) {
+      __syncthreads();  // the previous slice (or item) is no longer read
+      sl.store(As, Bs);
       __syncthreads();
-      for (int g = wv; g < ng; g += nw) {  // wavefront wv finishes token groups wv, wv + nw, ...
-        const int idx = tg0 + 16 * g + (lane & 15);
-        if (idx < it.n) {
-          const int p = item_pair(a, it, r, idx);
+      if (kb + 1 < nk) sl.load(w0, mat, H, (kb + 1) * kGemmK, bp);
+      const float s2[2] = {FP8 ? sc[(kb * kGemmK) / 128] : 1.f, FP8 ? sc[nsc + (kb * kGemmK) / 128] : 1.f};
+      gemm_slice<FP8, 2>(As, Bs, s2, acc);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int idx = 32 * (wv & 1) + 16 * j + (lane & 15);
+      if (idx < n_here) {
+        const int p = item_pair(a, g.it, g.r, g.n0 + idx);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int f = m0 + 32 * (wv >> 1) + 16 * i + 4 * (lane >> 4);
           uint16_t hv[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float gs = red[0][g][0][i][lane], us = red[0][g][1][i][lane];
-            for (int w = 1; w < nw; ++w) {
-              gs = gs + red[w][g][0][i][lane];
-              us = us + red[w][g][1][i][lane];
-            }
-            hv[i] = f32_to_bf16(silu_mul(gs, us));
-          }
+          for (int e = 0; e < 4; ++e) hv[e] = f32_to_bf16(silu_mul(acc[0][i][j][e], acc[1][i][j][e]));
           uint2 st;
           st.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
           st.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
-          *reinterpret_cast<uint2*>(hb + (uint64_t)p * F + f0 + 4 * (lane >> 4)) = st;
+          *reinterpret_cast<uint2*>(hb + (uint64_t)p * F + f) = st;
         }
       }
-      __syncthreads();
     }
   }
 }
 
-// ------------------------------------------------------------------ down (bf16, fp8)
-// A work item is (record, 16 rows of H); K = F split like gate/up; fp32
-// partial outputs per (t, j) go to the workspace for the combine kernel.
+// down: part[p][r] = Wd[r] . h[p] (fp32 partial outputs)
 template <bool FP8>
-__global__ __launch_bounds__(64 * kSplit) void k_down(FfnArgs a) {
-  __shared__ float red[kSplit][kNG][4][64];  // [wave][token group][row][lane]
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
+__global__ __launch_bounds__(256) void k_gemm_dn(FfnArgs a) {
+  __shared__ uint16_t As[1][kGemmRows][kLdsRow];
+  __shared__ uint16_t Bs[kGemmTok][kLdsRow];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nr = a.grp[0];
-  const int nrt = nr + (a.shared ? 1 : 0);
-  const int HT = a.H / kTile;
-  const int H = a.H, F = a.F;
-  const int nchunk = F / kChunk;
-  const uint64_t mat = (uint64_t)F * H * (FP8 ? 1 : 2);
+  int routed;
+  const int ntiles = gemm_tiles(a, nr, &routed);
+  const int H = a.H, F = a.F, RT = H / kGemmRows, nk = F / kGemmK;
+  const uint64_t esz = FP8 ? 1 : 2;
+  const uint64_t mat = (uint64_t)F * H * esz;
   const int nsc = (F / 128) * (H / 128);
-  const int kq = 32 * (lane >> 4);
   const uint16_t* __restrict__ hb = (const uint16_t*)a.hbuf;
   float* __restrict__ part = a.part;
-  for (int item = blockIdx.x; item < nrt * HT; item += gridDim.x) {
-    const int r = item / HT, ht = item % HT, h0 = ht * kTile;
-    const Item it = item_record(a, nr, r);
-    const int row = h0 + (lane & 15);
-    const float* sc = reinterpret_cast<const float*>(it.rec + 3 * mat) + 2 * nsc + (h0 / 128) * (F / 128);
-    for (int tg0 = 0; tg0 < it.n; tg0 += kTokGroup) {
-      const int ng = min(kNG, (it.n - tg0 + 15) / 16);
-      int pr[kNG];
-      bool tv[kNG];
+  for (int item = blockIdx.x; item < ntiles * RT; item += gridDim.x) {
+    const GemmItem g = gemm_item(a, nr, routed, RT, item);
+    const int m0 = g.rt * kGemmRows, n_here = min(kGemmTok, g.it.n - g.n0);
+    const uint16_t* bp[2];
 #pragma unroll
-      for (int g = 0; g < kNG; ++g) {
-        const int idx = tg0 + 16 * g + (lane & 15);
-        tv[g] = g < ng && idx < it.n;
-        pr[g] = tv[g] ? item_pair(a, it, r, idx) : 0;
-      }
-      f32x4 acc[kNG];
+    for (int q = 0; q < 2; ++q) {
+      const int idx = (tid >> 3) + 32 * q;
+      bp[q] = idx < n_here ? hb + (uint64_t)item_pair(a, g.it, g.r, g.n0 + idx) * F + (tid & 7) * 8 : nullptr;
+    }
+    const uint8_t* w0 = g.it.rec + 2 * mat + (uint64_t)m0 * F * esz;
+    const float* sc = reinterpret_cast<const float*>(g.it.rec + 3 * mat) + 2 * nsc + (m0 / 128) * (F / 128);
+    f32x4 acc[1][2][2];
 #pragma unroll
-      for (int g = 0; g < kNG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int c0 = wv; c0 < nchunk; c0 += 2 * nw) {
-        const int c1 = c0 + nw;
-        const bool two = c1 < nchunk;
-        bf16x8 wd0[4], wd1[4];
-        load_chunk<FP8>(it.rec + 2 * mat, F, row, c0 * kChunk, kq, wd0);
-        if (two) load_chunk<FP8>(it.rec + 2 * mat, F, row, c1 * kChunk, kq, wd1);
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int g = 0; g < kNG; ++g) {
-          if (g < ng) {
-            bf16x8 b0[4];
-            load_b_bf16(hb + (uint64_t)pr[g] * F + c0 * kChunk + kq, tv[g], b0);
-            if (FP8) {
-              const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-              acc[g] = fma4(sc[c0], mfma4(wd0, b0, z), acc[g]);
-            } else {
-              acc[g] = mfma4(wd0, b0, acc[g]);
-            }
-            if (two) {
-              bf16x8 b1[4];
-              load_b_bf16(hb + (uint64_t)pr[g] * F + c1 * kChunk + kq, tv[g], b1);
-              if (FP8) {
-                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                acc[g] = fma4(sc[c1], mfma4(wd1, b1, z), acc[g]);
-              } else {
-                acc[g] = mfma4(wd1, b1, acc[g]);
-              }
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int g = 0; g < kNG; ++g)
-        if (g < ng) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) red[wv][g][i][lane] = acc[g][i];
-        }
+      for (int j = 0; j < 2; ++j) acc[0][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    Slice<FP8, 1> sl;
+    sl.load(w0, mat, F, 0, bp);
+    for (int kb = 0; kb < nk; ++kb) {
       __syncthreads();
-      for (int g = wv; g < ng; g += nw) {
-        const int idx = tg0 + 16 * g + (lane & 15);
-        if (idx < it.n) {
-          const int p = item_pair(a, it, r, idx);
-          float4 o;
-          float* ov = reinterpret_cast<float*>(&o);
+      sl.store(As, Bs);
+      __syncthreads();
+      if (kb + 1 < nk) sl.load(w0, mat, F, (kb + 1) * kGemmK, bp);
+      const float s1[1] = {FP8 ? sc[(kb * kGemmK) / 128] : 1.f};
+      gemm_slice<FP8, 1>(As, Bs, s1, acc);
+    }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float v = red[0][g][i][lane];
-            for (int w = 1; w < nw; ++w) v = v + red[w][g][i][lane];
-            ov[i] = v;
-          }
-          *reinterpret_cast<float4*>(part + (uint64_t)p * H + h0 + 4 * (lane >> 4)) = o;
+    for (int j = 0; j < 2; ++j) {
+      const int idx = 32 * (wv & 1) + 16 * j + (lane & 15);
+      if (idx < n_here) {
+        const int p = item_pair(a, g.it, g.r, g.n0 + idx);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int r = m0 + 32 * (wv >> 1) + 16 * i + 4 * (lane >> 4);
+          *reinterpret_cast<float4*>(part + (uint64_t)p * H + r) =
+              make_float4(acc[0][i][j][0], acc[0][i][j][1], acc[0][i][j][2], acc[0][i][j][3]);
         }
       }
-      __syncthreads();
     }
   }
 }
@@ -723,6 +731,7 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
   a.S = h->S;
   a.E = h->E;
   a.off_pairs = h->gl.off_pairs();
+  a.off_tiles = h->gl.off_tiles();
   // distinct records a call can touch (+ the shared expert)
   const int max_items_r = std::min(T * h->k, h->E) + (shared ? 1 : 0);
   if (!grouped) {
@@ -745,13 +754,15 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
     g1 = dim3(std::min((max_items_r * (h->F / 4) + 3) / 4, 8192));
     g2 = dim3(std::min((max_items_r * (h->H / 8) + 3) / 4, 8192));
     b1 = b2 = dim3(256);
-  } else {  // wavefronts per work item: one per 128-wide K chunk, at most kSplit
-    gu = fp8 ? k_gateup<true> : k_gateup<false>;
-    dn = fp8 ? k_down<true> : k_down<false>;
-    g1 = dim3(std::min(max_items_r * (h->F / kTile), 4096));
-    g2 = dim3(std::min(max_items_r * (h->H / kTile), 4096));
-    b1 = dim3(64 * std::min(kSplit, h->H / kChunk));
-    b2 = dim3(64 * std::min(kSplit, h->F / kChunk));
+  } else {  // grouped GEMM over (record tile, 64 rows) work items; the grid strides over the call's list
+    gu = fp8 ? k_gemm_gu<true> : k_gemm_gu<false>;
+    dn = fp8 ? k_gemm_dn<true> : k_gemm_dn<false>;
+    // tiles of a call: at most one partial tile per record on top of the full ones
+    const int tiles = (T * h->k) / kGemmTok + std::min(T * h->k, h->S + h->E) +
+                      (shared ? (T + kGemmTok - 1) / kGemmTok : 0);
+    g1 = dim3(std::min(tiles * (h->F / kGemmRows), 2048));
+    g2 = dim3(std::min(tiles * (h->H / kGemmRows), 2048));
+    b1 = b2 = dim3(256);
   }
   {
     launch_k(h, MOE_K_GATEUP, gu, g1, b1, 0, s, a);

@@ -85,6 +85,17 @@ def test_fp8_block_scaled_with_shared_expert(S):
     run_sequence(12, S, 3, 256, 384, 2, 0.0, 31, 12, [1, 5, 16], shared=True)
 
 
+def test_fp8_prefill_gemm_ragged_tiles():
+    # > 64 tokens per call: the grouped GEMM; records with partial 64-pair tiles,
+    # several K slices and row tiles, the shared expert's own tiles
+    run_sequence(12, 6, 3, 256, 384, 2, 1.2, 33, 3, [100, 130, 65], shared=True)
+
+
+def test_bf16_prefill_gemm_one_hot_record():
+    # every token routed to the same experts (k = E = S): one long record per expert
+    run_sequence(2, 2, 2, 128, 256, 1, 0.0, 34, 2, [257, 64])
+
+
 def test_fp8_without_shared_expert():
     run_sequence(10, 5, 2, 128, 256, 2, 1.2, 32, 10, [2, 7])
 
