@@ -3,7 +3,9 @@
 // router-lookahead prefetch variant with a predictor stream and a copy stream.
 // Per layer on the compute stream: router logits; one control workgroup (top-k,
 // ensure, FFN grouping); the miss copy; the FFN kernels with the combine,
-// residual and the next layer's norm.  In the lookahead variant the logits
+// residual and the next layer's norm.  For small bf16/fp8 batches the combine
+// of layer l is instead recomputed by every workgroup of layer l+1's router
+// launch, which also writes y_l, x_{l+1} and xn_{l+1} (same bits).  In the lookahead variant the logits
 // launch also runs the next layer's router on this layer's input, and the
 // control workgroup also installs the predicted experts into the next layer;
 // only the prefetch copy runs on a side stream.  (Calls with more than
@@ -64,6 +66,9 @@ hipError_t issue(moe_chain* c, hipStream_t cs) {
   const int T = c->T, n = c->T * c->k;
   const bool pf = c->prefetch_n > 0;
   const bool fused = n <= moe::kDecideMaxPairs;
+  // the previous layer's combine rides in the next router launch (small bf16 / fp8 decode batches)
+  const moe_offload* l0 = c->layers[0];
+  const bool fuse_cl = fused && l0->dtype != MOE_F32 && c->H <= moe::kFusedCombineMaxH && T <= 8;
   for (int l = 0; l < c->L; ++l) {
     moe_offload* h = c->layers[l];
     const bool look = pf && l + 1 < c->L;
@@ -75,8 +80,24 @@ hipError_t issue(moe_chain* c, hipStream_t cs) {
       // router logits (and, for the lookahead, the next layer's router on the same
       // input in the same launch), then one control workgroup: top-k, ensure, FFN
       // grouping (and the next layer's prediction and install)
-      CHK(moe::launch_logits(h, XN(c, l), c->wr[l], c->bias[l], T, cs, hn, look ? c->wr[l + 1] : nullptr,
-                             look ? c->bias[l + 1] : nullptr));
+      if (fuse_cl && l > 0) {  // with layer l-1's combine, which forms this layer's input xn_l
+        moe::CombineSrc cb;
+        cb.part = c->layers[l - 1]->part;
+        cb.w = c->w + R(c, l - 1);
+        cb.T = T;
+        cb.k = c->k;
+        cb.shared = c->shared[l - 1] != nullptr;
+        cb.y = Y(c, l - 1);
+        cb.residual = X(c, l - 1);
+        cb.x_next = X(c, l);
+        cb.xn_next = XN(c, l);
+        cb.eps = kRmsEps;
+        CHK(moe::launch_combine_logits(h, cb, c->wr[l], c->bias[l], T, cs, hn, look ? c->wr[l + 1] : nullptr,
+                                       look ? c->bias[l + 1] : nullptr));
+      } else {
+        CHK(moe::launch_logits(h, XN(c, l), c->wr[l], c->bias[l], T, cs, hn, look ? c->wr[l + 1] : nullptr,
+                               look ? c->bias[l + 1] : nullptr));
+      }
       CHK(moe::launch_decide(h, T, c->ids + R(c, l), c->w + R(c, l), c->sid + R(c, l), cs, hn,
                              look ? c->pred + R(c, l + 1) : nullptr, look ? c->prefetch_n : 0));
     } else {
@@ -103,7 +124,7 @@ hipError_t issue(moe_chain* c, hipStream_t cs) {
       CHK(hipEventRecord(c->ev_pf[l + 1], c->sf));
     }
     CHK(moe::launch_ffn(h, XN(c, l), c->sid + R(c, l), c->w + R(c, l), T, c->shared[l], Y(c, l), X(c, l), X(c, l + 1),
-                        l + 1 < c->L ? XN(c, l + 1) : nullptr, kRmsEps, cs, fused));
+                        l + 1 < c->L ? XN(c, l + 1) : nullptr, kRmsEps, cs, fused, !(fuse_cl && l + 1 < c->L)));
   }
   if (pf && c->L > 1) {  // rejoin the side streams (the predictor stream is used only without fusion)
     if (!fused) {

@@ -65,6 +65,9 @@ __device__ __forceinline__ void group_body(const int32_t* rec, int n, int nb, in
     blk[2] = pre + c0;
   }
   if (tid == 0) grp[0] = nr;
+  // blocks past the last record, up to the most a call of n pairs can have, are
+  // marked empty, so decode work items can read their block without nr
+  for (int r = nr + tid; r < min(n, nb); r += kBlock) grp[kRecWords * (1 + r) + 1] = 0;
   __syncthreads();
   // each pair goes to its record's list, and the first kInline of a list also
   // into the record block

@@ -93,6 +93,25 @@ hipError_t launch_reset(moe_offload* h, hipStream_t s);
 // h->logits = x . wr^T + bias; with hn, also hn->logits = x . wrn^T + biasn in the same launch
 hipError_t launch_logits(moe_offload* h, const void* x, const void* wr, const float* bias, int T, hipStream_t s,
                          moe_offload* hn = nullptr, const void* wrn = nullptr, const float* biasn = nullptr);
+// The previous layer's top-k combine (y, residual, next norm), taken into this
+// layer's router launch in the decode chain (bf16 activations, H <= 8192, one
+// token per workgroup): every workgroup forms its token's normalised input in
+// LDS in the combine's own order; workgroup 0 of each token writes y, x_next
+// and xn_next.
+struct CombineSrc {
+  const float* part;     // [T*k (+T)][H] fp32 expert outputs of the previous layer
+  const float* w;        // [T][k] its routing weights
+  int T, k, shared;      // shared: rows T*k + t hold the shared expert's output
+  void* y;               // [T][H] previous layer output
+  const void* residual;  // [T][H] its input stream x_l
+  void* x_next;          // [T][H] x_{l+1} = round(x_l + y)
+  void* xn_next;         // [T][H] rmsnorm(x_{l+1}): this layer's router and expert input
+  float eps;
+};
+constexpr int kFusedCombineMaxH = 8192;
+hipError_t launch_combine_logits(moe_offload* h, const CombineSrc& cb, const void* wr, const float* bias, int T,
+                                 hipStream_t s, moe_offload* hn = nullptr, const void* wrn = nullptr,
+                                 const float* biasn = nullptr);
 hipError_t launch_route(moe_offload* h, const void* x, const void* wr, const float* bias, int T, int32_t* ids,
                         float* w, hipStream_t s);
 hipError_t launch_ensure(moe_offload* h, const int32_t* ids, int n, int32_t* slot_ids, hipStream_t s);
@@ -102,9 +121,10 @@ hipError_t launch_distinct(moe_offload* h, const int32_t* ids, int n, int32_t* o
 hipError_t launch_stage_all(moe_offload* h, const int32_t* ids, int n, int32_t* slot_ids, hipStream_t s);
 // xn_next (optional, needs x_next): rmsnorm(x_next) with eps, for the next layer of a chain;
 // grouped: the group descriptor for slot_ids was already built (launch_decide)
+// combine = false: stop after the down projection (the chain takes the combine into the next router launch)
 hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int T,
                       const void* shared, void* y, const void* residual, void* x_next, void* xn_next, float eps,
-                      hipStream_t s, bool grouped = false);
+                      hipStream_t s, bool grouped = false, bool combine = true);
 // Decode control step in one workgroup: top-k of h->logits (launch_logits first),
 // ensure, and the FFN grouping.  With hn (max_n > 0): also the top-k of
 // hn->logits (the lookahead prediction, ids to pred) and the prefetch install

@@ -61,6 +61,7 @@ struct FfnArgs {
   int32_t* err;
   int T, k, H, F, S, E;
   int off_pairs, off_tiles;
+  int max_routed;  // record blocks a call can fill: min(T * k, S + E); unused ones are marked empty
 };
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)rn_to_bf16(f); }
@@ -87,6 +88,25 @@ __device__ __forceinline__ Item item_record(const FfnArgs& a, int nr, int r) {
     const int ri = blk[0];
     it.rec = ri < a.S ? a.slots + (uint64_t)ri * a.stride : a.staging + (uint64_t)(ri - a.S) * a.stride;
     it.n = blk[1];
+    it.sh = false;
+  } else {
+    it.rec = a.shared;
+    it.n = a.T;
+    it.sh = true;
+  }
+  return it;
+}
+
+// Record of decode work item r without the record count: blocks below
+// max_routed are real or marked empty (n = 0); r == max_routed is the shared expert.
+__device__ __forceinline__ Item item_block(const FfnArgs& a, int r) {
+  Item it;
+  if (r < a.max_routed) {
+    const int32_t* blk = a.grp + kRecWords * (1 + r);
+    const int ri = blk[0];
+    it.n = blk[1];
+    it.rec = it.n == 0 ? nullptr
+                       : (ri < a.S ? a.slots + (uint64_t)ri * a.stride : a.staging + (uint64_t)(ri - a.S) * a.stride);
     it.sh = false;
   } else {
     it.rec = a.shared;
@@ -517,8 +537,7 @@ __device__ __forceinline__ void vec_pass(const uint8_t* row0, const uint8_t* row
 template <bool FP8>
 __global__ __launch_bounds__(256) void k_gateup_vec(FfnArgs a) {
   const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
-  const int nr = a.grp[0];
-  const int nrt = nr + (a.shared ? 1 : 0);
+  const int nrt = a.max_routed + (a.shared ? 1 : 0);
   const int RG = a.F / 4;
   const int H = a.H, F = a.F;
   const int nk = H / 128;
@@ -530,7 +549,8 @@ __global__ __launch_bounds__(256) void k_gateup_vec(FfnArgs a) {
   const int nwave = gridDim.x * 4;
   for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < nrt * RG; item += nwave) {
     const int r = item / RG, fg = (item % RG) * 4, f = fg + q;
-    const Item it = item_record(a, nr, r);
+    const Item it = item_block(a, r);
+    if (it.n == 0) continue;
     const uint8_t* wg = it.rec + (uint64_t)f * H * esz;
     const float* sc = reinterpret_cast<const float*>(it.rec + 3 * mat) + (fg / 128) * (H / 128);
     for (int tg = 0; tg < it.n; tg += kVecTok) {
@@ -565,8 +585,7 @@ __global__ __launch_bounds__(256) void k_gateup_vec(FfnArgs a) {
 template <bool FP8>
 __global__ __launch_bounds__(256) void k_down_vec(FfnArgs a) {
   const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
-  const int nr = a.grp[0];
-  const int nrt = nr + (a.shared ? 1 : 0);
+  const int nrt = a.max_routed + (a.shared ? 1 : 0);
   const int RG = a.H / 8;
   const int H = a.H, F = a.F;
   const int nk = F / 128;
@@ -578,7 +597,8 @@ __global__ __launch_bounds__(256) void k_down_vec(FfnArgs a) {
   const int nwave = gridDim.x * 4;
   for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < nrt * RG; item += nwave) {
     const int r = item / RG, hg = (item % RG) * 8, h0 = hg + q;
-    const Item it = item_record(a, nr, r);
+    const Item it = item_block(a, r);
+    if (it.n == 0) continue;
     const uint8_t* wd = it.rec + 2 * mat + (uint64_t)h0 * F * esz;
     const float* sc = reinterpret_cast<const float*>(it.rec + 3 * mat) + 2 * nsc + (hg / 128) * (F / 128);
     for (int tg = 0; tg < it.n; tg += kVecTok) {
@@ -708,7 +728,7 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(FfnArgs a, void* __rest
 
 hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int T,
                       const void* shared, void* y, const void* residual, void* x_next, void* xn_next, float eps,
-                      hipStream_t s, bool grouped) {
+                      hipStream_t s, bool grouped, bool combine) {
   FfnArgs a;
   a.x = x;
   a.slot_ids = slot_ids;
@@ -732,8 +752,9 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
   a.E = h->E;
   a.off_pairs = h->gl.off_pairs();
   a.off_tiles = h->gl.off_tiles();
+  a.max_routed = std::min(T * h->k, h->S + h->E);
   // distinct records a call can touch (+ the shared expert)
-  const int max_items_r = std::min(T * h->k, h->E) + (shared ? 1 : 0);
+  const int max_items_r = a.max_routed + (shared ? 1 : 0);
   if (!grouped) {
     launch_k(h, MOE_K_GROUP, k_group, dim3(1), dim3(kBlock), 0, s, a);
   }
@@ -770,7 +791,7 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
   {
     launch_k(h, MOE_K_DOWN, dn, g2, b2, 0, s, a);
   }
-  {
+  if (combine) {
     if (h->dtype == MOE_F32)
       launch_k(h, MOE_K_COMBINE, k_combine<true>, dim3(T), dim3(kRowThreads), 0, s, a, xn_next, eps);
     else

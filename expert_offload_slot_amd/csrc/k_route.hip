@@ -21,6 +21,7 @@
 #include <algorithm>
 
 #include "prof.h"
+#include "rownorm.h"
 #include "topk.h"
 
 namespace moe {
@@ -87,6 +88,102 @@ __global__ __launch_bounds__(256) void k_logits(const A* __restrict__ x, RouterJ
   }
 }
 
+// Decode chain: the previous layer's combine taken into this layer's router
+// launch.  Workgroup (x, t, z) recomputes token t's combine exactly as the
+// combine kernel does (thread i owns the chunks i, i + 256, ...; y and x_next
+// rounded once each; the row norm in rownorm.h's order), keeps the normalised
+// row in LDS, and its four wavefronts take the logits of experts 4x .. 4x+3 of
+// router z in the canonical order above.  The router rows are requested before
+// the combine so both loads are in flight together.
+constexpr int kRowChunks = kFusedCombineMaxH / (8 * kRowThreads);  // combine chunks per thread
+constexpr int kRouterChunks = kFusedCombineMaxH / (8 * 64);         // router chunks per lane
+
+__global__ __launch_bounds__(kRowThreads) void k_combine_logits(CombineSrc cb, RouterJob<uint16_t> j0,
+                                                                RouterJob<uint16_t> j1, int H) {
+  __shared__ float s_wave[4];
+  __shared__ __align__(16) uint16_t xs[kFusedCombineMaxH];
+  const RouterJob<uint16_t> j = blockIdx.z == 0 ? j0 : j1;
+  const int t = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int e = blockIdx.x * 4 + (tid >> 6);
+  const bool ev = e < j.E;
+  const bool lead = blockIdx.x == 0 && blockIdx.z == 0;
+  uint4 wr[kRouterChunks];
+#pragma unroll
+  for (int i = 0; i < kRouterChunks; ++i) {
+    const int c = lane + 64 * i;
+    if (ev && c * 8 < H) wr[i] = *reinterpret_cast<const uint4*>(j.wr + (size_t)e * H + c * 8);
+  }
+  // combine of token t
+  const int k = cb.k, routed = cb.T * cb.k;
+  const size_t roff = (size_t)t * H * 2;
+  void* yrow = lead ? (uint8_t*)cb.y + roff : nullptr;
+  void* xrow = lead ? (uint8_t*)cb.x_next + roff : nullptr;
+  void* xnrow = lead ? (uint8_t*)cb.xn_next + roff : nullptr;
+  const void* rrow = (const uint8_t*)cb.residual + roff;
+  float xv[kRowChunks][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int q = 0; q < kRowChunks; ++q) {
+    const int c = tid + kRowThreads * q;
+    if (c * 8 < H) {
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int jj = 0; jj < k; ++jj) {
+        const float wj = cb.w[(size_t)t * k + jj];
+        const float4* pr = reinterpret_cast<const float4*>(cb.part + (uint64_t)(t * k + jj) * H + c * 8);
+        const float4 p0 = pr[0], p1 = pr[1];
+        acc[0] = __builtin_fmaf(wj, p0.x, acc[0]); acc[1] = __builtin_fmaf(wj, p0.y, acc[1]);
+        acc[2] = __builtin_fmaf(wj, p0.z, acc[2]); acc[3] = __builtin_fmaf(wj, p0.w, acc[3]);
+        acc[4] = __builtin_fmaf(wj, p1.x, acc[4]); acc[5] = __builtin_fmaf(wj, p1.y, acc[5]);
+        acc[6] = __builtin_fmaf(wj, p1.z, acc[6]); acc[7] = __builtin_fmaf(wj, p1.w, acc[7]);
+      }
+      if (cb.shared) {
+        const float4* pr = reinterpret_cast<const float4*>(cb.part + (uint64_t)(routed + t) * H + c * 8);
+        const float4 p0 = pr[0], p1 = pr[1];
+        acc[0] = acc[0] + p0.x; acc[1] = acc[1] + p0.y; acc[2] = acc[2] + p0.z; acc[3] = acc[3] + p0.w;
+        acc[4] = acc[4] + p1.x; acc[5] = acc[5] + p1.y; acc[6] = acc[6] + p1.z; acc[7] = acc[7] + p1.w;
+      }
+      chunk_store<false>(yrow, c, acc);  // acc now holds y as stored
+      float res[8];
+      chunk_load<false>(rrow, c, res);
+#pragma unroll
+      for (int qq = 0; qq < 8; ++qq) xv[q][qq] = res[qq] + acc[qq];
+      chunk_store<false>(xrow, c, xv[q]);  // x_next as stored
+      ss = chunk_sumsq(xv[q], ss);
+    }
+  }
+  const float inv = row_inv_rms(row_block_sum(ss, s_wave), H, cb.eps);
+#pragma unroll
+  for (int q = 0; q < kRowChunks; ++q) {
+    const int c = tid + kRowThreads * q;
+    if (c * 8 < H) {
+      float v[8];
+#pragma unroll
+      for (int qq = 0; qq < 8; ++qq) v[qq] = xv[q][qq] * inv;
+      chunk_store<false>(xnrow, c, v);
+      chunk_store<false>(xs, c, v);
+    }
+  }
+  __syncthreads();
+  if (!ev) return;
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < kRouterChunks; ++i) {
+    const int c = lane + 64 * i;
+    if (c * 8 < H) {
+      float xv8[8], wv8[8];
+      load8(xs + c * 8, xv8);
+      const uint4 a4 = wr[i];
+      wv8[0] = bf16_lo(a4.x); wv8[1] = bf16_hi(a4.x); wv8[2] = bf16_lo(a4.y); wv8[3] = bf16_hi(a4.y);
+      wv8[4] = bf16_lo(a4.z); wv8[5] = bf16_hi(a4.z); wv8[6] = bf16_lo(a4.w); wv8[7] = bf16_hi(a4.w);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc = __builtin_fmaf(xv8[q], wv8[q], acc);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc = acc + __shfl_xor(acc, o);
+  if (lane == 0) j.logits[(size_t)t * j.E + e] = acc + j.bias[e];
+}
+
 // Top-k (topk.h): one wavefront per token, 4 tokens per workgroup.
 template <int J>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
@@ -125,6 +222,17 @@ hipError_t launch_logits(moe_offload* h, const void* x, const void* wr, const fl
     logits_jobs<float>(h, x, wr, bias, hn, wrn, biasn, T, s);
   else
     logits_jobs<uint16_t>(h, x, wr, bias, hn, wrn, biasn, T, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_logits(moe_offload* h, const CombineSrc& cb, const void* wr, const float* bias, int T,
+                                 hipStream_t s, moe_offload* hn, const void* wrn, const float* biasn) {
+  if (h->dtype == MOE_F32 || h->H > kFusedCombineMaxH || (hn && hn->dtype == MOE_F32)) return hipErrorInvalidValue;
+  RouterJob<uint16_t> j0{(const uint16_t*)wr, bias, h->logits, h->E};
+  RouterJob<uint16_t> j1 = hn ? RouterJob<uint16_t>{(const uint16_t*)wrn, biasn, hn->logits, hn->E} : j0;
+  const int E = hn ? std::max(h->E, hn->E) : h->E;
+  launch_k(h, MOE_K_LOGITS, k_combine_logits, dim3((E + 3) / 4, T, hn ? 2 : 1), dim3(kRowThreads), 0, s, cb, j0, j1,
+           h->H);
   return hipGetLastError();
 }
 

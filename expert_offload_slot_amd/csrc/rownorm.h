@@ -38,10 +38,12 @@ __device__ __forceinline__ void chunk_load(const void* row, int c, float v[8]) {
   }
 }
 
-// stores round(v) (bf16) or v (fp32); returns nothing.  `v` is updated to the stored values.
+// rounds v to the activation type (bf16 RNE; fp32 unchanged) and, if row is not
+// null, stores the chunk.  `v` is updated to the rounded values.
 template <bool F32>
 __device__ __forceinline__ void chunk_store(void* row, int c, float v[8]) {
   if (F32) {
+    if (!row) return;
     float4* p = reinterpret_cast<float4*>((float*)row + c * 8);
     p[0] = make_float4(v[0], v[1], v[2], v[3]);
     p[1] = make_float4(v[4], v[5], v[6], v[7]);
@@ -52,8 +54,9 @@ __device__ __forceinline__ void chunk_store(void* row, int c, float v[8]) {
       b[q] = rn_to_bf16(v[q]);
       v[q] = __uint_as_float(b[q] << 16);
     }
-    *reinterpret_cast<uint4*>((uint16_t*)row + c * 8) =
-        make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16));
+    if (row)
+      *reinterpret_cast<uint4*>((uint16_t*)row + c * 8) =
+          make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16));
   }
 }
 
