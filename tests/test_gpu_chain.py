@@ -37,22 +37,25 @@ def test_rmsnorm_parity():
 
 
 class ChainModel:
-    def __init__(self, L, E, S, k, H, F, wdt, T, seed, prefetch_n=0, zipf=1.2, rho=0.9):
+    def __init__(self, L, E, S, k, H, F, wdt, T, seed, prefetch_n=0, zipf=1.2, rho=0.9, shared=False):
         self.L, self.E, self.S, self.k, self.H, self.F, self.wdt, self.T = L, E, S, k, H, F, wdt, T
-        self.hosts, self.routers, self.handles = [], [], []
+        self.hosts, self.routers, self.handles, self.shared = [], [], [], []
+        rdt = 1 if wdt == 2 else wdt  # fp8 layers take a bf16 router and bf16 activations
         for l in range(L):
             self.hosts.append(synth.records(seed, l, E, H, F, wdt))
-            self.routers.append(synth.router(seed, l, E, H, wdt, zipf_s=zipf))
+            self.routers.append(synth.router(seed, l, E, H, rdt, zipf_s=zipf))
+            self.shared.append(synth.records(seed, l, 1, H, F, wdt, shared=True)[0] if shared else None)
             h = m.moe_offload_create(E, S, H, F, k, wdt, T, 0, m.FLAG_AUDIT, None,
                                      self.handles[0] if l else None)
             m.host_array(h, E)[:, :self.hosts[l].shape[1]] = self.hosts[l]
             self.handles.append(h)
         self.wr = [to_dev(w) for w, _ in self.routers]
         self.b = [to_dev(b) for _, b in self.routers]
-        self.chain = m.moe_chain_create(self.handles, self.wr, self.b, T, prefetch_n)
+        self.sh = [to_dev(s) for s in self.shared] if shared else None
+        self.chain = m.moe_chain_create(self.handles, self.wr, self.b, T, prefetch_n, self.sh)
         self.bufs = m.moe_chain_get_buffers(self.chain)
         self.info = [m.moe_offload_query(h) for h in self.handles]
-        self.xs = synth.tokens(seed, 5, T, H, 64, rho, wdt)
+        self.xs = synth.tokens(seed, 5, T, H, 64, rho, rdt)
         self.act = 4 if wdt == 0 else 2
 
     def run(self, s, graph=True):
@@ -65,7 +68,7 @@ class ChainModel:
 
     def snapshot(self):
         L, T, H, k = self.L, self.T, self.H, self.k
-        dt = np.float32 if self.wdt == 0 else np.uint16
+        dt = np.float32 if self.wdt == 0 else np.uint16  # activations are bf16 for fp8 layers
         return dict(
             x=d2h(self.bufs["x"], (L + 1) * T * H * self.act, dt).reshape(L + 1, T, H),
             xn=d2h(self.bufs["xn"], L * T * H * self.act, dt).reshape(L, T, H),
@@ -92,24 +95,25 @@ class ChainModel:
 def oracle_replay_step(cm, caches, snap, prefetch_n, check_ffn=True):
     """Teacher-forced oracle for one chain step; asserts parity for every layer."""
     L = cm.L
+    adt = 1 if cm.wdt == 2 else cm.wdt  # activation / router format
     for l in range(L):
         xn = snap["xn"][l]
         # the block input itself: the GPU norm of the GPU stream, within one bf16 step
-        ref_xn = oracle.rmsnorm(snap["x"][l], cm.wdt)
-        if cm.wdt != 0:
+        ref_xn = oracle.rmsnorm(snap["x"][l], adt)
+        if adt != 0:
             assert np.abs(xn.astype(np.int32) - ref_xn.astype(np.int32)).max() <= 1
-        ids, w, _ = oracle.route(xn, cm.routers[l][0], cm.routers[l][1], cm.k, cm.wdt)
+        ids, w, _ = oracle.route(xn, cm.routers[l][0], cm.routers[l][1], cm.k, adt)
         assert np.array_equal(ids, snap["ids"][l]), (l, ids, snap["ids"][l])
         sid, mode, pairs = caches[l].ensure(ids)
         caches[l].copy(mode, pairs)
         assert np.array_equal(sid, snap["sid"][l]), l
         if prefetch_n and l + 1 < L:
-            pred, _, _ = oracle.route(xn, cm.routers[l + 1][0], cm.routers[l + 1][1], cm.k, cm.wdt)
+            pred, _, _ = oracle.route(xn, cm.routers[l + 1][0], cm.routers[l + 1][1], cm.k, adt)
             inst = caches[l + 1].install(pred, prefetch_n)
             caches[l + 1].copy(0, inst)
         if check_ffn:
-            y, y64 = oracle.ffn(xn, cm.wdt, cm.H, cm.F, caches[l].records(sid), w, want_f64=True)
-            assert row_rel_err(snap["y"][l], y64, cm.wdt) <= 2e-2, l
+            y, y64 = oracle.ffn(xn, cm.wdt, cm.H, cm.F, caches[l].records(sid), w, cm.shared[l], want_f64=True)
+            assert row_rel_err(snap["y"][l], y64, cm.wdt) <= (1e-5 if cm.wdt == 0 else 2e-2), l
             assert np.array_equal(snap["x"][l + 1], oracle.residual(snap["x"][l], snap["y"][l], cm.wdt))
     # lists and tables of every layer after the step (each handle's last call)
     for l in range(L):
@@ -162,3 +166,35 @@ def test_prefetch_keeps_outputs_identical():
     finally:
         a.close()
         b.close()
+
+
+@pytest.mark.parametrize("case", [
+    # (E, S, k, H, F, wdt, T, prefetch, shared): the fused router launch with a shared expert and fp8 records,
+    # the batch limits of that fusion (8 fused, 9 not), 256 experts, and more than 512 (t, j) pairs (separate
+    # kernels and the predictor stream for the lookahead)
+    (16, 6, 4, 256, 256, 2, 3, 2, True),
+    (16, 6, 4, 256, 256, 1, 8, 2, True),
+    (16, 6, 4, 256, 256, 1, 9, 0, False),
+    (256, 20, 8, 256, 256, 1, 2, 3, False),
+    (32, 12, 8, 128, 256, 1, 72, 2, False),
+])
+def test_chain_variants_match_eager_and_oracle(case):
+    E, S, k, H, F, wdt, T, prefetch_n, shared = case
+    L = 3
+    print("chain variant E=%d S=%d k=%d H=%d F=%d wdt=%d T=%d prefetch=%d shared=%s" % case, flush=True)
+    cg = ChainModel(L, E, S, k, H, F, wdt, T, 85, prefetch_n, shared=shared)
+    ce = ChainModel(L, E, S, k, H, F, wdt, T, 85, prefetch_n, shared=shared)
+    rb = oracle.record_bytes(wdt, H, F)
+    caches = [oracle.Cache(E, S, cg.hosts[l], rb) for l in range(L)]
+    try:
+        for s in range(5):
+            cg.run(s, graph=True)
+            ce.run(s, graph=False)
+            sg, se = cg.snapshot(), ce.snapshot()
+            for key in sg:
+                assert np.array_equal(sg[key], se[key]), (s, key)
+            oracle_replay_step(cg, caches, sg, prefetch_n)
+        assert all(m.moe_offload_stats(h)["error"] == 0 for h in cg.handles)
+    finally:
+        cg.close()
+        ce.close()
