@@ -47,12 +47,20 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def code_sha256(path):
+    """sha256 of a C++ source with its comments and whitespace removed (comment edits keep the hash)."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
+
+
 def measured_traffic():
-    """HBM bytes per gate/up launch from the committed counter summary, if taken on the current kernel source."""
+    """HBM bytes per gate/up launch from the committed counter summary, if taken on the current kernel code."""
     if not os.path.exists(COUNTERS):
         return None
     text = open(COUNTERS).read()
-    sha = hashlib.sha256(open(FFN_SRC, "rb").read()).hexdigest()
+    sha = code_sha256(FFN_SRC)
     got = dict(re.findall(r"^(\w+):\s*(\S+)\s*$", text, re.M))
     if got.get("source_sha256") != sha:
         return None

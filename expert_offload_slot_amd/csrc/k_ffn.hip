@@ -17,10 +17,10 @@
 //              registers and met by every token of the record with the bf16
 //              pair-dot instruction.  Few tokens per record make this a
 //              weight-streaming (HBM) problem, not a matrix-core one.
-//     larger T: k_gateup / k_down, bf16 MFMA 16x16x32 tiles, work item =
-//              (record, 16 rows), K split over the workgroup's wavefronts and
-//              reduced in LDS in wavefront order, up to 32 tokens per pass.
-//     fp32 records: plain fp32 FMA kernels with the same work split.
+//     larger T (prefill): k_gemm_gu / k_gemm_dn, a grouped GEMM whose work
+//              items are (tile of 64 pairs of one record, 64 weight rows), K
+//              slices staged through LDS, bf16 MFMA 16x16x32 tiles.
+//     fp32 records: plain fp32 FMA kernels, work item (record, 64 rows).
 //   h is stored in bf16 (fp32 for fp32 records); down writes fp32 partial
 //   outputs per (t, j) to the workspace.
 //   k_combine  one workgroup per token: sum over j in order (+ shared), round,

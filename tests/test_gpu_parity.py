@@ -4,7 +4,7 @@ Bit-exact: router ids, slot ids, copy lists, slot tables, slot bytes.
 Within tolerance: routing weights (1e-5) and layer outputs (per token row,
 ||y - ref||_inf <= tol * ||ref||_inf with tol 1e-5 for fp32 and 2e-2 for
 bf16/fp8; ref = the oracle's double sums).
-Sizes span several MFMA tiles, ragged token counts, staging, and more than
+Sizes span several kernel tiles, ragged token counts, staging, and more than
 one 64-token pass per expert.
 """
 import numpy as np
