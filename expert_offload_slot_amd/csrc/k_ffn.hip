@@ -10,7 +10,8 @@
 //              index -> distinct records, each with its token list (the first
 //              kInline pair ids inline, so one load trip serves a work item).
 //              The decode chain builds the same descriptor in its control
-//              workgroup instead.
+//              workgroup instead.  A single token needs none: its k records
+//              are distinct, so each (t, j) pair is its own work item.
 //   gate/up + SiLU and down, one of three kernel pairs by call size:
 //     T <= kDecodeMaxT (decode): k_gateup_vec / k_down_vec, one wavefront per
 //              (record, 4 or 8 weight rows); the rows are loaded once, held in
@@ -62,6 +63,7 @@ struct FfnArgs {
   int T, k, H, F, S, E;
   int off_pairs, off_tiles;
   int max_routed;  // record blocks a call can fill: min(T * k, S + E); unused ones are marked empty
+  int pair_items;  // one token: its k records are distinct, so every pair is its own record (no grouping)
 };
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)rn_to_bf16(f); }
@@ -77,12 +79,14 @@ __global__ __launch_bounds__(kBlock) void k_group(FfnArgs a) {
 // 128-byte record block, so one load trip serves the item.
 struct Item {
   const uint8_t* rec;
-  int n;    // tokens of the item
-  bool sh;  // the always-resident shared expert
+  int n;     // tokens of the item
+  bool sh;   // the always-resident shared expert
+  int pair;  // >= 0: the item is this single (t, j) pair (pair items, no grouping)
 };
 
 __device__ __forceinline__ Item item_record(const FfnArgs& a, int nr, int r) {
   Item it;
+  it.pair = -1;
   if (r < nr) {
     const int32_t* blk = a.grp + kRecWords * (1 + r);
     const int ri = blk[0];
@@ -101,7 +105,18 @@ __device__ __forceinline__ Item item_record(const FfnArgs& a, int nr, int r) {
 // max_routed are real or marked empty (n = 0); r == max_routed is the shared expert.
 __device__ __forceinline__ Item item_block(const FfnArgs& a, int r) {
   Item it;
-  if (r < a.max_routed) {
+  it.pair = -1;
+  if (a.pair_items && r < a.max_routed) {  // max_routed = k here
+    int ri = a.slot_ids[r];
+    if ((unsigned)ri >= (unsigned)(a.S + a.E)) {
+      atomicOr(a.err, MOE_DEV_ERR_AUDIT);
+      ri = 0;
+    }
+    it.rec = ri < a.S ? a.slots + (uint64_t)ri * a.stride : a.staging + (uint64_t)(ri - a.S) * a.stride;
+    it.n = 1;
+    it.sh = false;
+    it.pair = r;
+  } else if (r < a.max_routed) {
     const int32_t* blk = a.grp + kRecWords * (1 + r);
     const int ri = blk[0];
     it.n = blk[1];
@@ -118,6 +133,7 @@ __device__ __forceinline__ Item item_block(const FfnArgs& a, int r) {
 
 // pair id (row of h / part) of entry idx of record r
 __device__ __forceinline__ int item_pair(const FfnArgs& a, const Item& it, int r, int idx) {
+  if (it.pair >= 0) return it.pair;
   if (it.sh) return a.T * a.k + idx;
   const int32_t* blk = a.grp + kRecWords * (1 + r);
   return idx < kInline ? blk[3 + idx] : a.grp[a.off_pairs + blk[2] + idx];
@@ -753,9 +769,10 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
   a.off_pairs = h->gl.off_pairs();
   a.off_tiles = h->gl.off_tiles();
   a.max_routed = std::min(T * h->k, h->S + h->E);
+  a.pair_items = T == 1 && h->dtype != MOE_F32 ? 1 : 0;
   // distinct records a call can touch (+ the shared expert)
   const int max_items_r = a.max_routed + (shared ? 1 : 0);
-  if (!grouped) {
+  if (!grouped && !a.pair_items) {
     launch_k(h, MOE_K_GROUP, k_group, dim3(1), dim3(kBlock), 0, s, a);
   }
   const bool fp8 = h->dtype == MOE_FP8_E4M3_B128;

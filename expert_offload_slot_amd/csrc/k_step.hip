@@ -31,7 +31,8 @@ template <int J>
 __global__ __launch_bounds__(kBlock) void k_decide(CacheDev c, const float* __restrict__ logits, int T, int k,
                                                    int32_t* __restrict__ ids, float* __restrict__ w,
                                                    int32_t* __restrict__ slot_ids, int32_t* __restrict__ grp,
-                                                   int off_pairs, int off_tiles, int audit, CacheDev nc,
+                                                   int off_pairs, int off_tiles, int do_group, int audit,
+                                                   CacheDev nc,
                                                    int audit_next,
                                                    const float* __restrict__ pred_logits,
                                                    int32_t* __restrict__ pred, int max_n) {
@@ -60,7 +61,7 @@ __global__ __launch_bounds__(kBlock) void k_decide(CacheDev c, const float* __re
   __syncthreads();
   ensure_body(c, t, ids_l, n, slot_ids, rec_l, audit, u.keys);
   __syncthreads();
-  group_body(rec_l, n, c.S + c.E, grp, off_pairs, off_tiles, c.err, u.g);
+  if (do_group) group_body(rec_l, n, c.S + c.E, grp, off_pairs, off_tiles, c.err, u.g);
   if (max_n <= 0) return;  // uniform
   // lookahead: the next layer's router on this layer's input predicts its experts;
   // up to max_n of them are installed into the next layer's table
@@ -90,10 +91,12 @@ hipError_t launch_decide(moe_offload* h, int T, int32_t* ids, float* w, int32_t*
   const int J = topk_lanes(E);
   auto kd = J == 1 ? k_decide<1> : J == 2 ? k_decide<2> : J == 4 ? k_decide<4> : J == 8 ? k_decide<8> : k_decide<16>;
   const int audit = (h->flags & MOE_FLAG_AUDIT) ? 1 : 0;
+  // a single token's FFN reads its k distinct records straight from slot_ids (launch_ffn)
+  const int do_group = T == 1 && h->dtype != MOE_F32 ? 0 : 1;
   const CacheDev nc = max_n > 0 ? hn->cache : h->cache;
   const int audit_next = max_n > 0 && (hn->flags & MOE_FLAG_AUDIT) ? 1 : 0;
   launch_k(h, MOE_K_DECIDE, kd, dim3(1), dim3(kBlock), 0, s, h->cache, h->logits, T, h->k, ids, w, slot_ids, h->grp,
-           h->gl.off_pairs(), h->gl.off_tiles(), audit, nc, audit_next, max_n > 0 ? hn->logits : h->logits, pred,
+           h->gl.off_pairs(), h->gl.off_tiles(), do_group, audit, nc, audit_next, max_n > 0 ? hn->logits : h->logits, pred,
            max_n);
   return hipGetLastError();
 }
