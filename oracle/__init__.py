@@ -65,7 +65,7 @@ def lib():
         L.orc_cache_free.argtypes = [vp]
         L.orc_cache_state.argtypes = [vp, vp, vp, vp, vp]
         L.orc_cache_counters.argtypes = [vp, vp]
-        L.orc_ensure.argtypes = [vp, vp, i32, vp, vp]
+        L.orc_ensure.argtypes = [vp, vp, i32, i32, vp, vp]
         L.orc_ensure.restype = i32
         L.orc_stage_all.argtypes = [vp, vp, i32, vp, vp]
         L.orc_stage_all.restype = i32
@@ -185,7 +185,8 @@ class Cache:
         ids = np.ascontiguousarray(ids, dtype=np.int32)
         slot_ids = np.empty_like(ids)
         desc = self._desc()
-        rc = lib().orc_ensure(self._c, _p(ids), ids.size, _p(slot_ids), _p(desc))
+        k = ids.shape[-1] if ids.ndim > 1 else max(ids.size, 1)
+        rc = lib().orc_ensure(self._c, _p(ids), ids.size, k, _p(slot_ids), _p(desc))
         if rc != 0:
             raise ValueError("expert id out of range")
         mode, pairs = self._unpack(desc)

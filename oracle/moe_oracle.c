@@ -199,10 +199,15 @@ int orc_topk(const float* logits, int T, int E, int k, int32_t* ids, double* w) 
  *        recently used, ties to the lower slot.  M[i] goes to victim i; the
  *        evicted expert leaves the map.  Every e in D gets last_use = tick.
  *        slot_ids = slot_of[id].  Copy list = (M[i], victim i).
- *     3. |D| > S (STAGED): the slot state is left unchanged (only tick
- *        advanced).  Resident experts are read from their slots; every
- *        e in D \ R is copied to staging record e and its ids are rewritten
- *        to S + e.  Copy list = (e, S + e) for e in D \ R ascending.
+ *     3. |D| > S (STAGED; not on the page, which stages whole layers for
+ *        prefill only): hits as in 2.  The eligible victims, in the same
+ *        order, are fewer than the misses; the misses claim them in install
+ *        order (pairs routed to e descending, best top-k position ascending,
+ *        id ascending; see orc_install) and every miss left over is copied
+ *        to staging record e and read at S + e for this call only.  Every e
+ *        of D holding a slot gets last_use = tick.  Copy list = (e, its slot
+ *        or S + e) for e in D \ R ascending.  So a batch wider than the
+ *        cache still leaves its most used experts resident for the next call.
  *   A record index r < S names slot r; r >= S names staging record r - S.
  *   Prefetch install ([freetoken] "Install"): see orc_install.
  */
@@ -275,63 +280,100 @@ static int victim_order(const orc_cache* c, const unsigned char* protect, int* o
   return n;
 }
 
+/* does expert a come before expert b in install order (count desc, best asc, id asc)? */
+static int install_before(const int* cnt, const int* best, int a, int b) {
+  if (cnt[a] != cnt[b]) return cnt[a] > cnt[b];
+  if (best[a] != best[b]) return best[a] < best[b];
+  return a < b;
+}
+
 /* desc layout: desc[0] = mode, desc[1] = count, then count pairs (expert, record index).
- * ids: n = T*k routed ids.  Returns ORC_EINVAL (state untouched) on an id outside [0, E). */
-int orc_ensure(orc_cache* c, const int32_t* ids, int n, int32_t* slot_ids, int32_t* desc) {
+ * ids: n = T*k routed ids, k per token.  Returns ORC_EINVAL (state untouched) on an id
+ * outside [0, E). */
+int orc_ensure(orc_cache* c, const int32_t* ids, int n, int k, int32_t* slot_ids, int32_t* desc) {
+  if (k <= 0 || n % k != 0) return ORC_EINVAL;
   for (int i = 0; i < n; ++i)
     if (ids[i] < 0 || ids[i] >= c->E) return ORC_EINVAL;
+  int E = c->E, S = c->S;
   c->tick += 1;
   c->calls += 1;
-  unsigned char* inD = (unsigned char*)calloc((size_t)c->E, 1);
-  int nd = 0;
+  unsigned char* inD = (unsigned char*)calloc((size_t)E, 1);
+  unsigned char* miss = (unsigned char*)calloc((size_t)E, 1);
+  int nd = 0, nm = 0;
   for (int i = 0; i < n; ++i)
     if (!inD[ids[i]]) { inD[ids[i]] = 1; ++nd; }
-  int count = 0;
-  if (nd > c->S) {
-    desc[0] = ORC_STAGED;
-    for (int e = 0; e < c->E; ++e)
-      if (inD[e] && c->slot_of[e] < 0) {
-        desc[2 + 2 * count] = e;
-        desc[3 + 2 * count] = c->S + e;
-        ++count;
-      }
-    for (int i = 0; i < n; ++i) {
-      int e = ids[i];
-      slot_ids[i] = c->slot_of[e] >= 0 ? c->slot_of[e] : c->S + e;
-    }
-    desc[1] = count;
-    c->staged_calls += 1;
-    c->staged_copies += (uint64_t)count;
-    free(inD);
-    return ORC_OK;
-  }
-  /* SLOTS */
-  int* order = (int*)malloc(sizeof(int) * (size_t)c->S);
-  victim_order(c, inD, order);
-  for (int e = 0; e < c->E; ++e) {
+  /* hits are the experts of D resident before the call */
+  for (int e = 0; e < E; ++e) {
     if (!inD[e]) continue;
     int s = c->slot_of[e];
     if (s >= 0) {
       c->hits += 1;
       if (c->last_use[s] == 0) c->prefetch_hits += 1; /* installed by prefetch, first use */
-      continue;
+    } else {
+      miss[e] = 1;
+      ++nm;
     }
-    int v = order[count]; /* enough victims exist: |D| <= S */
+  }
+  /* the order in which the misses claim the eligible slots */
+  int* claim = (int*)malloc(sizeof(int) * (size_t)(nm > 0 ? nm : 1));
+  int nc = 0;
+  if (nd <= S) {
+    for (int e = 0; e < E; ++e)
+      if (miss[e]) claim[nc++] = e;
+  } else {
+    int* cnt = (int*)calloc((size_t)E, sizeof(int));
+    int* best = (int*)malloc(sizeof(int) * (size_t)E);
+    for (int e = 0; e < E; ++e) best[e] = k;
+    for (int i = 0; i < n; ++i) {
+      int e = ids[i];
+      cnt[e] += 1;
+      if (i % k < best[e]) best[e] = i % k;
+    }
+    for (int e = 0; e < E; ++e) {
+      if (!miss[e]) continue;
+      int pos = nc++;
+      while (pos > 0 && install_before(cnt, best, e, claim[pos - 1])) {
+        claim[pos] = claim[pos - 1];
+        --pos;
+      }
+      claim[pos] = e;
+    }
+    free(cnt);
+    free(best);
+  }
+  int* order = (int*)malloc(sizeof(int) * (size_t)S);
+  int nv = victim_order(c, inD, order);
+  int ns = nm < nv ? nm : nv; /* nm <= nv whenever |D| <= S */
+  for (int r = 0; r < ns; ++r) {
+    int v = order[r], e = claim[r];
     int old = c->expert_of[v];
     if (old >= 0) c->slot_of[old] = -1;
     c->expert_of[v] = e;
     c->slot_of[e] = v;
+  }
+  for (int e = 0; e < E; ++e)
+    if (inD[e] && c->slot_of[e] >= 0) c->last_use[c->slot_of[e]] = c->tick;
+  int count = 0;
+  for (int e = 0; e < E; ++e) {
+    if (!miss[e]) continue;
     desc[2 + 2 * count] = e;
-    desc[3 + 2 * count] = v;
+    desc[3 + 2 * count] = c->slot_of[e] >= 0 ? c->slot_of[e] : S + e;
     ++count;
   }
-  for (int e = 0; e < c->E; ++e)
-    if (inD[e]) c->last_use[c->slot_of[e]] = c->tick;
-  for (int i = 0; i < n; ++i) slot_ids[i] = c->slot_of[ids[i]];
-  desc[0] = ORC_SLOTS;
+  for (int i = 0; i < n; ++i) {
+    int e = ids[i];
+    slot_ids[i] = c->slot_of[e] >= 0 ? c->slot_of[e] : S + e;
+  }
+  desc[0] = nd > S ? ORC_STAGED : ORC_SLOTS;
   desc[1] = count;
-  c->misses += (uint64_t)count;
+  c->misses += (uint64_t)ns;
+  if (nd > S) {
+    c->staged_calls += 1;
+    c->staged_copies += (uint64_t)(nm - ns);
+  }
   free(order);
+  free(claim);
+  free(miss);
   free(inD);
   return ORC_OK;
 }
@@ -399,11 +441,8 @@ int orc_install(orc_cache* c, const int32_t* pred, int T, int k, int max_n, int3
   for (int e = 0; e < E; ++e) {
     if (!inP[e] || c->slot_of[e] >= 0) continue;
     int pos = nc++;
-    while (pos > 0) {
-      int p = cand[pos - 1];
-      int before = cnt[e] != cnt[p] ? cnt[e] > cnt[p] : (best[e] != best[p] ? best[e] < best[p] : e < p);
-      if (!before) break;
-      cand[pos] = p;
+    while (pos > 0 && install_before(cnt, best, e, cand[pos - 1])) {
+      cand[pos] = cand[pos - 1];
       --pos;
     }
     cand[pos] = e;

@@ -6,7 +6,10 @@
   * a brute-force re-statement of the batched rules (tie order, staging,
     install) compared exactly on random traces;
   * invariants after every call (maps inverse, D resident, misses = D \\ R,
-    free slots first, staging iff |D| > S, state untouched when staged);
+    free slots first, staging iff |D| > S; a call wider than the cache
+    leaves every slot holding one of its experts, the most used ones);
+  * a hand-worked example of the threshold, the overflow claim order and
+    the LRU ties;
   * capacity >= distinct experts ever seen: only compulsory misses.
 """
 from collections import OrderedDict
@@ -77,18 +80,22 @@ class BruteCache:
         self.held[s] = e
         self.home[e] = s
 
-    def ensure(self, ids):
+    def ensure(self, ids, k):
         self.clock += 1
         D = sorted(set(ids))
         miss = [e for e in D if e not in self.home]
-        if len(D) > self.S:
-            return [self.home.get(e, self.S + e) for e in ids], 1, [(e, self.S + e) for e in miss]
-        pairs = list(zip(miss, self._victims(set(D))))
-        for e, s in pairs:
+        claim = miss
+        if len(D) > self.S:  # more misses than free victims: the most used misses claim them
+            count = {e: ids.count(e) for e in D}
+            best = {e: min(i % k for i, x in enumerate(ids) if x == e) for e in D}
+            claim = sorted(miss, key=lambda e: (-count[e], best[e], e))
+        for e, s in zip(claim, self._victims(set(D))):
             self._put(e, s)
         for e in D:
-            self.used[self.home[e]] = self.clock
-        return [self.home[e] for e in ids], 0, pairs
+            if e in self.home:
+                self.used[self.home[e]] = self.clock
+        rec = lambda e: self.home.get(e, self.S + e)
+        return [rec(e) for e in ids], int(len(D) > self.S), [(e, rec(e)) for e in miss]
 
     def install(self, pred, n_max):
         T, k = len(pred), len(pred[0])
@@ -122,10 +129,23 @@ def _check_invariants(c, ids, slot_ids, mode, pairs, before):
     assert tick == tick0 + 1
     if len(D) > S:
         assert mode == 1
-        assert np.array_equal(so, so0) and np.array_equal(eo, eo0) and np.array_equal(lu, lu0)
         assert [int(p[0]) for p in pairs] == [e for e in D if e not in R0]
+        # residents stay; every slot now holds an expert of D, last used now
+        for e in D:
+            if so0[e] >= 0:
+                assert so[e] == so0[e]
+        assert all(eo[s] in D and lu[s] == tick for s in range(S))
+        # the misses that got a slot were used by at least as many pairs as those staged
+        n_of = {e: int((ids == e).sum()) for e in D}
+        got = [int(p[0]) for p in pairs if p[1] < S]
+        staged = [int(p[0]) for p in pairs if p[1] >= S]
+        assert len(got) + len(staged) == len(pairs) and len(staged) > 0
+        if got:
+            assert min(n_of[e] for e in got) >= max(n_of[e] for e in staged)
+        for p in pairs:
+            assert p[1] == (so[p[0]] if p[1] < S else S + p[0])
         for i, e in np.ndenumerate(ids):
-            assert slot_ids[i] == (so0[e] if so0[e] >= 0 else S + e)
+            assert slot_ids[i] == (so[e] if so[e] >= 0 else S + e)
         return
     assert mode == 0
     assert [int(p[0]) for p in pairs] == [e for e in D if e not in R0]  # misses ascending
@@ -162,7 +182,7 @@ def test_batched_calls_match_brute_force(orc, seed):
             assert [tuple(map(int, r)) for r in got] == exp
             before = c.state()
         slot_ids, mode, pairs = c.ensure(ids)
-        es, em, ep = b.ensure(ids.reshape(-1).tolist())
+        es, em, ep = b.ensure(ids.reshape(-1).tolist(), k)
         assert slot_ids.reshape(-1).tolist() == es
         assert mode == em
         assert [tuple(map(int, r)) for r in pairs] == ep
@@ -181,21 +201,31 @@ def test_enough_capacity_gives_only_compulsory_misses(orc):
 
 def test_staging_threshold_and_free_first(orc):
     c = orc.Cache(8, 3)
-    # three distinct experts fit
+    # three distinct experts fit: misses ascending into the free slots 0, 1, 2
     sid, mode, pairs = c.ensure(np.array([[5, 1], [1, 7]], np.int32))
     assert mode == 0 and pairs.tolist() == [[1, 0], [5, 1], [7, 2]] and sid.tolist() == [[1, 0], [0, 2]]
-    # four distinct do not: staged, state untouched, residents read in place
-    before = c.state()
+    # four distinct do not.  Hits 5 (slot 1) and 1 (slot 0) stay; slot 2 (expert 7, not routed) is
+    # the one eligible victim.  Misses 2 and 3 are each routed once; 3 is at top-k position 0 and 2
+    # at position 1, so 3 claims slot 2 and 2 is staged at S + 2 = 5.
     sid, mode, pairs = c.ensure(np.array([[5, 2], [3, 1]], np.int32))
-    assert mode == 1 and pairs.tolist() == [[2, 5], [3, 6]]
-    assert sid.tolist() == [[1, 5], [6, 0]]
-    after = c.state()
-    assert all(np.array_equal(a, b) for a, b in zip(before[:3], after[:3])) and after[3] == before[3] + 1
-    # LRU victim: expert 5 (slot 1) and 1 (slot 0) and 7 (slot 2) all last used at tick 1 -> lowest slot first
+    assert mode == 1 and pairs.tolist() == [[2, 5], [3, 2]]
+    assert sid.tolist() == [[1, 5], [2, 0]]
+    so, eo, lu, tick = c.state()
+    assert eo.tolist() == [1, 5, 3] and lu.tolist() == [2, 2, 2] and tick == 2 and so[7] == -1 and so[2] == -1
+    cnt = c.counters()
+    assert (cnt["hits"], cnt["misses"], cnt["staged_calls"], cnt["staged_copies"]) == (2, 4, 1, 1)
+    # all slots last used at tick 2: misses 4, 7 take the lowest slots
     sid, mode, pairs = c.ensure(np.array([[4, 7]], np.int32))
-    assert pairs.tolist() == [[4, 0]]
+    assert mode == 0 and pairs.tolist() == [[4, 0], [7, 1]]
     sid, mode, pairs = c.ensure(np.array([[6, 4]], np.int32))
-    assert pairs.tolist() == [[6, 1]]  # slot 1 (tick 1) is older than slot 2 (tick 3)
+    assert pairs.tolist() == [[6, 2]]  # slot 2 (tick 2) is older than slot 1 (tick 3)
+    # an overflow call whose misses outnumber the eligible slots by count: expert 0 is routed by
+    # both tokens, so it claims the one eligible slot (slot 1, expert 7) ahead of experts 1, 2, 3
+    c2 = orc.Cache(8, 2)
+    c2.ensure(np.array([[6, 7]], np.int32))
+    sid, mode, pairs = c2.ensure(np.array([[3, 0, 6], [0, 1, 2]], np.int32))
+    assert mode == 1 and pairs.tolist() == [[0, 1], [1, 3], [2, 4], [3, 5]]
+    assert sid.tolist() == [[5, 1, 0], [1, 3, 4]]
 
 
 def test_invalid_id_leaves_state_untouched(orc):
