@@ -179,9 +179,9 @@ def main():
         after = stats_sum()
         delta = {kk: after[kk] - before[kk] for kk in after}
         assert after["error"] == 0, "device error %d" % after["error"]
-        log("%s: batch %d, %d steps in %.1f ms: %.1f tok/s, misses/token %.2f, staged calls %d/%d" %
-            (tag, T, steps, ms, T * steps * 1e3 / ms, delta["misses"] / (T * steps), delta["staged_calls"],
-             delta["calls"]))
+        log("%s: batch %d, %d steps in %.1f ms: %.1f tok/s, copies/token %.2f (%.2f into slots), staged calls %d/%d" %
+            (tag, T, steps, ms, T * steps * 1e3 / ms, (delta["misses"] + delta["staged_copies"]) / (T * steps),
+             delta["misses"] / (T * steps), delta["staged_calls"], delta["calls"]))
         return T * steps * 1e3 / ms, ms / steps, delta, c, bufs, xs_d
 
     tok_s, ms_step, delta, chain, bufs, xs_d = run_decode(T0, args.warmup, args.steps, "decode")
@@ -244,7 +244,7 @@ def main():
         "decode_stats": {"misses_per_token": round(delta["misses"] / (T0 * args.steps), 4),
                          "staged_calls": delta["staged_calls"], "calls": delta["calls"],
                          "staged_copies_per_token": round(delta["staged_copies"] / (T0 * args.steps), 4),
-                         "hit_rate": round(delta["hits"] / max(1, delta["hits"] + delta["misses"]), 4)},
+                         "hit_rate": round(delta["hits"] / max(1, delta["hits"] + delta["misses"] + delta["staged_copies"]), 4)},
         "roofline": {"bound": "hbm", "kernel": "k_gateup_vec (gate/up + SiLU, decode)",
                      "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
@@ -283,7 +283,7 @@ def main():
     kern = []
     for r in range(4):
         m.moe_offload_reset(hl, stream)
-        m.moe_slot_ensure(hl, ids_all, 16, sid, stream)  # 128 distinct > 26 slots: all 128 staged
+        m.moe_slot_ensure(hl, ids_all, 16, sid, stream)  # cold cache: all 128 experts miss (26 to slots, 102 staged)
         a, b_ = ev(), ev()
         a.record(stream)
         m.moe_copy_misses(hl, stream)

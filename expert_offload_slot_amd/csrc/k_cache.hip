@@ -14,12 +14,12 @@ namespace moe {
 namespace {
 
 // ---------------------------------------------------------------- ensure
-__global__ __launch_bounds__(kBlock) void k_ensure(CacheDev c, const int32_t* __restrict__ ids, int n,
+__global__ __launch_bounds__(kBlock) void k_ensure(CacheDev c, const int32_t* __restrict__ ids, int n, int k,
                                                    int32_t* __restrict__ slot_ids, int audit) {
   __shared__ SharedTable t;
-  __shared__ uint64_t vkey[kMaxExperts];
+  __shared__ uint64_t keys[2 * kMaxExperts];
   load_table(c, t);
-  ensure_body(c, t, ids, n, slot_ids, nullptr, audit, vkey);
+  ensure_body(c, t, ids, n, k, slot_ids, nullptr, audit, keys);
 }
 
 // ---------------------------------------------------------------- prefetch install
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kCopyThreads) void k_copy(const int32_t* __restrict
 }  // namespace
 
 hipError_t launch_ensure(moe_offload* h, const int32_t* ids, int n, int32_t* slot_ids, hipStream_t s) {
-  launch_k(h, MOE_K_ENSURE, k_ensure, dim3(1), dim3(kBlock), 0, s, h->cache, ids, n, slot_ids,
+  launch_k(h, MOE_K_ENSURE, k_ensure, dim3(1), dim3(kBlock), 0, s, h->cache, ids, n, h->k, slot_ids,
                      (h->flags & MOE_FLAG_AUDIT) ? 1 : 0);
   return hipGetLastError();
 }

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kBlock) void k_decide(CacheDev c, const float* __re
     }
   }
   __syncthreads();
-  ensure_body(c, t, ids_l, n, slot_ids, rec_l, audit, u.keys);
+  ensure_body(c, t, ids_l, n, k, slot_ids, rec_l, audit, u.keys);
   __syncthreads();
   if (do_group) group_body(rec_l, n, c.S + c.E, grp, off_pairs, off_tiles, c.err, u.g);
   if (max_n <= 0) return;  // uniform

@@ -22,8 +22,8 @@ struct SharedTable {
   int expert_of[kMaxExperts];
   uint64_t last_use[kMaxExperts];
   int flag[kMaxExperts];   // ensure: expert in D; install: tokens predicting it
-  int aux[kMaxExperts];    // install: best top-k position
-  int cand[kMaxExperts];   // install: candidate expert by rank
+  int aux[kMaxExperts];    // ensure: pairs routed to it; install: best top-k position
+  int cand[kMaxExperts];   // ensure: best top-k position; install: candidate by rank
   int vic[kMaxExperts];    // victim slot by rank
   int wave[4 * kWaves];
   int bad;
@@ -84,23 +84,29 @@ __device__ __forceinline__ void audit_table(const CacheDev& c, const SharedTable
   if (bad) atomicOr(c.err, MOE_DEV_ERR_AUDIT);
 }
 
-// Ensure for the n expert ids of a call (ids may live in LDS or global memory).
-// The table must already be in `t` (load_table, then a barrier).  Writes the
-// record index of every id to slot_ids (global) and, if given, to slot_lds.
-// Record index r < S is slot r; r >= S is staging record r - S.
-//   |D| <= S: misses take victims in (free first, then least recently used,
-//             then lowest slot) order among slots not holding an expert of D;
-//             every expert of D gets last_use = tick.
-//   |D| >  S: staged call; the table is untouched, residents are read in place
-//             and each missing expert e is copied to staging record S + e.
+// Ensure for the n = T*k expert ids of a call (ids may live in LDS or global
+// memory).  The table must already be in `t` (load_table, then a barrier).
+// Writes the record index of every id to slot_ids (global) and, if given, to
+// slot_lds.  Record index r < S is slot r; r >= S is staging record r - S.
+//   victims:  slots not holding an expert of D, in (free first, then least
+//             recently used, then lowest slot) order;
+//   |D| <= S: misses in ascending id take the victims;
+//   |D| >  S: there are fewer victims than misses; the misses claim them in
+//             install order (pairs routed to it desc, best top-k position asc,
+//             id asc) and the rest are copied to staging record S + e for
+//             this call (mode STAGED);
+//   every expert of D holding a slot gets last_use = tick; the copy list holds
+//   the misses in ascending id with their record index;
 //   an id outside [0, E): nothing changes, slot ids are 0, error bit set.
-// vkey: LDS scratch of S entries.  All threads of the block must call it; it
-// ends with the table stored back.
-__device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, const int32_t* ids, int n,
+// keys: LDS scratch of 2 * kMaxExperts entries.  All threads of the block must
+// call it; it ends with the table stored back.
+__device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, const int32_t* ids, int n, int k,
                                             int32_t* __restrict__ slot_ids, int32_t* slot_lds, int audit,
-                                            uint64_t* vkey) {
+                                            uint64_t* keys) {
   const int tid = threadIdx.x;
   const int E = c.E, S = c.S;
+  uint64_t* vkey = keys;
+  uint64_t* ckey = keys + kMaxExperts;
   if (tid < E) t.flag[tid] = 0;
   if (tid == 0) t.bad = 0;
   __syncthreads();
@@ -131,78 +137,90 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
   int rk[4], tot[4];
   block_rank4(f, t.wave, rk, tot);
   const int nd = tot[0], mrank = rk[1], nm = tot[1], nh = tot[2], npf = tot[3];
+  const bool over = nd > S;
 
-  if (nd > S) {  // staged: table untouched, residents read in place, misses staged at S + e
-    if (miss) {
-      c.copy_list[2 + 2 * mrank] = tid;
-      c.copy_list[3 + 2 * mrank] = S + tid;
-    }
-    for (int i = tid; i < n; i += kBlock) {
-      const int e = ids[i];
-      const int r = t.slot_of[e];
-      const int v = r >= 0 ? r : S + e;
-      slot_ids[i] = v;
-      if (slot_lds) slot_lds[i] = v;
-    }
-    if (tid == 0) {
-      c.copy_list[0] = MOE_MODE_STAGED;
-      c.copy_list[1] = nm;
-      *c.tick = tick;
-      c.counters[C_CALLS] = t.cnt[C_CALLS] + 1;
-      c.counters[C_STAGED_CALLS] = t.cnt[C_STAGED_CALLS] + 1;
-      c.counters[C_STAGED_COPIES] = t.cnt[C_STAGED_COPIES] + (uint64_t)nm;
-      c.counters[C_BYTES] = t.cnt[C_BYTES] + (uint64_t)nm * c.record_bytes;
-    }
-    return;  // block-uniform
-  }
-
-  // victims: the nm eligible slots (not holding an expert of D) of smallest key
+  // eligible victims by rank; for an overflow call also each miss's install-order key
+  int ns = 0;  // misses that get a slot
   if (nm > 0) {
+    bool elig = false;
     if (tid < S) {
       const int ex = t.expert_of[tid];
       const bool occ = ex >= 0;
-      vkey[tid] = (!occ || !t.flag[ex]) ? victim_key(occ, t.last_use[tid], tid) : ~0ull;
+      elig = !occ || !t.flag[ex];
+      vkey[tid] = elig ? victim_key(occ, t.last_use[tid], tid) : ~0ull;
     }
-    __syncthreads();
-    if (tid < S) {
-      const uint64_t mine = vkey[tid];
-      if (mine != ~0ull) {
-        int rank = 0;
-#pragma unroll 8
-        for (int s2 = 0; s2 < S; ++s2) rank += vkey[s2] < mine ? 1 : 0;
-        if (rank < nm) t.vic[rank] = tid;
+    if (over) {  // pairs routed to each expert and its best top-k position
+      if (tid < E) {
+        t.aux[tid] = 0;
+        t.cand[tid] = k;
       }
+      __syncthreads();
+      for (int i = tid; i < n; i += kBlock) {
+        const int e = ids[i];
+        atomicAdd(&t.aux[e], 1);
+        atomicMin(&t.cand[e], i % k);
+      }
+    }
+    int nv;
+    (void)block_rank(elig, t.wave, &nv);  // its barriers also publish vkey and the counts
+    ns = nm < nv ? nm : nv;
+    if (over && tid < E)
+      ckey[tid] = miss ? ((uint64_t)(0xfffffu - (uint32_t)t.aux[tid]) << 40) | ((uint64_t)t.cand[tid] << 20) |
+                             (uint64_t)tid
+                       : ~0ull;
+    if (elig) {
+      const uint64_t mine = vkey[tid];
+      int rank = 0;
+#pragma unroll 8
+      for (int s2 = 0; s2 < S; ++s2) rank += vkey[s2] < mine ? 1 : 0;
+      t.vic[rank] = tid;  // rank < nv
     }
     __syncthreads();
     if (miss) {
-      const int v = t.vic[mrank];
-      const int old = t.expert_of[v];
-      if (old >= 0) t.slot_of[old] = -1;
-      t.expert_of[v] = tid;
-      t.slot_of[tid] = v;
+      int crank = mrank;  // claim order: ascending id, or install order when over
+      if (over) {
+        const uint64_t mine = ckey[tid];
+        crank = 0;
+#pragma unroll 8
+        for (int e2 = 0; e2 < E; ++e2) crank += ckey[e2] < mine ? 1 : 0;
+      }
+      int v = S + tid;
+      if (crank < ns) {
+        v = t.vic[crank];
+        const int old = t.expert_of[v];
+        if (old >= 0) t.slot_of[old] = -1;
+        t.expert_of[v] = tid;
+        t.slot_of[tid] = v;
+      }
       c.copy_list[2 + 2 * mrank] = tid;
       c.copy_list[3 + 2 * mrank] = v;
     }
     __syncthreads();
   }
-  if (inD) t.last_use[t.slot_of[tid]] = tick;
+  if (inD && t.slot_of[tid] >= 0) t.last_use[t.slot_of[tid]] = tick;
   __syncthreads();
   for (int i = tid; i < n; i += kBlock) {
-    const int v = t.slot_of[ids[i]];
+    const int e = ids[i];
+    const int r = t.slot_of[e];
+    const int v = r >= 0 ? r : S + e;
     slot_ids[i] = v;
     if (slot_lds) slot_lds[i] = v;
   }
   store_table(c, t);
-  if (audit) audit_table(c, t, true);
+  if (audit) audit_table(c, t, !over);
   if (tid == 0) {
-    c.copy_list[0] = MOE_MODE_SLOTS;
+    c.copy_list[0] = over ? MOE_MODE_STAGED : MOE_MODE_SLOTS;
     c.copy_list[1] = nm;
     *c.tick = tick;
     c.counters[C_CALLS] = t.cnt[C_CALLS] + 1;
     c.counters[C_HITS] = t.cnt[C_HITS] + (uint64_t)nh;
-    c.counters[C_MISSES] = t.cnt[C_MISSES] + (uint64_t)nm;
+    c.counters[C_MISSES] = t.cnt[C_MISSES] + (uint64_t)ns;
     c.counters[C_PF_HITS] = t.cnt[C_PF_HITS] + (uint64_t)npf;
     c.counters[C_BYTES] = t.cnt[C_BYTES] + (uint64_t)nm * c.record_bytes;
+    if (over) {
+      c.counters[C_STAGED_CALLS] = t.cnt[C_STAGED_CALLS] + 1;
+      c.counters[C_STAGED_COPIES] = t.cnt[C_STAGED_COPIES] + (uint64_t)(nm - ns);
+    }
   }
 }
 

@@ -126,10 +126,10 @@ typedef struct {
 
 typedef struct {
   uint64_t calls;             /* ensure + prefill-stage calls */
-  uint64_t hits;              /* distinct routed experts found resident (slot-mode calls) */
-  uint64_t misses;            /* demand misses: records copied into slots */
+  uint64_t hits;              /* distinct routed experts found resident */
+  uint64_t misses;            /* demand misses copied into slots */
   uint64_t staged_calls;      /* calls with more distinct experts than slots */
-  uint64_t staged_copies;     /* records copied into staging by those calls */
+  uint64_t staged_copies;     /* misses of those calls copied into staging */
   uint64_t prefetch_installs; /* experts installed by moe_prefetch_install */
   uint64_t prefetch_hits;     /* installed experts found by a later ensure before any other use */
   uint64_t bytes_copied;      /* bytes moved host -> device by this handle */
@@ -189,12 +189,16 @@ int moe_route_topk(moe_offload* h, const void* x, const void* w_router, const fl
                    int32_t* ids, float* w, void* stream);
 
 /* LRU slot table update for one call (single workgroup, fixed shape):
- * D = distinct ids.  |D| <= S: misses (ascending id) take the free slots,
- * then the least recently used (ties to the lower slot) among slots not
- * holding an expert of D; ids are rewritten to slot ids; the copy list is
- * {SLOTS, |misses|, (expert, slot)...}.  |D| > S: the table is left as is,
- * resident experts are read in place, each missing expert e is staged and
- * rewritten to S + e; copy list {STAGED, n, (e, S + e)...}.
+ * D = distinct ids.  Victims are the slots not holding an expert of D, in
+ * (free first, then least recently used, then lowest slot) order.
+ * |D| <= S: misses (ascending id) take the victims; copy list
+ * {SLOTS, |misses|, (expert, slot)...}.  |D| > S (decode batches wider than
+ * the cache; the page stages whole layers only for prefill): the victims are
+ * fewer than the misses and go to the misses routed by most pairs (then best
+ * top-k position, then lowest id); every other miss e is staged for this call
+ * and read at S + e; copy list {STAGED, |misses|, (expert, slot or S + e)...}
+ * in ascending expert id.  Residents are read in place, ids are rewritten to
+ * record indices, and every expert of D holding a slot becomes most recent.
  *   ids: device [T, k] int32;  slot_ids: device [T, k] int32 (out).
  * Asynchronous, capture-safe; the table's only writer besides install/stage. */
 int moe_slot_ensure(moe_offload* h, const int32_t* ids, int32_t T, int32_t* slot_ids, void* stream);
