@@ -39,7 +39,7 @@ sys.path.insert(0, ROOT)
 E, K_TOP, H, F, SLOTS, LAYERS = 128, 8, 2048, 768, 26, 48
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 LINK_PEAK_GBPS = 64.0           # PCIe 5.0 x16, one direction, published
-COUNTERS = os.path.join(ROOT, "profiles", "k_gateup_vec_decode_b1_counters.md")
+COUNTERS = os.path.join(ROOT, "profiles", "k_gateup_one_decode_b1_counters.md")
 FFN_SRC = os.path.join(ROOT, "expert_offload_slot_amd", "csrc", "k_ffn.hip")
 
 
@@ -245,13 +245,13 @@ def main():
                          "staged_calls": delta["staged_calls"], "calls": delta["calls"],
                          "staged_copies_per_token": round(delta["staged_copies"] / (T0 * args.steps), 4),
                          "hit_rate": round(delta["hits"] / max(1, delta["hits"] + delta["misses"] + delta["staged_copies"]), 4)},
-        "roofline": {"bound": "hbm", "kernel": "k_gateup_vec (gate/up + SiLU, decode)",
+        "roofline": {"bound": "hbm", "kernel": "k_gateup_one<bf16, 16> (gate/up + SiLU, single-token decode)",
                      "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else traffic,
                      "avg_launch_us": round(gu_ms * 1e3 / gu_n, 3), "launches": gu_n,
                      "algorithmic_bytes_per_launch": int(gu_bytes // gu_n)},
-        "roofline_down": {"bound": "hbm", "kernel": "k_down_vec", "achieved": round(dn_gbps, 1),
+        "roofline_down": {"bound": "hbm", "kernel": "k_down_one<bf16, 6>", "achieved": round(dn_gbps, 1),
                           "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dn_gbps / HBM_PEAK_GBPS, 4),
                           "avg_launch_us": round(dn_ms * 1e3 / dn_n, 3),
                           "algorithmic_bytes_per_launch": int(dn_bytes // dn_n)},

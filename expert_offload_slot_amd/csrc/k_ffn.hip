@@ -63,7 +63,7 @@ struct FfnArgs {
   int T, k, H, F, S, E;
   int off_pairs, off_tiles;
   int max_routed;  // record blocks a call can fill: min(T * k, S + E); unused ones are marked empty
-  int pair_items;  // one token: its k records are distinct, so every pair is its own record (no grouping)
+  int pair_items;  // one token: its k records are distinct, so each choice is its own work item (no grouping)
 };
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)rn_to_bf16(f); }
@@ -79,14 +79,12 @@ __global__ __launch_bounds__(kBlock) void k_group(FfnArgs a) {
 // 128-byte record block, so one load trip serves the item.
 struct Item {
   const uint8_t* rec;
-  int n;     // tokens of the item
-  bool sh;   // the always-resident shared expert
-  int pair;  // >= 0: the item is this single (t, j) pair (pair items, no grouping)
+  int n;    // tokens of the item
+  bool sh;  // the always-resident shared expert
 };
 
 __device__ __forceinline__ Item item_record(const FfnArgs& a, int nr, int r) {
   Item it;
-  it.pair = -1;
   if (r < nr) {
     const int32_t* blk = a.grp + kRecWords * (1 + r);
     const int ri = blk[0];
@@ -105,18 +103,7 @@ __device__ __forceinline__ Item item_record(const FfnArgs& a, int nr, int r) {
 // max_routed are real or marked empty (n = 0); r == max_routed is the shared expert.
 __device__ __forceinline__ Item item_block(const FfnArgs& a, int r) {
   Item it;
-  it.pair = -1;
-  if (a.pair_items && r < a.max_routed) {  // max_routed = k here
-    int ri = a.slot_ids[r];
-    if ((unsigned)ri >= (unsigned)(a.S + a.E)) {
-      atomicOr(a.err, MOE_DEV_ERR_AUDIT);
-      ri = 0;
-    }
-    it.rec = ri < a.S ? a.slots + (uint64_t)ri * a.stride : a.staging + (uint64_t)(ri - a.S) * a.stride;
-    it.n = 1;
-    it.sh = false;
-    it.pair = r;
-  } else if (r < a.max_routed) {
+  if (r < a.max_routed) {
     const int32_t* blk = a.grp + kRecWords * (1 + r);
     const int ri = blk[0];
     it.n = blk[1];
@@ -133,7 +120,6 @@ __device__ __forceinline__ Item item_block(const FfnArgs& a, int r) {
 
 // pair id (row of h / part) of entry idx of record r
 __device__ __forceinline__ int item_pair(const FfnArgs& a, const Item& it, int r, int idx) {
-  if (it.pair >= 0) return it.pair;
   if (it.sh) return a.T * a.k + idx;
   const int32_t* blk = a.grp + kRecWords * (1 + r);
   return idx < kInline ? blk[3 + idx] : a.grp[a.off_pairs + blk[2] + idx];
@@ -513,12 +499,24 @@ __device__ __forceinline__ float reduce16_scatter(const float v[16], int c) {
   return mine + __shfl_xor(give, 1);
 }
 
-// Two weight rows (stream 0, stream 1) of length K against up to kVecTok
-// activation rows act[t] (bf16, length K); acc[t][s] gets the lane's partial sums.
-template <bool FP8>
+// v summed over the 16 lanes of a quarter, every lane getting the sum: the same
+// pairing tree as reduce16_scatter (bit 3, then 2, 1, 0), so the same bits.
+__device__ __forceinline__ float reduce16_all(float v) {
+  v += __shfl_xor(v, 8);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 2);
+  return v + __shfl_xor(v, 1);
+}
+
+// Two weight rows (stream 0, stream 1) of length K against up to NT activation
+// rows act[t] (bf16, length K); acc[t][s] gets the lane's partial sums.  NT = 1
+// is the single-token kernel: a few hundred instructions instead of the
+// 8-token unrolled body, which matters because every layer's launch starts
+// with this code cold in the instruction cache.
+template <bool FP8, int NT>
 __device__ __forceinline__ void vec_pass(const uint8_t* row0, const uint8_t* row1, const float* sc0,
-                                         const float* sc1, int nk, int c, const uint16_t* const act[kVecTok],
-                                         int nt, float acc[kVecTok][2]) {
+                                         const float* sc1, int nk, int c, const uint16_t* const act[NT],
+                                         int nt, float acc[NT][2]) {
   for (int k0 = 0; k0 < nk; k0 += kVecK) {
     typename WChunk<FP8>::T w0[kVecK], w1[kVecK];
     float s0[kVecK], s1[kVecK];
@@ -532,7 +530,7 @@ __device__ __forceinline__ void vec_pass(const uint8_t* row0, const uint8_t* row
       }
     }
 #pragma unroll
-    for (int t = 0; t < kVecTok; ++t) {
+    for (int t = 0; t < NT; ++t) {
       if (t < nt) {
         const uint4* xr = reinterpret_cast<const uint4*>(act[t]);
 #pragma unroll
@@ -546,6 +544,39 @@ __device__ __forceinline__ void vec_pass(const uint8_t* row0, const uint8_t* row
       }
     }
   }
+}
+
+// vec_pass for one activation row with CH K blocks per pass and nk a multiple
+// of CH: no per-block guards, so each pass is one unbroken run of loads then
+// pair dots.  Same per-lane order as vec_pass, so the same bits.
+template <bool FP8, int CH>
+__device__ __forceinline__ void one_pass(const uint8_t* row0, const uint8_t* row1, const float* sc0, const float* sc1,
+                                         int nk, int c, const uint16_t* act, float& acc0, float& acc1) {
+  const uint4* xr = reinterpret_cast<const uint4*>(act);
+  for (int k0 = 0; k0 < nk; k0 += CH) {
+    typename WChunk<FP8>::T w0[CH], w1[CH];
+    float s0[CH], s1[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      w0[i] = load_w<FP8>(row0, k0 + i, c);
+      w1[i] = load_w<FP8>(row1, k0 + i, c);
+      s0[i] = FP8 ? sc0[k0 + i] : 1.f;
+      s1[i] = FP8 ? sc1[k0 + i] : 1.f;
+    }
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const uint4 xv = xr[16 * (k0 + i) + c];
+      acc0 = wdot<FP8>(w0[i], xv, acc0, s0[i]);
+      acc1 = wdot<FP8>(w1[i], xv, acc1, s1[i]);
+    }
+  }
+}
+
+// K blocks per pass of the single-token kernels: the largest listed divisor of nk
+inline int one_chunks(int nk) {
+  for (int ch : {16, 8, 6, 4, 2})
+    if (nk % ch == 0) return ch;
+  return 1;
 }
 
 // gate/up: work item = (record, 4 rows of F); quarter q takes row f = 4*g + q of
@@ -578,7 +609,7 @@ __global__ __launch_bounds__(256) void k_gateup_vec(FfnArgs a) {
       float acc[kVecTok][2];
 #pragma unroll
       for (int t = 0; t < kVecTok; ++t) acc[t][0] = acc[t][1] = 0.f;
-      vec_pass<FP8>(wg, wg + mat, sc, sc + nsc, nk, c, act, nt, acc);
+      vec_pass<FP8, kVecTok>(wg, wg + mat, sc, sc + nsc, nk, c, act, nt, acc);
       float v[16];
 #pragma unroll
       for (int t = 0; t < kVecTok; ++t) {
@@ -625,7 +656,7 @@ __global__ __launch_bounds__(256) void k_down_vec(FfnArgs a) {
       float acc[kVecTok][2];
 #pragma unroll
       for (int t = 0; t < kVecTok; ++t) acc[t][0] = acc[t][1] = 0.f;
-      vec_pass<FP8>(wd, wd + 4ull * F * esz, sc, sc, nk, c, act, nt, acc);
+      vec_pass<FP8, kVecTok>(wd, wd + 4ull * F * esz, sc, sc, nk, c, act, nt, acc);
       float v[16];
 #pragma unroll
       for (int t = 0; t < kVecTok; ++t) {
@@ -639,6 +670,96 @@ __global__ __launch_bounds__(256) void k_down_vec(FfnArgs a) {
         part[(uint64_t)p * H + h0 + 4 * (c & 1)] = mine;
       }
     }
+  }
+}
+
+// Single-token calls (T = 1): the k choices are distinct records, so work item
+// (choice j, rows) reads record slot_ids[j] (j = k: the shared expert) against
+// the one activation row, and its pair id is j.  Same rows per wavefront, same
+// per-lane order and the same 16-lane pairing tree as the kernels above, so the
+// same bits; the code is a few hundred instructions instead of the 8-token
+// unrolled body, which every layer's launch fetches cold.
+__device__ __forceinline__ const uint8_t* one_record(const FfnArgs& a, int j) {
+  if (j == a.k) return a.shared;
+  int ri = a.slot_ids[j];
+  if ((unsigned)ri >= (unsigned)(a.S + a.E)) {
+    atomicOr(a.err, MOE_DEV_ERR_AUDIT);
+    ri = 0;
+  }
+  return ri < a.S ? a.slots + (uint64_t)ri * a.stride : a.staging + (uint64_t)(ri - a.S) * a.stride;
+}
+
+template <bool FP8, int CH>
+__global__ __launch_bounds__(256) void k_gateup_one(FfnArgs a) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
+  const int RG = a.F / 4;
+  const int H = a.H, F = a.F;
+  const int nk = H / 128;
+  const uint64_t esz = FP8 ? 1 : 2;
+  const uint64_t mat = (uint64_t)F * H * esz;
+  const int nsc = (F / 128) * (H / 128);
+  const int items = (a.k + (a.shared ? 1 : 0)) * RG;
+  const uint16_t* __restrict__ x = (const uint16_t*)a.x;
+  uint16_t* __restrict__ hb = (uint16_t*)a.hbuf;
+  for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < items; item += gridDim.x * 4) {
+    const int j = item / RG, fg = (item % RG) * 4, f = fg + q;
+    const uint8_t* rec = one_record(a, j);
+    const uint8_t* wg = rec + (uint64_t)f * H * esz;
+    const float* sc = reinterpret_cast<const float*>(rec + 3 * mat) + (fg / 128) * (H / 128);
+    float g = 0.f, up = 0.f;
+    one_pass<FP8, CH>(wg, wg + mat, sc, sc + nsc, nk, c, x, g, up);
+    g = reduce16_all(g);
+    up = reduce16_all(up);
+    if (c == 0) hb[(uint64_t)j * F + f] = f32_to_bf16(silu_mul(g, up));
+  }
+}
+
+template <bool FP8, int CH>
+__global__ __launch_bounds__(256) void k_down_one(FfnArgs a) {
+  const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
+  const int RG = a.H / 8;
+  const int H = a.H, F = a.F;
+  const int nk = F / 128;
+  const uint64_t esz = FP8 ? 1 : 2;
+  const uint64_t mat = (uint64_t)F * H * esz;
+  const int nsc = (F / 128) * (H / 128);
+  const int items = (a.k + (a.shared ? 1 : 0)) * RG;
+  const uint16_t* __restrict__ hb = (const uint16_t*)a.hbuf;
+  float* __restrict__ part = a.part;
+  for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < items; item += gridDim.x * 4) {
+    const int j = item / RG, hg = (item % RG) * 8, h0 = hg + q;
+    const uint8_t* rec = one_record(a, j);
+    const uint8_t* wd = rec + 2 * mat + (uint64_t)h0 * F * esz;
+    const float* sc = reinterpret_cast<const float*>(rec + 3 * mat) + 2 * nsc + (hg / 128) * (F / 128);
+    float s0 = 0.f, s1 = 0.f;
+    one_pass<FP8, CH>(wd, wd + 4ull * F * esz, sc, sc, nk, c, hb + (uint64_t)j * F, s0, s1);
+    s0 = reduce16_all(s0);
+    s1 = reduce16_all(s1);
+    if (c < 2) part[(uint64_t)j * H + h0 + 4 * c] = c ? s1 : s0;
+  }
+}
+
+template <bool FP8>
+void (*gateup_one(int nk))(FfnArgs) {
+  switch (one_chunks(nk)) {
+    case 16: return k_gateup_one<FP8, 16>;
+    case 8: return k_gateup_one<FP8, 8>;
+    case 6: return k_gateup_one<FP8, 6>;
+    case 4: return k_gateup_one<FP8, 4>;
+    case 2: return k_gateup_one<FP8, 2>;
+    default: return k_gateup_one<FP8, 1>;
+  }
+}
+
+template <bool FP8>
+void (*down_one(int nk))(FfnArgs) {
+  switch (one_chunks(nk)) {
+    case 16: return k_down_one<FP8, 16>;
+    case 8: return k_down_one<FP8, 8>;
+    case 6: return k_down_one<FP8, 6>;
+    case 4: return k_down_one<FP8, 4>;
+    case 2: return k_down_one<FP8, 2>;
+    default: return k_down_one<FP8, 1>;
   }
 }
 
@@ -787,8 +908,13 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
     g2 = dim3(std::min(max_items_r * (h->H / kF32Rows), 2048));
     b1 = b2 = dim3(256);
   } else if (T <= kDecodeMaxT) {  // one wavefront per work item, 4 per workgroup
-    gu = fp8 ? k_gateup_vec<true> : k_gateup_vec<false>;
-    dn = fp8 ? k_down_vec<true> : k_down_vec<false>;
+    if (a.pair_items) {
+      gu = fp8 ? gateup_one<true>(h->H / 128) : gateup_one<false>(h->H / 128);
+      dn = fp8 ? down_one<true>(h->F / 128) : down_one<false>(h->F / 128);
+    } else {
+      gu = fp8 ? k_gateup_vec<true> : k_gateup_vec<false>;
+      dn = fp8 ? k_down_vec<true> : k_down_vec<false>;
+    }
     g1 = dim3(std::min((max_items_r * (h->F / 4) + 3) / 4, 8192));
     g2 = dim3(std::min((max_items_r * (h->H / 8) + 3) / 4, 8192));
     b1 = b2 = dim3(256);

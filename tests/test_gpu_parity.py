@@ -96,6 +96,15 @@ def test_bf16_prefill_gemm_one_hot_record():
     run_sequence(2, 2, 2, 128, 256, 1, 0.0, 34, 2, [257, 64])
 
 
+@pytest.mark.parametrize("H,F", [(2048, 512), (1024, 768), (768, 1024), (512, 128), (384, 2048), (1792, 256)])
+@pytest.mark.parametrize("wdt", [1, 2])
+def test_single_token_every_pass_width(H, F, wdt):
+    # one-token calls stream each weight row in passes of 16, 8, 6, 4, 2 or 1 K blocks of 128 (the
+    # largest that divides the row): these shapes reach every width in gate/up (H / 128 blocks) and
+    # in down (F / 128), bf16 and fp8 with the shared expert
+    run_sequence(8, 4, 3, H, F, wdt, 1.2, 40 + H // 128, 6, [1], shared=(wdt == 2))
+
+
 def test_fp8_without_shared_expert():
     run_sequence(10, 5, 2, 128, 256, 2, 1.2, 32, 10, [2, 7])
 
