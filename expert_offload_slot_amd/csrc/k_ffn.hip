@@ -424,8 +424,9 @@ __global__ __launch_bounds__(256) void k_gemm_dn(FfnArgs a) {
 // bf16 pair dot (fp32 accumulate); fp8 codes are widened exactly to bf16 pairs
 // first and each 128-wide K block is scaled on its fp32 partial sum.  The 16
 // lanes' partial sums of the (token, stream) pairs are reduced by a transposing
-// butterfly that leaves pair v's sum in lane v.  Fixed order throughout.
-constexpr int kVecK = 16;    // 128-wide K blocks held per stream (2048 K values)
+// butterfly that leaves pair v's sum in lane v.  Fixed order throughout.  The
+// number of K blocks loaded per pass is a template parameter (one_chunks), so
+// a pass is one unbroken run of loads with no per-block bounds tests.
 constexpr int kVecTok = 8;   // tokens per pass over the held weights (8 x 2 streams = 16 lanes)
 constexpr int kDecodeMaxT = 64;
 
@@ -508,47 +509,40 @@ __device__ __forceinline__ float reduce16_all(float v) {
   return v + __shfl_xor(v, 1);
 }
 
-// Two weight rows (stream 0, stream 1) of length K against up to NT activation
-// rows act[t] (bf16, length K); acc[t][s] gets the lane's partial sums.  NT = 1
-// is the single-token kernel: a few hundred instructions instead of the
-// 8-token unrolled body, which matters because every layer's launch starts
-// with this code cold in the instruction cache.
-template <bool FP8, int NT>
+// Two weight rows (stream 0, stream 1) of length K = 128 * nk against up to
+// kVecTok activation rows act[t] (bf16, length K), CH K blocks per pass (nk a
+// multiple of CH, so no per-block guards); acc[t][s] gets the lane's partial sums.
+template <bool FP8, int CH>
 __device__ __forceinline__ void vec_pass(const uint8_t* row0, const uint8_t* row1, const float* sc0,
-                                         const float* sc1, int nk, int c, const uint16_t* const act[NT],
-                                         int nt, float acc[NT][2]) {
-  for (int k0 = 0; k0 < nk; k0 += kVecK) {
-    typename WChunk<FP8>::T w0[kVecK], w1[kVecK];
-    float s0[kVecK], s1[kVecK];
+                                         const float* sc1, int nk, int c, const uint16_t* const act[kVecTok],
+                                         int nt, float acc[kVecTok][2]) {
+  for (int k0 = 0; k0 < nk; k0 += CH) {
+    typename WChunk<FP8>::T w0[CH], w1[CH];
+    float s0[CH], s1[CH];
 #pragma unroll
-    for (int i = 0; i < kVecK; ++i) {
-      if (k0 + i < nk) {
-        w0[i] = load_w<FP8>(row0, k0 + i, c);
-        w1[i] = load_w<FP8>(row1, k0 + i, c);
-        s0[i] = FP8 ? sc0[k0 + i] : 1.f;
-        s1[i] = FP8 ? sc1[k0 + i] : 1.f;
-      }
+    for (int i = 0; i < CH; ++i) {
+      w0[i] = load_w<FP8>(row0, k0 + i, c);
+      w1[i] = load_w<FP8>(row1, k0 + i, c);
+      s0[i] = FP8 ? sc0[k0 + i] : 1.f;
+      s1[i] = FP8 ? sc1[k0 + i] : 1.f;
     }
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
+    for (int t = 0; t < kVecTok; ++t) {
       if (t < nt) {
         const uint4* xr = reinterpret_cast<const uint4*>(act[t]);
 #pragma unroll
-        for (int i = 0; i < kVecK; ++i) {
-          if (k0 + i < nk) {
-            const uint4 xv = xr[16 * (k0 + i) + c];
-            acc[t][0] = wdot<FP8>(w0[i], xv, acc[t][0], s0[i]);
-            acc[t][1] = wdot<FP8>(w1[i], xv, acc[t][1], s1[i]);
-          }
+        for (int i = 0; i < CH; ++i) {
+          const uint4 xv = xr[16 * (k0 + i) + c];
+          acc[t][0] = wdot<FP8>(w0[i], xv, acc[t][0], s0[i]);
+          acc[t][1] = wdot<FP8>(w1[i], xv, acc[t][1], s1[i]);
         }
       }
     }
   }
 }
 
-// vec_pass for one activation row with CH K blocks per pass and nk a multiple
-// of CH: no per-block guards, so each pass is one unbroken run of loads then
-// pair dots.  Same per-lane order as vec_pass, so the same bits.
+// vec_pass for one activation row: each pass one unbroken run of loads, then
+// the pair dots.  Same per-lane order as vec_pass, so the same bits.
 template <bool FP8, int CH>
 __device__ __forceinline__ void one_pass(const uint8_t* row0, const uint8_t* row1, const float* sc0, const float* sc1,
                                          int nk, int c, const uint16_t* act, float& acc0, float& acc1) {
@@ -572,7 +566,8 @@ __device__ __forceinline__ void one_pass(const uint8_t* row0, const uint8_t* row
   }
 }
 
-// K blocks per pass of the single-token kernels: the largest listed divisor of nk
+// K blocks per pass: the largest listed divisor of nk (16 blocks = 2048 K values
+// per stream held in registers)
 inline int one_chunks(int nk) {
   for (int ch : {16, 8, 6, 4, 2})
     if (nk % ch == 0) return ch;
@@ -581,7 +576,7 @@ inline int one_chunks(int nk) {
 
 // gate/up: work item = (record, 4 rows of F); quarter q takes row f = 4*g + q of
 // gate (stream 0) and up (stream 1); h = silu(gate) * up stored in bf16.
-template <bool FP8>
+template <bool FP8, int CH>
 __global__ __launch_bounds__(256) void k_gateup_vec(FfnArgs a) {
   const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
   const int nrt = a.max_routed + (a.shared ? 1 : 0);
@@ -609,7 +604,7 @@ __global__ __launch_bounds__(256) void k_gateup_vec(FfnArgs a) {
       float acc[kVecTok][2];
 #pragma unroll
       for (int t = 0; t < kVecTok; ++t) acc[t][0] = acc[t][1] = 0.f;
-      vec_pass<FP8, kVecTok>(wg, wg + mat, sc, sc + nsc, nk, c, act, nt, acc);
+      vec_pass<FP8, CH>(wg, wg + mat, sc, sc + nsc, nk, c, act, nt, acc);
       float v[16];
 #pragma unroll
       for (int t = 0; t < kVecTok; ++t) {
@@ -629,7 +624,7 @@ __global__ __launch_bounds__(256) void k_gateup_vec(FfnArgs a) {
 
 // down: work item = (record, 8 rows of H); quarter q takes rows 8*g + q (stream 0)
 // and 8*g + 4 + q (stream 1) against h of the record's pairs; fp32 partial outputs.
-template <bool FP8>
+template <bool FP8, int CH>
 __global__ __launch_bounds__(256) void k_down_vec(FfnArgs a) {
   const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
   const int nrt = a.max_routed + (a.shared ? 1 : 0);
@@ -656,7 +651,7 @@ __global__ __launch_bounds__(256) void k_down_vec(FfnArgs a) {
       float acc[kVecTok][2];
 #pragma unroll
       for (int t = 0; t < kVecTok; ++t) acc[t][0] = acc[t][1] = 0.f;
-      vec_pass<FP8, kVecTok>(wd, wd + 4ull * F * esz, sc, sc, nk, c, act, nt, acc);
+      vec_pass<FP8, CH>(wd, wd + 4ull * F * esz, sc, sc, nk, c, act, nt, acc);
       float v[16];
 #pragma unroll
       for (int t = 0; t < kVecTok; ++t) {
@@ -739,29 +734,29 @@ __global__ __launch_bounds__(256) void k_down_one(FfnArgs a) {
   }
 }
 
-template <bool FP8>
-void (*gateup_one(int nk))(FfnArgs) {
-  switch (one_chunks(nk)) {
-    case 16: return k_gateup_one<FP8, 16>;
-    case 8: return k_gateup_one<FP8, 8>;
-    case 6: return k_gateup_one<FP8, 6>;
-    case 4: return k_gateup_one<FP8, 4>;
-    case 2: return k_gateup_one<FP8, 2>;
-    default: return k_gateup_one<FP8, 1>;
+// kernel instantiation by K blocks per pass
+#define MOE_BY_CHUNKS(KERN, FP8, NK)                   \
+  switch (one_chunks(NK)) {                            \
+    case 16: return KERN<FP8, 16>;                     \
+    case 8: return KERN<FP8, 8>;                       \
+    case 6: return KERN<FP8, 6>;                       \
+    case 4: return KERN<FP8, 4>;                       \
+    case 2: return KERN<FP8, 2>;                       \
+    default: return KERN<FP8, 1>;                      \
   }
-}
 
+typedef void (*FfnKernel)(FfnArgs);
 template <bool FP8>
-void (*down_one(int nk))(FfnArgs) {
-  switch (one_chunks(nk)) {
-    case 16: return k_down_one<FP8, 16>;
-    case 8: return k_down_one<FP8, 8>;
-    case 6: return k_down_one<FP8, 6>;
-    case 4: return k_down_one<FP8, 4>;
-    case 2: return k_down_one<FP8, 2>;
-    default: return k_down_one<FP8, 1>;
-  }
+FfnKernel gateup_decode(bool one, int nk) {
+  if (one) { MOE_BY_CHUNKS(k_gateup_one, FP8, nk) }
+  MOE_BY_CHUNKS(k_gateup_vec, FP8, nk)
 }
+template <bool FP8>
+FfnKernel down_decode(bool one, int nk) {
+  if (one) { MOE_BY_CHUNKS(k_down_one, FP8, nk) }
+  MOE_BY_CHUNKS(k_down_vec, FP8, nk)
+}
+#undef MOE_BY_CHUNKS
 
 // ------------------------------------------------------------------ fp32 path
 __global__ __launch_bounds__(256) void k_gateup_f32(FfnArgs a) {
@@ -908,13 +903,9 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
     g2 = dim3(std::min(max_items_r * (h->H / kF32Rows), 2048));
     b1 = b2 = dim3(256);
   } else if (T <= kDecodeMaxT) {  // one wavefront per work item, 4 per workgroup
-    if (a.pair_items) {
-      gu = fp8 ? gateup_one<true>(h->H / 128) : gateup_one<false>(h->H / 128);
-      dn = fp8 ? down_one<true>(h->F / 128) : down_one<false>(h->F / 128);
-    } else {
-      gu = fp8 ? k_gateup_vec<true> : k_gateup_vec<false>;
-      dn = fp8 ? k_down_vec<true> : k_down_vec<false>;
-    }
+    const bool one = a.pair_items != 0;
+    gu = fp8 ? gateup_decode<true>(one, h->H / 128) : gateup_decode<false>(one, h->H / 128);
+    dn = fp8 ? down_decode<true>(one, h->F / 128) : down_decode<false>(one, h->F / 128);
     g1 = dim3(std::min((max_items_r * (h->F / 4) + 3) / 4, 8192));
     g2 = dim3(std::min((max_items_r * (h->H / 8) + 3) / 4, 8192));
     b1 = b2 = dim3(256);
