@@ -30,7 +30,7 @@ _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB = os.path.join(_HERE, "_build", "libmoe_oracle.so")
 _lib = None
 
-F32, BF16, FP8 = 0, 1, 2
+F32, BF16, FP8, MXFP4 = 0, 1, 2, 3
 SLOTS, STAGED, STAGED_ALL = 0, 1, 2
 
 
@@ -55,6 +55,10 @@ def lib():
         L.orc_f64_to_bf16.restype = ctypes.c_uint16
         L.orc_fp8_to_f64.argtypes = [ctypes.c_uint8]
         L.orc_fp8_to_f64.restype = f64
+        L.orc_e2m1_to_f64.argtypes = [ctypes.c_uint8]
+        L.orc_e2m1_to_f64.restype = f64
+        L.orc_e8m0_to_f64.argtypes = [ctypes.c_uint8]
+        L.orc_e8m0_to_f64.restype = f64
         L.orc_record_bytes.argtypes = [i32, i32, i32]
         L.orc_record_bytes.restype = sz
         L.orc_router_logits.argtypes = [vp, vp, i32, vp, i32, i32, i32, vp]
@@ -107,6 +111,14 @@ def f64_to_bf16(v):
 
 def fp8_to_f64(code):
     return lib().orc_fp8_to_f64(int(code))
+
+
+def e2m1_to_f64(code):
+    return lib().orc_e2m1_to_f64(int(code))
+
+
+def e8m0_to_f64(code):
+    return lib().orc_e8m0_to_f64(int(code))
 
 
 def record_bytes(wdt, H, F):

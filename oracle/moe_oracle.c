@@ -29,7 +29,7 @@
 #include <string.h>
 
 /* weight dtype codes */
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2, ORC_MXFP4 = 3 };
 /* descriptor modes */
 enum { ORC_SLOTS = 0, ORC_STAGED = 1, ORC_STAGED_ALL = 2 };
 /* error codes */
@@ -80,6 +80,22 @@ double orc_fp8_to_f64(uint8_t c) {
   return s ? -v : v;
 }
 
+/* OCP Microscaling (MX) v1.0 FP4 element, E2M1: sign bit 3, exponent bits 2:1
+ * with bias 1, mantissa bit 0, no infinities or NaN.  Normal (e > 0):
+ * (-1)^s 2^(e-1) (1 + m/2); subnormal (e = 0): (-1)^s (m/2).  Magnitudes
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+double orc_e2m1_to_f64(uint8_t c) {
+  int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+  double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return s ? -v : v;
+}
+
+/* MX shared scale, E8M0: 2^(e - 127); e = 255 is NaN. */
+double orc_e8m0_to_f64(uint8_t e) {
+  if (e == 255) return NAN;
+  return ldexp(1.0, (int)e - 127);
+}
+
 static double load_w(const uint8_t* base, int wdt, size_t i) {
   if (wdt == ORC_F32) { float f; memcpy(&f, base + 4 * i, 4); return (double)f; }
   if (wdt == ORC_BF16) { uint16_t b; memcpy(&b, base + 2 * i, 2); return orc_bf16_to_f64(b); }
@@ -97,11 +113,17 @@ static void store_act(void* y, int wdt, size_t i, double v) {
   else ((uint16_t*)y)[i] = orc_f64_to_bf16(v);
 }
 
-/* record = [gate F x H | up F x H | down H x F | fp8 only: scales gate, up, down] */
+/* record = [gate F x H | up F x H | down H x F | scales gate, up, down]
+ *   fp32 / bf16: no scales;
+ *   fp8:   one byte per weight, fp32 scale per 128 x 128 block;
+ *   MXFP4: two E2M1 codes per byte (element 2i in the low nibble, 2i + 1 in
+ *          the high nibble, row-major), one E8M0 scale per 32 consecutive
+ *          weights of a row ([rows][cols / 32] bytes per matrix). */
 size_t orc_record_bytes(int wdt, int H, int F) {
   size_t n = 3 * (size_t)H * (size_t)F;
   if (wdt == ORC_F32) return 4 * n;
   if (wdt == ORC_BF16) return 2 * n;
+  if (wdt == ORC_MXFP4) return n / 2 + n / 32;
   return n + 3 * (size_t)(H / 128) * (size_t)(F / 128) * 4;
 }
 
@@ -486,8 +508,13 @@ void orc_copy(const int32_t* desc, int S, const uint8_t* host, size_t host_strid
   }
 }
 
-/* weight W[n][kk] of a [R][C] matrix at byte offset `off` of a record (fp8: times its block scale) */
+/* weight W[n][kk] of a [R][C] matrix at byte offset `off` of a record (fp8, MXFP4: times its scale) */
 static double weight_at(const uint8_t* rec, int wdt, size_t off, size_t scale_off, int C, int n, int kk) {
+  if (wdt == ORC_MXFP4) {
+    size_t i = (size_t)n * C + kk;
+    uint8_t code = (uint8_t)((rec[off + i / 2] >> (4 * (i & 1))) & 15);
+    return orc_e2m1_to_f64(code) * orc_e8m0_to_f64(rec[scale_off + (size_t)n * (size_t)(C / 32) + (size_t)(kk / 32)]);
+  }
   double v = load_w(rec + off, wdt, (size_t)n * C + kk);
   if (wdt == ORC_FP8) {
     float s;
@@ -502,8 +529,8 @@ static double weight_at(const uint8_t* rec, int wdt, size_t off, size_t scale_of
  *   o = Wd h (H).  Everything in double on exactly widened operands. */
 static void expert_ffn(const uint8_t* rec, int wdt, int H, int F, const double* x, double* h, double* o) {
   size_t esz = wdt == ORC_F32 ? 4 : (wdt == ORC_BF16 ? 2 : 1);
-  size_t mat = (size_t)H * F * esz;
-  size_t nsc = (size_t)(H / 128) * (size_t)(F / 128) * 4;
+  size_t mat = wdt == ORC_MXFP4 ? (size_t)H * F / 2 : (size_t)H * F * esz;
+  size_t nsc = wdt == ORC_MXFP4 ? (size_t)H * F / 32 : (size_t)(H / 128) * (size_t)(F / 128) * 4;
   size_t sc0 = 3 * mat;
 #pragma omp parallel for schedule(static)
   for (int f = 0; f < F; ++f) {

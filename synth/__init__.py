@@ -16,7 +16,7 @@ _SRC = os.path.join(_HERE, "synth.c")
 _LIB = os.path.join(_HERE, "_build", "libsynth.so")
 _lib = None
 
-F32, BF16, FP8 = 0, 1, 2
+F32, BF16, FP8, MXFP4 = 0, 1, 2, 3
 
 
 def build():

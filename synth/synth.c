@@ -125,19 +125,65 @@ void syn_encode_e4m3(const float* in, uint64_t n, uint8_t* out) {
   for (uint64_t i = 0; i < n; ++i) out[i] = to_e4m3_rne_sat(in[i]);
 }
 
-/* weight dtype codes: 0 = fp32, 1 = bf16, 2 = fp8 e4m3 with 128x128 fp32 block scales */
+/* OCP MX v1.0 FP4 (E2M1) code of v: round to nearest, ties to the code with an
+ * even mantissa bit, magnitudes above 6 saturate to 6. */
+static uint8_t to_e2m1_rne_sat(float v) {
+  static const float mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+  float a = fabsf(v);
+  int best = 0;
+  for (int c = 1; c < 8; ++c) {
+    float d = fabsf(a - mag[c]), db = fabsf(a - mag[best]);
+    if (d < db || (d == db && (c & 1) == 0)) best = c;
+  }
+  return (uint8_t)((v < 0.0f && best != 0 ? 8 : 0) | best);
+}
+
+/* weight dtype codes: 0 = fp32, 1 = bf16, 2 = fp8 e4m3 with 128x128 fp32 block
+ * scales, 3 = MXFP4 (E2M1 codes, two per byte, E8M0 scale per 32 weights of a row) */
 uint64_t syn_record_bytes(int wdt, int H, int F) {
   uint64_t n = 3ull * (uint64_t)H * (uint64_t)F;
   if (wdt == 0) return 4 * n;
   if (wdt == 1) return 2 * n;
+  if (wdt == 3) return n / 2 + n / 32;
   return n + 3ull * (uint64_t)(H / 128) * (uint64_t)(F / 128) * 4ull;
 }
 
 /* Fill one weight matrix [R][C] (row-major) of one expert into dst.
  * fp8: per 128x128 block, scale = amax/448 and q = e4m3(w/scale); the scales
- * ([R/128][C/128], fp32) go to sdst. */
-static void fill_matrix(uint64_t seed, uint64_t stream, int R, int C, int wdt, float sigma, uint8_t* dst, float* sdst) {
-  if (wdt == 0) {
+ * ([R/128][C/128], fp32) go to sdst.
+ * MXFP4 (OCP MX v1.0 conversion): per 32 weights of a row, shared exponent
+ * floor(log2(amax)) - 2 (2 = E2M1's largest exponent), X = 2^that,
+ * q = e2m1(w / X); the E8M0 bytes ([R][C/32]) go to sdst. */
+static void fill_matrix(uint64_t seed, uint64_t stream, int R, int C, int wdt, float sigma, uint8_t* dst, void* sdst) {
+  if (wdt == 3) {
+    uint8_t* sc = (uint8_t*)sdst;
+    for (int r = 0; r < R; ++r)
+      for (int cb = 0; cb < C / 32; ++cb) {
+        uint64_t base = (uint64_t)r * (uint64_t)C + (uint64_t)cb * 32;
+        float w[32], amax = 0.0f;
+        for (int c = 0; c < 32; c += 4) {
+          float z[4];
+          normals4(seed, stream, (base + (uint64_t)c) >> 2, z);
+          for (int q = 0; q < 4; ++q) {
+            w[c + q] = sigma * z[q];
+            if (fabsf(w[c + q]) > amax) amax = fabsf(w[c + q]);
+          }
+        }
+        int e2 = 0;
+        if (amax > 0.0f) {
+          frexpf(amax, &e2); /* amax in [2^(e2-1), 2^e2) */
+          e2 = e2 - 1 - 2;
+        }
+        if (e2 < -127) e2 = -127;
+        if (e2 > 127) e2 = 127;
+        sc[(uint64_t)r * (uint64_t)(C / 32) + (uint64_t)cb] = (uint8_t)(e2 + 127);
+        const float inv = ldexpf(1.0f, -e2);
+        for (int c = 0; c < 32; c += 2) {
+          uint8_t lo = to_e2m1_rne_sat(w[c] * inv), hi = to_e2m1_rne_sat(w[c + 1] * inv);
+          dst[(base + (uint64_t)c) / 2] = (uint8_t)(lo | (hi << 4));
+        }
+      }
+  } else if (wdt == 0) {
     float* o = (float*)dst;
     for (int64_t i = 0; i < (int64_t)R * C; i += 4) {
       float z[4];
@@ -171,7 +217,7 @@ static void fill_matrix(uint64_t seed, uint64_t stream, int R, int C, int wdt, f
           }
         }
         float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
-        sdst[rb * CB + cb] = scale;
+        ((float*)sdst)[rb * CB + cb] = scale;
         for (int r = 0; r < B; ++r) {
           uint8_t* orow = dst + (uint64_t)(rb * B + r) * (uint64_t)C + (uint64_t)cb * B;
           for (int c = 0; c < B; ++c) orow[c] = to_e4m3_rne_sat(blk[r * B + c] / scale);
@@ -181,12 +227,12 @@ static void fill_matrix(uint64_t seed, uint64_t stream, int R, int C, int wdt, f
 }
 
 /* Expert records e0 .. e0+count-1 of `layer` into dst (record i at dst + i*stride).
- * Record = [gate F x H | up F x H | down H x F | scales (fp8 only): gate, up, down].
+ * Record = [gate F x H | up F x H | down H x F | scales (fp8, MXFP4): gate, up, down].
  * shared != 0 draws the layer's shared expert instead (count must be 1). */
 void syn_fill_records(uint64_t seed, int layer, int e0, int count, int H, int F, int wdt, float sigma,
                       uint8_t* dst, uint64_t stride, int shared) {
   uint64_t esz = wdt == 0 ? 4 : (wdt == 1 ? 2 : 1);
-  uint64_t mat = (uint64_t)H * (uint64_t)F * esz;
+  uint64_t mat = wdt == 3 ? (uint64_t)H * (uint64_t)F / 2 : (uint64_t)H * (uint64_t)F * esz;
   uint64_t nsc = (uint64_t)(H / 128) * (uint64_t)(F / 128);
 #pragma omp parallel for collapse(2) schedule(dynamic, 1)
   for (int i = 0; i < count; ++i)
@@ -194,7 +240,9 @@ void syn_fill_records(uint64_t seed, int layer, int e0, int count, int H, int F,
       uint8_t* rec = dst + (uint64_t)i * stride;
       uint64_t sid = stream_id(shared ? KIND_SHARED : KIND_EXPERT, (uint64_t)layer, (uint64_t)(e0 + i), (uint64_t)part);
       int R = part < 2 ? F : H, C = part < 2 ? H : F;
-      float* sc = wdt == 2 ? (float*)(rec + 3 * mat) + (uint64_t)part * nsc : NULL;
+      void* sc = wdt == 2   ? (void*)((float*)(rec + 3 * mat) + (uint64_t)part * nsc)
+                 : wdt == 3 ? (void*)(rec + 3 * mat + (uint64_t)part * ((uint64_t)H * (uint64_t)F / 32))
+                            : NULL;
       fill_matrix(seed, sid, R, C, wdt, sigma, rec + (uint64_t)part * mat, sc);
     }
 }

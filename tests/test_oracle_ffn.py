@@ -1,8 +1,11 @@
 """Pins for the oracle's expert FFN and combine.
 
   * numpy float64 matrix products on records decoded with torch's own
-    bf16 / float8_e4m3fn dtypes (the brute force; no cache involved) agree
-    with the oracle to 1e-12 relative;
+    bf16 / float8_e4m3fn / float8_e8m0fnu dtypes and the E2M1 bit-field
+    formula (the brute force; no cache involved) agree with the oracle to
+    1e-12 relative;
+  * an MXFP4 record and a bf16 record holding the same weights (every MXFP4
+    weight is a bf16 value) give bitwise identical oracle outputs;
   * placement invariance: outputs through the oracle's own slot copies are
     bitwise identical at every slot count S = k..E and with every call
     staged, and equal the cache-free result (the pages' statement that
@@ -15,6 +18,23 @@ import pytest
 import torch
 
 
+def e2m1_closed_form(code):
+    # OCP MX v1.0 E2M1 bit fields: sign bit 3, exponent bits 2:1 (bias 1), mantissa bit 0
+    s, e, m = (code >> 3) & 1, (code >> 1) & 3, code & 1
+    mag = m / 2.0 if e == 0 else 2.0 ** (e - 1) * (1.0 + m / 2.0)
+    return -mag if s else mag
+
+
+def _decode_mx(rec_codes, rec_scales, R, C):
+    # codes: two per byte, element 2i in the low nibble; scales: E8M0, one per 32 of a row
+    b = np.frombuffer(rec_codes[:R * C // 2].tobytes(), np.uint8)
+    codes = np.stack([b & 15, b >> 4], axis=1).reshape(-1)
+    lut = np.array([e2m1_closed_form(c) for c in range(16)])
+    sc = torch.from_numpy(np.frombuffer(rec_scales[:R * C // 32].tobytes(), np.uint8).copy()).view(
+        torch.float8_e8m0fnu).double().numpy()
+    return lut[codes].reshape(R, C) * np.repeat(sc.reshape(R, C // 32), 32, axis=1)
+
+
 def _decode(raw, wdt, n):
     if wdt == 0:
         return np.frombuffer(raw[:4 * n].tobytes(), np.float32).astype(np.float64)
@@ -25,6 +45,10 @@ def _decode(raw, wdt, n):
 
 def expert_mats(rec, wdt, H, F):
     n = H * F
+    if wdt == 3:
+        sc0 = 3 * n // 2
+        return (_decode_mx(rec[0:], rec[sc0:], F, H), _decode_mx(rec[n // 2:], rec[sc0 + n // 32:], F, H),
+                _decode_mx(rec[n:], rec[sc0 + 2 * n // 32:], H, F))
     esz = {0: 4, 1: 2, 2: 1}[wdt]
     g = _decode(rec[0:], wdt, n).reshape(F, H)
     u = _decode(rec[esz * n:], wdt, n).reshape(F, H)
@@ -68,6 +92,7 @@ CASES = [  # wdt, E, k, H, F, T
     (0, 8, 2, 64, 128, 4),
     (1, 16, 4, 128, 64, 3),
     (2, 6, 2, 256, 256, 2),
+    (3, 6, 2, 256, 512, 2),
 ]
 
 
@@ -77,7 +102,7 @@ def test_ffn_matches_numpy_brute_force(orc, syn, wdt, E, k, H, F, T):
     wr, b = syn.router(21, 0, E, H, wdt, zipf_s=0.0)
     x = syn.tokens(21, 9, T, H, 1, 0.0, wdt)[0]
     ids, w, _ = orc.route(x, wr, b, k, wdt)
-    shared = syn.records(21, 0, 1, H, F, wdt, shared=True)[0] if wdt == 2 else None
+    shared = syn.records(21, 0, 1, H, F, wdt, shared=True)[0] if wdt >= 2 else None
     y, y64 = orc.ffn(x, wdt, H, F, orc.host_records(host, ids), w, shared, want_f64=True)
     ref = brute_layer(x, host, ids, w, wdt, H, F, shared)
     assert np.max(np.abs(y64 - ref)) <= 1e-12 * np.max(np.abs(ref))
@@ -184,3 +209,21 @@ def test_prenorm_chain_stays_bounded(orc, syn):
             rms[norm] = np.inf
     assert rms[True] < 2.0
     assert rms[False] > 2 * rms[True]
+
+
+def test_mxfp4_equals_bf16_record_of_the_same_weights(orc, syn):
+    E, k, H, F, T = 4, 2, 256, 256, 3
+    mx = syn.records(23, 0, E, H, F, 3)
+    bf = np.zeros((E, orc.record_bytes(1, H, F)), np.uint8)
+    for e in range(E):
+        g, u, d = expert_mats(mx[e], 3, H, F)
+        w = np.concatenate([g.reshape(-1), u.reshape(-1), d.reshape(-1)])
+        bits = torch.from_numpy(w).to(torch.bfloat16)
+        assert np.array_equal(bits.double().numpy(), w)  # each weight is exactly a bf16 value
+        bf[e] = bits.view(torch.int16).numpy().view(np.uint8)
+    wr, b = syn.router(23, 0, E, H, 1, zipf_s=0.0)
+    x = syn.tokens(23, 4, T, H, 1, 0.0, 1)[0]
+    ids, w, _ = orc.route(x, wr, b, k, 1)
+    y3, y3_64 = orc.ffn(x, 3, H, F, orc.host_records(mx, ids), w, want_f64=True)
+    y1, y1_64 = orc.ffn(x, 1, H, F, orc.host_records(bf, ids), w, want_f64=True)
+    assert np.array_equal(y3_64, y1_64) and np.array_equal(y3, y1)

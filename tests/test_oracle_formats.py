@@ -112,3 +112,45 @@ def test_record_sizes_agree(orc, syn):
     assert orc.record_bytes(1, 2048, 768) == 9437184
     assert orc.record_bytes(1, 4096, 14336) == 352321536
     assert orc.record_bytes(2, 7168, 2048) == 44050944
+
+
+def test_e2m1_decode_all_codes(orc):
+    # OCP MX v1.0 FP4: sign, 2 exponent bits with bias 1, 1 mantissa bit; no inf/NaN.
+    # Closed form written from the bit fields, separately from the oracle's expression.
+    for code in range(16):
+        sign = -1.0 if code & 8 else 1.0
+        e, m = (code >> 1) & 3, code & 1
+        want = sign * (0.5 * m if e == 0 else (1 + 0.5 * m) * 2.0 ** (e - 1))
+        got = orc.e2m1_to_f64(code)
+        assert got == want and math.copysign(1.0, got) == sign, code
+    mags = sorted({abs(orc.e2m1_to_f64(c)) for c in range(16)})
+    assert mags == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]  # largest normal 6, smallest subnormal 0.5
+
+
+def test_e8m0_decode_matches_torch(orc):
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e8m0fnu).double().numpy()
+    for c in range(256):
+        got = orc.e8m0_to_f64(c)
+        if c == 255:
+            assert math.isnan(got) and math.isnan(ref[c])
+        else:
+            assert got == ref[c] == 2.0 ** (c - 127)
+
+
+def test_mxfp4_record_size_and_generator(orc, syn):
+    for H, F in ((256, 512), (2048, 768), (7168, 2048)):
+        n = 3 * H * F
+        assert orc.record_bytes(3, H, F) == syn.record_bytes(3, H, F) == n // 2 + n // 32
+    H, F = 512, 256
+    rec = syn.records(3, 1, 1, H, F, 3)[0]
+    n = H * F
+    codes = np.frombuffer(rec[:3 * n // 2].tobytes(), np.uint8)
+    scales = rec[3 * n // 2:3 * n // 2 + 3 * n // 32]
+    lut = np.array([orc.e2m1_to_f64(c) for c in range(16)])
+    vals = lut[np.stack([codes & 15, codes >> 4], axis=1).reshape(-1)].reshape(-1, 32)
+    # OCP conversion: X = 2^(floor(log2 amax) - 2), so each block's largest |w| / X lies in [4, 8)
+    # and rounds to 4 or 6 (saturating); the dequantized weights keep sigma = 0.02
+    assert set(np.abs(vals).max(axis=1).tolist()) <= {4.0, 6.0}
+    deq = vals * np.array([orc.e8m0_to_f64(int(e)) for e in scales])[:, None]
+    assert abs(deq.std() - 0.02) < 0.002 and abs(deq.mean()) < 5e-4
