@@ -17,7 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "_build", "libmoe_offload.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe_offload.h")
 
-F32, BF16, FP8 = 0, 1, 2
+F32, BF16, FP8, MXFP4 = 0, 1, 2, 3
 MODE_SLOTS, MODE_STAGED, MODE_STAGED_ALL = 0, 1, 2
 FLAG_AUDIT, FLAG_HOST_COHERENT = 1, 2
 DEV_ERR_BAD_ID, DEV_ERR_NAN, DEV_ERR_AUDIT = 1, 2, 4

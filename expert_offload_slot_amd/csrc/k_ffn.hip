@@ -28,6 +28,8 @@
 //              residual add, and optionally the next block's RMS norm.
 // fp8 records: e4m3 codes are widened exactly to bf16 by the hardware pair
 // converter and each 128-wide K block is scaled on its fp32 partial sum.
+// MXFP4 records: E2M1 codes are widened by the hardware scaled converter with
+// their row's E8M0 block scale folded in (a power of two: the bf16 is exact).
 //
 // Nothing depends on which slot holds an expert, on S, or on the order of the
 // tokens inside a record's list: every output element is one fixed-order sum.
@@ -159,13 +161,62 @@ __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// ------------------------------------------------------------------ prefill GEMMs (bf16, fp8)
+// ------------------------------------------------------------------ weight formats
+// Kernels with bf16 activations take the weight format W (the moe_dtype code):
+//   bf16:  2 bytes per weight, no scales;
+//   fp8:   e4m3 codes, an fp32 scale per 128 x 128 block of a matrix;
+//   MXFP4: E2M1 codes two per byte (element 2i in the low nibble), an E8M0
+//          scale (2^(e - 127)) per 32 consecutive weights of a row.
+// Record = gate [F][H] | up [F][H] | down [H][F] codes, then the scales of
+// gate, up, down.  Codes are widened exactly to bf16 (MXFP4 with its scale
+// folded in, a power of two, so the bf16 value is exact); fp8 block scales
+// multiply fp32 partial sums.
+constexpr int kBf16 = MOE_BF16, kFp8 = MOE_FP8_E4M3_B128, kMx4 = MOE_MXFP4;
+
+template <int W>
+__device__ __forceinline__ uint64_t code_bytes(uint64_t n) {
+  return W == kBf16 ? 2 * n : (W == kFp8 ? n : n / 2);
+}
+
+// scale base of row r of matrix m (0 gate, 1 up, 2 down; C columns):
+// fp8: its 128-row block's fp32 scales; MXFP4: the row's E8M0 bytes
+template <int W>
+__device__ __forceinline__ const uint8_t* scale_row(const uint8_t* rec, uint64_t mat, int F, int H, int m, int r,
+                                                    int C) {
+  if (W == kFp8)
+    return rec + 3 * mat + 4 * ((uint64_t)m * (F / 128) * (H / 128) + (uint64_t)(r / 128) * (C / 128));
+  if (W == kMx4) return rec + 3 * mat + (uint64_t)m * ((uint64_t)F * H / 32) + (uint64_t)r * (C / 32);
+  return rec;
+}
+
+__device__ __forceinline__ float e8m0_scale(uint32_t e) {
+  return __uint_as_float(e == 0 ? 0x00400000u : (e == 255 ? 0x7fc00000u : e << 23));
+}
+
+template <int B>
+__device__ __forceinline__ uint32_t cvt2_fp4(uint32_t d, float s) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, B));
+}
+
+// 16 E2M1 codes times scale s, widened to 16 bf16
+__device__ __forceinline__ void widen16_fp4(uint2 q, float s, uint4& lo, uint4& hi) {
+  lo.x = cvt2_fp4<0>(q.x, s);
+  lo.y = cvt2_fp4<1>(q.x, s);
+  lo.z = cvt2_fp4<2>(q.x, s);
+  lo.w = cvt2_fp4<3>(q.x, s);
+  hi.x = cvt2_fp4<0>(q.y, s);
+  hi.y = cvt2_fp4<1>(q.y, s);
+  hi.z = cvt2_fp4<2>(q.y, s);
+  hi.w = cvt2_fp4<3>(q.y, s);
+}
+
+// ------------------------------------------------------------------ prefill GEMMs (bf16, fp8, MXFP4)
 // Many tokens per record: a call becomes a grouped GEMM over record tiles.
 // Work item = (tile of kGemmTok pairs of one record, kGemmRows weight rows);
 // the items of a call follow the tile starts of the group descriptor (routed
 // records, then the shared expert's ceil(T / kGemmTok) tiles).  A 256-thread
 // workgroup stages kGemmK-wide K slices of its weight rows and of its gathered
-// token rows through LDS with coalesced 16-byte loads (fp8 codes widened
+// token rows through LDS with coalesced loads (fp8 and MXFP4 codes widened
 // exactly to bf16 on the way in), loads the next slice into registers while
 // the current one feeds bf16 MFMA 16x16x32 tiles, and each wavefront owns a
 // 32 x 32 corner of the 64 x 64 output tile.  fp8: one scale per 128 x 128
@@ -211,25 +262,37 @@ __device__ __forceinline__ int gemm_tiles(const FfnArgs& a, int nr, int* routed)
   return *routed + (a.shared ? (a.T + kGemmTok - 1) / kGemmTok : 0);
 }
 
-// one K slice of NM weight matrices (kGemmRows rows each, row stride K elements)
-// and of the tile's token rows, from memory into registers
-template <bool FP8, int NM>
+// one K slice of NM weight matrices (kGemmRows rows each, row stride K weights)
+// and of the tile's token rows, from memory into registers.
+//   bf16:  2 x 16 bytes per matrix (rows tid/8 and tid/8 + 32, 8 weights each);
+//   fp8:   16 codes of row tid/4;  MXFP4: 16 codes of row tid/4 and their scale.
+template <int W, int NM>
 struct Slice {
-  uint4 a[FP8 ? NM : 2 * NM];  // bf16: 2 per matrix (rows tid/8 and tid/8 + 32); fp8: 1 (row tid/4)
-  uint4 b[2];                  // token rows tid/8 and tid/8 + 32
+  static constexpr int NA = W == kBf16 ? 2 : 1;
+  uint4 a[NA * NM];  // MXFP4 uses .x, .y
+  float s[NM];
+  uint4 b[2];        // token rows tid/8 and tid/8 + 32
 
-  __device__ __forceinline__ void load(const uint8_t* w0, uint64_t mat, int K, int k0,
-                                       const uint16_t* const bp[2]) {
+  // w0: row 0 of the tile in matrix 0, matrices mat bytes apart; sr0: for
+  // MXFP4, the scale bytes of row 0 of the tile in matrix 0, matrices sstride apart
+  __device__ __forceinline__ void load(const uint8_t* w0, uint64_t mat, const uint8_t* sr0, uint64_t sstride, int K,
+                                       int k0, const uint16_t* const bp[2]) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      if (FP8) {
-        a[m] = *reinterpret_cast<const uint4*>(w0 + m * mat + (uint64_t)(tid >> 2) * K + k0 + (tid & 3) * 16);
-      } else {
+      if (W == kBf16) {
 #pragma unroll
         for (int q = 0; q < 2; ++q)
           a[2 * m + q] = *reinterpret_cast<const uint4*>(
               w0 + m * mat + ((uint64_t)((tid >> 3) + 32 * q) * K + k0 + (tid & 7) * 8) * 2);
+      } else if (W == kFp8) {
+        a[m] = *reinterpret_cast<const uint4*>(w0 + m * mat + (uint64_t)(tid >> 2) * K + k0 + (tid & 3) * 16);
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(w0 + m * mat + ((uint64_t)(tid >> 2) * K + k0) / 2 +
+                                                        (tid & 3) * 8);
+        a[m].x = v.x;
+        a[m].y = v.y;
+        s[m] = e8m0_scale(sr0[m * sstride + (uint64_t)(tid >> 2) * (K / 32) + (k0 + (tid & 3) * 16) / 32]);
       }
     }
 #pragma unroll
@@ -240,16 +303,17 @@ struct Slice {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      if (FP8) {
-        uint4 lo, hi;
-        widen16(a[m], lo, hi);
-        uint4* d = reinterpret_cast<uint4*>(&As[m][tid >> 2][(tid & 3) * 16]);
-        d[0] = lo;
-        d[1] = hi;
-      } else {
+      if (W == kBf16) {
 #pragma unroll
         for (int q = 0; q < 2; ++q)
           *reinterpret_cast<uint4*>(&As[m][(tid >> 3) + 32 * q][(tid & 7) * 8]) = a[2 * m + q];
+      } else {
+        uint4 lo, hi;
+        if (W == kFp8) widen16(a[m], lo, hi);
+        else widen16_fp4(make_uint2(a[m].x, a[m].y), s[m], lo, hi);
+        uint4* d = reinterpret_cast<uint4*>(&As[m][tid >> 2][(tid & 3) * 16]);
+        d[0] = lo;
+        d[1] = hi;
       }
     }
 #pragma unroll
@@ -258,8 +322,8 @@ struct Slice {
 };
 
 // acc[m][i][j] += the wavefront's 32 x 32 corner (row tiles i, token tiles j) of
-// matrix m over the LDS slice; fp8: the slice's sum is scaled by sc[m] first
-template <bool FP8, int NM>
+// matrix m over the LDS slice; SC (fp8): the slice's sum is scaled by sc[m] first
+template <bool SC, int NM>
 __device__ __forceinline__ void gemm_slice(const uint16_t (*As)[kGemmRows][kLdsRow], const uint16_t (*Bs)[kLdsRow],
                                            const float* sc, f32x4 acc[NM][2][2]) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -270,7 +334,7 @@ __device__ __forceinline__ void gemm_slice(const uint16_t (*As)[kGemmRows][kLdsR
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) part[m][i][j] = FP8 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[m][i][j];
+      for (int j = 0; j < 2; ++j) part[m][i][j] = SC ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[m][i][j];
 #pragma unroll
   for (int ks = 0; ks < kGemmK; ks += 32) {
     bf16x8 bf[2];
@@ -290,11 +354,11 @@ __device__ __forceinline__ void gemm_slice(const uint16_t (*As)[kGemmRows][kLdsR
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[m][i][j] = FP8 ? fma4(sc[m], part[m][i][j], acc[m][i][j]) : part[m][i][j];
+      for (int j = 0; j < 2; ++j) acc[m][i][j] = SC ? fma4(sc[m], part[m][i][j], acc[m][i][j]) : part[m][i][j];
 }
 
 // gate/up: C[f][p] = W[f] . x[token(p)] for gate and up, h = silu(gate) * up in bf16
-template <bool FP8>
+template <int W>
 __global__ __launch_bounds__(256) void k_gemm_gu(FfnArgs a) {
   __shared__ uint16_t As[2][kGemmRows][kLdsRow];
   __shared__ uint16_t Bs[kGemmTok][kLdsRow];
@@ -303,8 +367,8 @@ __global__ __launch_bounds__(256) void k_gemm_gu(FfnArgs a) {
   int routed;
   const int ntiles = gemm_tiles(a, nr, &routed);
   const int H = a.H, F = a.F, RT = F / kGemmRows, nk = H / kGemmK;
-  const uint64_t esz = FP8 ? 1 : 2;
-  const uint64_t mat = (uint64_t)F * H * esz;
+  const uint64_t mat = code_bytes<W>((uint64_t)F * H);
+  const uint64_t sstride = (uint64_t)F * H / 32;  // MXFP4 scale bytes per matrix
   const int nsc = (F / 128) * (H / 128);
   const uint16_t* __restrict__ x = (const uint16_t*)a.x;
   uint16_t* __restrict__ hb = (uint16_t*)a.hbuf;
@@ -318,8 +382,9 @@ __global__ __launch_bounds__(256) void k_gemm_gu(FfnArgs a) {
       bp[q] = idx < n_here ? x + (uint64_t)pair_token(a, item_pair(a, g.it, g.r, g.n0 + idx)) * H + (tid & 7) * 8
                            : nullptr;
     }
-    const uint8_t* w0 = g.it.rec + (uint64_t)m0 * H * esz;
-    const float* sc = reinterpret_cast<const float*>(g.it.rec + 3 * mat) + (m0 / 128) * (H / 128);
+    const uint8_t* w0 = g.it.rec + code_bytes<W>((uint64_t)m0 * H);
+    const uint8_t* sr0 = scale_row<W>(g.it.rec, mat, F, H, 0, m0, H);
+    const float* sc = reinterpret_cast<const float*>(sr0);  // fp8: this row block's scales of gate
     f32x4 acc[2][2][2];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
@@ -327,15 +392,16 @@ __global__ __launch_bounds__(256) void k_gemm_gu(FfnArgs a) {
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    Slice<FP8, 2> sl;
-    sl.load(w0, mat, H, 0, bp);
+    Slice<W, 2> sl;
+    sl.load(w0, mat, sr0, sstride, H, 0, bp);
     for (int kb = 0; kb < nk; ++kb) {
       __syncthreads();  // the previous slice (or item) is no longer read
       sl.store(As, Bs);
       __syncthreads();
-      if (kb + 1 < nk) sl.load(w0, mat, H, (kb + 1) * kGemmK, bp);
-      const float s2[2] = {FP8 ? sc[(kb * kGemmK) / 128] : 1.f, FP8 ? sc[nsc + (kb * kGemmK) / 128] : 1.f};
-      gemm_slice<FP8, 2>(As, Bs, s2, acc);
+      if (kb + 1 < nk) sl.load(w0, mat, sr0, sstride, H, (kb + 1) * kGemmK, bp);
+      const float s2[2] = {W == kFp8 ? sc[(kb * kGemmK) / 128] : 1.f,
+                           W == kFp8 ? sc[nsc + (kb * kGemmK) / 128] : 1.f};
+      gemm_slice<W == kFp8, 2>(As, Bs, s2, acc);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -359,7 +425,7 @@ __global__ __launch_bounds__(256) void k_gemm_gu(FfnArgs a) {
 }
 
 // down: part[p][r] = Wd[r] . h[p] (fp32 partial outputs)
-template <bool FP8>
+template <int W>
 __global__ __launch_bounds__(256) void k_gemm_dn(FfnArgs a) {
   __shared__ uint16_t As[1][kGemmRows][kLdsRow];
   __shared__ uint16_t Bs[kGemmTok][kLdsRow];
@@ -368,9 +434,7 @@ __global__ __launch_bounds__(256) void k_gemm_dn(FfnArgs a) {
   int routed;
   const int ntiles = gemm_tiles(a, nr, &routed);
   const int H = a.H, F = a.F, RT = H / kGemmRows, nk = F / kGemmK;
-  const uint64_t esz = FP8 ? 1 : 2;
-  const uint64_t mat = (uint64_t)F * H * esz;
-  const int nsc = (F / 128) * (H / 128);
+  const uint64_t mat = code_bytes<W>((uint64_t)F * H);
   const uint16_t* __restrict__ hb = (const uint16_t*)a.hbuf;
   float* __restrict__ part = a.part;
   for (int item = blockIdx.x; item < ntiles * RT; item += gridDim.x) {
@@ -382,22 +446,23 @@ __global__ __launch_bounds__(256) void k_gemm_dn(FfnArgs a) {
       const int idx = (tid >> 3) + 32 * q;
       bp[q] = idx < n_here ? hb + (uint64_t)item_pair(a, g.it, g.r, g.n0 + idx) * F + (tid & 7) * 8 : nullptr;
     }
-    const uint8_t* w0 = g.it.rec + 2 * mat + (uint64_t)m0 * F * esz;
-    const float* sc = reinterpret_cast<const float*>(g.it.rec + 3 * mat) + 2 * nsc + (m0 / 128) * (F / 128);
+    const uint8_t* w0 = g.it.rec + 2 * mat + code_bytes<W>((uint64_t)m0 * F);
+    const uint8_t* sr0 = scale_row<W>(g.it.rec, mat, F, H, 2, m0, F);
+    const float* sc = reinterpret_cast<const float*>(sr0);
     f32x4 acc[1][2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[0][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    Slice<FP8, 1> sl;
-    sl.load(w0, mat, F, 0, bp);
+    Slice<W, 1> sl;
+    sl.load(w0, mat, sr0, 0, F, 0, bp);
     for (int kb = 0; kb < nk; ++kb) {
       __syncthreads();
       sl.store(As, Bs);
       __syncthreads();
-      if (kb + 1 < nk) sl.load(w0, mat, F, (kb + 1) * kGemmK, bp);
-      const float s1[1] = {FP8 ? sc[(kb * kGemmK) / 128] : 1.f};
-      gemm_slice<FP8, 1>(As, Bs, s1, acc);
+      if (kb + 1 < nk) sl.load(w0, mat, sr0, 0, F, (kb + 1) * kGemmK, bp);
+      const float s1[1] = {W == kFp8 ? sc[(kb * kGemmK) / 128] : 1.f};
+      gemm_slice<W == kFp8, 1>(As, Bs, s1, acc);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -415,22 +480,30 @@ __global__ __launch_bounds__(256) void k_gemm_dn(FfnArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ decode path (bf16, fp8)
+// ------------------------------------------------------------------ decode path (bf16, fp8, MXFP4)
 // Few tokens per record: the weights are streamed once and every byte meets all
 // of the record's tokens while it sits in registers.  A wavefront owns a work
 // item; each 16-lane quarter owns one weight row per stream and reads it in
-// coalesced 16-byte pieces (lane c takes the 8 K values at chunk 16*i + c), so
-// a quarter covers 256 contiguous bytes per load.  Products use the hardware
-// bf16 pair dot (fp32 accumulate); fp8 codes are widened exactly to bf16 pairs
-// first and each 128-wide K block is scaled on its fp32 partial sum.  The 16
-// lanes' partial sums of the (token, stream) pairs are reduced by a transposing
-// butterfly that leaves pair v's sum in lane v.  Fixed order throughout.  The
-// number of K blocks loaded per pass is a template parameter (one_chunks), so
-// a pass is one unbroken run of loads with no per-block bounds tests.
+// coalesced pieces: lane c takes lane chunk 16*i + c of K block i, a chunk
+// being 8 weights (bf16: 16 bytes, fp8: 8 bytes) or 16 MXFP4 weights (8
+// bytes), so a quarter covers 256 (bf16) or 128 contiguous bytes per load.
+// Products use the hardware bf16 pair dot (fp32 accumulate); fp8 codes are
+// widened exactly to bf16 pairs and each 128-wide K block is scaled on its
+// fp32 partial sum; MXFP4 codes are widened with their scale folded in.  The
+// 16 lanes' partial sums of the (token, stream) pairs are reduced by a
+// transposing butterfly that leaves pair v's sum in lane v.  Fixed order
+// throughout.  The number of K blocks loaded per pass is a template parameter
+// (one_chunks), so a pass is one unbroken run of loads with no bounds tests.
 constexpr int kVecTok = 8;   // tokens per pass over the held weights (8 x 2 streams = 16 lanes)
 constexpr int kDecodeMaxT = 64;
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// weights per lane chunk; a K block is 16 lane chunks
+template <int W>
+constexpr int lane_weights() {
+  return W == kMx4 ? 16 : 8;
+}
 
 // 8 bf16 weights (as 4 pairs) . 8 bf16 activations
 __device__ __forceinline__ float dot8(uint4 w, uint4 x, float acc) {
@@ -451,29 +524,40 @@ __device__ __forceinline__ uint4 widen8(uint2 d) {
   return u;
 }
 
-template <bool FP8>
+template <int W>
 struct WChunk {
-  typedef uint4 T;
+  typedef uint2 T;  // fp8, MXFP4: 8 bytes
 };
 template <>
-struct WChunk<true> {
-  typedef uint2 T;
+struct WChunk<kBf16> {
+  typedef uint4 T;
 };
 
-template <bool FP8>
-__device__ __forceinline__ typename WChunk<FP8>::T load_w(const uint8_t* row, int kb, int c) {
-  if (FP8)
-    return *reinterpret_cast<const typename WChunk<FP8>::T*>(row + (uint64_t)(16 * kb + c) * 8);
-  else
-    return *reinterpret_cast<const typename WChunk<FP8>::T*>(row + (uint64_t)(16 * kb + c) * 16);
+template <int W>
+__device__ __forceinline__ typename WChunk<W>::T load_w(const uint8_t* row, int kb, int c) {
+  return *reinterpret_cast<const typename WChunk<W>::T*>(row + (uint64_t)(16 * kb + c) * sizeof(typename WChunk<W>::T));
 }
 
-template <bool FP8>
-__device__ __forceinline__ float wdot(typename WChunk<FP8>::T w, uint4 x, float acc, float scale) {
-  if constexpr (FP8) {
-    return __builtin_fmaf(scale, dot8(widen8(w), x, 0.f), acc);
+// the scale lane c applies in K block kb (srow from scale_row)
+template <int W>
+__device__ __forceinline__ float load_s(const uint8_t* srow, int kb, int c) {
+  if (W == kFp8) return reinterpret_cast<const float*>(srow)[kb];
+  if (W == kMx4) return e8m0_scale(srow[8 * kb + (c >> 1)]);
+  return 1.f;
+}
+
+// acc += lane chunk w (K block kb) . the matching activations of row xr
+template <int W>
+__device__ __forceinline__ float wdot(typename WChunk<W>::T w, const uint4* xr, int kb, int c, float acc, float s) {
+  if constexpr (W == kFp8) {
+    return __builtin_fmaf(s, dot8(widen8(w), xr[16 * kb + c], 0.f), acc);
+  } else if constexpr (W == kMx4) {
+    uint4 lo, hi;
+    widen16_fp4(w, s, lo, hi);
+    acc = dot8(lo, xr[2 * (16 * kb + c)], acc);
+    return dot8(hi, xr[2 * (16 * kb + c) + 1], acc);
   } else {
-    return dot8(w, x, acc);
+    return dot8(w, xr[16 * kb + c], acc);
   }
 }
 
@@ -509,22 +593,22 @@ __device__ __forceinline__ float reduce16_all(float v) {
   return v + __shfl_xor(v, 1);
 }
 
-// Two weight rows (stream 0, stream 1) of length K = 128 * nk against up to
-// kVecTok activation rows act[t] (bf16, length K), CH K blocks per pass (nk a
-// multiple of CH, so no per-block guards); acc[t][s] gets the lane's partial sums.
-template <bool FP8, int CH>
-__device__ __forceinline__ void vec_pass(const uint8_t* row0, const uint8_t* row1, const float* sc0,
-                                         const float* sc1, int nk, int c, const uint16_t* const act[kVecTok],
+// Two weight rows (stream 0 at row0 / scales sr0, stream 1 at row1 / sr1) of nk
+// K blocks against up to kVecTok activation rows act[t] (bf16), CH K blocks per
+// pass (nk a multiple of CH); acc[t][s] gets the lane's partial sums.
+template <int W, int CH>
+__device__ __forceinline__ void vec_pass(const uint8_t* row0, const uint8_t* row1, const uint8_t* sr0,
+                                         const uint8_t* sr1, int nk, int c, const uint16_t* const act[kVecTok],
                                          int nt, float acc[kVecTok][2]) {
   for (int k0 = 0; k0 < nk; k0 += CH) {
-    typename WChunk<FP8>::T w0[CH], w1[CH];
+    typename WChunk<W>::T w0[CH], w1[CH];
     float s0[CH], s1[CH];
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      w0[i] = load_w<FP8>(row0, k0 + i, c);
-      w1[i] = load_w<FP8>(row1, k0 + i, c);
-      s0[i] = FP8 ? sc0[k0 + i] : 1.f;
-      s1[i] = FP8 ? sc1[k0 + i] : 1.f;
+      w0[i] = load_w<W>(row0, k0 + i, c);
+      w1[i] = load_w<W>(row1, k0 + i, c);
+      s0[i] = load_s<W>(sr0, k0 + i, c);
+      s1[i] = load_s<W>(sr1, k0 + i, c);
     }
 #pragma unroll
     for (int t = 0; t < kVecTok; ++t) {
@@ -532,9 +616,8 @@ __device__ __forceinline__ void vec_pass(const uint8_t* row0, const uint8_t* row
         const uint4* xr = reinterpret_cast<const uint4*>(act[t]);
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-          const uint4 xv = xr[16 * (k0 + i) + c];
-          acc[t][0] = wdot<FP8>(w0[i], xv, acc[t][0], s0[i]);
-          acc[t][1] = wdot<FP8>(w1[i], xv, acc[t][1], s1[i]);
+          acc[t][0] = wdot<W>(w0[i], xr, k0 + i, c, acc[t][0], s0[i]);
+          acc[t][1] = wdot<W>(w1[i], xr, k0 + i, c, acc[t][1], s1[i]);
         }
       }
     }
@@ -543,31 +626,31 @@ __device__ __forceinline__ void vec_pass(const uint8_t* row0, const uint8_t* row
 
 // vec_pass for one activation row: each pass one unbroken run of loads, then
 // the pair dots.  Same per-lane order as vec_pass, so the same bits.
-template <bool FP8, int CH>
-__device__ __forceinline__ void one_pass(const uint8_t* row0, const uint8_t* row1, const float* sc0, const float* sc1,
-                                         int nk, int c, const uint16_t* act, float& acc0, float& acc1) {
+template <int W, int CH>
+__device__ __forceinline__ void one_pass(const uint8_t* row0, const uint8_t* row1, const uint8_t* sr0,
+                                         const uint8_t* sr1, int nk, int c, const uint16_t* act, float& acc0,
+                                         float& acc1) {
   const uint4* xr = reinterpret_cast<const uint4*>(act);
   for (int k0 = 0; k0 < nk; k0 += CH) {
-    typename WChunk<FP8>::T w0[CH], w1[CH];
+    typename WChunk<W>::T w0[CH], w1[CH];
     float s0[CH], s1[CH];
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      w0[i] = load_w<FP8>(row0, k0 + i, c);
-      w1[i] = load_w<FP8>(row1, k0 + i, c);
-      s0[i] = FP8 ? sc0[k0 + i] : 1.f;
-      s1[i] = FP8 ? sc1[k0 + i] : 1.f;
+      w0[i] = load_w<W>(row0, k0 + i, c);
+      w1[i] = load_w<W>(row1, k0 + i, c);
+      s0[i] = load_s<W>(sr0, k0 + i, c);
+      s1[i] = load_s<W>(sr1, k0 + i, c);
     }
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      const uint4 xv = xr[16 * (k0 + i) + c];
-      acc0 = wdot<FP8>(w0[i], xv, acc0, s0[i]);
-      acc1 = wdot<FP8>(w1[i], xv, acc1, s1[i]);
+      acc0 = wdot<W>(w0[i], xr, k0 + i, c, acc0, s0[i]);
+      acc1 = wdot<W>(w1[i], xr, k0 + i, c, acc1, s1[i]);
     }
   }
 }
 
-// K blocks per pass: the largest listed divisor of nk (16 blocks = 2048 K values
-// per stream held in registers)
+// K blocks per pass: the largest listed divisor of nk (16 blocks = 2048 bf16 or
+// fp8, 4096 MXFP4 weights per stream held in registers)
 inline int one_chunks(int nk) {
   for (int ch : {16, 8, 6, 4, 2})
     if (nk % ch == 0) return ch;
@@ -576,16 +659,14 @@ inline int one_chunks(int nk) {
 
 // gate/up: work item = (record, 4 rows of F); quarter q takes row f = 4*g + q of
 // gate (stream 0) and up (stream 1); h = silu(gate) * up stored in bf16.
-template <bool FP8, int CH>
+template <int W, int CH>
 __global__ __launch_bounds__(256) void k_gateup_vec(FfnArgs a) {
   const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
   const int nrt = a.max_routed + (a.shared ? 1 : 0);
   const int RG = a.F / 4;
   const int H = a.H, F = a.F;
-  const int nk = H / 128;
-  const uint64_t esz = FP8 ? 1 : 2;
-  const uint64_t mat = (uint64_t)F * H * esz;
-  const int nsc = (F / 128) * (H / 128);
+  const int nk = H / (16 * lane_weights<W>());
+  const uint64_t mat = code_bytes<W>((uint64_t)F * H);
   const uint16_t* __restrict__ x = (const uint16_t*)a.x;
   uint16_t* __restrict__ hb = (uint16_t*)a.hbuf;
   const int nwave = gridDim.x * 4;
@@ -593,8 +674,9 @@ __global__ __launch_bounds__(256) void k_gateup_vec(FfnArgs a) {
     const int r = item / RG, fg = (item % RG) * 4, f = fg + q;
     const Item it = item_block(a, r);
     if (it.n == 0) continue;
-    const uint8_t* wg = it.rec + (uint64_t)f * H * esz;
-    const float* sc = reinterpret_cast<const float*>(it.rec + 3 * mat) + (fg / 128) * (H / 128);
+    const uint8_t* wg = it.rec + code_bytes<W>((uint64_t)f * H);
+    const uint8_t* sg = scale_row<W>(it.rec, mat, F, H, 0, f, H);
+    const uint8_t* su = scale_row<W>(it.rec, mat, F, H, 1, f, H);
     for (int tg = 0; tg < it.n; tg += kVecTok) {
       const int nt = min(kVecTok, it.n - tg);
       const uint16_t* act[kVecTok];
@@ -604,7 +686,7 @@ __global__ __launch_bounds__(256) void k_gateup_vec(FfnArgs a) {
       float acc[kVecTok][2];
 #pragma unroll
       for (int t = 0; t < kVecTok; ++t) acc[t][0] = acc[t][1] = 0.f;
-      vec_pass<FP8, CH>(wg, wg + mat, sc, sc + nsc, nk, c, act, nt, acc);
+      vec_pass<W, CH>(wg, wg + mat, sg, su, nk, c, act, nt, acc);
       float v[16];
 #pragma unroll
       for (int t = 0; t < kVecTok; ++t) {
@@ -624,16 +706,14 @@ __global__ __launch_bounds__(256) void k_gateup_vec(FfnArgs a) {
 
 // down: work item = (record, 8 rows of H); quarter q takes rows 8*g + q (stream 0)
 // and 8*g + 4 + q (stream 1) against h of the record's pairs; fp32 partial outputs.
-template <bool FP8, int CH>
+template <int W, int CH>
 __global__ __launch_bounds__(256) void k_down_vec(FfnArgs a) {
   const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
   const int nrt = a.max_routed + (a.shared ? 1 : 0);
   const int RG = a.H / 8;
   const int H = a.H, F = a.F;
-  const int nk = F / 128;
-  const uint64_t esz = FP8 ? 1 : 2;
-  const uint64_t mat = (uint64_t)F * H * esz;
-  const int nsc = (F / 128) * (H / 128);
+  const int nk = F / (16 * lane_weights<W>());
+  const uint64_t mat = code_bytes<W>((uint64_t)F * H);
   const uint16_t* __restrict__ hb = (const uint16_t*)a.hbuf;
   float* __restrict__ part = a.part;
   const int nwave = gridDim.x * 4;
@@ -641,8 +721,9 @@ __global__ __launch_bounds__(256) void k_down_vec(FfnArgs a) {
     const int r = item / RG, hg = (item % RG) * 8, h0 = hg + q;
     const Item it = item_block(a, r);
     if (it.n == 0) continue;
-    const uint8_t* wd = it.rec + 2 * mat + (uint64_t)h0 * F * esz;
-    const float* sc = reinterpret_cast<const float*>(it.rec + 3 * mat) + 2 * nsc + (hg / 128) * (F / 128);
+    const uint8_t* wd = it.rec + 2 * mat + code_bytes<W>((uint64_t)h0 * F);
+    const uint8_t* s0 = scale_row<W>(it.rec, mat, F, H, 2, h0, F);
+    const uint8_t* s1 = scale_row<W>(it.rec, mat, F, H, 2, h0 + 4, F);
     for (int tg = 0; tg < it.n; tg += kVecTok) {
       const int nt = min(kVecTok, it.n - tg);
       const uint16_t* act[kVecTok];
@@ -651,7 +732,7 @@ __global__ __launch_bounds__(256) void k_down_vec(FfnArgs a) {
       float acc[kVecTok][2];
 #pragma unroll
       for (int t = 0; t < kVecTok; ++t) acc[t][0] = acc[t][1] = 0.f;
-      vec_pass<FP8, CH>(wd, wd + 4ull * F * esz, sc, sc, nk, c, act, nt, acc);
+      vec_pass<W, CH>(wd, wd + code_bytes<W>(4ull * F), s0, s1, nk, c, act, nt, acc);
       float v[16];
 #pragma unroll
       for (int t = 0; t < kVecTok; ++t) {
@@ -684,50 +765,46 @@ __device__ __forceinline__ const uint8_t* one_record(const FfnArgs& a, int j) {
   return ri < a.S ? a.slots + (uint64_t)ri * a.stride : a.staging + (uint64_t)(ri - a.S) * a.stride;
 }
 
-template <bool FP8, int CH>
+template <int W, int CH>
 __global__ __launch_bounds__(256) void k_gateup_one(FfnArgs a) {
   const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
   const int RG = a.F / 4;
   const int H = a.H, F = a.F;
-  const int nk = H / 128;
-  const uint64_t esz = FP8 ? 1 : 2;
-  const uint64_t mat = (uint64_t)F * H * esz;
-  const int nsc = (F / 128) * (H / 128);
+  const int nk = H / (16 * lane_weights<W>());
+  const uint64_t mat = code_bytes<W>((uint64_t)F * H);
   const int items = (a.k + (a.shared ? 1 : 0)) * RG;
   const uint16_t* __restrict__ x = (const uint16_t*)a.x;
   uint16_t* __restrict__ hb = (uint16_t*)a.hbuf;
   for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < items; item += gridDim.x * 4) {
-    const int j = item / RG, fg = (item % RG) * 4, f = fg + q;
+    const int j = item / RG, f = (item % RG) * 4 + q;
     const uint8_t* rec = one_record(a, j);
-    const uint8_t* wg = rec + (uint64_t)f * H * esz;
-    const float* sc = reinterpret_cast<const float*>(rec + 3 * mat) + (fg / 128) * (H / 128);
+    const uint8_t* wg = rec + code_bytes<W>((uint64_t)f * H);
     float g = 0.f, up = 0.f;
-    one_pass<FP8, CH>(wg, wg + mat, sc, sc + nsc, nk, c, x, g, up);
+    one_pass<W, CH>(wg, wg + mat, scale_row<W>(rec, mat, F, H, 0, f, H), scale_row<W>(rec, mat, F, H, 1, f, H), nk,
+                    c, x, g, up);
     g = reduce16_all(g);
     up = reduce16_all(up);
     if (c == 0) hb[(uint64_t)j * F + f] = f32_to_bf16(silu_mul(g, up));
   }
 }
 
-template <bool FP8, int CH>
+template <int W, int CH>
 __global__ __launch_bounds__(256) void k_down_one(FfnArgs a) {
   const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
   const int RG = a.H / 8;
   const int H = a.H, F = a.F;
-  const int nk = F / 128;
-  const uint64_t esz = FP8 ? 1 : 2;
-  const uint64_t mat = (uint64_t)F * H * esz;
-  const int nsc = (F / 128) * (H / 128);
+  const int nk = F / (16 * lane_weights<W>());
+  const uint64_t mat = code_bytes<W>((uint64_t)F * H);
   const int items = (a.k + (a.shared ? 1 : 0)) * RG;
   const uint16_t* __restrict__ hb = (const uint16_t*)a.hbuf;
   float* __restrict__ part = a.part;
   for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < items; item += gridDim.x * 4) {
-    const int j = item / RG, hg = (item % RG) * 8, h0 = hg + q;
+    const int j = item / RG, h0 = (item % RG) * 8 + q;
     const uint8_t* rec = one_record(a, j);
-    const uint8_t* wd = rec + 2 * mat + (uint64_t)h0 * F * esz;
-    const float* sc = reinterpret_cast<const float*>(rec + 3 * mat) + 2 * nsc + (hg / 128) * (F / 128);
+    const uint8_t* wd = rec + 2 * mat + code_bytes<W>((uint64_t)h0 * F);
     float s0 = 0.f, s1 = 0.f;
-    one_pass<FP8, CH>(wd, wd + 4ull * F * esz, sc, sc, nk, c, hb + (uint64_t)j * F, s0, s1);
+    one_pass<W, CH>(wd, wd + code_bytes<W>(4ull * F), scale_row<W>(rec, mat, F, H, 2, h0, F),
+                    scale_row<W>(rec, mat, F, H, 2, h0 + 4, F), nk, c, hb + (uint64_t)j * F, s0, s1);
     s0 = reduce16_all(s0);
     s1 = reduce16_all(s1);
     if (c < 2) part[(uint64_t)j * H + h0 + 4 * c] = c ? s1 : s0;
@@ -735,26 +812,28 @@ __global__ __launch_bounds__(256) void k_down_one(FfnArgs a) {
 }
 
 // kernel instantiation by K blocks per pass
-#define MOE_BY_CHUNKS(KERN, FP8, NK)                   \
-  switch (one_chunks(NK)) {                            \
-    case 16: return KERN<FP8, 16>;                     \
-    case 8: return KERN<FP8, 8>;                       \
-    case 6: return KERN<FP8, 6>;                       \
-    case 4: return KERN<FP8, 4>;                       \
-    case 2: return KERN<FP8, 2>;                       \
-    default: return KERN<FP8, 1>;                      \
+#define MOE_BY_CHUNKS(KERN, W, NK) \
+  switch (one_chunks(NK)) {        \
+    case 16: return KERN<W, 16>;   \
+    case 8: return KERN<W, 8>;     \
+    case 6: return KERN<W, 6>;     \
+    case 4: return KERN<W, 4>;     \
+    case 2: return KERN<W, 2>;     \
+    default: return KERN<W, 1>;    \
   }
 
 typedef void (*FfnKernel)(FfnArgs);
-template <bool FP8>
-FfnKernel gateup_decode(bool one, int nk) {
-  if (one) { MOE_BY_CHUNKS(k_gateup_one, FP8, nk) }
-  MOE_BY_CHUNKS(k_gateup_vec, FP8, nk)
+template <int W>
+FfnKernel gateup_decode(bool one, int H) {
+  const int nk = H / (16 * lane_weights<W>());
+  if (one) { MOE_BY_CHUNKS(k_gateup_one, W, nk) }
+  MOE_BY_CHUNKS(k_gateup_vec, W, nk)
 }
-template <bool FP8>
-FfnKernel down_decode(bool one, int nk) {
-  if (one) { MOE_BY_CHUNKS(k_down_one, FP8, nk) }
-  MOE_BY_CHUNKS(k_down_vec, FP8, nk)
+template <int W>
+FfnKernel down_decode(bool one, int F) {
+  const int nk = F / (16 * lane_weights<W>());
+  if (one) { MOE_BY_CHUNKS(k_down_one, W, nk) }
+  MOE_BY_CHUNKS(k_down_vec, W, nk)
 }
 #undef MOE_BY_CHUNKS
 
@@ -891,7 +970,7 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
   if (!grouped && !a.pair_items) {
     launch_k(h, MOE_K_GROUP, k_group, dim3(1), dim3(kBlock), 0, s, a);
   }
-  const bool fp8 = h->dtype == MOE_FP8_E4M3_B128;
+  const int wf = h->dtype;  // weight format
   // gate/up and down: fp32 FMA kernels, the decode kernels (T <= kDecodeMaxT), or the MFMA kernels
   void (*gu)(FfnArgs) = nullptr;
   void (*dn)(FfnArgs) = nullptr;
@@ -904,14 +983,16 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
     b1 = b2 = dim3(256);
   } else if (T <= kDecodeMaxT) {  // one wavefront per work item, 4 per workgroup
     const bool one = a.pair_items != 0;
-    gu = fp8 ? gateup_decode<true>(one, h->H / 128) : gateup_decode<false>(one, h->H / 128);
-    dn = fp8 ? down_decode<true>(one, h->F / 128) : down_decode<false>(one, h->F / 128);
+    gu = wf == kFp8 ? gateup_decode<kFp8>(one, h->H)
+                    : (wf == kMx4 ? gateup_decode<kMx4>(one, h->H) : gateup_decode<kBf16>(one, h->H));
+    dn = wf == kFp8 ? down_decode<kFp8>(one, h->F)
+                    : (wf == kMx4 ? down_decode<kMx4>(one, h->F) : down_decode<kBf16>(one, h->F));
     g1 = dim3(std::min((max_items_r * (h->F / 4) + 3) / 4, 8192));
     g2 = dim3(std::min((max_items_r * (h->H / 8) + 3) / 4, 8192));
     b1 = b2 = dim3(256);
   } else {  // grouped GEMM over (record tile, 64 rows) work items; the grid strides over the call's list
-    gu = fp8 ? k_gemm_gu<true> : k_gemm_gu<false>;
-    dn = fp8 ? k_gemm_dn<true> : k_gemm_dn<false>;
+    gu = wf == kFp8 ? k_gemm_gu<kFp8> : (wf == kMx4 ? k_gemm_gu<kMx4> : k_gemm_gu<kBf16>);
+    dn = wf == kFp8 ? k_gemm_dn<kFp8> : (wf == kMx4 ? k_gemm_dn<kMx4> : k_gemm_dn<kBf16>);
     // tiles of a call: at most one partial tile per record on top of the full ones
     const int tiles = (T * h->k) / kGemmTok + std::min(T * h->k, h->S + h->E) +
                       (shared ? (T + kGemmTok - 1) / kGemmTok : 0);

@@ -36,7 +36,12 @@ size_t record_bytes_of(int dtype, int H, int F) {
   size_t n = 3 * (size_t)H * (size_t)F;
   if (dtype == MOE_F32) return 4 * n;
   if (dtype == MOE_BF16) return 2 * n;
+  if (dtype == MOE_MXFP4) return n / 2 + n / 32;  // codes + one scale byte per 32
   return n + 3 * (size_t)(H / 128) * (size_t)(F / 128) * 4;
+}
+
+bool known_dtype(int dtype) {
+  return dtype == MOE_F32 || dtype == MOE_BF16 || dtype == MOE_FP8_E4M3_B128 || dtype == MOE_MXFP4;
 }
 
 bool same_shape(const moe_offload* a, const moe_offload_desc* d) {
@@ -93,15 +98,15 @@ int moe_offload_create(const moe_offload_desc* d, moe_offload** out) {
   g_err[0] = 0;
   if (!d || !out) return fail(MOE_EINVAL, "null argument");
   *out = nullptr;
-  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16 && d->dtype != MOE_FP8_E4M3_B128)
-    return fail(MOE_EUNSUPPORTED, "unsupported dtype %d", d->dtype);
+  if (!known_dtype(d->dtype)) return fail(MOE_EUNSUPPORTED, "unsupported dtype %d", d->dtype);
   if (d->num_experts < 1 || d->num_experts > moe::kMaxExperts)
     return fail(MOE_EINVAL, "num_experts=%d outside [1, %d]", d->num_experts, moe::kMaxExperts);
   if (d->top_k < 1 || d->top_k > moe::kMaxTopK || d->top_k > d->num_experts)
     return fail(MOE_EINVAL, "top_k=%d outside [1, min(%d, E)]", d->top_k, moe::kMaxTopK);
   if (d->num_slots < d->top_k || d->num_slots > d->num_experts)
     return fail(MOE_EINVAL, "num_slots=%d outside [top_k=%d, E=%d]", d->num_slots, d->top_k, d->num_experts);
-  int mult = d->dtype == MOE_F32 ? 64 : 128;
+  // decode kernels: a K block is 16 lanes x 8 weights (16 x 16 MXFP4 weights); fp32: 64-row tiles
+  int mult = d->dtype == MOE_F32 ? 64 : (d->dtype == MOE_MXFP4 ? 256 : 128);
   if (d->hidden < mult || d->hidden % mult || d->ffn < mult || d->ffn % mult)
     return fail(MOE_EUNSUPPORTED, "hidden=%d / ffn=%d must be positive multiples of %d for this dtype", d->hidden,
                 d->ffn, mult);
@@ -272,8 +277,7 @@ int moe_slot_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const f
 int moe_rmsnorm(const void* x, void* out, int32_t T, int32_t H, int32_t dtype, float eps, void* stream) {
   if (!x || !out) return fail(MOE_EINVAL, "moe_rmsnorm: null pointer");
   if (T < 1 || H < 8 || H % 8) return fail(MOE_EINVAL, "moe_rmsnorm: T=%d, H=%d (H must be a multiple of 8)", T, H);
-  if (dtype != MOE_F32 && dtype != MOE_BF16 && dtype != MOE_FP8_E4M3_B128)
-    return fail(MOE_EUNSUPPORTED, "moe_rmsnorm: dtype %d", dtype);
+  if (!known_dtype(dtype)) return fail(MOE_EUNSUPPORTED, "moe_rmsnorm: dtype %d", dtype);
   if (!(eps > 0.0f)) return fail(MOE_EINVAL, "moe_rmsnorm: eps must be positive");
   HIP_TRY(moe::launch_rmsnorm(x, out, T, H, dtype, eps, (hipStream_t)stream));
   return MOE_OK;

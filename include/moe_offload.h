@@ -51,11 +51,15 @@
  *     all be issued on the same (compute) stream.
  *
  * Record layout (one expert, `record_bytes`, records `record_stride` apart):
- *     gate [F][H] | up [F][H] | down [H][F] | (fp8 only) scales
+ *     gate [F][H] | up [F][H] | down [H][F] | (fp8, MXFP4) scales
  *   rows are contiguous along the reduction dimension; elements are fp32,
- *   bf16, or fp8 e4m3 (OCP "fn": bias 7, no infinities).  fp8 records end with
- *   fp32 block scales, one per 128 x 128 block, row-major: gate [F/128][H/128],
- *   up [F/128][H/128], down [H/128][F/128]; weight = decode(q) * scale.
+ *   bf16, fp8 e4m3 (OCP "fn": bias 7, no infinities), or MXFP4.  fp8 records
+ *   end with fp32 block scales, one per 128 x 128 block, row-major: gate
+ *   [F/128][H/128], up [F/128][H/128], down [H/128][F/128]; weight =
+ *   decode(q) * scale.  MXFP4 (OCP Microscaling v1.0): E2M1 codes, two per
+ *   byte, element 2i of a row in the low nibble; then E8M0 scale bytes, one per
+ *   32 consecutive weights of a row: gate [F][H/32], up [F][H/32], down
+ *   [H][F/32]; weight = e2m1(q) * 2^(e - 127).
  *
  * Record index ("slot id") space used by slot_ids:
  *   r in [0, S)       slot r of the slot tensor
@@ -77,7 +81,8 @@ typedef struct moe_offload moe_offload;
 enum moe_dtype {
   MOE_F32 = 0,            /* fp32 weights, fp32 activations */
   MOE_BF16 = 1,           /* bf16 weights, bf16 activations */
-  MOE_FP8_E4M3_B128 = 2   /* fp8 e4m3 weights + fp32 128x128 block scales, bf16 activations */
+  MOE_FP8_E4M3_B128 = 2,  /* fp8 e4m3 weights + fp32 128x128 block scales, bf16 activations */
+  MOE_MXFP4 = 3           /* MXFP4 weights (E2M1 + E8M0 per 32), bf16 activations; H, F multiples of 256 */
 };
 
 /* return codes */

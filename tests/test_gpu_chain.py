@@ -40,7 +40,7 @@ class ChainModel:
     def __init__(self, L, E, S, k, H, F, wdt, T, seed, prefetch_n=0, zipf=1.2, rho=0.9, shared=False):
         self.L, self.E, self.S, self.k, self.H, self.F, self.wdt, self.T = L, E, S, k, H, F, wdt, T
         self.hosts, self.routers, self.handles, self.shared = [], [], [], []
-        rdt = 1 if wdt == 2 else wdt  # fp8 layers take a bf16 router and bf16 activations
+        rdt = 1 if wdt >= 2 else wdt  # fp8 and MXFP4 layers take a bf16 router and bf16 activations
         for l in range(L):
             self.hosts.append(synth.records(seed, l, E, H, F, wdt))
             self.routers.append(synth.router(seed, l, E, H, rdt, zipf_s=zipf))
@@ -95,7 +95,7 @@ class ChainModel:
 def oracle_replay_step(cm, caches, snap, prefetch_n, check_ffn=True):
     """Teacher-forced oracle for one chain step; asserts parity for every layer."""
     L = cm.L
-    adt = 1 if cm.wdt == 2 else cm.wdt  # activation / router format
+    adt = 1 if cm.wdt >= 2 else cm.wdt  # activation / router format
     for l in range(L):
         xn = snap["xn"][l]
         # the block input itself: the GPU norm of the GPU stream, within one bf16 step
@@ -170,6 +170,7 @@ def test_prefetch_keeps_outputs_identical():
 
 @pytest.mark.parametrize("case", [
     # (E, S, k, H, F, wdt, T, prefetch, shared): the fused router launch with a shared expert and fp8 records,
+    # the same with MXFP4 records,
     # the batch limits of that fusion (8 fused, 9 not), 256 experts, and more than 512 (t, j) pairs (separate
     # kernels and the predictor stream for the lookahead)
     (16, 6, 4, 256, 256, 2, 3, 2, True),
@@ -177,6 +178,7 @@ def test_prefetch_keeps_outputs_identical():
     (16, 6, 4, 256, 256, 1, 9, 0, False),
     (256, 20, 8, 256, 256, 1, 2, 3, False),
     (32, 12, 8, 128, 256, 1, 72, 2, False),
+    (16, 6, 4, 256, 512, 3, 3, 2, True),
 ])
 def test_chain_variants_match_eager_and_oracle(case):
     E, S, k, H, F, wdt, T, prefetch_n, shared = case

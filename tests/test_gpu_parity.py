@@ -105,6 +105,23 @@ def test_single_token_every_pass_width(H, F, wdt):
     run_sequence(8, 4, 3, H, F, wdt, 1.2, 40 + H // 128, 6, [1], shared=(wdt == 2))
 
 
+@pytest.mark.parametrize("H,F", [(4096, 256), (2048, 1536), (1536, 2048), (1024, 4096), (512, 1024), (256, 512)])
+def test_mxfp4_single_token_every_pass_width(H, F):
+    # MXFP4 K blocks hold 256 weights: H / 256 blocks for gate/up, F / 256 for down; these shapes
+    # reach pass widths 16, 8, 6, 4, 2 and 1 in each, with the shared expert
+    run_sequence(8, 4, 3, H, F, 3, 1.2, 50 + H // 256, 6, [1], shared=True)
+
+
+@pytest.mark.parametrize("S", [4, 12])
+def test_mxfp4_decode_batches_with_shared_expert(S):
+    run_sequence(16, S, 4, 512, 768, 3, 1.2, 61, 12, [1, 2, 5, 17, 64], shared=True)
+
+
+def test_mxfp4_prefill_gemm_ragged_tiles():
+    # > 64 tokens per call: the grouped GEMM with E2M1 codes widened (scale folded in) into LDS
+    run_sequence(12, 6, 3, 256, 512, 3, 1.2, 62, 3, [100, 130, 65], shared=True)
+
+
 def test_fp8_without_shared_expert():
     run_sequence(10, 5, 2, 128, 256, 2, 1.2, 32, 10, [2, 7])
 
