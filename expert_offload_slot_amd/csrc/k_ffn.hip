@@ -652,7 +652,7 @@ __device__ __forceinline__ void one_pass(const uint8_t* row0, const uint8_t* row
 // K blocks per pass: the largest listed divisor of nk (16 blocks = 2048 bf16 or
 // fp8, 4096 MXFP4 weights per stream held in registers)
 inline int one_chunks(int nk) {
-  for (int ch : {16, 8, 6, 4, 2})
+  for (int ch : {16, 8, 6, 4, 3, 2})
     if (nk % ch == 0) return ch;
   return 1;
 }
@@ -818,6 +818,7 @@ __global__ __launch_bounds__(256) void k_down_one(FfnArgs a) {
     case 8: return KERN<W, 8>;     \
     case 6: return KERN<W, 6>;     \
     case 4: return KERN<W, 4>;     \
+    case 3: return KERN<W, 3>;     \
     case 2: return KERN<W, 2>;     \
     default: return KERN<W, 1>;    \
   }

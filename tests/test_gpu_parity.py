@@ -96,19 +96,21 @@ def test_bf16_prefill_gemm_one_hot_record():
     run_sequence(2, 2, 2, 128, 256, 1, 0.0, 34, 2, [257, 64])
 
 
-@pytest.mark.parametrize("H,F", [(2048, 512), (1024, 768), (768, 1024), (512, 128), (384, 2048), (1792, 256)])
+@pytest.mark.parametrize("H,F", [(2048, 512), (1024, 768), (768, 1024), (512, 128), (384, 2048), (1792, 256),
+                                 (128, 384)])
 @pytest.mark.parametrize("wdt", [1, 2])
 def test_single_token_every_pass_width(H, F, wdt):
-    # one-token calls stream each weight row in passes of 16, 8, 6, 4, 2 or 1 K blocks of 128 (the
+    # one-token calls stream each weight row in passes of 16, 8, 6, 4, 3, 2 or 1 K blocks of 128 (the
     # largest that divides the row): these shapes reach every width in gate/up (H / 128 blocks) and
     # in down (F / 128), bf16 and fp8 with the shared expert
     run_sequence(8, 4, 3, H, F, wdt, 1.2, 40 + H // 128, 6, [1], shared=(wdt == 2))
 
 
-@pytest.mark.parametrize("H,F", [(4096, 256), (2048, 1536), (1536, 2048), (1024, 4096), (512, 1024), (256, 512)])
+@pytest.mark.parametrize("H,F", [(4096, 256), (2048, 1536), (1536, 2048), (1024, 4096), (768, 512), (512, 768),
+                                 (256, 1024)])
 def test_mxfp4_single_token_every_pass_width(H, F):
     # MXFP4 K blocks hold 256 weights: H / 256 blocks for gate/up, F / 256 for down; these shapes
-    # reach pass widths 16, 8, 6, 4, 2 and 1 in each, with the shared expert
+    # reach pass widths 16, 8, 6, 4, 3, 2 and 1 in each, with the shared expert
     run_sequence(8, 4, 3, H, F, 3, 1.2, 50 + H // 256, 6, [1], shared=True)
 
 
