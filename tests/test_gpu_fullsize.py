@@ -3,7 +3,7 @@ launch configuration the benchmark times: 48 layers x 128 experts, top-8,
 hidden 2048, moe ffn 768, 26 slots per layer, bf16, every layer's 128 records
 (58 GB) in pinned host memory, the whole decode step replayed as one HIP graph
 at batch 1, 8 and 32, and the router-lookahead prefetch variant (4 installs
-per layer).
+per layer); and the same chain with MXFP4 records at batch 1.
 
 Every call is teacher-forced (the oracle routes the GPU's own block input) and
 checked bit for bit on ids, slot ids, copy lists, prefetch lists, slot tables
@@ -26,7 +26,7 @@ from gpu_harness import d2h, hip, row_rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
-BF16, FP8 = 1, 2
+BF16, FP8, MXFP4 = 1, 2, 3
 
 
 def log(*a):
@@ -38,19 +38,19 @@ def log(*a):
 class Qwen3Model:
     L, E, k, H, F, S, MAX_T = 48, 128, 8, 2048, 768, 26, 32
 
-    def __init__(self, seed=0):
+    def __init__(self, seed=0, wdt=BF16):
         t0 = time.time()
-        self.seed = seed
+        self.seed, self.wdt = seed, wdt  # weight format; activations and routers are bf16
         self.handles = []
         for l in range(self.L):
-            self.handles.append(m.moe_offload_create(self.E, self.S, self.H, self.F, self.k, BF16, self.MAX_T, 0,
+            self.handles.append(m.moe_offload_create(self.E, self.S, self.H, self.F, self.k, wdt, self.MAX_T, 0,
                                                      m.FLAG_AUDIT, None, self.handles[0] if l else None))
         self.info = [m.moe_offload_query(h) for h in self.handles]
         self.stride = self.info[0]["record_stride"]
         self.rb = self.info[0]["record_bytes"]
         for l, h in enumerate(self.handles):
             p, _, _ = m.moe_offload_host_records(h)
-            synth.fill_records(seed, l, 0, self.E, self.H, self.F, BF16, p, self.stride)
+            synth.fill_records(seed, l, 0, self.E, self.H, self.F, wdt, p, self.stride)
         self.hosts = [m.host_array(h, self.E) for h in self.handles]
         self.routers = [synth.router(seed, l, self.E, self.H, BF16, zipf_s=1.2) for l in range(self.L)]
         self.wr = [to_dev(w) for w, _ in self.routers]
@@ -133,8 +133,8 @@ def replay_step(mo, caches, snap, T, prefetch_n, ffn_layers=(), ffn_tokens=()):
         assert np.array_equal(so, oso) and np.array_equal(eo, oeo) and np.array_equal(lu, olu), l
         if l in ffn_layers:
             toks = [t for t in ffn_tokens if t < T]
-            _, y64 = oracle.ffn(xn[toks], BF16, mo.H, mo.F, oracle.host_records(mo.hosts[l], ids[toks]), w[toks],
-                                want_f64=True)
+            _, y64 = oracle.ffn(xn[toks], mo.wdt, mo.H, mo.F, oracle.host_records(mo.hosts[l], ids[toks]),
+                                w[toks], want_f64=True)
             err = row_rel_err(snap["y"][l][toks], y64, BF16)
             assert err <= 2e-2, (l, err)
             worst = max(worst, err)
@@ -218,3 +218,26 @@ def test_qwen3_lookahead_prefetch_full_size(qwen3):
         assert np.array_equal(a, b)
     log("demand misses over %d steps: %d without prefetch, %d with" % (steps, misses[0], misses[4]))
     assert misses[4] <= misses[0]
+
+
+def test_qwen3_mxfp4_chain_full_size():
+    """The same 48-layer chain with MXFP4 expert records (2.5 MB each, 15 GB host store), batch 1."""
+    mo = Qwen3Model(seed=1, wdt=MXFP4)
+    try:
+        caches = mo.reset()
+        ch = Chain(mo, 1, 0, 401)
+        try:
+            worst = 0.0
+            for s in range(12):
+                log("qwen3 mxfp4 chain step %d" % s)
+                ch.run(s)
+                snap = ch.snapshot()
+                sample = s in (0, 6, 11)
+                worst = max(worst, replay_step(mo, caches, snap, 1, 0, (0, 17, 47) if sample else (), (0,)))
+            log("qwen3 mxfp4 chain: 12 steps bit-exact, sampled rows within %.2e" % worst)
+        finally:
+            ch.close()
+        check_counters(mo, caches)
+        check_slot_bytes(mo, (0, 47))
+    finally:
+        mo.close()
