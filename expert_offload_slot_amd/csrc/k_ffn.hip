@@ -18,6 +18,8 @@
 //              registers and met by every token of the record with the bf16
 //              pair-dot instruction.  Few tokens per record make this a
 //              weight-streaming (HBM) problem, not a matrix-core one.
+//              T = 1: k_gateup_one / k_down_one, the same rows per wavefront
+//              for one activation row, work item (choice j, rows).
 //     larger T (prefill): k_gemm_gu / k_gemm_dn, a grouped GEMM whose work
 //              items are (tile of 64 pairs of one record, 64 weight rows), K
 //              slices staged through LDS, bf16 MFMA 16x16x32 tiles.
