@@ -160,6 +160,31 @@ def check_slot_bytes(mo, layers):
                 assert np.array_equal(got, mo.hosts[l][eo[s], :mo.rb]), (l, s, eo[s])
 
 
+def test_qwen3_mxfp4_chain_full_size():
+    """The same 48-layer chain with MXFP4 expert records (2.5 MB each, 15 GB host store), batch 1.  It runs
+    before the module's bf16 model exists and frees its own: both host stores at once exceed what the box
+    lets a process pin."""
+    mo = Qwen3Model(seed=1, wdt=MXFP4)
+    try:
+        caches = mo.reset()
+        ch = Chain(mo, 1, 0, 401)
+        try:
+            worst = 0.0
+            for s in range(12):
+                log("qwen3 mxfp4 chain step %d" % s)
+                ch.run(s)
+                snap = ch.snapshot()
+                sample = s in (0, 6, 11)
+                worst = max(worst, replay_step(mo, caches, snap, 1, 0, (0, 17, 47) if sample else (), (0,)))
+            log("qwen3 mxfp4 chain: 12 steps bit-exact, sampled rows within %.2e" % worst)
+        finally:
+            ch.close()
+        check_counters(mo, caches)
+        check_slot_bytes(mo, (0, 47))
+    finally:
+        mo.close()
+
+
 @pytest.fixture(scope="module")
 def qwen3():
     mo = Qwen3Model()
@@ -219,25 +244,3 @@ def test_qwen3_lookahead_prefetch_full_size(qwen3):
     log("demand misses over %d steps: %d without prefetch, %d with" % (steps, misses[0], misses[4]))
     assert misses[4] <= misses[0]
 
-
-def test_qwen3_mxfp4_chain_full_size():
-    """The same 48-layer chain with MXFP4 expert records (2.5 MB each, 15 GB host store), batch 1."""
-    mo = Qwen3Model(seed=1, wdt=MXFP4)
-    try:
-        caches = mo.reset()
-        ch = Chain(mo, 1, 0, 401)
-        try:
-            worst = 0.0
-            for s in range(12):
-                log("qwen3 mxfp4 chain step %d" % s)
-                ch.run(s)
-                snap = ch.snapshot()
-                sample = s in (0, 6, 11)
-                worst = max(worst, replay_step(mo, caches, snap, 1, 0, (0, 17, 47) if sample else (), (0,)))
-            log("qwen3 mxfp4 chain: 12 steps bit-exact, sampled rows within %.2e" % worst)
-        finally:
-            ch.close()
-        check_counters(mo, caches)
-        check_slot_bytes(mo, (0, 47))
-    finally:
-        mo.close()

@@ -254,6 +254,11 @@ def test_create_rejects_bad_shapes():
     with pytest.raises(m.MoeError) as ei:
         m.moe_offload_create(8, 4, 100, 128, 2, 1, 4)  # hidden not a multiple of 128
     assert ei.value.code == m.EUNSUPPORTED
+    for H, F in ((384, 256), (256, 128)):  # MXFP4: hidden and ffn must be multiples of 256
+        with pytest.raises(m.MoeError) as ei:
+            m.moe_offload_create(8, 4, H, F, 2, m.MXFP4, 4)
+        assert ei.value.code == m.EUNSUPPORTED
+    m.moe_offload_destroy(m.moe_offload_create(8, 4, 256, 256, 2, m.MXFP4, 4))
     with pytest.raises(m.MoeError) as ei:
         m.moe_offload_create(8, 4, 128, 128, 2, 1, 4, device=99)
     assert ei.value.code == m.EINVAL
