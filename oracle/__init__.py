@@ -31,6 +31,8 @@ _LIB = os.path.join(_HERE, "_build", "libmoe_oracle.so")
 _lib = None
 
 F32, BF16, FP8, MXFP4 = 0, 1, 2, 3
+LRU, SCORED = 0, 1  # eviction policies
+SCORE_MAX = (1 << 20) - 1
 SLOTS, STAGED, STAGED_ALL = 0, 1, 2
 
 
@@ -67,6 +69,8 @@ def lib():
         L.orc_cache_new.argtypes = [i32, i32]
         L.orc_cache_new.restype = vp
         L.orc_cache_free.argtypes = [vp]
+        L.orc_cache_set_policy.argtypes = [vp, i32]
+        L.orc_cache_scores.argtypes = [vp, vp]
         L.orc_cache_state.argtypes = [vp, vp, vp, vp, vp]
         L.orc_cache_counters.argtypes = [vp, vp]
         L.orc_ensure.argtypes = [vp, vp, i32, i32, vp, vp]
@@ -166,11 +170,12 @@ class Cache:
     staging: optional shared uint8 [E, stride] array; allocated on first use.
     """
 
-    def __init__(self, E, S, host=None, record_bytes_=None, staging=None, keep_bytes=True):
+    def __init__(self, E, S, host=None, record_bytes_=None, staging=None, keep_bytes=True, policy=LRU):
         self.E, self.S = E, S
         self._c = lib().orc_cache_new(E, S)
         if not self._c:
             raise ValueError("bad cache shape E=%d S=%d" % (E, S))
+        lib().orc_cache_set_policy(self._c, policy)
         self.host = host
         self.keep_bytes = keep_bytes and host is not None
         if self.keep_bytes:
@@ -251,6 +256,11 @@ class Cache:
         lib().orc_cache_state(self._c, _p(so), _p(eo), _p(lu), _p(tick))
         return so, eo, lu, int(tick[0])
 
+    def scores(self):
+        out = np.empty(self.S, np.uint32)
+        lib().orc_cache_scores(self._c, _p(out))
+        return out
+
     def counters(self):
         out = np.zeros(7, np.uint64)
         lib().orc_cache_counters(self._c, _p(out))
@@ -312,10 +322,10 @@ def rmsnorm(x, wdt, eps=RMS_EPS):
 class Layer:
     """One MoE layer as the oracle sees it: router + cache + FFN."""
 
-    def __init__(self, E, S, k, H, F, wdt, host, wr, bias, shared=None, staging=None):
+    def __init__(self, E, S, k, H, F, wdt, host, wr, bias, shared=None, staging=None, policy=None):
         self.E, self.S, self.k, self.H, self.F, self.wdt = E, S, k, H, F, wdt
         self.wr, self.bias, self.shared = wr, bias, shared
-        self.cache = Cache(E, S, host, record_bytes(wdt, H, F), staging)
+        self.cache = Cache(E, S, host, record_bytes(wdt, H, F), staging, policy=LRU if policy is None else policy)
 
     def step(self, x, stage_all=False, compute_ffn=True):
         ids, w, _ = route(x, self.wr, self.bias, self.k, self.wdt)

@@ -232,12 +232,26 @@ int orc_topk(const float* logits, int T, int E, int k, int32_t* ids, double* w) 
  *        cache still leaves its most used experts resident for the next call.
  *   A record index r < S names slot r; r >= S names staging record r - S.
  *   Prefetch install ([freetoken] "Install"): see orc_install.
+ *
+ * Scored eviction (READING of the baseline policy [freetoken] "Measured"
+ * names, "scored eviction", whose only stated rule is that installed slots
+ * start at usage 0 and go first): each slot keeps a usage score, the number
+ * of ensure calls that routed to its expert since it was loaded (per call,
+ * like the LRU clock), saturating at 2^20 - 1; a slot's score is 0 when an
+ * expert is loaded or installed into it.  With policy ORC_SCORED the victim
+ * key is (occupied, score, last_use, slot): least used first, then least
+ * recently used, then the lower slot.  Everything else is as above.
  */
+enum { ORC_LRU = 0, ORC_SCORED = 1 };
+#define ORC_SCORE_MAX ((1u << 20) - 1u)
+
 typedef struct {
   int E, S;
+  int policy;
   int32_t* slot_of;
   int32_t* expert_of;
   uint64_t* last_use;
+  uint32_t* score;
   uint64_t tick;
   /* cumulative counters */
   uint64_t calls, hits, misses, staged_calls, staged_copies, prefetch_installs, prefetch_hits;
@@ -251,6 +265,7 @@ orc_cache* orc_cache_new(int E, int S) {
   c->slot_of = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
   c->expert_of = (int32_t*)malloc(sizeof(int32_t) * (size_t)S);
   c->last_use = (uint64_t*)calloc((size_t)S, sizeof(uint64_t));
+  c->score = (uint32_t*)calloc((size_t)S, sizeof(uint32_t));
   for (int e = 0; e < E; ++e) c->slot_of[e] = -1;
   for (int s = 0; s < S; ++s) c->expert_of[s] = -1;
   return c;
@@ -261,7 +276,14 @@ void orc_cache_free(orc_cache* c) {
   free(c->slot_of);
   free(c->expert_of);
   free(c->last_use);
+  free(c->score);
   free(c);
+}
+
+void orc_cache_set_policy(orc_cache* c, int policy) { c->policy = policy == ORC_SCORED ? ORC_SCORED : ORC_LRU; }
+
+void orc_cache_scores(const orc_cache* c, uint32_t* score) {
+  memcpy(score, c->score, sizeof(uint32_t) * (size_t)c->S);
 }
 
 void orc_cache_state(const orc_cache* c, int32_t* slot_of, int32_t* expert_of, uint64_t* last_use, uint64_t* tick) {
@@ -281,6 +303,7 @@ void orc_cache_counters(const orc_cache* c, uint64_t out[7]) {
 static int victim_before(const orc_cache* c, int a, int b) {
   int oa = c->expert_of[a] >= 0, ob = c->expert_of[b] >= 0;
   if (oa != ob) return oa < ob;
+  if (c->policy == ORC_SCORED && c->score[a] != c->score[b]) return c->score[a] < c->score[b];
   if (c->last_use[a] != c->last_use[b]) return c->last_use[a] < c->last_use[b];
   return a < b;
 }
@@ -372,9 +395,14 @@ int orc_ensure(orc_cache* c, const int32_t* ids, int n, int k, int32_t* slot_ids
     if (old >= 0) c->slot_of[old] = -1;
     c->expert_of[v] = e;
     c->slot_of[e] = v;
+    c->score[v] = 0;
   }
   for (int e = 0; e < E; ++e)
-    if (inD[e] && c->slot_of[e] >= 0) c->last_use[c->slot_of[e]] = c->tick;
+    if (inD[e] && c->slot_of[e] >= 0) {
+      int s = c->slot_of[e];
+      c->last_use[s] = c->tick;
+      if (c->score[s] < ORC_SCORE_MAX) c->score[s] += 1;
+    }
   int count = 0;
   for (int e = 0; e < E; ++e) {
     if (!miss[e]) continue;
@@ -482,6 +510,7 @@ int orc_install(orc_cache* c, const int32_t* pred, int T, int k, int max_n, int3
     c->expert_of[v] = e;
     c->slot_of[e] = v;
     c->last_use[v] = 0;
+    c->score[v] = 0;
     desc[2 + 2 * i] = e;
     desc[3 + 2 * i] = v;
   }

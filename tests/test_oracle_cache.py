@@ -61,17 +61,22 @@ def test_single_id_calls_match_mattson_and_textbook_lru(orc, seed):
 
 
 class BruteCache:
-    """The batched rules restated plainly (sorted(), dicts), independently of the C code."""
+    """The batched rules restated plainly (sorted(), dicts), independently of the C code.
+    scored=True: least-used slots go first (usage = calls since loaded, capped), then LRU."""
 
-    def __init__(self, E, S):
+    def __init__(self, E, S, scored=False, cap=(1 << 20) - 1):
         self.E, self.S = E, S
         self.held = [None] * S
         self.home = {}
         self.used = [0] * S
+        self.uses = [0] * S
         self.clock = 0
+        self.scored, self.cap = scored, cap
 
     def _victims(self, protect):
         cands = [s for s in range(self.S) if self.held[s] is None or self.held[s] not in protect]
+        if self.scored:
+            return sorted(cands, key=lambda s: (self.held[s] is not None, self.uses[s], self.used[s], s))
         return sorted(cands, key=lambda s: (self.held[s] is not None, self.used[s], s))
 
     def _put(self, e, s):
@@ -79,6 +84,7 @@ class BruteCache:
             del self.home[self.held[s]]
         self.held[s] = e
         self.home[e] = s
+        self.uses[s] = 0
 
     def ensure(self, ids, k):
         self.clock += 1
@@ -94,6 +100,7 @@ class BruteCache:
         for e in D:
             if e in self.home:
                 self.used[self.home[e]] = self.clock
+                self.uses[self.home[e]] = min(self.uses[self.home[e]] + 1, self.cap)
         rec = lambda e: self.home.get(e, self.S + e)
         return [rec(e) for e in ids], int(len(D) > self.S), [(e, rec(e)) for e in miss]
 
@@ -161,14 +168,15 @@ def _check_invariants(c, ids, slot_ids, mode, pairs, before):
         assert eo0[s] < 0 or eo0[s] not in D
 
 
+@pytest.mark.parametrize("scored", [False, True])
 @pytest.mark.parametrize("seed", range(8))
-def test_batched_calls_match_brute_force(orc, seed):
+def test_batched_calls_match_brute_force(orc, seed, scored):
     rng = np.random.default_rng(100 + seed)
     E = int(rng.choice([8, 16, 32]))
     k = int(rng.choice([1, 2, 4]))
     S = int(rng.integers(k, E + 1))
-    c = orc.Cache(E, S)
-    b = BruteCache(E, S)
+    c = orc.Cache(E, S, policy=orc.SCORED if scored else orc.LRU)
+    b = BruteCache(E, S, scored=scored)
     p = 1.0 / np.arange(1, E + 1) ** rng.uniform(0.3, 1.5)
     for step in range(200):
         T = int(rng.integers(1, 6))
@@ -186,6 +194,7 @@ def test_batched_calls_match_brute_force(orc, seed):
         assert slot_ids.reshape(-1).tolist() == es
         assert mode == em
         assert [tuple(map(int, r)) for r in pairs] == ep
+        assert c.scores().tolist() == b.uses
         _check_invariants(c, ids, slot_ids, mode, pairs, before)
 
 
@@ -270,3 +279,35 @@ def test_install_budget_zero_changes_nothing(orc):
         assert len(a.install(ids[::-1], 0)) == 0
         ra, rb = a.ensure(ids), b.ensure(ids)
         assert np.array_equal(ra[0], rb[0]) and ra[1] == rb[1] and np.array_equal(ra[2], rb[2])
+
+
+def test_scored_eviction_prefers_the_least_used_slot(orc):
+    # two slots; expert 0 is routed three times, expert 1 once but more recently: LRU evicts expert 0
+    # (slot 0, last used at tick 3), scored eviction evicts expert 1 (slot 1, used once since loaded)
+    calls = [[[0, 1]], [[0]], [[0]], [[1]], [[2]]]
+    victims = {}
+    for policy in (orc.LRU, orc.SCORED):
+        c = orc.Cache(4, 2, policy=policy)
+        for ids in calls:
+            _, _, pairs = c.ensure(np.array(ids, np.int32))
+        victims[policy] = pairs.tolist()
+        so, eo, lu, tick = c.state()
+        if policy == orc.SCORED:
+            assert eo.tolist() == [0, 2] and c.scores().tolist() == [3, 1] and lu.tolist() == [3, 5]
+    assert victims[orc.LRU] == [[2, 0]] and victims[orc.SCORED] == [[2, 1]]
+
+
+def test_scored_installs_start_at_zero_and_go_first(orc):
+    c = orc.Cache(8, 3, policy=orc.SCORED)
+    c.ensure(np.array([[0, 1]], np.int32))
+    c.ensure(np.array([[0]], np.int32))
+    inst = c.install(np.array([[5]], np.int32), 1)  # into the free slot, at usage 0
+    assert inst.tolist() == [[5, 2]] and c.scores().tolist() == [2, 1, 0]
+    _, _, pairs = c.ensure(np.array([[7, 0]], np.int32))
+    assert pairs.tolist() == [[7, 2]]  # the installed, never used slot goes before expert 1 (used once)
+    # with a budget of two, the second install takes the least used occupied slot (expert 1, not expert 0)
+    c2 = orc.Cache(8, 3, policy=orc.SCORED)
+    c2.ensure(np.array([[0, 1]], np.int32))
+    c2.ensure(np.array([[0]], np.int32))
+    assert c2.install(np.array([[5, 6]], np.int32), 2).tolist() == [[5, 2], [6, 1]]
+    assert c2.scores().tolist() == [2, 0, 0]
