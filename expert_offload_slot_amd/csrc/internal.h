@@ -25,12 +25,14 @@ struct CacheDev {
   int32_t* slot_of;     // [E]
   int32_t* expert_of;   // [S]
   uint64_t* last_use;   // [S]
+  uint32_t* score;      // [S] usage score (scored eviction)
   uint64_t* tick;       // [1]
   int32_t* copy_list;   // [2 + 2*max(S,E)]
   int32_t* pf_list;     // [2 + 2*S]
   uint64_t* counters;   // [C_N]
   int32_t* err;         // [1] sticky MOE_DEV_ERR_* bits
   int E, S;
+  int scored;           // 1: victims by (occupied, score, last_use, slot)
   uint64_t record_bytes;
 };
 

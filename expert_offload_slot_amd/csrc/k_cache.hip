@@ -79,6 +79,7 @@ __global__ void k_reset(CacheDev c) {
   for (int s = i0; s < c.S; s += step) {
     c.expert_of[s] = -1;
     c.last_use[s] = 0;
+    c.score[s] = 0;
   }
   for (int i = i0; i < C_N; i += step) c.counters[i] = 0;
   if (i0 == 0) {

@@ -184,6 +184,7 @@ int moe_offload_create(const moe_offload_desc* d, moe_offload** out) {
     return o;
   };
   size_t o_slot_of = take(4 * (size_t)h->E), o_expert_of = take(4 * (size_t)h->S), o_last = take(8 * (size_t)h->S);
+  size_t o_score = take(4 * (size_t)h->S);
   size_t o_tick = take(8), o_list = take(4 * (2 + 2 * (size_t)maxSE)), o_pf = take(4 * (2 + 2 * (size_t)h->S));
   size_t o_cnt = take(8 * moe::C_N), o_err = take(4), o_logits = take(4 * (size_t)h->max_tokens * h->E);
   size_t o_grp = take(4 * (size_t)h->gl.words());
@@ -195,6 +196,8 @@ int moe_offload_create(const moe_offload_desc* d, moe_offload** out) {
   h->cache.slot_of = (int32_t*)(b + o_slot_of);
   h->cache.expert_of = (int32_t*)(b + o_expert_of);
   h->cache.last_use = (uint64_t*)(b + o_last);
+  h->cache.score = (uint32_t*)(b + o_score);
+  h->cache.scored = (h->flags & MOE_FLAG_SCORED) ? 1 : 0;
   h->cache.tick = (uint64_t*)(b + o_tick);
   h->cache.copy_list = (int32_t*)(b + o_list);
   h->cache.pf_list = (int32_t*)(b + o_pf);
@@ -409,6 +412,7 @@ int moe_offload_query(const moe_offload* h, moe_info* out) {
   out->slot_of = h->cache.slot_of;
   out->expert_of = h->cache.expert_of;
   out->last_use = h->cache.last_use;
+  out->score = h->cache.score;
   out->copy_list = h->cache.copy_list;
   out->prefetch_list = h->cache.pf_list;
   out->slots = h->slots;

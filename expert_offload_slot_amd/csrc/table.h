@@ -11,9 +11,13 @@
 
 namespace moe {
 
-// victim order as one integer: (occupied, last_use, slot) ascending.  last_use
-// is a call count, far below 2^53.
-__device__ __forceinline__ uint64_t victim_key(bool occ, uint64_t lu, int slot) {
+// victim order as one integer, ascending: LRU (occupied, last_use, slot); scored
+// (occupied, score, last_use, slot).  last_use is a call count, below 2^33 in
+// any run; scores saturate at kScoreMax (20 bits).
+constexpr uint32_t kScoreMax = (1u << 20) - 1u;
+__device__ __forceinline__ uint64_t victim_key(const CacheDev& c, bool occ, uint32_t score, uint64_t lu, int slot) {
+  if (c.scored)
+    return (occ ? (1ull << 63) : 0ull) | ((uint64_t)score << 43) | ((lu & ((1ull << 33) - 1)) << 10) | (uint64_t)slot;
   return (occ ? (1ull << 63) : 0ull) | ((lu & ((1ull << 53) - 1)) << 10) | (uint64_t)slot;
 }
 
@@ -21,6 +25,7 @@ struct SharedTable {
   int slot_of[kMaxExperts];
   int expert_of[kMaxExperts];
   uint64_t last_use[kMaxExperts];
+  uint32_t score[kMaxExperts];
   int flag[kMaxExperts];   // ensure: expert in D; install: tokens predicting it
   int aux[kMaxExperts];    // ensure: pairs routed to it; install: best top-k position
   int cand[kMaxExperts];   // ensure: best top-k position; install: candidate by rank
@@ -52,6 +57,7 @@ __device__ __forceinline__ void load_table(const CacheDev& c, SharedTable& t) {
     }
     t.expert_of[tid] = e;
     t.last_use[tid] = c.last_use[tid];
+    t.score[tid] = c.score[tid];
   }
   // the call counter and the statistics, from another wavefront
   const int u = tid - 64 * (kWaves - 1);
@@ -65,6 +71,7 @@ __device__ __forceinline__ void store_table(const CacheDev& c, const SharedTable
   if (tid < c.S) {
     c.expert_of[tid] = t.expert_of[tid];
     c.last_use[tid] = t.last_use[tid];
+    c.score[tid] = t.score[tid];
   }
 }
 
@@ -147,7 +154,7 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
       const int ex = t.expert_of[tid];
       const bool occ = ex >= 0;
       elig = !occ || !t.flag[ex];
-      vkey[tid] = elig ? victim_key(occ, t.last_use[tid], tid) : ~0ull;
+      vkey[tid] = elig ? victim_key(c, occ, t.score[tid], t.last_use[tid], tid) : ~0ull;
     }
     if (over) {  // pairs routed to each expert and its best top-k position
       if (tid < E) {
@@ -197,7 +204,12 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
     }
     __syncthreads();
   }
-  if (inD && t.slot_of[tid] >= 0) t.last_use[t.slot_of[tid]] = tick;
+  if (inD && t.slot_of[tid] >= 0) {  // used now; a slot just loaded starts from 0
+    const int s = t.slot_of[tid];
+    const uint32_t old = miss ? 0u : t.score[s];
+    t.last_use[s] = tick;
+    t.score[s] = old < kScoreMax ? old + 1 : old;
+  }
   __syncthreads();
   for (int i = tid; i < n; i += kBlock) {
     const int e = ids[i];
@@ -273,7 +285,7 @@ __device__ __forceinline__ void install_body(const CacheDev& c, SharedTable& t, 
     const int ex = t.expert_of[tid];
     const bool occ = ex >= 0;
     elig = !occ || t.flag[ex] == 0;
-    vkey[tid] = elig ? victim_key(occ, t.last_use[tid], tid) : ~0ull;
+    vkey[tid] = elig ? victim_key(c, occ, t.score[tid], t.last_use[tid], tid) : ~0ull;
   }
   int nc, nv;
   (void)block_rank(cand, t.wave, &nc);  // its barriers also publish ckey / vkey
@@ -302,6 +314,7 @@ __device__ __forceinline__ void install_body(const CacheDev& c, SharedTable& t, 
     t.expert_of[v] = e;
     t.slot_of[e] = v;
     t.last_use[v] = 0;
+    t.score[v] = 0;
     c.pf_list[2 + 2 * tid] = e;
     c.pf_list[3 + 2 * tid] = v;
   }

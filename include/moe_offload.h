@@ -106,7 +106,8 @@ enum {
 /* creation flags */
 enum {
   MOE_FLAG_AUDIT = 1,          /* check the slot table after every ensure/install (sets MOE_DEV_ERR_AUDIT) */
-  MOE_FLAG_HOST_COHERENT = 2   /* fine-grained (coherent) host store instead of coarse-grained */
+  MOE_FLAG_HOST_COHERENT = 2,  /* fine-grained (coherent) host store instead of coarse-grained */
+  MOE_FLAG_SCORED = 4          /* scored eviction: victims by (occupied, usage score, last_use, slot) */
 };
 
 typedef struct {
@@ -162,6 +163,8 @@ typedef struct {
   size_t record_bytes;
   size_t record_stride;
   int32_t E, S, H, F, k, dtype, max_tokens, device;
+  uint32_t* score;        /* [S]  usage score: ensure calls routed to the slot's expert since it was loaded
+                             (saturating at 2^20 - 1); kept under both policies, used by MOE_FLAG_SCORED */
 } moe_info;
 
 /* copy-list modes (copy_list[0]) */

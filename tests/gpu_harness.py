@@ -135,6 +135,9 @@ class GpuLayer:
         lu = d2h(self.info["last_use"], 8 * self.S, np.uint64)
         return so, eo, lu
 
+    def scores(self):
+        return d2h(self.info["score"], 4 * self.S, np.uint32)
+
     def stats(self):
         return m.moe_offload_stats(self.h)
 
@@ -167,6 +170,7 @@ def compare_call(gl, ol_step, T, y64=None, check_table=True, oracle_cache=None):
         so, eo, lu = gl.table()
         oso, oeo, olu, _ = oracle_cache.state()
         assert np.array_equal(so, oso) and np.array_equal(eo, oeo) and np.array_equal(lu, olu)
+        assert np.array_equal(gl.scores(), oracle_cache.scores())
     if y64 is not None:
         err = row_rel_err(to_np(gl.y[:T]), y64, gl.wdt)
         assert err <= TOL[gl.wdt], err

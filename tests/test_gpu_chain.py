@@ -37,7 +37,7 @@ def test_rmsnorm_parity():
 
 
 class ChainModel:
-    def __init__(self, L, E, S, k, H, F, wdt, T, seed, prefetch_n=0, zipf=1.2, rho=0.9, shared=False):
+    def __init__(self, L, E, S, k, H, F, wdt, T, seed, prefetch_n=0, zipf=1.2, rho=0.9, shared=False, scored=False):
         self.L, self.E, self.S, self.k, self.H, self.F, self.wdt, self.T = L, E, S, k, H, F, wdt, T
         self.hosts, self.routers, self.handles, self.shared = [], [], [], []
         rdt = 1 if wdt >= 2 else wdt  # fp8 and MXFP4 layers take a bf16 router and bf16 activations
@@ -45,8 +45,8 @@ class ChainModel:
             self.hosts.append(synth.records(seed, l, E, H, F, wdt))
             self.routers.append(synth.router(seed, l, E, H, rdt, zipf_s=zipf))
             self.shared.append(synth.records(seed, l, 1, H, F, wdt, shared=True)[0] if shared else None)
-            h = m.moe_offload_create(E, S, H, F, k, wdt, T, 0, m.FLAG_AUDIT, None,
-                                     self.handles[0] if l else None)
+            h = m.moe_offload_create(E, S, H, F, k, wdt, T, 0, m.FLAG_AUDIT | (m.FLAG_SCORED if scored else 0),
+                                     None, self.handles[0] if l else None)
             m.host_array(h, E)[:, :self.hosts[l].shape[1]] = self.hosts[l]
             self.handles.append(h)
         self.wr = [to_dev(w) for w, _ in self.routers]
@@ -84,7 +84,8 @@ class ChainModel:
         so = d2h(i["slot_of"], 4 * self.E, np.int32)
         eo = d2h(i["expert_of"], 4 * self.S, np.int32)
         lu = d2h(i["last_use"], 8 * self.S, np.uint64)
-        return (int(lst[0]), lst[2:2 + 2 * lst[1]].reshape(-1, 2)), pf[2:2 + 2 * pf[1]].reshape(-1, 2), (so, eo, lu)
+        sc = d2h(i["score"], 4 * self.S, np.uint32)
+        return (int(lst[0]), lst[2:2 + 2 * lst[1]].reshape(-1, 2)), pf[2:2 + 2 * pf[1]].reshape(-1, 2), (so, eo, lu, sc)
 
     def close(self):
         m.moe_chain_destroy(self.chain)
@@ -117,9 +118,10 @@ def oracle_replay_step(cm, caches, snap, prefetch_n, check_ffn=True):
             assert np.array_equal(snap["x"][l + 1], oracle.residual(snap["x"][l], snap["y"][l], cm.wdt))
     # lists and tables of every layer after the step (each handle's last call)
     for l in range(L):
-        (mode, pairs), pf, (so, eo, lu) = cm.lists(l)
+        (mode, pairs), pf, (so, eo, lu, sc) = cm.lists(l)
         oso, oeo, olu, _ = caches[l].state()
         assert np.array_equal(so, oso) and np.array_equal(eo, oeo) and np.array_equal(lu, olu), l
+        assert np.array_equal(sc, caches[l].scores()), l
 
 
 @pytest.mark.parametrize("prefetch_n", [0, 2])
@@ -200,3 +202,19 @@ def test_chain_variants_match_eager_and_oracle(case):
     finally:
         cg.close()
         ce.close()
+
+
+@pytest.mark.parametrize("prefetch_n,T", [(0, 1), (3, 2)])
+def test_chain_scored_eviction(prefetch_n, T):
+    """Scored eviction in the decode chain, with and without lookahead installs (usage 0, first out)."""
+    L, E, S, k, H, F = 3, 32, 8, 4, 256, 256
+    print("chain scored eviction prefetch=%d T=%d" % (prefetch_n, T), flush=True)
+    cg = ChainModel(L, E, S, k, H, F, 1, T, 87, prefetch_n, scored=True)
+    caches = [oracle.Cache(E, S, cg.hosts[l], oracle.record_bytes(1, H, F), policy=oracle.SCORED) for l in range(L)]
+    try:
+        for s in range(10):
+            cg.run(s, graph=True)
+            oracle_replay_step(cg, caches, cg.snapshot(), prefetch_n)
+        assert all(m.moe_offload_stats(h)["error"] == 0 for h in cg.handles)
+    finally:
+        cg.close()

@@ -105,7 +105,8 @@ def layer_lists(mo, l):
     so = d2h(i["slot_of"], 4 * mo.E, np.int32)
     eo = d2h(i["expert_of"], 4 * mo.S, np.int32)
     lu = d2h(i["last_use"], 8 * mo.S, np.uint64)
-    return (int(lst[0]), lst[2:2 + 2 * lst[1]].reshape(-1, 2)), pf[2:2 + 2 * pf[1]].reshape(-1, 2), (so, eo, lu)
+    sc = d2h(i["score"], 4 * mo.S, np.uint32)
+    return (int(lst[0]), lst[2:2 + 2 * lst[1]].reshape(-1, 2)), pf[2:2 + 2 * pf[1]].reshape(-1, 2), (so, eo, lu, sc)
 
 
 def replay_step(mo, caches, snap, T, prefetch_n, ffn_layers=(), ffn_tokens=()):
@@ -122,7 +123,7 @@ def replay_step(mo, caches, snap, T, prefetch_n, ffn_layers=(), ffn_tokens=()):
         assert np.abs(snap["w"][l] - w).max() <= 1e-5, l
         sid, mode, pairs = caches[l].ensure(ids)
         assert np.array_equal(sid, snap["sid"][l]), l
-        (gmode, gpairs), gpf, (so, eo, lu) = layer_lists(mo, l)
+        (gmode, gpairs), gpf, (so, eo, lu, sc) = layer_lists(mo, l)
         assert gmode == mode and np.array_equal(gpairs, pairs), (l, gmode, gpairs, mode, pairs)
         if l in installs:
             assert np.array_equal(gpf, installs[l]), (l, gpf, installs[l])
@@ -131,6 +132,7 @@ def replay_step(mo, caches, snap, T, prefetch_n, ffn_layers=(), ffn_tokens=()):
             installs[l + 1] = caches[l + 1].install(pred, prefetch_n)
         oso, oeo, olu, _ = caches[l].state()
         assert np.array_equal(so, oso) and np.array_equal(eo, oeo) and np.array_equal(lu, olu), l
+        assert np.array_equal(sc, caches[l].scores()), l
         if l in ffn_layers:
             toks = [t for t in ffn_tokens if t < T]
             _, y64 = oracle.ffn(xn[toks], mo.wdt, mo.H, mo.F, oracle.host_records(mo.hosts[l], ids[toks]),

@@ -25,7 +25,8 @@ def run_sequence(E, S, k, H, F, wdt, zipf, seed, steps, Ts, shared=False, flags=
     host, wr, b, sh = make_layer_inputs(seed, 0, E, H, F, wdt, zipf, shared)
     maxT = max(Ts)
     gl = GpuLayer(E, S, k, H, F, wdt, maxT, host, wr, b, flags=flags, shared=sh)
-    ol = oracle.Layer(E, S, k, H, F, wdt, host, wr, b, shared=sh)
+    ol = oracle.Layer(E, S, k, H, F, wdt, host, wr, b, shared=sh,
+                      policy=oracle.SCORED if flags & m.FLAG_SCORED else oracle.LRU)
     xs = synth.tokens(seed, 7, maxT, H, steps, 0.0, wdt)
     modes, errs = [], []
     try:
@@ -122,6 +123,13 @@ def test_mxfp4_decode_batches_with_shared_expert(S):
 def test_mxfp4_prefill_gemm_ragged_tiles():
     # > 64 tokens per call: the grouped GEMM with E2M1 codes widened (scale folded in) into LDS
     run_sequence(12, 6, 3, 256, 512, 3, 1.2, 62, 3, [100, 130, 65], shared=True)
+
+
+@pytest.mark.parametrize("E,S,k,Ts", [(16, 6, 4, [1, 2, 3]), (32, 10, 4, [1, 4, 9]), (64, 12, 8, [1, 2])])
+def test_scored_eviction_parity(E, S, k, Ts):
+    # scored eviction: slot tables, usage scores, copy lists and counters bit-exact against the oracle,
+    # with Zipf routing (repeat customers) and batches that overflow the cache
+    run_sequence(E, S, k, 256, 256, 1, 1.2, 70 + E, 30, Ts, flags=m.FLAG_AUDIT | m.FLAG_SCORED)
 
 
 def test_fp8_without_shared_expert():
