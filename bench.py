@@ -151,11 +151,12 @@ def main():
         xs = synth.tokens(args.seed, 100 + T, T, H, n, 0.9, synth.BF16)
         return torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16).to(dev)
 
-    def run_decode(T, warm, steps, tag, prefetch_n=0, xs_d=None):
+    def run_decode(T, warm, steps, tag, prefetch_n=0, xs_d=None, hs=None):
         """graph replays of the whole step; returns (tok/s, ms/step, stats delta, chain, buffers, tokens)"""
+        hs = hs or handles
         if xs_d is None:
             xs_d = token_stream(T, warm + steps + args.prof_steps)
-        c = m.moe_chain_create(handles, wr_d, b_d, T, prefetch_n)
+        c = m.moe_chain_create(hs, wr_d, b_d, T, prefetch_n)
         bufs = m.moe_chain_get_buffers(c)
         nbytes = T * H * 2
 
@@ -167,7 +168,7 @@ def main():
         for s in range(warm):
             step(s)
         torch.cuda.synchronize()
-        before = stats_sum()
+        before = stats_sum(hs)
         a, b_ = ev(), ev()
         torch.cuda.synchronize()
         a.record(stream)
@@ -176,7 +177,7 @@ def main():
         b_.record(stream)
         torch.cuda.synchronize()
         ms = a.elapsed_time(b_)
-        after = stats_sum()
+        after = stats_sum(hs)
         delta = {kk: after[kk] - before[kk] for kk in after}
         assert after["error"] == 0, "device error %d" % after["error"]
         log("%s: batch %d, %d steps in %.1f ms: %.1f tok/s, copies/token %.2f (%.2f into slots), staged calls %d/%d" %
@@ -311,6 +312,7 @@ def main():
                                      "staged_copies_per_token": round(d["staged_copies"] / (T * steps), 4)}
             m.moe_chain_destroy(c2)
         result["prefetch"] = prefetch_compare(args, m, hip, handles, run_decode, token_stream)
+        result["eviction"] = eviction_compare(args, m, hip, handles, run_decode, token_stream)
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args, handles, routers, stride, T0)
@@ -572,6 +574,33 @@ def prefetch_compare(args, m, hip, handles, run_decode, token_stream):
                                   "prefetch_hits_per_token": round(d["prefetch_hits"] / (T * steps), 4)}
         m.moe_chain_destroy(c)
     out["outputs_identical"] = bool(np.array_equal(last[0], last[4]))
+    return out
+
+
+def eviction_compare(args, m, hip, handles, run_decode, token_stream):
+    """LRU against scored eviction (least used first, then LRU), each from an empty cache on the same token
+    stream; the scored layers share the LRU layers' host stores.  Outputs must be bitwise identical."""
+    import numpy as np
+    T, warm, steps = 1, 16, 128
+    xs_d = token_stream(T, warm + steps + args.prof_steps)
+    scored = [m.moe_offload_create(E, SLOTS, H, F, K_TOP, m.BF16, 32, 0, m.FLAG_SCORED, h, handles[0])
+              for h in handles]
+    out, last = {}, {}
+    try:
+        for name, hs in (("lru", handles), ("scored", scored)):
+            for h in hs:
+                m.moe_offload_reset(h)
+            ts, msps, d, c, bufs, _ = run_decode(T, warm, steps, "eviction-" + name, xs_d=xs_d, hs=hs)
+            xl = np.empty((T, H), dtype=np.uint16)
+            assert hip.hipMemcpy(xl.ctypes.data, bufs["x"] + len(hs) * T * H * 2, xl.nbytes, 2) == 0
+            last[name] = xl
+            out[name] = {"tokens_per_s": round(ts, 2), "ms_per_step": round(msps, 3),
+                         "misses_per_token": round(d["misses"] / (T * steps), 4)}
+            m.moe_chain_destroy(c)
+    finally:
+        for h in reversed(scored):
+            m.moe_offload_destroy(h)
+    out["outputs_identical"] = bool(np.array_equal(last["lru"], last["scored"]))
     return out
 
 
