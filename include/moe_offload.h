@@ -198,7 +198,11 @@ int moe_route_topk(moe_offload* h, const void* x, const void* w_router, const fl
 
 /* LRU slot table update for one call (single workgroup, fixed shape):
  * D = distinct ids.  Victims are the slots not holding an expert of D, in
- * (free first, then least recently used, then lowest slot) order.
+ * (free first, then least recently used, then lowest slot) order; with
+ * MOE_FLAG_SCORED, (free first, then lowest usage score, then least recently
+ * used, then lowest slot), the score counting the calls that routed to the
+ * slot's expert since it was loaded.  Every slot used by the call gets
+ * last_use = tick and its score incremented (a slot just loaded: 1).
  * |D| <= S: misses (ascending id) take the victims; copy list
  * {SLOTS, |misses|, (expert, slot)...}.  |D| > S (decode batches wider than
  * the cache; the page stages whole layers only for prefill): the victims are
@@ -254,7 +258,7 @@ int moe_prefill_stage(moe_offload* h, const int32_t* ids, int32_t T, int32_t* sl
  * predicted experts that are not resident, ordered by (number of tokens
  * predicting them desc, best top-k position asc, id asc), and place them in
  * victim slots (same order as ensure, never a slot holding a predicted
- * expert) with last_use = 0, i.e. evicted first.  Writes the prefetch copy
+ * expert) with last_use = 0 and usage score 0, i.e. evicted first.  Writes the prefetch copy
  * list.  Must be issued on the compute stream (single slot-table writer).
  *   pred_ids: device [T, k] int32.  0 <= max_n <= S. */
 int moe_prefetch_install(moe_offload* h, const int32_t* pred_ids, int32_t T, int32_t max_n, void* stream);
