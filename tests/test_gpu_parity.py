@@ -92,6 +92,13 @@ def test_fp8_prefill_gemm_ragged_tiles():
     run_sequence(12, 6, 3, 256, 384, 2, 1.2, 33, 3, [100, 130, 65], shared=True)
 
 
+@pytest.mark.parametrize("wdt", [1, 2, 3])
+def test_prefill_gemm_several_tiles_per_record(wdt):
+    # the grouped GEMM at H = F = 512 (8 row tiles each way) in bf16, fp8 and MXFP4; Zipf routing gives
+    # records several 64-pair token tiles and a ragged last one
+    run_sequence(8, 8, 2, 512, 512, wdt, 1.2, 80 + wdt, 3, [300, 129, 70], shared=(wdt != 1))
+
+
 def test_bf16_prefill_gemm_one_hot_record():
     # every token routed to the same experts (k = E = S): one long record per expert
     run_sequence(2, 2, 2, 128, 256, 1, 0.0, 34, 2, [257, 64])
