@@ -71,6 +71,9 @@ def lib():
         L.orc_cache_free.argtypes = [vp]
         L.orc_cache_set_policy.argtypes = [vp, i32]
         L.orc_cache_scores.argtypes = [vp, vp]
+        L.orc_cache_pinned.argtypes = [vp, vp]
+        L.orc_pin.argtypes = [vp, vp, i32, vp]
+        L.orc_pin.restype = i32
         L.orc_cache_state.argtypes = [vp, vp, vp, vp, vp]
         L.orc_cache_counters.argtypes = [vp, vp]
         L.orc_ensure.argtypes = [vp, vp, i32, i32, vp, vp]
@@ -255,6 +258,19 @@ class Cache:
         tick = np.zeros(1, np.uint64)
         lib().orc_cache_state(self._c, _p(so), _p(eo), _p(lu), _p(tick))
         return so, eo, lu, int(tick[0])
+
+    def pin(self, experts):
+        """Pin the distinct experts (replacing the pinned set); returns the load list [(expert, slot)]."""
+        ex = np.ascontiguousarray(experts, dtype=np.int32).reshape(-1)
+        desc = self._desc()
+        if lib().orc_pin(self._c, _p(ex), ex.size, _p(desc)) != 0:
+            raise ValueError("bad pin set")
+        return self._unpack(desc)[1]
+
+    def pinned(self):
+        out = np.empty(self.S, np.int32)
+        lib().orc_cache_pinned(self._c, _p(out))
+        return out
 
     def scores(self):
         out = np.empty(self.S, np.uint32)

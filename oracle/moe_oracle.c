@@ -221,7 +221,8 @@ int orc_topk(const float* logits, int T, int E, int k, int32_t* ids, double* w) 
  *        recently used, ties to the lower slot.  M[i] goes to victim i; the
  *        evicted expert leaves the map.  Every e in D gets last_use = tick.
  *        slot_ids = slot_of[id].  Copy list = (M[i], victim i).
- *     3. |D| > S (STAGED; not on the page, which stages whole layers for
+ *     3. more misses than eligible victims, i.e. |D| > S when no slot is
+ *        pinned (STAGED; not on the page, which stages whole layers for
  *        prefill only): hits as in 2.  The eligible victims, in the same
  *        order, are fewer than the misses; the misses claim them in install
  *        order (pairs routed to e descending, best top-k position ascending,
@@ -252,6 +253,7 @@ typedef struct {
   int32_t* expert_of;
   uint64_t* last_use;
   uint32_t* score;
+  unsigned char* pinned; /* [S] profile-guided placement: never a victim */
   uint64_t tick;
   /* cumulative counters */
   uint64_t calls, hits, misses, staged_calls, staged_copies, prefetch_installs, prefetch_hits;
@@ -266,6 +268,7 @@ orc_cache* orc_cache_new(int E, int S) {
   c->expert_of = (int32_t*)malloc(sizeof(int32_t) * (size_t)S);
   c->last_use = (uint64_t*)calloc((size_t)S, sizeof(uint64_t));
   c->score = (uint32_t*)calloc((size_t)S, sizeof(uint32_t));
+  c->pinned = (unsigned char*)calloc((size_t)S, 1);
   for (int e = 0; e < E; ++e) c->slot_of[e] = -1;
   for (int s = 0; s < S; ++s) c->expert_of[s] = -1;
   return c;
@@ -277,6 +280,7 @@ void orc_cache_free(orc_cache* c) {
   free(c->expert_of);
   free(c->last_use);
   free(c->score);
+  free(c->pinned);
   free(c);
 }
 
@@ -284,6 +288,10 @@ void orc_cache_set_policy(orc_cache* c, int policy) { c->policy = policy == ORC_
 
 void orc_cache_scores(const orc_cache* c, uint32_t* score) {
   memcpy(score, c->score, sizeof(uint32_t) * (size_t)c->S);
+}
+
+void orc_cache_pinned(const orc_cache* c, int32_t* pinned) {
+  for (int s = 0; s < c->S; ++s) pinned[s] = c->pinned[s];
 }
 
 void orc_cache_state(const orc_cache* c, int32_t* slot_of, int32_t* expert_of, uint64_t* last_use, uint64_t* tick) {
@@ -308,12 +316,12 @@ static int victim_before(const orc_cache* c, int a, int b) {
   return a < b;
 }
 
-/* eligible slots (protect[expert] == 0) sorted into victim order; returns how many */
+/* eligible slots (not pinned, protect[expert] == 0) sorted into victim order; returns how many */
 static int victim_order(const orc_cache* c, const unsigned char* protect, int* order) {
   int n = 0;
   for (int s = 0; s < c->S; ++s) {
     int e = c->expert_of[s];
-    if (e >= 0 && protect[e]) continue;
+    if (c->pinned[s] || (e >= 0 && protect[e])) continue;
     /* insertion sort: plain and obviously ordered */
     int pos = n++;
     while (pos > 0 && victim_before(c, s, order[pos - 1])) {
@@ -359,10 +367,15 @@ int orc_ensure(orc_cache* c, const int32_t* ids, int n, int k, int32_t* slot_ids
       ++nm;
     }
   }
+  /* the eligible slots in victim order; the call overflows when the misses
+   * outnumber them (without pinned slots: exactly when |D| > S) */
+  int* order = (int*)malloc(sizeof(int) * (size_t)S);
+  int nv = victim_order(c, inD, order);
+  int over = nm > nv;
   /* the order in which the misses claim the eligible slots */
   int* claim = (int*)malloc(sizeof(int) * (size_t)(nm > 0 ? nm : 1));
   int nc = 0;
-  if (nd <= S) {
+  if (!over) {
     for (int e = 0; e < E; ++e)
       if (miss[e]) claim[nc++] = e;
   } else {
@@ -386,9 +399,7 @@ int orc_ensure(orc_cache* c, const int32_t* ids, int n, int k, int32_t* slot_ids
     free(cnt);
     free(best);
   }
-  int* order = (int*)malloc(sizeof(int) * (size_t)S);
-  int nv = victim_order(c, inD, order);
-  int ns = nm < nv ? nm : nv; /* nm <= nv whenever |D| <= S */
+  int ns = nm < nv ? nm : nv;
   for (int r = 0; r < ns; ++r) {
     int v = order[r], e = claim[r];
     int old = c->expert_of[v];
@@ -414,10 +425,10 @@ int orc_ensure(orc_cache* c, const int32_t* ids, int n, int k, int32_t* slot_ids
     int e = ids[i];
     slot_ids[i] = c->slot_of[e] >= 0 ? c->slot_of[e] : S + e;
   }
-  desc[0] = nd > S ? ORC_STAGED : ORC_SLOTS;
+  desc[0] = over ? ORC_STAGED : ORC_SLOTS;
   desc[1] = count;
   c->misses += (uint64_t)ns;
-  if (nd > S) {
+  if (over) {
     c->staged_calls += 1;
     c->staged_copies += (uint64_t)(nm - ns);
   }
@@ -518,6 +529,59 @@ int orc_install(orc_cache* c, const int32_t* pred, int T, int k, int max_n, int3
   desc[1] = n;
   c->prefetch_installs += (uint64_t)n;
   free(cnt); free(best); free(inP); free(cand); free(order);
+  return ORC_OK;
+}
+
+/* Profile-guided placement (READING of [npu-offload] "PolyStrata" placement,
+ * a static hot set from a routing profile, mixed with the dynamic cache):
+ * pin(P) makes the distinct experts P resident and never-evicted, replacing
+ * any earlier pinned set.  Pinned slots are never victims of ensure or
+ * install; they are used (last_use, score) like any other slot.  Steps:
+ *   1. unpin every slot; experts of P already resident keep their slot and
+ *      are pinned there;
+ *   2. the others, ascending id, take victims in the ensure order among the
+ *      slots not pinned and not holding an expert of P; each is pinned with
+ *      last_use = tick (the clock does not advance) and score 0;
+ *   3. desc = {SLOTS, n, (expert, slot)...} for the loads.
+ * 0 <= |P| <= S - k_max is the caller's bound (so a call of k experts always
+ * finds slots); here |P| <= S.  ORC_EINVAL (nothing changed) on an id out of
+ * range or repeated. */
+int orc_pin(orc_cache* c, const int32_t* experts, int n, int32_t* desc) {
+  int E = c->E, S = c->S;
+  if (n < 0 || n > S) return ORC_EINVAL;
+  unsigned char* inP = (unsigned char*)calloc((size_t)E, 1);
+  for (int i = 0; i < n; ++i) {
+    if (experts[i] < 0 || experts[i] >= E || inP[experts[i]]) {
+      free(inP);
+      return ORC_EINVAL;
+    }
+    inP[experts[i]] = 1;
+  }
+  for (int s = 0; s < S; ++s) c->pinned[s] = 0;
+  for (int e = 0; e < E; ++e)
+    if (inP[e] && c->slot_of[e] >= 0) c->pinned[c->slot_of[e]] = 1;
+  int* order = (int*)malloc(sizeof(int) * (size_t)S);
+  int nv = victim_order(c, inP, order);
+  int count = 0;
+  for (int e = 0; e < E; ++e) {
+    if (!inP[e] || c->slot_of[e] >= 0) continue;
+    if (count >= nv) break; /* cannot happen for |P| <= S */
+    int v = order[count];
+    int old = c->expert_of[v];
+    if (old >= 0) c->slot_of[old] = -1;
+    c->expert_of[v] = e;
+    c->slot_of[e] = v;
+    c->last_use[v] = c->tick;
+    c->score[v] = 0;
+    c->pinned[v] = 1;
+    desc[2 + 2 * count] = e;
+    desc[3 + 2 * count] = v;
+    ++count;
+  }
+  desc[0] = ORC_SLOTS;
+  desc[1] = count;
+  free(order);
+  free(inP);
   return ORC_OK;
 }
 

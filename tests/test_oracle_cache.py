@@ -72,9 +72,11 @@ class BruteCache:
         self.uses = [0] * S
         self.clock = 0
         self.scored, self.cap = scored, cap
+        self.pinned = set()
 
     def _victims(self, protect):
-        cands = [s for s in range(self.S) if self.held[s] is None or self.held[s] not in protect]
+        cands = [s for s in range(self.S)
+                 if s not in self.pinned and (self.held[s] is None or self.held[s] not in protect)]
         if self.scored:
             return sorted(cands, key=lambda s: (self.held[s] is not None, self.uses[s], self.used[s], s))
         return sorted(cands, key=lambda s: (self.held[s] is not None, self.used[s], s))
@@ -91,18 +93,31 @@ class BruteCache:
         D = sorted(set(ids))
         miss = [e for e in D if e not in self.home]
         claim = miss
-        if len(D) > self.S:  # more misses than free victims: the most used misses claim them
+        victims = self._victims(set(D))
+        over = len(miss) > len(victims)
+        if over:  # more misses than victims: the most used misses claim them
             count = {e: ids.count(e) for e in D}
             best = {e: min(i % k for i, x in enumerate(ids) if x == e) for e in D}
             claim = sorted(miss, key=lambda e: (-count[e], best[e], e))
-        for e, s in zip(claim, self._victims(set(D))):
+        for e, s in zip(claim, victims):
             self._put(e, s)
         for e in D:
             if e in self.home:
                 self.used[self.home[e]] = self.clock
                 self.uses[self.home[e]] = min(self.uses[self.home[e]] + 1, self.cap)
         rec = lambda e: self.home.get(e, self.S + e)
-        return [rec(e) for e in ids], int(len(D) > self.S), [(e, rec(e)) for e in miss]
+        return [rec(e) for e in ids], int(over), [(e, rec(e)) for e in miss]
+
+    def pin(self, P):
+        P = list(P)
+        self.pinned = {self.home[e] for e in P if e in self.home}
+        loads = []
+        for e, s in zip(sorted(e for e in P if e not in self.home), self._victims(set(P))):
+            self._put(e, s)
+            self.used[s] = self.clock
+            self.pinned.add(s)
+            loads.append((e, s))
+        return loads
 
     def install(self, pred, n_max):
         T, k = len(pred), len(pred[0])
@@ -121,9 +136,10 @@ class BruteCache:
         return pairs
 
 
-def _check_invariants(c, ids, slot_ids, mode, pairs, before):
+def _check_invariants(c, ids, slot_ids, mode, pairs, before, pinned0=None):
     so, eo, lu, tick = c.state()
     S, E = c.S, c.E
+    pinned0 = np.zeros(S, np.int32) if pinned0 is None else pinned0
     for s in range(S):
         if eo[s] >= 0:
             assert so[eo[s]] == s
@@ -134,14 +150,15 @@ def _check_invariants(c, ids, slot_ids, mode, pairs, before):
     so0, eo0, lu0, tick0 = before
     R0 = set(int(v) for v in eo0 if v >= 0)
     assert tick == tick0 + 1
-    if len(D) > S:
+    eligible = [s for s in range(S) if not pinned0[s] and (eo0[s] < 0 or eo0[s] not in D)]
+    if len([e for e in D if e not in R0]) > len(eligible):
         assert mode == 1
         assert [int(p[0]) for p in pairs] == [e for e in D if e not in R0]
-        # residents stay; every slot now holds an expert of D, last used now
+        # residents stay; every slot not pinned now holds an expert of D, last used now
         for e in D:
             if so0[e] >= 0:
                 assert so[e] == so0[e]
-        assert all(eo[s] in D and lu[s] == tick for s in range(S))
+        assert all(eo[s] in D and lu[s] == tick for s in range(S) if not pinned0[s])
         # the misses that got a slot were used by at least as many pairs as those staged
         n_of = {e: int((ids == e).sum()) for e in D}
         got = [int(p[0]) for p in pairs if p[1] < S]
@@ -165,7 +182,7 @@ def _check_invariants(c, ids, slot_ids, mode, pairs, before):
     used = [int(p[1]) for p in pairs]
     assert used[:len(free0)] == free0[:len(used)]
     for s in used:
-        assert eo0[s] < 0 or eo0[s] not in D
+        assert (eo0[s] < 0 or eo0[s] not in D) and not pinned0[s]
 
 
 @pytest.mark.parametrize("scored", [False, True])
@@ -189,13 +206,19 @@ def test_batched_calls_match_brute_force(orc, seed, scored):
             exp = b.install(pred.tolist(), n)
             assert [tuple(map(int, r)) for r in got] == exp
             before = c.state()
+        if rng.random() < 0.05:  # a new pinned set (at most S - k experts, so every call fits)
+            P = rng.choice(E, size=int(rng.integers(0, S - k + 1)), replace=False).astype(np.int32)
+            assert [tuple(map(int, r)) for r in c.pin(P)] == b.pin(P.tolist())
+            assert [int(v) for v in c.pinned()] == [int(s_ in b.pinned) for s_ in range(S)]
+            before = c.state()
+        pinned0 = c.pinned()
         slot_ids, mode, pairs = c.ensure(ids)
         es, em, ep = b.ensure(ids.reshape(-1).tolist(), k)
         assert slot_ids.reshape(-1).tolist() == es
         assert mode == em
         assert [tuple(map(int, r)) for r in pairs] == ep
         assert c.scores().tolist() == b.uses
-        _check_invariants(c, ids, slot_ids, mode, pairs, before)
+        _check_invariants(c, ids, slot_ids, mode, pairs, before, pinned0)
 
 
 def test_enough_capacity_gives_only_compulsory_misses(orc):
@@ -311,3 +334,25 @@ def test_scored_installs_start_at_zero_and_go_first(orc):
     c2.ensure(np.array([[0]], np.int32))
     assert c2.install(np.array([[5, 6]], np.int32), 2).tolist() == [[5, 2], [6, 1]]
     assert c2.scores().tolist() == [2, 0, 0]
+
+
+def test_pinned_experts_are_never_evicted(orc):
+    c = orc.Cache(8, 3)
+    assert c.pin(np.array([5], np.int32)).tolist() == [[5, 0]]  # free slot 0, pinned
+    assert c.pinned().tolist() == [1, 0, 0]
+    for e, want in ((1, [[1, 1]]), (2, [[2, 2]]), (3, [[3, 1]]), (4, [[4, 2]])):
+        _, mode, pairs = c.ensure(np.array([[e]], np.int32))
+        assert mode == 0 and pairs.tolist() == want  # slots 1 and 2 take turns; slot 0 keeps expert 5
+    # two experts need slots and only two are eligible (slot 0 is pinned): they fit, expert 5 stays
+    _, mode, pairs = c.ensure(np.array([[6, 7]], np.int32))
+    assert mode == 0 and pairs.tolist() == [[6, 1], [7, 2]]
+    # three misses, two eligible slots: the call overflows although |D| = 3 = S
+    _, mode, pairs = c.ensure(np.array([[0, 1, 2]], np.int32))
+    assert mode == 1 and len(pairs) == 3 and sum(1 for p in pairs if p[1] >= 3) == 1
+    assert c.state()[1][0] == 5
+    # unpinning gives slot 0 back to the cache: last used at the pin (tick 0), it is the next victim
+    assert c.pin(np.array([], np.int32)).tolist() == [] and c.pinned().tolist() == [0, 0, 0]
+    _, _, pairs = c.ensure(np.array([[3]], np.int32))
+    assert pairs.tolist() == [[3, 0]]
+    with pytest.raises(ValueError):
+        c.pin(np.array([1, 1], np.int32))  # repeated id: nothing changes
