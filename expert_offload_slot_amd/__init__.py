@@ -61,7 +61,7 @@ class Info(ctypes.Structure):
                 ("ffn_h", ctypes.c_void_p), ("ffn_part", ctypes.c_void_p), ("ffn_groups", ctypes.c_void_p),
                 ("record_bytes", ctypes.c_size_t), ("record_stride", ctypes.c_size_t)] + \
                [(n, ctypes.c_int32) for n in ("E", "S", "H", "F", "k", "dtype", "max_tokens", "device")] + \
-               [("score", ctypes.c_void_p)]
+               [("score", ctypes.c_void_p), ("pinned", ctypes.c_void_p)]
 
 
 class ChainBuffers(ctypes.Structure):
@@ -91,6 +91,7 @@ def lib():
             "moe_rmsnorm": ([vp, vp, i32, i32, i32, ctypes.c_float, vp], i32),
             "moe_prefill_stage": ([vp, vp, i32, vp, P(ctypes.c_int32), vp], i32),
             "moe_prefetch_install": ([vp, vp, i32, i32, vp], i32),
+            "moe_offload_pin": ([vp, vp, i32, vp], i32),
             "moe_copy_prefetch": ([vp, vp], i32),
             "moe_offload_stats": ([vp, P(Stats)], i32),
             "moe_offload_reset": ([vp, vp], i32),
@@ -194,6 +195,10 @@ def moe_prefill_stage(h, ids, T, slot_ids, stream=None):
     out = ctypes.c_int32(-1)
     _check(lib().moe_prefill_stage(h, _addr(ids), T, _addr(slot_ids), ctypes.byref(out), _stream(stream)))
     return out.value
+
+
+def moe_offload_pin(h, experts_dev, n, stream=None):
+    return _check(lib().moe_offload_pin(h, _addr(experts_dev) if n else None, n, _stream(stream)))
 
 
 def moe_prefetch_install(h, pred_ids, T, max_n, stream=None):

@@ -26,6 +26,7 @@ struct CacheDev {
   int32_t* expert_of;   // [S]
   uint64_t* last_use;   // [S]
   uint32_t* score;      // [S] usage score (scored eviction)
+  int32_t* pinned;      // [S] 1: never a victim (profile-guided placement)
   uint64_t* tick;       // [1]
   int32_t* copy_list;   // [2 + 2*max(S,E)]
   int32_t* pf_list;     // [2 + 2*S]
@@ -118,6 +119,7 @@ hipError_t launch_route(moe_offload* h, const void* x, const void* wr, const flo
                         float* w, hipStream_t s);
 hipError_t launch_ensure(moe_offload* h, const int32_t* ids, int n, int32_t* slot_ids, hipStream_t s);
 hipError_t launch_install(moe_offload* h, const int32_t* pred, int T, int max_n, hipStream_t s);
+hipError_t launch_pin(moe_offload* h, const int32_t* experts, int n, hipStream_t s);
 hipError_t launch_copy(moe_offload* h, const int32_t* list, hipStream_t s);
 hipError_t launch_distinct(moe_offload* h, const int32_t* ids, int n, int32_t* out_dev, hipStream_t s);
 hipError_t launch_stage_all(moe_offload* h, const int32_t* ids, int n, int32_t* slot_ids, hipStream_t s);

@@ -32,6 +32,14 @@ __global__ __launch_bounds__(kBlock) void k_install(CacheDev c, const int32_t* _
   install_body(c, t, pred, n, k, max_n, audit, ckey, vkey);
 }
 
+// ---------------------------------------------------------------- profile-guided placement
+__global__ __launch_bounds__(kBlock) void k_pin(CacheDev c, const int32_t* __restrict__ P, int n) {
+  __shared__ SharedTable t;
+  __shared__ uint64_t vkey[kMaxExperts];
+  load_table(c, t);
+  pin_body(c, t, P, n, vkey);
+}
+
 // ---------------------------------------------------------------- prefill helpers
 // distinct ids of a call; -1 if any id is outside [0, E)
 __global__ __launch_bounds__(kBlock) void k_distinct(int E, const int32_t* __restrict__ ids, int n, int32_t* out) {
@@ -80,6 +88,7 @@ __global__ void k_reset(CacheDev c) {
     c.expert_of[s] = -1;
     c.last_use[s] = 0;
     c.score[s] = 0;
+    c.pinned[s] = 0;
   }
   for (int i = i0; i < C_N; i += step) c.counters[i] = 0;
   if (i0 == 0) {
@@ -153,6 +162,11 @@ hipError_t launch_distinct(moe_offload* h, const int32_t* ids, int n, int32_t* o
 
 hipError_t launch_stage_all(moe_offload* h, const int32_t* ids, int n, int32_t* slot_ids, hipStream_t s) {
   launch_k(h, MOE_K_STAGE, k_stage_all, dim3(64), dim3(256), 0, s, h->cache, ids, n, slot_ids);
+  return hipGetLastError();
+}
+
+hipError_t launch_pin(moe_offload* h, const int32_t* experts, int n, hipStream_t s) {
+  launch_k(h, MOE_K_ENSURE, k_pin, dim3(1), dim3(kBlock), 0, s, h->cache, experts, n);
   return hipGetLastError();
 }
 

@@ -184,7 +184,7 @@ int moe_offload_create(const moe_offload_desc* d, moe_offload** out) {
     return o;
   };
   size_t o_slot_of = take(4 * (size_t)h->E), o_expert_of = take(4 * (size_t)h->S), o_last = take(8 * (size_t)h->S);
-  size_t o_score = take(4 * (size_t)h->S);
+  size_t o_score = take(4 * (size_t)h->S), o_pinned = take(4 * (size_t)h->S);
   size_t o_tick = take(8), o_list = take(4 * (2 + 2 * (size_t)maxSE)), o_pf = take(4 * (2 + 2 * (size_t)h->S));
   size_t o_cnt = take(8 * moe::C_N), o_err = take(4), o_logits = take(4 * (size_t)h->max_tokens * h->E);
   size_t o_grp = take(4 * (size_t)h->gl.words());
@@ -197,6 +197,7 @@ int moe_offload_create(const moe_offload_desc* d, moe_offload** out) {
   h->cache.expert_of = (int32_t*)(b + o_expert_of);
   h->cache.last_use = (uint64_t*)(b + o_last);
   h->cache.score = (uint32_t*)(b + o_score);
+  h->cache.pinned = (int32_t*)(b + o_pinned);
   h->cache.scored = (h->flags & MOE_FLAG_SCORED) ? 1 : 0;
   h->cache.tick = (uint64_t*)(b + o_tick);
   h->cache.copy_list = (int32_t*)(b + o_list);
@@ -321,6 +322,16 @@ int moe_prefetch_install(moe_offload* h, const int32_t* pred_ids, int32_t T, int
   return MOE_OK;
 }
 
+int moe_offload_pin(moe_offload* h, const int32_t* experts, int32_t n, void* stream) {
+  if (int rc = check_handle(h)) return rc;
+  if (n < 0 || n > h->S - h->k) return fail(MOE_EINVAL, "moe_offload_pin: n=%d outside [0, S - k = %d]", n, h->S - h->k);
+  if (n > 0 && !experts) return fail(MOE_EINVAL, "moe_offload_pin: null pointer");
+  DeviceGuard g(h->device);
+  HIP_TRY(moe::launch_pin(h, experts, n, (hipStream_t)stream));
+  HIP_TRY(moe::launch_copy(h, h->cache.copy_list, (hipStream_t)stream));
+  return MOE_OK;
+}
+
 int moe_copy_prefetch(moe_offload* h, void* stream) {
   if (int rc = check_handle(h)) return rc;
   DeviceGuard g(h->device);
@@ -413,6 +424,7 @@ int moe_offload_query(const moe_offload* h, moe_info* out) {
   out->expert_of = h->cache.expert_of;
   out->last_use = h->cache.last_use;
   out->score = h->cache.score;
+  out->pinned = h->cache.pinned;
   out->copy_list = h->cache.copy_list;
   out->prefetch_list = h->cache.pf_list;
   out->slots = h->slots;

@@ -26,6 +26,7 @@ struct SharedTable {
   int expert_of[kMaxExperts];
   uint64_t last_use[kMaxExperts];
   uint32_t score[kMaxExperts];
+  int pinned[kMaxExperts];  // 1: never a victim (profile-guided placement)
   int flag[kMaxExperts];   // ensure: expert in D; install: tokens predicting it
   int aux[kMaxExperts];    // ensure: pairs routed to it; install: best top-k position
   int cand[kMaxExperts];   // ensure: best top-k position; install: candidate by rank
@@ -58,6 +59,7 @@ __device__ __forceinline__ void load_table(const CacheDev& c, SharedTable& t) {
     t.expert_of[tid] = e;
     t.last_use[tid] = c.last_use[tid];
     t.score[tid] = c.score[tid];
+    t.pinned[tid] = c.pinned[tid];
   }
   // the call counter and the statistics, from another wavefront
   const int u = tid - 64 * (kWaves - 1);
@@ -72,6 +74,7 @@ __device__ __forceinline__ void store_table(const CacheDev& c, const SharedTable
     c.expert_of[tid] = t.expert_of[tid];
     c.last_use[tid] = t.last_use[tid];
     c.score[tid] = t.score[tid];
+    c.pinned[tid] = t.pinned[tid];
   }
 }
 
@@ -95,10 +98,11 @@ __device__ __forceinline__ void audit_table(const CacheDev& c, const SharedTable
 // memory).  The table must already be in `t` (load_table, then a barrier).
 // Writes the record index of every id to slot_ids (global) and, if given, to
 // slot_lds.  Record index r < S is slot r; r >= S is staging record r - S.
-//   victims:  slots not holding an expert of D, in (free first, then least
-//             recently used, then lowest slot) order;
-//   |D| <= S: misses in ascending id take the victims;
-//   |D| >  S: there are fewer victims than misses; the misses claim them in
+//   victims:  slots not pinned and not holding an expert of D, in (free
+//             first, then least recently used, then lowest slot) order
+//             (scored: least used before least recently used);
+//   misses <= victims: the misses in ascending id take the victims;
+//   misses >  victims (no pins: |D| > S): the misses claim the victims in
 //             install order (pairs routed to it desc, best top-k position asc,
 //             id asc) and the rest are copied to staging record S + e for
 //             this call (mode STAGED);
@@ -143,20 +147,25 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
   const bool miss = f[1];
   int rk[4], tot[4];
   block_rank4(f, t.wave, rk, tot);
-  const int nd = tot[0], mrank = rk[1], nm = tot[1], nh = tot[2], npf = tot[3];
-  const bool over = nd > S;
+  const int mrank = rk[1], nm = tot[1], nh = tot[2], npf = tot[3];
 
-  // eligible victims by rank; for an overflow call also each miss's install-order key
+  // eligible victims by rank: slots not pinned and not holding an expert of D;
+  // the call overflows when the misses outnumber them (no pins: when |D| > S)
+  bool over = false;
   int ns = 0;  // misses that get a slot
   if (nm > 0) {
     bool elig = false;
     if (tid < S) {
       const int ex = t.expert_of[tid];
       const bool occ = ex >= 0;
-      elig = !occ || !t.flag[ex];
+      elig = !t.pinned[tid] && (!occ || !t.flag[ex]);
       vkey[tid] = elig ? victim_key(c, occ, t.score[tid], t.last_use[tid], tid) : ~0ull;
     }
-    if (over) {  // pairs routed to each expert and its best top-k position
+    int nv;
+    (void)block_rank(elig, t.wave, &nv);  // its barriers also publish vkey
+    ns = nm < nv ? nm : nv;
+    over = nm > nv;  // block-uniform
+    if (over) {  // install-order key of each miss: pairs routed to it, best top-k position, id
       if (tid < E) {
         t.aux[tid] = 0;
         t.cand[tid] = k;
@@ -167,14 +176,12 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
         atomicAdd(&t.aux[e], 1);
         atomicMin(&t.cand[e], i % k);
       }
+      __syncthreads();
+      if (tid < E)
+        ckey[tid] = miss ? ((uint64_t)(0xfffffu - (uint32_t)t.aux[tid]) << 40) | ((uint64_t)t.cand[tid] << 20) |
+                               (uint64_t)tid
+                         : ~0ull;
     }
-    int nv;
-    (void)block_rank(elig, t.wave, &nv);  // its barriers also publish vkey and the counts
-    ns = nm < nv ? nm : nv;
-    if (over && tid < E)
-      ckey[tid] = miss ? ((uint64_t)(0xfffffu - (uint32_t)t.aux[tid]) << 40) | ((uint64_t)t.cand[tid] << 20) |
-                             (uint64_t)tid
-                       : ~0ull;
     if (elig) {
       const uint64_t mine = vkey[tid];
       int rank = 0;
@@ -284,7 +291,7 @@ __device__ __forceinline__ void install_body(const CacheDev& c, SharedTable& t, 
   if (tid < S) {
     const int ex = t.expert_of[tid];
     const bool occ = ex >= 0;
-    elig = !occ || t.flag[ex] == 0;
+    elig = !t.pinned[tid] && (!occ || t.flag[ex] == 0);
     vkey[tid] = elig ? victim_key(c, occ, t.score[tid], t.last_use[tid], tid) : ~0ull;
   }
   int nc, nv;
@@ -326,6 +333,78 @@ __device__ __forceinline__ void install_body(const CacheDev& c, SharedTable& t, 
     c.pf_list[1] = m;
     c.counters[C_PF_INSTALLS] = t.cnt[C_PF_INSTALLS] + (uint64_t)m;
     c.counters[C_BYTES] = t.cnt[C_BYTES] + (uint64_t)m * c.record_bytes;
+  }
+}
+
+// Profile-guided placement: pin the n distinct experts of P (device ids,
+// replacing the pinned set).  Members already resident are pinned in place;
+// the others, ascending id, take victims in the ensure order among slots not
+// pinned and not holding a member, with last_use = the current tick (the clock
+// does not advance) and score 0.  The copy list gets {SLOTS, loads, (expert,
+// slot)...}.  An id out of range or repeated: nothing changes, empty list,
+// error bit.  keys: LDS scratch of kMaxExperts entries.
+__device__ __forceinline__ void pin_body(const CacheDev& c, SharedTable& t, const int32_t* P, int n,
+                                         uint64_t* vkey) {
+  const int tid = threadIdx.x;
+  const int E = c.E, S = c.S;
+  if (tid < E) t.flag[tid] = 0;
+  if (tid == 0) t.bad = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += kBlock) {
+    const int e = P[i];
+    if ((unsigned)e >= (unsigned)E || atomicAdd(&t.flag[e], 1) != 0) t.bad = 1;
+  }
+  __syncthreads();
+  if (t.bad) {
+    if (tid == 0) {
+      atomicOr(c.err, MOE_DEV_ERR_BAD_ID);
+      c.copy_list[0] = MOE_MODE_SLOTS;
+      c.copy_list[1] = 0;
+    }
+    return;  // block-uniform
+  }
+  if (tid < S) t.pinned[tid] = 0;
+  __syncthreads();
+  if (tid < E && t.flag[tid] && t.slot_of[tid] >= 0) t.pinned[t.slot_of[tid]] = 1;
+  __syncthreads();
+  const bool miss = tid < E && t.flag[tid] && t.slot_of[tid] < 0;
+  bool elig = false;
+  if (tid < S) {
+    const int ex = t.expert_of[tid];
+    const bool occ = ex >= 0;
+    elig = !t.pinned[tid] && (!occ || !t.flag[ex]);
+    vkey[tid] = elig ? victim_key(c, occ, t.score[tid], t.last_use[tid], tid) : ~0ull;
+  }
+  int nm, nv;
+  const int mrank = block_rank(miss, t.wave, &nm);  // its barriers also publish vkey
+  (void)block_rank(elig, t.wave, &nv);
+  const int nl = nm < nv ? nm : nv;  // nm <= nv for n <= S
+  if (elig) {
+    const uint64_t mine = vkey[tid];
+    int rank = 0;
+#pragma unroll 8
+    for (int s2 = 0; s2 < S; ++s2) rank += vkey[s2] < mine ? 1 : 0;
+    t.vic[rank] = tid;
+  }
+  __syncthreads();
+  if (miss && mrank < nl) {
+    const int v = t.vic[mrank];
+    const int old = t.expert_of[v];
+    if (old >= 0) t.slot_of[old] = -1;
+    t.expert_of[v] = tid;
+    t.slot_of[tid] = v;
+    t.last_use[v] = t.tick;
+    t.score[v] = 0;
+    t.pinned[v] = 1;
+    c.copy_list[2 + 2 * mrank] = tid;
+    c.copy_list[3 + 2 * mrank] = v;
+  }
+  __syncthreads();
+  store_table(c, t);
+  if (tid == 0) {
+    c.copy_list[0] = MOE_MODE_SLOTS;
+    c.copy_list[1] = nl;
+    c.counters[C_BYTES] = t.cnt[C_BYTES] + (uint64_t)nl * c.record_bytes;
   }
 }
 

@@ -165,6 +165,7 @@ typedef struct {
   int32_t E, S, H, F, k, dtype, max_tokens, device;
   uint32_t* score;        /* [S]  usage score: ensure calls routed to the slot's expert since it was loaded
                              (saturating at 2^20 - 1); kept under both policies, used by MOE_FLAG_SCORED */
+  int32_t* pinned;        /* [S]  1: the slot's expert is pinned (moe_offload_pin), never a victim */
 } moe_info;
 
 /* copy-list modes (copy_list[0]) */
@@ -266,6 +267,20 @@ int moe_prefetch_install(moe_offload* h, const int32_t* pred_ids, int32_t T, int
 /* Copy the prefetch copy list's records (may run on a side stream after an
  * event that follows the install; the demand copy of this layer must wait
  * for it). */
+/* Profile-guided placement (npu-offload README, PolyStrata placement: a hot
+ * set from a routing profile, here mixed with the dynamic cache): make the n
+ * distinct experts experts_dev[0..n) resident and pinned, replacing any
+ * earlier pinned set.  Pinned slots are never victims of ensure or install
+ * and are used like any other slot.  Members already resident are pinned in
+ * place; the others (ascending id) take victims in the ensure order among
+ * slots not pinned and not holding a member, with last_use = the current
+ * tick and score 0, and are copied in (the copy list is reused).  With pins,
+ * an ensure call overflows when its misses outnumber the unpinned victims.
+ *   experts_dev: device int32 [n];  0 <= n <= S - k (else MOE_EINVAL).
+ * An id out of range or repeated: nothing changes, the sticky bad-id bit is
+ * set.  Asynchronous; a slot-table writer: issue it on the compute stream. */
+int moe_offload_pin(moe_offload* h, const int32_t* experts_dev, int32_t n, void* stream);
+
 int moe_copy_prefetch(moe_offload* h, void* stream);
 
 /* Synchronise the device and read the counters and the sticky error word. */

@@ -138,6 +138,9 @@ class GpuLayer:
     def scores(self):
         return d2h(self.info["score"], 4 * self.S, np.uint32)
 
+    def pinned(self):
+        return d2h(self.info["pinned"], 4 * self.S, np.int32)
+
     def stats(self):
         return m.moe_offload_stats(self.h)
 
@@ -171,6 +174,7 @@ def compare_call(gl, ol_step, T, y64=None, check_table=True, oracle_cache=None):
         oso, oeo, olu, _ = oracle_cache.state()
         assert np.array_equal(so, oso) and np.array_equal(eo, oeo) and np.array_equal(lu, olu)
         assert np.array_equal(gl.scores(), oracle_cache.scores())
+        assert np.array_equal(gl.pinned(), oracle_cache.pinned())
     if y64 is not None:
         err = row_rel_err(to_np(gl.y[:T]), y64, gl.wdt)
         assert err <= TOL[gl.wdt], err

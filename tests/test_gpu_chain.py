@@ -218,3 +218,26 @@ def test_chain_scored_eviction(prefetch_n, T):
         assert all(m.moe_offload_stats(h)["error"] == 0 for h in cg.handles)
     finally:
         cg.close()
+
+
+def test_chain_with_pinned_experts():
+    """Each layer pins its own hot set before the decode chain runs (eager pin calls between graph replays)."""
+    L, E, S, k, H, F, T = 3, 32, 8, 4, 256, 256, 1
+    cg = ChainModel(L, E, S, k, H, F, 1, T, 89, 2)
+    caches = [oracle.Cache(E, S, cg.hosts[l], oracle.record_bytes(1, H, F)) for l in range(L)]
+    try:
+        for l in range(L):
+            P = np.array([(3 * l + j) % E for j in range(3)], np.int32)
+            m.moe_offload_pin(cg.handles[l], to_dev(P), len(P), torch.cuda.current_stream())
+            caches[l].copy(0, caches[l].pin(P))
+        torch.cuda.synchronize()
+        for s in range(10):
+            cg.run(s, graph=True)
+            oracle_replay_step(cg, caches, cg.snapshot(), 2)
+        for l in range(L):
+            so, eo, lu, sc = cg.lists(l)[2]
+            pinned = d2h(cg.info[l]["pinned"], 4 * S, np.int32)
+            assert np.array_equal(pinned, caches[l].pinned()) and pinned.sum() == 3
+        assert all(m.moe_offload_stats(h)["error"] == 0 for h in cg.handles)
+    finally:
+        cg.close()

@@ -19,7 +19,7 @@ from gpu_harness import (GpuLayer, compare_call, d2h, h2d, make_layer_inputs, ro
 pytestmark = pytest.mark.gpu
 
 
-def run_sequence(E, S, k, H, F, wdt, zipf, seed, steps, Ts, shared=False, flags=m.FLAG_AUDIT):
+def run_sequence(E, S, k, H, F, wdt, zipf, seed, steps, Ts, shared=False, flags=m.FLAG_AUDIT, pins=None):
     print("case E=%d S=%d k=%d H=%d F=%d wdt=%d zipf=%s seed=%d Ts=%s shared=%s" %
           (E, S, k, H, F, wdt, zipf, seed, Ts, shared), flush=True)
     host, wr, b, sh = make_layer_inputs(seed, 0, E, H, F, wdt, zipf, shared)
@@ -31,6 +31,14 @@ def run_sequence(E, S, k, H, F, wdt, zipf, seed, steps, Ts, shared=False, flags=
     modes, errs = [], []
     try:
         for s in range(steps):
+            if pins and s in pins:  # a new pinned set before this step, on both sides
+                P = np.array(pins[s], np.int32)
+                m.moe_offload_pin(gl.h, to_dev(P) if len(P) else None, len(P), torch.cuda.current_stream())
+                want = ol.cache.pin(P)
+                ol.cache.copy(0, want)
+                mode, got = gl.copy_list()
+                assert mode == 0 and np.array_equal(got, want), (s, got, want)
+                assert np.array_equal(gl.pinned(), ol.cache.pinned()), s
             T = Ts[s % len(Ts)]
             x = np.ascontiguousarray(xs[s][:T])
             xd = to_dev(x)
@@ -137,6 +145,16 @@ def test_scored_eviction_parity(E, S, k, Ts):
     # scored eviction: slot tables, usage scores, copy lists and counters bit-exact against the oracle,
     # with Zipf routing (repeat customers) and batches that overflow the cache
     run_sequence(E, S, k, 256, 256, 1, 1.2, 70 + E, 30, Ts, flags=m.FLAG_AUDIT | m.FLAG_SCORED)
+
+
+@pytest.mark.parametrize("flags", [m.FLAG_AUDIT, m.FLAG_AUDIT | m.FLAG_SCORED])
+def test_pinned_placement_parity(flags):
+    # pinned sets replaced mid-stream (overlapping, then empty); with 3 of 6 slots pinned a batch of 3
+    # overflows although |D| <= S
+    # (flat routing: 5-6 distinct experts per 3-token call against 3 unpinned slots)
+    pins = {0: [1, 4, 9], 12: [4, 2], 24: []}
+    modes, _ = run_sequence(16, 6, 2, 256, 256, 1, 0.0, 90, 32, [1, 2, 3], flags=flags, pins=pins)
+    assert 1 in modes and 0 in modes
 
 
 def test_fp8_without_shared_expert():
