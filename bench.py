@@ -312,7 +312,7 @@ def main():
                                      "staged_copies_per_token": round(d["staged_copies"] / (T * steps), 4)}
             m.moe_chain_destroy(c2)
         result["prefetch"] = prefetch_compare(args, m, hip, handles, run_decode, token_stream)
-        result["eviction"] = eviction_compare(args, m, hip, handles, run_decode, token_stream)
+        result["eviction"] = eviction_compare(args, m, hip, torch, handles, wr_d, b_d, run_decode, token_stream)
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args, handles, routers, stride, T0)
@@ -577,9 +577,35 @@ def prefetch_compare(args, m, hip, handles, run_decode, token_stream):
     return out
 
 
-def eviction_compare(args, m, hip, handles, run_decode, token_stream):
-    """LRU against scored eviction (least used first, then LRU), each from an empty cache on the same token
-    stream; the scored layers share the LRU layers' host stores.  Outputs must be bitwise identical."""
+def routing_profile(args, m, hip, torch, handles, wr_d, b_d, T, steps):
+    """Expert counts per layer over `steps` decode steps of a separate profiling token stream."""
+    import numpy as np
+    import synth
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    xs = synth.tokens(args.seed, 900 + T, T, H, steps, 0.9, synth.BF16)
+    xs_d = torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16).to(dev)
+    c = m.moe_chain_create(handles, wr_d, b_d, T, 0)
+    bufs = m.moe_chain_get_buffers(c)
+    L = len(handles)
+    ids = np.empty((L, T, K_TOP), dtype=np.int32)
+    cnt = np.zeros((L, E), dtype=np.int64)
+    for s in range(steps):
+        assert hip.hipMemcpyAsync(bufs["x"], xs_d[s].data_ptr(), T * H * 2, 3, stream.cuda_stream) == 0
+        m.moe_chain_run(c, stream)
+        torch.cuda.synchronize()
+        assert hip.hipMemcpy(ids.ctypes.data, bufs["ids"], ids.nbytes, 2) == 0
+        for l in range(L):
+            cnt[l] += np.bincount(ids[l].reshape(-1), minlength=E)
+    m.moe_chain_destroy(c)
+    return cnt
+
+
+def eviction_compare(args, m, hip, torch, handles, wr_d, b_d, run_decode, token_stream):
+    """LRU against scored eviction (least used first, then LRU) and against profile-guided placement (each
+    layer's SLOTS // 2 most routed experts of a separate profiling stream pinned, LRU for the rest), each from
+    an empty cache on the same token stream; the scored layers share the LRU layers' host stores.  Outputs
+    must be bitwise identical."""
     import numpy as np
     T, warm, steps = 1, 16, 128
     xs_d = token_stream(T, warm + steps + args.prof_steps)
@@ -587,9 +613,17 @@ def eviction_compare(args, m, hip, handles, run_decode, token_stream):
               for h in handles]
     out, last = {}, {}
     try:
-        for name, hs in (("lru", handles), ("scored", scored)):
+        for name, hs in (("lru", handles), ("scored", scored), ("pinned", handles)):
             for h in hs:
                 m.moe_offload_reset(h)
+            if name == "pinned":
+                cnt = routing_profile(args, m, hip, torch, handles, wr_d, b_d, T, 64)
+                for h in hs:
+                    m.moe_offload_reset(h)
+                for l, h in enumerate(hs):
+                    hot = np.argsort(-cnt[l], kind="stable")[:SLOTS // 2].astype(np.int32)
+                    m.moe_offload_pin(h, torch.from_numpy(hot).to("cuda"), len(hot), torch.cuda.current_stream())
+                torch.cuda.synchronize()
             ts, msps, d, c, bufs, _ = run_decode(T, warm, steps, "eviction-" + name, xs_d=xs_d, hs=hs)
             xl = np.empty((T, H), dtype=np.uint16)
             assert hip.hipMemcpy(xl.ctypes.data, bufs["x"] + len(hs) * T * H * 2, xl.nbytes, 2) == 0
@@ -600,7 +634,12 @@ def eviction_compare(args, m, hip, handles, run_decode, token_stream):
     finally:
         for h in reversed(scored):
             m.moe_offload_destroy(h)
-    out["outputs_identical"] = bool(np.array_equal(last["lru"], last["scored"]))
+    for h in handles:  # unpin: the default layers go back to plain LRU
+        m.moe_offload_pin(h, None, 0, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    out["pinned"]["pinned_per_layer"] = SLOTS // 2
+    out["outputs_identical"] = bool(np.array_equal(last["lru"], last["scored"]) and
+                                    np.array_equal(last["lru"], last["pinned"]))
     return out
 
 
