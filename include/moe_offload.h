@@ -309,9 +309,9 @@ enum moe_kernel_kind {
   MOE_K_LOGITS = 0,   /* router logits */
   MOE_K_TOPK = 1,     /* top-k + weights (moe_route_topk) */
   MOE_K_DECIDE = 2,   /* fused decode control: top-k + ensure + grouping (chain) */
-  MOE_K_ENSURE = 3,   /* moe_slot_ensure */
+  MOE_K_ENSURE = 3,   /* moe_slot_ensure, moe_offload_pin */
   MOE_K_INSTALL = 4,  /* moe_prefetch_install */
-  MOE_K_COPY = 5,     /* demand / staging copy (moe_copy_misses, prefill) */
+  MOE_K_COPY = 5,     /* demand / staging / pin copy (moe_copy_misses, prefill, moe_offload_pin) */
   MOE_K_PF_COPY = 6,  /* prefetch copy (moe_copy_prefetch) */
   MOE_K_GROUP = 7,    /* FFN grouping by record */
   MOE_K_GATEUP = 8,   /* FFN gate/up + SiLU */
