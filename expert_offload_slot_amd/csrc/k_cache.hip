@@ -1,6 +1,7 @@
 // Per-layer LRU slot table on the GPU: ensure (lookup, victims, id rewrite,
-// copy list, counters), prefetch install, whole-layer staging, reset, and the
-// copy kernel that moves records from device-mapped pinned host memory.
+// copy list, counters), prefetch install, the pinned set, whole-layer
+// staging, reset, and the copy kernel that moves records from device-mapped
+// pinned host memory.
 //
 // xinfer-ai 0.14.6 docs/moe_offload.md, "How it works" (Decode, Prefill);
 // FreeToken issue #677, "Proposal" (Install, Correctness constraint).

@@ -1,8 +1,12 @@
-// The per-layer LRU slot table as one workgroup sees it, and the ensure step.
+// The per-layer LRU slot table as one workgroup sees it: the ensure step, the
+// prefetch install and the pinned set.
 //
 // xinfer-ai 0.14.6 docs/moe_offload.md, "How it works" (Decode): look up the
 // experts a call needs, pick least-recently-used slots for the misses, rewrite
 // expert ids to slot ids and leave the miss list and count in device memory.
+// FreeToken issue #677 ("Proposal", "Measured"): installs at usage 0, and the
+// scored-eviction baseline (victims by usage score first).  npu-offload README
+// (PolyStrata placement): a pinned hot set, never evicted.
 // The table is only ever written by one workgroup of one kernel at a time, on
 // the caller's compute stream: no atomics on shared state, no races.
 #pragma once
