@@ -245,6 +245,35 @@ def test_bad_id_is_a_noop_with_sticky_error():
         gl.close()
 
 
+def test_pin_rejects_bad_sets():
+    E, S, k, H, F = 8, 4, 2, 128, 128
+    host, wr, b, _ = make_layer_inputs(62, 0, E, H, F, 1, 1.2)
+    gl = GpuLayer(E, S, k, H, F, 1, 4, host, wr, b)
+    try:
+        with pytest.raises(m.MoeError) as ei:  # more than S - k pinned experts
+            m.moe_offload_pin(gl.h, to_dev(np.array([0, 1, 2], np.int32)), 3)
+        assert ei.value.code == m.EINVAL
+        m.moe_offload_pin(gl.h, to_dev(np.array([5, 1], np.int32)), 2)
+        torch.cuda.synchronize()
+        before = gl.table() + (gl.pinned(),)
+        assert gl.pinned().sum() == 2
+        for bad in ([3, 3], [2, E]):  # repeated or out of range: nothing changes, sticky bad-id bit
+            m.moe_offload_pin(gl.h, to_dev(np.array(bad, np.int32)), 2)
+            torch.cuda.synchronize()
+            after = gl.table() + (gl.pinned(),)
+            assert all(np.array_equal(p, q) for p, q in zip(before, after))
+            assert gl.stats()["error"] & m.DEV_ERR_BAD_ID
+            m.moe_offload_reset(gl.h)
+            m.moe_offload_pin(gl.h, to_dev(np.array([5, 1], np.int32)), 2)
+            torch.cuda.synchronize()
+            before = gl.table() + (gl.pinned(),)
+        m.moe_offload_pin(gl.h, None, 0)  # the empty set unpins everything
+        torch.cuda.synchronize()
+        assert gl.pinned().sum() == 0 and gl.stats()["error"] == 0
+    finally:
+        gl.close()
+
+
 def test_nan_logit_sets_error():
     E, S, k, H, F = 8, 4, 2, 128, 128
     host, wr, b, _ = make_layer_inputs(62, 0, E, H, F, 1, 1.2)
