@@ -82,6 +82,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--extra", action="store_true", help="also batch 8/32 and the lookahead-prefetch comparison")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--mxfp4-only", action="store_true",
+                    help="only the same decode chain with MXFP4 expert records (prints its own JSON line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
@@ -105,6 +107,16 @@ def main():
     hip.hipMemcpy.restype = ctypes.c_int
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    if args.mxfp4_only:
+        routers = [synth.router(args.seed, l, E, H, synth.BF16, zipf_s=1.2) for l in range(L)]
+        wr_d = [torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to(dev) for w, _ in routers]
+        b_d = [torch.from_numpy(b).to(dev) for _, b in routers]
+        out = qwen3_mxfp4(args, m, torch, hip, wr_d, b_d)
+        print(json.dumps({"workload": "qwen3-30b-a3b-shaped offloaded MoE decode, MXFP4 expert records: %d layers x "
+                                      "128 experts, top-8, hidden 2048, moe ffn 768, 26 slots/layer, batch 1, "
+                                      "HIP-graph step" % L, "qwen3_mxfp4": out}), flush=True)
+        return
 
     # ---------------- layers: pinned host stores, slots, routers
     t0 = time.time()
