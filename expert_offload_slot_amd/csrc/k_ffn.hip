@@ -214,19 +214,24 @@ __device__ __forceinline__ void widen16_fp4(uint2 q, float s, uint4& lo, uint4& 
 
 // ------------------------------------------------------------------ prefill GEMMs (bf16, fp8, MXFP4)
 // Many tokens per record: a call becomes a grouped GEMM over record tiles.
-// Work item = (tile of kGemmTok pairs of one record, kGemmRows weight rows);
+// Work item = (tile of kGemmTok pairs of one record, R weight rows: 64 for gate/up,
+// 128 for down);
 // the items of a call follow the tile starts of the group descriptor (routed
 // records, then the shared expert's ceil(T / kGemmTok) tiles).  A 256-thread
 // workgroup stages kGemmK-wide K slices of its weight rows and of its gathered
 // token rows through LDS with coalesced loads (fp8 and MXFP4 codes widened
 // exactly to bf16 on the way in), loads the next slice into registers while
-// the current one feeds bf16 MFMA 16x16x32 tiles, and each wavefront owns a
-// 32 x 32 corner of the 64 x 64 output tile.  fp8: one scale per 128 x 128
+// the current one feeds bf16 MFMA 16x16x32 tiles, and each wavefront owns an
+// (R/2) x 32 corner of the R x 64 output tile.  Down holds one weight matrix,
+// so it takes taller tiles (fewer loaded bytes per FLOP); gate/up holds two and
+// keeps 64 rows, which keeps its LDS and registers for more resident waves.
+// fp8: one scale per 128 x 128
 // block, so one per K slice and matrix, multiplies the slice's partial sum.
 // MFMA operands: lane l supplies row (l & 15) and the 8 K values at
 // 8 * (l >> 4) of a 32-wide K step, for A (weight rows) and B (tokens) alike;
 // the result holds rows 4 * (l >> 4) + i and token column (l & 15).
-constexpr int kGemmRows = 64;         // weight rows per tile
+constexpr int kGemmRowsGu = 64;       // weight rows per gate/up tile (two matrices)
+constexpr int kGemmRowsDn = 128;      // weight rows per down tile (one matrix)
 constexpr int kGemmK = 64;            // K per LDS slice
 constexpr int kLdsRow = kGemmK + 8;   // LDS row stride in bf16: rows start on different banks
 
@@ -264,15 +269,16 @@ __device__ __forceinline__ int gemm_tiles(const FfnArgs& a, int nr, int* routed)
   return *routed + (a.shared ? (a.T + kGemmTok - 1) / kGemmTok : 0);
 }
 
-// one K slice of NM weight matrices (kGemmRows rows each, row stride K weights)
-// and of the tile's token rows, from memory into registers.
-//   bf16:  2 x 16 bytes per matrix (rows tid/8 and tid/8 + 32, 8 weights each);
-//   fp8:   16 codes of row tid/4;  MXFP4: 16 codes of row tid/4 and their scale.
-template <int W, int NM>
+// one K slice of NM weight matrices (R rows each, row stride K weights) and of
+// the tile's token rows, from memory into registers.
+//   bf16:  R/32 x 16 bytes per matrix (rows tid/8 + 32q, 8 weights each);
+//   fp8:   16 codes of rows tid/4 + 64q;  MXFP4: 16 codes of rows tid/4 + 64q
+//          and their scales.
+template <int W, int NM, int R>
 struct Slice {
-  static constexpr int NA = W == kBf16 ? 2 : 1;
+  static constexpr int NA = W == kBf16 ? R / 32 : R / 64;
   uint4 a[NA * NM];  // MXFP4 uses .x, .y
-  float s[NM];
+  float s[NA * NM];
   uint4 b[2];        // token rows tid/8 and tid/8 + 32
 
   // w0: row 0 of the tile in matrix 0, matrices mat bytes apart; sr0: for
@@ -282,40 +288,44 @@ struct Slice {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      if (W == kBf16) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-          a[2 * m + q] = *reinterpret_cast<const uint4*>(
+      for (int q = 0; q < NA; ++q) {
+        if (W == kBf16) {
+          a[NA * m + q] = *reinterpret_cast<const uint4*>(
               w0 + m * mat + ((uint64_t)((tid >> 3) + 32 * q) * K + k0 + (tid & 7) * 8) * 2);
-      } else if (W == kFp8) {
-        a[m] = *reinterpret_cast<const uint4*>(w0 + m * mat + (uint64_t)(tid >> 2) * K + k0 + (tid & 3) * 16);
-      } else {
-        const uint2 v = *reinterpret_cast<const uint2*>(w0 + m * mat + ((uint64_t)(tid >> 2) * K + k0) / 2 +
-                                                        (tid & 3) * 8);
-        a[m].x = v.x;
-        a[m].y = v.y;
-        s[m] = e8m0_scale(sr0[m * sstride + (uint64_t)(tid >> 2) * (K / 32) + (k0 + (tid & 3) * 16) / 32]);
+        } else if (W == kFp8) {
+          a[NA * m + q] = *reinterpret_cast<const uint4*>(w0 + m * mat + (uint64_t)((tid >> 2) + 64 * q) * K + k0 +
+                                                           (tid & 3) * 16);
+        } else {
+          const int row = (tid >> 2) + 64 * q;
+          const uint2 v =
+              *reinterpret_cast<const uint2*>(w0 + m * mat + ((uint64_t)row * K + k0) / 2 + (tid & 3) * 8);
+          a[NA * m + q].x = v.x;
+          a[NA * m + q].y = v.y;
+          s[NA * m + q] = e8m0_scale(sr0[m * sstride + (uint64_t)row * (K / 32) + (k0 + (tid & 3) * 16) / 32]);
+        }
       }
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) b[q] = bp[q] ? *reinterpret_cast<const uint4*>(bp[q] + k0) : make_uint4(0, 0, 0, 0);
   }
 
-  __device__ __forceinline__ void store(uint16_t (*As)[kGemmRows][kLdsRow], uint16_t (*Bs)[kLdsRow]) const {
+  __device__ __forceinline__ void store(uint16_t (*As)[R][kLdsRow], uint16_t (*Bs)[kLdsRow]) const {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      if (W == kBf16) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-          *reinterpret_cast<uint4*>(&As[m][(tid >> 3) + 32 * q][(tid & 7) * 8]) = a[2 * m + q];
-      } else {
-        uint4 lo, hi;
-        if (W == kFp8) widen16(a[m], lo, hi);
-        else widen16_fp4(make_uint2(a[m].x, a[m].y), s[m], lo, hi);
-        uint4* d = reinterpret_cast<uint4*>(&As[m][tid >> 2][(tid & 3) * 16]);
-        d[0] = lo;
-        d[1] = hi;
+      for (int q = 0; q < NA; ++q) {
+        if (W == kBf16) {
+          *reinterpret_cast<uint4*>(&As[m][(tid >> 3) + 32 * q][(tid & 7) * 8]) = a[NA * m + q];
+        } else {
+          uint4 lo, hi;
+          if (W == kFp8) widen16(a[NA * m + q], lo, hi);
+          else widen16_fp4(make_uint2(a[NA * m + q].x, a[NA * m + q].y), s[NA * m + q], lo, hi);
+          uint4* d = reinterpret_cast<uint4*>(&As[m][(tid >> 2) + 64 * q][(tid & 3) * 16]);
+          d[0] = lo;
+          d[1] = hi;
+        }
       }
     }
 #pragma unroll
@@ -323,18 +333,19 @@ struct Slice {
   }
 };
 
-// acc[m][i][j] += the wavefront's 32 x 32 corner (row tiles i, token tiles j) of
-// matrix m over the LDS slice; SC (fp8): the slice's sum is scaled by sc[m] first
-template <bool SC, int NM>
-__device__ __forceinline__ void gemm_slice(const uint16_t (*As)[kGemmRows][kLdsRow], const uint16_t (*Bs)[kLdsRow],
-                                           const float* sc, f32x4 acc[NM][2][2]) {
+// acc[m][i][j] += the wavefront's (R/2) x 32 corner (row tiles i, token tiles j)
+// of matrix m over the LDS slice; SC (fp8): the slice's sum is scaled by sc[m] first
+template <bool SC, int NM, int R>
+__device__ __forceinline__ void gemm_slice(const uint16_t (*As)[R][kLdsRow], const uint16_t (*Bs)[kLdsRow],
+                                           const float* sc, f32x4 acc[NM][R / 32][2]) {
+  constexpr int RI = R / 32;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int r0 = 32 * (wv >> 1) + (lane & 15), c0 = 32 * (wv & 1) + (lane & 15), kq = 8 * (lane >> 4);
-  f32x4 part[NM][2][2];
+  const int r0 = (R / 2) * (wv >> 1) + (lane & 15), c0 = 32 * (wv & 1) + (lane & 15), kq = 8 * (lane >> 4);
+  f32x4 part[NM][RI][2];
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < RI; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) part[m][i][j] = SC ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[m][i][j];
 #pragma unroll
@@ -345,7 +356,7 @@ __device__ __forceinline__ void gemm_slice(const uint16_t (*As)[kGemmRows][kLdsR
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < RI; ++i) {
         const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[m][r0 + 16 * i][ks + kq]);
 #pragma unroll
         for (int j = 0; j < 2; ++j) part[m][i][j] = mfma(af, bf[j], part[m][i][j]);
@@ -354,21 +365,21 @@ __device__ __forceinline__ void gemm_slice(const uint16_t (*As)[kGemmRows][kLdsR
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < RI; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[m][i][j] = SC ? fma4(sc[m], part[m][i][j], acc[m][i][j]) : part[m][i][j];
 }
 
 // gate/up: C[f][p] = W[f] . x[token(p)] for gate and up, h = silu(gate) * up in bf16
-template <int W>
+template <int W, int R = kGemmRowsGu>
 __global__ __launch_bounds__(256) void k_gemm_gu(FfnArgs a) {
-  __shared__ uint16_t As[2][kGemmRows][kLdsRow];
+  __shared__ uint16_t As[2][R][kLdsRow];
   __shared__ uint16_t Bs[kGemmTok][kLdsRow];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nr = a.grp[0];
   int routed;
   const int ntiles = gemm_tiles(a, nr, &routed);
-  const int H = a.H, F = a.F, RT = F / kGemmRows, nk = H / kGemmK;
+  const int H = a.H, F = a.F, RT = F / R, nk = H / kGemmK;
   const uint64_t mat = code_bytes<W>((uint64_t)F * H);
   const uint64_t sstride = (uint64_t)F * H / 32;  // MXFP4 scale bytes per matrix
   const int nsc = (F / 128) * (H / 128);
@@ -376,7 +387,7 @@ __global__ __launch_bounds__(256) void k_gemm_gu(FfnArgs a) {
   uint16_t* __restrict__ hb = (uint16_t*)a.hbuf;
   for (int item = blockIdx.x; item < ntiles * RT; item += gridDim.x) {
     const GemmItem g = gemm_item(a, nr, routed, RT, item);
-    const int m0 = g.rt * kGemmRows, n_here = min(kGemmTok, g.it.n - g.n0);
+    const int m0 = g.rt * R, n_here = min(kGemmTok, g.it.n - g.n0);
     const uint16_t* bp[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -387,14 +398,14 @@ __global__ __launch_bounds__(256) void k_gemm_gu(FfnArgs a) {
     const uint8_t* w0 = g.it.rec + code_bytes<W>((uint64_t)m0 * H);
     const uint8_t* sr0 = scale_row<W>(g.it.rec, mat, F, H, 0, m0, H);
     const float* sc = reinterpret_cast<const float*>(sr0);  // fp8: this row block's scales of gate
-    f32x4 acc[2][2][2];
+    f32x4 acc[2][R / 32][2];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < R / 32; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    Slice<W, 2> sl;
+    Slice<W, 2, R> sl;
     sl.load(w0, mat, sr0, sstride, H, 0, bp);
     for (int kb = 0; kb < nk; ++kb) {
       __syncthreads();  // the previous slice (or item) is no longer read
@@ -403,7 +414,7 @@ __global__ __launch_bounds__(256) void k_gemm_gu(FfnArgs a) {
       if (kb + 1 < nk) sl.load(w0, mat, sr0, sstride, H, (kb + 1) * kGemmK, bp);
       const float s2[2] = {W == kFp8 ? sc[(kb * kGemmK) / 128] : 1.f,
                            W == kFp8 ? sc[nsc + (kb * kGemmK) / 128] : 1.f};
-      gemm_slice<W == kFp8, 2>(As, Bs, s2, acc);
+      gemm_slice<W == kFp8, 2, R>(As, Bs, s2, acc);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -411,8 +422,8 @@ __global__ __launch_bounds__(256) void k_gemm_gu(FfnArgs a) {
       if (idx < n_here) {
         const int p = item_pair(a, g.it, g.r, g.n0 + idx);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int f = m0 + 32 * (wv >> 1) + 16 * i + 4 * (lane >> 4);
+        for (int i = 0; i < R / 32; ++i) {
+          const int f = m0 + (R / 2) * (wv >> 1) + 16 * i + 4 * (lane >> 4);
           uint16_t hv[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) hv[e] = f32_to_bf16(silu_mul(acc[0][i][j][e], acc[1][i][j][e]));
@@ -427,21 +438,21 @@ __global__ __launch_bounds__(256) void k_gemm_gu(FfnArgs a) {
 }
 
 // down: part[p][r] = Wd[r] . h[p] (fp32 partial outputs)
-template <int W>
+template <int W, int R = kGemmRowsDn>
 __global__ __launch_bounds__(256) void k_gemm_dn(FfnArgs a) {
-  __shared__ uint16_t As[1][kGemmRows][kLdsRow];
+  __shared__ uint16_t As[1][R][kLdsRow];
   __shared__ uint16_t Bs[kGemmTok][kLdsRow];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nr = a.grp[0];
   int routed;
   const int ntiles = gemm_tiles(a, nr, &routed);
-  const int H = a.H, F = a.F, RT = H / kGemmRows, nk = F / kGemmK;
+  const int H = a.H, F = a.F, RT = H / R, nk = F / kGemmK;
   const uint64_t mat = code_bytes<W>((uint64_t)F * H);
   const uint16_t* __restrict__ hb = (const uint16_t*)a.hbuf;
   float* __restrict__ part = a.part;
   for (int item = blockIdx.x; item < ntiles * RT; item += gridDim.x) {
     const GemmItem g = gemm_item(a, nr, routed, RT, item);
-    const int m0 = g.rt * kGemmRows, n_here = min(kGemmTok, g.it.n - g.n0);
+    const int m0 = g.rt * R, n_here = min(kGemmTok, g.it.n - g.n0);
     const uint16_t* bp[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -451,12 +462,12 @@ __global__ __launch_bounds__(256) void k_gemm_dn(FfnArgs a) {
     const uint8_t* w0 = g.it.rec + 2 * mat + code_bytes<W>((uint64_t)m0 * F);
     const uint8_t* sr0 = scale_row<W>(g.it.rec, mat, F, H, 2, m0, F);
     const float* sc = reinterpret_cast<const float*>(sr0);
-    f32x4 acc[1][2][2];
+    f32x4 acc[1][R / 32][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < R / 32; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[0][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    Slice<W, 1> sl;
+    Slice<W, 1, R> sl;
     sl.load(w0, mat, sr0, 0, F, 0, bp);
     for (int kb = 0; kb < nk; ++kb) {
       __syncthreads();
@@ -464,7 +475,7 @@ __global__ __launch_bounds__(256) void k_gemm_dn(FfnArgs a) {
       __syncthreads();
       if (kb + 1 < nk) sl.load(w0, mat, sr0, 0, F, (kb + 1) * kGemmK, bp);
       const float s1[1] = {W == kFp8 ? sc[(kb * kGemmK) / 128] : 1.f};
-      gemm_slice<W == kFp8, 1>(As, Bs, s1, acc);
+      gemm_slice<W == kFp8, 1, R>(As, Bs, s1, acc);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -472,8 +483,8 @@ __global__ __launch_bounds__(256) void k_gemm_dn(FfnArgs a) {
       if (idx < n_here) {
         const int p = item_pair(a, g.it, g.r, g.n0 + idx);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int r = m0 + 32 * (wv >> 1) + 16 * i + 4 * (lane >> 4);
+        for (int i = 0; i < R / 32; ++i) {
+          const int r = m0 + (R / 2) * (wv >> 1) + 16 * i + 4 * (lane >> 4);
           *reinterpret_cast<float4*>(part + (uint64_t)p * H + r) =
               make_float4(acc[0][i][j][0], acc[0][i][j][1], acc[0][i][j][2], acc[0][i][j][3]);
         }
@@ -999,8 +1010,8 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
     // tiles of a call: at most one partial tile per record on top of the full ones
     const int tiles = (T * h->k) / kGemmTok + std::min(T * h->k, h->S + h->E) +
                       (shared ? (T + kGemmTok - 1) / kGemmTok : 0);
-    g1 = dim3(std::min(tiles * (h->F / kGemmRows), 2048));
-    g2 = dim3(std::min(tiles * (h->H / kGemmRows), 2048));
+    g1 = dim3(std::min(tiles * (h->F / kGemmRowsGu), 2048));
+    g2 = dim3(std::min(tiles * (h->H / kGemmRowsDn), 2048));
     b1 = b2 = dim3(256);
   }
   {
