@@ -84,6 +84,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--mxfp4-only", action="store_true",
                     help="only the same decode chain with MXFP4 expert records (prints its own JSON line)")
+    ap.add_argument("--deepseek-only", action="store_true",
+                    help="only the DeepSeek-V3-shaped layer: fp8 decode at batch 16 and the 2048-token prefill "
+                         "(prints its own JSON line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
@@ -107,6 +110,12 @@ def main():
     hip.hipMemcpy.restype = ctypes.c_int
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    if args.deepseek_only:
+        print(json.dumps({"workload": "deepseek-v3-shaped offloaded MoE layer, fp8 e4m3 experts with 128x128 "
+                                      "scales: 256 experts + shared, top-8, hidden 7168, moe ffn 2048, 26 slots",
+                          "deepseek_v3_layer": deepseek_layer(args, m, torch)}), flush=True)
+        return
 
     if args.mxfp4_only:
         routers = [synth.router(args.seed, l, E, H, synth.BF16, zipf_s=1.2) for l in range(L)]
@@ -163,12 +172,16 @@ def main():
         xs = synth.tokens(args.seed, 100 + T, T, H, n, 0.9, synth.BF16)
         return torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16).to(dev)
 
-    def run_decode(T, warm, steps, tag, prefetch_n=0, xs_d=None, hs=None):
-        """graph replays of the whole step; returns (tok/s, ms/step, stats delta, chain, buffers, tokens)"""
+    def run_decode(T, warm, steps, tag, prefetch_n=0, xs_d=None, hs=None, cold=None, read_through=True):
+        """graph replays of the whole step; returns (tok/s, ms/step, stats delta, chain, buffers, tokens).
+        With a dict `cold`, the graph is captured and replayed once, every layer's cache is emptied again,
+        and the warm-up replays (from that empty cache) are timed into it."""
         hs = hs or handles
         if xs_d is None:
             xs_d = token_stream(T, warm + steps + args.prof_steps)
         c = m.moe_chain_create(hs, wr_d, b_d, T, prefetch_n)
+        if not read_through:
+            m.moe_chain_set_read_through(c, 0)
         bufs = m.moe_chain_get_buffers(c)
         nbytes = T * H * 2
 
@@ -177,9 +190,28 @@ def main():
             assert rc == 0
             m.moe_chain_run(c, stream)
 
+        if cold is not None:
+            step(0)  # capture + instantiate outside the timed window
+            torch.cuda.synchronize()
+            for h in hs:
+                m.moe_offload_reset(h, stream)
+            torch.cuda.synchronize()
+            c0, c1 = ev(), ev()
+            c0.record(stream)
         for s in range(warm):
             step(s)
+        if cold is not None:
+            c1.record(stream)
         torch.cuda.synchronize()
+        if cold is not None:
+            st = stats_sum(hs)
+            cms = c0.elapsed_time(c1)
+            cold.update({"steps": "0-%d" % (warm - 1), "tokens_per_s": round(T * warm * 1e3 / cms, 2),
+                         "ms_per_step": round(cms / warm, 4),
+                         "misses_per_token": round(st["misses"] / (T * warm), 4),
+                         "staged_copies_per_token": round(st["staged_copies"] / (T * warm), 4)})
+            log("%s cold start (steps 0-%d from an empty cache): %.1f tok/s, %.2f copies/token" %
+                (tag, warm - 1, T * warm * 1e3 / cms, (st["misses"] + st["staged_copies"]) / (T * warm)))
         before = stats_sum(hs)
         a, b_ = ev(), ev()
         torch.cuda.synchronize()
@@ -197,15 +229,26 @@ def main():
              delta["misses"] / (T * steps), delta["staged_calls"], delta["calls"]))
         return T * steps * 1e3 / ms, ms / steps, delta, c, bufs, xs_d
 
-    tok_s, ms_step, delta, chain, bufs, xs_d = run_decode(T0, args.warmup, args.steps, "decode")
+    cold = {}
+    tok_s, ms_step, delta, chain, bufs, xs_d = run_decode(T0, args.warmup, args.steps, "decode", cold=cold)
+    m.moe_chain_destroy(chain)
 
-    # ---------------- eager pass of the same chain with per-kernel HIP events on the launch stream
+    # ---------------- the same stream from empty caches with the misses moved by the copy kernel before the FFN
+    for h in handles:
+        m.moe_offload_reset(h, stream)
+    tok_cp, ms_cp, delta_cp, chain, bufs, _ = run_decode(T0, args.warmup, args.steps, "decode-copy-kernel",
+                                                         xs_d=xs_d, read_through=False)
+    assert delta_cp["misses"] == delta["misses"] and delta_cp["staged_copies"] == delta["staged_copies"]
+
+    # ---------------- eager pass of the copy-kernel chain with per-kernel HIP events on the launch stream:
+    # each kernel's bytes come from one memory (the FFN from HBM, the copy over the host link)
     T = T0
     for h in handles:
         m.moe_offload_profile(h, 1)
     before = stats_sum()
     s0 = args.warmup + args.steps
     gu_bytes = dn_bytes = 0
+    distinct = 0  # distinct records the FFN reads, summed over the profiled calls
     sid_host = np.empty((L, T, K_TOP), dtype=np.int32)
     for s in range(s0, s0 + args.prof_steps):
         hip.hipMemcpyAsync(bufs["x"], xs_d[s].data_ptr(), T * H * 2, 3, stream.cuda_stream)
@@ -215,6 +258,7 @@ def main():
         assert hip.hipMemcpy(sid_host.ctypes.data, bufs["slot_ids"], sid_host.nbytes, 2) == 0
         for l in range(L):
             nrec = len(np.unique(sid_host[l]))
+            distinct += nrec
             gu_bytes += nrec * 2 * F * H * 2 + T * H * 2 + T * K_TOP * F * 2
             dn_bytes += nrec * F * H * 2 + T * K_TOP * F * 2 + T * K_TOP * H * 4
     kt = {}
@@ -257,14 +301,19 @@ def main():
         "decode_stats": {"misses_per_token": round(delta["misses"] / (T0 * args.steps), 4),
                          "staged_calls": delta["staged_calls"], "calls": delta["calls"],
                          "staged_copies_per_token": round(delta["staged_copies"] / (T0 * args.steps), 4),
-                         "hit_rate": round(delta["hits"] / max(1, delta["hits"] + delta["misses"] + delta["staged_copies"]), 4)},
-        "roofline": {"bound": "hbm", "kernel": "k_gateup_one<bf16, 16> (gate/up + SiLU, single-token decode)",
+                         "hit_rate": round(delta["hits"] / max(1, delta["hits"] + delta["misses"] + delta["staged_copies"]), 4),
+                         "steady_state_steps": "%d-%d" % (args.warmup, args.warmup + args.steps - 1)},
+        "cold_start": cold,
+        "read_through": {"on_tokens_per_s": round(tok_s, 2), "off_tokens_per_s": round(tok_cp, 2),
+                         "on_ms_per_step": round(ms_step, 4), "off_ms_per_step": round(ms_cp, 4),
+                         "speedup": round(tok_s / tok_cp, 4)},
+        "roofline": {"bound": "hbm", "kernel": "k_gateup_one<bf16, 16, false> (gate/up + SiLU, single-token decode, records read in place)",
                      "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else traffic,
                      "avg_launch_us": round(gu_ms * 1e3 / gu_n, 3), "launches": gu_n,
                      "algorithmic_bytes_per_launch": int(gu_bytes // gu_n)},
-        "roofline_down": {"bound": "hbm", "kernel": "k_down_one<bf16, 6>", "achieved": round(dn_gbps, 1),
+        "roofline_down": {"bound": "hbm", "kernel": "k_down_one<bf16, 6, false>", "achieved": round(dn_gbps, 1),
                           "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dn_gbps / HBM_PEAK_GBPS, 4),
                           "avg_launch_us": round(dn_ms * 1e3 / dn_n, 3),
                           "algorithmic_bytes_per_launch": int(dn_bytes // dn_n)},
@@ -311,6 +360,19 @@ def main():
                            "decode_copy_frac_of_measured_link": round(cp_gbps / link, 4)}
     log("host link: SDMA %.2f GB/s, copy kernel %.2f GB/s; decode copies at %.1f %% of measured link" %
         (sdma, kernel_link, 100 * cp_gbps / link))
+
+    # ---------------- summed roofline of the timed steps: every copied record over the measured host link,
+    # every distinct record the FFN reads once from HBM at the datasheet rate
+    copies_step = (delta["misses"] + delta["staged_copies"]) / args.steps
+    distinct_step = distinct / args.prof_steps
+    bound_ms = (copies_step * rb / (link * 1e9) + distinct_step * rb / (HBM_PEAK_GBPS * 1e9)) * 1e3
+    result["summed_roofline"] = {"ms_per_step": round(bound_ms, 4), "tokens_per_s": round(T0 * 1e3 / bound_ms, 2),
+                                 "frac": round(bound_ms / ms_step, 4),
+                                 "copied_records_per_step": round(copies_step, 3),
+                                 "distinct_records_per_step": round(distinct_step, 3),
+                                 "record_bytes": rb, "link_GBps": round(link, 2), "hbm_GBps": HBM_PEAK_GBPS}
+    log("summed roofline: %.3f ms/step (%.1f tok/s); measured %.3f ms/step = %.1f %% of it" %
+        (bound_ms, T0 * 1e3 / bound_ms, ms_step, 100 * bound_ms / ms_step))
 
     if args.extra:
         for T in (8, 32):
@@ -387,6 +449,19 @@ def qwen3_mxfp4(args, m, torch, hip, wr_d, b_d):
     ms = a.elapsed_time(b)
     d = {kk: v - before[kk] for kk, v in stats().items()}
     assert d["error"] == 0
+    # the same replays from empty caches with the copy kernel moving the misses before the FFN; the eager
+    # profile below runs this way too, so that each kernel's bytes come from one memory
+    m.moe_chain_set_read_through(c, 0)
+    for h in hs:
+        m.moe_offload_reset(h, stream)
+    for s in range(warm):
+        step(s, m.moe_chain_run)
+    a.record(stream)
+    for s in range(warm, warm + steps):
+        step(s, m.moe_chain_run)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms_off = a.elapsed_time(b)
     for h in hs:
         m.moe_offload_profile(h, 1)
     gu_bytes = dn_bytes = 0
@@ -412,21 +487,22 @@ def qwen3_mxfp4(args, m, torch, hip, wr_d, b_d):
         m.moe_offload_destroy(h)
     (gu_ms, gu_n), (dn_ms, dn_n), (cp_ms, cp_n) = kt["gateup"], kt["down"], kt["copy"]
     out = {"tokens_per_s": round(T * steps * 1e3 / ms, 2), "ms_per_step": round(ms / steps, 4), "steps": steps,
+           "copy_kernel_tokens_per_s": round(T * steps * 1e3 / ms_off, 2),
            "record_bytes": rb, "host_store_GB": round(L * E * stride / 1e9, 2),
            "copies_per_token": round((d["misses"] + d["staged_copies"]) / (T * steps), 4),
            "copy_GBps": round(copy_bytes / (cp_ms * 1e-3) / 1e9, 2) if cp_ms > 0 else 0.0,
-           "roofline_gateup": {"kernel": "k_gateup_one<mxfp4, 8>", "avg_launch_us": round(gu_ms * 1e3 / gu_n, 3),
+           "roofline_gateup": {"kernel": "k_gateup_one<mxfp4, 8, false>", "avg_launch_us": round(gu_ms * 1e3 / gu_n, 3),
                                "algorithmic_bytes_per_launch": int(gu_bytes // gu_n),
                                "achieved": round(gu_bytes / (gu_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
                                "unit": "GB/s", "frac": round(gu_bytes / (gu_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
-           "roofline_down": {"kernel": "k_down_one<mxfp4, 3>", "avg_launch_us": round(dn_ms * 1e3 / dn_n, 3),
+           "roofline_down": {"kernel": "k_down_one<mxfp4, 3, false>", "avg_launch_us": round(dn_ms * 1e3 / dn_n, 3),
                              "algorithmic_bytes_per_launch": int(dn_bytes // dn_n),
                              "achieved": round(dn_bytes / (dn_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
                              "unit": "GB/s", "frac": round(dn_bytes / (dn_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
            "kernels_us": {kind: round(v * 1e3 / n, 3) for kind, (v, n) in kt.items() if n}}
-    log("qwen3 mxfp4 decode: %.1f tok/s, %.2f copies/token of %.2f MB, gateup %.2f us, down %.2f us" %
-        (out["tokens_per_s"], out["copies_per_token"], rb / 1e6, out["roofline_gateup"]["avg_launch_us"],
-         out["roofline_down"]["avg_launch_us"]))
+    log("qwen3 mxfp4 decode: %.1f tok/s (copy kernel: %.1f), %.2f copies/token of %.2f MB, gateup %.2f us, "
+        "down %.2f us" % (out["tokens_per_s"], out["copy_kernel_tokens_per_s"], out["copies_per_token"], rb / 1e6,
+                          out["roofline_gateup"]["avg_launch_us"], out["roofline_down"]["avg_launch_us"]))
     return out
 
 
@@ -558,7 +634,11 @@ def deepseek_layer(args, m, torch):
         "down_us": round(dn_us, 1), "down_TFLOPs": round(flop_dn / (dn_us * 1e-6) / 1e12, 1),
         "mfma_peak_TFLOPs": 2500.0, "mfma_dtype": "bf16 (fp8 codes widened exactly)",
         "frac_of_mfma_peak": round((flop_gu + flop_dn) / (ffn_ms * 1e-3) / 1e12 / 2500.0, 4),
-        "hbm_bound_ms": round(wbytes / 8e12 * 1e3, 3), "tokens_per_expert_max": int(cnt.max()),
+        "hbm_bound_ms": round(wbytes / 8e12 * 1e3, 3),
+        # attainable roofline: the slower of streaming the distinct records once and the dense bf16 MFMA rate
+        "attainable_bound_ms": round(max(wbytes / 8e12, (flop_gu + flop_dn) / 2.5e15) * 1e3, 3),
+        "frac_of_attainable": round(max(wbytes / 8e12, (flop_gu + flop_dn) / 2.5e15) * 1e3 / ffn_ms, 4),
+        "tokens_per_expert_max": int(cnt.max()),
         "experts_used": int((cnt > 0).sum())}
     log("deepseek prefill T=2048: stage %.1f ms (%.1f GB/s), ffn %.2f ms = %.1f TFLOP/s" %
         (stage_ms, E * rb / (stage_ms * 1e-3) / 1e9, ffn_ms, (flop_gu + flop_dn) / (ffn_ms * 1e-3) / 1e12))
@@ -679,11 +759,32 @@ def cpu_baseline(args, handles, routers, stride, T):
         if time.time() - t0 > args.cpu_seconds:
             break
     dt = time.time() - t0
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    log("cpu oracle: %d steps x %d layers in %.1f s" % (steps, L, dt))
+    threads = oracle.threads()
+    log("cpu oracle: %d steps x %d layers in %.1f s on %d threads" % (steps, L, dt, threads))
     return {"value": round(T * steps / dt, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "first %d decode steps (batch %d, all %d layers) of the same token stream, from a cold cache"
-                      % (steps, T, L)}
+                      % (steps, T, L),
+            "host": host_cpu()}
+
+
+def host_cpu():
+    """nproc, the CPU model, sockets and hardware threads of the host, from /proc/cpuinfo."""
+    model, sockets, logical = None, set(), 0
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                key, _, val = line.partition(":")
+                key, val = key.strip(), val.strip()
+                if key == "processor":
+                    logical += 1
+                elif key == "model name" and model is None:
+                    model = val
+                elif key == "physical id":
+                    sockets.add(val)
+    except OSError:
+        pass
+    return {"nproc": len(os.sched_getaffinity(0)), "model": model, "sockets": len(sockets) or None,
+            "threads": logical or os.cpu_count()}
 
 
 if __name__ == "__main__":

@@ -103,6 +103,7 @@ def lib():
             "moe_chain_get_buffers": ([vp, P(ChainBuffers)], i32),
             "moe_chain_run": ([vp, vp], i32),
             "moe_chain_run_eager": ([vp, vp], i32),
+            "moe_chain_set_read_through": ([vp, i32], i32),
             "moe_chain_destroy": ([vp], None),
         }
         for name, (args, res) in sig.items():
@@ -265,6 +266,10 @@ def moe_chain_run(c, stream=None):
 
 def moe_chain_run_eager(c, stream=None):
     return _check(lib().moe_chain_run_eager(c, _stream(stream)))
+
+
+def moe_chain_set_read_through(c, on):
+    return _check(lib().moe_chain_set_read_through(c, 1 if on else 0))
 
 
 def moe_chain_destroy(c):

@@ -28,6 +28,7 @@ struct moe_chain {
   std::vector<const float*> bias;
   std::vector<const void*> shared;
   int L = 0, T = 0, k = 0, H = 0, prefetch_n = 0, device = 0;
+  int read_through = 1;  // single-token steps: the FFN fills missed slots from the host store
   size_t act = 2;
   void* block = nullptr;
   uint8_t* x = nullptr;
@@ -116,7 +117,9 @@ hipError_t issue(moe_chain* c, hipStream_t cs) {
       }
     }
     if (pf && l >= 1) CHK(hipStreamWaitEvent(cs, c->ev_pf[l], 0));  // this layer's prefetch copy first
-    CHK(moe::launch_copy(h, h->cache.copy_list, cs));
+    // a single token's misses are read through by its FFN launches instead of a copy launch
+    const bool fill = c->read_through && moe::ffn_reads_through(h, T);
+    if (!fill) CHK(moe::launch_copy(h, h->cache.copy_list, cs));
     if (look) {  // prefetch copy for layer l+1 behind layer l's demand copy
       CHK(hipEventRecord(c->ev_demand[l], cs));
       CHK(hipStreamWaitEvent(c->sf, c->ev_demand[l], 0));
@@ -124,7 +127,8 @@ hipError_t issue(moe_chain* c, hipStream_t cs) {
       CHK(hipEventRecord(c->ev_pf[l + 1], c->sf));
     }
     CHK(moe::launch_ffn(h, XN(c, l), c->sid + R(c, l), c->w + R(c, l), T, c->shared[l], Y(c, l), X(c, l), X(c, l + 1),
-                        l + 1 < c->L ? XN(c, l + 1) : nullptr, kRmsEps, cs, fused, !(fuse_cl && l + 1 < c->L)));
+                        l + 1 < c->L ? XN(c, l + 1) : nullptr, kRmsEps, cs, fused, !(fuse_cl && l + 1 < c->L),
+                        fill));
   }
   if (pf && c->L > 1) {  // rejoin the side streams (the predictor stream is used only without fusion)
     if (!fused) {
@@ -253,6 +257,23 @@ int moe_chain_run(moe_chain* c, void* stream) {
     if (e == hipSuccess) e = hipGraphInstantiate(&c->exec, c->graph, nullptr, nullptr, 0);
   }
   if (e == hipSuccess) e = hipGraphLaunch(c->exec, (hipStream_t)stream);
+  (void)hipSetDevice(prev);
+  if (e != hipSuccess) return cfail(MOE_EHIP, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+int moe_chain_set_read_through(moe_chain* c, int on) {
+  if (!c) return cfail(MOE_EINVAL, "moe_chain_set_read_through: null chain");
+  if ((on != 0) == (c->read_through != 0)) return MOE_OK;
+  int prev = 0;
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(c->device);
+  hipError_t e = hipDeviceSynchronize();  // no replay of the old graph may still run
+  if (c->exec) (void)hipGraphExecDestroy(c->exec);
+  if (c->graph) (void)hipGraphDestroy(c->graph);
+  c->exec = nullptr;
+  c->graph = nullptr;
+  c->read_through = on != 0;
   (void)hipSetDevice(prev);
   if (e != hipSuccess) return cfail(MOE_EHIP, hipGetErrorString(e));
   return MOE_OK;

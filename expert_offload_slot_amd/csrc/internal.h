@@ -126,9 +126,12 @@ hipError_t launch_stage_all(moe_offload* h, const int32_t* ids, int n, int32_t* 
 // xn_next (optional, needs x_next): rmsnorm(x_next) with eps, for the next layer of a chain;
 // grouped: the group descriptor for slot_ids was already built (launch_decide)
 // combine = false: stop after the down projection (the chain takes the combine into the next router launch)
+// fill: where ffn_reads_through(h, T), the records of the copy list are read from the host store and
+// written to their slots by the FFN itself (the caller then launches no copy for the call)
 hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int T,
                       const void* shared, void* y, const void* residual, void* x_next, void* xn_next, float eps,
-                      hipStream_t s, bool grouped = false, bool combine = true);
+                      hipStream_t s, bool grouped = false, bool combine = true, bool fill = false);
+bool ffn_reads_through(const moe_offload* h, int T);
 // Decode control step in one workgroup: top-k of h->logits (launch_logits first),
 // ensure, and the FFN grouping.  With hn (max_n > 0): also the top-k of
 // hn->logits (the lookahead prediction, ids to pred) and the prefetch install

@@ -68,6 +68,10 @@ struct FfnArgs {
   int off_pairs, off_tiles;
   int max_routed;  // record blocks a call can fill: min(T * k, S + E); unused ones are marked empty
   int pair_items;  // one token: its k records are distinct, so each choice is its own work item (no grouping)
+  // single-token read-through: the ensure's copy list, and the device address of the host store
+  // (null list: every record is read where slot_ids points)
+  const int32_t* fill_list;
+  const uint8_t* host;
 };
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)rn_to_bf16(f); }
@@ -551,12 +555,52 @@ __device__ __forceinline__ typename WChunk<W>::T load_w(const uint8_t* row, int 
   return *reinterpret_cast<const typename WChunk<W>::T*>(row + (uint64_t)(16 * kb + c) * sizeof(typename WChunk<W>::T));
 }
 
-// the scale lane c applies in K block kb (srow from scale_row)
+// the stored scale lane c applies in K block kb (srow from scale_row), as raw
+// bits: fp8 the fp32 word, MXFP4 the E8M0 byte, bf16 none
+template <int W>
+__device__ __forceinline__ uint32_t load_sr(const uint8_t* srow, int kb, int c) {
+  if (W == kFp8) return reinterpret_cast<const uint32_t*>(srow)[kb];
+  if (W == kMx4) return srow[8 * kb + (c >> 1)];
+  return 0u;
+}
+
+template <int W>
+__device__ __forceinline__ float scale_of(uint32_t raw) {
+  if (W == kFp8) return __uint_as_float(raw);
+  if (W == kMx4) return e8m0_scale(raw);
+  return 1.f;
+}
+
+// the scale lane c applies in K block kb
 template <int W>
 __device__ __forceinline__ float load_s(const uint8_t* srow, int kb, int c) {
-  if (W == kFp8) return reinterpret_cast<const float*>(srow)[kb];
-  if (W == kMx4) return e8m0_scale(srow[8 * kb + (c >> 1)]);
-  return 1.f;
+  return scale_of<W>(load_sr<W>(srow, kb, c));
+}
+
+// Where a read-through pass writes what it reads: the two rows' codes in the
+// slot, and their scales when this row is the one that owns them (fp8: the
+// first row of a 128-row block, lane 0 per K block; MXFP4: every row, even
+// lanes, one E8M0 byte per 32 weights).
+struct Fill {
+  uint8_t* w0 = nullptr;
+  uint8_t* w1 = nullptr;
+  uint8_t* s0 = nullptr;
+  uint8_t* s1 = nullptr;
+  bool own0 = false, own1 = false;
+};
+
+template <int W>
+__device__ __forceinline__ void store_w(uint8_t* row, int kb, int c, typename WChunk<W>::T v) {
+  *reinterpret_cast<typename WChunk<W>::T*>(row + (uint64_t)(16 * kb + c) * sizeof(typename WChunk<W>::T)) = v;
+}
+
+template <int W>
+__device__ __forceinline__ void store_sr(uint8_t* srow, int kb, int c, uint32_t raw) {
+  if (W == kFp8) {
+    if (c == 0) reinterpret_cast<uint32_t*>(srow)[kb] = raw;
+  } else if (W == kMx4) {
+    if ((c & 1) == 0) srow[8 * kb + (c >> 1)] = (uint8_t)raw;
+  }
 }
 
 // acc += lane chunk w (K block kb) . the matching activations of row xr
@@ -638,26 +682,34 @@ __device__ __forceinline__ void vec_pass(const uint8_t* row0, const uint8_t* row
 }
 
 // vec_pass for one activation row: each pass one unbroken run of loads, then
-// the pair dots.  Same per-lane order as vec_pass, so the same bits.
-template <int W, int CH>
+// the pair dots.  Same per-lane order as vec_pass, so the same bits.  With
+// FILL every chunk and owned scale read is also stored to fl (the read-through
+// of a missed record: the bytes are the same either way).
+template <int W, int CH, bool FILL>
 __device__ __forceinline__ void one_pass(const uint8_t* row0, const uint8_t* row1, const uint8_t* sr0,
                                          const uint8_t* sr1, int nk, int c, const uint16_t* act, float& acc0,
-                                         float& acc1) {
+                                         float& acc1, const Fill& fl) {
   const uint4* xr = reinterpret_cast<const uint4*>(act);
   for (int k0 = 0; k0 < nk; k0 += CH) {
     typename WChunk<W>::T w0[CH], w1[CH];
-    float s0[CH], s1[CH];
+    uint32_t s0[CH], s1[CH];
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       w0[i] = load_w<W>(row0, k0 + i, c);
       w1[i] = load_w<W>(row1, k0 + i, c);
-      s0[i] = load_s<W>(sr0, k0 + i, c);
-      s1[i] = load_s<W>(sr1, k0 + i, c);
+      s0[i] = load_sr<W>(sr0, k0 + i, c);
+      s1[i] = load_sr<W>(sr1, k0 + i, c);
     }
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      acc0 = wdot<W>(w0[i], xr, k0 + i, c, acc0, s0[i]);
-      acc1 = wdot<W>(w1[i], xr, k0 + i, c, acc1, s1[i]);
+      if constexpr (FILL) {
+        store_w<W>(fl.w0, k0 + i, c, w0[i]);
+        store_w<W>(fl.w1, k0 + i, c, w1[i]);
+        if (fl.own0) store_sr<W>(fl.s0, k0 + i, c, s0[i]);
+        if (fl.own1) store_sr<W>(fl.s1, k0 + i, c, s1[i]);
+      }
+      acc0 = wdot<W>(w0[i], xr, k0 + i, c, acc0, scale_of<W>(s0[i]));
+      acc1 = wdot<W>(w1[i], xr, k0 + i, c, acc1, scale_of<W>(s1[i]));
     }
   }
 }
@@ -669,6 +721,12 @@ inline int one_chunks(int nk) {
     if (nk % ch == 0) return ch;
   return 1;
 }
+
+// K blocks per read-through pass: half of 16 or 8 (still a divisor of nk), so
+// that the values held for the stores do not raise the kernel's register count
+// above the in-place pass; the summation order is the same for any pass width
+template <int CH>
+constexpr int kFillChunks = CH >= 8 ? CH / 2 : CH;
 
 // gate/up: work item = (record, 4 rows of F); quarter q takes row f = 4*g + q of
 // gate (stream 0) and up (stream 1); h = silu(gate) * up stored in bf16.
@@ -778,7 +836,32 @@ __device__ __forceinline__ const uint8_t* one_record(const FfnArgs& a, int j) {
   return ri < a.S ? a.slots + (uint64_t)ri * a.stride : a.staging + (uint64_t)(ri - a.S) * a.stride;
 }
 
-template <int W, int CH>
+// Read-through (FILL): choice j's record was assigned to its slot by this
+// call's ensure when the copy list pairs slot_ids[j] with an expert e.  Then
+// the record is read from e's row of the device-mapped host store and every
+// byte is written to the slot as the FFN reads it: the gate/up launch fills
+// the gate and up matrices and their scales, the down launch the rest, so at
+// the end of the call the slot holds the whole record, as after the copy
+// kernel.  Returns e's host record, or null when j reads its record in place.
+__device__ __forceinline__ const uint8_t* fill_source(const FfnArgs& a, int j) {
+  if (j == a.k) return nullptr;  // the shared expert is device resident
+  const int32_t* __restrict__ lst = a.fill_list;
+  if (lst[0] == MOE_MODE_STAGED_ALL) return nullptr;
+  const int n = min(lst[1], a.k);  // a single token has at most k misses
+  const int r = a.slot_ids[j];
+  for (int m = 0; m < n; ++m) {
+    if (lst[3 + 2 * m] != r) continue;
+    const int e = lst[2 + 2 * m];
+    if ((unsigned)e >= (unsigned)a.E) {
+      atomicOr(a.err, MOE_DEV_ERR_AUDIT);
+      return nullptr;
+    }
+    return a.host + (uint64_t)e * a.stride;
+  }
+  return nullptr;
+}
+
+template <int W, int CH, bool FILL>
 __global__ __launch_bounds__(256) void k_gateup_one(FfnArgs a) {
   const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
   const int RG = a.F / 4;
@@ -791,17 +874,35 @@ __global__ __launch_bounds__(256) void k_gateup_one(FfnArgs a) {
   for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < items; item += gridDim.x * 4) {
     const int j = item / RG, f = (item % RG) * 4 + q;
     const uint8_t* rec = one_record(a, j);
-    const uint8_t* wg = rec + code_bytes<W>((uint64_t)f * H);
     float g = 0.f, up = 0.f;
-    one_pass<W, CH>(wg, wg + mat, scale_row<W>(rec, mat, F, H, 0, f, H), scale_row<W>(rec, mat, F, H, 1, f, H), nk,
-                    c, x, g, up);
+    bool done = false;
+    if constexpr (FILL) {
+      if (const uint8_t* src = fill_source(a, j)) {  // uniform per wavefront
+        uint8_t* dst = const_cast<uint8_t*>(rec);
+        Fill fl;
+        fl.w0 = dst + code_bytes<W>((uint64_t)f * H);
+        fl.w1 = fl.w0 + mat;
+        fl.s0 = const_cast<uint8_t*>(scale_row<W>(dst, mat, F, H, 0, f, H));
+        fl.s1 = const_cast<uint8_t*>(scale_row<W>(dst, mat, F, H, 1, f, H));
+        fl.own0 = fl.own1 = W == kMx4 || (f & 127) == 0;
+        const uint8_t* wg = src + code_bytes<W>((uint64_t)f * H);
+        one_pass<W, kFillChunks<CH>, true>(wg, wg + mat, scale_row<W>(src, mat, F, H, 0, f, H),
+                                           scale_row<W>(src, mat, F, H, 1, f, H), nk, c, x, g, up, fl);
+        done = true;
+      }
+    }
+    if (!done) {
+      const uint8_t* wg = rec + code_bytes<W>((uint64_t)f * H);
+      one_pass<W, CH, false>(wg, wg + mat, scale_row<W>(rec, mat, F, H, 0, f, H),
+                             scale_row<W>(rec, mat, F, H, 1, f, H), nk, c, x, g, up, Fill());
+    }
     g = reduce16_all(g);
     up = reduce16_all(up);
     if (c == 0) hb[(uint64_t)j * F + f] = f32_to_bf16(silu_mul(g, up));
   }
 }
 
-template <int W, int CH>
+template <int W, int CH, bool FILL>
 __global__ __launch_bounds__(256) void k_down_one(FfnArgs a) {
   const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
   const int RG = a.H / 8;
@@ -814,10 +915,31 @@ __global__ __launch_bounds__(256) void k_down_one(FfnArgs a) {
   for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < items; item += gridDim.x * 4) {
     const int j = item / RG, h0 = (item % RG) * 8 + q;
     const uint8_t* rec = one_record(a, j);
-    const uint8_t* wd = rec + 2 * mat + code_bytes<W>((uint64_t)h0 * F);
     float s0 = 0.f, s1 = 0.f;
-    one_pass<W, CH>(wd, wd + code_bytes<W>(4ull * F), scale_row<W>(rec, mat, F, H, 2, h0, F),
-                    scale_row<W>(rec, mat, F, H, 2, h0 + 4, F), nk, c, hb + (uint64_t)j * F, s0, s1);
+    bool done = false;
+    if constexpr (FILL) {
+      if (const uint8_t* src = fill_source(a, j)) {  // uniform per wavefront
+        uint8_t* dst = const_cast<uint8_t*>(rec);
+        Fill fl;
+        fl.w0 = dst + 2 * mat + code_bytes<W>((uint64_t)h0 * F);
+        fl.w1 = fl.w0 + code_bytes<W>(4ull * F);
+        fl.s0 = const_cast<uint8_t*>(scale_row<W>(dst, mat, F, H, 2, h0, F));
+        fl.s1 = const_cast<uint8_t*>(scale_row<W>(dst, mat, F, H, 2, h0 + 4, F));
+        fl.own0 = W == kMx4 || (h0 & 127) == 0;
+        fl.own1 = W == kMx4;  // h0 + 4 is never the first row of a 128-row block
+        const uint8_t* wd = src + 2 * mat + code_bytes<W>((uint64_t)h0 * F);
+        one_pass<W, kFillChunks<CH>, true>(wd, wd + code_bytes<W>(4ull * F), scale_row<W>(src, mat, F, H, 2, h0, F),
+                                           scale_row<W>(src, mat, F, H, 2, h0 + 4, F), nk, c, hb + (uint64_t)j * F,
+                                           s0, s1, fl);
+        done = true;
+      }
+    }
+    if (!done) {
+      const uint8_t* wd = rec + 2 * mat + code_bytes<W>((uint64_t)h0 * F);
+      one_pass<W, CH, false>(wd, wd + code_bytes<W>(4ull * F), scale_row<W>(rec, mat, F, H, 2, h0, F),
+                             scale_row<W>(rec, mat, F, H, 2, h0 + 4, F), nk, c, hb + (uint64_t)j * F, s0, s1,
+                             Fill());
+    }
     s0 = reduce16_all(s0);
     s1 = reduce16_all(s1);
     if (c < 2) part[(uint64_t)j * H + h0 + 4 * c] = c ? s1 : s0;
@@ -825,29 +947,31 @@ __global__ __launch_bounds__(256) void k_down_one(FfnArgs a) {
 }
 
 // kernel instantiation by K blocks per pass
-#define MOE_BY_CHUNKS(KERN, W, NK) \
-  switch (one_chunks(NK)) {        \
-    case 16: return KERN<W, 16>;   \
-    case 8: return KERN<W, 8>;     \
-    case 6: return KERN<W, 6>;     \
-    case 4: return KERN<W, 4>;     \
-    case 3: return KERN<W, 3>;     \
-    case 2: return KERN<W, 2>;     \
-    default: return KERN<W, 1>;    \
+#define MOE_BY_CHUNKS(KERN, NK, ...)        \
+  switch (one_chunks(NK)) {                 \
+    case 16: return KERN<W, 16, ##__VA_ARGS__>; \
+    case 8: return KERN<W, 8, ##__VA_ARGS__>;   \
+    case 6: return KERN<W, 6, ##__VA_ARGS__>;   \
+    case 4: return KERN<W, 4, ##__VA_ARGS__>;   \
+    case 3: return KERN<W, 3, ##__VA_ARGS__>;   \
+    case 2: return KERN<W, 2, ##__VA_ARGS__>;   \
+    default: return KERN<W, 1, ##__VA_ARGS__>;  \
   }
 
 typedef void (*FfnKernel)(FfnArgs);
 template <int W>
-FfnKernel gateup_decode(bool one, int H) {
+FfnKernel gateup_decode(bool one, bool fill, int H) {
   const int nk = H / (16 * lane_weights<W>());
-  if (one) { MOE_BY_CHUNKS(k_gateup_one, W, nk) }
-  MOE_BY_CHUNKS(k_gateup_vec, W, nk)
+  if (one && fill) { MOE_BY_CHUNKS(k_gateup_one, nk, true) }
+  if (one) { MOE_BY_CHUNKS(k_gateup_one, nk, false) }
+  MOE_BY_CHUNKS(k_gateup_vec, nk)
 }
 template <int W>
-FfnKernel down_decode(bool one, int F) {
+FfnKernel down_decode(bool one, bool fill, int F) {
   const int nk = F / (16 * lane_weights<W>());
-  if (one) { MOE_BY_CHUNKS(k_down_one, W, nk) }
-  MOE_BY_CHUNKS(k_down_vec, W, nk)
+  if (one && fill) { MOE_BY_CHUNKS(k_down_one, nk, true) }
+  if (one) { MOE_BY_CHUNKS(k_down_one, nk, false) }
+  MOE_BY_CHUNKS(k_down_vec, nk)
 }
 #undef MOE_BY_CHUNKS
 
@@ -951,9 +1075,11 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(FfnArgs a, void* __rest
 
 }  // namespace
 
+bool ffn_reads_through(const moe_offload* h, int T) { return T == 1 && h->dtype != MOE_F32; }
+
 hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int T,
                       const void* shared, void* y, const void* residual, void* x_next, void* xn_next, float eps,
-                      hipStream_t s, bool grouped, bool combine) {
+                      hipStream_t s, bool grouped, bool combine, bool fill) {
   FfnArgs a;
   a.x = x;
   a.slot_ids = slot_ids;
@@ -979,6 +1105,9 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
   a.off_tiles = h->gl.off_tiles();
   a.max_routed = std::min(T * h->k, h->S + h->E);
   a.pair_items = T == 1 && h->dtype != MOE_F32 ? 1 : 0;
+  fill = fill && a.pair_items;
+  a.fill_list = fill ? h->cache.copy_list : nullptr;
+  a.host = h->host_dev;
   // distinct records a call can touch (+ the shared expert)
   const int max_items_r = a.max_routed + (shared ? 1 : 0);
   if (!grouped && !a.pair_items) {
@@ -997,10 +1126,10 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
     b1 = b2 = dim3(256);
   } else if (T <= kDecodeMaxT) {  // one wavefront per work item, 4 per workgroup
     const bool one = a.pair_items != 0;
-    gu = wf == kFp8 ? gateup_decode<kFp8>(one, h->H)
-                    : (wf == kMx4 ? gateup_decode<kMx4>(one, h->H) : gateup_decode<kBf16>(one, h->H));
-    dn = wf == kFp8 ? down_decode<kFp8>(one, h->F)
-                    : (wf == kMx4 ? down_decode<kMx4>(one, h->F) : down_decode<kBf16>(one, h->F));
+    gu = wf == kFp8 ? gateup_decode<kFp8>(one, fill, h->H)
+                    : (wf == kMx4 ? gateup_decode<kMx4>(one, fill, h->H) : gateup_decode<kBf16>(one, fill, h->H));
+    dn = wf == kFp8 ? down_decode<kFp8>(one, fill, h->F)
+                    : (wf == kMx4 ? down_decode<kMx4>(one, fill, h->F) : down_decode<kBf16>(one, fill, h->F));
     g1 = dim3(std::min((max_items_r * (h->F / 4) + 3) / 4, 8192));
     g2 = dim3(std::min((max_items_r * (h->H / 8) + 3) / 4, 8192));
     b1 = b2 = dim3(256);

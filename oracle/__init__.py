@@ -89,8 +89,15 @@ def lib():
         L.orc_resolve.argtypes = [vp, i32, i32, vp, vp, sz, vp]
         L.orc_residual.argtypes = [vp, vp, i32, sz, vp]
         L.orc_rmsnorm.argtypes = [vp, i32, i32, i32, f64, vp]
+        L.orc_threads.argtypes = []
+        L.orc_threads.restype = i32
         _lib = L
     return _lib
+
+
+def threads():
+    """OpenMP threads the oracle's parallel loops run on."""
+    return int(lib().orc_threads())
 
 
 def _p(a):

@@ -24,6 +24,7 @@
  * Build: gcc -O2 -ffp-contract=off (no fast-math; denormals kept).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -708,3 +709,6 @@ void orc_rmsnorm(const void* x, int wdt, int T, int H, double eps, void* out) {
     for (int i = 0; i < H; ++i) store_act(out, wdt, (size_t)t * H + i, load_act(x, wdt, (size_t)t * H + i) * inv);
   }
 }
+
+/* threads the OpenMP loops above use (for reporting how the oracle was timed) */
+int orc_threads(void) { return omp_get_max_threads(); }

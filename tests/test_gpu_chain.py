@@ -241,3 +241,44 @@ def test_chain_with_pinned_experts():
         assert all(m.moe_offload_stats(h)["error"] == 0 for h in cg.handles)
     finally:
         cg.close()
+
+
+@pytest.mark.parametrize("wdt,shared,prefetch_n,H,F", [
+    # small passes for each format, the lookahead beside it, and the 16- and 8-block passes (read through
+    # at half the width) for bf16, fp8 and MXFP4
+    (1, False, 0, 256, 512), (2, True, 0, 256, 512), (3, True, 0, 256, 512), (1, False, 2, 256, 512),
+    (1, False, 0, 2048, 256), (2, False, 0, 1024, 1024), (3, True, 0, 2048, 512)])
+def test_chain_read_through_matches_copy_kernel(wdt, shared, prefetch_n, H, F):
+    """Single-token read-through (the FFN fills missed slots from the host store, no copy launch) against the
+    same chain with the copy kernel: identical outputs, routing, tables and counters on every step, every
+    occupied slot byte-identical to its expert's host record, and the oracle replay on the read-through chain."""
+    L, E, S, k, T = 3, 16, 6, 4, 1
+    print("chain read-through wdt=%d shared=%s prefetch=%d H=%d F=%d" % (wdt, shared, prefetch_n, H, F), flush=True)
+    rt = ChainModel(L, E, S, k, H, F, wdt, T, 93, prefetch_n, shared=shared)
+    cp = ChainModel(L, E, S, k, H, F, wdt, T, 93, prefetch_n, shared=shared)
+    m.moe_chain_set_read_through(cp.chain, 0)
+    rb = oracle.record_bytes(wdt, H, F)
+    caches = [oracle.Cache(E, S, rt.hosts[l], rb) for l in range(L)]
+    try:
+        for s in range(10):
+            graph = s % 3 != 2  # mostly graph replays, every third step eager
+            rt.run(s, graph=graph)
+            cp.run(s, graph=graph)
+            sr, sc = rt.snapshot(), cp.snapshot()
+            for key in sr:
+                assert np.array_equal(sr[key], sc[key]), (s, key)
+            for l in range(L):
+                assert all(np.array_equal(a, b) for a, b in zip(rt.lists(l)[2], cp.lists(l)[2])), (s, l)
+                eo = rt.lists(l)[2][1]
+                for slot in range(S):
+                    if eo[slot] >= 0:
+                        got = d2h(rt.info[l]["slots"] + slot * rt.info[l]["record_stride"], rb, np.uint8)
+                        assert np.array_equal(got, rt.hosts[l][eo[slot], :rb]), (s, l, slot, int(eo[slot]))
+            oracle_replay_step(rt, caches, sr, prefetch_n)
+        sa = [m.moe_offload_stats(h) for h in rt.handles]
+        sb = [m.moe_offload_stats(h) for h in cp.handles]
+        assert sa == sb and all(x["error"] == 0 for x in sa)
+        assert sum(x["misses"] for x in sa) > 0
+    finally:
+        rt.close()
+        cp.close()
