@@ -222,7 +222,7 @@ __device__ __forceinline__ void widen16_fp4(uint2 q, float s, uint4& lo, uint4& 
 // 128 for down);
 // the items of a call follow the tile starts of the group descriptor (routed
 // records, then the shared expert's ceil(T / kGemmTok) tiles).  A 256-thread
-// workgroup stages kGemmK-wide K slices of its weight rows and of its gathered
+// workgroup stages 128-wide K slices of its weight rows and of its gathered
 // token rows through LDS with coalesced loads (fp8 and MXFP4 codes widened
 // exactly to bf16 on the way in), loads the next slice into registers while
 // the current one feeds bf16 MFMA 16x16x32 tiles, and each wavefront owns an
@@ -230,13 +230,14 @@ __device__ __forceinline__ void widen16_fp4(uint2 q, float s, uint4& lo, uint4& 
 // so it takes taller tiles (fewer loaded bytes per FLOP); gate/up holds two and
 // keeps 64 rows, which keeps its LDS and registers for more resident waves.
 // fp8: one scale per 128 x 128
-// block, so one per K slice and matrix, multiplies the slice's partial sum.
+// block, so one per K slice and matrix (slices are 128-aligned), multiplies
+// the slice's partial sum.
 // MFMA operands: lane l supplies row (l & 15) and the 8 K values at
 // 8 * (l >> 4) of a 32-wide K step, for A (weight rows) and B (tokens) alike;
 // the result holds rows 4 * (l >> 4) + i and token column (l & 15).
 constexpr int kGemmRowsGu = 64;       // weight rows per gate/up tile (two matrices)
 constexpr int kGemmRowsDn = 128;      // weight rows per down tile (one matrix)
-constexpr int kGemmK = 64;            // K per LDS slice
+constexpr int kGemmK = 128;           // K per LDS slice
 constexpr int kLdsRow = kGemmK + 8;   // LDS row stride in bf16: rows start on different banks
 
 struct GemmItem {
@@ -274,44 +275,48 @@ __device__ __forceinline__ int gemm_tiles(const FfnArgs& a, int nr, int* routed)
 }
 
 // one K slice of NM weight matrices (R rows each, row stride K weights) and of
-// the tile's token rows, from memory into registers.
-//   bf16:  R/32 x 16 bytes per matrix (rows tid/8 + 32q, 8 weights each);
-//   fp8:   16 codes of rows tid/4 + 64q;  MXFP4: 16 codes of rows tid/4 + 64q
-//          and their scales.
+// the tile's token rows, from memory into registers.  TW threads share a
+// weight row: bf16 8 weights (16 bytes) each, fp8 and MXFP4 16 codes each (16
+// or 8 bytes, MXFP4 with the scale of their 32-group); TB threads share a
+// token row, 8 activations each.
 template <int W, int NM, int R>
 struct Slice {
-  static constexpr int NA = W == kBf16 ? R / 32 : R / 64;
+  static constexpr int TW = W == kBf16 ? kGemmK / 8 : kGemmK / 16;  // threads per weight row
+  static constexpr int RW = 256 / TW;                                // weight rows per pass
+  static constexpr int NA = R / RW;
+  static constexpr int TB = kGemmK / 8;                              // threads per token row
+  static constexpr int RBT = 256 / TB;                               // token rows per pass
+  static constexpr int NB = kGemmTok / RBT;
   uint4 a[NA * NM];  // MXFP4 uses .x, .y
   float s[NA * NM];
-  uint4 b[2];        // token rows tid/8 and tid/8 + 32
+  uint4 b[NB];
 
   // w0: row 0 of the tile in matrix 0, matrices mat bytes apart; sr0: for
   // MXFP4, the scale bytes of row 0 of the tile in matrix 0, matrices sstride apart
   __device__ __forceinline__ void load(const uint8_t* w0, uint64_t mat, const uint8_t* sr0, uint64_t sstride, int K,
-                                       int k0, const uint16_t* const bp[2]) {
+                                       int k0, const uint16_t* const bp[NB]) {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
 #pragma unroll
       for (int q = 0; q < NA; ++q) {
+        const int row = tid / TW + RW * q;
         if (W == kBf16) {
-          a[NA * m + q] = *reinterpret_cast<const uint4*>(
-              w0 + m * mat + ((uint64_t)((tid >> 3) + 32 * q) * K + k0 + (tid & 7) * 8) * 2);
+          a[NA * m + q] =
+              *reinterpret_cast<const uint4*>(w0 + m * mat + ((uint64_t)row * K + k0 + (tid % TW) * 8) * 2);
         } else if (W == kFp8) {
-          a[NA * m + q] = *reinterpret_cast<const uint4*>(w0 + m * mat + (uint64_t)((tid >> 2) + 64 * q) * K + k0 +
-                                                           (tid & 3) * 16);
+          a[NA * m + q] = *reinterpret_cast<const uint4*>(w0 + m * mat + (uint64_t)row * K + k0 + (tid % TW) * 16);
         } else {
-          const int row = (tid >> 2) + 64 * q;
           const uint2 v =
-              *reinterpret_cast<const uint2*>(w0 + m * mat + ((uint64_t)row * K + k0) / 2 + (tid & 3) * 8);
+              *reinterpret_cast<const uint2*>(w0 + m * mat + ((uint64_t)row * K + k0) / 2 + (tid % TW) * 8);
           a[NA * m + q].x = v.x;
           a[NA * m + q].y = v.y;
-          s[NA * m + q] = e8m0_scale(sr0[m * sstride + (uint64_t)row * (K / 32) + (k0 + (tid & 3) * 16) / 32]);
+          s[NA * m + q] = e8m0_scale(sr0[m * sstride + (uint64_t)row * (K / 32) + (k0 + (tid % TW) * 16) / 32]);
         }
       }
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) b[q] = bp[q] ? *reinterpret_cast<const uint4*>(bp[q] + k0) : make_uint4(0, 0, 0, 0);
+    for (int q = 0; q < NB; ++q) b[q] = bp[q] ? *reinterpret_cast<const uint4*>(bp[q] + k0) : make_uint4(0, 0, 0, 0);
   }
 
   __device__ __forceinline__ void store(uint16_t (*As)[R][kLdsRow], uint16_t (*Bs)[kLdsRow]) const {
@@ -320,22 +325,41 @@ struct Slice {
     for (int m = 0; m < NM; ++m) {
 #pragma unroll
       for (int q = 0; q < NA; ++q) {
+        const int row = tid / TW + RW * q;
         if (W == kBf16) {
-          *reinterpret_cast<uint4*>(&As[m][(tid >> 3) + 32 * q][(tid & 7) * 8]) = a[NA * m + q];
+          *reinterpret_cast<uint4*>(&As[m][row][(tid % TW) * 8]) = a[NA * m + q];
         } else {
           uint4 lo, hi;
           if (W == kFp8) widen16(a[NA * m + q], lo, hi);
           else widen16_fp4(make_uint2(a[NA * m + q].x, a[NA * m + q].y), s[NA * m + q], lo, hi);
-          uint4* d = reinterpret_cast<uint4*>(&As[m][(tid >> 2) + 64 * q][(tid & 3) * 16]);
+          uint4* d = reinterpret_cast<uint4*>(&As[m][row][(tid % TW) * 16]);
           d[0] = lo;
           d[1] = hi;
         }
       }
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) *reinterpret_cast<uint4*>(&Bs[(tid >> 3) + 32 * q][(tid & 7) * 8]) = b[q];
+    for (int q = 0; q < NB; ++q) *reinterpret_cast<uint4*>(&Bs[tid / TB + RBT * q][(tid % TB) * 8]) = b[q];
   }
 };
+
+// token rows of the tile's pairs for Slice::load (null: past the tile's last pair)
+template <int NB>
+__device__ __forceinline__ void tile_rows(const uint16_t* base, uint64_t stride, const FfnArgs& a, const GemmItem& g,
+                                          int n_here, bool by_token, const uint16_t* bp[NB]) {
+  constexpr int TB = kGemmK / 8, RBT = 256 / TB;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < NB; ++q) {
+    const int idx = tid / TB + RBT * q;
+    if (idx < n_here) {
+      const int p = item_pair(a, g.it, g.r, g.n0 + idx);
+      bp[q] = base + (uint64_t)(by_token ? pair_token(a, p) : p) * stride + (tid % TB) * 8;
+    } else {
+      bp[q] = nullptr;
+    }
+  }
+}
 
 // acc[m][i][j] += the wavefront's (R/2) x 32 corner (row tiles i, token tiles j)
 // of matrix m over the LDS slice; SC (fp8): the slice's sum is scaled by sc[m] first
@@ -392,13 +416,8 @@ __global__ __launch_bounds__(256) void k_gemm_gu(FfnArgs a) {
   for (int item = blockIdx.x; item < ntiles * RT; item += gridDim.x) {
     const GemmItem g = gemm_item(a, nr, routed, RT, item);
     const int m0 = g.rt * R, n_here = min(kGemmTok, g.it.n - g.n0);
-    const uint16_t* bp[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int idx = (tid >> 3) + 32 * q;
-      bp[q] = idx < n_here ? x + (uint64_t)pair_token(a, item_pair(a, g.it, g.r, g.n0 + idx)) * H + (tid & 7) * 8
-                           : nullptr;
-    }
+    const uint16_t* bp[Slice<W, 2, R>::NB];
+    tile_rows<Slice<W, 2, R>::NB>(x, H, a, g, n_here, true, bp);
     const uint8_t* w0 = g.it.rec + code_bytes<W>((uint64_t)m0 * H);
     const uint8_t* sr0 = scale_row<W>(g.it.rec, mat, F, H, 0, m0, H);
     const float* sc = reinterpret_cast<const float*>(sr0);  // fp8: this row block's scales of gate
@@ -457,12 +476,8 @@ __global__ __launch_bounds__(256) void k_gemm_dn(FfnArgs a) {
   for (int item = blockIdx.x; item < ntiles * RT; item += gridDim.x) {
     const GemmItem g = gemm_item(a, nr, routed, RT, item);
     const int m0 = g.rt * R, n_here = min(kGemmTok, g.it.n - g.n0);
-    const uint16_t* bp[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int idx = (tid >> 3) + 32 * q;
-      bp[q] = idx < n_here ? hb + (uint64_t)item_pair(a, g.it, g.r, g.n0 + idx) * F + (tid & 7) * 8 : nullptr;
-    }
+    const uint16_t* bp[Slice<W, 1, R>::NB];
+    tile_rows<Slice<W, 1, R>::NB>(hb, F, a, g, n_here, false, bp);
     const uint8_t* w0 = g.it.rec + 2 * mat + code_bytes<W>((uint64_t)m0 * F);
     const uint8_t* sr0 = scale_row<W>(g.it.rec, mat, F, H, 2, m0, F);
     const float* sc = reinterpret_cast<const float*>(sr0);
