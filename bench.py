@@ -390,6 +390,8 @@ def main():
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args, handles, routers, stride, T0)
+        if args.extra:
+            result["cpu_oracle"] = cpu_oracle_rates(args)
 
     m.moe_chain_destroy(chain)
     for h in reversed(handles):
@@ -765,6 +767,67 @@ def cpu_baseline(args, handles, routers, stride, T):
             "sample": "first %d decode steps (batch %d, all %d layers) of the same token stream, from a cold cache"
                       % (steps, T, L),
             "host": host_cpu()}
+
+
+def cpu_oracle_rates(args):
+    """The oracle's own rates on the host, on all its threads and on one: the tiny fp32 layer's decode
+    tokens/s, one Qwen3-shaped layer step at batch 1 (route, ensure, copy of its misses from a cold cache,
+    FFN), the copy of 26 records into its slot arrays, and its FFN over 16 tokens x top-8."""
+    import numpy as np
+    import oracle
+    import synth
+
+    def c1():
+        E, k, Hs, Fs, S, T, steps = 8, 2, 64, 128, 4, 4, 32
+        host = synth.records(args.seed, 0, E, Hs, Fs, synth.F32)
+        wr, b = synth.router(args.seed, 0, E, Hs, synth.F32, zipf_s=1.2)
+        lay = oracle.Layer(E, S, k, Hs, Fs, oracle.F32, host, wr, b)
+        xs = synth.tokens(args.seed, 7, T, Hs, steps, 0.0, synth.F32)
+        t0 = time.time()
+        for s in range(steps):
+            lay.step(xs[s])
+        return T * steps / (time.time() - t0)
+
+    host = synth.records(args.seed, 0, E, H, F, synth.BF16)
+    rb = oracle.record_bytes(oracle.BF16, H, F)
+    wr, b = synth.router(args.seed, 0, E, H, synth.BF16, zipf_s=1.2)
+    xs = synth.tokens(args.seed, 8, 1, H, 8, 0.9, synth.BF16)
+    x16 = synth.tokens(args.seed, 9, 16, H, 1, 0.0, synth.BF16)[0]
+    ids16 = np.arange(16 * K_TOP, dtype=np.int32).reshape(16, K_TOP) % E
+    w16 = np.full((16, K_TOP), 1.0 / K_TOP)
+
+    def layer_step_ms():
+        lay = oracle.Layer(E, SLOTS, K_TOP, H, F, oracle.BF16, host, wr, b)
+        t0 = time.time()
+        for s in range(len(xs)):
+            lay.step(xs[s])
+        return (time.time() - t0) * 1e3 / len(xs)
+
+    def copy_gbps():
+        cache = oracle.Cache(E, SLOTS, host, rb)
+        pairs = np.array([[e, e] for e in range(SLOTS)], dtype=np.int32)
+        cache.copy(0, pairs)  # first touch of the slot arrays
+        t0 = time.time()
+        cache.copy(0, pairs)
+        return SLOTS * rb / (time.time() - t0) / 1e9
+
+    def ffn_gflops():
+        recs = oracle.host_records(host, ids16)
+        t0 = time.time()
+        oracle.ffn(x16, oracle.BF16, H, F, recs, w16)
+        return 6.0 * H * F * 16 * K_TOP / (time.time() - t0) / 1e9
+
+    full = oracle.threads()
+    out = {"threads": full, "host": host_cpu()}
+    for label, n in (("all_threads", full), ("one_thread", 1)):
+        oracle.set_threads(n)
+        out[label] = {"tiny_fp32_decode_tokens_per_s": round(c1(), 1),
+                      "qwen3_layer_step_b1_ms": round(layer_step_ms(), 2),
+                      "copy_26_records_GBps": round(copy_gbps(), 2),
+                      "ffn_16x8_GFLOPs": round(ffn_gflops(), 2)}
+        log("cpu oracle on %d thread(s): %s" % (n, out[label]))
+    oracle.set_threads(full)
+    return out
 
 
 def host_cpu():

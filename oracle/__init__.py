@@ -91,6 +91,8 @@ def lib():
         L.orc_rmsnorm.argtypes = [vp, i32, i32, i32, f64, vp]
         L.orc_threads.argtypes = []
         L.orc_threads.restype = i32
+        L.orc_set_threads.argtypes = [i32]
+        L.orc_set_threads.restype = None
         _lib = L
     return _lib
 
@@ -98,6 +100,11 @@ def lib():
 def threads():
     """OpenMP threads the oracle's parallel loops run on."""
     return int(lib().orc_threads())
+
+
+def set_threads(n):
+    """Run the oracle's parallel loops on n threads from now on (n < 1: all processors)."""
+    lib().orc_set_threads(int(n))
 
 
 def _p(a):

@@ -712,3 +712,6 @@ void orc_rmsnorm(const void* x, int wdt, int T, int H, double eps, void* out) {
 
 /* threads the OpenMP loops above use (for reporting how the oracle was timed) */
 int orc_threads(void) { return omp_get_max_threads(); }
+
+/* threads for the parallel loops from now on (n < 1: all the host's processors) */
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : omp_get_num_procs()); }

@@ -251,7 +251,8 @@ def test_chain_with_pinned_experts():
 def test_chain_read_through_matches_copy_kernel(wdt, shared, prefetch_n, H, F):
     """Single-token read-through (the FFN fills missed slots from the host store, no copy launch) against the
     same chain with the copy kernel: identical outputs, routing, tables and counters on every step, every
-    occupied slot byte-identical to its expert's host record, and the oracle replay on the read-through chain."""
+    occupied slot byte-identical to its expert's host record, and the oracle replay; the two chains swap
+    modes after six steps (graph dropped and captured again)."""
     L, E, S, k, T = 3, 16, 6, 4, 1
     print("chain read-through wdt=%d shared=%s prefetch=%d H=%d F=%d" % (wdt, shared, prefetch_n, H, F), flush=True)
     rt = ChainModel(L, E, S, k, H, F, wdt, T, 93, prefetch_n, shared=shared)
@@ -261,6 +262,9 @@ def test_chain_read_through_matches_copy_kernel(wdt, shared, prefetch_n, H, F):
     caches = [oracle.Cache(E, S, rt.hosts[l], rb) for l in range(L)]
     try:
         for s in range(10):
+            if s == 6:  # swap the modes mid-stream: both graphs are dropped and captured again
+                m.moe_chain_set_read_through(rt.chain, 0)
+                m.moe_chain_set_read_through(cp.chain, 1)
             graph = s % 3 != 2  # mostly graph replays, every third step eager
             rt.run(s, graph=graph)
             cp.run(s, graph=graph)
