@@ -39,3 +39,48 @@ def test_kernel_kinds_match_the_header_enum():
 
 def test_last_error_is_empty_string_initially():
     assert isinstance(m.lib().moe_offload_last_error(), bytes)
+
+
+def test_null_handles_are_rejected_before_any_device_call():
+    """Every per-handle call checks its handle first and returns EINVAL with a message; destroy
+    calls are null-safe.  No HIP call is reached, so this runs without a GPU."""
+    L = m.lib()
+    calls = {
+        "moe_route_topk": (None, None, None, None, 1, None, None, None),
+        "moe_slot_ensure": (None, None, 1, None, None),
+        "moe_copy_misses": (None, None),
+        "moe_slot_ffn": (None, None, None, None, 1, None, None, None, None, None),
+        "moe_prefill_stage": (None, None, 1, None, None, None),
+        "moe_prefetch_install": (None, None, 1, 1, None),
+        "moe_offload_pin": (None, None, 0, None),
+        "moe_copy_prefetch": (None, None),
+        "moe_offload_stats": (None, None),
+        "moe_offload_reset": (None, None),
+        "moe_offload_query": (None, None),
+        "moe_offload_profile": (None, 1),
+        "moe_offload_kernel_times": (None, None),
+        "moe_offload_host_records": (None, None, None, None),
+        "moe_chain_run": (None, None),
+        "moe_chain_run_eager": (None, None),
+        "moe_chain_set_read_through": (None, 1),
+        "moe_chain_get_buffers": (None, None),
+    }
+    for name, args in calls.items():
+        rc = getattr(L, name)(*args)
+        assert rc == m.EINVAL, (name, rc)
+        assert L.moe_offload_last_error(), name
+    assert L.moe_offload_create(None, None) == m.EINVAL
+    assert b"null" in L.moe_offload_last_error()
+    assert L.moe_chain_create(None, 0, None, None, None, 1, 0, None) == m.EINVAL
+    assert L.moe_rmsnorm(None, None, 1, 64, m.BF16, 1e-6, None) == m.EINVAL
+    L.moe_offload_destroy(None)
+    L.moe_chain_destroy(None)
+
+
+def test_rmsnorm_rejects_bad_sizes_without_a_device():
+    import numpy as np
+    L = m.lib()
+    buf = np.zeros(64, np.float32)
+    p = buf.ctypes.data
+    for T, H, eps in ((0, 64, 1e-6), (1, 60, 1e-6), (1, 4, 1e-6), (1, 64, 0.0), (1, 64, -1.0)):
+        assert L.moe_rmsnorm(p, p, T, H, m.F32, eps, None) == m.EINVAL, (T, H, eps)

@@ -326,6 +326,50 @@ def test_create_rejects_bad_shapes():
     assert ei.value.code == m.EINVAL
 
 
+def test_calls_reject_bad_sizes_and_null_pointers():
+    """Call-level argument checks on a live handle: T outside [1, max_tokens], null tensors and
+    install budgets outside [0, S] return EINVAL with a message and leave the state untouched."""
+    E, S, k, H, F, maxT = 8, 4, 2, 128, 128, 4
+    print("case call-level argument checks", flush=True)
+    h = m.moe_offload_create(E, S, H, F, k, m.BF16, maxT)
+    try:
+        dev = torch.device("cuda", 0)
+        x = torch.zeros((maxT + 1, H), dtype=torch.bfloat16, device=dev)
+        wr = torch.zeros((E, H), dtype=torch.bfloat16, device=dev)
+        b = torch.zeros(E, dtype=torch.float32, device=dev)
+        ids = torch.zeros((maxT + 1, k), dtype=torch.int32, device=dev)
+        w = torch.zeros((maxT + 1, k), dtype=torch.float32, device=dev)
+        sid = torch.zeros_like(ids)
+        y = torch.zeros_like(x)
+        for T in (0, -1, maxT + 1):
+            for call in (lambda: m.moe_route_topk(h, x, wr, b, T, ids, w),
+                         lambda: m.moe_slot_ensure(h, ids, T, sid),
+                         lambda: m.moe_slot_ffn(h, x, sid, w, T, None, y),
+                         lambda: m.moe_prefill_stage(h, ids, T, sid),
+                         lambda: m.moe_prefetch_install(h, ids, T, 1)):
+                with pytest.raises(m.MoeError) as ei:
+                    call()
+                assert ei.value.code == m.EINVAL and "T=" in str(ei.value), (T, str(ei.value))
+        for call in (lambda: m.moe_route_topk(h, None, wr, b, 1, ids, w),
+                     lambda: m.moe_route_topk(h, x, wr, None, 1, ids, w),
+                     lambda: m.moe_slot_ensure(h, ids, 1, None),
+                     lambda: m.moe_slot_ffn(h, x, sid, w, 1, None, None),
+                     lambda: m.moe_prefill_stage(h, None, 1, sid),
+                     lambda: m.moe_prefetch_install(h, None, 1, 1)):
+            with pytest.raises(m.MoeError) as ei:
+                call()
+            assert ei.value.code == m.EINVAL and "null" in str(ei.value)
+        for n in (-1, S + 1):
+            with pytest.raises(m.MoeError) as ei:
+                m.moe_prefetch_install(h, ids, 1, n)
+            assert ei.value.code == m.EINVAL
+        torch.cuda.synchronize()
+        st = m.moe_offload_stats(h)
+        assert st["calls"] == 0 and st["resident"] == 0 and st["error"] == 0, st
+    finally:
+        m.moe_offload_destroy(h)
+
+
 def test_graph_replay_matches_eager():
     """Two layers captured once in a HIP graph (via torch.cuda.graph) and replayed."""
     E, S, k, H, F, wdt, T = 16, 6, 4, 256, 256, 1, 3
