@@ -1055,27 +1055,11 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(FfnArgs a, void* __rest
   const void* __restrict__ rrow = (const uint8_t*)a.residual + roff;
   float ss = 0.f;
   for (int c = threadIdx.x; c * 8 < H; c += kRowThreads) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int j = 0; j < k; ++j) {
-      const float wj = wt[j];
-      const float4* pr = reinterpret_cast<const float4*>(part + (uint64_t)(t * k + j) * H + c * 8);
-      const float4 p0 = pr[0], p1 = pr[1];
-      acc[0] = __builtin_fmaf(wj, p0.x, acc[0]); acc[1] = __builtin_fmaf(wj, p0.y, acc[1]);
-      acc[2] = __builtin_fmaf(wj, p0.z, acc[2]); acc[3] = __builtin_fmaf(wj, p0.w, acc[3]);
-      acc[4] = __builtin_fmaf(wj, p1.x, acc[4]); acc[5] = __builtin_fmaf(wj, p1.y, acc[5]);
-      acc[6] = __builtin_fmaf(wj, p1.z, acc[6]); acc[7] = __builtin_fmaf(wj, p1.w, acc[7]);
-    }
-    if (a.shared) {
-      const float4* pr = reinterpret_cast<const float4*>(part + (uint64_t)(routed + t) * H + c * 8);
-      const float4 p0 = pr[0], p1 = pr[1];
-      acc[0] = acc[0] + p0.x; acc[1] = acc[1] + p0.y; acc[2] = acc[2] + p0.z; acc[3] = acc[3] + p0.w;
-      acc[4] = acc[4] + p1.x; acc[5] = acc[5] + p1.y; acc[6] = acc[6] + p1.z; acc[7] = acc[7] + p1.w;
-    }
+    float acc[8], res[8];
+    combine_chunk<F32>(part + (uint64_t)t * k * H, wt, k, H, c, a.shared ? part + (uint64_t)(routed + t) * H : nullptr,
+                       xrow ? rrow : nullptr, acc, res);
     chunk_store<F32>(yrow, c, acc);  // acc now holds y as stored
     if (xrow) {
-      float res[8];
-      chunk_load<F32>(rrow, c, res);
 #pragma unroll
       for (int q = 0; q < 8; ++q) res[q] = res[q] + acc[q];
       chunk_store<F32>(xrow, c, res);  // res now holds x_next as stored

@@ -126,25 +126,10 @@ __global__ __launch_bounds__(kRowThreads) void k_combine_logits(CombineSrc cb, R
   for (int q = 0; q < kRowChunks; ++q) {
     const int c = tid + kRowThreads * q;
     if (c * 8 < H) {
-      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int jj = 0; jj < k; ++jj) {
-        const float wj = cb.w[(size_t)t * k + jj];
-        const float4* pr = reinterpret_cast<const float4*>(cb.part + (uint64_t)(t * k + jj) * H + c * 8);
-        const float4 p0 = pr[0], p1 = pr[1];
-        acc[0] = __builtin_fmaf(wj, p0.x, acc[0]); acc[1] = __builtin_fmaf(wj, p0.y, acc[1]);
-        acc[2] = __builtin_fmaf(wj, p0.z, acc[2]); acc[3] = __builtin_fmaf(wj, p0.w, acc[3]);
-        acc[4] = __builtin_fmaf(wj, p1.x, acc[4]); acc[5] = __builtin_fmaf(wj, p1.y, acc[5]);
-        acc[6] = __builtin_fmaf(wj, p1.z, acc[6]); acc[7] = __builtin_fmaf(wj, p1.w, acc[7]);
-      }
-      if (cb.shared) {
-        const float4* pr = reinterpret_cast<const float4*>(cb.part + (uint64_t)(routed + t) * H + c * 8);
-        const float4 p0 = pr[0], p1 = pr[1];
-        acc[0] = acc[0] + p0.x; acc[1] = acc[1] + p0.y; acc[2] = acc[2] + p0.z; acc[3] = acc[3] + p0.w;
-        acc[4] = acc[4] + p1.x; acc[5] = acc[5] + p1.y; acc[6] = acc[6] + p1.z; acc[7] = acc[7] + p1.w;
-      }
+      float acc[8], res[8];
+      combine_chunk<false>(cb.part + (uint64_t)t * k * H, cb.w + (size_t)t * k, k, H, c,
+                           cb.shared ? cb.part + (uint64_t)(routed + t) * H : nullptr, rrow, acc, res);
       chunk_store<false>(yrow, c, acc);  // acc now holds y as stored
-      float res[8];
-      chunk_load<false>(rrow, c, res);
 #pragma unroll
       for (int qq = 0; qq < 8; ++qq) xv[q][qq] = res[qq] + acc[qq];
       chunk_store<false>(xrow, c, xv[q]);  // x_next as stored

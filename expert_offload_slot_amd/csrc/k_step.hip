@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kBlock) void k_decide(CacheDev c, const float* __re
   __shared__ int rec_l[kDecideMaxPairs];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n = T * k;
-  load_table(c, t);  // its loads are in flight while the top-k reads the logits
+  const TableRegs tr = fetch_table(c);  // in flight while the top-k reads the logits
   for (int tok = wv; tok < T; tok += kWaves) {
     int id;
     float wt;
@@ -58,6 +58,7 @@ __global__ __launch_bounds__(kBlock) void k_decide(CacheDev c, const float* __re
       ids_l[tok * k + lane] = id;
     }
   }
+  put_table(c, tr, t);
   __syncthreads();
   ensure_body(c, t, ids_l, n, k, slot_ids, rec_l, audit, u.keys);
   __syncthreads();

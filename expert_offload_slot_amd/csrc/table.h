@@ -41,13 +41,38 @@ struct SharedTable {
   uint64_t cnt[C_N];       // the counters as loaded
 };
 
-// Loads the table into LDS.  Entries outside their range (only possible if
-// the table was overwritten from outside) are dropped and flagged, so every
+// The table as one thread holds it between fetch_table and put_table.
+struct TableRegs {
+  int s = -1, e = -1, pin = 0;
+  uint32_t sc = 0u;
+  uint64_t lu = 0ull, tc = 0ull;
+};
+
+// Issues this thread's loads of the table (slot_of, the slot entries, and in the
+// last wavefront the call counter and the statistics) without waiting for them,
+// so a caller can start other loads before put_table consumes the values.
+__device__ __forceinline__ TableRegs fetch_table(const CacheDev& c) {
+  const int tid = threadIdx.x, u = tid - 64 * (kWaves - 1);
+  TableRegs r;
+  if (tid < c.E) r.s = c.slot_of[tid];
+  if (tid < c.S) {
+    r.e = c.expert_of[tid];
+    r.lu = c.last_use[tid];
+    r.sc = c.score[tid];
+    r.pin = c.pinned[tid];
+  }
+  if (u == 0) r.tc = *c.tick;
+  if (u >= 1 && u <= C_N) r.tc = c.counters[u - 1];
+  return r;
+}
+
+// Writes the fetched table to LDS.  Entries outside their range (only possible
+// if the table was overwritten from outside) are dropped and flagged, so every
 // later index stays in bounds.
-__device__ __forceinline__ void load_table(const CacheDev& c, SharedTable& t) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void put_table(const CacheDev& c, const TableRegs& r, SharedTable& t) {
+  const int tid = threadIdx.x, u = tid - 64 * (kWaves - 1);
   if (tid < c.E) {
-    int s = c.slot_of[tid];
+    int s = r.s;
     if (s < -1 || s >= c.S) {
       atomicOr(c.err, MOE_DEV_ERR_AUDIT);
       s = -1;
@@ -55,21 +80,22 @@ __device__ __forceinline__ void load_table(const CacheDev& c, SharedTable& t) {
     t.slot_of[tid] = s;
   }
   if (tid < c.S) {
-    int e = c.expert_of[tid];
+    int e = r.e;
     if (e < -1 || e >= c.E) {
       atomicOr(c.err, MOE_DEV_ERR_AUDIT);
       e = -1;
     }
     t.expert_of[tid] = e;
-    t.last_use[tid] = c.last_use[tid];
-    t.score[tid] = c.score[tid];
-    t.pinned[tid] = c.pinned[tid];
+    t.last_use[tid] = r.lu;
+    t.score[tid] = r.sc;
+    t.pinned[tid] = r.pin;
   }
-  // the call counter and the statistics, from another wavefront
-  const int u = tid - 64 * (kWaves - 1);
-  if (u == 0) t.tick = *c.tick;
-  if (u >= 1 && u <= C_N) t.cnt[u - 1] = c.counters[u - 1];
+  if (u == 0) t.tick = r.tc;
+  if (u >= 1 && u <= C_N) t.cnt[u - 1] = r.tc;
 }
+
+// Loads the table into LDS (fetch_table, then put_table).
+__device__ __forceinline__ void load_table(const CacheDev& c, SharedTable& t) { put_table(c, fetch_table(c), t); }
 
 __device__ __forceinline__ void store_table(const CacheDev& c, const SharedTable& t) {
   const int tid = threadIdx.x;

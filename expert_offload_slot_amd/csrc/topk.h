@@ -59,12 +59,14 @@ __device__ __forceinline__ bool wave_topk(const float* __restrict__ l, int E, in
   const uint64_t below = (1ull << lane) - 1ull;
   uint32_t key[J];
   bool nan = false;
+  float lv[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) lv[j] = lane + 64 * j < E ? l[lane + 64 * j] : 0.f;  // every load issued first
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    const int e = lane + 64 * j;
     key[j] = 0;  // below every real key (-inf maps to 0x007fffff)
-    if (e < E) {
-      float v = l[e];
+    if (lane + 64 * j < E) {
+      float v = lv[j];
       if (v != v) {
         nan = true;
         v = -INFINITY;
