@@ -841,9 +841,29 @@ __global__ __launch_bounds__(256) void k_down_vec(FfnArgs a) {
 // per-lane order and the same 16-lane pairing tree as the kernels above, so the
 // same bits; the code is a few hundred instructions instead of the 8-token
 // unrolled body, which every layer's launch fetches cold.
-__device__ __forceinline__ const uint8_t* one_record(const FfnArgs& a, int j) {
+//
+// The call's record indices and the head of its copy list, one entry per lane,
+// requested by every wavefront in its first load: lane j < k holds slot_ids[j];
+// with read-through, lane i < 2 + 2k holds entry i of the copy list {mode,
+// count, (expert, record)...}, which a single token's at most k misses fit.
+// The work items read them from those lanes (a wavefront-uniform index), so
+// the weight stream waits for one memory round trip instead of one per entry.
+struct OneHead {
+  int sid = 0, lst = 0;
+};
+
+__device__ __forceinline__ OneHead one_head(const FfnArgs& a, bool fill) {
+  const int lane = threadIdx.x & 63;
+  OneHead o;
+  if (lane < a.k) o.sid = a.slot_ids[lane];
+  if (fill && lane < 2 + 2 * a.k) o.lst = a.fill_list[lane];
+  return o;
+}
+
+// record of choice j (j = k: the shared expert); j is wavefront-uniform
+__device__ __forceinline__ const uint8_t* one_record(const FfnArgs& a, int j, const OneHead& o) {
   if (j == a.k) return a.shared;
-  int ri = a.slot_ids[j];
+  int ri = __builtin_amdgcn_readlane(o.sid, j);
   if ((unsigned)ri >= (unsigned)(a.S + a.E)) {
     atomicOr(a.err, MOE_DEV_ERR_AUDIT);
     ri = 0;
@@ -858,15 +878,15 @@ __device__ __forceinline__ const uint8_t* one_record(const FfnArgs& a, int j) {
 // the gate and up matrices and their scales, the down launch the rest, so at
 // the end of the call the slot holds the whole record, as after the copy
 // kernel.  Returns e's host record, or null when j reads its record in place.
-__device__ __forceinline__ const uint8_t* fill_source(const FfnArgs& a, int j) {
+// j is wavefront-uniform, so the entries are read from their lanes as scalars.
+__device__ __forceinline__ const uint8_t* fill_source(const FfnArgs& a, int j, const OneHead& o) {
   if (j == a.k) return nullptr;  // the shared expert is device resident
-  const int32_t* __restrict__ lst = a.fill_list;
-  if (lst[0] == MOE_MODE_STAGED_ALL) return nullptr;
-  const int n = min(lst[1], a.k);  // a single token has at most k misses
-  const int r = a.slot_ids[j];
+  if (__builtin_amdgcn_readlane(o.lst, 0) == MOE_MODE_STAGED_ALL) return nullptr;
+  const int n = min(__builtin_amdgcn_readlane(o.lst, 1), a.k);  // a single token has at most k misses
+  const int r = __builtin_amdgcn_readlane(o.sid, j);
   for (int m = 0; m < n; ++m) {
-    if (lst[3 + 2 * m] != r) continue;
-    const int e = lst[2 + 2 * m];
+    if (__builtin_amdgcn_readlane(o.lst, 3 + 2 * m) != r) continue;
+    const int e = __builtin_amdgcn_readlane(o.lst, 2 + 2 * m);
     if ((unsigned)e >= (unsigned)a.E) {
       atomicOr(a.err, MOE_DEV_ERR_AUDIT);
       return nullptr;
@@ -886,13 +906,14 @@ __global__ __launch_bounds__(256) void k_gateup_one(FfnArgs a) {
   const int items = (a.k + (a.shared ? 1 : 0)) * RG;
   const uint16_t* __restrict__ x = (const uint16_t*)a.x;
   uint16_t* __restrict__ hb = (uint16_t*)a.hbuf;
+  const OneHead o = one_head(a, FILL);
   for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < items; item += gridDim.x * 4) {
     const int j = item / RG, f = (item % RG) * 4 + q;
-    const uint8_t* rec = one_record(a, j);
+    const uint8_t* rec = one_record(a, j, o);
     float g = 0.f, up = 0.f;
     bool done = false;
     if constexpr (FILL) {
-      if (const uint8_t* src = fill_source(a, j)) {  // uniform per wavefront
+      if (const uint8_t* src = fill_source(a, j, o)) {  // uniform per wavefront
         uint8_t* dst = const_cast<uint8_t*>(rec);
         Fill fl;
         fl.w0 = dst + code_bytes<W>((uint64_t)f * H);
@@ -927,13 +948,14 @@ __global__ __launch_bounds__(256) void k_down_one(FfnArgs a) {
   const int items = (a.k + (a.shared ? 1 : 0)) * RG;
   const uint16_t* __restrict__ hb = (const uint16_t*)a.hbuf;
   float* __restrict__ part = a.part;
+  const OneHead o = one_head(a, FILL);
   for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < items; item += gridDim.x * 4) {
     const int j = item / RG, h0 = (item % RG) * 8 + q;
-    const uint8_t* rec = one_record(a, j);
+    const uint8_t* rec = one_record(a, j, o);
     float s0 = 0.f, s1 = 0.f;
     bool done = false;
     if constexpr (FILL) {
-      if (const uint8_t* src = fill_source(a, j)) {  // uniform per wavefront
+      if (const uint8_t* src = fill_source(a, j, o)) {  // uniform per wavefront
         uint8_t* dst = const_cast<uint8_t*>(rec);
         Fill fl;
         fl.w0 = dst + 2 * mat + code_bytes<W>((uint64_t)h0 * F);

@@ -63,6 +63,7 @@ __global__ __launch_bounds__(256) void k_logits(const A* __restrict__ x, RouterJ
   const int t0 = blockIdx.y * kRouteTokens;
   const int nt = min(kRouteTokens, T - t0);
   if (e >= j.E) return;
+  const float be = j.bias[e];  // requested with the first loads, not after the sum
   float acc[kRouteTokens] = {0.f, 0.f, 0.f, 0.f};
   const A* wrow = j.wr + (size_t)e * H;
 #pragma unroll 4
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(256) void k_logits(const A* __restrict__ x, RouterJ
     float p = acc[tt];
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) p = p + __shfl_xor(p, o);
-    if (lane == 0 && tt < nt) j.logits[(size_t)(t0 + tt) * j.E + e] = p + j.bias[e];
+    if (lane == 0 && tt < nt) j.logits[(size_t)(t0 + tt) * j.E + e] = p + be;
   }
 }
 
@@ -108,6 +109,7 @@ __global__ __launch_bounds__(kRowThreads) void k_combine_logits(CombineSrc cb, R
   const bool ev = e < j.E;
   const bool lead = blockIdx.x == 0 && blockIdx.z == 0;
   uint4 wr[kRouterChunks];
+  const float be = ev ? j.bias[e] : 0.f;  // requested with the router rows, not after the sum
 #pragma unroll
   for (int i = 0; i < kRouterChunks; ++i) {
     const int c = lane + 64 * i;
@@ -166,7 +168,7 @@ __global__ __launch_bounds__(kRowThreads) void k_combine_logits(CombineSrc cb, R
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) acc = acc + __shfl_xor(acc, o);
-  if (lane == 0) j.logits[(size_t)t * j.E + e] = acc + j.bias[e];
+  if (lane == 0) j.logits[(size_t)t * j.E + e] = acc + be;
 }
 
 // Top-k (topk.h): one wavefront per token, 4 tokens per workgroup.
