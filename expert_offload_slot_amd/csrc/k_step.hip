@@ -43,6 +43,7 @@ __global__ __launch_bounds__(kBlock) void k_decide(CacheDev c, const float* __re
     uint64_t keys[kDecideKeys];
   } u;
   __shared__ int ids_l[kDecideMaxPairs];
+  __shared__ float w_l[kDecideMaxPairs];
   __shared__ int rec_l[kDecideMaxPairs];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n = T * k;
@@ -53,16 +54,22 @@ __global__ __launch_bounds__(kBlock) void k_decide(CacheDev c, const float* __re
     const bool nan = wave_topk<J>(logits + (size_t)tok * c.E, c.E, k, u.tk[wv], &id, &wt);
     if (nan && lane == 0) atomicOr(c.err, MOE_DEV_ERR_NAN);
     if (lane < k) {
-      ids[(size_t)tok * k + lane] = id;
-      w[(size_t)tok * k + lane] = wt;
       ids_l[tok * k + lane] = id;
+      w_l[tok * k + lane] = wt;
     }
   }
+  // the table's values before any global store (the wait for a load also
+  // waits for the stores issued before it); the top-k results are written
+  // out after the ensure for the same reason
   put_table(c, tr, t);
   __syncthreads();
   ensure_body(c, t, ids_l, n, k, slot_ids, rec_l, audit, u.keys);
   __syncthreads();
   if (do_group) group_body(rec_l, n, c.S + c.E, grp, off_pairs, off_tiles, c.err, u.g);
+  for (int i = threadIdx.x; i < n; i += kBlock) {
+    ids[i] = ids_l[i];
+    w[i] = w_l[i];
+  }
   if (max_n <= 0) return;  // uniform
   // lookahead: the next layer's router on this layer's input predicts its experts;
   // up to max_n of them are installed into the next layer's table
