@@ -326,6 +326,20 @@ def test_create_rejects_bad_shapes():
     assert ei.value.code == m.EINVAL
 
 
+@pytest.mark.parametrize("wdt,zipf", [(1, 0.0), (2, 1.2)])
+def test_maximum_experts_and_top_k(wdt, zipf):
+    """The largest expert count and top-k the library accepts (1024 experts, top-16), 96 slots,
+    bf16 records under a uniform router (calls wider than the cache) and fp8 records with the
+    shared expert under a Zipf-skewed router (mostly hits): single tokens (one work item per
+    choice), decode batches, 512 pairs (the control workgroup's limit) and a call of 65 tokens
+    (1040 pairs, the grouped GEMM), every call against the oracle."""
+    modes, err = run_sequence(1024, 96, 16, 256, 256, wdt, zipf, 95 + wdt, 8, [1, 8, 32, 65],
+                              shared=(wdt == 2))
+    if zipf == 0.0:
+        assert max(modes) >= 1  # some calls wider than the cache
+    assert err <= 2e-2
+
+
 def test_calls_reject_bad_sizes_and_null_pointers():
     """Call-level argument checks on a live handle: T outside [1, max_tokens], null tensors and
     install budgets outside [0, S] return EINVAL with a message and leave the state untouched."""
