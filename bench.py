@@ -20,9 +20,12 @@ Also measured in the same run:
   * the host link: SDMA copy of 1 GiB pinned memory and the copy kernel over
     128 records;
   * the CPU oracle on a bounded sample of the same workload.
---extra adds batch 8 and 32, the router-lookahead prefetch comparison, the
-Mixtral-8x7B-shaped layer at 2/4/6 slots and the DeepSeek-V3-shaped fp8 layer
-(decode at batch 16, the 2048-token prefill: staging copy and FFN TFLOP/s).
+--extra adds batch 8 and 32, the router-lookahead prefetch comparison, LRU
+against scored eviction and pinned placement, decode at 10/20/40/100 % slots
+(outputs bitwise identical at every fraction), the CPU oracle's own rates, the
+MXFP4 records, the Mixtral-8x7B-shaped layer at 2/4/6 slots and the
+DeepSeek-V3-shaped fp8 layer (decode at batch 16, the 2048-token prefill:
+staging copy and FFN TFLOP/s).
 """
 import argparse
 import ctypes
@@ -387,6 +390,7 @@ def main():
             m.moe_chain_destroy(c2)
         result["prefetch"] = prefetch_compare(args, m, hip, handles, run_decode, token_stream)
         result["eviction"] = eviction_compare(args, m, hip, torch, handles, wr_d, b_d, run_decode, token_stream)
+        result["slot_fractions"] = slot_fraction_compare(args, m, hip, handles, run_decode, token_stream)
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args, handles, routers, stride, T0)
@@ -668,6 +672,37 @@ def prefetch_compare(args, m, hip, handles, run_decode, token_stream):
                                   "prefetch_hits_per_token": round(d["prefetch_hits"] / (T * steps), 4)}
         m.moe_chain_destroy(c)
     out["outputs_identical"] = bool(np.array_equal(last[0], last[4]))
+    return out
+
+
+def slot_fraction_compare(args, m, hip, handles, run_decode, token_stream):
+    """Decode at batch 1 with 10, 20, 40 and 100 % of each layer's experts in slots (13, 26, 52, 128 of 128),
+    each from an empty cache on the same token stream; the other fractions' layers share the 20 % layers' host
+    stores.  Every layer's output of the last step must be bitwise identical at every fraction."""
+    import numpy as np
+    T, warm, steps = 1, 16, 128
+    xs_d = token_stream(T, warm + steps + args.prof_steps)
+    out, last = {}, {}
+    for S in (13, SLOTS, 52, E):
+        hs = handles if S == SLOTS else [m.moe_offload_create(E, S, H, F, K_TOP, m.BF16, 32, 0, 0, h, handles[0])
+                                         for h in handles]
+        try:
+            for h in hs:
+                m.moe_offload_reset(h)
+            ts, msps, d, c, bufs, _ = run_decode(T, warm, steps, "slots-%d" % S, xs_d=xs_d, hs=hs)
+            xl = np.empty((len(hs) + 1, T, H), dtype=np.uint16)  # every layer's input stream x[0..L]
+            assert hip.hipMemcpy(xl.ctypes.data, bufs["x"], xl.nbytes, 2) == 0
+            last[S] = xl
+            out["slots_%d" % S] = {"slot_fraction": round(S / E, 4), "tokens_per_s": round(ts, 2),
+                                   "ms_per_step": round(msps, 3),
+                                   "misses_per_token": round(d["misses"] / (T * steps), 4)}
+            m.moe_chain_destroy(c)
+        finally:
+            if hs is not handles:
+                for h in reversed(hs):
+                    m.moe_offload_destroy(h)
+    out["outputs_identical"] = bool(all(np.array_equal(last[S], last[SLOTS]) for S in last))
+    assert out["outputs_identical"], "outputs differ between slot fractions"
     return out
 
 
