@@ -340,6 +340,18 @@ def test_maximum_experts_and_top_k(wdt, zipf):
     assert err <= 2e-2
 
 
+@pytest.mark.parametrize("wdt,S,zipf", [(0, 1, 0.0), (1, 1, 0.0), (1, 8, 1.2), (2, 2, 0.0)])
+def test_degenerate_top1_and_slot_counts(wdt, S, zipf):
+    """Top-1 routing (every weight exactly 1) with a single slot under a uniform router (calls
+    touching two experts are wider than the cache), with every expert resident (S = E), and fp8
+    records with two slots; fp32, bf16 and fp8, batches 1 to 5, every call against the oracle."""
+    modes, err = run_sequence(8, S, 1, 128, 256, wdt, zipf, 120 + 10 * wdt + S, 12, [1, 2, 5],
+                              shared=(wdt == 2))
+    if S == 1:
+        assert max(modes) >= 1
+    assert err <= (1e-5 if wdt == 0 else 2e-2)
+
+
 def test_calls_reject_bad_sizes_and_null_pointers():
     """Call-level argument checks on a live handle: T outside [1, max_tokens], null tensors and
     install budgets outside [0, S] return EINVAL with a message and leave the state untouched."""
