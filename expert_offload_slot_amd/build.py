@@ -16,6 +16,9 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # the router's binary32 order is part of its definition: no contraction, no denormal flushing
     "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
+    # MFMA accumulators in ordinary VGPRs: the prefill GEMM's per-slice fp8 scaling then needs no
+    # accumulator-register moves (gate/up 2.88 -> 2.79 ms, down 1.53 -> 1.49 ms, same bits)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 
