@@ -696,6 +696,45 @@ __device__ __forceinline__ void vec_pass(const uint8_t* row0, const uint8_t* row
   }
 }
 
+// vec_pass reading a missed record from the host store: every chunk and owned
+// scale read is also stored to fl (the same bytes the copy kernel would move),
+// raw scale bits held for the stores.  Same per-lane order as vec_pass, so the
+// same bits.
+template <int W, int CH>
+__device__ __forceinline__ void vec_pass_fill(const uint8_t* row0, const uint8_t* row1, const uint8_t* sr0,
+                                              const uint8_t* sr1, int nk, int c, const uint16_t* const act[kVecTok],
+                                              int nt, float acc[kVecTok][2], const Fill& fl) {
+  for (int k0 = 0; k0 < nk; k0 += CH) {
+    typename WChunk<W>::T w0[CH], w1[CH];
+    uint32_t s0[CH], s1[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      w0[i] = load_w<W>(row0, k0 + i, c);
+      w1[i] = load_w<W>(row1, k0 + i, c);
+      s0[i] = load_sr<W>(sr0, k0 + i, c);
+      s1[i] = load_sr<W>(sr1, k0 + i, c);
+    }
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      store_w<W>(fl.w0, k0 + i, c, w0[i]);
+      store_w<W>(fl.w1, k0 + i, c, w1[i]);
+      if (fl.own0) store_sr<W>(fl.s0, k0 + i, c, s0[i]);
+      if (fl.own1) store_sr<W>(fl.s1, k0 + i, c, s1[i]);
+    }
+#pragma unroll
+    for (int t = 0; t < kVecTok; ++t) {
+      if (t < nt) {
+        const uint4* xr = reinterpret_cast<const uint4*>(act[t]);
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+          acc[t][0] = wdot<W>(w0[i], xr, k0 + i, c, acc[t][0], scale_of<W>(s0[i]));
+          acc[t][1] = wdot<W>(w1[i], xr, k0 + i, c, acc[t][1], scale_of<W>(s1[i]));
+        }
+      }
+    }
+  }
+}
+
 // vec_pass for one activation row: each pass one unbroken run of loads, then
 // the pair dots.  Same per-lane order as vec_pass, so the same bits.  With
 // FILL every chunk and owned scale read is also stored to fl (the read-through
@@ -743,9 +782,52 @@ inline int one_chunks(int nk) {
 template <int CH>
 constexpr int kFillChunks = CH >= 8 ? CH / 2 : CH;
 
+// Read-through for 2 to kVecTok tokens (at most 64 pairs): the copy list
+// {mode, count, (expert, record)...} of the call, loaded once per wavefront in
+// one round trip, lane l holding pair l.  A work item whose record index is in
+// the list reads that expert's host record and stores every byte it reads into
+// the record (slot, or staging for the overflow of a call wider than the
+// cache), as the copy kernel would have; with at most kVecTok tokens a record's
+// tokens meet its weights in one pass, so each byte crosses the link once.
+struct VecHead {
+  int mode = 0, n = 0, e = 0, r = -1;
+};
+
+__device__ __forceinline__ VecHead vec_head(const FfnArgs& a, bool fill) {
+  const int lane = threadIdx.x & 63;
+  VecHead v;
+  if (!fill) return v;
+  const int32_t* __restrict__ lst = a.fill_list;
+  v.mode = lst[0];
+  v.n = lst[1];
+  if (lane < min(64, max(a.S, a.E))) {  // the list holds max(S, E) pairs
+    v.e = lst[2 + 2 * lane];
+    v.r = lst[3 + 2 * lane];
+  }
+  return v;
+}
+
+// host record that work item record index ri reads through, or null; ri is
+// wavefront-uniform
+__device__ __forceinline__ const uint8_t* vec_source(const FfnArgs& a, const VecHead& v, int ri) {
+  const int lane = threadIdx.x & 63;
+  if (v.mode == MOE_MODE_STAGED_ALL) return nullptr;
+  const uint64_t hit = __ballot(lane < min(v.n, 64) && v.r == ri);
+  if (!hit) return nullptr;
+  const int e = __builtin_amdgcn_readlane(v.e, __builtin_ctzll(hit));
+  if ((unsigned)e >= (unsigned)a.E) {
+    atomicOr(a.err, MOE_DEV_ERR_AUDIT);
+    return nullptr;
+  }
+  return a.host + (uint64_t)e * a.stride;
+}
+
+// record index of grouped record block r (r < max_routed)
+__device__ __forceinline__ int block_record(const FfnArgs& a, int r) { return a.grp[kRecWords * (1 + r)]; }
+
 // gate/up: work item = (record, 4 rows of F); quarter q takes row f = 4*g + q of
 // gate (stream 0) and up (stream 1); h = silu(gate) * up stored in bf16.
-template <int W, int CH>
+template <int W, int CH, bool FILL>
 __global__ __launch_bounds__(256) void k_gateup_vec(FfnArgs a) {
   const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
   const int nrt = a.max_routed + (a.shared ? 1 : 0);
@@ -756,13 +838,16 @@ __global__ __launch_bounds__(256) void k_gateup_vec(FfnArgs a) {
   const uint16_t* __restrict__ x = (const uint16_t*)a.x;
   uint16_t* __restrict__ hb = (uint16_t*)a.hbuf;
   const int nwave = gridDim.x * 4;
+  const VecHead vh = vec_head(a, FILL);
   for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < nrt * RG; item += nwave) {
     const int r = item / RG, fg = (item % RG) * 4, f = fg + q;
     const Item it = item_block(a, r);
     if (it.n == 0) continue;
-    const uint8_t* wg = it.rec + code_bytes<W>((uint64_t)f * H);
-    const uint8_t* sg = scale_row<W>(it.rec, mat, F, H, 0, f, H);
-    const uint8_t* su = scale_row<W>(it.rec, mat, F, H, 1, f, H);
+    const uint8_t* src = FILL && !it.sh ? vec_source(a, vh, block_record(a, r)) : nullptr;
+    const uint8_t* rd = src ? src : it.rec;
+    const uint8_t* wg = rd + code_bytes<W>((uint64_t)f * H);
+    const uint8_t* sg = scale_row<W>(rd, mat, F, H, 0, f, H);
+    const uint8_t* su = scale_row<W>(rd, mat, F, H, 1, f, H);
     for (int tg = 0; tg < it.n; tg += kVecTok) {
       const int nt = min(kVecTok, it.n - tg);
       const uint16_t* act[kVecTok];
@@ -772,7 +857,18 @@ __global__ __launch_bounds__(256) void k_gateup_vec(FfnArgs a) {
       float acc[kVecTok][2];
 #pragma unroll
       for (int t = 0; t < kVecTok; ++t) acc[t][0] = acc[t][1] = 0.f;
-      vec_pass<W, CH>(wg, wg + mat, sg, su, nk, c, act, nt, acc);
+      if (FILL && src) {  // uniform per wavefront; one token group (it.n <= kVecTok)
+        uint8_t* dst = const_cast<uint8_t*>(it.rec);
+        Fill fl;
+        fl.w0 = dst + code_bytes<W>((uint64_t)f * H);
+        fl.w1 = fl.w0 + mat;
+        fl.s0 = const_cast<uint8_t*>(scale_row<W>(dst, mat, F, H, 0, f, H));
+        fl.s1 = const_cast<uint8_t*>(scale_row<W>(dst, mat, F, H, 1, f, H));
+        fl.own0 = fl.own1 = W == kMx4 || (f & 127) == 0;
+        vec_pass_fill<W, kFillChunks<CH>>(wg, wg + mat, sg, su, nk, c, act, nt, acc, fl);
+      } else {
+        vec_pass<W, CH>(wg, wg + mat, sg, su, nk, c, act, nt, acc);
+      }
       float v[16];
 #pragma unroll
       for (int t = 0; t < kVecTok; ++t) {
@@ -792,7 +888,7 @@ __global__ __launch_bounds__(256) void k_gateup_vec(FfnArgs a) {
 
 // down: work item = (record, 8 rows of H); quarter q takes rows 8*g + q (stream 0)
 // and 8*g + 4 + q (stream 1) against h of the record's pairs; fp32 partial outputs.
-template <int W, int CH>
+template <int W, int CH, bool FILL>
 __global__ __launch_bounds__(256) void k_down_vec(FfnArgs a) {
   const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
   const int nrt = a.max_routed + (a.shared ? 1 : 0);
@@ -803,13 +899,16 @@ __global__ __launch_bounds__(256) void k_down_vec(FfnArgs a) {
   const uint16_t* __restrict__ hb = (const uint16_t*)a.hbuf;
   float* __restrict__ part = a.part;
   const int nwave = gridDim.x * 4;
+  const VecHead vh = vec_head(a, FILL);
   for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < nrt * RG; item += nwave) {
     const int r = item / RG, hg = (item % RG) * 8, h0 = hg + q;
     const Item it = item_block(a, r);
     if (it.n == 0) continue;
-    const uint8_t* wd = it.rec + 2 * mat + code_bytes<W>((uint64_t)h0 * F);
-    const uint8_t* s0 = scale_row<W>(it.rec, mat, F, H, 2, h0, F);
-    const uint8_t* s1 = scale_row<W>(it.rec, mat, F, H, 2, h0 + 4, F);
+    const uint8_t* src = FILL && !it.sh ? vec_source(a, vh, block_record(a, r)) : nullptr;
+    const uint8_t* rd = src ? src : it.rec;
+    const uint8_t* wd = rd + 2 * mat + code_bytes<W>((uint64_t)h0 * F);
+    const uint8_t* s0 = scale_row<W>(rd, mat, F, H, 2, h0, F);
+    const uint8_t* s1 = scale_row<W>(rd, mat, F, H, 2, h0 + 4, F);
     for (int tg = 0; tg < it.n; tg += kVecTok) {
       const int nt = min(kVecTok, it.n - tg);
       const uint16_t* act[kVecTok];
@@ -818,7 +917,19 @@ __global__ __launch_bounds__(256) void k_down_vec(FfnArgs a) {
       float acc[kVecTok][2];
 #pragma unroll
       for (int t = 0; t < kVecTok; ++t) acc[t][0] = acc[t][1] = 0.f;
-      vec_pass<W, CH>(wd, wd + code_bytes<W>(4ull * F), s0, s1, nk, c, act, nt, acc);
+      if (FILL && src) {  // uniform per wavefront; one token group (it.n <= kVecTok)
+        uint8_t* dst = const_cast<uint8_t*>(it.rec);
+        Fill fl;
+        fl.w0 = dst + 2 * mat + code_bytes<W>((uint64_t)h0 * F);
+        fl.w1 = fl.w0 + code_bytes<W>(4ull * F);
+        fl.s0 = const_cast<uint8_t*>(scale_row<W>(dst, mat, F, H, 2, h0, F));
+        fl.s1 = const_cast<uint8_t*>(scale_row<W>(dst, mat, F, H, 2, h0 + 4, F));
+        fl.own0 = W == kMx4 || (h0 & 127) == 0;
+        fl.own1 = W == kMx4;  // h0 + 4 is never the first row of a 128-row block
+        vec_pass_fill<W, kFillChunks<CH>>(wd, wd + code_bytes<W>(4ull * F), s0, s1, nk, c, act, nt, acc, fl);
+      } else {
+        vec_pass<W, CH>(wd, wd + code_bytes<W>(4ull * F), s0, s1, nk, c, act, nt, acc);
+      }
       float v[16];
 #pragma unroll
       for (int t = 0; t < kVecTok; ++t) {
@@ -1001,14 +1112,16 @@ FfnKernel gateup_decode(bool one, bool fill, int H) {
   const int nk = H / (16 * lane_weights<W>());
   if (one && fill) { MOE_BY_CHUNKS(k_gateup_one, nk, true) }
   if (one) { MOE_BY_CHUNKS(k_gateup_one, nk, false) }
-  MOE_BY_CHUNKS(k_gateup_vec, nk)
+  if (fill) { MOE_BY_CHUNKS(k_gateup_vec, nk, true) }
+  MOE_BY_CHUNKS(k_gateup_vec, nk, false)
 }
 template <int W>
 FfnKernel down_decode(bool one, bool fill, int F) {
   const int nk = F / (16 * lane_weights<W>());
   if (one && fill) { MOE_BY_CHUNKS(k_down_one, nk, true) }
   if (one) { MOE_BY_CHUNKS(k_down_one, nk, false) }
-  MOE_BY_CHUNKS(k_down_vec, nk)
+  if (fill) { MOE_BY_CHUNKS(k_down_vec, nk, true) }
+  MOE_BY_CHUNKS(k_down_vec, nk, false)
 }
 #undef MOE_BY_CHUNKS
 
@@ -1096,7 +1209,12 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(FfnArgs a, void* __rest
 
 }  // namespace
 
-bool ffn_reads_through(const moe_offload* h, int T) { return T == 1 && h->dtype != MOE_F32; }
+// read-through: one token (a work item per choice), or 2 to kVecTok tokens with
+// at most 64 pairs (the decode kernels, one token group per record, the copy
+// list in one load per wavefront)
+bool ffn_reads_through(const moe_offload* h, int T) {
+  return h->dtype != MOE_F32 && (T == 1 || (T <= kVecTok && T * h->k <= 64));
+}
 
 hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int T,
                       const void* shared, void* y, const void* residual, void* x_next, void* xn_next, float eps,
@@ -1126,7 +1244,7 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
   a.off_tiles = h->gl.off_tiles();
   a.max_routed = std::min(T * h->k, h->S + h->E);
   a.pair_items = T == 1 && h->dtype != MOE_F32 ? 1 : 0;
-  fill = fill && a.pair_items;
+  fill = fill && ffn_reads_through(h, T);
   a.fill_list = fill ? h->cache.copy_list : nullptr;
   a.host = h->host_dev;
   // distinct records a call can touch (+ the shared expert)

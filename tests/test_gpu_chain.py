@@ -243,18 +243,21 @@ def test_chain_with_pinned_experts():
         cg.close()
 
 
-@pytest.mark.parametrize("wdt,shared,prefetch_n,H,F", [
-    # small passes for each format, the lookahead beside it, and the 16- and 8-block passes (read through
-    # at half the width) for bf16, fp8 and MXFP4
-    (1, False, 0, 256, 512), (2, True, 0, 256, 512), (3, True, 0, 256, 512), (1, False, 2, 256, 512),
-    (1, False, 0, 2048, 256), (2, False, 0, 1024, 1024), (3, True, 0, 2048, 512)])
-def test_chain_read_through_matches_copy_kernel(wdt, shared, prefetch_n, H, F):
-    """Single-token read-through (the FFN fills missed slots from the host store, no copy launch) against the
-    same chain with the copy kernel: identical outputs, routing, tables and counters on every step, every
-    occupied slot byte-identical to its expert's host record, and the oracle replay; the two chains swap
-    modes after six steps (graph dropped and captured again)."""
-    L, E, S, k, T = 3, 16, 6, 4, 1
-    print("chain read-through wdt=%d shared=%s prefetch=%d H=%d F=%d" % (wdt, shared, prefetch_n, H, F), flush=True)
+@pytest.mark.parametrize("wdt,shared,prefetch_n,H,F,T", [
+    # single tokens: small passes for each format, the lookahead beside it, and the 16- and 8-block passes
+    # (read through at half the width) for bf16, fp8 and MXFP4; batches of 4 and 8 (calls wider than the
+    # 6 slots read their overflow through into staging) for each format, with and without the lookahead
+    (1, False, 0, 256, 512, 1), (2, True, 0, 256, 512, 1), (3, True, 0, 256, 512, 1), (1, False, 2, 256, 512, 1),
+    (1, False, 0, 2048, 256, 1), (2, False, 0, 1024, 1024, 1), (3, True, 0, 2048, 512, 1),
+    (1, False, 0, 256, 512, 4), (2, True, 0, 256, 512, 8), (3, True, 0, 512, 512, 4), (1, False, 2, 2048, 256, 8)])
+def test_chain_read_through_matches_copy_kernel(wdt, shared, prefetch_n, H, F, T):
+    """Read-through (the FFN fills missed slots, and the staging records of calls wider than the cache, from
+    the host store; no copy launch) against the same chain with the copy kernel: identical outputs, routing,
+    tables and counters on every step, every occupied slot byte-identical to its expert's host record, and
+    the oracle replay; the two chains swap modes after six steps (graph dropped and captured again)."""
+    L, E, S, k = 3, 16, 6, 4
+    print("chain read-through wdt=%d shared=%s prefetch=%d H=%d F=%d T=%d" % (wdt, shared, prefetch_n, H, F, T),
+          flush=True)
     rt = ChainModel(L, E, S, k, H, F, wdt, T, 93, prefetch_n, shared=shared)
     cp = ChainModel(L, E, S, k, H, F, wdt, T, 93, prefetch_n, shared=shared)
     m.moe_chain_set_read_through(cp.chain, 0)
