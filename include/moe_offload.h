@@ -389,19 +389,20 @@ int moe_chain_run(moe_chain* c, void* stream);
  * and for checking the graph against eager execution. */
 int moe_chain_run_eager(moe_chain* c, void* stream);
 
-/* Read-through of single-token misses (default on).  The pages move a
- * missed expert into its slot and then run the expert GEMMs on the slot
+/* Read-through of decode misses (default on).  The pages move a missed
+ * expert into its slot and then run the expert GEMMs on the slot
  * (xinfer-ai 0.14.6 docs/moe_offload.md, "How it works", Decode).  On: a
- * chain whose T is 1 (bf16, fp8 and MXFP4 layers) launches no copy kernel;
- * its gate/up and down launches read each record of the ensure's copy list
- * from the device-mapped host store and store every byte they read into the
- * record's slot, so the resident experts compute while the missed ones
- * cross the host link.  Off: the copy kernel moves the misses first.  Slots,
- * tables, counters and outputs are the same either way; only the launches
- * differ.  Changing the setting synchronises the device and drops the
- * captured graph (the next moe_chain_run captures again).  Other T and fp32
- * layers always use the copy kernel.  Errors: MOE_EINVAL (null chain),
- * MOE_EHIP. */
+ * chain whose T is 1, or 2 to 8 with T * top_k <= 64 (bf16, fp8 and MXFP4
+ * layers), launches no copy kernel; its gate/up and down launches read each
+ * record of the ensure's copy list from the device-mapped host store and
+ * store every byte they read into the record's slot (or, for the overflow of
+ * a call wider than the cache, its staging record), so the resident experts
+ * compute while the missed ones cross the host link.  Off: the copy kernel
+ * moves the misses first.  Slots, tables, counters and outputs are the same
+ * either way; only the launches differ.  Changing the setting synchronises
+ * the device and drops the captured graph (the next moe_chain_run captures
+ * again).  Other T and fp32 layers always use the copy kernel.  Errors:
+ * MOE_EINVAL (null chain), MOE_EHIP. */
 int moe_chain_set_read_through(moe_chain* c, int on);
 
 /* Synchronise and free the chain's graph, streams, events and buffers.  Null-safe. */
