@@ -28,7 +28,7 @@ struct moe_chain {
   std::vector<const float*> bias;
   std::vector<const void*> shared;
   int L = 0, T = 0, k = 0, H = 0, prefetch_n = 0, device = 0;
-  int read_through = 1;  // decode steps of 1-8 tokens: the FFN fills missed slots from the host store
+  int read_through = 1;  // decode steps (up to 64 tokens, 256 pairs): the FFN fills missed slots from the host store
   size_t act = 2;
   void* block = nullptr;
   uint8_t* x = nullptr;
@@ -117,7 +117,7 @@ hipError_t issue(moe_chain* c, hipStream_t cs) {
       }
     }
     if (pf && l >= 1) CHK(hipStreamWaitEvent(cs, c->ev_pf[l], 0));  // this layer's prefetch copy first
-    // the misses of a decode step of 1-8 tokens are read through by its FFN launches instead of a copy launch
+    // a decode step's misses are read through by its FFN launches instead of a copy launch
     const bool fill = c->read_through && moe::ffn_reads_through(h, T);
     if (!fill) CHK(moe::launch_copy(h, h->cache.copy_list, cs));
     if (look) {  // prefetch copy for layer l+1 behind layer l's demand copy

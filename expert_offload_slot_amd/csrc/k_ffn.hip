@@ -782,27 +782,43 @@ inline int one_chunks(int nk) {
 template <int CH>
 constexpr int kFillChunks = CH >= 8 ? CH / 2 : CH;
 
-// Read-through for 2 to kVecTok tokens (at most 64 pairs): the copy list
-// {mode, count, (expert, record)...} of the call, loaded once per wavefront in
-// one round trip, lane l holding pair l.  A work item whose record index is in
-// the list reads that expert's host record and stores every byte it reads into
-// the record (slot, or staging for the overflow of a call wider than the
-// cache), as the copy kernel would have; with at most kVecTok tokens a record's
-// tokens meet its weights in one pass, so each byte crosses the link once.
+// Read-through for 2 to kDecodeMaxT tokens (at most kFillPairs pairs): the copy
+// list {mode, count, (expert, record)...} of the call, loaded once per
+// wavefront in one round trip, lane l holding pairs l, l + 64, ...  A work item
+// whose record index is in the list reads that expert's host record in its
+// first token group and stores every byte it reads into the record (slot, or
+// staging for the overflow of a call wider than the cache), as the copy kernel
+// would have; its later token groups read the weights back from the record,
+// each lane the bytes it stored itself, and the scales again from the host
+// (another wavefront may own them), so each weight byte crosses the link once.
+constexpr int kFillPairs = 256;
+constexpr int kFillRegs = kFillPairs / 64;
+
 struct VecHead {
-  int mode = 0, n = 0, e = 0, r = -1;
+  int mode = 0, n = 0;
+  int e[kFillRegs], r[kFillRegs];
 };
 
 __device__ __forceinline__ VecHead vec_head(const FfnArgs& a, bool fill) {
   const int lane = threadIdx.x & 63;
   VecHead v;
+#pragma unroll
+  for (int i = 0; i < kFillRegs; ++i) {
+    v.e[i] = 0;
+    v.r[i] = -1;
+  }
   if (!fill) return v;
   const int32_t* __restrict__ lst = a.fill_list;
   v.mode = lst[0];
   v.n = lst[1];
-  if (lane < min(64, max(a.S, a.E))) {  // the list holds max(S, E) pairs
-    v.e = lst[2 + 2 * lane];
-    v.r = lst[3 + 2 * lane];
+  const int cap = min(kFillPairs, max(a.S, a.E));  // the list holds max(S, E) pairs
+#pragma unroll
+  for (int i = 0; i < kFillRegs; ++i) {
+    const int p = lane + 64 * i;
+    if (p < cap) {
+      v.e[i] = lst[2 + 2 * p];
+      v.r[i] = lst[3 + 2 * p];
+    }
   }
   return v;
 }
@@ -812,14 +828,19 @@ __device__ __forceinline__ VecHead vec_head(const FfnArgs& a, bool fill) {
 __device__ __forceinline__ const uint8_t* vec_source(const FfnArgs& a, const VecHead& v, int ri) {
   const int lane = threadIdx.x & 63;
   if (v.mode == MOE_MODE_STAGED_ALL) return nullptr;
-  const uint64_t hit = __ballot(lane < min(v.n, 64) && v.r == ri);
-  if (!hit) return nullptr;
-  const int e = __builtin_amdgcn_readlane(v.e, __builtin_ctzll(hit));
-  if ((unsigned)e >= (unsigned)a.E) {
-    atomicOr(a.err, MOE_DEV_ERR_AUDIT);
-    return nullptr;
+  const int n = min(v.n, kFillPairs);
+#pragma unroll
+  for (int i = 0; i < kFillRegs; ++i) {
+    const uint64_t hit = __ballot(lane + 64 * i < n && v.r[i] == ri);
+    if (!hit) continue;
+    const int e = __builtin_amdgcn_readlane(v.e[i], __builtin_ctzll(hit));
+    if ((unsigned)e >= (unsigned)a.E) {
+      atomicOr(a.err, MOE_DEV_ERR_AUDIT);
+      return nullptr;
+    }
+    return a.host + (uint64_t)e * a.stride;
   }
-  return a.host + (uint64_t)e * a.stride;
+  return nullptr;
 }
 
 // record index of grouped record block r (r < max_routed)
@@ -844,8 +865,9 @@ __global__ __launch_bounds__(256) void k_gateup_vec(FfnArgs a) {
     const Item it = item_block(a, r);
     if (it.n == 0) continue;
     const uint8_t* src = FILL && !it.sh ? vec_source(a, vh, block_record(a, r)) : nullptr;
-    const uint8_t* rd = src ? src : it.rec;
+    const uint8_t* rd = src ? src : it.rec;  // weights of the first token group, and the scales
     const uint8_t* wg = rd + code_bytes<W>((uint64_t)f * H);
+    const uint8_t* wgr = it.rec + code_bytes<W>((uint64_t)f * H);  // weights of later groups
     const uint8_t* sg = scale_row<W>(rd, mat, F, H, 0, f, H);
     const uint8_t* su = scale_row<W>(rd, mat, F, H, 1, f, H);
     for (int tg = 0; tg < it.n; tg += kVecTok) {
@@ -857,7 +879,7 @@ __global__ __launch_bounds__(256) void k_gateup_vec(FfnArgs a) {
       float acc[kVecTok][2];
 #pragma unroll
       for (int t = 0; t < kVecTok; ++t) acc[t][0] = acc[t][1] = 0.f;
-      if (FILL && src) {  // uniform per wavefront; one token group (it.n <= kVecTok)
+      if (FILL && src && tg == 0) {  // uniform per wavefront
         uint8_t* dst = const_cast<uint8_t*>(it.rec);
         Fill fl;
         fl.w0 = dst + code_bytes<W>((uint64_t)f * H);
@@ -866,6 +888,8 @@ __global__ __launch_bounds__(256) void k_gateup_vec(FfnArgs a) {
         fl.s1 = const_cast<uint8_t*>(scale_row<W>(dst, mat, F, H, 1, f, H));
         fl.own0 = fl.own1 = W == kMx4 || (f & 127) == 0;
         vec_pass_fill<W, kFillChunks<CH>>(wg, wg + mat, sg, su, nk, c, act, nt, acc, fl);
+      } else if (FILL && src) {
+        vec_pass<W, CH>(wgr, wgr + mat, sg, su, nk, c, act, nt, acc);
       } else {
         vec_pass<W, CH>(wg, wg + mat, sg, su, nk, c, act, nt, acc);
       }
@@ -905,8 +929,9 @@ __global__ __launch_bounds__(256) void k_down_vec(FfnArgs a) {
     const Item it = item_block(a, r);
     if (it.n == 0) continue;
     const uint8_t* src = FILL && !it.sh ? vec_source(a, vh, block_record(a, r)) : nullptr;
-    const uint8_t* rd = src ? src : it.rec;
+    const uint8_t* rd = src ? src : it.rec;  // weights of the first token group, and the scales
     const uint8_t* wd = rd + 2 * mat + code_bytes<W>((uint64_t)h0 * F);
+    const uint8_t* wdr = it.rec + 2 * mat + code_bytes<W>((uint64_t)h0 * F);  // weights of later groups
     const uint8_t* s0 = scale_row<W>(rd, mat, F, H, 2, h0, F);
     const uint8_t* s1 = scale_row<W>(rd, mat, F, H, 2, h0 + 4, F);
     for (int tg = 0; tg < it.n; tg += kVecTok) {
@@ -917,7 +942,7 @@ __global__ __launch_bounds__(256) void k_down_vec(FfnArgs a) {
       float acc[kVecTok][2];
 #pragma unroll
       for (int t = 0; t < kVecTok; ++t) acc[t][0] = acc[t][1] = 0.f;
-      if (FILL && src) {  // uniform per wavefront; one token group (it.n <= kVecTok)
+      if (FILL && src && tg == 0) {  // uniform per wavefront
         uint8_t* dst = const_cast<uint8_t*>(it.rec);
         Fill fl;
         fl.w0 = dst + 2 * mat + code_bytes<W>((uint64_t)h0 * F);
@@ -927,6 +952,8 @@ __global__ __launch_bounds__(256) void k_down_vec(FfnArgs a) {
         fl.own0 = W == kMx4 || (h0 & 127) == 0;
         fl.own1 = W == kMx4;  // h0 + 4 is never the first row of a 128-row block
         vec_pass_fill<W, kFillChunks<CH>>(wd, wd + code_bytes<W>(4ull * F), s0, s1, nk, c, act, nt, acc, fl);
+      } else if (FILL && src) {
+        vec_pass<W, CH>(wdr, wdr + code_bytes<W>(4ull * F), s0, s1, nk, c, act, nt, acc);
       } else {
         vec_pass<W, CH>(wd, wd + code_bytes<W>(4ull * F), s0, s1, nk, c, act, nt, acc);
       }
@@ -1209,11 +1236,11 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(FfnArgs a, void* __rest
 
 }  // namespace
 
-// read-through: one token (a work item per choice), or 2 to kVecTok tokens with
-// at most 64 pairs (the decode kernels, one token group per record, the copy
-// list in one load per wavefront)
+// read-through: one token (a work item per choice), or up to kDecodeMaxT tokens
+// with at most kFillPairs pairs (the decode kernels, the copy list in one load
+// per wavefront)
 bool ffn_reads_through(const moe_offload* h, int T) {
-  return h->dtype != MOE_F32 && (T == 1 || (T <= kVecTok && T * h->k <= 64));
+  return h->dtype != MOE_F32 && (T == 1 || (T <= kDecodeMaxT && T * h->k <= kFillPairs));
 }
 
 hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int T,

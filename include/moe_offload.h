@@ -392,8 +392,8 @@ int moe_chain_run_eager(moe_chain* c, void* stream);
 /* Read-through of decode misses (default on).  The pages move a missed
  * expert into its slot and then run the expert GEMMs on the slot
  * (xinfer-ai 0.14.6 docs/moe_offload.md, "How it works", Decode).  On: a
- * chain whose T is 1, or 2 to 8 with T * top_k <= 64 (bf16, fp8 and MXFP4
- * layers), launches no copy kernel; its gate/up and down launches read each
+ * chain whose T is 1, or 2 to 64 with T * top_k <= 256 (bf16, fp8 and
+ * MXFP4 layers), launches no copy kernel; its gate/up and down launches read each
  * record of the ensure's copy list from the device-mapped host store and
  * store every byte they read into the record's slot (or, for the overflow of
  * a call wider than the cache, its staging record), so the resident experts

@@ -249,7 +249,10 @@ def test_chain_with_pinned_experts():
     # 6 slots read their overflow through into staging) for each format, with and without the lookahead
     (1, False, 0, 256, 512, 1), (2, True, 0, 256, 512, 1), (3, True, 0, 256, 512, 1), (1, False, 2, 256, 512, 1),
     (1, False, 0, 2048, 256, 1), (2, False, 0, 1024, 1024, 1), (3, True, 0, 2048, 512, 1),
-    (1, False, 0, 256, 512, 4), (2, True, 0, 256, 512, 8), (3, True, 0, 512, 512, 4), (1, False, 2, 2048, 256, 8)])
+    (1, False, 0, 256, 512, 4), (2, True, 0, 256, 512, 8), (3, True, 0, 512, 512, 4), (1, False, 2, 2048, 256, 8),
+    # 16 and 32 tokens: records with more than 8 tokens read the host once and their later token groups
+    # read back what the first one stored
+    (1, False, 0, 256, 512, 16), (2, True, 0, 512, 256, 32), (3, False, 0, 512, 512, 32), (1, False, 2, 256, 512, 32)])
 def test_chain_read_through_matches_copy_kernel(wdt, shared, prefetch_n, H, F, T):
     """Read-through (the FFN fills missed slots, and the staging records of calls wider than the cache, from
     the host store; no copy launch) against the same chain with the copy kernel: identical outputs, routing,
