@@ -565,9 +565,21 @@ struct WChunk<kBf16> {
   typedef uint4 T;
 };
 
+// Weight chunks are read once per call and never again before the next layer
+// has streamed its own: non-temporal loads keep them from displacing other
+// lines in L2 (single-token gate/up 11.45 -> 10.79 us, down 5.84 -> 5.70 us).
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_nt __attribute__((ext_vector_type(2)));
 template <int W>
 __device__ __forceinline__ typename WChunk<W>::T load_w(const uint8_t* row, int kb, int c) {
-  return *reinterpret_cast<const typename WChunk<W>::T*>(row + (uint64_t)(16 * kb + c) * sizeof(typename WChunk<W>::T));
+  const uint8_t* p = row + (uint64_t)(16 * kb + c) * sizeof(typename WChunk<W>::T);
+  if constexpr (W == kBf16) {
+    const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  } else {
+    const u32x2_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_nt*>(p));
+    return make_uint2(v.x, v.y);
+  }
 }
 
 // the stored scale lane c applies in K block kb (srow from scale_row), as raw
