@@ -1047,7 +1047,7 @@ __device__ __forceinline__ const uint8_t* fill_source(const FfnArgs& a, int j, c
 }
 
 template <int W, int CH, bool FILL>
-__global__ __launch_bounds__(256) void k_gateup_one(FfnArgs a) {
+__global__ __launch_bounds__(128) void k_gateup_one(FfnArgs a) {
   const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
   const int RG = a.F / 4;
   const int H = a.H, F = a.F;
@@ -1057,7 +1057,7 @@ __global__ __launch_bounds__(256) void k_gateup_one(FfnArgs a) {
   const uint16_t* __restrict__ x = (const uint16_t*)a.x;
   uint16_t* __restrict__ hb = (uint16_t*)a.hbuf;
   const OneHead o = one_head(a, FILL);
-  for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < items; item += gridDim.x * 4) {
+  for (int item = blockIdx.x * 2 + (threadIdx.x >> 6); item < items; item += gridDim.x * 2) {
     const int j = item / RG, f = (item % RG) * 4 + q;
     const uint8_t* rec = one_record(a, j, o);
     float g = 0.f, up = 0.f;
@@ -1089,7 +1089,7 @@ __global__ __launch_bounds__(256) void k_gateup_one(FfnArgs a) {
 }
 
 template <int W, int CH, bool FILL>
-__global__ __launch_bounds__(256) void k_down_one(FfnArgs a) {
+__global__ __launch_bounds__(128) void k_down_one(FfnArgs a) {
   const int lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
   const int RG = a.H / 8;
   const int H = a.H, F = a.F;
@@ -1099,7 +1099,7 @@ __global__ __launch_bounds__(256) void k_down_one(FfnArgs a) {
   const uint16_t* __restrict__ hb = (const uint16_t*)a.hbuf;
   float* __restrict__ part = a.part;
   const OneHead o = one_head(a, FILL);
-  for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < items; item += gridDim.x * 4) {
+  for (int item = blockIdx.x * 2 + (threadIdx.x >> 6); item < items; item += gridDim.x * 2) {
     const int j = item / RG, h0 = (item % RG) * 8 + q;
     const uint8_t* rec = one_record(a, j, o);
     float s0 = 0.f, s1 = 0.f;
@@ -1302,15 +1302,21 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
     g1 = dim3(std::min(max_items_r * (h->F / kF32Rows), 2048));
     g2 = dim3(std::min(max_items_r * (h->H / kF32Rows), 2048));
     b1 = b2 = dim3(256);
-  } else if (T <= kDecodeMaxT) {  // one wavefront per work item, 4 per workgroup
+  } else if (T <= kDecodeMaxT) {  // one wavefront per work item
     const bool one = a.pair_items != 0;
     gu = wf == kFp8 ? gateup_decode<kFp8>(one, fill, h->H)
                     : (wf == kMx4 ? gateup_decode<kMx4>(one, fill, h->H) : gateup_decode<kBf16>(one, fill, h->H));
     dn = wf == kFp8 ? down_decode<kFp8>(one, fill, h->F)
                     : (wf == kMx4 ? down_decode<kMx4>(one, fill, h->F) : down_decode<kBf16>(one, fill, h->F));
-    g1 = dim3(std::min((max_items_r * (h->F / 4) + 3) / 4, 8192));
-    g2 = dim3(std::min((max_items_r * (h->H / 8) + 3) / 4, 8192));
-    b1 = b2 = dim3(256);
+    if (one) {  // 2 per workgroup: a single token's items spread evenly over the CUs (batch-1 step 1 % faster)
+      g1 = dim3(std::min((max_items_r * (h->F / 4) + 1) / 2, 16384));
+      g2 = dim3(std::min((max_items_r * (h->H / 8) + 1) / 2, 16384));
+      b1 = b2 = dim3(128);
+    } else {  // 4 per workgroup
+      g1 = dim3(std::min((max_items_r * (h->F / 4) + 3) / 4, 8192));
+      g2 = dim3(std::min((max_items_r * (h->H / 8) + 3) / 4, 8192));
+      b1 = b2 = dim3(256);
+    }
   } else {  // grouped GEMM over (record tile, 64 rows) work items; the grid strides over the call's list
     gu = wf == kFp8 ? k_gemm_gu<kFp8> : (wf == kMx4 ? k_gemm_gu<kMx4> : k_gemm_gu<kBf16>);
     dn = wf == kFp8 ? k_gemm_dn<kFp8> : (wf == kMx4 ? k_gemm_dn<kMx4> : k_gemm_dn<kBf16>);
