@@ -1,31 +1,37 @@
 #!/usr/bin/env python3
 """MoE-layer decode throughput of the offloaded MoE layer step on one MI355X.
 
-Workload (one JSON line on stdout): Qwen3-30B-A3B-shaped decode in bf16 -- 48
-MoE layers, each 128 experts, top-8 with renormalised softmax, hidden 2048,
-moe ffn 768, 26 GPU slots per layer (20 %), batch 1, token hidden states from
-an AR(1) process (rho 0.9), router bias ranked by a seeded Zipf(1.2)
-permutation.  Every expert of every layer (58 GB) sits in pinned,
+Workload of `value` (one JSON line on stdout): Qwen3-30B-A3B-shaped decode in
+bf16 -- 48 MoE layers, each 128 experts, top-8 with renormalised softmax,
+hidden 2048, moe ffn 768, 26 GPU slots per layer (20 %), batch 1, token hidden
+states from an AR(1) process (rho 0.9), router bias ranked by a seeded
+Zipf(1.2) permutation.  Every expert of every layer (58 GB) sits in pinned,
 device-mapped host memory.  A step = for each layer: router logits, one
 control workgroup (top-k, LRU slot ensure, grouping), the miss copy from host
-memory, the expert FFN with combine and residual; all 48 layers replayed as
-one captured HIP graph.  Inputs are resident in HBM before the timed region.
+memory (read through by the FFN launches), the expert FFN with combine and
+residual; all 48 layers replayed as one captured HIP graph.  Inputs are
+resident in HBM before the timed region.
 
-Also measured in the same run:
+`value` times exactly the --steps replays that follow --warmup untimed
+replays, from empty caches.  The same line carries, measured in the same run:
+  * steady_state: a fixed untimed warm-up of 32 replays from empty caches,
+    then 224 timed replays (steps 32-255), and the summed link + HBM roofline;
+    the same with the copy kernel instead of read-through; batch 8 and 32;
   * per-kernel average durations from HIP events on the launch stream
     (library profiling switch) over an eager pass of the same chain; the
-    gate/up kernel's HBM roofline and the miss copy's host-link fraction;
-  * a 256 MiB device-to-device copy (HBM reference, and the known-size kernel
-    that scales the rocprofv3 FETCH_SIZE / WRITE_SIZE counters);
-  * the host link: SDMA copy of 1 GiB pinned memory and the copy kernel over
-    128 records;
+    gate/up kernel's HBM roofline, the down kernel's and the miss copy's
+    host-link fraction;
+  * a 256 MiB device-to-device copy (HBM reference) and the host link (SDMA
+    copy of 1 GiB pinned memory, the copy kernel over 128 records);
+  * router-lookahead prefetch against none, LRU against scored eviction and
+    pinned placement, decode at 10/20/40/100 % slots (outputs bitwise
+    identical at every fraction);
+  * the MXFP4 records, the Mixtral-8x7B-shaped layer at 2/4/6 slots and the
+    DeepSeek-V3-shaped fp8 layer (decode at batch 16, the 2048-token prefill:
+    staging copy, FFN TFLOP/s and the fraction of its attainable roofline);
   * the CPU oracle on a bounded sample of the same workload.
---extra adds batch 8 and 32, the router-lookahead prefetch comparison, LRU
-against scored eviction and pinned placement, decode at 10/20/40/100 % slots
-(outputs bitwise identical at every fraction), the CPU oracle's own rates, the
-MXFP4 records, the Mixtral-8x7B-shaped layer at 2/4/6 slots and the
-DeepSeek-V3-shaped fp8 layer (decode at batch 16, the 2048-token prefill:
-staging copy and FFN TFLOP/s).
+--quick keeps only the batch-1 window, its steady state, the eager profile
+and the host link.
 """
 import argparse
 import ctypes
@@ -43,6 +49,9 @@ E, K_TOP, H, F, SLOTS, LAYERS = 128, 8, 2048, 768, 26, 48
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 LINK_PEAK_GBPS = 64.0           # PCIe 5.0 x16, one direction, published
 COUNTERS = os.path.join(ROOT, "profiles", "k_gateup_one_decode_b1_counters.md")
+TRACE = os.path.join(ROOT, "profiles", "decode_qwen3_30b_b1_kernel_trace.md")
+GU_KERNEL_TRACE_NAME = "k_gateup_one<1, 16, false>"
+SS_WARM, SS_STEPS = 32, 224     # steady state: untimed cache warm-up from an empty cache, then timed replays
 FFN_SRC = os.path.join(ROOT, "expert_offload_slot_amd", "csrc", "k_ffn.hip")
 
 
@@ -73,6 +82,14 @@ def measured_traffic():
         return None
 
 
+def traced_avg_us(path, kernel):
+    """Average duration of `kernel` over the eager profile pass, from the committed rocprofv3 summary."""
+    if not os.path.exists(path):
+        return None
+    m_ = re.search(r"^eager_pass_avg_us\[%s\]:\s*(\S+)\s*$" % re.escape(kernel), open(path).read(), re.M)
+    return float(m_.group(1)) if m_ else None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -83,7 +100,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--prof-steps", type=int, default=16)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--extra", action="store_true", help="also batch 8/32 and the lookahead-prefetch comparison")
+    ap.add_argument("--quick", action="store_true",
+                    help="only the batch-1 window, its steady state, the eager profile and the host link")
+    ap.add_argument("--cpu-rates", action="store_true", help="also the CPU oracle's own rates on all threads and one")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--mxfp4-only", action="store_true",
                     help="only the same decode chain with MXFP4 expert records (prints its own JSON line)")
@@ -175,10 +194,12 @@ def main():
         xs = synth.tokens(args.seed, 100 + T, T, H, n, 0.9, synth.BF16)
         return torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16).to(dev)
 
-    def run_decode(T, warm, steps, tag, prefetch_n=0, xs_d=None, hs=None, cold=None, read_through=True):
+    def run_decode(T, warm, steps, tag, prefetch_n=0, xs_d=None, hs=None, cold=None, read_through=True, fresh=True):
         """graph replays of the whole step; returns (tok/s, ms/step, stats delta, chain, buffers, tokens).
-        With a dict `cold`, the graph is captured and replayed once, every layer's cache is emptied again,
-        and the warm-up replays (from that empty cache) are timed into it."""
+        fresh: the graph is captured and replayed once outside the timed window and every layer's cache is
+        emptied again, so the warm-up replays start from an empty cache (fresh=False keeps the caches as
+        they are: the capture replay is then step 0 and the warm-up covers steps 1..warm-1).
+        With a dict `cold`, the warm-up replays are timed into it."""
         hs = hs or handles
         if xs_d is None:
             xs_d = token_stream(T, warm + steps + args.prof_steps)
@@ -193,15 +214,16 @@ def main():
             assert rc == 0
             m.moe_chain_run(c, stream)
 
-        if cold is not None:
-            step(0)  # capture + instantiate outside the timed window
-            torch.cuda.synchronize()
+        step(0)  # capture + instantiate outside the timed window
+        torch.cuda.synchronize()
+        if fresh:
             for h in hs:
                 m.moe_offload_reset(h, stream)
             torch.cuda.synchronize()
+        if cold is not None:
             c0, c1 = ev(), ev()
             c0.record(stream)
-        for s in range(warm):
+        for s in range(0 if fresh else 1, warm):
             step(s)
         if cold is not None:
             c1.record(stream)
@@ -232,16 +254,25 @@ def main():
              delta["misses"] / (T * steps), delta["staged_calls"], delta["calls"]))
         return T * steps * 1e3 / ms, ms / steps, delta, c, bufs, xs_d
 
-    cold = {}
-    tok_s, ms_step, delta, chain, bufs, xs_d = run_decode(T0, args.warmup, args.steps, "decode", cold=cold)
+    # ---------------- the timed window: --warmup untimed replays from an empty cache, then --steps timed
+    # replays (the headline value; cold start included when the window is short)
+    tok_s, ms_step, delta, chain, bufs, xs_d = run_decode(T0, args.warmup, args.steps, "decode-window")
     m.moe_chain_destroy(chain)
+
+    # ---------------- steady state: a fixed untimed cache warm-up of SS_WARM replays from an empty cache,
+    # then SS_STEPS timed replays (steps SS_WARM .. SS_WARM + SS_STEPS - 1 of the same token stream)
+    for h in handles:
+        m.moe_offload_reset(h, stream)
+    cold = {}
+    ss_tok, ss_ms, ss_d, chain, bufs, xs_ss = run_decode(T0, SS_WARM, SS_STEPS, "decode-steady", cold=cold)
 
     # ---------------- the same stream from empty caches with the misses moved by the copy kernel before the FFN
     for h in handles:
         m.moe_offload_reset(h, stream)
-    tok_cp, ms_cp, delta_cp, chain, bufs, _ = run_decode(T0, args.warmup, args.steps, "decode-copy-kernel",
-                                                         xs_d=xs_d, read_through=False)
-    assert delta_cp["misses"] == delta["misses"] and delta_cp["staged_copies"] == delta["staged_copies"]
+    m.moe_chain_destroy(chain)
+    tok_cp, ms_cp, delta_cp, chain, bufs, _ = run_decode(T0, SS_WARM, SS_STEPS, "decode-steady-copy-kernel",
+                                                         xs_d=xs_ss, read_through=False)
+    assert delta_cp["misses"] == ss_d["misses"] and delta_cp["staged_copies"] == ss_d["staged_copies"]
 
     # ---------------- eager pass of the copy-kernel chain with per-kernel HIP events on the launch stream:
     # each kernel's bytes come from one memory (the FFN from HBM, the copy over the host link)
@@ -249,12 +280,12 @@ def main():
     for h in handles:
         m.moe_offload_profile(h, 1)
     before = stats_sum()
-    s0 = args.warmup + args.steps
+    s0 = SS_WARM + SS_STEPS
     gu_bytes = dn_bytes = 0
     distinct = 0  # distinct records the FFN reads, summed over the profiled calls
     sid_host = np.empty((L, T, K_TOP), dtype=np.int32)
     for s in range(s0, s0 + args.prof_steps):
-        hip.hipMemcpyAsync(bufs["x"], xs_d[s].data_ptr(), T * H * 2, 3, stream.cuda_stream)
+        hip.hipMemcpyAsync(bufs["x"], xs_ss[s].data_ptr(), T * H * 2, 3, stream.cuda_stream)
         m.moe_chain_run_eager(chain, stream)
         torch.cuda.synchronize()
         # algorithmic bytes of this step's FFN launches: distinct records of each call
@@ -283,6 +314,11 @@ def main():
     dn_gbps = dn_bytes / (dn_ms * 1e-3) / 1e9
     cp_gbps = copy_bytes / (cp_ms * 1e-3) / 1e9 if cp_ms > 0 else 0.0
     traffic = measured_traffic()
+    gu_alg = int(gu_bytes // gu_n)
+    traced = traced_avg_us(TRACE, GU_KERNEL_TRACE_NAME)
+
+    def hit_rate(d):
+        return round(d["hits"] / max(1, d["hits"] + d["misses"] + d["staged_copies"]), 4)
 
     result = {
         "metric": "MoE-layer decode tokens/s at 20% slots (Qwen3-30B-A3B-shaped, 48 layers, bf16)",
@@ -300,22 +336,38 @@ def main():
         "config": {"workload": "qwen3-30b-a3b-shaped offloaded MoE decode: 48 layers x 128 experts, top-8, "
                                "hidden 2048, moe ffn 768, 26 slots/layer, batch %d, HIP-graph step" % T0,
                    "layers": L, "experts": E, "top_k": K_TOP, "hidden": H, "ffn": F, "slots": SLOTS,
-                   "batch": T0, "host_store_GB": round(L * E * stride / 1e9, 2)},
-        "decode_stats": {"misses_per_token": round(delta["misses"] / (T0 * args.steps), 4),
+                   "batch": T0, "host_store_GB": round(L * E * stride / 1e9, 2),
+                   "window": "value times steps %d-%d of the token stream, replayed from empty caches after "
+                             "%d untimed replays" % (args.warmup, args.warmup + args.steps - 1, args.warmup),
+                   "steady_state_warmup_steps": SS_WARM, "steady_state_timed_steps": SS_STEPS},
+        "window_stats": {"misses_per_token": round(delta["misses"] / (T0 * args.steps), 4),
                          "staged_calls": delta["staged_calls"], "calls": delta["calls"],
                          "staged_copies_per_token": round(delta["staged_copies"] / (T0 * args.steps), 4),
-                         "hit_rate": round(delta["hits"] / max(1, delta["hits"] + delta["misses"] + delta["staged_copies"]), 4),
-                         "steady_state_steps": "%d-%d" % (args.warmup, args.warmup + args.steps - 1)},
+                         "hit_rate": hit_rate(delta)},
+        "steady_state": {"batch": T0, "steps": "%d-%d" % (SS_WARM, SS_WARM + SS_STEPS - 1),
+                         "untimed_cache_warmup_steps": SS_WARM,
+                         "tokens_per_s": round(ss_tok, 2), "ms_per_step": round(ss_ms, 4),
+                         "misses_per_token": round(ss_d["misses"] / (T0 * SS_STEPS), 4),
+                         "staged_copies_per_token": round(ss_d["staged_copies"] / (T0 * SS_STEPS), 4),
+                         "hit_rate": hit_rate(ss_d)},
         "cold_start": cold,
-        "read_through": {"on_tokens_per_s": round(tok_s, 2), "off_tokens_per_s": round(tok_cp, 2),
-                         "on_ms_per_step": round(ms_step, 4), "off_ms_per_step": round(ms_cp, 4),
-                         "speedup": round(tok_s / tok_cp, 4)},
+        "read_through": {"on_tokens_per_s": round(ss_tok, 2), "off_tokens_per_s": round(tok_cp, 2),
+                         "on_ms_per_step": round(ss_ms, 4), "off_ms_per_step": round(ms_cp, 4),
+                         "speedup": round(ss_tok / tok_cp, 4), "steps": "%d-%d steady state" % (SS_WARM, SS_WARM + SS_STEPS - 1)},
         "roofline": {"bound": "hbm", "kernel": "k_gateup_one<bf16, 16, false> (gate/up + SiLU, single-token decode, records read in place)",
                      "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gu_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": None if traffic is None else traffic,
                      "avg_launch_us": round(gu_ms * 1e3 / gu_n, 3), "launches": gu_n,
-                     "algorithmic_bytes_per_launch": int(gu_bytes // gu_n)},
+                     "algorithmic_bytes_per_launch": gu_alg,
+                     "duration_source": "HIP start/stop events recorded with each dispatch on its launch stream "
+                                        "(hipExtLaunchKernelGGL), eager pass of %d steps in this run" % args.prof_steps,
+                     "traffic_source": None if traffic is None else
+                     "scaled FETCH_SIZE + WRITE_SIZE per launch from %s (taken on this kernel source)" %
+                     os.path.relpath(COUNTERS, ROOT),
+                     "rocprof": None if traced is None else
+                     {"avg_launch_us": traced, "frac": round(gu_alg / (traced * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                      "source": "%s (rocprofv3 kernel trace of this command's eager pass)" % os.path.relpath(TRACE, ROOT)}},
         "roofline_down": {"bound": "hbm", "kernel": "k_down_one<bf16, 6, false>", "achieved": round(dn_gbps, 1),
                           "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dn_gbps / HBM_PEAK_GBPS, 4),
                           "avg_launch_us": round(dn_ms * 1e3 / dn_n, 3),
@@ -364,47 +416,63 @@ def main():
     log("host link: SDMA %.2f GB/s, copy kernel %.2f GB/s; decode copies at %.1f %% of measured link" %
         (sdma, kernel_link, 100 * cp_gbps / link))
 
-    # ---------------- summed roofline of the timed steps: every copied record over the measured host link,
-    # every distinct record the FFN reads once from HBM at the datasheet rate
-    copies_step = (delta["misses"] + delta["staged_copies"]) / args.steps
-    distinct_step = distinct / args.prof_steps
-    bound_ms = (copies_step * rb / (link * 1e9) + distinct_step * rb / (HBM_PEAK_GBPS * 1e9)) * 1e3
-    result["summed_roofline"] = {"ms_per_step": round(bound_ms, 4), "tokens_per_s": round(T0 * 1e3 / bound_ms, 2),
-                                 "frac": round(bound_ms / ms_step, 4),
-                                 "copied_records_per_step": round(copies_step, 3),
-                                 "distinct_records_per_step": round(distinct_step, 3),
-                                 "record_bytes": rb, "link_GBps": round(link, 2), "hbm_GBps": HBM_PEAK_GBPS}
-    log("summed roofline: %.3f ms/step (%.1f tok/s); measured %.3f ms/step = %.1f %% of it" %
-        (bound_ms, T0 * 1e3 / bound_ms, ms_step, 100 * bound_ms / ms_step))
+    # ---------------- summed roofline of the steady-state steps: every copied record over the measured host
+    # link, every distinct record the FFN reads once from HBM at the datasheet rate
+    def summed(d, steps, ms, T_, distinct_per_step):
+        copies_step = (d["misses"] + d["staged_copies"]) / steps
+        bound_ms = (copies_step * rb / (link * 1e9) + distinct_per_step * rb / (HBM_PEAK_GBPS * 1e9)) * 1e3
+        return {"ms_per_step": round(bound_ms, 4), "tokens_per_s": round(T_ * 1e3 / bound_ms, 2),
+                "frac": round(bound_ms / ms, 4), "copied_records_per_step": round(copies_step, 3),
+                "distinct_records_per_step": round(distinct_per_step, 3), "record_bytes": rb,
+                "link_GBps": round(link, 2), "hbm_GBps": HBM_PEAK_GBPS}
 
-    if args.extra:
-        for T in (8, 32):
+    result["steady_state"]["summed_roofline"] = summed(ss_d, SS_STEPS, ss_ms, T0, distinct / args.prof_steps)
+    log("steady state: %.1f tok/s = %.1f %% of the summed roofline (%.1f tok/s)" %
+        (ss_tok, 100 * result["steady_state"]["summed_roofline"]["frac"],
+         result["steady_state"]["summed_roofline"]["tokens_per_s"]))
+    m.moe_chain_destroy(chain)
+
+    if not args.quick:
+        result["steady_state_batches"] = {}
+        for T, steps in ((8, 64), (32, 32)):
             if T == T0:
                 continue
-            steps = 64 if T == 8 else 32
-            ts, msps, d, c2, _, _ = run_decode(T, 8, steps, "decode-b%d" % T)
-            result["batch%d" % T] = {"tokens_per_s": round(ts, 2), "ms_per_step": round(msps, 3), "steps": steps,
-                                     "misses_per_token": round(d["misses"] / (T * steps), 4),
-                                     "staged_calls": d["staged_calls"], "calls": d["calls"],
-                                     "staged_copies_per_token": round(d["staged_copies"] / (T * steps), 4)}
+            for h in handles:
+                m.moe_offload_reset(h, stream)
+            ts, msps, d, c2, b2, _ = run_decode(T, SS_WARM, steps, "decode-steady-b%d" % T)
+            nd = distinct_records(hip, b2, L, T, SS_WARM + steps - 1)
             m.moe_chain_destroy(c2)
+            result["steady_state_batches"]["batch%d" % T] = {
+                "tokens_per_s": round(ts, 2), "ms_per_step": round(msps, 3),
+                "steps": "%d-%d" % (SS_WARM, SS_WARM + steps - 1), "untimed_cache_warmup_steps": SS_WARM,
+                "misses_per_token": round(d["misses"] / (T * steps), 4),
+                "staged_calls": d["staged_calls"], "calls": d["calls"],
+                "staged_copies_per_token": round(d["staged_copies"] / (T * steps), 4),
+                "summed_roofline": summed(d, steps, msps, T, nd)}
         result["prefetch"] = prefetch_compare(args, m, hip, handles, run_decode, token_stream)
         result["eviction"] = eviction_compare(args, m, hip, torch, handles, wr_d, b_d, run_decode, token_stream)
         result["slot_fractions"] = slot_fraction_compare(args, m, hip, handles, run_decode, token_stream)
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args, handles, routers, stride, T0)
-        if args.extra:
+        if args.cpu_rates:
             result["cpu_oracle"] = cpu_oracle_rates(args)
 
-    m.moe_chain_destroy(chain)
     for h in reversed(handles):
         m.moe_offload_destroy(h)
-    if args.extra:  # after the bf16 layers' host stores are released
+    if not args.quick:  # after the bf16 layers' host stores are released
         result["qwen3_mxfp4"] = qwen3_mxfp4(args, m, torch, hip, wr_d, b_d)
         result["mixtral_8x7b_layer"] = mixtral_layer(args, m, torch)
         result["deepseek_v3_layer"] = deepseek_layer(args, m, torch)
     print(json.dumps(result), flush=True)
+
+
+def distinct_records(hip, bufs, L, T, step):
+    """Distinct records each layer's FFN read in the chain's last step, summed over the layers."""
+    import numpy as np
+    sid = np.empty((L, T, K_TOP), dtype=np.int32)
+    assert hip.hipMemcpy(sid.ctypes.data, bufs["slot_ids"], sid.nbytes, 2) == 0
+    return sum(len(np.unique(sid[l])) for l in range(L))
 
 
 def qwen3_mxfp4(args, m, torch, hip, wr_d, b_d):
@@ -425,7 +493,7 @@ def qwen3_mxfp4(args, m, torch, hip, wr_d, b_d):
         synth.fill_records(args.seed, l, 0, E, H, F, synth.MXFP4, p, stride)
         if l % 16 == 15:
             log("mxfp4 host store: %d/%d layers filled (%.0f s)" % (l + 1, L, time.time() - t0))
-    warm, steps, prof = args.warmup, args.steps, args.prof_steps
+    warm, steps, prof = SS_WARM, SS_STEPS, args.prof_steps
     xs = synth.tokens(args.seed, 100 + T, T, H, warm + steps + prof, 0.9, synth.BF16)
     xs_d = torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16).to(dev)
     c = m.moe_chain_create(hs, wr_d, b_d, T, 0)
@@ -753,7 +821,8 @@ def eviction_compare(args, m, hip, torch, handles, wr_d, b_d, run_decode, token_
                     hot = np.argsort(-cnt[l], kind="stable")[:SLOTS // 2].astype(np.int32)
                     m.moe_offload_pin(h, torch.from_numpy(hot).to("cuda"), len(hot), torch.cuda.current_stream())
                 torch.cuda.synchronize()
-            ts, msps, d, c, bufs, _ = run_decode(T, warm, steps, "eviction-" + name, xs_d=xs_d, hs=hs)
+            ts, msps, d, c, bufs, _ = run_decode(T, warm, steps, "eviction-" + name, xs_d=xs_d, hs=hs,
+                                                 fresh=name != "pinned")
             xl = np.empty((T, H), dtype=np.uint16)
             assert hip.hipMemcpy(xl.ctypes.data, bufs["x"] + len(hs) * T * H * 2, xl.nbytes, 2) == 0
             last[name] = xl

@@ -120,7 +120,7 @@ hipError_t issue(moe_chain* c, hipStream_t cs) {
     // a decode step's misses are read through by its FFN launches instead of a copy launch
     const bool fill = c->read_through && moe::ffn_reads_through(h, T);
     if (!fill) CHK(moe::launch_copy(h, h->cache.copy_list, cs));
-    if (look) {  // prefetch copy for layer l+1 behind layer l's demand copy
+    if (look) {  // prefetch copy for layer l+1, after layer l's copy launch (read-through: after its control step)
       CHK(hipEventRecord(c->ev_demand[l], cs));
       CHK(hipStreamWaitEvent(c->sf, c->ev_demand[l], 0));
       CHK(moe::launch_copy(hn, hn->cache.pf_list, c->sf));

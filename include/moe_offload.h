@@ -26,8 +26,9 @@
  *     host sync), Prefill (whole-layer staging when a call touches more distinct
  *     experts than slots), and the GEMM reading [num_slots, N, K] instead of
  *     [num_experts, N, K]; "Supported" — every [E, ...] tensor (weights and scales)
- *     in host RAM, unsupported inputs fail with a clear error; the opening
- *     paragraph — placement never changes routing or precision.
+ *     in host RAM, inputs outside the supported set rejected with an explanatory
+ *     message; the opening paragraph — the share of experts kept on the GPU
+ *     alters neither the routing nor the numerics.
  *   FreeToken issue #677, "Proposal" — router lookahead, install of predicted
  *     experts as low-priority slots (usage 0, first evicted), copy on a side
  *     stream, every slot-map writer on the compute stream.
@@ -99,9 +100,10 @@ enum {
 enum {
   MOE_DEV_ERR_BAD_ID = 1,     /* a routed or predicted id outside [0, E) */
   MOE_DEV_ERR_NAN = 2,        /* a NaN router logit (selection then treats it as -inf) */
-  MOE_DEV_ERR_AUDIT = 4,      /* audit mode: slot maps not mutually inverse, or a needed expert not resident */
-  MOE_DEV_ERR_TOO_MANY = 8    /* more (t, j) pairs than max_tokens * top_k */
+  MOE_DEV_ERR_AUDIT = 4       /* audit mode: slot maps not mutually inverse, or a needed expert not resident */
 };
+/* (A call with more pairs than max_tokens * top_k cannot reach the device: every
+ * entry point rejects T > max_tokens with MOE_EINVAL before it launches.) */
 
 /* creation flags */
 enum {
@@ -112,7 +114,8 @@ enum {
 
 typedef struct {
   int32_t num_experts;   /* E, 1..1024 */
-  int32_t num_slots;     /* S, top_k <= S <= E ("at least one top-k decode step") */
+  int32_t num_slots;     /* S, top_k <= S <= E (xinfer-ai docs, "Options": the slot count never falls
+                            below what one token's top-k needs) */
   int32_t hidden;        /* H, multiple of 64 for MOE_F32, of 128 otherwise */
   int32_t ffn;           /* F, multiple of 64 for MOE_F32, of 128 otherwise */
   int32_t top_k;         /* k, 1..16 */
@@ -185,7 +188,10 @@ void moe_offload_destroy(moe_offload* h);
  * (record e at host + e * record_stride).  Host address; pinned, mapped. */
 int moe_offload_host_records(moe_offload* h, void** host, size_t* record_stride, size_t* record_bytes);
 
-/* Router: logits l = x Wr^T + b (binary32, one fixed summation order: chunks
+/* Router (xinfer-ai 0.14.6 docs/moe_offload.md, "How it works", Decode: the
+ * routed experts of each call are what the slot table is asked for; opening
+ * paragraph: slot placement leaves this routing untouched).
+ * Logits l = x Wr^T + b (binary32, one fixed summation order: chunks
  * of 8 elements, 64 lanes each owning every 64th chunk, an FMA chain per lane,
  * an xor-butterfly over the lanes, then + b), top-k by (logit descending, id
  * ascending), weights = softmax over the k chosen logits.
@@ -197,7 +203,10 @@ int moe_offload_host_records(moe_offload* h, void** host, size_t* record_stride,
 int moe_route_topk(moe_offload* h, const void* x, const void* w_router, const float* bias, int32_t T,
                    int32_t* ids, float* w, void* stream);
 
-/* LRU slot table update for one call (single workgroup, fixed shape):
+/* LRU slot table update for one call (xinfer-ai 0.14.6 docs/moe_offload.md,
+ * "How it works", Decode: look-up in a per-layer LRU table on the GPU,
+ * least-recently-used slots for the misses, expert ids rewritten to slot ids,
+ * the miss count left in device memory, a fixed launch shape; single workgroup):
  * D = distinct ids.  Victims are the slots not holding an expert of D, in
  * (free first, then least recently used, then lowest slot) order; with
  * MOE_FLAG_SCORED, (free first, then lowest usage score, then least recently
@@ -216,13 +225,19 @@ int moe_route_topk(moe_offload* h, const void* x, const void* w_router, const fl
  * Asynchronous, capture-safe; the table's only writer besides install/stage. */
 int moe_slot_ensure(moe_offload* h, const int32_t* ids, int32_t T, int32_t* slot_ids, void* stream);
 
-/* Copy the current copy list's records from the mapped host store into slots
+/* Miss copy (xinfer-ai 0.14.6 docs/moe_offload.md, "How it works", Decode: a
+ * second kernel moves the missing experts from device-mapped pinned host
+ * memory into their slots, its launch shape fixed and its count read on the
+ * device).
+ * Copy the current copy list's records from the mapped host store into slots
  * or staging with 16-byte loads (fixed grid; the count is read on the device,
  * an empty list costs one empty launch).  No-op for MOE_MODE_STAGED_ALL.
  * Asynchronous, capture-safe. */
 int moe_copy_misses(moe_offload* h, void* stream);
 
-/* Expert FFN and combine over the slot tensor:
+/* Expert FFN and combine over the slot tensor (xinfer-ai 0.14.6
+ * docs/moe_offload.md, "How it works": the expert GEMMs read [num_slots, N, K]
+ * slot tensors in place of [num_experts, N, K]):
  *   y_t = sum_j w[t][j] * Wd_r silu(Wg_r x_t) * (Wu_r x_t)   (j = 0..k-1 in order)
  *         + the same FFN of shared_record on x_t (weight 1) if shared_record != NULL,
  *   r = slot_ids[t][j] (slot or staging record), rounded once to the activation dtype.
@@ -244,7 +259,11 @@ int moe_slot_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const f
  * Asynchronous, capture-safe. */
 int moe_rmsnorm(const void* x, void* out, int32_t T, int32_t H, int32_t dtype, float eps, void* stream);
 
-/* Prefill entry (host-synchronising, not capturable): count the distinct ids
+/* Prefill entry (xinfer-ai 0.14.6 docs/moe_offload.md, "How it works",
+ * Prefill: a call needing more distinct experts than the layer has slots gets
+ * the whole layer copied into a staging buffer by a pinned asynchronous copy,
+ * and the GEMMs read the staging buffer).
+ * Host-synchronising, not capturable: count the distinct ids
  * of the call.  More than S: copy the whole layer host -> staging with an
  * asynchronous DMA copy, rewrite ids to S + id, copy list {STAGED_ALL, E, ...},
  * slot table untouched (tick advances), *staged_out = 1.  Otherwise run
@@ -264,9 +283,6 @@ int moe_prefill_stage(moe_offload* h, const int32_t* ids, int32_t T, int32_t* sl
  *   pred_ids: device [T, k] int32.  0 <= max_n <= S. */
 int moe_prefetch_install(moe_offload* h, const int32_t* pred_ids, int32_t T, int32_t max_n, void* stream);
 
-/* Copy the prefetch copy list's records (may run on a side stream after an
- * event that follows the install; the demand copy of this layer must wait
- * for it). */
 /* Profile-guided placement (npu-offload README, PolyStrata placement: a hot
  * set from a routing profile, here mixed with the dynamic cache): make the n
  * distinct experts experts_dev[0..n) resident and pinned, replacing any
@@ -281,6 +297,12 @@ int moe_prefetch_install(moe_offload* h, const int32_t* pred_ids, int32_t T, int
  * set.  Asynchronous; a slot-table writer: issue it on the compute stream. */
 int moe_offload_pin(moe_offload* h, const int32_t* experts_dev, int32_t n, void* stream);
 
+/* Prefetch copy (FreeToken issue #677, "Proposal", Install: the installed
+ * experts move on a separate stream, and the layer's own miss copy is ordered
+ * after them).  Copies the prefetch copy list's records from the mapped host
+ * store into their slots; it may run on a side stream after an event that
+ * follows the install, and this layer's FFN (and demand copy) must wait for it.
+ * Asynchronous, capture-safe. */
 int moe_copy_prefetch(moe_offload* h, void* stream);
 
 /* Synchronise the device and read the counters and the sticky error word. */
@@ -344,12 +366,14 @@ int moe_offload_kernel_times(moe_offload* h, moe_kernel_times* out);
  *     x_{l+1} = round(x_l + y_l)
  * (a pre-norm residual stream between MoE layers; no other sublayer is modelled).
  * prefetch_n > 0 builds the router-lookahead variant (FreeToken issue #677,
- * "Proposal"): at the start of layer l-1 (l >= 1) a side stream runs layer l's
- * router on layer l-1's router input xn_{l-1}; after ensure of layer l-1 the compute stream joins it
- * and installs up to prefetch_n predicted experts into layer l (the only
- * slot-table writers stay on the compute stream); a copy stream copies them
- * after layer l-1's demand copy, and layer l's demand copy waits for it.
- * All streams have the default priority.
+ * "Proposal"): layer l's router (l >= 1) also runs on layer l-1's router input
+ * xn_{l-1}, and layer l-1's control step installs up to prefetch_n of the
+ * predicted experts into layer l (every slot-table writer stays on the compute
+ * stream).  The installed records move on a separate copy stream, started
+ * once layer l-1's own missed records are in hand (after its copy launch; with
+ * read-through, after its control step, since its FFN launches fetch them
+ * themselves); nothing of layer l that reads slots starts before that copy has
+ * finished.  All streams have the default priority.
  *
  * The chain owns its activation buffers (device):
  *   x      [L+1][T][H]  x[0] is the step input (caller writes it before run), x[l+1] = x[l] + y[l]

@@ -9,7 +9,8 @@
  * Sources ("the pages"):
  *   [xinfer]   xinfer-ai 0.14.6 docs/moe_offload.md (my.diffend.io npm diff page),
  *              sections "How it works" (Decode, Prefill, slot tensors) and the
- *              opening paragraph ("Placement never changes routing or precision").
+ *              opening paragraph (how many experts sit on the GPU changes neither
+ *              the routing nor the numerics).
  *   [freetoken] FreeToken issue #677 "prefetch the next layer's experts from a router
  *              lookahead during offloaded decode", section "Proposal"
  *              (Lookahead, Install, Correctness constraint).
@@ -471,8 +472,8 @@ int orc_distinct(const int32_t* ids, int n, int E) {
 }
 
 /* Prefetch install, [freetoken] "Install": up to max_n predicted experts that
- * are not resident become low-priority entries ("held, usage 0, first to be
- * evicted").  READING:
+ * are not resident become low-priority entries: kept resident at usage 0, so
+ * they are the first victims.  READING:
  *   P = distinct predicted ids (pred: T rows of k ids, in top-k position order);
  *   candidates = P \ R ordered by (number of tokens predicting e descending,
  *                best top-k position ascending, id ascending);
