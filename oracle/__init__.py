@@ -31,7 +31,7 @@ _LIB = os.path.join(_HERE, "_build", "libmoe_oracle.so")
 _lib = None
 
 F32, BF16, FP8, MXFP4 = 0, 1, 2, 3
-LRU, SCORED = 0, 1  # eviction policies
+LRU, SCORED, FREQ = 0, 1, 2  # eviction policies
 SCORE_MAX = (1 << 20) - 1
 SLOTS, STAGED, STAGED_ALL = 0, 1, 2
 
@@ -71,6 +71,7 @@ def lib():
         L.orc_cache_free.argtypes = [vp]
         L.orc_cache_set_policy.argtypes = [vp, i32]
         L.orc_cache_scores.argtypes = [vp, vp]
+        L.orc_cache_act.argtypes = [vp, vp]
         L.orc_cache_pinned.argtypes = [vp, vp]
         L.orc_pin.argtypes = [vp, vp, i32, vp]
         L.orc_pin.restype = i32
@@ -289,6 +290,11 @@ class Cache:
     def scores(self):
         out = np.empty(self.S, np.uint32)
         lib().orc_cache_scores(self._c, _p(out))
+        return out
+
+    def activations(self):
+        out = np.empty(self.E, np.uint32)
+        lib().orc_cache_act(self._c, _p(out))
         return out
 
     def counters(self):

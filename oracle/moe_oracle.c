@@ -244,8 +244,19 @@ int orc_topk(const float* logits, int T, int E, int k, int32_t* ids, double* w) 
  * expert is loaded or installed into it.  With policy ORC_SCORED the victim
  * key is (occupied, score, last_use, slot): least used first, then least
  * recently used, then the lower slot.  Everything else is as above.
+ *
+ * Activation-aware eviction (READING of [moe-infinity] "Overview" and "Key
+ * Features": the cache keeps the experts that are activated most often on the
+ * GPU; the page gives no rule beyond that): every expert keeps an activation
+ * count, the number of ensure calls that routed to it since the cache was
+ * created (per call, saturating at 2^20 - 1), which survives eviction and
+ * reloading.  With policy ORC_FREQ the victim key is (occupied, never used
+ * since install (last_use = 0) first, activation count of the held expert,
+ * last_use, slot): installed slots still go first as the prefetch rule asks,
+ * then the least activated expert, then the least recently used, then the
+ * lower slot.  Installs and pins do not count as activations.
  */
-enum { ORC_LRU = 0, ORC_SCORED = 1 };
+enum { ORC_LRU = 0, ORC_SCORED = 1, ORC_FREQ = 2 };
 #define ORC_SCORE_MAX ((1u << 20) - 1u)
 
 typedef struct {
@@ -255,6 +266,7 @@ typedef struct {
   int32_t* expert_of;
   uint64_t* last_use;
   uint32_t* score;
+  uint32_t* act;         /* [E] activation count (ORC_FREQ key; kept under every policy) */
   unsigned char* pinned; /* [S] profile-guided placement: never a victim */
   uint64_t tick;
   /* cumulative counters */
@@ -270,6 +282,7 @@ orc_cache* orc_cache_new(int E, int S) {
   c->expert_of = (int32_t*)malloc(sizeof(int32_t) * (size_t)S);
   c->last_use = (uint64_t*)calloc((size_t)S, sizeof(uint64_t));
   c->score = (uint32_t*)calloc((size_t)S, sizeof(uint32_t));
+  c->act = (uint32_t*)calloc((size_t)E, sizeof(uint32_t));
   c->pinned = (unsigned char*)calloc((size_t)S, 1);
   for (int e = 0; e < E; ++e) c->slot_of[e] = -1;
   for (int s = 0; s < S; ++s) c->expert_of[s] = -1;
@@ -282,11 +295,16 @@ void orc_cache_free(orc_cache* c) {
   free(c->expert_of);
   free(c->last_use);
   free(c->score);
+  free(c->act);
   free(c->pinned);
   free(c);
 }
 
-void orc_cache_set_policy(orc_cache* c, int policy) { c->policy = policy == ORC_SCORED ? ORC_SCORED : ORC_LRU; }
+void orc_cache_set_policy(orc_cache* c, int policy) {
+  c->policy = (policy == ORC_SCORED || policy == ORC_FREQ) ? policy : ORC_LRU;
+}
+
+void orc_cache_act(const orc_cache* c, uint32_t* act) { memcpy(act, c->act, sizeof(uint32_t) * (size_t)c->E); }
 
 void orc_cache_scores(const orc_cache* c, uint32_t* score) {
   memcpy(score, c->score, sizeof(uint32_t) * (size_t)c->S);
@@ -309,11 +327,18 @@ void orc_cache_counters(const orc_cache* c, uint64_t out[7]) {
   out[4] = c->staged_copies; out[5] = c->prefetch_installs; out[6] = c->prefetch_hits;
 }
 
-/* does slot a come before slot b in victim order (occupied, last_use, slot)? */
+/* does slot a come before slot b in victim order?  LRU (occupied, last_use, slot); scored (occupied,
+ * score, last_use, slot); activation-aware (occupied, last_use != 0, activation count, last_use, slot) */
 static int victim_before(const orc_cache* c, int a, int b) {
   int oa = c->expert_of[a] >= 0, ob = c->expert_of[b] >= 0;
   if (oa != ob) return oa < ob;
   if (c->policy == ORC_SCORED && c->score[a] != c->score[b]) return c->score[a] < c->score[b];
+  if (c->policy == ORC_FREQ && oa) { /* both occupied */
+    int ua = c->last_use[a] != 0, ub = c->last_use[b] != 0;
+    if (ua != ub) return ua < ub;
+    uint32_t fa = c->act[c->expert_of[a]], fb = c->act[c->expert_of[b]];
+    if (fa != fb) return fa < fb;
+  }
   if (c->last_use[a] != c->last_use[b]) return c->last_use[a] < c->last_use[b];
   return a < b;
 }
@@ -416,6 +441,8 @@ int orc_ensure(orc_cache* c, const int32_t* ids, int n, int k, int32_t* slot_ids
       c->last_use[s] = c->tick;
       if (c->score[s] < ORC_SCORE_MAX) c->score[s] += 1;
     }
+  for (int e = 0; e < E; ++e) /* every routed expert, resident or staged, was activated by this call */
+    if (inD[e] && c->act[e] < ORC_SCORE_MAX) c->act[e] += 1;
   int count = 0;
   for (int e = 0; e < E; ++e) {
     if (!miss[e]) continue;

@@ -62,16 +62,19 @@ def test_single_id_calls_match_mattson_and_textbook_lru(orc, seed):
 
 class BruteCache:
     """The batched rules restated plainly (sorted(), dicts), independently of the C code.
-    scored=True: least-used slots go first (usage = calls since loaded, capped), then LRU."""
+    scored=True: least-used slots go first (usage = calls since loaded, capped), then LRU.
+    freq=True: slots installed and not used since go first, then the expert activated by the fewest
+    calls since the cache was created (kept across evictions, capped), then LRU."""
 
-    def __init__(self, E, S, scored=False, cap=(1 << 20) - 1):
+    def __init__(self, E, S, scored=False, cap=(1 << 20) - 1, freq=False):
         self.E, self.S = E, S
         self.held = [None] * S
         self.home = {}
         self.used = [0] * S
         self.uses = [0] * S
+        self.fired = [0] * E  # activations per expert
         self.clock = 0
-        self.scored, self.cap = scored, cap
+        self.scored, self.cap, self.freq = scored, cap, freq
         self.pinned = set()
 
     def _victims(self, protect):
@@ -79,6 +82,12 @@ class BruteCache:
                  if s not in self.pinned and (self.held[s] is None or self.held[s] not in protect)]
         if self.scored:
             return sorted(cands, key=lambda s: (self.held[s] is not None, self.uses[s], self.used[s], s))
+        if self.freq:
+            def key(s):
+                if self.held[s] is None:
+                    return (0, 0, 0, 0, s)
+                return (1, self.used[s] != 0, self.fired[self.held[s]], self.used[s], s)
+            return sorted(cands, key=key)
         return sorted(cands, key=lambda s: (self.held[s] is not None, self.used[s], s))
 
     def _put(self, e, s):
@@ -105,6 +114,7 @@ class BruteCache:
             if e in self.home:
                 self.used[self.home[e]] = self.clock
                 self.uses[self.home[e]] = min(self.uses[self.home[e]] + 1, self.cap)
+            self.fired[e] = min(self.fired[e] + 1, self.cap)
         rec = lambda e: self.home.get(e, self.S + e)
         return [rec(e) for e in ids], int(over), [(e, rec(e)) for e in miss]
 
@@ -185,15 +195,15 @@ def _check_invariants(c, ids, slot_ids, mode, pairs, before, pinned0=None):
         assert (eo0[s] < 0 or eo0[s] not in D) and not pinned0[s]
 
 
-@pytest.mark.parametrize("scored", [False, True])
+@pytest.mark.parametrize("policy", ["lru", "scored", "freq"])
 @pytest.mark.parametrize("seed", range(8))
-def test_batched_calls_match_brute_force(orc, seed, scored):
+def test_batched_calls_match_brute_force(orc, seed, policy):
     rng = np.random.default_rng(100 + seed)
     E = int(rng.choice([8, 16, 32]))
     k = int(rng.choice([1, 2, 4]))
     S = int(rng.integers(k, E + 1))
-    c = orc.Cache(E, S, policy=orc.SCORED if scored else orc.LRU)
-    b = BruteCache(E, S, scored=scored)
+    c = orc.Cache(E, S, policy={"lru": orc.LRU, "scored": orc.SCORED, "freq": orc.FREQ}[policy])
+    b = BruteCache(E, S, scored=policy == "scored", freq=policy == "freq")
     p = 1.0 / np.arange(1, E + 1) ** rng.uniform(0.3, 1.5)
     for step in range(200):
         T = int(rng.integers(1, 6))
@@ -218,6 +228,7 @@ def test_batched_calls_match_brute_force(orc, seed, scored):
         assert mode == em
         assert [tuple(map(int, r)) for r in pairs] == ep
         assert c.scores().tolist() == b.uses
+        assert c.activations().tolist() == b.fired
         _check_invariants(c, ids, slot_ids, mode, pairs, before, pinned0)
 
 
@@ -356,3 +367,35 @@ def test_pinned_experts_are_never_evicted(orc):
     assert pairs.tolist() == [[3, 0]]
     with pytest.raises(ValueError):
         c.pin(np.array([1, 1], np.int32))  # repeated id: nothing changes
+
+
+def test_activation_aware_eviction_keeps_the_most_activated_expert(orc):
+    # two slots, four experts.  Expert 0 is routed by three calls, evicted by a call that needs both
+    # slots, and reloaded; expert 1 is loaded once and routed twice.  At the last call both slots were
+    # used at the same tick: LRU takes the lower slot (expert 0), scored eviction takes expert 0 as
+    # well (used once since its reload, against twice for expert 1), the activation-aware cache keeps
+    # expert 0 (four activations, expert 1 two) and evicts expert 1.
+    calls = [[[0]], [[0]], [[0]], [[1, 2]], [[0, 1]], [[3]]]
+    last = {}
+    for policy in (orc.LRU, orc.SCORED, orc.FREQ):
+        c = orc.Cache(4, 2, policy=policy)
+        for ids in calls:
+            _, mode, pairs = c.ensure(np.array(ids, np.int32))
+            assert mode == orc.SLOTS
+        last[policy] = pairs.tolist()
+        if policy == orc.FREQ:
+            so, eo, lu, tick = c.state()
+            assert eo.tolist() == [0, 3] and c.activations().tolist() == [4, 2, 1, 1] and lu.tolist() == [5, 6]
+    assert last[orc.LRU] == [[3, 0]] and last[orc.SCORED] == [[3, 0]] and last[orc.FREQ] == [[3, 1]]
+
+
+def test_activation_aware_installs_go_first(orc):
+    # an installed expert with a long history is still the first victim until a call uses it
+    c = orc.Cache(4, 2, policy=orc.FREQ)
+    for ids in ([[0]], [[0]], [[0]], [[1, 2]]):
+        c.ensure(np.array(ids, np.int32))
+    # slots hold 2 (slot 0) and 1 (slot 1); expert 0 has three activations and is installed over one of them
+    assert c.install(np.array([[0]], np.int32), 1).tolist() == [[0, 0]]
+    _, _, pairs = c.ensure(np.array([[3]], np.int32))
+    assert pairs.tolist() == [[3, 0]]  # the installed, unused expert 0 goes first despite its count
+    assert c.activations().tolist() == [3, 1, 1, 1]
