@@ -19,7 +19,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe_offload.h")
 
 F32, BF16, FP8, MXFP4 = 0, 1, 2, 3
 MODE_SLOTS, MODE_STAGED, MODE_STAGED_ALL = 0, 1, 2
-FLAG_AUDIT, FLAG_HOST_COHERENT, FLAG_SCORED = 1, 2, 4
+FLAG_AUDIT, FLAG_HOST_COHERENT, FLAG_SCORED, FLAG_FREQ = 1, 2, 4, 8
 DEV_ERR_BAD_ID, DEV_ERR_NAN, DEV_ERR_AUDIT = 1, 2, 4
 EINVAL, ENOMEM, EHIP, EUNSUPPORTED, EDEVICE = -1, -2, -3, -4, -5
 
@@ -61,7 +61,7 @@ class Info(ctypes.Structure):
                 ("ffn_h", ctypes.c_void_p), ("ffn_part", ctypes.c_void_p), ("ffn_groups", ctypes.c_void_p),
                 ("record_bytes", ctypes.c_size_t), ("record_stride", ctypes.c_size_t)] + \
                [(n, ctypes.c_int32) for n in ("E", "S", "H", "F", "k", "dtype", "max_tokens", "device")] + \
-               [("score", ctypes.c_void_p), ("pinned", ctypes.c_void_p)]
+               [("score", ctypes.c_void_p), ("pinned", ctypes.c_void_p), ("act", ctypes.c_void_p)]
 
 
 class ChainBuffers(ctypes.Structure):

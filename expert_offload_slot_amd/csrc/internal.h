@@ -17,6 +17,9 @@ constexpr int kCopyUnroll = 4;      // 16-byte loads in flight per thread
 constexpr int kRouteTokens = 4;     // tokens per router wave
 constexpr int kF32Rows = 64;        // rows per work item on the fp32 path
 
+// victim orders of the slot table (table.h victim_key)
+constexpr int kPolicyLru = 0, kPolicyScored = 1, kPolicyFreq = 2;
+
 // counters[] layout (device, uint64)
 enum { C_CALLS = 0, C_HITS, C_MISSES, C_STAGED_CALLS, C_STAGED_COPIES, C_PF_INSTALLS, C_PF_HITS, C_BYTES, C_N };
 
@@ -26,6 +29,7 @@ struct CacheDev {
   int32_t* expert_of;   // [S]
   uint64_t* last_use;   // [S]
   uint32_t* score;      // [S] usage score (scored eviction)
+  uint32_t* act;        // [E] activation count per expert (activation-aware eviction)
   int32_t* pinned;      // [S] 1: never a victim (profile-guided placement)
   uint64_t* tick;       // [1]
   int32_t* copy_list;   // [2 + 2*max(S,E)]
@@ -33,7 +37,7 @@ struct CacheDev {
   uint64_t* counters;   // [C_N]
   int32_t* err;         // [1] sticky MOE_DEV_ERR_* bits
   int E, S;
-  int scored;           // 1: victims by (occupied, score, last_use, slot)
+  int policy;           // victim order: kPolicyLru, kPolicyScored, kPolicyFreq (table.h)
   uint64_t record_bytes;
 };
 

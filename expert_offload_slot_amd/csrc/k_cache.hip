@@ -84,7 +84,10 @@ __global__ void k_stage_all(CacheDev c, const int32_t* __restrict__ ids, int n, 
 // empty cache, zero counters and error, empty lists
 __global__ void k_reset(CacheDev c) {
   const int i0 = blockIdx.x * blockDim.x + threadIdx.x, step = gridDim.x * blockDim.x;
-  for (int e = i0; e < c.E; e += step) c.slot_of[e] = -1;
+  for (int e = i0; e < c.E; e += step) {
+    c.slot_of[e] = -1;
+    c.act[e] = 0;
+  }
   for (int s = i0; s < c.S; s += step) {
     c.expert_of[s] = -1;
     c.last_use[s] = 0;

@@ -112,6 +112,8 @@ int moe_offload_create(const moe_offload_desc* d, moe_offload** out) {
                 d->ffn, mult);
   if (d->hidden > 65536 || d->ffn > 65536) return fail(MOE_EINVAL, "hidden/ffn above 65536");
   if (d->max_tokens < 1 || d->max_tokens > 65536) return fail(MOE_EINVAL, "max_tokens=%d outside [1, 65536]", d->max_tokens);
+  if ((d->flags & MOE_FLAG_SCORED) && (d->flags & MOE_FLAG_FREQ))
+    return fail(MOE_EINVAL, "MOE_FLAG_SCORED and MOE_FLAG_FREQ are exclusive");
   if (d->share_host && !same_shape(d->share_host, d)) return fail(MOE_EINVAL, "share_host handle has another shape");
   if (d->share_staging && !same_shape(d->share_staging, d))
     return fail(MOE_EINVAL, "share_staging handle has another shape");
@@ -184,7 +186,7 @@ int moe_offload_create(const moe_offload_desc* d, moe_offload** out) {
     return o;
   };
   size_t o_slot_of = take(4 * (size_t)h->E), o_expert_of = take(4 * (size_t)h->S), o_last = take(8 * (size_t)h->S);
-  size_t o_score = take(4 * (size_t)h->S), o_pinned = take(4 * (size_t)h->S);
+  size_t o_score = take(4 * (size_t)h->S), o_pinned = take(4 * (size_t)h->S), o_act = take(4 * (size_t)h->E);
   size_t o_tick = take(8), o_list = take(4 * (2 + 2 * (size_t)maxSE)), o_pf = take(4 * (2 + 2 * (size_t)h->S));
   size_t o_cnt = take(8 * moe::C_N), o_err = take(4), o_logits = take(4 * (size_t)h->max_tokens * h->E);
   size_t o_grp = take(4 * (size_t)h->gl.words());
@@ -198,7 +200,9 @@ int moe_offload_create(const moe_offload_desc* d, moe_offload** out) {
   h->cache.last_use = (uint64_t*)(b + o_last);
   h->cache.score = (uint32_t*)(b + o_score);
   h->cache.pinned = (int32_t*)(b + o_pinned);
-  h->cache.scored = (h->flags & MOE_FLAG_SCORED) ? 1 : 0;
+  h->cache.act = (uint32_t*)(b + o_act);
+  h->cache.policy = (h->flags & MOE_FLAG_SCORED) ? moe::kPolicyScored
+                                                 : ((h->flags & MOE_FLAG_FREQ) ? moe::kPolicyFreq : moe::kPolicyLru);
   h->cache.tick = (uint64_t*)(b + o_tick);
   h->cache.copy_list = (int32_t*)(b + o_list);
   h->cache.pf_list = (int32_t*)(b + o_pf);
@@ -425,6 +429,7 @@ int moe_offload_query(const moe_offload* h, moe_info* out) {
   out->last_use = h->cache.last_use;
   out->score = h->cache.score;
   out->pinned = h->cache.pinned;
+  out->act = h->cache.act;
   out->copy_list = h->cache.copy_list;
   out->prefetch_list = h->cache.pf_list;
   out->slots = h->slots;

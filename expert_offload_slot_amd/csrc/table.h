@@ -15,14 +15,25 @@
 
 namespace moe {
 
-// victim order as one integer, ascending: LRU (occupied, last_use, slot); scored
-// (occupied, score, last_use, slot).  last_use is a call count, below 2^33 in
-// any run; scores saturate at kScoreMax (20 bits).
+// victim order as one integer, ascending:
+//   LRU              (occupied, last_use, slot);
+//   scored           (occupied, score, last_use, slot);
+//   activation-aware (occupied, used since install (last_use != 0), activations of the held expert,
+//                     last_use, slot).
+// last_use is a call count, below 2^32 in any run; scores and activation counts saturate at kScoreMax
+// (20 bits).
 constexpr uint32_t kScoreMax = (1u << 20) - 1u;
-__device__ __forceinline__ uint64_t victim_key(const CacheDev& c, bool occ, uint32_t score, uint64_t lu, int slot) {
-  if (c.scored)
-    return (occ ? (1ull << 63) : 0ull) | ((uint64_t)score << 43) | ((lu & ((1ull << 33) - 1)) << 10) | (uint64_t)slot;
-  return (occ ? (1ull << 63) : 0ull) | ((lu & ((1ull << 53) - 1)) << 10) | (uint64_t)slot;
+__device__ __forceinline__ uint64_t victim_key(const CacheDev& c, bool occ, uint32_t score, uint32_t act, uint64_t lu,
+                                               int slot) {
+  const uint64_t o = occ ? (1ull << 63) : 0ull;
+  if (c.policy == kPolicyScored)
+    return o | ((uint64_t)score << 43) | ((lu & ((1ull << 33) - 1)) << 10) | (uint64_t)slot;
+  if (c.policy == kPolicyFreq) {
+    if (!occ) return (uint64_t)slot;
+    return o | (lu != 0 ? (1ull << 62) : 0ull) | ((uint64_t)act << 42) | ((lu & ((1ull << 32) - 1)) << 10) |
+           (uint64_t)slot;
+  }
+  return o | ((lu & ((1ull << 53) - 1)) << 10) | (uint64_t)slot;
 }
 
 struct SharedTable {
@@ -30,6 +41,7 @@ struct SharedTable {
   int expert_of[kMaxExperts];
   uint64_t last_use[kMaxExperts];
   uint32_t score[kMaxExperts];
+  uint32_t act[kMaxExperts];  // activation count per expert
   int pinned[kMaxExperts];  // 1: never a victim (profile-guided placement)
   int flag[kMaxExperts];   // ensure: expert in D; install: tokens predicting it
   int aux[kMaxExperts];    // ensure: pairs routed to it; install: best top-k position
@@ -44,7 +56,7 @@ struct SharedTable {
 // The table as one thread holds it between fetch_table and put_table.
 struct TableRegs {
   int s = -1, e = -1, pin = 0;
-  uint32_t sc = 0u;
+  uint32_t sc = 0u, ac = 0u;
   uint64_t lu = 0ull, tc = 0ull;
 };
 
@@ -54,7 +66,10 @@ struct TableRegs {
 __device__ __forceinline__ TableRegs fetch_table(const CacheDev& c) {
   const int tid = threadIdx.x, u = tid - 64 * (kWaves - 1);
   TableRegs r;
-  if (tid < c.E) r.s = c.slot_of[tid];
+  if (tid < c.E) {
+    r.s = c.slot_of[tid];
+    r.ac = c.act[tid];
+  }
   if (tid < c.S) {
     r.e = c.expert_of[tid];
     r.lu = c.last_use[tid];
@@ -78,6 +93,7 @@ __device__ __forceinline__ void put_table(const CacheDev& c, const TableRegs& r,
       s = -1;
     }
     t.slot_of[tid] = s;
+    t.act[tid] = r.ac;
   }
   if (tid < c.S) {
     int e = r.e;
@@ -99,7 +115,10 @@ __device__ __forceinline__ void load_table(const CacheDev& c, SharedTable& t) { 
 
 __device__ __forceinline__ void store_table(const CacheDev& c, const SharedTable& t) {
   const int tid = threadIdx.x;
-  if (tid < c.E) c.slot_of[tid] = t.slot_of[tid];
+  if (tid < c.E) {
+    c.slot_of[tid] = t.slot_of[tid];
+    c.act[tid] = t.act[tid];
+  }
   if (tid < c.S) {
     c.expert_of[tid] = t.expert_of[tid];
     c.last_use[tid] = t.last_use[tid];
@@ -130,7 +149,8 @@ __device__ __forceinline__ void audit_table(const CacheDev& c, const SharedTable
 // slot_lds.  Record index r < S is slot r; r >= S is staging record r - S.
 //   victims:  slots not pinned and not holding an expert of D, in (free
 //             first, then least recently used, then lowest slot) order
-//             (scored: least used before least recently used);
+//             (scored: least used before least recently used; activation-aware:
+//             installed-unused, then least activated, before least recently used);
 //   misses <= victims: the misses in ascending id take the victims;
 //   misses >  victims (no pins: |D| > S): the misses claim the victims in
 //             install order (pairs routed to it desc, best top-k position asc,
@@ -189,7 +209,7 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
       const int ex = t.expert_of[tid];
       const bool occ = ex >= 0;
       elig = !t.pinned[tid] && (!occ || !t.flag[ex]);
-      vkey[tid] = elig ? victim_key(c, occ, t.score[tid], t.last_use[tid], tid) : ~0ull;
+      vkey[tid] = elig ? victim_key(c, occ, t.score[tid], occ ? t.act[ex] : 0u, t.last_use[tid], tid) : ~0ull;
     }
     int nv;
     (void)block_rank(elig, t.wave, &nv);  // its barriers also publish vkey
@@ -247,6 +267,7 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
     t.last_use[s] = tick;
     t.score[s] = old < kScoreMax ? old + 1 : old;
   }
+  if (inD && t.act[tid] < kScoreMax) t.act[tid] += 1;  // every routed expert, resident or staged
   __syncthreads();
   for (int i = tid; i < n; i += kBlock) {
     const int e = ids[i];
@@ -322,7 +343,7 @@ __device__ __forceinline__ void install_body(const CacheDev& c, SharedTable& t, 
     const int ex = t.expert_of[tid];
     const bool occ = ex >= 0;
     elig = !t.pinned[tid] && (!occ || t.flag[ex] == 0);
-    vkey[tid] = elig ? victim_key(c, occ, t.score[tid], t.last_use[tid], tid) : ~0ull;
+    vkey[tid] = elig ? victim_key(c, occ, t.score[tid], occ ? t.act[ex] : 0u, t.last_use[tid], tid) : ~0ull;
   }
   int nc, nv;
   (void)block_rank(cand, t.wave, &nc);  // its barriers also publish ckey / vkey
@@ -403,7 +424,7 @@ __device__ __forceinline__ void pin_body(const CacheDev& c, SharedTable& t, cons
     const int ex = t.expert_of[tid];
     const bool occ = ex >= 0;
     elig = !t.pinned[tid] && (!occ || !t.flag[ex]);
-    vkey[tid] = elig ? victim_key(c, occ, t.score[tid], t.last_use[tid], tid) : ~0ull;
+    vkey[tid] = elig ? victim_key(c, occ, t.score[tid], occ ? t.act[ex] : 0u, t.last_use[tid], tid) : ~0ull;
   }
   int nm, nv;
   const int mrank = block_rank(miss, t.wave, &nm);  // its barriers also publish vkey

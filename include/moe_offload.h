@@ -109,7 +109,13 @@ enum {
 enum {
   MOE_FLAG_AUDIT = 1,          /* check the slot table after every ensure/install (sets MOE_DEV_ERR_AUDIT) */
   MOE_FLAG_HOST_COHERENT = 2,  /* fine-grained (coherent) host store instead of coarse-grained */
-  MOE_FLAG_SCORED = 4          /* scored eviction: victims by (occupied, usage score, last_use, slot) */
+  MOE_FLAG_SCORED = 4,         /* scored eviction: victims by (occupied, usage score, last_use, slot) */
+  MOE_FLAG_FREQ = 8            /* activation-aware eviction (MoE-Infinity README, "Overview": the cache keeps
+                                  the most often activated experts): victims by (occupied, installed and
+                                  unused first, activation count of the held expert, last_use, slot); the
+                                  count of an expert is the number of ensure calls that routed to it since
+                                  create or reset (saturating at 2^20 - 1), kept across evictions.
+                                  Exclusive with MOE_FLAG_SCORED. */
 };
 
 typedef struct {
@@ -169,6 +175,8 @@ typedef struct {
   uint32_t* score;        /* [S]  usage score: ensure calls routed to the slot's expert since it was loaded
                              (saturating at 2^20 - 1); kept under both policies, used by MOE_FLAG_SCORED */
   int32_t* pinned;        /* [S]  1: the slot's expert is pinned (moe_offload_pin), never a victim */
+  uint32_t* act;          /* [E]  activation count per expert (ensure calls routing to it; kept under every
+                             policy, used by MOE_FLAG_FREQ) */
 } moe_info;
 
 /* copy-list modes (copy_list[0]) */

@@ -141,6 +141,9 @@ class GpuLayer:
     def pinned(self):
         return d2h(self.info["pinned"], 4 * self.S, np.int32)
 
+    def activations(self):
+        return d2h(self.info["act"], 4 * self.E, np.uint32)
+
     def stats(self):
         return m.moe_offload_stats(self.h)
 
@@ -149,6 +152,15 @@ class GpuLayer:
 
     def staging_bytes(self, e, nbytes):
         return d2h(self.info["staging"] + e * self.info["record_stride"], nbytes)
+
+
+def oracle_policy(flags):
+    """The oracle's eviction policy for a handle's create flags."""
+    if flags & m.FLAG_SCORED:
+        return oracle.SCORED
+    if flags & m.FLAG_FREQ:
+        return oracle.FREQ
+    return oracle.LRU
 
 
 def make_layer_inputs(seed, layer, E, H, F, wdt, zipf_s, shared=False):
@@ -175,6 +187,7 @@ def compare_call(gl, ol_step, T, y64=None, check_table=True, oracle_cache=None):
         assert np.array_equal(so, oso) and np.array_equal(eo, oeo) and np.array_equal(lu, olu)
         assert np.array_equal(gl.scores(), oracle_cache.scores())
         assert np.array_equal(gl.pinned(), oracle_cache.pinned())
+        assert np.array_equal(gl.activations(), oracle_cache.activations())
     if y64 is not None:
         err = row_rel_err(to_np(gl.y[:T]), y64, gl.wdt)
         assert err <= TOL[gl.wdt], err

@@ -84,3 +84,13 @@ def test_rmsnorm_rejects_bad_sizes_without_a_device():
     p = buf.ctypes.data
     for T, H, eps in ((0, 64, 1e-6), (1, 60, 1e-6), (1, 4, 1e-6), (1, 64, 0.0), (1, 64, -1.0)):
         assert L.moe_rmsnorm(p, p, T, H, m.F32, eps, None) == m.EINVAL, (T, H, eps)
+
+
+def test_exclusive_eviction_flags_are_rejected_before_any_device_call():
+    """Scored and activation-aware eviction are two victim orders: asking for both is EINVAL, decided
+    from the descriptor alone (no device is touched, so this runs without a GPU)."""
+    L = m.lib()
+    d = m.Desc(8, 4, 128, 128, 2, m.BF16, 4, 0, m.FLAG_SCORED | m.FLAG_FREQ, None, None)
+    out = ctypes.c_void_p()
+    assert L.moe_offload_create(ctypes.byref(d), ctypes.byref(out)) == m.EINVAL
+    assert b"exclusive" in L.moe_offload_last_error() and not out.value

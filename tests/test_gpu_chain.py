@@ -37,7 +37,8 @@ def test_rmsnorm_parity():
 
 
 class ChainModel:
-    def __init__(self, L, E, S, k, H, F, wdt, T, seed, prefetch_n=0, zipf=1.2, rho=0.9, shared=False, scored=False):
+    def __init__(self, L, E, S, k, H, F, wdt, T, seed, prefetch_n=0, zipf=1.2, rho=0.9, shared=False, scored=False,
+                 policy_flag=0):
         self.L, self.E, self.S, self.k, self.H, self.F, self.wdt, self.T = L, E, S, k, H, F, wdt, T
         self.hosts, self.routers, self.handles, self.shared = [], [], [], []
         rdt = 1 if wdt >= 2 else wdt  # fp8 and MXFP4 layers take a bf16 router and bf16 activations
@@ -45,7 +46,8 @@ class ChainModel:
             self.hosts.append(synth.records(seed, l, E, H, F, wdt))
             self.routers.append(synth.router(seed, l, E, H, rdt, zipf_s=zipf))
             self.shared.append(synth.records(seed, l, 1, H, F, wdt, shared=True)[0] if shared else None)
-            h = m.moe_offload_create(E, S, H, F, k, wdt, T, 0, m.FLAG_AUDIT | (m.FLAG_SCORED if scored else 0),
+            h = m.moe_offload_create(E, S, H, F, k, wdt, T, 0,
+                                     m.FLAG_AUDIT | (m.FLAG_SCORED if scored else 0) | policy_flag,
                                      None, self.handles[0] if l else None)
             m.host_array(h, E)[:, :self.hosts[l].shape[1]] = self.hosts[l]
             self.handles.append(h)
@@ -87,6 +89,9 @@ class ChainModel:
         sc = d2h(i["score"], 4 * self.S, np.uint32)
         return (int(lst[0]), lst[2:2 + 2 * lst[1]].reshape(-1, 2)), pf[2:2 + 2 * pf[1]].reshape(-1, 2), (so, eo, lu, sc)
 
+    def activations(self, l):
+        return d2h(self.info[l]["act"], 4 * self.E, np.uint32)
+
     def close(self):
         m.moe_chain_destroy(self.chain)
         for h in reversed(self.handles):
@@ -122,6 +127,7 @@ def oracle_replay_step(cm, caches, snap, prefetch_n, check_ffn=True):
         oso, oeo, olu, _ = caches[l].state()
         assert np.array_equal(so, oso) and np.array_equal(eo, oeo) and np.array_equal(lu, olu), l
         assert np.array_equal(sc, caches[l].scores()), l
+        assert np.array_equal(cm.activations(l), caches[l].activations()), l
 
 
 @pytest.mark.parametrize("prefetch_n", [0, 2])
@@ -213,6 +219,22 @@ def test_chain_scored_eviction(prefetch_n, T):
     caches = [oracle.Cache(E, S, cg.hosts[l], oracle.record_bytes(1, H, F), policy=oracle.SCORED) for l in range(L)]
     try:
         for s in range(10):
+            cg.run(s, graph=True)
+            oracle_replay_step(cg, caches, cg.snapshot(), prefetch_n)
+        assert all(m.moe_offload_stats(h)["error"] == 0 for h in cg.handles)
+    finally:
+        cg.close()
+
+
+@pytest.mark.parametrize("prefetch_n,T", [(0, 1), (3, 2), (0, 8)])
+def test_chain_activation_aware_eviction(prefetch_n, T):
+    """Activation-aware eviction in the decode chain, with and without lookahead installs."""
+    L, E, S, k, H, F = 3, 32, 8, 4, 256, 256
+    print("chain activation-aware eviction prefetch=%d T=%d" % (prefetch_n, T), flush=True)
+    cg = ChainModel(L, E, S, k, H, F, 1, T, 88, prefetch_n, policy_flag=m.FLAG_FREQ)
+    caches = [oracle.Cache(E, S, cg.hosts[l], oracle.record_bytes(1, H, F), policy=oracle.FREQ) for l in range(L)]
+    try:
+        for s in range(12):
             cg.run(s, graph=True)
             oracle_replay_step(cg, caches, cg.snapshot(), prefetch_n)
         assert all(m.moe_offload_stats(h)["error"] == 0 for h in cg.handles)

@@ -14,7 +14,8 @@ import torch
 import expert_offload_slot_amd as m
 import oracle
 import synth
-from gpu_harness import (GpuLayer, compare_call, d2h, h2d, make_layer_inputs, row_rel_err, to_dev, to_np)
+from gpu_harness import (GpuLayer, compare_call, d2h, h2d, make_layer_inputs, oracle_policy, row_rel_err, to_dev,
+                         to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -26,7 +27,7 @@ def run_sequence(E, S, k, H, F, wdt, zipf, seed, steps, Ts, shared=False, flags=
     maxT = max(Ts)
     gl = GpuLayer(E, S, k, H, F, wdt, maxT, host, wr, b, flags=flags, shared=sh)
     ol = oracle.Layer(E, S, k, H, F, wdt, host, wr, b, shared=sh,
-                      policy=oracle.SCORED if flags & m.FLAG_SCORED else oracle.LRU)
+                      policy=oracle_policy(flags))
     xs = synth.tokens(seed, 7, maxT, H, steps, 0.0, wdt)
     modes, errs = [], []
     try:
@@ -147,7 +148,14 @@ def test_scored_eviction_parity(E, S, k, Ts):
     run_sequence(E, S, k, 256, 256, 1, 1.2, 70 + E, 30, Ts, flags=m.FLAG_AUDIT | m.FLAG_SCORED)
 
 
-@pytest.mark.parametrize("flags", [m.FLAG_AUDIT, m.FLAG_AUDIT | m.FLAG_SCORED])
+@pytest.mark.parametrize("E,S,k,Ts", [(16, 6, 4, [1, 2, 3]), (32, 10, 4, [1, 4, 9]), (64, 12, 8, [1, 2])])
+def test_activation_aware_eviction_parity(E, S, k, Ts):
+    # activation-aware eviction: slot tables, per-expert activation counts, copy lists and counters
+    # bit-exact against the oracle, with Zipf routing and batches that overflow the cache
+    run_sequence(E, S, k, 256, 256, 1, 1.2, 75 + E, 30, Ts, flags=m.FLAG_AUDIT | m.FLAG_FREQ)
+
+
+@pytest.mark.parametrize("flags", [m.FLAG_AUDIT, m.FLAG_AUDIT | m.FLAG_SCORED, m.FLAG_AUDIT | m.FLAG_FREQ])
 def test_pinned_placement_parity(flags):
     # pinned sets replaced mid-stream (overlapping, then empty); with 3 of 6 slots pinned a batch of 3
     # overflows although |D| <= S
