@@ -88,6 +88,7 @@ def lib():
             "moe_slot_ensure": ([vp, vp, i32, vp, vp], i32),
             "moe_copy_misses": ([vp, vp], i32),
             "moe_slot_ffn": ([vp, vp, vp, vp, i32, vp, vp, vp, vp, vp], i32),
+            "moe_slot_ffn_noalloc": ([vp, vp, vp, vp, i32, vp, vp, vp, vp, vp], i32),
             "moe_rmsnorm": ([vp, vp, i32, i32, i32, ctypes.c_float, vp], i32),
             "moe_prefill_stage": ([vp, vp, i32, vp, P(ctypes.c_int32), vp], i32),
             "moe_prefetch_install": ([vp, vp, i32, i32, vp], i32),
@@ -183,6 +184,13 @@ def moe_slot_ffn(h, x, slot_ids, w, T, shared_record, y, residual=None, x_next=N
     return _check(lib().moe_slot_ffn(h, _addr(x), _addr(slot_ids), _addr(w), T, _addr(shared_record), _addr(y),
                                      _addr(residual), _addr(x_next), _stream(stream)))
 
+
+def moe_slot_ffn_noalloc(h, x, slot_ids, w, T, shared_record, y, residual=None, x_next=None, stream=None):
+    return _check(lib().moe_slot_ffn_noalloc(h, _addr(x), _addr(slot_ids), _addr(w), T, _addr(shared_record),
+                                             _addr(y), _addr(residual), _addr(x_next), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 RMS_EPS = 1e-6
 

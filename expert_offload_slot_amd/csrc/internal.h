@@ -132,9 +132,30 @@ hipError_t launch_stage_all(moe_offload* h, const int32_t* ids, int n, int32_t* 
 // combine = false: stop after the down projection (the chain takes the combine into the next router launch)
 // fill: where ffn_reads_through(h, T), the records of the copy list are read from the host store and
 // written to their slots by the FFN itself (the caller then launches no copy for the call)
+// The FFN workspace of one call: the group descriptor (layout from GroupLayout),
+// the h rows [T*k + T][F] and the fp32 partial outputs [T*k + T][H].  Null in
+// launch_ffn: the handle's own workspace (sized for max_tokens at create).
+struct FfnWork {
+  int32_t* grp;
+  void* hbuf;
+  float* part;
+  GroupLayout gl;
+};
 hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int T,
                       const void* shared, void* y, const void* residual, void* x_next, void* xn_next, float eps,
-                      hipStream_t s, bool grouped = false, bool combine = true, bool fill = false);
+                      hipStream_t s, bool grouped = false, bool combine = true, bool fill = false,
+                      const FfnWork* ws = nullptr);
+
+// File-scope device scratch for callers that cannot allocate (k_ffn.hip).
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+// Once per device, with that device current: looks up the scratch array's device
+// address (hipGetSymbolAddress) and keeps it; later calls return at once.
+hipError_t scratch_init(int device);
+// The device address kept by scratch_init (null before it succeeded on `device`).
+void* scratch_ptr(int device);
+// The FFN workspace of a call of T tokens carved from `base` (any 256-aligned
+// device buffer); *bytes gets its size.
+FfnWork ffn_work_in(const moe_offload* h, int T, void* base, size_t* bytes);
 bool ffn_reads_through(const moe_offload* h, int T);
 // Decode control step in one workgroup: top-k of h->logits (launch_logits first),
 // ensure, and the FFN grouping.  With hn (max_n > 0): also the top-k of

@@ -38,6 +38,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "grouping.h"
 #include "prof.h"
@@ -1255,9 +1256,60 @@ bool ffn_reads_through(const moe_offload* h, int T) {
   return h->dtype != MOE_F32 && (T == 1 || (T <= kDecodeMaxT && T * h->k <= kFillPairs));
 }
 
+// ------------------------------------------------------------------ scratch workspace
+// For callers that cannot allocate (graph capture, serving loops that forbid
+// allocation): one FFN workspace per device in a file-scope device array.  Host
+// code never passes `scratch` itself to a kernel: its name is a host-side
+// stand-in; the device address comes from hipGetSymbolAddress, once per device.
+namespace {
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+}  // namespace
+
+hipError_t scratch_init(int device) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch[device]) return hipSuccess;
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  if (cur != device) return hipErrorInvalidDevice;  // the caller makes `device` current
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (!ptr) return hipErrorInvalidSymbol;
+  g_scratch[device] = ptr;
+  return hipSuccess;
+}
+
+void* scratch_ptr(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  return g_scratch[device];
+}
+
+FfnWork ffn_work_in(const moe_offload* h, int T, void* base, size_t* bytes) {
+  FfnWork w;
+  w.gl.max_pairs = T * h->k;
+  w.gl.max_recs = std::min(T * h->k, h->S + h->E) + 1;
+  const size_t rows = (size_t)T * h->k + T;
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  const size_t g = al(4 * (size_t)w.gl.words());
+  const size_t hb = al((h->dtype == MOE_F32 ? 4 : 2) * rows * h->F);
+  const size_t pb = 4 * rows * h->H;
+  uint8_t* b = (uint8_t*)base;
+  w.grp = (int32_t*)b;
+  w.hbuf = b ? (void*)(b + g) : nullptr;
+  w.part = b ? (float*)(b + g + hb) : nullptr;
+  if (bytes) *bytes = g + hb + pb;
+  return w;
+}
+
 hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int T,
                       const void* shared, void* y, const void* residual, void* x_next, void* xn_next, float eps,
-                      hipStream_t s, bool grouped, bool combine, bool fill) {
+                      hipStream_t s, bool grouped, bool combine, bool fill, const FfnWork* ws) {
   FfnArgs a;
   a.x = x;
   a.slot_ids = slot_ids;
@@ -1266,9 +1318,9 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
   a.staging = h->staging;
   a.shared = (const uint8_t*)shared;
   a.stride = h->record_stride;
-  a.grp = h->grp;
-  a.hbuf = h->hbuf;
-  a.part = h->part;
+  a.grp = ws ? ws->grp : h->grp;
+  a.hbuf = ws ? ws->hbuf : h->hbuf;
+  a.part = ws ? ws->part : h->part;
   a.y = y;
   a.residual = residual ? residual : x;
   a.x_next = x_next;
@@ -1279,8 +1331,8 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
   a.F = h->F;
   a.S = h->S;
   a.E = h->E;
-  a.off_pairs = h->gl.off_pairs();
-  a.off_tiles = h->gl.off_tiles();
+  a.off_pairs = ws ? ws->gl.off_pairs() : h->gl.off_pairs();
+  a.off_tiles = ws ? ws->gl.off_tiles() : h->gl.off_tiles();
   a.max_routed = std::min(T * h->k, h->S + h->E);
   a.pair_items = T == 1 && h->dtype != MOE_F32 ? 1 : 0;
   fill = fill && ffn_reads_through(h, T);

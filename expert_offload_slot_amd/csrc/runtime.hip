@@ -218,6 +218,8 @@ int moe_offload_create(const moe_offload_desc* d, moe_offload** out) {
   h->scratch_i32 = (int32_t*)(b + o_scr);
   e = hipHostMalloc((void**)&h->pinned_i32, 64, hipHostMallocDefault);
   if (e != hipSuccess) return bail(hip_fail(e, "pinned scratch"));
+  e = moe::scratch_init(h->device);  // once per device: the no-allocation FFN's workspace address
+  if (e != hipSuccess) return bail(hip_fail(e, "device scratch address"));
   // zero everything (counters, workspaces), then set the empty-cache state
   e = hipMemset(h->state_block, 0, off);
   if (e != hipSuccess) return bail(hip_fail(e, "hipMemset"));
@@ -279,6 +281,25 @@ int moe_slot_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const f
   DeviceGuard g(h->device);
   HIP_TRY(moe::launch_ffn(h, x, slot_ids, w, T, shared_record, y, residual, x_next, nullptr, 0.f,
                           (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_slot_ffn_noalloc(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int32_t T,
+                         const void* shared_record, void* y, const void* residual, void* x_next, void* stream) {
+  if (int rc = check_handle(h)) return rc;
+  if (int rc = check_T(h, T)) return rc;
+  if (!x || !slot_ids || !w || !y) return fail(MOE_EINVAL, "moe_slot_ffn_noalloc: null pointer");
+  size_t need = 0;
+  (void)moe::ffn_work_in(h, T, nullptr, &need);
+  if (need > moe::kScratchBytes)
+    return fail(MOE_EINVAL, "moe_slot_ffn_noalloc: T=%d needs %zu bytes of workspace, the device scratch holds %zu",
+                T, need, (size_t)moe::kScratchBytes);
+  void* base = moe::scratch_ptr(h->device);
+  if (!base) return fail(MOE_EHIP, "moe_slot_ffn_noalloc: no device scratch address for device %d", h->device);
+  DeviceGuard g(h->device);
+  const moe::FfnWork ws = moe::ffn_work_in(h, T, base, nullptr);
+  HIP_TRY(moe::launch_ffn(h, x, slot_ids, w, T, shared_record, y, residual, x_next, nullptr, 0.f,
+                          (hipStream_t)stream, false, true, false, &ws));
   return MOE_OK;
 }
 

@@ -259,6 +259,24 @@ int moe_copy_misses(moe_offload* h, void* stream);
 int moe_slot_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int32_t T,
                  const void* shared_record, void* y, const void* residual, void* x_next, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): moe_slot_ffn with the
+ * same arguments and the same results, bit for bit, whose workspace (the
+ * grouping of the call's pairs by record, the h rows and the fp32 per-choice
+ * outputs) lives in one file-scope device array of MOE_NOALLOC_SCRATCH_BYTES
+ * per GPU instead of the handle's workspace.  The array's device address is
+ * looked up once per device by moe_offload_create; this call allocates and
+ * frees nothing.  Every call on one GPU shares that array: calls that overlap
+ * on one GPU (other streams, other handles, other host threads) race and
+ * must be ordered by the caller.  Nothing in it needs to start at zero.
+ * Errors: as moe_slot_ffn, and MOE_EINVAL when the call's workspace,
+ * 256-aligned (4 x (32 x (min(T k, S + E) + 2) + T k + min(T k, S + E) + 2)
+ * bytes) + (T k + T) F (2, or 4 for MOE_F32) + 4 (T k + T) H bytes, exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32ull << 20)
+int moe_slot_ffn_noalloc(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int32_t T,
+                         const void* shared_record, void* y, const void* residual, void* x_next, void* stream);
+
 /* Per-token RMS normalisation, out = round(x / sqrt(mean(x^2) + eps)) (fp32 arithmetic,
  * no learned scale): the input of each MoE block in the decode-step chain.  The pages
  * describe no norm; it is this build's reading of the inter-layer glue (a 48-layer
