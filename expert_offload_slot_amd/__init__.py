@@ -83,6 +83,7 @@ def lib():
         sig = {
             "moe_offload_create": ([P(Desc), P(vp)], i32),
             "moe_offload_destroy": ([vp], None),
+            "moe_offload_auto_slots": ([P(Desc), i32, i32, ctypes.c_uint64, ctypes.c_uint64, P(ctypes.c_int32)], i32),
             "moe_offload_host_records": ([vp, P(vp), P(ctypes.c_size_t), P(ctypes.c_size_t)], i32),
             "moe_route_topk": ([vp, vp, vp, vp, i32, vp, vp, vp], i32),
             "moe_slot_ensure": ([vp, vp, i32, vp, vp], i32),
@@ -154,6 +155,17 @@ def moe_offload_create(E, S, H, F, k, dtype, max_tokens, device=0, flags=0, shar
     h = ctypes.c_void_p()
     _check(lib().moe_offload_create(ctypes.byref(d), ctypes.byref(h)))
     return h.value
+
+
+def moe_offload_auto_slots(E, H, F, k, dtype, max_tokens, layers, reserve_bytes, free_bytes=0, share_staging=True,
+                           device=0, flags=0):
+    """Slots per layer that `layers` handles of this shape can take from free device memory, leaving
+    reserve_bytes (free_bytes = 0: the device's free memory now)."""
+    d = Desc(E, k, H, F, k, dtype, max_tokens, device, flags, None, None)
+    out = ctypes.c_int32()
+    _check(lib().moe_offload_auto_slots(ctypes.byref(d), layers, 1 if share_staging else 0, reserve_bytes,
+                                        free_bytes, ctypes.byref(out)))
+    return out.value
 
 
 def moe_offload_destroy(h):

@@ -76,6 +76,69 @@ void free_all(moe_offload* h) {
   }
 }
 
+int check_desc(const moe_offload_desc* d) {
+  if (!known_dtype(d->dtype)) return fail(MOE_EUNSUPPORTED, "unsupported dtype %d", d->dtype);
+  if (d->num_experts < 1 || d->num_experts > moe::kMaxExperts)
+    return fail(MOE_EINVAL, "num_experts=%d outside [1, %d]", d->num_experts, moe::kMaxExperts);
+  if (d->top_k < 1 || d->top_k > moe::kMaxTopK || d->top_k > d->num_experts)
+    return fail(MOE_EINVAL, "top_k=%d outside [1, min(%d, E)]", d->top_k, moe::kMaxTopK);
+  if (d->num_slots < d->top_k || d->num_slots > d->num_experts)
+    return fail(MOE_EINVAL, "num_slots=%d outside [top_k=%d, E=%d]", d->num_slots, d->top_k, d->num_experts);
+  // decode kernels: a K block is 16 lanes x 8 weights (16 x 16 MXFP4 weights); fp32: 64-row tiles
+  int mult = d->dtype == MOE_F32 ? 64 : (d->dtype == MOE_MXFP4 ? 256 : 128);
+  if (d->hidden < mult || d->hidden % mult || d->ffn < mult || d->ffn % mult)
+    return fail(MOE_EUNSUPPORTED, "hidden=%d / ffn=%d must be positive multiples of %d for this dtype", d->hidden,
+                d->ffn, mult);
+  if (d->hidden > 65536 || d->ffn > 65536) return fail(MOE_EINVAL, "hidden/ffn above 65536");
+  if (d->max_tokens < 1 || d->max_tokens > 65536) return fail(MOE_EINVAL, "max_tokens=%d outside [1, 65536]", d->max_tokens);
+  if ((d->flags & MOE_FLAG_SCORED) && (d->flags & MOE_FLAG_FREQ))
+    return fail(MOE_EINVAL, "MOE_FLAG_SCORED and MOE_FLAG_FREQ are exclusive");
+  if (d->share_host && !same_shape(d->share_host, d)) return fail(MOE_EINVAL, "share_host handle has another shape");
+  if (d->share_staging && !same_shape(d->share_staging, d))
+    return fail(MOE_EINVAL, "share_staging handle has another shape");
+  return MOE_OK;
+}
+
+// Offsets of everything in a handle's state block (one device allocation);
+// sets h->gl.  Depends on E, S, H, F, k, dtype and max_tokens only.
+struct StateLayout {
+  size_t o_slot_of, o_expert_of, o_last, o_score, o_pinned, o_act, o_tick, o_list, o_pf, o_cnt, o_err, o_logits,
+      o_grp, o_h, o_part, o_scr, total;
+};
+
+StateLayout state_layout(moe_offload* h) {
+  const int maxSE = std::max(h->S, h->E);
+  const int max_pairs = h->max_tokens * h->k;
+  h->gl.max_pairs = max_pairs;
+  h->gl.max_recs = std::min(max_pairs, h->S + h->E) + 1;
+  const int rows = max_pairs + h->max_tokens;  // routed pairs + shared-expert rows
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  StateLayout l;
+  l.o_slot_of = take(4 * (size_t)h->E);
+  l.o_expert_of = take(4 * (size_t)h->S);
+  l.o_last = take(8 * (size_t)h->S);
+  l.o_score = take(4 * (size_t)h->S);
+  l.o_pinned = take(4 * (size_t)h->S);
+  l.o_act = take(4 * (size_t)h->E);
+  l.o_tick = take(8);
+  l.o_list = take(4 * (2 + 2 * (size_t)maxSE));
+  l.o_pf = take(4 * (2 + 2 * (size_t)h->S));
+  l.o_cnt = take(8 * moe::C_N);
+  l.o_err = take(4);
+  l.o_logits = take(4 * (size_t)h->max_tokens * h->E);
+  l.o_grp = take(4 * (size_t)h->gl.words());
+  l.o_h = take((h->dtype == MOE_F32 ? 4 : 2) * (size_t)rows * h->F);
+  l.o_part = take(4 * (size_t)rows * h->H);
+  l.o_scr = take(64);
+  l.total = off;
+  return l;
+}
+
 int check_handle(const moe_offload* h) {
   if (!h) return fail(MOE_EINVAL, "null handle");
   return MOE_OK;
@@ -98,25 +161,7 @@ int moe_offload_create(const moe_offload_desc* d, moe_offload** out) {
   g_err[0] = 0;
   if (!d || !out) return fail(MOE_EINVAL, "null argument");
   *out = nullptr;
-  if (!known_dtype(d->dtype)) return fail(MOE_EUNSUPPORTED, "unsupported dtype %d", d->dtype);
-  if (d->num_experts < 1 || d->num_experts > moe::kMaxExperts)
-    return fail(MOE_EINVAL, "num_experts=%d outside [1, %d]", d->num_experts, moe::kMaxExperts);
-  if (d->top_k < 1 || d->top_k > moe::kMaxTopK || d->top_k > d->num_experts)
-    return fail(MOE_EINVAL, "top_k=%d outside [1, min(%d, E)]", d->top_k, moe::kMaxTopK);
-  if (d->num_slots < d->top_k || d->num_slots > d->num_experts)
-    return fail(MOE_EINVAL, "num_slots=%d outside [top_k=%d, E=%d]", d->num_slots, d->top_k, d->num_experts);
-  // decode kernels: a K block is 16 lanes x 8 weights (16 x 16 MXFP4 weights); fp32: 64-row tiles
-  int mult = d->dtype == MOE_F32 ? 64 : (d->dtype == MOE_MXFP4 ? 256 : 128);
-  if (d->hidden < mult || d->hidden % mult || d->ffn < mult || d->ffn % mult)
-    return fail(MOE_EUNSUPPORTED, "hidden=%d / ffn=%d must be positive multiples of %d for this dtype", d->hidden,
-                d->ffn, mult);
-  if (d->hidden > 65536 || d->ffn > 65536) return fail(MOE_EINVAL, "hidden/ffn above 65536");
-  if (d->max_tokens < 1 || d->max_tokens > 65536) return fail(MOE_EINVAL, "max_tokens=%d outside [1, 65536]", d->max_tokens);
-  if ((d->flags & MOE_FLAG_SCORED) && (d->flags & MOE_FLAG_FREQ))
-    return fail(MOE_EINVAL, "MOE_FLAG_SCORED and MOE_FLAG_FREQ are exclusive");
-  if (d->share_host && !same_shape(d->share_host, d)) return fail(MOE_EINVAL, "share_host handle has another shape");
-  if (d->share_staging && !same_shape(d->share_staging, d))
-    return fail(MOE_EINVAL, "share_staging handle has another shape");
+  if (int rc = check_desc(d)) return rc;
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || d->device < 0 || d->device >= ndev)
     return fail(MOE_EINVAL, "device %d not available (%d devices)", d->device, ndev);
@@ -174,24 +219,11 @@ int moe_offload_create(const moe_offload_desc* d, moe_offload** out) {
   }
 
   // one allocation for the table, lists, counters and workspaces
-  const int maxSE = std::max(h->S, h->E);
-  const int max_pairs = h->max_tokens * h->k;
-  h->gl.max_pairs = max_pairs;
-  h->gl.max_recs = std::min(max_pairs, h->S + h->E) + 1;
-  const int rows = max_pairs + h->max_tokens;  // routed pairs + shared-expert rows
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    size_t o = off;
-    off = align_up(off + bytes, 256);
-    return o;
-  };
-  size_t o_slot_of = take(4 * (size_t)h->E), o_expert_of = take(4 * (size_t)h->S), o_last = take(8 * (size_t)h->S);
-  size_t o_score = take(4 * (size_t)h->S), o_pinned = take(4 * (size_t)h->S), o_act = take(4 * (size_t)h->E);
-  size_t o_tick = take(8), o_list = take(4 * (2 + 2 * (size_t)maxSE)), o_pf = take(4 * (2 + 2 * (size_t)h->S));
-  size_t o_cnt = take(8 * moe::C_N), o_err = take(4), o_logits = take(4 * (size_t)h->max_tokens * h->E);
-  size_t o_grp = take(4 * (size_t)h->gl.words());
-  size_t o_h = take((h->dtype == MOE_F32 ? 4 : 2) * (size_t)rows * h->F), o_part = take(4 * (size_t)rows * h->H);
-  size_t o_scr = take(64);
+  const StateLayout sl = state_layout(h);
+  const size_t o_slot_of = sl.o_slot_of, o_expert_of = sl.o_expert_of, o_last = sl.o_last, o_score = sl.o_score,
+               o_pinned = sl.o_pinned, o_act = sl.o_act, o_tick = sl.o_tick, o_list = sl.o_list, o_pf = sl.o_pf,
+               o_cnt = sl.o_cnt, o_err = sl.o_err, o_logits = sl.o_logits, o_grp = sl.o_grp, o_h = sl.o_h,
+               o_part = sl.o_part, o_scr = sl.o_scr, off = sl.total;
   e = hipMalloc(&h->state_block, off);
   if (e != hipSuccess) return bail(hip_fail(e, "state block"));
   uint8_t* b = (uint8_t*)h->state_block;
@@ -228,6 +260,50 @@ int moe_offload_create(const moe_offload_desc* d, moe_offload** out) {
   e = hipDeviceSynchronize();
   if (e != hipSuccess) return bail(hip_fail(e, "hipDeviceSynchronize"));
   *out = h;
+  return MOE_OK;
+}
+
+int moe_offload_auto_slots(const moe_offload_desc* d, int32_t layers, int32_t share_staging, uint64_t reserve_bytes,
+                           uint64_t free_bytes, int32_t* slots_out) {
+  g_err[0] = 0;
+  if (!d || !slots_out) return fail(MOE_EINVAL, "moe_offload_auto_slots: null argument");
+  if (layers < 1) return fail(MOE_EINVAL, "moe_offload_auto_slots: layers=%d < 1", layers);
+  moe_offload_desc dk = *d;  // num_slots is the result: validate the rest with the smallest legal value
+  dk.num_slots = d->top_k;
+  dk.share_host = dk.share_staging = nullptr;
+  if (int rc = check_desc(&dk)) return rc;
+  if (free_bytes == 0) {
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || d->device < 0 || d->device >= ndev)
+      return fail(MOE_EINVAL, "device %d not available (%d devices)", d->device, ndev);
+    DeviceGuard g(d->device);
+    if (!g.ok) return fail(MOE_EHIP, "hipSetDevice(%d) failed", d->device);
+    size_t fr = 0, tot = 0;
+    HIP_TRY(hipMemGetInfo(&fr, &tot));
+    free_bytes = fr;
+  }
+  moe_offload probe;  // sizes only: the state block at its largest (S = E)
+  memset(&probe, 0, sizeof probe);
+  probe.E = d->num_experts;
+  probe.S = d->num_experts;
+  probe.H = d->hidden;
+  probe.F = d->ffn;
+  probe.k = d->top_k;
+  probe.dtype = d->dtype;
+  probe.max_tokens = d->max_tokens;
+  const size_t stride = align_up(record_bytes_of(d->dtype, d->hidden, d->ffn), 4096);
+  const uint64_t staging = (uint64_t)(share_staging ? 1 : layers) * d->num_experts * stride;
+  const uint64_t fixed = staging + (uint64_t)layers * state_layout(&probe).total + reserve_bytes;
+  const uint64_t per_slot = (uint64_t)layers * stride;  // one more slot in every layer
+  const uint64_t room = free_bytes > fixed ? free_bytes - fixed : 0;
+  const uint64_t fit = room / per_slot;
+  if (fit < (uint64_t)d->top_k) {
+    *slots_out = d->top_k;
+    return fail(MOE_ENOMEM, "moe_offload_auto_slots: %llu free bytes minus %llu (reserve, staging, state) hold %llu "
+                "slots per layer, fewer than top_k=%d", (unsigned long long)free_bytes, (unsigned long long)fixed,
+                (unsigned long long)fit, d->top_k);
+  }
+  *slots_out = fit > (uint64_t)d->num_experts ? d->num_experts : (int32_t)fit;
   return MOE_OK;
 }
 

@@ -189,6 +189,23 @@ enum { MOE_MODE_SLOTS = 0, MOE_MODE_STAGED = 1, MOE_MODE_STAGED_ALL = 2 };
  * Errors: MOE_EINVAL (shape/limits), MOE_EUNSUPPORTED (dtype), MOE_ENOMEM, MOE_EHIP. */
 int moe_offload_create(const moe_offload_desc* desc, moe_offload** out);
 
+/* Slot count for automatic sizing (xinfer-ai 0.14.6 docs/moe_offload.md,
+ * "Options", `auto`: after loading, every layer's slots grow by the same
+ * amount into the free device memory, leaving a reserve for the KV cache and
+ * workspaces).  For `layers` handles created with *d (num_slots ignored):
+ *   S = min(E, floor((free - reserve - staging - layers * state) / (layers * record_stride)))
+ * where staging is one [E, record_stride] buffer (share_staging != 0: the
+ * layers share one, as moe_offload_desc.share_staging allows) or one per layer,
+ * and state is a handle's state block (tables, lists, workspaces) at its
+ * largest.  free_bytes = 0: the device's free memory now (hipMemGetInfo on
+ * d->device); otherwise the given figure, and no device is touched.
+ *   *slots_out: the S to pass to moe_offload_create for every layer.
+ * Errors: MOE_EINVAL / MOE_EUNSUPPORTED (the descriptor, layers < 1),
+ * MOE_ENOMEM when not even top_k slots per layer fit (*slots_out = top_k),
+ * MOE_EHIP. */
+int moe_offload_auto_slots(const moe_offload_desc* d, int32_t layers, int32_t share_staging, uint64_t reserve_bytes,
+                           uint64_t free_bytes, int32_t* slots_out);
+
 /* Synchronise the device, free everything the handle owns.  Null-safe. */
 void moe_offload_destroy(moe_offload* h);
 

@@ -443,3 +443,36 @@ def test_graph_replay_matches_eager():
             assert all(np.array_equal(p, q) for p, q in zip(gl.table(), tab))
     for gl in eager + graphed:
         gl.close()
+
+
+def test_auto_slots_fill_free_memory_up_to_the_reserve():
+    """moe_offload_auto_slots on the device's own free memory: `layers` handles created with the
+    returned slot count (sharing one staging buffer) leave at least the reserve free, and one more
+    slot per layer would not have fitted."""
+    E, H, F, k, L, T = 64, 1024, 512, 4, 4, 8
+    stride = 3 * H * F * 2  # bf16, a multiple of 4096
+    # threshold of the rule from its arithmetic-only mode: free bytes giving exactly k slots per layer
+    lo, hi = 1, 1 << 44
+    while lo < hi:
+        mid = (lo + hi) // 2
+        try:
+            m.moe_offload_auto_slots(E, H, F, k, m.BF16, T, L, 0, mid)
+            hi = mid
+        except m.MoeError:
+            lo = mid + 1
+    torch.cuda.synchronize()
+    free_now = torch.cuda.mem_get_info()[0]
+    reserve = free_now - lo - 10 * L * stride - stride // 2  # room for k + 10 slots per layer, not k + 11
+    S = m.moe_offload_auto_slots(E, H, F, k, m.BF16, T, L, reserve)
+    assert S == k + 10, S
+    hs = []
+    try:
+        for l in range(L):
+            hs.append(m.moe_offload_create(E, S, H, F, k, m.BF16, T, 0, 0, hs[0] if l else None,
+                                           hs[0] if l else None))
+        torch.cuda.synchronize()
+        # allocation granularity aside (a few MiB per allocation), the reserve is still free
+        assert torch.cuda.mem_get_info()[0] >= reserve - 64 * (1 << 20)
+    finally:
+        for h in reversed(hs):
+            m.moe_offload_destroy(h)
