@@ -799,7 +799,8 @@ def routing_profile(args, m, hip, torch, handles, wr_d, b_d, T, steps):
 
 
 def eviction_compare(args, m, hip, torch, handles, wr_d, b_d, run_decode, token_stream):
-    """LRU against scored eviction (least used first, then LRU) and against profile-guided placement (each
+    """LRU against scored eviction (least used first, then LRU), activation-aware eviction (least activated
+    expert first, counts kept across evictions, then LRU) and profile-guided placement (each
     layer's SLOTS // 2 most routed experts of a separate profiling stream pinned, LRU for the rest), each from
     an empty cache on the same token stream; the scored layers share the LRU layers' host stores.  Outputs
     must be bitwise identical."""
@@ -808,9 +809,11 @@ def eviction_compare(args, m, hip, torch, handles, wr_d, b_d, run_decode, token_
     xs_d = token_stream(T, warm + steps + args.prof_steps)
     scored = [m.moe_offload_create(E, SLOTS, H, F, K_TOP, m.BF16, 32, 0, m.FLAG_SCORED, h, handles[0])
               for h in handles]
+    freq = [m.moe_offload_create(E, SLOTS, H, F, K_TOP, m.BF16, 32, 0, m.FLAG_FREQ, h, handles[0])
+            for h in handles]
     out, last = {}, {}
     try:
-        for name, hs in (("lru", handles), ("scored", scored), ("pinned", handles)):
+        for name, hs in (("lru", handles), ("scored", scored), ("activation_aware", freq), ("pinned", handles)):
             for h in hs:
                 m.moe_offload_reset(h)
             if name == "pinned":
@@ -830,14 +833,13 @@ def eviction_compare(args, m, hip, torch, handles, wr_d, b_d, run_decode, token_
                          "misses_per_token": round(d["misses"] / (T * steps), 4)}
             m.moe_chain_destroy(c)
     finally:
-        for h in reversed(scored):
+        for h in reversed(scored + freq):
             m.moe_offload_destroy(h)
     for h in handles:  # unpin: the default layers go back to plain LRU
         m.moe_offload_pin(h, None, 0, torch.cuda.current_stream())
     torch.cuda.synchronize()
     out["pinned"]["pinned_per_layer"] = SLOTS // 2
-    out["outputs_identical"] = bool(np.array_equal(last["lru"], last["scored"]) and
-                                    np.array_equal(last["lru"], last["pinned"]))
+    out["outputs_identical"] = bool(all(np.array_equal(last["lru"], last[n]) for n in last))
     return out
 
 

@@ -33,7 +33,7 @@ _lib = None
 F32, BF16, FP8, MXFP4 = 0, 1, 2, 3
 LRU, SCORED, FREQ = 0, 1, 2  # eviction policies
 SCORE_MAX = (1 << 20) - 1
-SLOTS, STAGED, STAGED_ALL = 0, 1, 2
+SLOTS, STAGED, STAGED_ALL, COLD = 0, 1, 2, 3
 
 
 def build():
@@ -72,6 +72,7 @@ def lib():
         L.orc_cache_set_policy.argtypes = [vp, i32]
         L.orc_cache_scores.argtypes = [vp, vp]
         L.orc_cache_act.argtypes = [vp, vp]
+        L.orc_cache_set_cold.argtypes = [vp, i32]
         L.orc_cache_pinned.argtypes = [vp, vp]
         L.orc_pin.argtypes = [vp, vp, i32, vp]
         L.orc_pin.restype = i32
@@ -87,7 +88,7 @@ def lib():
         L.orc_install.restype = i32
         L.orc_copy.argtypes = [vp, i32, vp, sz, vp, vp, sz, sz]
         L.orc_ffn.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]
-        L.orc_resolve.argtypes = [vp, i32, i32, vp, vp, sz, vp]
+        L.orc_resolve.argtypes = [vp, i32, i32, i32, vp, vp, vp, sz, vp]
         L.orc_residual.argtypes = [vp, vp, i32, sz, vp]
         L.orc_rmsnorm.argtypes = [vp, i32, i32, i32, f64, vp]
         L.orc_threads.argtypes = []
@@ -248,7 +249,7 @@ class Cache:
 
     def copy(self, mode, pairs):
         """Apply a copy list to the oracle's own slot/staging bytes."""
-        if not self.keep_bytes or len(pairs) == 0:
+        if not self.keep_bytes or len(pairs) == 0 or mode == COLD:  # cold experts are never copied
             return
         if self.staging is None and (pairs[:, 1] >= self.S).any():
             self.staging = np.zeros((self.E, self.stride), dtype=np.uint8)
@@ -259,12 +260,16 @@ class Cache:
         lib().orc_copy(_p(desc), self.S, _p(self.host), self.stride, _p(self.slots), _p(st), self.stride, self.rb)
 
     def records(self, slot_ids):
-        """Pointers to the records that each (t, j) reads (slots or staging)."""
+        """Pointers to the records that each (t, j) reads (slots, staging, or host records of cold experts)."""
         sid = np.ascontiguousarray(slot_ids, dtype=np.int32).reshape(-1)
         recs = (ctypes.c_void_p * sid.size)()
         st = self.staging if self.staging is not None else self.slots
-        lib().orc_resolve(_p(sid), sid.size, self.S, _p(self.slots), _p(st), self.stride, recs)
+        lib().orc_resolve(_p(sid), sid.size, self.S, self.E, _p(self.slots), _p(st), _p(self.host), self.stride, recs)
         return recs
+
+    def set_cold(self, on):
+        """Cold mode: later ensure calls load nothing; misses are read from their host records."""
+        lib().orc_cache_set_cold(self._c, 1 if on else 0)
 
     def state(self):
         so = np.empty(self.E, np.int32)
@@ -298,9 +303,10 @@ class Cache:
         return out
 
     def counters(self):
-        out = np.zeros(7, np.uint64)
+        out = np.zeros(8, np.uint64)
         lib().orc_cache_counters(self._c, _p(out))
-        keys = ("calls", "hits", "misses", "staged_calls", "staged_copies", "prefetch_installs", "prefetch_hits")
+        keys = ("calls", "hits", "misses", "staged_calls", "staged_copies", "prefetch_installs", "prefetch_hits",
+                "cold")
         return dict(zip(keys, (int(v) for v in out)))
 
 

@@ -33,7 +33,7 @@
 /* weight dtype codes */
 enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2, ORC_MXFP4 = 3 };
 /* descriptor modes */
-enum { ORC_SLOTS = 0, ORC_STAGED = 1, ORC_STAGED_ALL = 2 };
+enum { ORC_SLOTS = 0, ORC_STAGED = 1, ORC_STAGED_ALL = 2, ORC_COLD = 3 };
 /* error codes */
 enum { ORC_OK = 0, ORC_EINVAL = -1, ORC_ENAN = -2 };
 
@@ -255,6 +255,17 @@ int orc_topk(const float* logits, int T, int E, int k, int32_t* ids, double* w) 
  * last_use, slot): installed slots still go first as the prefetch rule asks,
  * then the least activated expert, then the least recently used, then the
  * lower slot.  Installs and pins do not count as activations.
+ *
+ * Host-computed cold experts (READING of [npu-offload] intro, "Results" and
+ * "Architecture": hot experts stay in accelerator memory, the host CPU computes
+ * the cold ones from host DRAM, only activations cross the link and weights
+ * never move): with the cold mode on, an ensure call loads nothing.  D, the
+ * hits and their last_use / score / activation updates are as above, and every
+ * routed expert's activation count advances; a miss keeps no slot, takes no
+ * victim and is read at record index S + E + e (host record e) for this call.
+ * Copy list = {COLD, |misses|, (e, S + E + e) for e in D \ R ascending}.  The
+ * table is otherwise unchanged; there is no overflow.  Counters: calls, hits,
+ * and cold (the misses computed on the host).
  */
 enum { ORC_LRU = 0, ORC_SCORED = 1, ORC_FREQ = 2 };
 #define ORC_SCORE_MAX ((1u << 20) - 1u)
@@ -268,9 +279,10 @@ typedef struct {
   uint32_t* score;
   uint32_t* act;         /* [E] activation count (ORC_FREQ key; kept under every policy) */
   unsigned char* pinned; /* [S] profile-guided placement: never a victim */
+  int cold;              /* 1: misses are computed on the host, never loaded */
   uint64_t tick;
   /* cumulative counters */
-  uint64_t calls, hits, misses, staged_calls, staged_copies, prefetch_installs, prefetch_hits;
+  uint64_t calls, hits, misses, staged_calls, staged_copies, prefetch_installs, prefetch_hits, cold_misses;
 } orc_cache;
 
 orc_cache* orc_cache_new(int E, int S) {
@@ -304,6 +316,8 @@ void orc_cache_set_policy(orc_cache* c, int policy) {
   c->policy = (policy == ORC_SCORED || policy == ORC_FREQ) ? policy : ORC_LRU;
 }
 
+void orc_cache_set_cold(orc_cache* c, int on) { c->cold = on != 0; }
+
 void orc_cache_act(const orc_cache* c, uint32_t* act) { memcpy(act, c->act, sizeof(uint32_t) * (size_t)c->E); }
 
 void orc_cache_scores(const orc_cache* c, uint32_t* score) {
@@ -321,10 +335,10 @@ void orc_cache_state(const orc_cache* c, int32_t* slot_of, int32_t* expert_of, u
   if (tick) *tick = c->tick;
 }
 
-/* counters: calls, hits, misses, staged_calls, staged_copies, prefetch_installs, prefetch_hits */
-void orc_cache_counters(const orc_cache* c, uint64_t out[7]) {
+/* counters: calls, hits, misses, staged_calls, staged_copies, prefetch_installs, prefetch_hits, cold */
+void orc_cache_counters(const orc_cache* c, uint64_t out[8]) {
   out[0] = c->calls; out[1] = c->hits; out[2] = c->misses; out[3] = c->staged_calls;
-  out[4] = c->staged_copies; out[5] = c->prefetch_installs; out[6] = c->prefetch_hits;
+  out[4] = c->staged_copies; out[5] = c->prefetch_installs; out[6] = c->prefetch_hits; out[7] = c->cold_misses;
 }
 
 /* does slot a come before slot b in victim order?  LRU (occupied, last_use, slot); scored (occupied,
@@ -393,6 +407,34 @@ int orc_ensure(orc_cache* c, const int32_t* ids, int n, int k, int32_t* slot_ids
       miss[e] = 1;
       ++nm;
     }
+  }
+  if (c->cold) { /* nothing loads: hits are used in place, misses are read from the host */
+    for (int e = 0; e < E; ++e) {
+      if (!inD[e]) continue;
+      int s = c->slot_of[e];
+      if (s >= 0) {
+        c->last_use[s] = c->tick;
+        if (c->score[s] < ORC_SCORE_MAX) c->score[s] += 1;
+      }
+      if (c->act[e] < ORC_SCORE_MAX) c->act[e] += 1;
+    }
+    int count = 0;
+    for (int e = 0; e < E; ++e) {
+      if (!miss[e]) continue;
+      desc[2 + 2 * count] = e;
+      desc[3 + 2 * count] = S + E + e;
+      ++count;
+    }
+    for (int i = 0; i < n; ++i) {
+      int e = ids[i];
+      slot_ids[i] = c->slot_of[e] >= 0 ? c->slot_of[e] : S + E + e;
+    }
+    desc[0] = ORC_COLD;
+    desc[1] = count;
+    c->cold_misses += (uint64_t)nm;
+    free(miss);
+    free(inD);
+    return ORC_OK;
   }
   /* the eligible slots in victim order; the call overflows when the misses
    * outnumber them (without pinned slots: exactly when |D| > S) */
@@ -622,6 +664,7 @@ int orc_pin(orc_cache* c, const int32_t* experts, int n, int32_t* desc) {
  * (r >= S).  Strides are the distances between consecutive records. */
 void orc_copy(const int32_t* desc, int S, const uint8_t* host, size_t host_stride, uint8_t* slots, uint8_t* staging,
               size_t dev_stride, size_t record_bytes) {
+  if (desc[0] == ORC_COLD) return; /* cold experts stay on the host: nothing moves */
   int count = desc[1];
   for (int i = 0; i < count; ++i) {
     int e = desc[2 + 2 * i], r = desc[3 + 2 * i];
@@ -705,11 +748,13 @@ void orc_ffn(const void* x, int wdt, int H, int F, int T, int k, const uint8_t* 
 }
 
 /* Resolve record indices (slot ids) to record pointers: r < S -> slots, else staging. */
-void orc_resolve(const int32_t* slot_ids, int n, int S, const uint8_t* slots, const uint8_t* staging, size_t stride,
-                 const uint8_t** recs) {
+void orc_resolve(const int32_t* slot_ids, int n, int S, int E, const uint8_t* slots, const uint8_t* staging,
+                 const uint8_t* host, size_t stride, const uint8_t** recs) {
   for (int i = 0; i < n; ++i) {
     int r = slot_ids[i];
-    recs[i] = r < S ? slots + (size_t)r * stride : staging + (size_t)(r - S) * stride;
+    if (r < S) recs[i] = slots + (size_t)r * stride;
+    else if (r < S + E) recs[i] = staging + (size_t)(r - S) * stride;
+    else recs[i] = host + (size_t)(r - S - E) * stride; /* a cold expert: its host record */
   }
 }
 

@@ -66,7 +66,7 @@ class BruteCache:
     freq=True: slots installed and not used since go first, then the expert activated by the fewest
     calls since the cache was created (kept across evictions, capped), then LRU."""
 
-    def __init__(self, E, S, scored=False, cap=(1 << 20) - 1, freq=False):
+    def __init__(self, E, S, scored=False, cap=(1 << 20) - 1, freq=False, cold=False):
         self.E, self.S = E, S
         self.held = [None] * S
         self.home = {}
@@ -74,7 +74,7 @@ class BruteCache:
         self.uses = [0] * S
         self.fired = [0] * E  # activations per expert
         self.clock = 0
-        self.scored, self.cap, self.freq = scored, cap, freq
+        self.scored, self.cap, self.freq, self.cold = scored, cap, freq, cold
         self.pinned = set()
 
     def _victims(self, protect):
@@ -101,6 +101,14 @@ class BruteCache:
         self.clock += 1
         D = sorted(set(ids))
         miss = [e for e in D if e not in self.home]
+        if self.cold:  # nothing loads; misses are read at S + E + e from the host
+            for e in D:
+                if e in self.home:
+                    self.used[self.home[e]] = self.clock
+                    self.uses[self.home[e]] = min(self.uses[self.home[e]] + 1, self.cap)
+                self.fired[e] = min(self.fired[e] + 1, self.cap)
+            rec = lambda e: self.home.get(e, self.S + self.E + e)
+            return [rec(e) for e in ids], 3, [(e, rec(e)) for e in miss]
         claim = miss
         victims = self._victims(set(D))
         over = len(miss) > len(victims)
@@ -399,3 +407,52 @@ def test_activation_aware_installs_go_first(orc):
     _, _, pairs = c.ensure(np.array([[3]], np.int32))
     assert pairs.tolist() == [[3, 0]]  # the installed, unused expert 0 goes first despite its count
     assert c.activations().tolist() == [3, 1, 1, 1]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_cold_mode_matches_brute_force_and_never_moves_weights(orc, seed):
+    """Host-computed cold experts: calls in cold mode load nothing (the slot maps never change), hits
+    are used in place, misses are listed at S + E + e; switching the mode on and off mid-trace."""
+    rng = np.random.default_rng(300 + seed)
+    E = int(rng.choice([8, 16, 32]))
+    k = int(rng.choice([1, 2, 4]))
+    S = int(rng.integers(k, E + 1))
+    policy = [orc.LRU, orc.SCORED, orc.FREQ][seed % 3]
+    c = orc.Cache(E, S, policy=policy)
+    b = BruteCache(E, S, scored=policy == orc.SCORED, freq=policy == orc.FREQ)
+    p = 1.0 / np.arange(1, E + 1) ** rng.uniform(0.3, 1.5)
+    cold_total = 0
+    for step in range(150):
+        if step % 25 == 0:
+            on = bool(rng.integers(0, 2))
+            c.set_cold(on)
+            b.cold = on
+        T = int(rng.integers(1, 6))
+        ids = np.stack([rng.choice(E, size=k, replace=False, p=p / p.sum()) for _ in range(T)]).astype(np.int32)
+        before = c.state()
+        slot_ids, mode, pairs = c.ensure(ids)
+        es, em, ep = b.ensure(ids.reshape(-1).tolist(), k)
+        assert slot_ids.reshape(-1).tolist() == es and mode == em
+        assert [tuple(map(int, r)) for r in pairs] == ep
+        assert c.scores().tolist() == b.uses and c.activations().tolist() == b.fired
+        if b.cold:
+            so, eo, lu, tick = c.state()
+            assert np.array_equal(so, before[0]) and np.array_equal(eo, before[1]) and tick == before[3] + 1
+            cold_total += len(pairs)
+        else:
+            _check_invariants(c, ids, slot_ids, mode, pairs, before)
+    assert c.counters()["cold"] == cold_total
+
+
+def test_cold_mode_hand_example(orc):
+    c = orc.Cache(8, 3)
+    c.ensure(np.array([[1, 2]], np.int32))  # slots 0, 1 hold experts 1, 2 (tick 1)
+    c.set_cold(True)
+    sid, mode, pairs = c.ensure(np.array([[2, 5], [6, 1]], np.int32))
+    assert mode == orc.COLD and pairs.tolist() == [[5, 16], [6, 17]]  # S + E + e = 3 + 8 + e
+    assert sid.tolist() == [[1, 16], [17, 0]]
+    so, eo, lu, tick = c.state()
+    assert eo.tolist() == [1, 2, -1] and lu.tolist() == [2, 2, 0] and tick == 2
+    cnt = c.counters()
+    assert (cnt["hits"], cnt["misses"], cnt["cold"]) == (2, 2, 2)
+    assert c.activations().tolist() == [0, 2, 2, 0, 0, 1, 1, 0]

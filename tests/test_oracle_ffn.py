@@ -128,6 +128,15 @@ def test_placement_invariance_in_the_oracle(orc, syn, wdt, E, k, H, F, T):
             modes.add(r["mode"])
             assert np.array_equal(r["y"], ref[s]), (S, s)
     assert modes == {0, 1, 2}  # slots, decode staging and whole-layer staging all exercised
+    # host-computed cold experts: the misses are read from their host records at S + E + e
+    for S in (k, (k + E) // 2):
+        L = orc.Layer(E, S, k, H, F, wdt, host, wr, b)
+        for s in range(len(xs)):
+            if s == 4:
+                L.cache.set_cold(True)
+            r = L.step(xs[s])
+            assert r["mode"] == (orc.COLD if s >= 4 else r["mode"])
+            assert np.array_equal(r["y"], ref[s]), ("cold", S, s)
 
 
 def test_wrong_slot_map_would_change_the_output(orc, syn):
