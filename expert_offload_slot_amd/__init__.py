@@ -40,7 +40,7 @@ class Desc(ctypes.Structure):
 class Stats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in ("calls", "hits", "misses", "staged_calls", "staged_copies",
                                                "prefetch_installs", "prefetch_hits", "bytes_copied", "tick")] + \
-               [("error", ctypes.c_int32), ("resident", ctypes.c_int32)]
+               [("error", ctypes.c_int32), ("resident", ctypes.c_int32), ("cold_misses", ctypes.c_uint64)]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -90,6 +90,8 @@ def lib():
             "moe_copy_misses": ([vp, vp], i32),
             "moe_slot_ffn": ([vp, vp, vp, vp, i32, vp, vp, vp, vp, vp], i32),
             "moe_slot_ffn_noalloc": ([vp, vp, vp, vp, i32, vp, vp, vp, vp, vp], i32),
+            "moe_slot_ffn_host_cold": ([vp, vp, vp, vp, i32, vp, vp, vp, vp, vp], i32),
+            "moe_offload_set_cold": ([vp, i32, vp, P(ctypes.c_int32), P(ctypes.c_double), P(ctypes.c_double)], i32),
             "moe_rmsnorm": ([vp, vp, i32, i32, i32, ctypes.c_float, vp], i32),
             "moe_prefill_stage": ([vp, vp, i32, vp, P(ctypes.c_int32), vp], i32),
             "moe_prefetch_install": ([vp, vp, i32, i32, vp], i32),
@@ -203,6 +205,22 @@ def moe_slot_ffn_noalloc(h, x, slot_ids, w, T, shared_record, y, residual=None, 
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20
+
+COLD_OFF, COLD_ON, COLD_AUTO = 0, 1, 2
+MODE_COLD = 3
+
+
+def moe_offload_set_cold(h, mode, stream=None):
+    """-> (chosen 0/1, host FFN us per record, link us per record); the times are measured for COLD_AUTO only."""
+    chosen, cpu, link = ctypes.c_int32(), ctypes.c_double(), ctypes.c_double()
+    _check(lib().moe_offload_set_cold(h, mode, _stream(stream), ctypes.byref(chosen), ctypes.byref(cpu),
+                                      ctypes.byref(link)))
+    return chosen.value, cpu.value, link.value
+
+
+def moe_slot_ffn_host_cold(h, x, slot_ids, w, T, shared_record, y, residual=None, x_next=None, stream=None):
+    return _check(lib().moe_slot_ffn_host_cold(h, _addr(x), _addr(slot_ids), _addr(w), T, _addr(shared_record),
+                                               _addr(y), _addr(residual), _addr(x_next), _stream(stream)))
 
 RMS_EPS = 1e-6
 

@@ -6,10 +6,13 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+HOST_SRC = sorted(glob.glob(os.path.join(HERE, "csrc", "*.cpp")))  # host-only C++ (the cold-expert CPU FFN)
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT_DIR, "libmoe_offload.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CXX = os.environ.get("CXX", "g++")
+HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-pthread", "-ffp-contract=off", "-Wall", "-Wno-unused-function"]
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
     # no packed fp32 instructions anywhere
@@ -38,8 +41,17 @@ def build(verbose=False):
         if err and verbose:
             print(err, file=sys.stderr)
         objs.append(obj)
+    for src in HOST_SRC:
+        obj = os.path.join(OUT_DIR, os.path.basename(src).replace(".cpp", ".host.o"))
+        cmd = [CXX] + HOST_FLAGS + ["-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("%s failed for %s:\n%s" % (CXX, src, r.stderr))
+        objs.append(obj)
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-pthread", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s" % r.stderr)

@@ -241,8 +241,16 @@ int moe_chain_get_buffers(const moe_chain* c, moe_chain_buffers* out) {
   return MOE_OK;
 }
 
+// the decode chain runs without a host round trip: a layer in cold mode cannot join it
+static bool any_cold(const moe_chain* c) {
+  for (const moe_offload* h : c->layers)
+    if (h->cold_on) return true;
+  return false;
+}
+
 int moe_chain_run(moe_chain* c, void* stream) {
   if (!c) return cfail(MOE_EINVAL, "moe_chain_run: null chain");
+  if (any_cold(c)) return cfail(MOE_EINVAL, "moe_chain_run: a layer is in cold mode (host-computed experts)");
   int prev = 0;
   (void)hipGetDevice(&prev);
   (void)hipSetDevice(c->device);
@@ -281,6 +289,7 @@ int moe_chain_set_read_through(moe_chain* c, int on) {
 
 int moe_chain_run_eager(moe_chain* c, void* stream) {
   if (!c) return cfail(MOE_EINVAL, "moe_chain_run_eager: null chain");
+  if (any_cold(c)) return cfail(MOE_EINVAL, "moe_chain_run_eager: a layer is in cold mode (host-computed experts)");
   int prev = 0;
   (void)hipGetDevice(&prev);
   (void)hipSetDevice(c->device);

@@ -16,16 +16,20 @@ struct GroupShared {
 };
 
 // rec[i] (LDS or global) is the record index of pair i = t*k + j, in [0, nb).
-// An index outside that range is flagged (audit bit) and treated as record 0.
+// An index in [nb, cold_hi) names a cold expert computed on the host: the pair
+// is left out of every record list.  Any other index outside [0, nb) is flagged
+// (audit bit) and treated as record 0.
 // All threads of the block must call it.  The order of the pairs inside a
 // record's list is not fixed, and nothing downstream depends on it.
 __device__ __forceinline__ void group_body(const int32_t* rec, int n, int nb, int32_t* __restrict__ grp,
-                                           int off_pairs, int off_tiles, int32_t* err, GroupShared& g) {
+                                           int off_pairs, int off_tiles, int32_t* err, GroupShared& g,
+                                           int cold_hi = 0) {
   const int tid = threadIdx.x;
   for (int b = tid; b < 2 * kMaxExperts; b += kBlock) g.cnt[b] = 0;
   __syncthreads();
   for (int i = tid; i < n; i += kBlock) {
     int r = rec[i];
+    if (r >= nb && r < cold_hi) continue;  // a cold expert: computed on the host
     if ((unsigned)r >= (unsigned)nb) {
       atomicOr(err, MOE_DEV_ERR_AUDIT);
       r = 0;
@@ -73,6 +77,7 @@ __device__ __forceinline__ void group_body(const int32_t* rec, int n, int nb, in
   // into the record block
   for (int i = tid; i < n; i += kBlock) {
     int r = rec[i];
+    if (r >= nb && r < cold_hi) continue;
     if ((unsigned)r >= (unsigned)nb) r = 0;
     const int pos = atomicAdd(&g.cur[r], 1);
     pairs[pos] = i;

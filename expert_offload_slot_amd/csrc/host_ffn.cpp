@@ -1,0 +1,383 @@
+// Expert FFN on the host CPU for cold experts: the misses of a call are
+// computed from their records in host DRAM instead of crossing the host link.
+//
+// npu-offload README, intro, "Results" (where the time goes: the CPU's cold
+// experts are bound by DRAM bandwidth) and "Architecture" (hot experts on the
+// accelerator and cold experts on the host run in parallel per layer; only
+// activations cross PCIe, weights never move).
+//
+// Work is split by weight rows, so every weight byte is read from DRAM once per
+// call and meets every token routed to its expert while it sits in cache:
+//   phase 1: (cold expert, block of F rows)  gate/up dot products, h = silu(g) * u
+//   phase 2: (cold expert, block of H rows)  down dot products into the output rows
+// Dot products accumulate in fp32 over 16 interleaved lanes: with AVX-512 (picked
+// when the library loads) one register per token, fused multiply-adds, codes
+// widened in registers; otherwise the same sums in portable C++.  A persistent
+// pool of worker threads claims blocks from an atomic counter.
+#include <immintrin.h>
+#include <math.h>
+#include <sched.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <atomic>
+#include <condition_variable>
+#include <functional>
+#include <mutex>
+#include <thread>
+#include <vector>
+
+#include "../../include/moe_offload.h"
+#include "host_ffn.h"
+
+namespace moe {
+namespace {
+
+
+// ---------------------------------------------------------------- weight formats
+// e4m3 ("fn": bias 7, no infinities, S.1111.111 is NaN) and E2M1 values, built
+// from their bit fields when the library loads.
+struct Tables {
+  float e4m3[256];
+  float e2m1[16];
+  Tables() {
+    for (int c = 0; c < 256; ++c) {
+      const int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+      float v;
+      if (e == 15 && m == 7) v = NAN;
+      else if (e == 0) v = ldexpf((float)m / 8.0f, -6);
+      else v = ldexpf(1.0f + (float)m / 8.0f, e - 7);
+      e4m3[c] = s ? -v : v;
+    }
+    for (int c = 0; c < 16; ++c) {
+      const int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+      const float v = e == 0 ? 0.5f * (float)m : ldexpf(1.0f + 0.5f * (float)m, e - 1);
+      e2m1[c] = s ? -v : v;
+    }
+  }
+};
+const Tables g_tab;
+
+inline float bf16_to_f32(uint16_t b) {
+  const uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+inline float e8m0_to_f32(uint8_t e) {
+  if (e == 255) return NAN;
+  if (e == 0) return ldexpf(1.0f, -127);
+  const uint32_t u = (uint32_t)e << 23;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+// One weight row of C columns (codes at w; fp8: block scales `sc` per 128
+// columns; MXFP4: E8M0 bytes `sc` per 32 columns) times nt activation rows
+// a[t] (fp32, C long): acc[t] = sum_c W[c] a[t][c], 16 lanes per row (one
+// AVX-512 register per token).  The AVX-512 versions keep the nt accumulators in
+// registers; the portable versions do the same sums lane by lane.
+constexpr int kLanes = 16;
+constexpr int kMaxTok = 8;  // activation rows per pass
+
+// ---- portable
+void dot_f32_p(const float* w, int C, const float* const* a, int nt, float* acc) {
+  for (int t = 0; t < nt; ++t) {
+    float l[kLanes] = {};
+    for (int c = 0; c < C; c += kLanes)
+      for (int i = 0; i < kLanes; ++i) l[i] += w[c + i] * a[t][c + i];
+    float s = 0.f;
+    for (int i = 0; i < kLanes; ++i) s += l[i];
+    acc[t] = s;
+  }
+}
+
+template <typename Dec>
+void dot_dec_p(const Dec& dec, int C, int block, const float* sc, const float* const* a, int nt, float* acc) {
+  for (int t = 0; t < nt; ++t) acc[t] = 0.f;
+  for (int c0 = 0; c0 < C; c0 += block) {
+    for (int t = 0; t < nt; ++t) {
+      float l[kLanes] = {};
+      for (int c = c0; c < c0 + block; c += kLanes)
+        for (int i = 0; i < kLanes; ++i) l[i] += dec(c + i) * a[t][c + i];
+      float p = 0.f;
+      for (int i = 0; i < kLanes; ++i) p += l[i];
+      acc[t] += (sc ? sc[c0 / block] : 1.0f) * p;
+    }
+  }
+}
+
+// ---- AVX-512
+#define MOE_AVX512 __attribute__((target("avx512f")))
+
+MOE_AVX512 inline float hsum(__m512 v) { return _mm512_reduce_add_ps(v); }
+
+// 16 bf16 -> 16 fp32
+MOE_AVX512 inline __m512 ld_bf16(const uint16_t* w) {
+  const __m256i b = _mm256_loadu_si256(reinterpret_cast<const __m256i*>(w));
+  return _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(b), 16));
+}
+
+// 16 e4m3 codes -> 16 fp32: sign, then exponent + 120 into place for normals,
+// m * 2^-9 for subnormals, NaN for the two NaN codes
+MOE_AVX512 inline __m512 ld_e4m3(const uint8_t* w) {
+  const __m512i u = _mm512_cvtepu8_epi32(_mm_loadu_si128(reinterpret_cast<const __m128i*>(w)));
+  const __m512i em = _mm512_and_si512(u, _mm512_set1_epi32(0x7f));
+  const __m512i sign = _mm512_slli_epi32(_mm512_and_si512(u, _mm512_set1_epi32(0x80)), 24);
+  const __m512i norm = _mm512_add_epi32(_mm512_slli_epi32(em, 20), _mm512_set1_epi32(120 << 23));
+  const __m512 sub = _mm512_mul_ps(_mm512_cvtepi32_ps(em), _mm512_set1_ps(1.0f / 512.0f));
+  const __mmask16 is_sub = _mm512_cmplt_epi32_mask(em, _mm512_set1_epi32(8));
+  const __mmask16 is_nan = _mm512_cmpeq_epi32_mask(em, _mm512_set1_epi32(0x7f));
+  __m512i bits = _mm512_mask_mov_epi32(norm, is_sub, _mm512_castps_si512(sub));
+  bits = _mm512_mask_mov_epi32(bits, is_nan, _mm512_set1_epi32(0x7fc00000));
+  return _mm512_castsi512_ps(_mm512_or_si512(bits, sign));
+}
+
+// 16 E2M1 codes (8 bytes, element 2i in the low nibble) -> 16 fp32, times s
+MOE_AVX512 inline __m512 ld_e2m1(const uint8_t* w, __m512 table, __m512 s) {
+  const __m512i b = _mm512_cvtepu8_epi32(_mm_loadl_epi64(reinterpret_cast<const __m128i*>(w)));
+  const __m512i lo = _mm512_and_si512(b, _mm512_set1_epi32(15));
+  const __m512i hi = _mm512_srli_epi32(b, 4);
+  const __m512i idx = _mm512_set_epi32(23, 7, 22, 6, 21, 5, 20, 4, 19, 3, 18, 2, 17, 1, 16, 0);
+  const __m512i codes = _mm512_permutex2var_epi32(lo, idx, hi);
+  return _mm512_mul_ps(_mm512_permutexvar_ps(codes, table), s);
+}
+
+template <int NT, typename Load>
+MOE_AVX512 inline void dot_blocks(const Load& ld, int C, int block, const float* sc, const float* const* a,
+                                  float* acc) {
+  float out[NT] = {};
+  for (int c0 = 0; c0 < C; c0 += block) {
+    __m512 l[NT];
+    for (int t = 0; t < NT; ++t) l[t] = _mm512_setzero_ps();
+    for (int c = c0; c < c0 + block; c += kLanes) {
+      const __m512 wv = ld(c);
+      for (int t = 0; t < NT; ++t) l[t] = _mm512_fmadd_ps(wv, _mm512_loadu_ps(a[t] + c), l[t]);
+    }
+    const float s = sc ? sc[c0 / block] : 1.0f;
+    for (int t = 0; t < NT; ++t) out[t] += s * hsum(l[t]);
+  }
+  for (int t = 0; t < NT; ++t) acc[t] = out[t];
+}
+
+template <typename Load>
+MOE_AVX512 void dot_any(const Load& ld, int C, int block, const float* sc, const float* const* a, int nt,
+                        float* acc) {
+  switch (nt) {
+    case 1: dot_blocks<1>(ld, C, block, sc, a, acc); return;
+    case 2: dot_blocks<2>(ld, C, block, sc, a, acc); return;
+    case 3: dot_blocks<3>(ld, C, block, sc, a, acc); return;
+    case 4: dot_blocks<4>(ld, C, block, sc, a, acc); return;
+    case 5: dot_blocks<5>(ld, C, block, sc, a, acc); return;
+    case 6: dot_blocks<6>(ld, C, block, sc, a, acc); return;
+    case 7: dot_blocks<7>(ld, C, block, sc, a, acc); return;
+    default: dot_blocks<8>(ld, C, block, sc, a, acc); return;
+  }
+}
+
+MOE_AVX512 void dot_f32_v(const float* w, int C, const float* const* a, int nt, float* acc) {
+  dot_any([&](int c) MOE_AVX512 { return _mm512_loadu_ps(w + c); }, C, C, nullptr, a, nt, acc);
+}
+MOE_AVX512 void dot_bf16_v(const uint16_t* w, int C, const float* const* a, int nt, float* acc) {
+  dot_any([&](int c) MOE_AVX512 { return ld_bf16(w + c); }, C, C, nullptr, a, nt, acc);
+}
+MOE_AVX512 void dot_fp8_v(const uint8_t* w, const float* sc, int C, const float* const* a, int nt, float* acc) {
+  dot_any([&](int c) MOE_AVX512 { return ld_e4m3(w + c); }, C, 128, sc, a, nt, acc);
+}
+MOE_AVX512 void dot_mx4_v(const uint8_t* w, const uint8_t* sc, int C, const float* const* a, int nt, float* acc) {
+  const __m512 table = _mm512_loadu_ps(g_tab.e2m1);
+  dot_any([&](int c) MOE_AVX512 { return ld_e2m1(w + c / 2, table, _mm512_set1_ps(e8m0_to_f32(sc[c / 32]))); },
+          C, C, nullptr, a, nt, acc);
+}
+
+const bool g_avx512 = __builtin_cpu_supports("avx512f");
+
+void dot_f32(const float* w, int C, const float* const* a, int nt, float* acc) {
+  if (g_avx512) return dot_f32_v(w, C, a, nt, acc);
+  dot_f32_p(w, C, a, nt, acc);
+}
+void dot_bf16(const uint16_t* w, int C, const float* const* a, int nt, float* acc) {
+  if (g_avx512) return dot_bf16_v(w, C, a, nt, acc);
+  dot_dec_p([&](int c) { return bf16_to_f32(w[c]); }, C, C, nullptr, a, nt, acc);
+}
+void dot_fp8(const uint8_t* w, const float* sc, int C, const float* const* a, int nt, float* acc) {
+  if (g_avx512) return dot_fp8_v(w, sc, C, a, nt, acc);
+  dot_dec_p([&](int c) { return g_tab.e4m3[w[c]]; }, C, 128, sc, a, nt, acc);
+}
+void dot_mx4(const uint8_t* w, const uint8_t* sc, int C, const float* const* a, int nt, float* acc) {
+  if (g_avx512) return dot_mx4_v(w, sc, C, a, nt, acc);
+  dot_dec_p([&](int c) { return g_tab.e2m1[(w[c / 2] >> (4 * (c & 1))) & 15] * e8m0_to_f32(sc[c / 32]); }, C, C,
+            nullptr, a, nt, acc);
+}
+
+// row r of matrix m (0 gate, 1 up: [F][H]; 2 down: [H][F]) of a record against nt rows
+void dot_row(const uint8_t* rec, int dtype, int H, int F, int m, int r, const float* const* a, int nt, float* acc) {
+  const uint64_t n = (uint64_t)F * H;
+  const int C = m == 2 ? F : H;
+  switch (dtype) {
+    case MOE_F32:
+      dot_f32(reinterpret_cast<const float*>(rec) + m * n + (uint64_t)r * C, C, a, nt, acc);
+      return;
+    case MOE_BF16:
+      dot_bf16(reinterpret_cast<const uint16_t*>(rec) + m * n + (uint64_t)r * C, C, a, nt, acc);
+      return;
+    case MOE_FP8_E4M3_B128: {
+      const float* scales = reinterpret_cast<const float*>(rec + 3 * n);
+      const uint64_t per = (uint64_t)(F / 128) * (H / 128);
+      dot_fp8(rec + m * n + (uint64_t)r * C, scales + m * per + (uint64_t)(r / 128) * (C / 128), C, a, nt, acc);
+      return;
+    }
+    default: {  // MOE_MXFP4
+      const uint8_t* scales = rec + 3 * n / 2;
+      dot_mx4(rec + m * n / 2 + (uint64_t)r * C / 2, scales + m * (n / 32) + (uint64_t)r * (C / 32), C, a, nt, acc);
+      return;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- worker pool
+class Pool {
+ public:
+  Pool() {
+    cpu_set_t set;
+    int n = 0;
+    if (sched_getaffinity(0, sizeof set, &set) == 0) n = CPU_COUNT(&set);
+    if (n <= 0) n = (int)std::thread::hardware_concurrency();
+    nthreads_ = std::max(1, n);
+    for (int i = 1; i < nthreads_; ++i) workers_.emplace_back([this] { loop(); });
+  }
+  ~Pool() {
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      stop_ = true;
+      ++gen_;
+    }
+    cv_.notify_all();
+    for (auto& t : workers_) t.join();
+  }
+  int threads() const { return nthreads_; }
+
+  // runs fn(i) for i in [0, n) on every thread of the pool and the caller; returns when all are done
+  void run(int n, const std::function<void(int)>& fn) {
+    if (n <= 0) return;
+    std::unique_lock<std::mutex> call(call_mu_);  // one parallel region at a time
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      fn_ = &fn;
+      n_ = n;
+      next_.store(0);
+      busy_ = (int)workers_.size();
+      ++gen_;
+    }
+    cv_.notify_all();
+    work();
+    std::unique_lock<std::mutex> lk(mu_);
+    done_cv_.wait(lk, [this] { return busy_ == 0; });
+    fn_ = nullptr;
+  }
+
+ private:
+  void work() {
+    for (int i = next_.fetch_add(1); i < n_; i = next_.fetch_add(1)) (*fn_)(i);
+  }
+  void loop() {
+    uint64_t seen = 0;
+    for (;;) {
+      {
+        std::unique_lock<std::mutex> lk(mu_);
+        cv_.wait(lk, [&] { return gen_ != seen; });
+        seen = gen_;
+        if (stop_) return;
+      }
+      work();
+      {
+        std::lock_guard<std::mutex> lk(mu_);
+        if (--busy_ == 0) done_cv_.notify_one();
+      }
+    }
+  }
+  int nthreads_ = 1;
+  std::vector<std::thread> workers_;
+  std::mutex mu_, call_mu_;
+  std::condition_variable cv_, done_cv_;
+  const std::function<void(int)>* fn_ = nullptr;
+  int n_ = 0, busy_ = 0;
+  std::atomic<int> next_{0};
+  uint64_t gen_ = 0;
+  bool stop_ = false;
+};
+
+Pool& pool() {
+  static Pool p;  // created on first use, joined when the library unloads
+  return p;
+}
+
+}  // namespace
+
+int host_threads() { return pool().threads(); }
+
+void host_cold_ffn(const HostFfnJob& j) {
+  const int H = j.H, F = j.F, n = j.T * j.k;
+  // group the cold pairs by expert (ascending expert id, pairs in call order)
+  std::vector<int> order;
+  for (int p = 0; p < n; ++p)
+    if (j.sid[p] >= j.S + j.E && j.sid[p] < j.S + 2 * j.E) order.push_back(p);
+  if (order.empty()) return;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return j.sid[a] < j.sid[b]; });
+  struct Group {
+    int e, first, count;
+  };
+  std::vector<Group> groups;
+  for (int i = 0; i < (int)order.size(); ++i) {
+    const int e = j.sid[order[i]] - j.S - j.E;
+    if (groups.empty() || groups.back().e != e) groups.push_back({e, i, 0});
+    groups.back().count += 1;
+  }
+  // activations as fp32 rows, and the h rows of every cold pair
+  std::vector<float> xf((size_t)j.T * H);
+  for (size_t i = 0; i < xf.size(); ++i)
+    xf[i] = j.dtype == MOE_F32 ? reinterpret_cast<const float*>(j.x)[i]
+                               : bf16_to_f32(reinterpret_cast<const uint16_t*>(j.x)[i]);
+  std::vector<float> hbuf((size_t)order.size() * F);
+  constexpr int kRowsF = 16, kRowsH = 32;  // weight rows per block
+  const int bf = F / kRowsF, bh = (H + kRowsH - 1) / kRowsH;
+  // phase 1: gate/up rows of each cold expert against its tokens (kMaxTok at a time)
+  pool().run((int)groups.size() * bf, [&](int item) {
+    const Group& g = groups[item / bf];
+    const int f0 = (item % bf) * kRowsF;
+    const uint8_t* rec = j.host + (uint64_t)g.e * j.stride;
+    for (int t0 = 0; t0 < g.count; t0 += kMaxTok) {
+      const int nt = std::min(kMaxTok, g.count - t0);
+      const float* a[kMaxTok];
+      for (int t = 0; t < nt; ++t) a[t] = xf.data() + (size_t)(order[g.first + t0 + t] / j.k) * H;
+      for (int f = f0; f < f0 + kRowsF; ++f) {
+        float gv[kMaxTok], uv[kMaxTok];
+        dot_row(rec, j.dtype, H, F, 0, f, a, nt, gv);
+        dot_row(rec, j.dtype, H, F, 1, f, a, nt, uv);
+        for (int t = 0; t < nt; ++t)
+          hbuf[(size_t)(g.first + t0 + t) * F + f] = gv[t] / (1.0f + expf(-gv[t])) * uv[t];
+      }
+    }
+  });
+  // phase 2: down rows of each cold expert against its h rows, into the output rows
+  pool().run((int)groups.size() * bh, [&](int item) {
+    const Group& g = groups[item / bh];
+    const int r0 = (item % bh) * kRowsH, r1 = std::min(H, r0 + kRowsH);
+    const uint8_t* rec = j.host + (uint64_t)g.e * j.stride;
+    for (int t0 = 0; t0 < g.count; t0 += kMaxTok) {
+      const int nt = std::min(kMaxTok, g.count - t0);
+      const float* a[kMaxTok];
+      for (int t = 0; t < nt; ++t) a[t] = hbuf.data() + (size_t)(g.first + t0 + t) * F;
+      for (int r = r0; r < r1; ++r) {
+        float o[kMaxTok];
+        dot_row(rec, j.dtype, H, F, 2, r, a, nt, o);
+        for (int t = 0; t < nt; ++t) j.out[(size_t)order[g.first + t0 + t] * H + r] = o[t];
+      }
+    }
+  });
+}
+
+}  // namespace moe

@@ -105,6 +105,11 @@ __global__ void k_reset(CacheDev c) {
   }
 }
 
+// the layer's cold-mode flag, written in stream order like the table itself
+__global__ void k_set_cold(int32_t* cold, int on) {
+  if (threadIdx.x == 0) *cold = on;
+}
+
 // ---------------------------------------------------------------- copy
 // Fixed grid; the list (mode, count, pairs) is read on the device.  Each
 // workgroup moves 16 KiB chunks: 256 threads x 4 loads of 16 bytes in flight,
@@ -115,7 +120,7 @@ __global__ __launch_bounds__(kCopyThreads) void k_copy(const int32_t* __restrict
                                                       int S, int E, int32_t* err) {
   const int mode = list[0];
   const int count = list[1];
-  if (mode == MOE_MODE_STAGED_ALL || count <= 0) return;
+  if (mode == MOE_MODE_STAGED_ALL || mode == MOE_MODE_COLD || count <= 0) return;  // cold experts never move
   constexpr uint64_t CH = (uint64_t)kCopyThreads * kCopyUnroll;
   const uint64_t per = (rb16 + CH - 1) / CH;
   const uint64_t total = (uint64_t)count * per;
@@ -171,6 +176,11 @@ hipError_t launch_stage_all(moe_offload* h, const int32_t* ids, int n, int32_t* 
 
 hipError_t launch_pin(moe_offload* h, const int32_t* experts, int n, hipStream_t s) {
   launch_k(h, MOE_K_ENSURE, k_pin, dim3(1), dim3(kBlock), 0, s, h->cache, experts, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_cold(moe_offload* h, int on, hipStream_t s) {
+  hipLaunchKernelGGL(k_set_cold, dim3(1), dim3(64), 0, s, h->cache.cold, on ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -37,6 +37,8 @@
 // tokens inside a record's list: every output element is one fixed-order sum.
 #include <math.h>
 
+#include <string.h>
+
 #include <algorithm>
 #include <mutex>
 
@@ -81,7 +83,7 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 // ------------------------------------------------------------------ grouping
 __global__ __launch_bounds__(kBlock) void k_group(FfnArgs a) {
   __shared__ GroupShared g;
-  group_body(a.slot_ids, a.T * a.k, a.S + a.E, a.grp, a.off_pairs, a.off_tiles, a.err, g);
+  group_body(a.slot_ids, a.T * a.k, a.S + a.E, a.grp, a.off_pairs, a.off_tiles, a.err, g, a.S + 2 * a.E);
 }
 
 // A work item's record (pointer, token count); its pair ids come from the same
@@ -1011,10 +1013,12 @@ __device__ __forceinline__ OneHead one_head(const FfnArgs& a, bool fill) {
   return o;
 }
 
-// record of choice j (j = k: the shared expert); j is wavefront-uniform
+// record of choice j (j = k: the shared expert), or null for a cold expert
+// (index S + E + e: computed on the host); j is wavefront-uniform
 __device__ __forceinline__ const uint8_t* one_record(const FfnArgs& a, int j, const OneHead& o) {
   if (j == a.k) return a.shared;
   int ri = __builtin_amdgcn_readlane(o.sid, j);
+  if (ri >= a.S + a.E && ri < a.S + 2 * a.E) return nullptr;
   if ((unsigned)ri >= (unsigned)(a.S + a.E)) {
     atomicOr(a.err, MOE_DEV_ERR_AUDIT);
     ri = 0;
@@ -1061,6 +1065,7 @@ __global__ __launch_bounds__(128) void k_gateup_one(FfnArgs a) {
   for (int item = blockIdx.x * 2 + (threadIdx.x >> 6); item < items; item += gridDim.x * 2) {
     const int j = item / RG, f = (item % RG) * 4 + q;
     const uint8_t* rec = one_record(a, j, o);
+    if (!rec) continue;  // a cold expert (wavefront-uniform)
     float g = 0.f, up = 0.f;
     bool done = false;
     if constexpr (FILL) {
@@ -1103,6 +1108,7 @@ __global__ __launch_bounds__(128) void k_down_one(FfnArgs a) {
   for (int item = blockIdx.x * 2 + (threadIdx.x >> 6); item < items; item += gridDim.x * 2) {
     const int j = item / RG, h0 = (item % RG) * 8 + q;
     const uint8_t* rec = one_record(a, j, o);
+    if (!rec) continue;  // a cold expert (wavefront-uniform)
     float s0 = 0.f, s1 = 0.f;
     bool done = false;
     if constexpr (FILL) {
@@ -1247,7 +1253,46 @@ __global__ __launch_bounds__(kRowThreads) void k_combine(FfnArgs a, void* __rest
   }
 }
 
+// part rows of the cold pairs (record index in [S + E, S + 2E)) from the host's
+// output rows (device-mapped host memory): one workgroup per pair
+__global__ __launch_bounds__(256) void k_cold_scatter(const int32_t* __restrict__ slot_ids, int n, int S, int E,
+                                                      int H, const float* __restrict__ host_rows,
+                                                      float* __restrict__ part) {
+  for (int p = blockIdx.x; p < n; p += gridDim.x) {
+    const int r = slot_ids[p];
+    if (r < S + E || r >= S + 2 * E) continue;  // workgroup-uniform
+    const float4* src = reinterpret_cast<const float4*>(host_rows + (uint64_t)p * H);
+    float4* dst = reinterpret_cast<float4*>(part + (uint64_t)p * H);
+    for (int i = threadIdx.x; i < H / 4; i += blockDim.x) dst[i] = src[i];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_cold_combine(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int T,
+                               const void* shared, void* y, const void* residual, void* x_next, hipStream_t s) {
+  const int n = T * h->k;
+  launch_k(h, MOE_K_COMBINE, k_cold_scatter, dim3(std::min(n, 1024)), dim3(256), 0, s, slot_ids, n, h->S, h->E, h->H,
+           (const float*)h->cold_out_dev, h->part);
+  FfnArgs a;
+  memset(&a, 0, sizeof a);
+  a.x = x;
+  a.w = w;
+  a.part = h->part;
+  a.y = y;
+  a.residual = residual ? residual : x;
+  a.x_next = x_next;
+  a.shared = (const uint8_t*)shared;
+  a.T = T;
+  a.k = h->k;
+  a.H = h->H;
+  a.F = h->F;
+  if (h->dtype == MOE_F32)
+    launch_k(h, MOE_K_COMBINE, k_combine<true>, dim3(T), dim3(kRowThreads), 0, s, a, (void*)nullptr, 0.f);
+  else
+    launch_k(h, MOE_K_COMBINE, k_combine<false>, dim3(T), dim3(kRowThreads), 0, s, a, (void*)nullptr, 0.f);
+  return hipGetLastError();
+}
 
 // read-through: one token (a work item per choice), or up to kDecodeMaxT tokens
 // with at most kFillPairs pairs (the decode kernels, the copy list in one load

@@ -4,8 +4,10 @@
 #include <string.h>
 
 #include <algorithm>
+#include <chrono>
 #include <new>
 
+#include "host_ffn.h"
 #include "prof.h"
 
 namespace {
@@ -67,6 +69,10 @@ void free_all(moe_offload* h) {
   if (h->own_staging && h->staging) (void)hipFree(h->staging);
   if (h->state_block) (void)hipFree(h->state_block);
   if (h->pinned_i32) (void)hipHostFree(h->pinned_i32);
+  if (h->cold_sid) (void)hipHostFree(h->cold_sid);
+  if (h->cold_x) (void)hipHostFree(h->cold_x);
+  if (h->cold_out) (void)hipHostFree(h->cold_out);
+  if (h->cold_ev) (void)hipEventDestroy(h->cold_ev);
   if (h->prof) {
     for (auto& pair : h->prof->ev)
       for (hipEvent_t e : pair)
@@ -103,7 +109,7 @@ int check_desc(const moe_offload_desc* d) {
 // sets h->gl.  Depends on E, S, H, F, k, dtype and max_tokens only.
 struct StateLayout {
   size_t o_slot_of, o_expert_of, o_last, o_score, o_pinned, o_act, o_tick, o_list, o_pf, o_cnt, o_err, o_logits,
-      o_grp, o_h, o_part, o_scr, total;
+      o_grp, o_h, o_part, o_scr, o_cold, total;
 };
 
 StateLayout state_layout(moe_offload* h) {
@@ -135,6 +141,7 @@ StateLayout state_layout(moe_offload* h) {
   l.o_h = take((h->dtype == MOE_F32 ? 4 : 2) * (size_t)rows * h->F);
   l.o_part = take(4 * (size_t)rows * h->H);
   l.o_scr = take(64);
+  l.o_cold = take(4);
   l.total = off;
   return l;
 }
@@ -240,6 +247,7 @@ int moe_offload_create(const moe_offload_desc* d, moe_offload** out) {
   h->cache.pf_list = (int32_t*)(b + o_pf);
   h->cache.counters = (uint64_t*)(b + o_cnt);
   h->cache.err = (int32_t*)(b + o_err);
+  h->cache.cold = (int32_t*)(b + sl.o_cold);
   h->cache.E = h->E;
   h->cache.S = h->S;
   h->cache.record_bytes = h->record_bytes;
@@ -354,9 +362,44 @@ int moe_slot_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const f
   if (int rc = check_handle(h)) return rc;
   if (int rc = check_T(h, T)) return rc;
   if (!x || !slot_ids || !w || !y) return fail(MOE_EINVAL, "moe_slot_ffn: null pointer");
+  if (h->cold_on) return fail(MOE_EINVAL, "moe_slot_ffn: the layer is in cold mode; use moe_slot_ffn_host_cold");
   DeviceGuard g(h->device);
   HIP_TRY(moe::launch_ffn(h, x, slot_ids, w, T, shared_record, y, residual, x_next, nullptr, 0.f,
                           (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_slot_ffn_host_cold(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int32_t T,
+                           const void* shared_record, void* y, const void* residual, void* x_next, void* stream) {
+  if (int rc = check_handle(h)) return rc;
+  if (int rc = check_T(h, T)) return rc;
+  if (!x || !slot_ids || !w || !y) return fail(MOE_EINVAL, "moe_slot_ffn_host_cold: null pointer");
+  if (!h->cold_out) return fail(MOE_EINVAL, "moe_slot_ffn_host_cold: the cold mode was never switched on");
+  DeviceGuard g(h->device);
+  hipStream_t s = (hipStream_t)stream;
+  const size_t es = h->dtype == MOE_F32 ? 4 : 2;
+  // the call's record indices and activations to the host, then the GPU's share of the FFN
+  HIP_TRY(hipMemcpyAsync(h->cold_sid, slot_ids, 4 * (size_t)T * h->k, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipMemcpyAsync(h->cold_x, x, es * (size_t)T * h->H, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipEventRecord(h->cold_ev, s));
+  HIP_TRY(moe::launch_ffn(h, x, slot_ids, w, T, shared_record, y, residual, x_next, nullptr, 0.f, s, false, false));
+  HIP_TRY(hipEventSynchronize(h->cold_ev));
+  // the host's share meanwhile, into the mapped output rows
+  moe::HostFfnJob job;
+  job.host = h->host;
+  job.stride = h->record_stride;
+  job.dtype = h->dtype;
+  job.H = h->H;
+  job.F = h->F;
+  job.x = h->cold_x;
+  job.T = T;
+  job.k = h->k;
+  job.sid = h->cold_sid;
+  job.S = h->S;
+  job.E = h->E;
+  job.out = h->cold_out;
+  moe::host_cold_ffn(job);
+  HIP_TRY(moe::launch_cold_combine(h, x, slot_ids, w, T, shared_record, y, residual, x_next, s));
   return MOE_OK;
 }
 
@@ -440,6 +483,80 @@ int moe_copy_prefetch(moe_offload* h, void* stream) {
   return MOE_OK;
 }
 
+int moe_offload_set_cold(moe_offload* h, int32_t mode, void* stream, int32_t* chosen, double* cpu_us,
+                         double* link_us) {
+  if (int rc = check_handle(h)) return rc;
+  if (mode != MOE_COLD_OFF && mode != MOE_COLD_ON && mode != MOE_COLD_AUTO)
+    return fail(MOE_EINVAL, "moe_offload_set_cold: mode %d", mode);
+  DeviceGuard g(h->device);
+  hipStream_t s = (hipStream_t)stream;
+  if (cpu_us) *cpu_us = 0.0;
+  if (link_us) *link_us = 0.0;
+  if (mode != MOE_COLD_OFF && !h->cold_out) {  // the host side's buffers, once
+    const size_t es = h->dtype == MOE_F32 ? 4 : 2;
+    HIP_TRY(hipHostMalloc((void**)&h->cold_sid, 4 * (size_t)h->max_tokens * h->k, hipHostMallocDefault));
+    HIP_TRY(hipHostMalloc(&h->cold_x, es * (size_t)h->max_tokens * h->H, hipHostMallocDefault));
+    HIP_TRY(hipHostMalloc((void**)&h->cold_out, 4 * (size_t)h->max_tokens * h->k * h->H,
+                          hipHostMallocMapped | hipHostMallocCoherent));
+    HIP_TRY(hipHostGetDevicePointer((void**)&h->cold_out_dev, h->cold_out, 0));
+    HIP_TRY(hipEventCreateWithFlags(&h->cold_ev, hipEventDisableTiming));
+  }
+  int on = mode == MOE_COLD_ON;
+  if (mode == MOE_COLD_AUTO) {
+    // one record's FFN on the host at one token, against one record over the link (a pinned
+    // host-to-device copy into staging); the median of three records, each touched once
+    HIP_TRY(hipStreamSynchronize(s));
+    const int reps = std::min(3, h->E);
+    double cpu[3] = {0, 0, 0}, link[3] = {0, 0, 0};
+    memset(h->cold_x, 0, (h->dtype == MOE_F32 ? 4 : 2) * (size_t)h->H);
+    hipEvent_t a = nullptr, b = nullptr;
+    HIP_TRY(hipEventCreate(&a));
+    hipError_t e = hipEventCreate(&b);
+    for (int r = 0; r < reps && e == hipSuccess; ++r) {
+      const int ex = h->E - 1 - r;  // records the calls of this layer are least likely to have touched
+      h->cold_sid[0] = h->S + h->E + ex;
+      moe::HostFfnJob job;
+      job.host = h->host;
+      job.stride = h->record_stride;
+      job.dtype = h->dtype;
+      job.H = h->H;
+      job.F = h->F;
+      job.x = h->cold_x;
+      job.T = 1;
+      job.k = 1;
+      job.sid = h->cold_sid;
+      job.S = h->S;
+      job.E = h->E;
+      job.out = h->cold_out;
+      const auto t0 = std::chrono::steady_clock::now();
+      moe::host_cold_ffn(job);
+      cpu[r] = std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
+      e = hipEventRecord(a, s);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(h->staging + (size_t)(r % h->E) * h->record_stride, h->host + (size_t)ex * h->record_stride,
+                           h->record_bytes, hipMemcpyHostToDevice, s);
+      if (e == hipSuccess) e = hipEventRecord(b, s);
+      if (e == hipSuccess) e = hipEventSynchronize(b);
+      float ms = 0.f;
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+      link[r] = 1e3 * ms;
+    }
+    (void)hipEventDestroy(a);
+    (void)hipEventDestroy(b);
+    if (e != hipSuccess) return hip_fail(e, "moe_offload_set_cold: calibration");
+    std::sort(cpu, cpu + reps);
+    std::sort(link, link + reps);
+    const double c_us = cpu[reps / 2], l_us = link[reps / 2];
+    if (cpu_us) *cpu_us = c_us;
+    if (link_us) *link_us = l_us;
+    on = c_us < l_us;
+  }
+  HIP_TRY(moe::launch_set_cold(h, on, s));
+  h->cold_on = on != 0;
+  if (chosen) *chosen = on;
+  return MOE_OK;
+}
+
 int moe_offload_stats(moe_offload* h, moe_stats* out) {
   if (int rc = check_handle(h)) return rc;
   if (!out) return fail(MOE_EINVAL, "null stats");
@@ -466,6 +583,7 @@ int moe_offload_stats(moe_offload* h, moe_stats* out) {
   out->prefetch_installs = c[moe::C_PF_INSTALLS];
   out->prefetch_hits = c[moe::C_PF_HITS];
   out->bytes_copied = c[moe::C_BYTES];
+  out->cold_misses = c[moe::C_COLD];
   out->tick = tick;
   out->error = err;
   out->resident = resident;

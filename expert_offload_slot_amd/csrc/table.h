@@ -49,6 +49,7 @@ struct SharedTable {
   int vic[kMaxExperts];    // victim slot by rank
   int wave[4 * kWaves];
   int bad;
+  int cold;                // the layer's cold-mode flag as loaded
   uint64_t tick;           // the table's call counter as loaded
   uint64_t cnt[C_N];       // the counters as loaded
 };
@@ -78,6 +79,7 @@ __device__ __forceinline__ TableRegs fetch_table(const CacheDev& c) {
   }
   if (u == 0) r.tc = *c.tick;
   if (u >= 1 && u <= C_N) r.tc = c.counters[u - 1];
+  if (u == C_N + 1) r.tc = (uint64_t)(uint32_t)*c.cold;
   return r;
 }
 
@@ -108,6 +110,7 @@ __device__ __forceinline__ void put_table(const CacheDev& c, const TableRegs& r,
   }
   if (u == 0) t.tick = r.tc;
   if (u >= 1 && u <= C_N) t.cnt[u - 1] = r.tc;
+  if (u == C_N + 1) t.cold = r.tc != 0;
 }
 
 // Loads the table into LDS (fetch_table, then put_table).
@@ -198,6 +201,39 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
   int rk[4], tot[4];
   block_rank4(f, t.wave, rk, tot);
   const int mrank = rk[1], nm = tot[1], nh = tot[2], npf = tot[3];
+
+  if (t.cold) {  // host-computed cold experts: nothing loads, misses are read at S + E + e
+    if (inD && sl >= 0) {
+      const uint32_t old = t.score[sl];
+      t.last_use[sl] = tick;
+      t.score[sl] = old < kScoreMax ? old + 1 : old;
+    }
+    if (inD && t.act[tid] < kScoreMax) t.act[tid] += 1;
+    if (miss) {
+      c.copy_list[2 + 2 * mrank] = tid;
+      c.copy_list[3 + 2 * mrank] = S + E + tid;
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += kBlock) {
+      const int e = ids[i];
+      const int r = t.slot_of[e];
+      const int v = r >= 0 ? r : S + E + e;
+      slot_ids[i] = v;
+      if (slot_lds) slot_lds[i] = v;
+    }
+    store_table(c, t);
+    if (audit) audit_table(c, t, false);
+    if (tid == 0) {
+      c.copy_list[0] = MOE_MODE_COLD;
+      c.copy_list[1] = nm;
+      *c.tick = tick;
+      c.counters[C_CALLS] = t.cnt[C_CALLS] + 1;
+      c.counters[C_HITS] = t.cnt[C_HITS] + (uint64_t)nh;
+      c.counters[C_PF_HITS] = t.cnt[C_PF_HITS] + (uint64_t)npf;
+      c.counters[C_COLD] = t.cnt[C_COLD] + (uint64_t)nm;
+    }
+    return;  // block-uniform
+  }
 
   // eligible victims by rank: slots not pinned and not holding an expert of D;
   // the call overflows when the misses outnumber them (no pins: when |D| > S)

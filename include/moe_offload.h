@@ -63,8 +63,9 @@
  *   [H][F/32]; weight = e2m1(q) * 2^(e - 127).
  *
  * Record index ("slot id") space used by slot_ids:
- *   r in [0, S)       slot r of the slot tensor
- *   r in [S, S + E)   staging record r - S (expert r - S staged for this call)
+ *   r in [0, S)          slot r of the slot tensor
+ *   r in [S, S + E)      staging record r - S (expert r - S staged for this call)
+ *   r in [S + E, S + 2E) cold mode: expert r - S - E, computed by the host CPU from its host record
  */
 #ifndef MOE_OFFLOAD_H
 #define MOE_OFFLOAD_H
@@ -151,6 +152,7 @@ typedef struct {
   uint64_t tick;              /* LRU clock (ensure and stage calls) */
   int32_t error;              /* sticky MOE_DEV_ERR_* bits */
   int32_t resident;           /* experts currently resident in slots */
+  uint64_t cold_misses;       /* misses computed on the host in cold mode (moe_offload_set_cold) */
 } moe_stats;
 
 /* Device addresses and sizes of the handle's state, for inspection and tests.
@@ -179,8 +181,9 @@ typedef struct {
                              policy, used by MOE_FLAG_FREQ) */
 } moe_info;
 
-/* copy-list modes (copy_list[0]) */
-enum { MOE_MODE_SLOTS = 0, MOE_MODE_STAGED = 1, MOE_MODE_STAGED_ALL = 2 };
+/* copy-list modes (copy_list[0]); MOE_MODE_COLD: the listed misses are computed on the host
+ * (record index S + E + e), nothing is copied */
+enum { MOE_MODE_SLOTS = 0, MOE_MODE_STAGED = 1, MOE_MODE_STAGED_ALL = 2, MOE_MODE_COLD = 3 };
 
 /* Create one layer's handle: pinned mapped host store [E, record_stride]
  * (contents undefined until the caller writes it), slot tensor, slot table
@@ -275,6 +278,44 @@ int moe_copy_misses(moe_offload* h, void* stream);
  * Asynchronous, capture-safe. */
 int moe_slot_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int32_t T,
                  const void* shared_record, void* y, const void* residual, void* x_next, void* stream);
+
+/* Host-computed cold experts (npu-offload README, intro and "Architecture":
+ * hot experts stay in accelerator memory, the host CPU computes the cold ones
+ * from host DRAM in parallel, only activations cross the link; "Results", where
+ * the time goes: the CPU's share is bound by DRAM bandwidth).
+ * In cold mode an ensure call loads nothing: hits are used in place (last_use,
+ * usage score and activation count as usual), each miss e keeps no slot, takes
+ * no victim and is read at record index S + E + e; the copy list is
+ * {MOE_MODE_COLD, |misses|, (e, S + E + e)...} in ascending id and the copy
+ * kernel moves nothing; stats.cold_misses counts them.
+ *   mode: MOE_COLD_OFF, MOE_COLD_ON, or MOE_COLD_AUTO: measure, for one record
+ *         of this layer, the host FFN at one token (on the library's worker
+ *         threads) against a pinned host-to-device copy of the record, and turn
+ *         the cold mode on when the host is faster (the layer's misses then go
+ *         to the CPU instead of over the link).
+ *   chosen (may be NULL): the resulting mode (0 off, 1 on);
+ *   cpu_us, link_us (may be NULL): the two measured times per record (AUTO only;
+ *         0 otherwise).
+ * Host-synchronising on `stream`; the flag is written on the device in stream
+ * order, so issue it on the compute stream between calls.  Switching on the
+ * first time allocates the pinned host buffers the cold FFN uses (max_tokens
+ * rows).  While the mode is on, the FFN must be moe_slot_ffn_host_cold:
+ * moe_slot_ffn and the decode chain refuse the handle (MOE_EINVAL).
+ * Errors: MOE_EINVAL, MOE_ENOMEM, MOE_EHIP. */
+enum { MOE_COLD_OFF = 0, MOE_COLD_ON = 1, MOE_COLD_AUTO = 2 };
+int moe_offload_set_cold(moe_offload* h, int32_t mode, void* stream, int32_t* chosen, double* cpu_us,
+                         double* link_us);
+
+/* The expert FFN of a cold-mode call (same arguments and results as
+ * moe_slot_ffn): the GPU computes the resident experts while the host CPU
+ * computes every pair whose record index is S + E + e from expert e's host
+ * record (fp32 sums; h kept in fp32), then the host's rows join the GPU's in
+ * the same top-k weighted combine.  Host-synchronising (it waits for the
+ * call's indices and activations), not capturable.  Outputs match the plain
+ * definition within the same tolerance as the GPU path, not bit for bit.
+ * Errors: as moe_slot_ffn; MOE_EINVAL if the cold mode was never switched on. */
+int moe_slot_ffn_host_cold(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int32_t T,
+                           const void* shared_record, void* y, const void* residual, void* x_next, void* stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc): moe_slot_ffn with the

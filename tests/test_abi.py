@@ -22,9 +22,9 @@ def test_exported_symbols_are_plain_c():
 
 
 def test_struct_sizes_match_the_header_layout():
-    # moe_offload_desc: 9 x 32-bit fields + 2 pointers; moe_stats: 9 x u64 + 2 x i32
+    # moe_offload_desc: 9 x 32-bit fields + 2 pointers; moe_stats: 9 x u64 + 2 x i32 + 1 x u64
     assert ctypes.sizeof(m.Desc) == 9 * 4 + 4 + 2 * 8
-    assert ctypes.sizeof(m.Stats) == 9 * 8 + 2 * 4
+    assert ctypes.sizeof(m.Stats) == 9 * 8 + 2 * 4 + 8
     # moe_kernel_times: MOE_K_N doubles + MOE_K_N u64
     assert ctypes.sizeof(m.KernelTimes) == 2 * 8 * len(m.KERNEL_KINDS)
 
@@ -64,6 +64,9 @@ def test_null_handles_are_rejected_before_any_device_call():
         "moe_chain_run_eager": (None, None),
         "moe_chain_set_read_through": (None, 1),
         "moe_chain_get_buffers": (None, None),
+        "moe_slot_ffn_host_cold": (None, None, None, None, 1, None, None, None, None, None),
+        "moe_slot_ffn_noalloc": (None, None, None, None, 1, None, None, None, None, None),
+        "moe_offload_set_cold": (None, 1, None, None, None, None),
     }
     for name, args in calls.items():
         rc = getattr(L, name)(*args)

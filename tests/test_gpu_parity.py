@@ -476,3 +476,86 @@ def test_auto_slots_fill_free_memory_up_to_the_reserve():
     finally:
         for h in reversed(hs):
             m.moe_offload_destroy(h)
+
+
+@pytest.mark.parametrize("wdt,E,S,k,H,F,Ts,shared", [
+    (1, 32, 8, 4, 512, 256, [1, 3, 9, 2], False),   # single-token and batch kernels around the host's pairs
+    (2, 16, 6, 4, 256, 256, [2, 5, 70], True),      # fp8 + shared expert; 70 tokens: the grouped GEMM
+    (3, 16, 8, 4, 256, 512, [1, 4], True),          # MXFP4
+    (0, 8, 4, 2, 64, 128, [4, 1], False),           # fp32
+])
+def test_host_cold_experts_parity(wdt, E, S, k, H, F, Ts, shared):
+    """Cold mode switched on mid-stream and off again: ids, slot ids, copy lists (mode COLD, index
+    S + E + e), tables, scores and activation counts bit-exact against the oracle's cold rule; layer
+    outputs (GPU hits + host-computed misses) within tolerance; resident slots keep their bytes."""
+    print("cold wdt=%d E=%d S=%d k=%d H=%d F=%d Ts=%s" % (wdt, E, S, k, H, F, Ts), flush=True)
+    host, wr, b, sh = make_layer_inputs(51, 0, E, H, F, wdt, 1.2, shared)
+    gl = GpuLayer(E, S, k, H, F, wdt, max(Ts), host, wr, b, shared=sh)
+    ol = oracle.Layer(E, S, k, H, F, wdt, host, wr, b, shared=sh)
+    steps = 16
+    xs = synth.tokens(51, 7, max(Ts), H, steps, 0.0, wdt)
+    st = torch.cuda.current_stream()
+    cold_seen = 0
+    try:
+        for s in range(steps):
+            if s == 4:
+                chosen, _, _ = m.moe_offload_set_cold(gl.h, m.COLD_ON, st)
+                assert chosen == 1
+                ol.cache.set_cold(True)
+            if s == 12:
+                assert m.moe_offload_set_cold(gl.h, m.COLD_OFF, st)[0] == 0
+                ol.cache.set_cold(False)
+            cold = 4 <= s < 12
+            T = Ts[s % len(Ts)]
+            x = np.ascontiguousarray(xs[s][:T])
+            xd = to_dev(x)
+            gl.route(xd, T)
+            gl.ensure(T)
+            gl.copy()
+            if cold:
+                with pytest.raises(m.MoeError) as ei:
+                    gl.ffn(xd, T)
+                assert ei.value.code == m.EINVAL
+                m.moe_slot_ffn_host_cold(gl.h, xd, gl.slot_ids, gl.w, T, gl.shared, gl.y, None, gl.xn, st)
+            else:
+                gl.ffn(xd, T)
+            r = ol.step(x)
+            assert r["mode"] == (oracle.COLD if cold else r["mode"])
+            if cold:
+                cold_seen += len(r["pairs"])
+            compare_call(gl, r, T, r["y64"], oracle_cache=ol.cache)
+            assert np.array_equal(to_np(gl.xn[:T]), oracle.residual(x, to_np(gl.y[:T]), wdt))
+        stt = gl.stats()
+        c = ol.cache.counters()
+        assert stt["error"] == 0 and stt["cold_misses"] == c["cold"] == cold_seen and cold_seen > 0
+        for key in ("calls", "hits", "misses", "staged_calls", "staged_copies"):
+            assert stt[key] == c[key], key
+        so, eo, lu = gl.table()
+        rb = oracle.record_bytes(wdt, H, F)
+        for s_ in range(S):
+            if eo[s_] >= 0:
+                assert np.array_equal(gl.slot_bytes(s_, rb), host[eo[s_], :rb])
+    finally:
+        gl.close()
+
+
+def test_host_cold_policy_measures_both_paths():
+    """MOE_COLD_AUTO: the host FFN of one record against one record over the link, measured on this box;
+    the layer goes cold exactly when the host is faster, and the device flag follows (the next ensure
+    lists its misses as cold or loads them)."""
+    E, S, k, H, F = 16, 4, 4, 2048, 768
+    host, wr, b, _ = make_layer_inputs(52, 0, E, H, F, 1, 1.2)
+    gl = GpuLayer(E, S, k, H, F, 1, 4, host, wr, b)
+    st = torch.cuda.current_stream()
+    try:
+        chosen, cpu_us, link_us = m.moe_offload_set_cold(gl.h, m.COLD_AUTO, st)
+        print("cold policy: host FFN %.1f us, link %.1f us per record -> %s" %
+              (cpu_us, link_us, "host" if chosen else "link"), flush=True)
+        assert cpu_us > 0 and link_us > 0 and chosen == int(cpu_us < link_us)
+        x = to_dev(synth.tokens(52, 1, 4, H, 1, 0.0, 1)[0])
+        gl.route(x, 4)
+        gl.ensure(4)
+        mode, pairs = gl.copy_list()
+        assert len(pairs) > 0 and mode == (m.MODE_COLD if chosen else 0)
+    finally:
+        gl.close()
