@@ -460,6 +460,9 @@ def test_auto_slots_fill_free_memory_up_to_the_reserve():
             hi = mid
         except m.MoeError:
             lo = mid + 1
+    # the runtime's own first-use allocations (code objects, the library's device scratch array, kernel
+    # resources) come with the first handle on a device: take them before measuring
+    m.moe_offload_destroy(m.moe_offload_create(E, k, H, F, k, m.BF16, T, 0, 0))
     torch.cuda.synchronize()
     free_now = torch.cuda.mem_get_info()[0]
     reserve = free_now - lo - 10 * L * stride - stride // 2  # room for k + 10 slots per layer, not k + 11
@@ -489,7 +492,7 @@ def test_host_cold_experts_parity(wdt, E, S, k, H, F, Ts, shared):
     S + E + e), tables, scores and activation counts bit-exact against the oracle's cold rule; layer
     outputs (GPU hits + host-computed misses) within tolerance; resident slots keep their bytes."""
     print("cold wdt=%d E=%d S=%d k=%d H=%d F=%d Ts=%s" % (wdt, E, S, k, H, F, Ts), flush=True)
-    host, wr, b, sh = make_layer_inputs(51, 0, E, H, F, wdt, 1.2, shared)
+    host, wr, b, sh = make_layer_inputs(51, 0, E, H, F, wdt, 0.0, shared)  # flat routing: misses in every phase
     gl = GpuLayer(E, S, k, H, F, wdt, max(Ts), host, wr, b, shared=sh)
     ol = oracle.Layer(E, S, k, H, F, wdt, host, wr, b, shared=sh)
     steps = 16
@@ -556,6 +559,6 @@ def test_host_cold_policy_measures_both_paths():
         gl.route(x, 4)
         gl.ensure(4)
         mode, pairs = gl.copy_list()
-        assert len(pairs) > 0 and mode == (m.MODE_COLD if chosen else 0)
+        assert len(pairs) > 0 and (mode == m.MODE_COLD) == bool(chosen)
     finally:
         gl.close()
