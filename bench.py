@@ -103,8 +103,6 @@ def main():
     ap.add_argument("--quick", action="store_true",
                     help="only the batch-1 window, its steady state, the eager profile and the host link")
     ap.add_argument("--cpu-rates", action="store_true", help="also the CPU oracle's own rates on all threads and one")
-    ap.add_argument("--prefetch-only", action="store_true",
-                    help="only the lookahead-prefetch comparison on the 48-layer workload (its own JSON line)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--mxfp4-only", action="store_true",
                     help="only the same decode chain with MXFP4 expert records (prints its own JSON line)")
@@ -255,14 +253,6 @@ def main():
             (tag, T, steps, ms, T * steps * 1e3 / ms, (delta["misses"] + delta["staged_copies"]) / (T * steps),
              delta["misses"] / (T * steps), delta["staged_calls"], delta["calls"]))
         return T * steps * 1e3 / ms, ms / steps, delta, c, bufs, xs_d
-
-    if args.prefetch_only:
-        print(json.dumps({"workload": "qwen3-30b-a3b-shaped offloaded MoE decode, 48 layers, batch 1: router-"
-                                      "lookahead prefetch (4 installs per layer) against none",
-                          "prefetch": prefetch_compare(args, m, hip, handles, run_decode, token_stream)}), flush=True)
-        for h in reversed(handles):
-            m.moe_offload_destroy(h)
-        return
 
     # ---------------- the timed window: --warmup untimed replays from an empty cache, then --steps timed
     # replays (the headline value; cold start included when the window is short)
@@ -462,7 +452,6 @@ def main():
         result["prefetch"] = prefetch_compare(args, m, hip, handles, run_decode, token_stream)
         result["eviction"] = eviction_compare(args, m, hip, torch, handles, wr_d, b_d, run_decode, token_stream)
         result["slot_fractions"] = slot_fraction_compare(args, m, hip, handles, run_decode, token_stream)
-        result["host_cold"] = host_cold_compare(args, m, hip, torch, handles, wr_d, b_d, token_stream)
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args, handles, routers, stride, T0)
@@ -851,88 +840,6 @@ def eviction_compare(args, m, hip, torch, handles, wr_d, b_d, run_decode, token_
     torch.cuda.synchronize()
     out["pinned"]["pinned_per_layer"] = SLOTS // 2
     out["outputs_identical"] = bool(all(np.array_equal(last["lru"], last[n]) for n in last))
-    return out
-
-
-def host_cold_compare(args, m, hip, torch, handles, wr_d, b_d, token_stream):
-    """Host-computed cold experts against copying them, batch 1, entry-point calls layer by layer (the cold
-    FFN synchronises with the host every layer, so no graph): every layer pins its SLOTS - K_TOP most routed
-    experts of a separate profiling stream, then (a) its misses go over the host link (LRU in the free slots)
-    or (b) the host CPU computes them from host DRAM while the GPU computes the resident ones.  Also the
-    policy's own measurement of one record: host FFN time against a copy over the link."""
-    import numpy as np
-    stream = torch.cuda.current_stream()
-    T, warm, steps = 1, 8, 32
-    L = len(handles)
-    xs_d = token_stream(T, warm + steps)
-    cnt = routing_profile(args, m, hip, torch, handles, wr_d, b_d, T, 64)
-    chosen, cpu_us, link_us = m.moe_offload_set_cold(handles[0], m.COLD_AUTO, stream)
-    m.moe_offload_set_cold(handles[0], m.COLD_OFF, stream)
-    log("cold policy on one record: host FFN %.1f us, link %.1f us -> %s" % (cpu_us, link_us,
-                                                                         "host" if chosen else "link"))
-    dev = torch.device("cuda", 0)
-    x = torch.empty((L + 1, T, H), dtype=torch.bfloat16, device=dev)
-    xn = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    ids = torch.empty((T, K_TOP), dtype=torch.int32, device=dev)
-    w = torch.empty((T, K_TOP), dtype=torch.float32, device=dev)
-    sid = torch.empty_like(ids)
-    out = {"policy": {"host_ffn_us_per_record": round(cpu_us, 1), "link_us_per_record": round(link_us, 1),
-                            "record_bytes": int(m.moe_offload_query(handles[0])["record_bytes"]),
-                            "host_threads_GBps": round(m.moe_offload_query(handles[0])["record_bytes"] /
-                                                       (cpu_us * 1e-6) / 1e9, 2),
-                            "chosen": "host" if chosen else "link"}}
-    pinned = SLOTS - K_TOP
-    for name in ("link", "host"):
-        for h in handles:
-            m.moe_offload_reset(h, stream)
-        for l, h in enumerate(handles):
-            hot = np.argsort(-cnt[l], kind="stable")[:pinned].astype(np.int32)
-            m.moe_offload_pin(h, torch.from_numpy(hot).to(dev), len(hot), stream)
-            if name == "host":
-                m.moe_offload_set_cold(h, m.COLD_ON, stream)
-        torch.cuda.synchronize()
-        ffn = m.moe_slot_ffn_host_cold if name == "host" else m.moe_slot_ffn
-
-        def step(s_):
-            x[0].copy_(xs_d[s_])
-            for l, h in enumerate(handles):
-                m.moe_rmsnorm(x[l], xn, T, H, m.BF16, stream=stream)
-                m.moe_route_topk(h, xn, wr_d[l], b_d[l], T, ids, w, stream)
-                m.moe_slot_ensure(h, ids, T, sid, stream)
-                m.moe_copy_misses(h, stream)
-                ffn(h, xn, sid, w, T, None, y, x[l], x[l + 1], stream)
-
-        for s_ in range(warm):
-            step(s_)
-        torch.cuda.synchronize()
-        before = {}
-        for h in handles:
-            for kk, v in m.moe_offload_stats(h).items():
-                before[kk] = before.get(kk, 0) + v
-        t0 = time.time()
-        for s_ in range(warm, warm + steps):
-            step(s_)
-        torch.cuda.synchronize()
-        dt = time.time() - t0
-        after = {}
-        for h in handles:
-            for kk, v in m.moe_offload_stats(h).items():
-                after[kk] = after.get(kk, 0) + v
-        assert after["error"] == 0
-        d = {kk: after[kk] - before[kk] for kk in after}
-        out[name] = {"tokens_per_s": round(T * steps / dt, 2), "ms_per_step": round(dt * 1e3 / steps, 3),
-                     "copied_misses_per_token": round((d["misses"] + d["staged_copies"]) / (T * steps), 4),
-                     "host_computed_per_token": round(d["cold_misses"] / (T * steps), 4)}
-        log("host-cold compare %s: %.1f tok/s, copied %.2f, host-computed %.2f per token" %
-            (name, out[name]["tokens_per_s"], out[name]["copied_misses_per_token"],
-             out[name]["host_computed_per_token"]))
-        for h in handles:
-            m.moe_offload_set_cold(h, m.COLD_OFF, stream)
-            m.moe_offload_pin(h, None, 0, stream)
-            m.moe_offload_reset(h, stream)
-        torch.cuda.synchronize()
-    out["pinned_per_layer"] = pinned
     return out
 
 

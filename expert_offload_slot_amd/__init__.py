@@ -61,8 +61,7 @@ class Info(ctypes.Structure):
                 ("ffn_h", ctypes.c_void_p), ("ffn_part", ctypes.c_void_p), ("ffn_groups", ctypes.c_void_p),
                 ("record_bytes", ctypes.c_size_t), ("record_stride", ctypes.c_size_t)] + \
                [(n, ctypes.c_int32) for n in ("E", "S", "H", "F", "k", "dtype", "max_tokens", "device")] + \
-               [("score", ctypes.c_void_p), ("pinned", ctypes.c_void_p), ("act", ctypes.c_void_p),
-                ("valid", ctypes.c_void_p)]
+               [("score", ctypes.c_void_p), ("pinned", ctypes.c_void_p), ("act", ctypes.c_void_p)]
 
 
 class ChainBuffers(ctypes.Structure):

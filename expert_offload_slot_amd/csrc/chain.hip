@@ -21,7 +21,6 @@
 #include <vector>
 
 #include "internal.h"
-#include "pfhelp.h"
 
 struct moe_chain {
   std::vector<moe_offload*> layers;
@@ -71,9 +70,6 @@ hipError_t issue(moe_chain* c, hipStream_t cs) {
   // the previous layer's combine rides in the next router launch (small bf16 / fp8 decode batches)
   const moe_offload* l0 = c->layers[0];
   const bool fuse_cl = fused && l0->dtype != MOE_F32 && c->H <= moe::kFusedCombineMaxH && T <= 8;
-  // lookahead with read-through decode launches: the installs are copied by helper workgroups inside
-  // the chain's own launches (pfhelp.h) instead of on a side stream
-  const bool helpers = pf && fused && c->read_through && moe::ffn_reads_through(l0, T);
   for (int l = 0; l < c->L; ++l) {
     moe_offload* h = c->layers[l];
     const bool look = pf && l + 1 < c->L;
@@ -97,9 +93,8 @@ hipError_t issue(moe_chain* c, hipStream_t cs) {
         cb.x_next = X(c, l);
         cb.xn_next = XN(c, l);
         cb.eps = kRmsEps;
-        const moe::PfHelp own = moe::pf_help_for(h);  // this layer's installs, made by layer l-1
         CHK(moe::launch_combine_logits(h, cb, c->wr[l], c->bias[l], T, cs, hn, look ? c->wr[l + 1] : nullptr,
-                                       look ? c->bias[l + 1] : nullptr, helpers ? &own : nullptr));
+                                       look ? c->bias[l + 1] : nullptr));
       } else {
         CHK(moe::launch_logits(h, XN(c, l), c->wr[l], c->bias[l], T, cs, hn, look ? c->wr[l + 1] : nullptr,
                                look ? c->bias[l + 1] : nullptr));
@@ -121,23 +116,21 @@ hipError_t issue(moe_chain* c, hipStream_t cs) {
         CHK(moe::launch_install(hn, c->pred + R(c, l + 1), T, c->prefetch_n, cs));
       }
     }
-    if (pf && !helpers && l >= 1) CHK(hipStreamWaitEvent(cs, c->ev_pf[l], 0));  // this layer's prefetch copy first
+    if (pf && l >= 1) CHK(hipStreamWaitEvent(cs, c->ev_pf[l], 0));  // this layer's prefetch copy first
     // a decode step's misses are read through by its FFN launches instead of a copy launch
     const bool fill = c->read_through && moe::ffn_reads_through(h, T);
-    if (!fill) CHK(moe::launch_copy(h, h->cache.fill_list, cs));
-    if (look && !helpers) {  // prefetch copy for layer l+1 on a side stream, after layer l's copy launch
+    if (!fill) CHK(moe::launch_copy(h, h->cache.copy_list, cs));
+    if (look) {  // prefetch copy for layer l+1, after layer l's copy launch (read-through: after its control step)
       CHK(hipEventRecord(c->ev_demand[l], cs));
       CHK(hipStreamWaitEvent(c->sf, c->ev_demand[l], 0));
       CHK(moe::launch_copy(hn, hn->cache.pf_list, c->sf));
       CHK(hipEventRecord(c->ev_pf[l + 1], c->sf));
     }
-    moe::PfHelp next;
-    if (look && helpers) next = moe::pf_help_for(hn);  // layer l+1's installs, made by this layer's control step
     CHK(moe::launch_ffn(h, XN(c, l), c->sid + R(c, l), c->w + R(c, l), T, c->shared[l], Y(c, l), X(c, l), X(c, l + 1),
                         l + 1 < c->L ? XN(c, l + 1) : nullptr, kRmsEps, cs, fused, !(fuse_cl && l + 1 < c->L),
-                        fill, nullptr, look && helpers ? &next : nullptr));
+                        fill));
   }
-  if (pf && !helpers && c->L > 1) {  // rejoin the side streams (the predictor stream is used only without fusion)
+  if (pf && c->L > 1) {  // rejoin the side streams (the predictor stream is used only without fusion)
     if (!fused) {
       CHK(hipEventRecord(c->ev_sp_done, c->sp));
       CHK(hipStreamWaitEvent(cs, c->ev_sp_done, 0));

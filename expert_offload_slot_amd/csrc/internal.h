@@ -14,8 +14,6 @@ constexpr int kMaxTopK = 16;
 constexpr int kCopyGrid = 64;       // copy kernel: fixed grid; 48+ workgroups already fill the host link
 constexpr int kCopyThreads = 256;
 constexpr int kCopyUnroll = 4;      // 16-byte loads in flight per thread
-constexpr uint64_t kCopyChunk = (uint64_t)kCopyThreads * kCopyUnroll * 16;  // bytes per copy chunk (16 KiB)
-constexpr int kPfHelpers = 8;       // prefetch copy helpers per chain launch (workgroups of kCopyThreads)
 constexpr int kRouteTokens = 4;     // tokens per router wave
 constexpr int kF32Rows = 64;        // rows per work item on the fp32 path
 
@@ -39,17 +37,6 @@ struct CacheDev {
   uint64_t* counters;   // [C_N]
   int32_t* err;         // [1] sticky MOE_DEV_ERR_* bits
   int32_t* cold;        // [1] 1: ensure loads nothing, misses are computed on the host (index S + E + e)
-  // Copy state.  valid[s] = 1: slot s holds its expert's whole record.  Installed
-  // (prefetched) slots start at 0 and become valid once every chunk of the record
-  // has been copied (pf_done[i] == pf_chunks for prefetch-list entry i), which the
-  // next ensure resolves; a hit on a slot still invalid is refilled by that call.
-  int32_t* valid;       // [S]
-  int32_t* fill_list;   // [2 + 2*max(S,E)] {mode, count, (expert, record)...}: what this call's FFN (read-through)
-                        // or copy kernel moves: the copy list's entries, then the refills
-  uint32_t* pf_claim;   // [1] prefetch chunks claimed by copy helpers
-  uint32_t* pf_done;    // [S] chunks copied per prefetch-list entry
-  uint32_t* run_ctl;    // [4] workgroups finished in this layer's launches: [0] gate/up, [1] down, [2] router
-  int pf_chunks;        // copy chunks per record (kCopyChunk bytes each)
   int E, S;
   int policy;           // victim order: kPolicyLru, kPolicyScored, kPolicyFreq (table.h)
   uint64_t record_bytes;
@@ -76,8 +63,7 @@ struct GroupLayout {
   int words() const { return off_tiles() + max_recs + 1; }
 };
 
-struct Prof;    // prof.h
-struct PfHelp;  // pfhelp.h
+struct Prof;  // prof.h
 
 }  // namespace moe
 
@@ -140,7 +126,7 @@ struct CombineSrc {
 constexpr int kFusedCombineMaxH = 8192;
 hipError_t launch_combine_logits(moe_offload* h, const CombineSrc& cb, const void* wr, const float* bias, int T,
                                  hipStream_t s, moe_offload* hn = nullptr, const void* wrn = nullptr,
-                                 const float* biasn = nullptr, const PfHelp* help = nullptr);
+                                 const float* biasn = nullptr);
 hipError_t launch_route(moe_offload* h, const void* x, const void* wr, const float* bias, int T, int32_t* ids,
                         float* w, hipStream_t s);
 hipError_t launch_ensure(moe_offload* h, const int32_t* ids, int n, int32_t* slot_ids, hipStream_t s);
@@ -166,9 +152,7 @@ struct FfnWork {
 hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int T,
                       const void* shared, void* y, const void* residual, void* x_next, void* xn_next, float eps,
                       hipStream_t s, bool grouped = false, bool combine = true, bool fill = false,
-                      const FfnWork* ws = nullptr, const PfHelp* help = nullptr);
-// the copy helpers' view of layer hn's prefetch queue (stop counter and busy list filled in per launch)
-PfHelp pf_help_for(const moe_offload* hn);
+                      const FfnWork* ws = nullptr);
 
 // File-scope device scratch for callers that cannot allocate (k_ffn.hip).
 constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;

@@ -8,7 +8,6 @@
 //
 // The table is only ever written by one workgroup of one kernel at a time,
 // on the caller's compute stream: no atomics on shared state, no races.
-#include "pfhelp.h"
 #include "prof.h"
 #include "table.h"
 
@@ -74,8 +73,6 @@ __global__ void k_stage_all(CacheDev c, const int32_t* __restrict__ ids, int n, 
   if (i0 == 0) {
     c.copy_list[0] = MOE_MODE_STAGED_ALL;
     c.copy_list[1] = c.E;
-    c.fill_list[0] = MOE_MODE_STAGED_ALL;  // the layer was staged by the host's copy: nothing to read through
-    c.fill_list[1] = 0;
     *c.tick += 1;
     c.counters[C_CALLS] += 1;
     c.counters[C_STAGED_CALLS] += 1;
@@ -96,8 +93,6 @@ __global__ void k_reset(CacheDev c) {
     c.last_use[s] = 0;
     c.score[s] = 0;
     c.pinned[s] = 0;
-    c.valid[s] = 0;
-    c.pf_done[s] = 0;
   }
   for (int i = i0; i < C_N; i += step) c.counters[i] = 0;
   if (i0 == 0) {
@@ -107,9 +102,6 @@ __global__ void k_reset(CacheDev c) {
     c.copy_list[1] = 0;
     c.pf_list[0] = MOE_MODE_SLOTS;
     c.pf_list[1] = 0;
-    c.fill_list[0] = MOE_MODE_SLOTS;
-    c.fill_list[1] = 0;
-    *c.pf_claim = 0;
   }
 }
 
@@ -122,12 +114,10 @@ __global__ void k_set_cold(int32_t* cold, int on) {
 // Fixed grid; the list (mode, count, pairs) is read on the device.  Each
 // workgroup moves 16 KiB chunks: 256 threads x 4 loads of 16 bytes in flight,
 // read from the device-mapped host store over the host link, written to HBM.
-// With `done` (a prefetch list), each copied chunk is counted for its entry, in
-// the chunk units the copy helpers use, so the next ensure sees the record complete.
 __global__ __launch_bounds__(kCopyThreads) void k_copy(const int32_t* __restrict__ list,
                                                       const uint8_t* __restrict__ host, uint8_t* __restrict__ slots,
                                                       uint8_t* __restrict__ staging, uint64_t stride, uint64_t rb16,
-                                                      int S, int E, int32_t* err, uint32_t* done) {
+                                                      int S, int E, int32_t* err) {
   const int mode = list[0];
   const int count = list[1];
   if (mode == MOE_MODE_STAGED_ALL || mode == MOE_MODE_COLD || count <= 0) return;  // cold experts never move
@@ -157,7 +147,6 @@ __global__ __launch_bounds__(kCopyThreads) void k_copy(const int32_t* __restrict
       const uint64_t i = (uint64_t)u * kCopyThreads + threadIdx.x;
       if (i < lim) dst[i] = v[u];
     }
-    if (done && threadIdx.x == 0) atomicAdd(&done[m], 1u);
   }
 }
 
@@ -201,33 +190,12 @@ hipError_t launch_reset(moe_offload* h, hipStream_t s) {
 }
 
 hipError_t launch_copy(moe_offload* h, const int32_t* list, hipStream_t s) {
-  const bool pf = list == h->cache.pf_list;
-  static_assert(kCopyChunk == (uint64_t)kCopyThreads * kCopyUnroll * 16, "copy chunks are the helpers' chunks");
-  launch_k(h, pf ? MOE_K_PF_COPY : MOE_K_COPY, k_copy, dim3(kCopyGrid), dim3(kCopyThreads), 0,
+  launch_k(h, list == h->cache.pf_list ? MOE_K_PF_COPY : MOE_K_COPY, k_copy, dim3(kCopyGrid), dim3(kCopyThreads), 0,
            s, list, h->host_dev, h->slots, h->staging,
            // whole 16-byte units: the record stride is a multiple of 4096, so rounding
            // the record up stays inside its own stride on both sides
-           (uint64_t)h->record_stride, (uint64_t)((h->record_bytes + 15) / 16), h->S, h->E, h->cache.err,
-           pf ? h->cache.pf_done : (uint32_t*)nullptr);
+           (uint64_t)h->record_stride, (uint64_t)((h->record_bytes + 15) / 16), h->S, h->E, h->cache.err);
   return hipGetLastError();
-}
-
-PfHelp pf_help_for(const moe_offload* hn) {
-  PfHelp p;
-  p.list = hn->cache.pf_list;
-  p.claim = hn->cache.pf_claim;
-  p.done = hn->cache.pf_done;
-  p.host = hn->host_dev;
-  p.slots = hn->slots;
-  p.stride = hn->record_stride;
-  p.rb16 = (hn->record_bytes + 15) / 16;
-  p.nc = hn->cache.pf_chunks;
-  p.S = hn->S;
-  p.E = hn->E;
-  p.stop = nullptr;
-  p.stop_at = 0;
-  p.busy = nullptr;
-  return p;
 }
 
 }  // namespace moe

@@ -43,7 +43,6 @@
 #include <mutex>
 
 #include "grouping.h"
-#include "pfhelp.h"
 #include "prof.h"
 #include "rownorm.h"
 
@@ -76,10 +75,6 @@ struct FfnArgs {
   // (null list: every record is read where slot_ids points)
   const int32_t* fill_list;
   const uint8_t* host;
-  // decode chain with lookahead: the first n_help workgroups copy the next layer's installs
-  PfHelp pf;
-  int n_help;
-  uint32_t* own_done;  // the other workgroups count themselves here when done
 };
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return (uint16_t)rn_to_bf16(f); }
@@ -878,13 +873,9 @@ __global__ __launch_bounds__(256) void k_gateup_vec(FfnArgs a) {
   const uint64_t mat = code_bytes<W>((uint64_t)F * H);
   const uint16_t* __restrict__ x = (const uint16_t*)a.x;
   uint16_t* __restrict__ hb = (uint16_t*)a.hbuf;
-  if ((int)blockIdx.x < a.n_help) {  // block-uniform: a prefetch copy helper
-    pf_help(a.pf);
-    return;
-  }
-  const int nwave = (gridDim.x - a.n_help) * 4;
+  const int nwave = gridDim.x * 4;
   const VecHead vh = vec_head(a, FILL);
-  for (int item = (blockIdx.x - a.n_help) * 4 + (threadIdx.x >> 6); item < nrt * RG; item += nwave) {
+  for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < nrt * RG; item += nwave) {
     const int r = item / RG, fg = (item % RG) * 4, f = fg + q;
     const Item it = item_block(a, r);
     if (it.n == 0) continue;
@@ -932,7 +923,6 @@ __global__ __launch_bounds__(256) void k_gateup_vec(FfnArgs a) {
       }
     }
   }
-  if (a.n_help) pf_own_done(a.own_done);
 }
 
 // down: work item = (record, 8 rows of H); quarter q takes rows 8*g + q (stream 0)
@@ -947,13 +937,9 @@ __global__ __launch_bounds__(256) void k_down_vec(FfnArgs a) {
   const uint64_t mat = code_bytes<W>((uint64_t)F * H);
   const uint16_t* __restrict__ hb = (const uint16_t*)a.hbuf;
   float* __restrict__ part = a.part;
-  if ((int)blockIdx.x < a.n_help) {  // block-uniform: a prefetch copy helper
-    pf_help(a.pf);
-    return;
-  }
-  const int nwave = (gridDim.x - a.n_help) * 4;
+  const int nwave = gridDim.x * 4;
   const VecHead vh = vec_head(a, FILL);
-  for (int item = (blockIdx.x - a.n_help) * 4 + (threadIdx.x >> 6); item < nrt * RG; item += nwave) {
+  for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < nrt * RG; item += nwave) {
     const int r = item / RG, hg = (item % RG) * 8, h0 = hg + q;
     const Item it = item_block(a, r);
     if (it.n == 0) continue;
@@ -1000,7 +986,6 @@ __global__ __launch_bounds__(256) void k_down_vec(FfnArgs a) {
       }
     }
   }
-  if (a.n_help) pf_own_done(a.own_done);
 }
 
 // Single-token calls (T = 1): the k choices are distinct records, so work item
@@ -1076,12 +1061,8 @@ __global__ __launch_bounds__(128) void k_gateup_one(FfnArgs a) {
   const int items = (a.k + (a.shared ? 1 : 0)) * RG;
   const uint16_t* __restrict__ x = (const uint16_t*)a.x;
   uint16_t* __restrict__ hb = (uint16_t*)a.hbuf;
-  if ((int)blockIdx.x < a.n_help) {  // block-uniform: a prefetch copy helper
-    pf_help(a.pf);
-    return;
-  }
   const OneHead o = one_head(a, FILL);
-  for (int item = (blockIdx.x - a.n_help) * 2 + (threadIdx.x >> 6); item < items; item += (gridDim.x - a.n_help) * 2) {
+  for (int item = blockIdx.x * 2 + (threadIdx.x >> 6); item < items; item += gridDim.x * 2) {
     const int j = item / RG, f = (item % RG) * 4 + q;
     const uint8_t* rec = one_record(a, j, o);
     if (!rec) continue;  // a cold expert (wavefront-uniform)
@@ -1111,7 +1092,6 @@ __global__ __launch_bounds__(128) void k_gateup_one(FfnArgs a) {
     up = reduce16_all(up);
     if (c == 0) hb[(uint64_t)j * F + f] = f32_to_bf16(silu_mul(g, up));
   }
-  if (a.n_help) pf_own_done(a.own_done);
 }
 
 template <int W, int CH, bool FILL>
@@ -1124,12 +1104,8 @@ __global__ __launch_bounds__(128) void k_down_one(FfnArgs a) {
   const int items = (a.k + (a.shared ? 1 : 0)) * RG;
   const uint16_t* __restrict__ hb = (const uint16_t*)a.hbuf;
   float* __restrict__ part = a.part;
-  if ((int)blockIdx.x < a.n_help) {  // block-uniform: a prefetch copy helper
-    pf_help(a.pf);
-    return;
-  }
   const OneHead o = one_head(a, FILL);
-  for (int item = (blockIdx.x - a.n_help) * 2 + (threadIdx.x >> 6); item < items; item += (gridDim.x - a.n_help) * 2) {
+  for (int item = blockIdx.x * 2 + (threadIdx.x >> 6); item < items; item += gridDim.x * 2) {
     const int j = item / RG, h0 = (item % RG) * 8 + q;
     const uint8_t* rec = one_record(a, j, o);
     if (!rec) continue;  // a cold expert (wavefront-uniform)
@@ -1162,7 +1138,6 @@ __global__ __launch_bounds__(128) void k_down_one(FfnArgs a) {
     s1 = reduce16_all(s1);
     if (c < 2) part[(uint64_t)j * H + h0 + 4 * c] = c ? s1 : s0;
   }
-  if (a.n_help) pf_own_done(a.own_done);
 }
 
 // kernel instantiation by K blocks per pass
@@ -1379,9 +1354,8 @@ FfnWork ffn_work_in(const moe_offload* h, int T, void* base, size_t* bytes) {
 
 hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int T,
                       const void* shared, void* y, const void* residual, void* x_next, void* xn_next, float eps,
-                      hipStream_t s, bool grouped, bool combine, bool fill, const FfnWork* ws, const PfHelp* help) {
+                      hipStream_t s, bool grouped, bool combine, bool fill, const FfnWork* ws) {
   FfnArgs a;
-  memset(&a, 0, sizeof a);
   a.x = x;
   a.slot_ids = slot_ids;
   a.w = w;
@@ -1407,7 +1381,7 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
   a.max_routed = std::min(T * h->k, h->S + h->E);
   a.pair_items = T == 1 && h->dtype != MOE_F32 ? 1 : 0;
   fill = fill && ffn_reads_through(h, T);
-  a.fill_list = fill ? h->cache.fill_list : nullptr;
+  a.fill_list = fill ? h->cache.copy_list : nullptr;
   a.host = h->host_dev;
   // distinct records a call can touch (+ the shared expert)
   const int max_items_r = a.max_routed + (shared ? 1 : 0);
@@ -1450,33 +1424,11 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
     g2 = dim3(std::min(tiles * (h->H / kGemmRowsDn), 2048));
     b1 = b2 = dim3(256);
   }
-  // the next layer's prefetch copy helpers ride in front of the decode launches
-  const bool helped = help && h->dtype != MOE_F32 && T <= kDecodeMaxT;
   {
-    FfnArgs ag = a;
-    if (helped) {
-      ag.pf = *help;
-      ag.n_help = kPfHelpers;
-      ag.own_done = h->cache.run_ctl + 0;
-      ag.pf.stop = ag.own_done;
-      ag.pf.stop_at = g1.x;
-      ag.pf.busy = fill ? h->cache.fill_list : nullptr;
-      g1.x += kPfHelpers;
-    }
-    launch_k(h, MOE_K_GATEUP, gu, g1, b1, 0, s, ag);
+    launch_k(h, MOE_K_GATEUP, gu, g1, b1, 0, s, a);
   }
   {
-    FfnArgs ad = a;
-    if (helped) {
-      ad.pf = *help;
-      ad.n_help = kPfHelpers;
-      ad.own_done = h->cache.run_ctl + 1;
-      ad.pf.stop = ad.own_done;
-      ad.pf.stop_at = g2.x;
-      ad.pf.busy = fill ? h->cache.fill_list : nullptr;
-      g2.x += kPfHelpers;
-    }
-    launch_k(h, MOE_K_DOWN, dn, g2, b2, 0, s, ad);
+    launch_k(h, MOE_K_DOWN, dn, g2, b2, 0, s, a);
   }
   if (combine) {
     if (h->dtype == MOE_F32)

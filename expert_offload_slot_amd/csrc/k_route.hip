@@ -17,11 +17,9 @@
 //             then the softmax over the k chosen logits (topk.h; the fused
 //             decode control kernel runs the same code).
 #include <math.h>
-#include <string.h>
 
 #include <algorithm>
 
-#include "pfhelp.h"
 #include "prof.h"
 #include "rownorm.h"
 #include "topk.h"
@@ -101,18 +99,10 @@ __global__ __launch_bounds__(256) void k_logits(const A* __restrict__ x, RouterJ
 constexpr int kRowChunks = kFusedCombineMaxH / (8 * kRowThreads);  // combine chunks per thread
 constexpr int kRouterChunks = kFusedCombineMaxH / (8 * 64);         // router chunks per lane
 
-// With the lookahead, one more z-plane of workgroups carries the prefetch copy
-// helpers for this layer's installs (pfhelp.h); every router wavefront counts
-// itself in own_done when it is finished, so the helpers know when to stop.
 __global__ __launch_bounds__(kRowThreads) void k_combine_logits(CombineSrc cb, RouterJob<uint16_t> j0,
-                                                                RouterJob<uint16_t> j1, int H, PfHelp pf,
-                                                                int help_z, uint32_t* own_done) {
+                                                                RouterJob<uint16_t> j1, int H) {
   __shared__ float s_wave[4];
   __shared__ __align__(16) uint16_t xs[kFusedCombineMaxH];
-  if ((int)blockIdx.z == help_z) {  // block-uniform: the helper plane
-    if (blockIdx.y * gridDim.x + blockIdx.x < (unsigned)kPfHelpers) pf_help(pf);
-    return;
-  }
   const RouterJob<uint16_t> j = blockIdx.z == 0 ? j0 : j1;
   const int t = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int e = blockIdx.x * 4 + (tid >> 6);
@@ -161,26 +151,24 @@ __global__ __launch_bounds__(kRowThreads) void k_combine_logits(CombineSrc cb, R
     }
   }
   __syncthreads();
-  if (ev) {  // wavefront-uniform
-    float acc = 0.f;
+  if (!ev) return;
+  float acc = 0.f;
 #pragma unroll
-    for (int i = 0; i < kRouterChunks; ++i) {
-      const int c = lane + 64 * i;
-      if (c * 8 < H) {
-        float xv8[8], wv8[8];
-        load8(xs + c * 8, xv8);
-        const uint4 a4 = wr[i];
-        wv8[0] = bf16_lo(a4.x); wv8[1] = bf16_hi(a4.x); wv8[2] = bf16_lo(a4.y); wv8[3] = bf16_hi(a4.y);
-        wv8[4] = bf16_lo(a4.z); wv8[5] = bf16_hi(a4.z); wv8[6] = bf16_lo(a4.w); wv8[7] = bf16_hi(a4.w);
+  for (int i = 0; i < kRouterChunks; ++i) {
+    const int c = lane + 64 * i;
+    if (c * 8 < H) {
+      float xv8[8], wv8[8];
+      load8(xs + c * 8, xv8);
+      const uint4 a4 = wr[i];
+      wv8[0] = bf16_lo(a4.x); wv8[1] = bf16_hi(a4.x); wv8[2] = bf16_lo(a4.y); wv8[3] = bf16_hi(a4.y);
+      wv8[4] = bf16_lo(a4.z); wv8[5] = bf16_hi(a4.z); wv8[6] = bf16_lo(a4.w); wv8[7] = bf16_hi(a4.w);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc = __builtin_fmaf(xv8[q], wv8[q], acc);
-      }
+      for (int q = 0; q < 8; ++q) acc = __builtin_fmaf(xv8[q], wv8[q], acc);
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) acc = acc + __shfl_xor(acc, o);
-    if (lane == 0) j.logits[(size_t)t * j.E + e] = acc + be;
   }
-  if (own_done && lane == 0) atomicAdd(own_done, 1u);  // this wavefront is finished
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) acc = acc + __shfl_xor(acc, o);
+  if (lane == 0) j.logits[(size_t)t * j.E + e] = acc + be;
 }
 
 // Top-k (topk.h): one wavefront per token, 4 tokens per workgroup.
@@ -225,28 +213,13 @@ hipError_t launch_logits(moe_offload* h, const void* x, const void* wr, const fl
 }
 
 hipError_t launch_combine_logits(moe_offload* h, const CombineSrc& cb, const void* wr, const float* bias, int T,
-                                 hipStream_t s, moe_offload* hn, const void* wrn, const float* biasn,
-                                 const PfHelp* help) {
+                                 hipStream_t s, moe_offload* hn, const void* wrn, const float* biasn) {
   if (h->dtype == MOE_F32 || h->H > kFusedCombineMaxH || (hn && hn->dtype == MOE_F32)) return hipErrorInvalidValue;
   RouterJob<uint16_t> j0{(const uint16_t*)wr, bias, h->logits, h->E};
   RouterJob<uint16_t> j1 = hn ? RouterJob<uint16_t>{(const uint16_t*)wrn, biasn, hn->logits, hn->E} : j0;
   const int E = hn ? std::max(h->E, hn->E) : h->E;
-  const int planes = hn ? 2 : 1;
-  dim3 grid((E + 3) / 4, T, planes);
-  PfHelp pf;
-  memset(&pf, 0, sizeof pf);
-  int help_z = -1;
-  uint32_t* own_done = nullptr;
-  if (help) {  // this layer's own installs: the helper plane after the router planes
-    pf = *help;
-    own_done = h->cache.run_ctl + 2;
-    pf.stop = own_done;
-    pf.stop_at = grid.x * grid.y * planes * (kRowThreads / 64);
-    pf.busy = nullptr;
-    help_z = planes;
-    grid.z = planes + 1;
-  }
-  launch_k(h, MOE_K_LOGITS, k_combine_logits, grid, dim3(kRowThreads), 0, s, cb, j0, j1, h->H, pf, help_z, own_done);
+  launch_k(h, MOE_K_LOGITS, k_combine_logits, dim3((E + 3) / 4, T, hn ? 2 : 1), dim3(kRowThreads), 0, s, cb, j0, j1,
+           h->H);
   return hipGetLastError();
 }
 

@@ -48,11 +48,6 @@ __global__ __launch_bounds__(kBlock) void k_decide(CacheDev c, const float* __re
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n = T * k;
   const TableRegs tr = fetch_table(c);  // in flight while the top-k reads the logits
-  if (threadIdx.x == 0) {  // the finish counters of the launches that follow (prefetch copy helpers)
-    c.run_ctl[0] = 0u;     // this layer's gate/up
-    c.run_ctl[1] = 0u;     // this layer's down
-    if (max_n > 0) nc.run_ctl[2] = 0u;  // the next layer's router launch
-  }
   for (int tok = wv; tok < T; tok += kWaves) {
     int id;
     float wt;

@@ -109,7 +109,7 @@ int check_desc(const moe_offload_desc* d) {
 // sets h->gl.  Depends on E, S, H, F, k, dtype and max_tokens only.
 struct StateLayout {
   size_t o_slot_of, o_expert_of, o_last, o_score, o_pinned, o_act, o_tick, o_list, o_pf, o_cnt, o_err, o_logits,
-      o_grp, o_h, o_part, o_scr, o_cold, o_valid, o_fill, o_pfc, o_pfd, o_run, total;
+      o_grp, o_h, o_part, o_scr, o_cold, total;
 };
 
 StateLayout state_layout(moe_offload* h) {
@@ -142,11 +142,6 @@ StateLayout state_layout(moe_offload* h) {
   l.o_part = take(4 * (size_t)rows * h->H);
   l.o_scr = take(64);
   l.o_cold = take(4);
-  l.o_valid = take(4 * (size_t)h->S);
-  l.o_fill = take(4 * (2 + 2 * (size_t)maxSE));
-  l.o_pfc = take(4);
-  l.o_pfd = take(4 * (size_t)h->S);
-  l.o_run = take(16);
   l.total = off;
   return l;
 }
@@ -253,12 +248,6 @@ int moe_offload_create(const moe_offload_desc* d, moe_offload** out) {
   h->cache.counters = (uint64_t*)(b + o_cnt);
   h->cache.err = (int32_t*)(b + o_err);
   h->cache.cold = (int32_t*)(b + sl.o_cold);
-  h->cache.valid = (int32_t*)(b + sl.o_valid);
-  h->cache.fill_list = (int32_t*)(b + sl.o_fill);
-  h->cache.pf_claim = (uint32_t*)(b + sl.o_pfc);
-  h->cache.pf_done = (uint32_t*)(b + sl.o_pfd);
-  h->cache.run_ctl = (uint32_t*)(b + sl.o_run);
-  h->cache.pf_chunks = (int)((h->record_bytes + moe::kCopyChunk - 1) / moe::kCopyChunk);
   h->cache.E = h->E;
   h->cache.S = h->S;
   h->cache.record_bytes = h->record_bytes;
@@ -364,7 +353,7 @@ int moe_slot_ensure(moe_offload* h, const int32_t* ids, int32_t T, int32_t* slot
 int moe_copy_misses(moe_offload* h, void* stream) {
   if (int rc = check_handle(h)) return rc;
   DeviceGuard g(h->device);
-  HIP_TRY(moe::launch_copy(h, h->cache.fill_list, (hipStream_t)stream));
+  HIP_TRY(moe::launch_copy(h, h->cache.copy_list, (hipStream_t)stream));
   return MOE_OK;
 }
 
@@ -461,7 +450,7 @@ int moe_prefill_stage(moe_offload* h, const int32_t* ids, int32_t T, int32_t* sl
     if (staged_out) *staged_out = 1;
   } else {
     HIP_TRY(moe::launch_ensure(h, ids, n, slot_ids, s));
-    HIP_TRY(moe::launch_copy(h, h->cache.fill_list, s));
+    HIP_TRY(moe::launch_copy(h, h->cache.copy_list, s));
     if (staged_out) *staged_out = 0;
   }
   return MOE_OK;
@@ -656,7 +645,6 @@ int moe_offload_query(const moe_offload* h, moe_info* out) {
   out->score = h->cache.score;
   out->pinned = h->cache.pinned;
   out->act = h->cache.act;
-  out->valid = h->cache.valid;
   out->copy_list = h->cache.copy_list;
   out->prefetch_list = h->cache.pf_list;
   out->slots = h->slots;

@@ -48,11 +48,6 @@ struct SharedTable {
   int cand[kMaxExperts];   // ensure: best top-k position; install: candidate by rank
   int vic[kMaxExperts];    // victim slot by rank
   int wave[4 * kWaves];
-  int valid[kMaxExperts];  // 1: the slot holds its expert's whole record
-  int pfe[kMaxExperts];    // the layer's prefetch list as loaded: expert, slot, chunks copied
-  int pfs[kMaxExperts];
-  uint32_t pfd[kMaxExperts];
-  int pfn;                 // its entry count
   int bad;
   int cold;                // the layer's cold-mode flag as loaded
   uint64_t tick;           // the table's call counter as loaded
@@ -61,8 +56,8 @@ struct SharedTable {
 
 // The table as one thread holds it between fetch_table and put_table.
 struct TableRegs {
-  int s = -1, e = -1, pin = 0, val = 0, pfe = -1, pfs = -1;
-  uint32_t sc = 0u, ac = 0u, pfd = 0u;
+  int s = -1, e = -1, pin = 0;
+  uint32_t sc = 0u, ac = 0u;
   uint64_t lu = 0ull, tc = 0ull;
 };
 
@@ -81,15 +76,10 @@ __device__ __forceinline__ TableRegs fetch_table(const CacheDev& c) {
     r.lu = c.last_use[tid];
     r.sc = c.score[tid];
     r.pin = c.pinned[tid];
-    r.val = c.valid[tid];
-    r.pfe = c.pf_list[2 + 2 * tid];
-    r.pfs = c.pf_list[3 + 2 * tid];
-    r.pfd = c.pf_done[tid];
   }
   if (u == 0) r.tc = *c.tick;
   if (u >= 1 && u <= C_N) r.tc = c.counters[u - 1];
   if (u == C_N + 1) r.tc = (uint64_t)(uint32_t)*c.cold;
-  if (u == C_N + 2) r.tc = (uint64_t)(uint32_t)c.pf_list[1];
   return r;
 }
 
@@ -117,27 +107,10 @@ __device__ __forceinline__ void put_table(const CacheDev& c, const TableRegs& r,
     t.last_use[tid] = r.lu;
     t.score[tid] = r.sc;
     t.pinned[tid] = r.pin;
-    t.valid[tid] = r.val;
-    t.pfe[tid] = r.pfe;
-    t.pfs[tid] = r.pfs;
-    t.pfd[tid] = r.pfd;
   }
   if (u == 0) t.tick = r.tc;
   if (u >= 1 && u <= C_N) t.cnt[u - 1] = r.tc;
   if (u == C_N + 1) t.cold = r.tc != 0;
-  if (u == C_N + 2) t.pfn = (int)(uint32_t)r.tc;
-}
-
-// The layer's last prefetch installs whose every chunk has been copied (by the
-// copy helpers or the prefetch copy kernel) since: their slots become valid if
-// they still hold the installed expert.  Idempotent.  Needs the table in `t`
-// and a barrier after it.
-__device__ __forceinline__ void resolve_installs(const CacheDev& c, SharedTable& t) {
-  const int tid = threadIdx.x;
-  if (tid < t.pfn && tid < c.S) {
-    const int e = t.pfe[tid], s = t.pfs[tid];
-    if ((unsigned)s < (unsigned)c.S && t.expert_of[s] == e && t.pfd[tid] >= (uint32_t)c.pf_chunks) t.valid[s] = 1;
-  }
 }
 
 // Loads the table into LDS (fetch_table, then put_table).
@@ -154,7 +127,6 @@ __device__ __forceinline__ void store_table(const CacheDev& c, const SharedTable
     c.last_use[tid] = t.last_use[tid];
     c.score[tid] = t.score[tid];
     c.pinned[tid] = t.pinned[tid];
-    c.valid[tid] = t.valid[tid];
   }
 }
 
@@ -217,14 +189,10 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
       atomicOr(c.err, MOE_DEV_ERR_BAD_ID);
       c.copy_list[0] = MOE_MODE_SLOTS;
       c.copy_list[1] = 0;
-      c.fill_list[0] = MOE_MODE_SLOTS;
-      c.fill_list[1] = 0;
     }
     return;  // block-uniform
   }
   if (audit) audit_table(c, t, false);
-  resolve_installs(c, t);
-  __syncthreads();
   const uint64_t tick = t.tick + 1;
   const bool inD = tid < E && t.flag[tid];
   const int sl = tid < E ? t.slot_of[tid] : -1;
@@ -233,11 +201,6 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
   int rk[4], tot[4];
   block_rank4(f, t.wave, rk, tot);
   const int mrank = rk[1], nm = tot[1], nh = tot[2], npf = tot[3];
-  // a hit on a slot whose installed record is not yet complete: this call refills it
-  const bool refill = inD && sl >= 0 && !t.valid[sl];
-  int nrf;
-  const int rrank = block_rank(refill, t.wave, &nrf);
-  if (refill) t.valid[sl] = 1;
 
   if (t.cold) {  // host-computed cold experts: nothing loads, misses are read at S + E + e
     if (inD && sl >= 0) {
@@ -249,10 +212,6 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
     if (miss) {
       c.copy_list[2 + 2 * mrank] = tid;
       c.copy_list[3 + 2 * mrank] = S + E + tid;
-    }
-    if (refill) {  // nothing else moves in cold mode
-      c.fill_list[2 + 2 * rrank] = tid;
-      c.fill_list[3 + 2 * rrank] = sl;
     }
     __syncthreads();
     for (int i = tid; i < n; i += kBlock) {
@@ -267,8 +226,6 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
     if (tid == 0) {
       c.copy_list[0] = MOE_MODE_COLD;
       c.copy_list[1] = nm;
-      c.fill_list[0] = MOE_MODE_SLOTS;
-      c.fill_list[1] = nrf;
       *c.tick = tick;
       c.counters[C_CALLS] = t.cnt[C_CALLS] + 1;
       c.counters[C_HITS] = t.cnt[C_HITS] + (uint64_t)nh;
@@ -334,18 +291,11 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
         if (old >= 0) t.slot_of[old] = -1;
         t.expert_of[v] = tid;
         t.slot_of[tid] = v;
-        t.valid[v] = 1;  // this call's copy or read-through fills it
       }
       c.copy_list[2 + 2 * mrank] = tid;
       c.copy_list[3 + 2 * mrank] = v;
-      c.fill_list[2 + 2 * mrank] = tid;
-      c.fill_list[3 + 2 * mrank] = v;
     }
     __syncthreads();
-  }
-  if (refill) {  // after the misses in the fill list
-    c.fill_list[2 + 2 * (nm + rrank)] = tid;
-    c.fill_list[3 + 2 * (nm + rrank)] = sl;
   }
   if (inD && t.slot_of[tid] >= 0) {  // used now; a slot just loaded starts from 0
     const int s = t.slot_of[tid];
@@ -367,8 +317,6 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
   if (tid == 0) {
     c.copy_list[0] = over ? MOE_MODE_STAGED : MOE_MODE_SLOTS;
     c.copy_list[1] = nm;
-    c.fill_list[0] = over ? MOE_MODE_STAGED : MOE_MODE_SLOTS;
-    c.fill_list[1] = nm + nrf;
     *c.tick = tick;
     c.counters[C_CALLS] = t.cnt[C_CALLS] + 1;
     c.counters[C_HITS] = t.cnt[C_HITS] + (uint64_t)nh;
@@ -420,8 +368,6 @@ __device__ __forceinline__ void install_body(const CacheDev& c, SharedTable& t, 
     }
     return;  // block-uniform
   }
-  resolve_installs(c, t);  // the earlier installs that completed stay valid when their list is replaced
-  __syncthreads();
   // candidate key, ascending = install order (count < 2^20, position < 16, id < 1024)
   const bool cand = tid < E && t.flag[tid] > 0 && t.slot_of[tid] < 0;
   if (tid < E)
@@ -463,10 +409,8 @@ __device__ __forceinline__ void install_body(const CacheDev& c, SharedTable& t, 
     t.slot_of[e] = v;
     t.last_use[v] = 0;
     t.score[v] = 0;
-    t.valid[v] = 0;  // complete once every chunk has been copied
     c.pf_list[2 + 2 * tid] = e;
     c.pf_list[3 + 2 * tid] = v;
-    c.pf_done[tid] = 0;
   }
   __syncthreads();
   store_table(c, t);
@@ -474,7 +418,6 @@ __device__ __forceinline__ void install_body(const CacheDev& c, SharedTable& t, 
   if (tid == 0) {
     c.pf_list[0] = MOE_MODE_SLOTS;
     c.pf_list[1] = m;
-    *c.pf_claim = 0;
     c.counters[C_PF_INSTALLS] = t.cnt[C_PF_INSTALLS] + (uint64_t)m;
     c.counters[C_BYTES] = t.cnt[C_BYTES] + (uint64_t)m * c.record_bytes;
   }
@@ -540,7 +483,6 @@ __device__ __forceinline__ void pin_body(const CacheDev& c, SharedTable& t, cons
     t.last_use[v] = t.tick;
     t.score[v] = 0;
     t.pinned[v] = 1;
-    t.valid[v] = 1;  // the pin's copy follows on the same stream
     c.copy_list[2 + 2 * mrank] = tid;
     c.copy_list[3 + 2 * mrank] = v;
   }

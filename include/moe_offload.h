@@ -179,8 +179,6 @@ typedef struct {
   int32_t* pinned;        /* [S]  1: the slot's expert is pinned (moe_offload_pin), never a victim */
   uint32_t* act;          /* [E]  activation count per expert (ensure calls routing to it; kept under every
                              policy, used by MOE_FLAG_FREQ) */
-  int32_t* valid;         /* [S]  1: the slot holds its expert's whole record; 0: free, or installed by the
-                             lookahead with its copy not yet complete (the next call that uses it refills it) */
 } moe_info;
 
 /* copy-list modes (copy_list[0]); MOE_MODE_COLD: the listed misses are computed on the host

@@ -154,17 +154,10 @@ def check_counters(mo, caches):
 
 
 def check_slot_bytes(mo, layers):
-    """Occupied slots hold their expert's host record; a lookahead install whose copy has not finished
-    (valid 0) is still unused since its install (last_use 0)."""
     for l in layers:
         eo = d2h(mo.info[l]["expert_of"], 4 * mo.S, np.int32)
-        valid = d2h(mo.info[l]["valid"], 4 * mo.S, np.int32)
-        lu = d2h(mo.info[l]["last_use"], 8 * mo.S, np.uint64)
         for s in range(mo.S):
             if eo[s] >= 0:
-                if not valid[s]:
-                    assert lu[s] == 0, (l, s, eo[s])
-                    continue
                 got = d2h(mo.info[l]["slots"] + s * mo.stride, mo.rb)
                 assert np.array_equal(got, mo.hosts[l][eo[s], :mo.rb]), (l, s, eo[s])
 
@@ -248,7 +241,6 @@ def test_qwen3_lookahead_prefetch_full_size(qwen3):
             st = [m.moe_offload_stats(h) for h in mo.handles]
             log("prefetch: installs %d, prefetch hits %d" % (sum(x["prefetch_installs"] for x in st),
                                                             sum(x["prefetch_hits"] for x in st)))
-        check_slot_bytes(mo, (1, 23, 47))
     for a, b in zip(outs[4], outs[0]):
         assert np.array_equal(a, b)
     log("demand misses over %d steps: %d without prefetch, %d with" % (steps, misses[0], misses[4]))
