@@ -103,6 +103,8 @@ def main():
     ap.add_argument("--quick", action="store_true",
                     help="only the batch-1 window, its steady state, the eager profile and the host link")
     ap.add_argument("--cpu-rates", action="store_true", help="also the CPU oracle's own rates on all threads and one")
+    ap.add_argument("--prefetch-only", action="store_true",
+                    help="only the lookahead-prefetch comparison on the 48-layer workload (its own JSON line)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--mxfp4-only", action="store_true",
                     help="only the same decode chain with MXFP4 expert records (prints its own JSON line)")
@@ -253,6 +255,14 @@ def main():
             (tag, T, steps, ms, T * steps * 1e3 / ms, (delta["misses"] + delta["staged_copies"]) / (T * steps),
              delta["misses"] / (T * steps), delta["staged_calls"], delta["calls"]))
         return T * steps * 1e3 / ms, ms / steps, delta, c, bufs, xs_d
+
+    if args.prefetch_only:
+        print(json.dumps({"workload": "qwen3-30b-a3b-shaped offloaded MoE decode, 48 layers, batch 1: router-"
+                                      "lookahead prefetch (4 installs per layer) against none",
+                          "prefetch": prefetch_compare(args, m, hip, handles, run_decode, token_stream)}), flush=True)
+        for h in reversed(handles):
+            m.moe_offload_destroy(h)
+        return
 
     # ---------------- the timed window: --warmup untimed replays from an empty cache, then --steps timed
     # replays (the headline value; cold start included when the window is short)
@@ -720,6 +730,11 @@ def deepseek_layer(args, m, torch):
     return out
 
 
+def torch_stream():
+    import torch
+    return torch.cuda.current_stream()
+
+
 def prefetch_compare(args, m, hip, handles, run_decode, token_stream):
     """Router-lookahead prefetch (up to 4 experts per layer) against none, each from an empty cache on the
     same token stream; the last step's output stream must be bitwise identical."""
@@ -734,10 +749,25 @@ def prefetch_compare(args, m, hip, handles, run_decode, token_stream):
         xl = np.empty((T, H), dtype=np.uint16)  # the last layer's output stream x[L] of the last step
         assert hip.hipMemcpy(xl.ctypes.data, bufs["x"] + len(handles) * T * H * 2, xl.nbytes, 2) == 0
         last[n] = xl
+        # per-kernel event times of a few eager steps of the same chain
+        stream = torch_stream()
+        for h in handles:
+            m.moe_offload_profile(h, 1)
+        for s_ in range(warm + steps, warm + steps + 8):
+            assert hip.hipMemcpyAsync(bufs["x"], xs_d[s_].data_ptr(), T * H * 2, 3, stream.cuda_stream) == 0
+            m.moe_chain_run_eager(c, stream)
+        kt = {}
+        for h in handles:
+            for kind, (ms_, n_) in m.moe_offload_kernel_times(h).items():
+                a_, b2 = kt.get(kind, (0.0, 0))
+                kt[kind] = (a_ + ms_, b2 + n_)
+            m.moe_offload_profile(h, 0)
+        kernels = {kind: round(v * 1e3 / k_, 3) for kind, (v, k_) in kt.items() if k_}
         out["prefetch_%d" % n] = {"tokens_per_s": round(ts, 2), "ms_per_step": round(msps, 3),
                                   "demand_misses_per_token": round(d["misses"] / (T * steps), 4),
                                   "prefetch_installs_per_token": round(d["prefetch_installs"] / (T * steps), 4),
-                                  "prefetch_hits_per_token": round(d["prefetch_hits"] / (T * steps), 4)}
+                                  "prefetch_hits_per_token": round(d["prefetch_hits"] / (T * steps), 4),
+                                  "eager_kernels_us": kernels}
         m.moe_chain_destroy(c)
     out["outputs_identical"] = bool(np.array_equal(last[0], last[4]))
     return out
