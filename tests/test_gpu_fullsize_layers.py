@@ -89,11 +89,11 @@ def test_deepseek_shape_fp8_decode_and_prefill():
         host = fill_layer(gl, seed, E, H, F, wdt)
         cache = oracle.Cache(E, S)
         worst = 0.0
-        for s in range(4):
+        for s in range(16):
             log("deepseek decode step %d (T=16)" % s)
             x = np.ascontiguousarray(synth.tokens(seed, 30 + s, 16, H, 1, 0.0, BF16)[0])
             gl.step(to_dev(x), 16)
-            _, err = check_call(gl, cache, x, 16, wr, b, wdt, H, F, host, (0, 15), shared)
+            _, err = check_call(gl, cache, x, 16, wr, b, wdt, H, F, host, (s % 16, 15 - s % 16), shared)
             worst = max(worst, err)
         log("deepseek prefill T=2048")
         T = 2048
