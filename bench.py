@@ -647,7 +647,7 @@ def mixtral_layer(args, m, torch):
         h = m.moe_offload_create(E, S, H, F, k, m.BF16, 64, 0, 0)
         p, stride, rb = m.moe_offload_host_records(h)
         synth.fill_records(seed, 0, 0, E, H, F, synth.BF16, p, stride)
-        for T in (1, 8, 64):
+        for T in (1, 8, 64, 65):
             xs = synth.tokens(seed, 50 + T, T, H, 24, 0.9, synth.BF16)
             xs_d = torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16).to(dev)
             r = layer_steps(m, torch, h, wr_d, b_d, None, xs_d, T, 16, 8)
@@ -655,32 +655,26 @@ def mixtral_layer(args, m, torch):
             log("mixtral S=%d T=%d: %.1f tok/s, %.3f misses/call, copy %s GB/s" %
                 (S, T, r["tokens_per_s"], r["misses_per_call"], r["copy_GBps"]))
         m.moe_offload_destroy(h)
+    # 64 tokens (16 per expert) take the pair-dot decode kernels, 65 the grouped MFMA GEMM: FFN kernel time per pair
+    out["mfma_vs_pairdot_16_tokens_per_expert"] = {
+        "S%d" % S: {"pairdot_T64_us_per_pair": round(sum(out["S%d_T64" % S]["kernels_us"].get(kk, 0) for kk in
+                                                             ("group", "gateup", "down")) / (64 * k), 4),
+                    "mfma_T65_us_per_pair": round(sum(out["S%d_T65" % S]["kernels_us"].get(kk, 0) for kk in
+                                                          ("group", "gateup", "down")) / (65 * k), 4)}
+        for S in (2, 4, 6)}
     return out
 
 
-def deepseek_layer(args, m, torch):
-    """DeepSeek-V3-shaped layer (fp8 e4m3 + 128x128 scales, 256 experts + shared, top-8, hidden 7168, ffn 2048,
-    26 slots): decode at batch 16, and a 2048-token prefill that stages the whole layer."""
+def prefill_ffn(m, torch, h, wr_d, b_d, sh_d, x, mfma_dtype):
+    """Route a prefill call, stage the layer (host-synchronising), then time the FFN (5 repetitions):
+    TFLOP/s and the fraction of its attainable roofline (the slower of streaming the distinct records once
+    at 8 TB/s and the dense bf16 MFMA rate)."""
     import numpy as np
-    import synth
-    E, k, H, F, S, seed = 256, 8, 7168, 2048, 26, args.seed + 9
+    info = m.moe_offload_query(h)
+    E, k, H, F, rb = info["E"], info["k"], info["H"], info["F"], info["record_bytes"]
+    T = x.shape[0]
     dev = torch.device("cuda", 0)
     st = torch.cuda.current_stream()
-    h = m.moe_offload_create(E, S, H, F, k, m.FP8, 2048, 0, 0)
-    p, stride, rb = m.moe_offload_host_records(h)
-    synth.fill_records(seed, 0, 0, E, H, F, synth.FP8, p, stride)
-    wr, b = synth.router(seed, 0, E, H, synth.BF16, zipf_s=1.2)
-    wr_d = torch.from_numpy(wr.view(np.int16)).view(torch.bfloat16).to(dev)
-    b_d = torch.from_numpy(b).to(dev)
-    sh_d = torch.from_numpy(synth.records(seed, 0, 1, H, F, synth.FP8, shared=True)[0]).to(dev)
-    out = {}
-    xs = synth.tokens(seed, 60, 16, H, 24, 0.0, synth.BF16)
-    xs_d = torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16).to(dev)
-    out["decode_T16"] = layer_steps(m, torch, h, wr_d, b_d, sh_d, xs_d, 16, 8, 4)
-    log("deepseek decode T=16: %.1f tok/s, %d/%d calls staged" % (out["decode_T16"]["tokens_per_s"],
-                                                                  out["decode_T16"]["staged_calls"], 8))
-    T = 2048
-    x = synth.tokens(seed, 70, T, H, 1, 0.0, synth.BF16)[0]
     xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
     ids = torch.empty((T, k), dtype=torch.int32, device=dev)
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
@@ -711,21 +705,56 @@ def deepseek_layer(args, m, torch):
     wbytes = (int((cnt > 0).sum()) + 1) * rb
     gu_us = kt["gateup"][0] * 1e3 / kt["gateup"][1]
     dn_us = kt["down"][0] * 1e3 / kt["down"][1]
-    out["prefill_T2048"] = {
-        "staged": staged, "stage_ms": round(stage_ms, 2), "stage_GBps": round(E * rb / (stage_ms * 1e-3) / 1e9, 2),
-        "ffn_ms": round(ffn_ms, 3), "ffn_TFLOPs": round((flop_gu + flop_dn) / (ffn_ms * 1e-3) / 1e12, 1),
-        "gateup_us": round(gu_us, 1), "gateup_TFLOPs": round(flop_gu / (gu_us * 1e-6) / 1e12, 1),
-        "down_us": round(dn_us, 1), "down_TFLOPs": round(flop_dn / (dn_us * 1e-6) / 1e12, 1),
-        "mfma_peak_TFLOPs": 2500.0, "mfma_dtype": "bf16 (fp8 codes widened exactly)",
-        "frac_of_mfma_peak": round((flop_gu + flop_dn) / (ffn_ms * 1e-3) / 1e12 / 2500.0, 4),
-        "hbm_bound_ms": round(wbytes / 8e12 * 1e3, 3),
-        # attainable roofline: the slower of streaming the distinct records once and the dense bf16 MFMA rate
-        "attainable_bound_ms": round(max(wbytes / 8e12, (flop_gu + flop_dn) / 2.5e15) * 1e3, 3),
-        "frac_of_attainable": round(max(wbytes / 8e12, (flop_gu + flop_dn) / 2.5e15) * 1e3 / ffn_ms, 4),
-        "tokens_per_expert_max": int(cnt.max()),
-        "experts_used": int((cnt > 0).sum())}
-    log("deepseek prefill T=2048: stage %.1f ms (%.1f GB/s), ffn %.2f ms = %.1f TFLOP/s" %
-        (stage_ms, E * rb / (stage_ms * 1e-3) / 1e9, ffn_ms, (flop_gu + flop_dn) / (ffn_ms * 1e-3) / 1e12))
+    bound_ms = max(wbytes / 8e12, (flop_gu + flop_dn) / 2.5e15) * 1e3
+    r = {"staged": staged, "stage_ms": round(stage_ms, 2), "stage_GBps": round(E * rb / (stage_ms * 1e-3) / 1e9, 2),
+         "record_bytes": rb, "ffn_ms": round(ffn_ms, 3),
+         "ffn_TFLOPs": round((flop_gu + flop_dn) / (ffn_ms * 1e-3) / 1e12, 1),
+         "gateup_us": round(gu_us, 1), "gateup_TFLOPs": round(flop_gu / (gu_us * 1e-6) / 1e12, 1),
+         "down_us": round(dn_us, 1), "down_TFLOPs": round(flop_dn / (dn_us * 1e-6) / 1e12, 1),
+         "mfma_peak_TFLOPs": 2500.0, "mfma_dtype": mfma_dtype,
+         "frac_of_mfma_peak": round((flop_gu + flop_dn) / (ffn_ms * 1e-3) / 1e12 / 2500.0, 4),
+         "hbm_bound_ms": round(wbytes / 8e12 * 1e3, 3), "attainable_bound_ms": round(bound_ms, 3),
+         "frac_of_attainable": round(bound_ms / ffn_ms, 4),
+         "tokens_per_expert_max": int(cnt.max()), "experts_used": int((cnt > 0).sum())}
+    log("prefill T=%d (%s records of %.1f MB): stage %.1f ms (%.1f GB/s), ffn %.2f ms = %.1f TFLOP/s, %.1f %% of "
+        "attainable" % (T, "fp8" if rb > 30e6 else "mxfp4", rb / 1e6, stage_ms, r["stage_GBps"], ffn_ms,
+                        r["ffn_TFLOPs"], 100 * r["frac_of_attainable"]))
+    return r
+
+
+def deepseek_layer(args, m, torch):
+    """DeepSeek-V3-shaped layer (fp8 e4m3 + 128x128 scales, 256 experts + shared, top-8, hidden 7168, ffn 2048,
+    26 slots): decode at batch 16, and a 2048-token prefill that stages the whole layer; the same prefill with
+    MXFP4 records."""
+    import numpy as np
+    import synth
+    E, k, H, F, S, seed = 256, 8, 7168, 2048, 26, args.seed + 9
+    dev = torch.device("cuda", 0)
+    st = torch.cuda.current_stream()
+    h = m.moe_offload_create(E, S, H, F, k, m.FP8, 2048, 0, 0)
+    p, stride, rb = m.moe_offload_host_records(h)
+    synth.fill_records(seed, 0, 0, E, H, F, synth.FP8, p, stride)
+    wr, b = synth.router(seed, 0, E, H, synth.BF16, zipf_s=1.2)
+    wr_d = torch.from_numpy(wr.view(np.int16)).view(torch.bfloat16).to(dev)
+    b_d = torch.from_numpy(b).to(dev)
+    sh_d = torch.from_numpy(synth.records(seed, 0, 1, H, F, synth.FP8, shared=True)[0]).to(dev)
+    out = {}
+    xs = synth.tokens(seed, 60, 16, H, 24, 0.0, synth.BF16)
+    xs_d = torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16).to(dev)
+    out["decode_T16"] = layer_steps(m, torch, h, wr_d, b_d, sh_d, xs_d, 16, 8, 4)
+    log("deepseek decode T=16: %.1f tok/s, %d/%d calls staged" % (out["decode_T16"]["tokens_per_s"],
+                                                                  out["decode_T16"]["staged_calls"], 8))
+    T = 2048
+    x = synth.tokens(seed, 70, T, H, 1, 0.0, synth.BF16)[0]
+    out["prefill_T2048"] = prefill_ffn(m, torch, h, wr_d, b_d, sh_d, x, "bf16 (fp8 codes widened exactly)")
+    m.moe_offload_destroy(h)
+    # the same prefill with MXFP4 expert records (E2M1 codes + E8M0 scale per 32, widened with the scale folded in)
+    h = m.moe_offload_create(E, S, H, F, k, m.MXFP4, 2048, 0, 0)
+    p, stride, rb = m.moe_offload_host_records(h)
+    synth.fill_records(seed, 0, 0, E, H, F, synth.MXFP4, p, stride)
+    sh_mx = torch.from_numpy(synth.records(seed, 0, 1, H, F, synth.MXFP4, shared=True)[0]).to(dev)
+    out["prefill_T2048_mxfp4"] = prefill_ffn(m, torch, h, wr_d, b_d, sh_mx, x,
+                                             "bf16 (E2M1 codes widened exactly, E8M0 scale folded in)")
     m.moe_offload_destroy(h)
     return out
 
