@@ -73,6 +73,7 @@ def lib():
         L.orc_cache_scores.argtypes = [vp, vp]
         L.orc_cache_act.argtypes = [vp, vp]
         L.orc_cache_set_cold.argtypes = [vp, i32]
+        L.orc_cache_set_split.argtypes = [vp, i32]
         L.orc_cache_pinned.argtypes = [vp, vp]
         L.orc_pin.argtypes = [vp, vp, i32, vp]
         L.orc_pin.restype = i32
@@ -251,6 +252,9 @@ class Cache:
         """Apply a copy list to the oracle's own slot/staging bytes."""
         if not self.keep_bytes or len(pairs) == 0 or mode == COLD:  # cold experts are never copied
             return
+        pairs = pairs[pairs[:, 1] < self.S + self.E]  # split mode: host-computed entries move nothing
+        if len(pairs) == 0:
+            return
         if self.staging is None and (pairs[:, 1] >= self.S).any():
             self.staging = np.zeros((self.E, self.stride), dtype=np.uint8)
         desc = np.zeros(2 + 2 * len(pairs), dtype=np.int32)
@@ -270,6 +274,11 @@ class Cache:
     def set_cold(self, on):
         """Cold mode: later ensure calls load nothing; misses are read from their host records."""
         lib().orc_cache_set_cold(self._c, 1 if on else 0)
+
+    def set_split(self, q):
+        """Split mode: of the misses a call wider than the cache stages for itself, the last
+        round(n * q / 256) (ascending id) are read from their host records instead."""
+        lib().orc_cache_set_split(self._c, int(q))
 
     def state(self):
         so = np.empty(self.E, np.int32)

@@ -266,6 +266,15 @@ int orc_topk(const float* logits, int T, int E, int k, int32_t* ids, double* w) 
  * Copy list = {COLD, |misses|, (e, S + E + e) for e in D \ R ascending}.  The
  * table is otherwise unchanged; there is no overflow.  Counters: calls, hits,
  * and cold (the misses computed on the host).
+ *
+ * Split mode (READING: the same pages, with the host and the link working at
+ * once, each on part of a call's misses): ensure runs as above, and of the
+ * misses a call wider than the cache stages for itself only (they keep no
+ * slot), the last round(n_staged * q / 256) in ascending id are read at
+ * S + E + e (computed on the host) instead of staging; q in [0, 256] is the
+ * host's share.  The copy list keeps mode STAGED and lists them with their
+ * S + E + e index; counters: staged_copies counts the staged ones left, cold
+ * the host's.  Calls that do not overflow are unchanged.
  */
 enum { ORC_LRU = 0, ORC_SCORED = 1, ORC_FREQ = 2 };
 #define ORC_SCORE_MAX ((1u << 20) - 1u)
@@ -279,7 +288,8 @@ typedef struct {
   uint32_t* score;
   uint32_t* act;         /* [E] activation count (ORC_FREQ key; kept under every policy) */
   unsigned char* pinned; /* [S] profile-guided placement: never a victim */
-  int cold;              /* 1: misses are computed on the host, never loaded */
+  int cold;              /* 1: misses are computed on the host, never loaded; 2: split (cold_q) */
+  int cold_q;            /* split mode: the host's share of the staged misses, in 1/256 */
   uint64_t tick;
   /* cumulative counters */
   uint64_t calls, hits, misses, staged_calls, staged_copies, prefetch_installs, prefetch_hits, cold_misses;
@@ -317,6 +327,11 @@ void orc_cache_set_policy(orc_cache* c, int policy) {
 }
 
 void orc_cache_set_cold(orc_cache* c, int on) { c->cold = on != 0; }
+
+void orc_cache_set_split(orc_cache* c, int q) {
+  c->cold = 2;
+  c->cold_q = q < 0 ? 0 : (q > 256 ? 256 : q);
+}
 
 void orc_cache_act(const orc_cache* c, uint32_t* act) { memcpy(act, c->act, sizeof(uint32_t) * (size_t)c->E); }
 
@@ -408,7 +423,7 @@ int orc_ensure(orc_cache* c, const int32_t* ids, int n, int k, int32_t* slot_ids
       ++nm;
     }
   }
-  if (c->cold) { /* nothing loads: hits are used in place, misses are read from the host */
+  if (c->cold == 1) { /* nothing loads: hits are used in place, misses are read from the host */
     for (int e = 0; e < E; ++e) {
       if (!inD[e]) continue;
       int s = c->slot_of[e];
@@ -485,24 +500,39 @@ int orc_ensure(orc_cache* c, const int32_t* ids, int n, int k, int32_t* slot_ids
     }
   for (int e = 0; e < E; ++e) /* every routed expert, resident or staged, was activated by this call */
     if (inD[e] && c->act[e] < ORC_SCORE_MAX) c->act[e] += 1;
+  /* split mode: the last n_host of the staged misses (ascending id) are computed on the host */
+  unsigned char* host_e = (unsigned char*)calloc((size_t)E, 1);
+  int n_host = 0;
+  if (over && c->cold == 2) {
+    int n_staged = nm - ns;
+    n_host = (n_staged * c->cold_q + 128) / 256;
+    int seen = 0;
+    for (int e = 0; e < E; ++e) {
+      if (!miss[e] || c->slot_of[e] >= 0) continue; /* a staged miss */
+      if (seen >= n_staged - n_host) host_e[e] = 1;
+      ++seen;
+    }
+  }
   int count = 0;
   for (int e = 0; e < E; ++e) {
     if (!miss[e]) continue;
     desc[2 + 2 * count] = e;
-    desc[3 + 2 * count] = c->slot_of[e] >= 0 ? c->slot_of[e] : S + e;
+    desc[3 + 2 * count] = c->slot_of[e] >= 0 ? c->slot_of[e] : (host_e[e] ? S + E + e : S + e);
     ++count;
   }
   for (int i = 0; i < n; ++i) {
     int e = ids[i];
-    slot_ids[i] = c->slot_of[e] >= 0 ? c->slot_of[e] : S + e;
+    slot_ids[i] = c->slot_of[e] >= 0 ? c->slot_of[e] : (host_e[e] ? S + E + e : S + e);
   }
   desc[0] = over ? ORC_STAGED : ORC_SLOTS;
   desc[1] = count;
   c->misses += (uint64_t)ns;
   if (over) {
     c->staged_calls += 1;
-    c->staged_copies += (uint64_t)(nm - ns);
+    c->staged_copies += (uint64_t)(nm - ns - n_host);
+    c->cold_misses += (uint64_t)n_host;
   }
+  free(host_e);
   free(order);
   free(claim);
   free(miss);
@@ -664,7 +694,8 @@ int orc_pin(orc_cache* c, const int32_t* experts, int n, int32_t* desc) {
  * (r >= S).  Strides are the distances between consecutive records. */
 void orc_copy(const int32_t* desc, int S, const uint8_t* host, size_t host_stride, uint8_t* slots, uint8_t* staging,
               size_t dev_stride, size_t record_bytes) {
-  if (desc[0] == ORC_COLD) return; /* cold experts stay on the host: nothing moves */
+  if (desc[0] == ORC_COLD) return; /* cold experts stay on the host: nothing moves (split mode: the caller
+                                       leaves the host-computed entries out of the list) */
   int count = desc[1];
   for (int i = 0; i < count; ++i) {
     int e = desc[2 + 2 * i], r = desc[3 + 2 * i];

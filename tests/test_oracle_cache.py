@@ -66,7 +66,7 @@ class BruteCache:
     freq=True: slots installed and not used since go first, then the expert activated by the fewest
     calls since the cache was created (kept across evictions, capped), then LRU."""
 
-    def __init__(self, E, S, scored=False, cap=(1 << 20) - 1, freq=False, cold=False):
+    def __init__(self, E, S, scored=False, cap=(1 << 20) - 1, freq=False, cold=False, split=None):
         self.E, self.S = E, S
         self.held = [None] * S
         self.home = {}
@@ -74,7 +74,7 @@ class BruteCache:
         self.uses = [0] * S
         self.fired = [0] * E  # activations per expert
         self.clock = 0
-        self.scored, self.cap, self.freq, self.cold = scored, cap, freq, cold
+        self.scored, self.cap, self.freq, self.cold, self.split = scored, cap, freq, cold, split
         self.pinned = set()
 
     def _victims(self, protect):
@@ -123,7 +123,12 @@ class BruteCache:
                 self.used[self.home[e]] = self.clock
                 self.uses[self.home[e]] = min(self.uses[self.home[e]] + 1, self.cap)
             self.fired[e] = min(self.fired[e] + 1, self.cap)
-        rec = lambda e: self.home.get(e, self.S + e)
+        host = set()
+        if over and self.split is not None:  # the last share of the staged misses go to the host
+            staged = sorted(e for e in miss if e not in self.home)
+            n_host = (len(staged) * self.split + 128) // 256
+            host = set(staged[len(staged) - n_host:])
+        rec = lambda e: self.home.get(e, self.S + self.E + e if e in host else self.S + e)
         return [rec(e) for e in ids], int(over), [(e, rec(e)) for e in miss]
 
     def pin(self, P):
@@ -456,3 +461,55 @@ def test_cold_mode_hand_example(orc):
     cnt = c.counters()
     assert (cnt["hits"], cnt["misses"], cnt["cold"]) == (2, 2, 2)
     assert c.activations().tolist() == [0, 2, 2, 0, 0, 1, 1, 0]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_split_mode_matches_brute_force(orc, seed):
+    """Split mode: calls wider than the cache hand the last share of their staged misses to the host
+    (index S + E + e); everything else, slot claims included, is unchanged."""
+    rng = np.random.default_rng(400 + seed)
+    E = int(rng.choice([16, 32]))
+    k = int(rng.choice([2, 4]))
+    S = int(rng.integers(k, E // 2))
+    q = int(rng.choice([0, 64, 115, 200, 256]))
+    c = orc.Cache(E, S)
+    c.set_split(q)
+    b = BruteCache(E, S, split=q)
+    host_total = staged_total = 0
+    for step in range(120):
+        T = int(rng.integers(1, 8))
+        ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+        before = c.state()
+        slot_ids, mode, pairs = c.ensure(ids)
+        es, em, ep = b.ensure(ids.reshape(-1).tolist(), k)
+        assert slot_ids.reshape(-1).tolist() == es and mode == em, (step, q)
+        assert [tuple(map(int, r)) for r in pairs] == ep
+        assert c.scores().tolist() == b.uses and c.activations().tolist() == b.fired
+        host_total += sum(1 for p_ in pairs if p_[1] >= S + E)
+        staged_total += sum(1 for p_ in pairs if S <= p_[1] < S + E)
+        so, eo, lu, tick = c.state()
+        for s_ in range(S):  # the maps stay mutually inverse
+            if eo[s_] >= 0:
+                assert so[eo[s_]] == s_
+    cnt = c.counters()
+    assert cnt["cold"] == host_total and cnt["staged_copies"] == staged_total
+    if q == 0:
+        assert host_total == 0
+    if q == 256:
+        assert staged_total == 0 and host_total > 0
+
+
+def test_split_mode_hand_example(orc):
+    # 3 slots hold experts 1, 2, 3; a call needs 1, 4, 5, 6, 7 (|D| = 5 > 3): experts 2 and 3 are the two
+    # eligible victims; the misses 4..7 are routed once each at positions 1, 2 (token 0) and 0, 1 (token 1)
+    # after 1, so 6 (position 0) and 4 (position 1, lower id than 7) claim slots 1 and 2; 5 and 7 are staged,
+    # and with q = 128 (half) the last of them, 7, goes to the host
+    c = orc.Cache(8, 3)
+    c.ensure(np.array([[1, 2, 3]], np.int32))
+    c.set_split(128)
+    sid, mode, pairs = c.ensure(np.array([[1, 4, 5], [6, 7, 1]], np.int32))
+    assert mode == orc.STAGED
+    assert pairs.tolist() == [[4, 2], [5, 8], [6, 1], [7, 18]]  # S + 5 = 8 staged, S + E + 7 = 18 host
+    assert sid.tolist() == [[0, 2, 8], [1, 18, 0]]
+    cnt = c.counters()
+    assert (cnt["staged_copies"], cnt["cold"]) == (1, 1)

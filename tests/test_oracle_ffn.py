@@ -128,6 +128,13 @@ def test_placement_invariance_in_the_oracle(orc, syn, wdt, E, k, H, F, T):
             modes.add(r["mode"])
             assert np.array_equal(r["y"], ref[s]), (S, s)
     assert modes == {0, 1, 2}  # slots, decode staging and whole-layer staging all exercised
+    # split mode: of a wide call's staged misses, half are read from their host records at S + E + e
+    for S in (k, (k + E) // 2):
+        L = orc.Layer(E, S, k, H, F, wdt, host, wr, b)
+        L.cache.set_split(128)
+        for s in range(len(xs)):
+            r = L.step(xs[s])
+            assert np.array_equal(r["y"], ref[s]), ("split", S, s)
     # host-computed cold experts: the misses are read from their host records at S + E + e
     for S in (k, (k + E) // 2):
         L = orc.Layer(E, S, k, H, F, wdt, host, wr, b)
