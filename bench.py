@@ -105,6 +105,8 @@ def main():
     ap.add_argument("--cpu-rates", action="store_true", help="also the CPU oracle's own rates on all threads and one")
     ap.add_argument("--prefetch-only", action="store_true",
                     help="only the lookahead-prefetch comparison on the 48-layer workload (its own JSON line)")
+    ap.add_argument("--split-only", action="store_true",
+                    help="only the batch-32 eager comparison of the link, split and host-cold modes (its own JSON line)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--mxfp4-only", action="store_true",
                     help="only the same decode chain with MXFP4 expert records (prints its own JSON line)")
@@ -260,6 +262,16 @@ def main():
         print(json.dumps({"workload": "qwen3-30b-a3b-shaped offloaded MoE decode, 48 layers, batch 1: router-"
                                       "lookahead prefetch (4 installs per layer) against none",
                           "prefetch": prefetch_compare(args, m, hip, handles, run_decode, token_stream)}), flush=True)
+        for h in reversed(handles):
+            m.moe_offload_destroy(h)
+        return
+
+    if args.split_only:
+        print(json.dumps({"workload": "qwen3-30b-a3b-shaped offloaded MoE decode, 48 layers, batch 32, eager "
+                                      "entry-point calls: staged misses over the link, split with the host CPU, "
+                                      "or all on the host",
+                          "host_split": host_split_compare(args, m, torch, handles, wr_d, b_d, token_stream)}),
+              flush=True)
         for h in reversed(handles):
             m.moe_offload_destroy(h)
         return
@@ -462,6 +474,7 @@ def main():
         result["prefetch"] = prefetch_compare(args, m, hip, handles, run_decode, token_stream)
         result["eviction"] = eviction_compare(args, m, hip, torch, handles, wr_d, b_d, run_decode, token_stream)
         result["slot_fractions"] = slot_fraction_compare(args, m, hip, handles, run_decode, token_stream)
+        result["host_split"] = host_split_compare(args, m, torch, handles, wr_d, b_d, token_stream)
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args, handles, routers, stride, T0)
@@ -644,7 +657,7 @@ def mixtral_layer(args, m, torch):
     b_d = torch.from_numpy(b).to(dev)
     out = {}
     for S in (2, 4, 6):
-        h = m.moe_offload_create(E, S, H, F, k, m.BF16, 64, 0, 0)
+        h = m.moe_offload_create(E, S, H, F, k, m.BF16, 65, 0, 0)
         p, stride, rb = m.moe_offload_host_records(h)
         synth.fill_records(seed, 0, 0, E, H, F, synth.BF16, p, stride)
         for T in (1, 8, 64, 65):
@@ -756,6 +769,80 @@ def deepseek_layer(args, m, torch):
     out["prefill_T2048_mxfp4"] = prefill_ffn(m, torch, h, wr_d, b_d, sh_mx, x,
                                              "bf16 (E2M1 codes widened exactly, E8M0 scale folded in)")
     m.moe_offload_destroy(h)
+    return out
+
+
+def host_split_compare(args, m, torch, handles, wr_d, b_d, token_stream, T=32, warm=4, steps=8):
+    """Batch-32 eager decode over the layers with entry-point calls (route, ensure, copy, FFN per layer; at
+    this batch nearly every call needs more experts than its 26 slots): the staged misses all over the host
+    link; split between the link and the host CPU at the share measured per layer (MOE_COLD_SPLIT); and every
+    miss computed on the host (cold mode).  Wall-clock tok/s over `steps` steps after `warm` untimed ones,
+    each mode from empty caches."""
+    import numpy as np
+    dev = torch.device("cuda", 0)
+    st = torch.cuda.current_stream()
+    L = len(handles)
+    ids = torch.empty((T, K_TOP), dtype=torch.int32, device=dev)
+    w = torch.empty((T, K_TOP), dtype=torch.float32, device=dev)
+    sid = torch.empty_like(ids)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    xa, xb, xn = torch.empty_like(y), torch.empty_like(y), torch.empty_like(y)
+    xs = token_stream(T, warm + steps)
+    out = {}
+    qs = []
+    try:
+        for mode in ("link", "split", "cold"):
+            for h in handles:
+                m.moe_offload_set_cold(h, m.COLD_OFF, st)
+                m.moe_offload_reset(h, st)
+            if mode == "split":
+                qs = [m.moe_offload_set_cold(h, m.COLD_SPLIT, st) for h in handles]
+            elif mode == "cold":
+                for h in handles:
+                    m.moe_offload_set_cold(h, m.COLD_ON, st)
+            ffn = m.moe_slot_ffn if mode == "link" else m.moe_slot_ffn_host_cold
+
+            def step(s):
+                a, b = xa, xb
+                a.copy_(xs[s])
+                for l, h in enumerate(handles):  # the decode chain's block: pre-norm, MoE, residual
+                    m.moe_rmsnorm(a, xn, T, H, m.BF16, stream=st)
+                    m.moe_route_topk(h, xn, wr_d[l], b_d[l], T, ids, w, st)
+                    m.moe_slot_ensure(h, ids, T, sid, st)
+                    m.moe_copy_misses(h, st)
+                    ffn(h, xn, sid, w, T, None, y, a, b, st)
+                    a, b = b, a
+
+            for s in range(warm):
+                step(s)
+            torch.cuda.synchronize()
+            before = [m.moe_offload_stats(h) for h in handles]
+            t0 = time.perf_counter()
+            for s in range(warm, warm + steps):
+                step(s)
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+            after = [m.moe_offload_stats(h) for h in handles]
+            assert all(a_["error"] == 0 for a_ in after), [a_["error"] for a_ in after]
+            d = {kk: sum(a_[kk] - b_[kk] for a_, b_ in zip(after, before)) for kk in after[0]}
+            out[mode] = {"tokens_per_s": round(T * steps / dt, 2), "ms_per_step": round(dt * 1e3 / steps, 3),
+                         "link_records_per_token": round((d["misses"] + d["staged_copies"]) / (T * steps), 3),
+                         "host_records_per_token": round(d["cold_misses"] / (T * steps), 3),
+                         "staged_calls": d["staged_calls"], "calls": d["calls"]}
+            log("host-split %s: batch %d, %.1f tok/s, %.2f records/token over the link, %.2f on the host" %
+                (mode, T, out[mode]["tokens_per_s"], out[mode]["link_records_per_token"],
+                 out[mode]["host_records_per_token"]))
+    finally:
+        for h in handles:
+            m.moe_offload_set_cold(h, m.COLD_OFF, st)
+            m.moe_offload_reset(h, st)
+        torch.cuda.synchronize()
+    if qs:
+        q = sorted(x[0] for x in qs)
+        out["split_share_q256"] = {"median": q[len(q) // 2], "min": q[0], "max": q[-1],
+                                   "host_us_per_record_median": round(float(np.median([x[1] for x in qs])), 1),
+                                   "link_us_per_record_median": round(float(np.median([x[2] for x in qs])), 1)}
+    out["split_speedup_vs_link"] = round(out["split"]["tokens_per_s"] / out["link"]["tokens_per_s"], 3)
     return out
 
 

@@ -92,6 +92,7 @@ def lib():
             "moe_slot_ffn_noalloc": ([vp, vp, vp, vp, i32, vp, vp, vp, vp, vp], i32),
             "moe_slot_ffn_host_cold": ([vp, vp, vp, vp, i32, vp, vp, vp, vp, vp], i32),
             "moe_offload_set_cold": ([vp, i32, vp, P(ctypes.c_int32), P(ctypes.c_double), P(ctypes.c_double)], i32),
+            "moe_offload_set_split": ([vp, i32, vp], i32),
             "moe_rmsnorm": ([vp, vp, i32, i32, i32, ctypes.c_float, vp], i32),
             "moe_prefill_stage": ([vp, vp, i32, vp, P(ctypes.c_int32), vp], i32),
             "moe_prefetch_install": ([vp, vp, i32, i32, vp], i32),
@@ -206,16 +207,21 @@ def moe_slot_ffn_noalloc(h, x, slot_ids, w, T, shared_record, y, residual=None, 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20
 
-COLD_OFF, COLD_ON, COLD_AUTO = 0, 1, 2
+COLD_OFF, COLD_ON, COLD_AUTO, COLD_SPLIT = 0, 1, 2, 3
 MODE_COLD = 3
 
 
 def moe_offload_set_cold(h, mode, stream=None):
-    """-> (chosen 0/1, host FFN us per record, link us per record); the times are measured for COLD_AUTO only."""
+    """-> (chosen: 0/1, or the host share q for COLD_SPLIT; host FFN us per record, link us per record); the
+    times are measured for COLD_AUTO and COLD_SPLIT only."""
     chosen, cpu, link = ctypes.c_int32(), ctypes.c_double(), ctypes.c_double()
     _check(lib().moe_offload_set_cold(h, mode, _stream(stream), ctypes.byref(chosen), ctypes.byref(cpu),
                                       ctypes.byref(link)))
     return chosen.value, cpu.value, link.value
+
+
+def moe_offload_set_split(h, q, stream=None):
+    return _check(lib().moe_offload_set_split(h, q, _stream(stream)))
 
 
 def moe_slot_ffn_host_cold(h, x, slot_ids, w, T, shared_record, y, residual=None, x_next=None, stream=None):

@@ -19,6 +19,10 @@ constexpr int kF32Rows = 64;        // rows per work item on the fp32 path
 
 // victim orders of the slot table (table.h victim_key)
 constexpr int kPolicyLru = 0, kPolicyScored = 1, kPolicyFreq = 2;
+// the layer's cold-mode word: 0 off; kColdAll: every miss is computed on the host;
+// kColdSplit | q << 8: of an overflowing call's staged misses, the last share q/256
+// (ascending id) is computed on the host, the rest crosses the link
+constexpr int kColdAll = 1, kColdSplit = 2;
 
 // counters[] layout (device, uint64)
 enum { C_CALLS = 0, C_HITS, C_MISSES, C_STAGED_CALLS, C_STAGED_COPIES, C_PF_INSTALLS, C_PF_HITS, C_BYTES, C_COLD, C_N };
@@ -36,7 +40,7 @@ struct CacheDev {
   int32_t* pf_list;     // [2 + 2*S]
   uint64_t* counters;   // [C_N]
   int32_t* err;         // [1] sticky MOE_DEV_ERR_* bits
-  int32_t* cold;        // [1] 1: ensure loads nothing, misses are computed on the host (index S + E + e)
+  int32_t* cold;        // [1] the cold-mode word (kColdAll, kColdSplit | q << 8); host-computed index S + E + e
   int E, S;
   int policy;           // victim order: kPolicyLru, kPolicyScored, kPolicyFreq (table.h)
   uint64_t record_bytes;
@@ -90,7 +94,10 @@ struct moe_offload {
   int32_t* pinned_i32;       // small pinned host scratch
   moe::Prof* prof;           // per-kernel timing, created on first enable
   // host-computed cold experts (allocated when the cold mode is first switched on)
-  bool cold_on;              // host mirror of the device flag
+  bool cold_on;              // host mirror of the device word: nonzero
+  bool cold_split;           // ... and in split mode (the copies run beside the host's share)
+  hipStream_t cold_stream;   // split mode: the call's indices and activations go to the host on it
+  hipEvent_t ens_ev;         // split mode: recorded after each ensure (the indices are final)
   int32_t* cold_sid;         // pinned host [max_tokens * k]: the call's record indices
   void* cold_x;              // pinned host [max_tokens * H]: the call's activations
   float* cold_out;           // pinned, mapped, coherent host [max_tokens * k][H]: cold pairs' outputs
@@ -174,7 +181,7 @@ hipError_t launch_decide(moe_offload* h, int T, int32_t* ids, float* w, int32_t*
                          moe_offload* hn = nullptr, int32_t* pred = nullptr, int max_n = 0);
 hipError_t launch_rmsnorm(const void* x, void* out, int T, int H, int dtype, float eps, hipStream_t s);
 // the layer's cold-mode flag on the device (ordered on s with the table's other writers)
-hipError_t launch_set_cold(moe_offload* h, int on, hipStream_t s);
+hipError_t launch_set_cold(moe_offload* h, int word, hipStream_t s);
 // part rows of the call's cold pairs (record index >= S + E) from h->cold_out, then the combine
 hipError_t launch_cold_combine(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int T,
                                const void* shared, void* y, const void* residual, void* x_next, hipStream_t s);

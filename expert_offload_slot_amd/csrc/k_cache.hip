@@ -105,9 +105,9 @@ __global__ void k_reset(CacheDev c) {
   }
 }
 
-// the layer's cold-mode flag, written in stream order like the table itself
-__global__ void k_set_cold(int32_t* cold, int on) {
-  if (threadIdx.x == 0) *cold = on;
+// the layer's cold-mode word, written in stream order like the table itself
+__global__ void k_set_cold(int32_t* cold, int word) {
+  if (threadIdx.x == 0) *cold = word;
 }
 
 // ---------------------------------------------------------------- copy
@@ -128,6 +128,7 @@ __global__ __launch_bounds__(kCopyThreads) void k_copy(const int32_t* __restrict
     const int m = (int)(cidx / per);
     const uint64_t off = (cidx - (uint64_t)m * per) * CH;
     const int e = list[2 + 2 * m], r = list[3 + 2 * m];
+    if (r >= S + E && r < S + 2 * E) continue;  // split mode: computed on the host, never moved
     if ((unsigned)e >= (unsigned)E || (unsigned)r >= (unsigned)(S + E)) {
       if (threadIdx.x == 0) atomicOr(err, MOE_DEV_ERR_AUDIT);
       continue;
@@ -179,8 +180,8 @@ hipError_t launch_pin(moe_offload* h, const int32_t* experts, int n, hipStream_t
   return hipGetLastError();
 }
 
-hipError_t launch_set_cold(moe_offload* h, int on, hipStream_t s) {
-  hipLaunchKernelGGL(k_set_cold, dim3(1), dim3(64), 0, s, h->cache.cold, on ? 1 : 0);
+hipError_t launch_set_cold(moe_offload* h, int word, hipStream_t s) {
+  hipLaunchKernelGGL(k_set_cold, dim3(1), dim3(64), 0, s, h->cache.cold, word);
   return hipGetLastError();
 }
 

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <chrono>
+#include <cmath>
 #include <new>
 
 #include "host_ffn.h"
@@ -73,6 +74,8 @@ void free_all(moe_offload* h) {
   if (h->cold_x) (void)hipHostFree(h->cold_x);
   if (h->cold_out) (void)hipHostFree(h->cold_out);
   if (h->cold_ev) (void)hipEventDestroy(h->cold_ev);
+  if (h->ens_ev) (void)hipEventDestroy(h->ens_ev);
+  if (h->cold_stream) (void)hipStreamDestroy(h->cold_stream);
   if (h->prof) {
     for (auto& pair : h->prof->ev)
       for (hipEvent_t e : pair)
@@ -347,6 +350,7 @@ int moe_slot_ensure(moe_offload* h, const int32_t* ids, int32_t T, int32_t* slot
   if (!ids || !slot_ids) return fail(MOE_EINVAL, "moe_slot_ensure: null pointer");
   DeviceGuard g(h->device);
   HIP_TRY(moe::launch_ensure(h, ids, T * h->k, slot_ids, (hipStream_t)stream));
+  if (h->cold_split) HIP_TRY(hipEventRecord(h->ens_ev, (hipStream_t)stream));
   return MOE_OK;
 }
 
@@ -378,10 +382,13 @@ int moe_slot_ffn_host_cold(moe_offload* h, const void* x, const int32_t* slot_id
   DeviceGuard g(h->device);
   hipStream_t s = (hipStream_t)stream;
   const size_t es = h->dtype == MOE_F32 ? 4 : 2;
-  // the call's record indices and activations to the host, then the GPU's share of the FFN
-  HIP_TRY(hipMemcpyAsync(h->cold_sid, slot_ids, 4 * (size_t)T * h->k, hipMemcpyDeviceToHost, s));
-  HIP_TRY(hipMemcpyAsync(h->cold_x, x, es * (size_t)T * h->H, hipMemcpyDeviceToHost, s));
-  HIP_TRY(hipEventRecord(h->cold_ev, s));
+  // the call's record indices and activations to the host, then the GPU's share of the FFN; in split
+  // mode on a stream of their own from the ensure on, so the host's share runs beside the copy kernel
+  hipStream_t ds = h->cold_split ? h->cold_stream : s;
+  if (h->cold_split) HIP_TRY(hipStreamWaitEvent(ds, h->ens_ev, 0));
+  HIP_TRY(hipMemcpyAsync(h->cold_sid, slot_ids, 4 * (size_t)T * h->k, hipMemcpyDeviceToHost, ds));
+  HIP_TRY(hipMemcpyAsync(h->cold_x, x, es * (size_t)T * h->H, hipMemcpyDeviceToHost, ds));
+  HIP_TRY(hipEventRecord(h->cold_ev, ds));
   HIP_TRY(moe::launch_ffn(h, x, slot_ids, w, T, shared_record, y, residual, x_next, nullptr, 0.f, s, false, false));
   HIP_TRY(hipEventSynchronize(h->cold_ev));
   // the host's share meanwhile, into the mapped output rows
@@ -453,6 +460,7 @@ int moe_prefill_stage(moe_offload* h, const int32_t* ids, int32_t T, int32_t* sl
     HIP_TRY(moe::launch_copy(h, h->cache.copy_list, s));
     if (staged_out) *staged_out = 0;
   }
+  if (h->cold_split) HIP_TRY(hipEventRecord(h->ens_ev, s));  // the indices are final
   return MOE_OK;
 }
 
@@ -483,26 +491,36 @@ int moe_copy_prefetch(moe_offload* h, void* stream) {
   return MOE_OK;
 }
 
+// the host side's buffers and the split mode's stream and events, once (the device must be current)
+static int cold_buffers(moe_offload* h) {
+  if (h->cold_stream) return MOE_OK;
+  const size_t es = h->dtype == MOE_F32 ? 4 : 2;
+  if (!h->cold_sid) HIP_TRY(hipHostMalloc((void**)&h->cold_sid, 4 * (size_t)h->max_tokens * h->k, hipHostMallocDefault));
+  if (!h->cold_x) HIP_TRY(hipHostMalloc(&h->cold_x, es * (size_t)h->max_tokens * h->H, hipHostMallocDefault));
+  if (!h->cold_out) {
+    HIP_TRY(hipHostMalloc((void**)&h->cold_out, 4 * (size_t)h->max_tokens * h->k * h->H,
+                          hipHostMallocMapped | hipHostMallocCoherent));
+    HIP_TRY(hipHostGetDevicePointer((void**)&h->cold_out_dev, h->cold_out, 0));
+  }
+  if (!h->cold_ev) HIP_TRY(hipEventCreateWithFlags(&h->cold_ev, hipEventDisableTiming));
+  if (!h->ens_ev) HIP_TRY(hipEventCreateWithFlags(&h->ens_ev, hipEventDisableTiming));
+  HIP_TRY(hipStreamCreateWithFlags(&h->cold_stream, hipStreamNonBlocking));
+  return MOE_OK;
+}
+
 int moe_offload_set_cold(moe_offload* h, int32_t mode, void* stream, int32_t* chosen, double* cpu_us,
                          double* link_us) {
   if (int rc = check_handle(h)) return rc;
-  if (mode != MOE_COLD_OFF && mode != MOE_COLD_ON && mode != MOE_COLD_AUTO)
+  if (mode != MOE_COLD_OFF && mode != MOE_COLD_ON && mode != MOE_COLD_AUTO && mode != MOE_COLD_SPLIT)
     return fail(MOE_EINVAL, "moe_offload_set_cold: mode %d", mode);
   DeviceGuard g(h->device);
   hipStream_t s = (hipStream_t)stream;
   if (cpu_us) *cpu_us = 0.0;
   if (link_us) *link_us = 0.0;
-  if (mode != MOE_COLD_OFF && !h->cold_out) {  // the host side's buffers, once
-    const size_t es = h->dtype == MOE_F32 ? 4 : 2;
-    HIP_TRY(hipHostMalloc((void**)&h->cold_sid, 4 * (size_t)h->max_tokens * h->k, hipHostMallocDefault));
-    HIP_TRY(hipHostMalloc(&h->cold_x, es * (size_t)h->max_tokens * h->H, hipHostMallocDefault));
-    HIP_TRY(hipHostMalloc((void**)&h->cold_out, 4 * (size_t)h->max_tokens * h->k * h->H,
-                          hipHostMallocMapped | hipHostMallocCoherent));
-    HIP_TRY(hipHostGetDevicePointer((void**)&h->cold_out_dev, h->cold_out, 0));
-    HIP_TRY(hipEventCreateWithFlags(&h->cold_ev, hipEventDisableTiming));
-  }
+  if (mode != MOE_COLD_OFF)
+    if (int rc = cold_buffers(h)) return rc;
   int on = mode == MOE_COLD_ON;
-  if (mode == MOE_COLD_AUTO) {
+  if (mode == MOE_COLD_AUTO || mode == MOE_COLD_SPLIT) {
     // one record's FFN on the host at one token, against one record over the link (a pinned
     // host-to-device copy into staging); the median of three records, each touched once
     HIP_TRY(hipStreamSynchronize(s));
@@ -550,10 +568,29 @@ int moe_offload_set_cold(moe_offload* h, int32_t mode, void* stream, int32_t* ch
     if (cpu_us) *cpu_us = c_us;
     if (link_us) *link_us = l_us;
     on = c_us < l_us;
+    if (mode == MOE_COLD_SPLIT) {
+      const int q = (int)std::lround(256.0 * l_us / (c_us + l_us));
+      if (chosen) *chosen = q;
+      return moe_offload_set_split(h, q, stream);
+    }
   }
-  HIP_TRY(moe::launch_set_cold(h, on, s));
+  HIP_TRY(moe::launch_set_cold(h, on ? moe::kColdAll : 0, s));
   h->cold_on = on != 0;
+  h->cold_split = false;
   if (chosen) *chosen = on;
+  return MOE_OK;
+}
+
+int moe_offload_set_split(moe_offload* h, int32_t q, void* stream) {
+  if (int rc = check_handle(h)) return rc;
+  if (q < 0 || q > 256) return fail(MOE_EINVAL, "moe_offload_set_split: q=%d outside [0, 256]", q);
+  DeviceGuard g(h->device);
+  if (int rc = cold_buffers(h)) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(moe::launch_set_cold(h, moe::kColdSplit | (q << 8), s));
+  HIP_TRY(hipStreamSynchronize(s));
+  h->cold_on = true;
+  h->cold_split = true;
   return MOE_OK;
 }
 

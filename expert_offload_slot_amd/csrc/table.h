@@ -49,7 +49,7 @@ struct SharedTable {
   int vic[kMaxExperts];    // victim slot by rank
   int wave[4 * kWaves];
   int bad;
-  int cold;                // the layer's cold-mode flag as loaded
+  int cold;                // the layer's cold-mode word as loaded (kCold*)
   uint64_t tick;           // the table's call counter as loaded
   uint64_t cnt[C_N];       // the counters as loaded
 };
@@ -110,7 +110,7 @@ __device__ __forceinline__ void put_table(const CacheDev& c, const TableRegs& r,
   }
   if (u == 0) t.tick = r.tc;
   if (u >= 1 && u <= C_N) t.cnt[u - 1] = r.tc;
-  if (u == C_N + 1) t.cold = r.tc != 0;
+  if (u == C_N + 1) t.cold = (int)(uint32_t)r.tc;
 }
 
 // Loads the table into LDS (fetch_table, then put_table).
@@ -202,7 +202,7 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
   block_rank4(f, t.wave, rk, tot);
   const int mrank = rk[1], nm = tot[1], nh = tot[2], npf = tot[3];
 
-  if (t.cold) {  // host-computed cold experts: nothing loads, misses are read at S + E + e
+  if (t.cold == kColdAll) {  // host-computed cold experts: nothing loads, misses are read at S + E + e
     if (inD && sl >= 0) {
       const uint32_t old = t.score[sl];
       t.last_use[sl] = tick;
@@ -238,7 +238,8 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
   // eligible victims by rank: slots not pinned and not holding an expert of D;
   // the call overflows when the misses outnumber them (no pins: when |D| > S)
   bool over = false;
-  int ns = 0;  // misses that get a slot
+  int ns = 0;      // misses that get a slot
+  int n_host = 0;  // split mode: staged misses handed to the host
   if (nm > 0) {
     bool elig = false;
     if (tid < S) {
@@ -276,6 +277,8 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
       t.vic[rank] = tid;  // rank < nv
     }
     __syncthreads();
+    int v = -1;
+    bool staged = false;
     if (miss) {
       int crank = mrank;  // claim order: ascending id, or install order when over
       if (over) {
@@ -284,7 +287,7 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
 #pragma unroll 8
         for (int e2 = 0; e2 < E; ++e2) crank += ckey[e2] < mine ? 1 : 0;
       }
-      int v = S + tid;
+      v = S + tid;
       if (crank < ns) {
         v = t.vic[crank];
         const int old = t.expert_of[v];
@@ -292,6 +295,19 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
         t.expert_of[v] = tid;
         t.slot_of[tid] = v;
       }
+      staged = crank >= ns;
+    }
+    if (over && (t.cold & 0xff) == kColdSplit) {  // block-uniform
+      // the last share q/256 of the staged misses (ascending id) are computed on the host
+      int nst;
+      const int srank = block_rank(staged, t.wave, &nst);
+      n_host = (nst * (t.cold >> 8) + 128) >> 8;
+      if (staged && srank >= nst - n_host) {
+        v = S + E + tid;
+        t.flag[tid] = 2;
+      }
+    }
+    if (miss) {
       c.copy_list[2 + 2 * mrank] = tid;
       c.copy_list[3 + 2 * mrank] = v;
     }
@@ -308,7 +324,7 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
   for (int i = tid; i < n; i += kBlock) {
     const int e = ids[i];
     const int r = t.slot_of[e];
-    const int v = r >= 0 ? r : S + e;
+    const int v = r >= 0 ? r : (t.flag[e] == 2 ? S + E + e : S + e);
     slot_ids[i] = v;
     if (slot_lds) slot_lds[i] = v;
   }
@@ -322,10 +338,11 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
     c.counters[C_HITS] = t.cnt[C_HITS] + (uint64_t)nh;
     c.counters[C_MISSES] = t.cnt[C_MISSES] + (uint64_t)ns;
     c.counters[C_PF_HITS] = t.cnt[C_PF_HITS] + (uint64_t)npf;
-    c.counters[C_BYTES] = t.cnt[C_BYTES] + (uint64_t)nm * c.record_bytes;
+    c.counters[C_BYTES] = t.cnt[C_BYTES] + (uint64_t)(nm - n_host) * c.record_bytes;
     if (over) {
       c.counters[C_STAGED_CALLS] = t.cnt[C_STAGED_CALLS] + 1;
-      c.counters[C_STAGED_COPIES] = t.cnt[C_STAGED_COPIES] + (uint64_t)(nm - ns);
+      c.counters[C_STAGED_COPIES] = t.cnt[C_STAGED_COPIES] + (uint64_t)(nm - ns - n_host);
+      if (n_host) c.counters[C_COLD] = t.cnt[C_COLD] + (uint64_t)n_host;
     }
   }
 }

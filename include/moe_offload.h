@@ -152,7 +152,7 @@ typedef struct {
   uint64_t tick;              /* LRU clock (ensure and stage calls) */
   int32_t error;              /* sticky MOE_DEV_ERR_* bits */
   int32_t resident;           /* experts currently resident in slots */
-  uint64_t cold_misses;       /* misses computed on the host in cold mode (moe_offload_set_cold) */
+  uint64_t cold_misses;       /* misses computed on the host in cold or split mode */
 } moe_stats;
 
 /* Device addresses and sizes of the handle's state, for inspection and tests.
@@ -292,19 +292,42 @@ int moe_slot_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const f
  *         of this layer, the host FFN at one token (on the library's worker
  *         threads) against a pinned host-to-device copy of the record, and turn
  *         the cold mode on when the host is faster (the layer's misses then go
- *         to the CPU instead of over the link).
- *   chosen (may be NULL): the resulting mode (0 off, 1 on);
- *   cpu_us, link_us (may be NULL): the two measured times per record (AUTO only;
- *         0 otherwise).
+ *         to the CPU instead of over the link);
+ *         or MOE_COLD_SPLIT: the same measurement, then split mode with the
+ *         host's share q = round(256 * link / (cpu + link)) (moe_offload_set_split).
+ *   chosen (may be NULL): the resulting mode (0 off, 1 on), or for MOE_COLD_SPLIT
+ *         the share q in [0, 256];
+ *   cpu_us, link_us (may be NULL): the two measured times per record (AUTO and
+ *         SPLIT; 0 otherwise).
  * Host-synchronising on `stream`; the flag is written on the device in stream
  * order, so issue it on the compute stream between calls.  Switching on the
  * first time allocates the pinned host buffers the cold FFN uses (max_tokens
  * rows).  While the mode is on, the FFN must be moe_slot_ffn_host_cold:
  * moe_slot_ffn and the decode chain refuse the handle (MOE_EINVAL).
  * Errors: MOE_EINVAL, MOE_ENOMEM, MOE_EHIP. */
-enum { MOE_COLD_OFF = 0, MOE_COLD_ON = 1, MOE_COLD_AUTO = 2 };
+enum { MOE_COLD_OFF = 0, MOE_COLD_ON = 1, MOE_COLD_AUTO = 2, MOE_COLD_SPLIT = 3 };
 int moe_offload_set_cold(moe_offload* h, int32_t mode, void* stream, int32_t* chosen, double* cpu_us,
                          double* link_us);
+
+/* Split mode (same pages: the host's DRAM-bound FFN and the host link are two
+ * independent channels out of host memory; a call wider than the cache uses
+ * both).  Calls that fit the cache are unchanged (mode SLOTS).  In a call that
+ * overflows (mode STAGED), slot claims, victims, usage updates and copy-list
+ * order are unchanged; of the n staged misses (those that got no slot), the
+ * last h = floor((n * q + 128) / 256) in ascending id are computed on the host:
+ * their record index is S + E + e in slot_ids and in the copy list, the copy
+ * kernel skips them, stats.staged_copies counts the other n - h and
+ * stats.cold_misses the h.
+ *   q: the host's share in 1/256, in [0, 256] (0: every staged miss crosses the
+ *      link, as with the mode off; 256: none does).
+ * While split mode is on the FFN must be moe_slot_ffn_host_cold, and the
+ * activations x it receives must already be final when the call's
+ * moe_slot_ensure is enqueued (they are whenever x fed moe_route_topk before
+ * it): the host reads the call's indices and activations on a stream of its
+ * own as soon as the ensure has run, so its share overlaps the copy kernel.
+ * Host-synchronising on `stream`; MOE_COLD_OFF (moe_offload_set_cold) ends it.
+ * Errors: MOE_EINVAL (q outside [0, 256]), MOE_ENOMEM, MOE_EHIP. */
+int moe_offload_set_split(moe_offload* h, int32_t q, void* stream);
 
 /* The expert FFN of a cold-mode call (same arguments and results as
  * moe_slot_ffn): the GPU computes the resident experts while the host CPU

@@ -254,7 +254,7 @@ def test_qwen3_slot_fractions_bitwise_identical_full_size(qwen3):
     """The pages' invariant at full size: the first 4 layers of the Qwen3 shape at 13, 26, 52 and 128 slots
     (10 / 20 / 40 / 100 %), each from an empty cache on the same token stream, read the same host records
     (one shared store) and must give bitwise identical block inputs and outputs on every layer and step,
-    while their miss counts differ."""
+    while the smallest cache misses more often than the larger ones."""
     mo = qwen3
     L, steps, T = 4, 48, 1
     xs = synth.tokens(mo.seed, 500, T, mo.H, steps, 0.9, BF16)
@@ -291,4 +291,6 @@ def test_qwen3_slot_fractions_bitwise_identical_full_size(qwen3):
         for s in range(steps):
             assert np.array_equal(runs[S][s][0], runs[26][s][0]), (S, s, "x")
             assert np.array_equal(runs[S][s][1], runs[26][s][1]), (S, s, "y")
-    assert misses[13] > misses[26] > misses[52] >= misses[128]
+    # over these 48 steps 26 slots may already hold every expert the 4 layers use: then only the
+    # compulsory misses remain from 26 slots up
+    assert misses[13] > misses[26] >= misses[52] >= misses[128]

@@ -542,6 +542,88 @@ def test_host_cold_experts_parity(wdt, E, S, k, H, F, Ts, shared):
         gl.close()
 
 
+@pytest.mark.parametrize("wdt,E,S,k,H,F,Ts,shared,q", [
+    (1, 32, 8, 4, 512, 256, [9, 3, 16, 1], False, 128),   # half of the staged misses on the host
+    (2, 16, 6, 4, 256, 256, [5, 70, 2], True, 256),       # fp8 + shared; every staged miss on the host
+    (3, 16, 8, 4, 256, 512, [8, 4], True, 77),            # MXFP4
+    (0, 8, 4, 2, 64, 128, [4, 1], False, 0),              # fp32; q = 0: the link carries every staged miss
+    (1, 32, 8, 4, 512, 256, [12, 6], False, None),         # q from the measured host and link times
+])
+def test_split_mode_parity(wdt, E, S, k, H, F, Ts, shared, q):
+    """Split mode switched on mid-stream and off again: of each overflowing call's staged misses the last
+    share q/256 (ascending id) is computed on the host (index S + E + e), the rest is staged over the link;
+    ids, slot ids, copy lists, tables, scores, activation counts and counters bit-exact against the
+    oracle's split rule; layer outputs within tolerance; staged and resident records hold their bytes."""
+    print("split wdt=%d E=%d S=%d k=%d H=%d F=%d Ts=%s q=%s" % (wdt, E, S, k, H, F, Ts, q), flush=True)
+    host, wr, b, sh = make_layer_inputs(53, 0, E, H, F, wdt, 0.0, shared)
+    gl = GpuLayer(E, S, k, H, F, wdt, max(Ts), host, wr, b, shared=sh)
+    ol = oracle.Layer(E, S, k, H, F, wdt, host, wr, b, shared=sh)
+    steps = 14
+    xs = synth.tokens(53, 9, max(Ts), H, steps, 0.0, wdt)
+    st = torch.cuda.current_stream()
+    rb = oracle.record_bytes(wdt, H, F)
+    host_seen = staged_seen = 0
+    try:
+        for s in range(steps):
+            if s == 3:
+                if q is None:
+                    qq, cpu_us, link_us = m.moe_offload_set_cold(gl.h, m.COLD_SPLIT, st)
+                    print("split: host FFN %.1f us, link %.1f us per record -> q %d" % (cpu_us, link_us, qq),
+                          flush=True)
+                    assert cpu_us > 0 and link_us > 0 and 0 <= qq <= 256
+                    assert qq == int(np.floor(256.0 * link_us / (cpu_us + link_us) + 0.5)) or \
+                        abs(qq - 256.0 * link_us / (cpu_us + link_us)) <= 0.5 + 1e-9
+                else:
+                    qq = q
+                    m.moe_offload_set_split(gl.h, q, st)
+                ol.cache.set_split(qq)
+            if s == 11:
+                assert m.moe_offload_set_cold(gl.h, m.COLD_OFF, st)[0] == 0
+                ol.cache.set_cold(False)
+            split = 3 <= s < 11
+            T = Ts[s % len(Ts)]
+            x = np.ascontiguousarray(xs[s][:T])
+            xd = to_dev(x)
+            gl.route(xd, T)
+            gl.ensure(T)
+            gl.copy()
+            if split:
+                with pytest.raises(m.MoeError) as ei:
+                    gl.ffn(xd, T)
+                assert ei.value.code == m.EINVAL
+                m.moe_slot_ffn_host_cold(gl.h, xd, gl.slot_ids, gl.w, T, gl.shared, gl.y, None, gl.xn, st)
+            else:
+                gl.ffn(xd, T)
+            r = ol.step(x)
+            if split:
+                recs = [int(p_[1]) for p_ in r["pairs"]]
+                host_seen += sum(1 for v in recs if v >= S + E)
+                staged_seen += sum(1 for v in recs if S <= v < S + E)
+            compare_call(gl, r, T, r["y64"], oracle_cache=ol.cache)
+            assert np.array_equal(to_np(gl.xn[:T]), oracle.residual(x, to_np(gl.y[:T]), wdt))
+            if r["mode"] == oracle.STAGED:  # the staged records crossed the link, the host's did not need to
+                for e_, v in r["pairs"]:
+                    if S <= v < S + E:
+                        assert np.array_equal(gl.staging_bytes(int(e_), rb), host[int(e_), :rb])
+        stt = gl.stats()
+        c = ol.cache.counters()
+        assert stt["error"] == 0 and stt["cold_misses"] == c["cold"] == host_seen
+        for key in ("calls", "hits", "misses", "staged_calls", "staged_copies"):
+            assert stt[key] == c[key], key
+        if q == 256:
+            assert host_seen > 0 and staged_seen == 0
+        elif q == 0:
+            assert host_seen == 0 and staged_seen > 0
+        elif q is not None:
+            assert host_seen > 0 and staged_seen > 0
+        for s_ in range(S):
+            so, eo, lu = gl.table()
+            if eo[s_] >= 0:
+                assert np.array_equal(gl.slot_bytes(s_, rb), host[eo[s_], :rb])
+    finally:
+        gl.close()
+
+
 def test_host_cold_policy_measures_both_paths():
     """MOE_COLD_AUTO: the host FFN of one record against one record over the link, measured on this box;
     the layer goes cold exactly when the host is faster, and the device flag follows (the next ensure
