@@ -801,16 +801,45 @@ void orc_residual(const void* x, const void* y, int wdt, size_t n, void* out) {
  * once to the activation dtype.  The pages describe no norm; without one the
  * residual stream of a 48-layer chain of gated FFNs with N(0, 0.02) weights
  * grows until it overflows, while the pre-norm block of the model family the
- * configurations are shaped after keeps it bounded. */
+ * configurations are shaped after keeps it bounded.
+ * The norm is glue around the layer, so its arithmetic is fixed here the way
+ * the router logits' is (READING): binary32 throughout, in one order, so that
+ * the activation codes it produces are a definition rather than a tolerance:
+ *   - 256 partial sums; partial i takes the 8-element chunks c = i, i + 256, ...
+ *     in ascending order and accumulates v*v with fused multiply-adds in
+ *     element order;
+ *   - the partials form four groups of 64; within a group, an xor butterfly:
+ *     for o = 32, 16, ..., 1, partial l becomes partial l + partial (l ^ o);
+ *   - the four group sums are added left to right;
+ *   - inv = 1 / sqrt(sum / H + eps), each operation correctly rounded;
+ *   - xn = x * inv in binary32, then rounded once to the activation dtype. */
 void orc_rmsnorm(const void* x, int wdt, int T, int H, double eps, void* out) {
+  const float epsf = (float)eps;
   for (int t = 0; t < T; ++t) {
-    double ss = 0.0;
-    for (int i = 0; i < H; ++i) {
-      double v = load_act(x, wdt, (size_t)t * H + i);
-      ss += v * v;
+    const size_t base = (size_t)t * H;
+    float part[256], grp[4];
+    for (int i = 0; i < 256; ++i) {
+      float ss = 0.0f;
+      for (int c = i; c * 8 < H; c += 256)
+        for (int q = 0; q < 8; ++q) {
+          const float v = (float)load_act(x, wdt, base + (size_t)c * 8 + q);
+          ss = fmaf(v, v, ss);
+        }
+      part[i] = ss;
     }
-    double inv = 1.0 / sqrt(ss / H + eps);
-    for (int i = 0; i < H; ++i) store_act(out, wdt, (size_t)t * H + i, load_act(x, wdt, (size_t)t * H + i) * inv);
+    for (int g = 0; g < 4; ++g) {
+      float a[64], b[64];
+      memcpy(a, part + 64 * g, sizeof a);
+      for (int o = 32; o >= 1; o >>= 1) {
+        for (int l = 0; l < 64; ++l) b[l] = a[l] + a[l ^ o];
+        memcpy(a, b, sizeof a);
+      }
+      grp[g] = a[0];
+    }
+    const float tot = ((grp[0] + grp[1]) + grp[2]) + grp[3];
+    const float inv = 1.0f / sqrtf(tot / (float)H + epsf);
+    for (int i = 0; i < H; ++i)
+      store_act(out, wdt, base + i, (double)((float)load_act(x, wdt, base + i) * inv));
   }
 }
 
