@@ -13,14 +13,22 @@
  *              the routing nor the numerics).
  *   [freetoken] FreeToken issue #677 "prefetch the next layer's experts from a router
  *              lookahead during offloaded decode", section "Proposal"
- *              (Lookahead, Install, Correctness constraint).
+ *              (Lookahead, Install, Correctness constraint), and "Measured" (the
+ *              scored-eviction baseline).
+ *   [moe-inf]  MoE-Infinity README, "Overview" and "Key Features" (the
+ *              activation-aware expert cache).
+ *   [npu]      npu-offload README, intro, "Architecture" and "Results" (cold
+ *              experts computed by the host CPU; profile-guided placement).
  * Where the pages are silent the plainest reading is taken; each such reading is
  * marked READING below and listed in the design notes.
  *
  * Precision: every floating-point step runs in double, except the router
- * logits.  Their fp32 value decides an integer (the top-k ids), so they are
- * computed in the GPU kernel's precision with one fixed summation order
- * (READING, see orc_router_logits); the order is part of the specification.
+ * logits and the pre-norm.  The logits' fp32 value decides an integer (the
+ * top-k ids), so they are computed in the GPU kernel's precision with one
+ * fixed summation order (READING, see orc_router_logits); the order is part of
+ * the specification.  The pre-norm is glue outside the method whose output is
+ * a quantised code; its binary32 order is fixed the same way (READING, see
+ * orc_rmsnorm).
  *
  * Build: gcc -O2 -ffp-contract=off (no fast-math; denormals kept).
  */
