@@ -105,6 +105,8 @@ def main():
     ap.add_argument("--cpu-rates", action="store_true", help="also the CPU oracle's own rates on all threads and one")
     ap.add_argument("--prefetch-only", action="store_true",
                     help="only the lookahead-prefetch comparison on the 48-layer workload (its own JSON line)")
+    ap.add_argument("--mixtral-only", action="store_true",
+                    help="only the Mixtral-8x7B-shaped layer (its own JSON line)")
     ap.add_argument("--split-only", action="store_true",
                     help="only the batch-32 eager comparison of the link, split and host-cold modes (its own JSON line)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -141,6 +143,12 @@ def main():
         print(json.dumps({"workload": "deepseek-v3-shaped offloaded MoE layer, fp8 e4m3 experts with 128x128 "
                                       "scales: 256 experts + shared, top-8, hidden 7168, moe ffn 2048, 26 slots",
                           "deepseek_v3_layer": deepseek_layer(args, m, torch)}), flush=True)
+        return
+
+    if args.mixtral_only:
+        print(json.dumps({"workload": "mixtral-8x7b-shaped offloaded MoE layer: 8 experts, top-2, hidden 4096, "
+                                      "moe ffn 14336, bf16, 2/4/6 slots",
+                          "mixtral_8x7b_layer": mixtral_layer(args, m, torch)}), flush=True)
         return
 
     if args.mxfp4_only:
@@ -647,7 +655,7 @@ def layer_steps(m, torch, h, wr, b, shared, xs, T, steps, warm):
 
 def mixtral_layer(args, m, torch):
     """Mixtral-8x7B-shaped layer (8 experts, top-2, hidden 4096, ffn 14336, bf16, uniform router): decode at
-    2, 4 and 6 slots."""
+    2, 4 and 6 slots, and at 6 slots both FFN kernel pairs on calls of 8 to 64 tokens."""
     import numpy as np
     import synth
     E, k, H, F, seed = 8, 2, 4096, 14336, args.seed + 7
@@ -657,24 +665,36 @@ def mixtral_layer(args, m, torch):
     b_d = torch.from_numpy(b).to(dev)
     out = {}
     for S in (2, 4, 6):
-        h = m.moe_offload_create(E, S, H, F, k, m.BF16, 65, 0, 0)
+        h = m.moe_offload_create(E, S, H, F, k, m.BF16, 64, 0, 0)
         p, stride, rb = m.moe_offload_host_records(h)
         synth.fill_records(seed, 0, 0, E, H, F, synth.BF16, p, stride)
-        for T in (1, 8, 64, 65):
+        for T in (1, 8, 64):
             xs = synth.tokens(seed, 50 + T, T, H, 24, 0.9, synth.BF16)
             xs_d = torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16).to(dev)
             r = layer_steps(m, torch, h, wr_d, b_d, None, xs_d, T, 16, 8)
             out["S%d_T%d" % (S, T)] = r
             log("mixtral S=%d T=%d: %.1f tok/s, %.3f misses/call, copy %s GB/s" %
                 (S, T, r["tokens_per_s"], r["misses_per_call"], r["copy_GBps"]))
+        if S == 6:
+            # the pair-dot decode kernels against the grouped MFMA GEMM on the same calls (2 to 16 pairs per
+            # expert): FFN kernel time (grouping, gate/up, down) per pair
+            paths = {}
+            for T in (8, 16, 32, 48, 64):
+                xs = synth.tokens(seed, 50 + T, T, H, 24, 0.9, synth.BF16)
+                xs_d = torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16).to(dev)
+                row = {"pairs_per_expert": T * k / E}
+                for name, path in (("pairdot", m.FFN_DECODE), ("mfma", m.FFN_GEMM)):
+                    m.moe_offload_set_ffn_path(h, path)
+                    r = layer_steps(m, torch, h, wr_d, b_d, None, xs_d, T, 8, 4)
+                    row[name + "_us_per_pair"] = round(sum(r["kernels_us"].get(kk, 0) for kk in
+                                                           ("group", "gateup", "down")) / (T * k), 3)
+                m.moe_offload_set_ffn_path(h, m.FFN_AUTO)
+                row["auto"] = "mfma" if T * k >= 12 * E else "pairdot"
+                paths["T%d" % T] = row
+                log("mixtral T=%d: pair-dot %.2f us/pair, MFMA %.2f us/pair (auto: %s)" %
+                    (T, row["pairdot_us_per_pair"], row["mfma_us_per_pair"], row["auto"]))
+            out["ffn_paths_S6"] = paths
         m.moe_offload_destroy(h)
-    # 64 tokens (16 per expert) take the pair-dot decode kernels, 65 the grouped MFMA GEMM: FFN kernel time per pair
-    out["mfma_vs_pairdot_16_tokens_per_expert"] = {
-        "S%d" % S: {"pairdot_T64_us_per_pair": round(sum(out["S%d_T64" % S]["kernels_us"].get(kk, 0) for kk in
-                                                             ("group", "gateup", "down")) / (64 * k), 4),
-                    "mfma_T65_us_per_pair": round(sum(out["S%d_T65" % S]["kernels_us"].get(kk, 0) for kk in
-                                                          ("group", "gateup", "down")) / (65 * k), 4)}
-        for S in (2, 4, 6)}
     return out
 
 

@@ -93,6 +93,7 @@ struct moe_offload {
   int32_t* scratch_i32;      // small device scratch (distinct count etc.)
   int32_t* pinned_i32;       // small pinned host scratch
   moe::Prof* prof;           // per-kernel timing, created on first enable
+  int ffn_path;              // MOE_FFN_AUTO / DECODE / GEMM (moe_offload_set_ffn_path)
   // host-computed cold experts (allocated when the cold mode is first switched on)
   bool cold_on;              // host mirror of the device word: nonzero
   bool cold_split;           // ... and in split mode (the copies run beside the host's share)
@@ -172,6 +173,8 @@ void* scratch_ptr(int device);
 // device buffer); *bytes gets its size.
 FfnWork ffn_work_in(const moe_offload* h, int T, void* base, size_t* bytes);
 bool ffn_reads_through(const moe_offload* h, int T);
+// true when a call of T tokens runs the grouped GEMM rather than the decode kernels
+bool ffn_uses_gemm(const moe_offload* h, int T);
 // Decode control step in one workgroup: top-k of h->logits (launch_logits first),
 // ensure, and the FFN grouping.  With hn (max_n > 0): also the top-k of
 // hn->logits (the lookahead prediction, ids to pred) and the prefetch install

@@ -12,15 +12,16 @@
 //              The decode chain builds the same descriptor in its control
 //              workgroup instead.  A single token needs none: its k records
 //              are distinct, so each (t, j) pair is its own work item.
-//   gate/up + SiLU and down, one of three kernel pairs by call size:
-//     T <= kDecodeMaxT (decode): k_gateup_vec / k_down_vec, one wavefront per
+//   gate/up + SiLU and down, one of three kernel pairs by call size
+//   (ffn_uses_gemm):
+//     few pairs per record, T <= kDecodeMaxT (decode): k_gateup_vec / k_down_vec, one wavefront per
 //              (record, 4 or 8 weight rows); the rows are loaded once, held in
 //              registers and met by every token of the record with the bf16
 //              pair-dot instruction.  Few tokens per record make this a
 //              weight-streaming (HBM) problem, not a matrix-core one.
 //              T = 1: k_gateup_one / k_down_one, the same rows per wavefront
 //              for one activation row, work item (choice j, rows).
-//     larger T (prefill): k_gemm_gu / k_gemm_dn, a grouped GEMM whose work
+//     larger T (prefill), or many pairs per record: k_gemm_gu / k_gemm_dn, a grouped GEMM whose work
 //              items are (tile of 64 pairs of one record, 64 weight rows), K
 //              slices staged through LDS, bf16 MFMA 16x16x32 tiles.
 //     fp32 records: plain fp32 FMA kernels, work item (record, 64 rows).
@@ -1298,7 +1299,27 @@ hipError_t launch_cold_combine(moe_offload* h, const void* x, const int32_t* slo
 // with at most kFillPairs pairs (the decode kernels, the copy list in one load
 // per wavefront)
 bool ffn_reads_through(const moe_offload* h, int T) {
-  return h->dtype != MOE_F32 && (T == 1 || (T <= kDecodeMaxT && T * h->k <= kFillPairs));
+  return h->dtype != MOE_F32 && !ffn_uses_gemm(h, T) && (T == 1 || (T <= kDecodeMaxT && T * h->k <= kFillPairs));
+}
+
+// Kernel pair of a multi-token call.  The decode kernels meet each weight row
+// once per 8-token group of a record, the grouped GEMM once per 64-pair tile,
+// so with many pairs per record the GEMM streams fewer bytes; the crossover
+// was measured per weight format (FFN time per pair of both pairs on the same
+// calls, every expert resident): bf16 between 11 and 12 pairs per record
+// (Mixtral shape), MXFP4 between 2 and 3 depending on the shape, fp8 below 1.3
+// (its decode kernels widen every code once per token group); fp8 switches at
+// 2 all the same, so decode batches below that keep read-through.  The rule
+// reads T * k / E, the fewest pairs per record a call can have on average, so
+// it depends only on the layer's shape and the call's token count (never on S
+// or on which experts are resident): every output bit stays independent of the
+// slot count.
+bool ffn_uses_gemm(const moe_offload* h, int T) {
+  if (h->dtype == MOE_F32 || T == 1) return false;
+  if (T > kDecodeMaxT || h->ffn_path == MOE_FFN_GEMM) return true;
+  if (h->ffn_path == MOE_FFN_DECODE) return false;
+  const int per_record = h->dtype == MOE_FP8_E4M3_B128 ? 2 : (h->dtype == MOE_MXFP4 ? 3 : 12);
+  return T * h->k >= per_record * h->E;
 }
 
 // ------------------------------------------------------------------ scratch workspace
@@ -1389,7 +1410,7 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
     launch_k(h, MOE_K_GROUP, k_group, dim3(1), dim3(kBlock), 0, s, a);
   }
   const int wf = h->dtype;  // weight format
-  // gate/up and down: fp32 FMA kernels, the decode kernels (T <= kDecodeMaxT), or the MFMA kernels
+  // gate/up and down: fp32 FMA kernels, the decode kernels, or the MFMA kernels (ffn_uses_gemm)
   void (*gu)(FfnArgs) = nullptr;
   void (*dn)(FfnArgs) = nullptr;
   dim3 g1, g2, b1, b2;
@@ -1399,7 +1420,7 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
     g1 = dim3(std::min(max_items_r * (h->F / kF32Rows), 2048));
     g2 = dim3(std::min(max_items_r * (h->H / kF32Rows), 2048));
     b1 = b2 = dim3(256);
-  } else if (T <= kDecodeMaxT) {  // one wavefront per work item
+  } else if (!ffn_uses_gemm(h, T)) {  // one wavefront per work item
     const bool one = a.pair_items != 0;
     gu = wf == kFp8 ? gateup_decode<kFp8>(one, fill, h->H)
                     : (wf == kMx4 ? gateup_decode<kMx4>(one, fill, h->H) : gateup_decode<kBf16>(one, fill, h->H));

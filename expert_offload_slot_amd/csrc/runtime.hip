@@ -491,6 +491,14 @@ int moe_copy_prefetch(moe_offload* h, void* stream) {
   return MOE_OK;
 }
 
+int moe_offload_set_ffn_path(moe_offload* h, int32_t path) {
+  if (int rc = check_handle(h)) return rc;
+  if (path != MOE_FFN_AUTO && path != MOE_FFN_DECODE && path != MOE_FFN_GEMM)
+    return fail(MOE_EINVAL, "moe_offload_set_ffn_path: path %d", path);
+  h->ffn_path = path;
+  return MOE_OK;
+}
+
 // the host side's buffers and the split mode's stream and events, once (the device must be current)
 static int cold_buffers(moe_offload* h) {
   if (h->cold_stream) return MOE_OK;

@@ -279,6 +279,25 @@ int moe_copy_misses(moe_offload* h, void* stream);
 int moe_slot_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int32_t T,
                  const void* shared_record, void* y, const void* residual, void* x_next, void* stream);
 
+/* Kernel pair of the expert FFN for calls of 2 to 64 tokens (xinfer-ai docs,
+ * "How it works": decode and prefill are the same grouped FFN; which kernels
+ * run is an implementation choice that never changes which experts are used).
+ *   MOE_FFN_AUTO (the default): the grouped MFMA GEMM when T * k >= c * E, with
+ *     c = 12 for bf16, 2 for fp8 and 3 for MXFP4 (the measured crossovers: the
+ *     decode kernels read each weight row once per 8-token group of a record,
+ *     the GEMM once per 64-pair tile), else the pair-dot decode kernels;
+ *   MOE_FFN_DECODE: always the decode kernels;  MOE_FFN_GEMM: always the GEMM.
+ * Calls of one token always take the single-token kernels, calls above 64
+ * tokens the GEMM, fp32 layers their fp32 kernels.  The choice depends on T
+ * and the handle only, never on S or on residency, so outputs stay bitwise
+ * independent of the slot count; the two pairs differ in summation order, so
+ * their outputs agree within the usual tolerance, not bit for bit.  Only the
+ * decode kernels read missed records through (decode chain).  Host-side
+ * setting; a decode chain keeps the kernels it captured at its first run.
+ * Errors: MOE_EINVAL (unknown path). */
+enum { MOE_FFN_AUTO = 0, MOE_FFN_DECODE = 1, MOE_FFN_GEMM = 2 };
+int moe_offload_set_ffn_path(moe_offload* h, int32_t path);
+
 /* Host-computed cold experts (npu-offload README, intro and "Architecture":
  * hot experts stay in accelerator memory, the host CPU computes the cold ones
  * from host DRAM in parallel, only activations cross the link; "Results", where

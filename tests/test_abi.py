@@ -67,6 +67,8 @@ def test_null_handles_are_rejected_before_any_device_call():
         "moe_slot_ffn_host_cold": (None, None, None, None, 1, None, None, None, None, None),
         "moe_slot_ffn_noalloc": (None, None, None, None, 1, None, None, None, None, None),
         "moe_offload_set_cold": (None, 1, None, None, None, None),
+        "moe_offload_set_split": (None, 128, None),
+        "moe_offload_set_ffn_path": (None, 0),
     }
     for name, args in calls.items():
         rc = getattr(L, name)(*args)

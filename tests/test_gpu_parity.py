@@ -14,8 +14,8 @@ import torch
 import expert_offload_slot_amd as m
 import oracle
 import synth
-from gpu_harness import (GpuLayer, compare_call, d2h, h2d, make_layer_inputs, oracle_policy, row_rel_err, to_dev,
-                         to_np)
+from gpu_harness import (TOL, GpuLayer, compare_call, d2h, h2d, make_layer_inputs, oracle_policy, row_rel_err,
+                         to_dev, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -622,6 +622,51 @@ def test_split_mode_parity(wdt, E, S, k, H, F, Ts, shared, q):
                 assert np.array_equal(gl.slot_bytes(s_, rb), host[eo[s_], :rb])
     finally:
         gl.close()
+
+
+@pytest.mark.parametrize("wdt,E,S,k,H,F,Ts,shared", [
+    (1, 8, 4, 2, 512, 256, [8, 24, 48, 64], False),   # bf16: the automatic rule takes the GEMM from 12 pairs per expert
+    (2, 16, 6, 4, 256, 256, [4, 8, 16], True),        # fp8 + shared: from 2
+    (3, 16, 8, 4, 256, 512, [8, 12, 32], False),      # MXFP4: from 3
+])
+def test_ffn_path_choice_parity(wdt, E, S, k, H, F, Ts, shared):
+    """The same calls through the decode kernels, the grouped GEMM and the automatic choice: each within
+    tolerance of the oracle; the automatic choice bitwise equal to the pair its rule names; and under the
+    automatic choice the outputs at S slots bitwise equal those of a layer holding every expert."""
+    print("ffn path wdt=%d E=%d S=%d k=%d H=%d F=%d Ts=%s" % (wdt, E, S, k, H, F, Ts), flush=True)
+    host, wr, b, sh = make_layer_inputs(57, 0, E, H, F, wdt, 0.0, shared)
+    st = torch.cuda.current_stream()
+    layers = [GpuLayer(E, S_, k, H, F, wdt, max(Ts), host, wr, b, shared=sh) for S_ in (S, E)]
+    ol = oracle.Layer(E, E, k, H, F, wdt, host, wr, b, shared=sh)
+    xs = synth.tokens(57, 3, max(Ts), H, len(Ts), 0.0, wdt)
+    per = {1: 12, 2: 2, 3: 3}[wdt]
+    try:
+        for s, T in enumerate(Ts):
+            x = np.ascontiguousarray(xs[s][:T])
+            xd = to_dev(x)
+            r = ol.step(x)
+            outs = {}
+            for li, gl in enumerate(layers):
+                gl.route(xd, T)
+                gl.ensure(T)
+                gl.copy()
+                for path in (m.FFN_DECODE, m.FFN_GEMM, m.FFN_AUTO):
+                    m.moe_offload_set_ffn_path(gl.h, path)
+                    gl.ffn(xd, T)
+                    y = to_np(gl.y[:T])
+                    assert row_rel_err(y, r["y64"], wdt) <= TOL[wdt], (T, li, path)
+                    outs[(li, path)] = y
+            want = m.FFN_GEMM if T * k >= per * E else m.FFN_DECODE
+            assert np.array_equal(outs[(0, m.FFN_AUTO)], outs[(0, want)]), T
+            for path in (m.FFN_DECODE, m.FFN_GEMM, m.FFN_AUTO):  # slot-count invariance on every path
+                assert np.array_equal(outs[(0, path)], outs[(1, path)]), (T, path)
+        for gl in layers:
+            assert gl.stats()["error"] == 0
+        with pytest.raises(m.MoeError):
+            m.moe_offload_set_ffn_path(layers[0].h, 3)
+    finally:
+        for gl in layers:
+            gl.close()
 
 
 def test_host_cold_policy_measures_both_paths():
