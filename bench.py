@@ -679,7 +679,7 @@ def mixtral_layer(args, m, torch):
             # the pair-dot decode kernels against the grouped MFMA GEMM on the same calls (2 to 16 pairs per
             # expert): FFN kernel time (grouping, gate/up, down) per pair
             paths = {}
-            for T in (8, 16, 32, 48, 64):
+            for T in (8, 16, 24, 32, 64):
                 xs = synth.tokens(seed, 50 + T, T, H, 24, 0.9, synth.BF16)
                 xs_d = torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16).to(dev)
                 row = {"pairs_per_expert": T * k / E}
@@ -689,7 +689,7 @@ def mixtral_layer(args, m, torch):
                     row[name + "_us_per_pair"] = round(sum(r["kernels_us"].get(kk, 0) for kk in
                                                            ("group", "gateup", "down")) / (T * k), 3)
                 m.moe_offload_set_ffn_path(h, m.FFN_AUTO)
-                row["auto"] = "mfma" if T * k >= 12 * E else "pairdot"
+                row["auto"] = "mfma" if T * k >= 5 * E else "pairdot"
                 paths["T%d" % T] = row
                 log("mixtral T=%d: pair-dot %.2f us/pair, MFMA %.2f us/pair (auto: %s)" %
                     (T, row["pairdot_us_per_pair"], row["mfma_us_per_pair"], row["auto"]))

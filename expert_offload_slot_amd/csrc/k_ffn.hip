@@ -52,6 +52,17 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte moves through a native vector: a uint4 struct copy becomes a memcpy,
+// which keeps an array of them in private (scratch) memory instead of registers
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st16(void* p, const uint4& v) {
+  *reinterpret_cast<u32x4*>(p) = u32x4{v.x, v.y, v.z, v.w};
+}
 
 struct FfnArgs {
   const void* x;
@@ -306,10 +317,9 @@ struct Slice {
       for (int q = 0; q < NA; ++q) {
         const int row = tid / TW + RW * q;
         if (W == kBf16) {
-          a[NA * m + q] =
-              *reinterpret_cast<const uint4*>(w0 + m * mat + ((uint64_t)row * K + k0 + (tid % TW) * 8) * 2);
+          a[NA * m + q] = ld16(w0 + m * mat + ((uint64_t)row * K + k0 + (tid % TW) * 8) * 2);
         } else if (W == kFp8) {
-          a[NA * m + q] = *reinterpret_cast<const uint4*>(w0 + m * mat + (uint64_t)row * K + k0 + (tid % TW) * 16);
+          a[NA * m + q] = ld16(w0 + m * mat + (uint64_t)row * K + k0 + (tid % TW) * 16);
         } else {
           const uint2 v =
               *reinterpret_cast<const uint2*>(w0 + m * mat + ((uint64_t)row * K + k0) / 2 + (tid % TW) * 8);
@@ -320,7 +330,7 @@ struct Slice {
       }
     }
 #pragma unroll
-    for (int q = 0; q < NB; ++q) b[q] = bp[q] ? *reinterpret_cast<const uint4*>(bp[q] + k0) : make_uint4(0, 0, 0, 0);
+    for (int q = 0; q < NB; ++q) b[q] = bp[q] ? ld16(bp[q] + k0) : make_uint4(0, 0, 0, 0);
   }
 
   __device__ __forceinline__ void store(uint16_t (*As)[R][kLdsRow], uint16_t (*Bs)[kLdsRow]) const {
@@ -331,19 +341,18 @@ struct Slice {
       for (int q = 0; q < NA; ++q) {
         const int row = tid / TW + RW * q;
         if (W == kBf16) {
-          *reinterpret_cast<uint4*>(&As[m][row][(tid % TW) * 8]) = a[NA * m + q];
+          st16(&As[m][row][(tid % TW) * 8], a[NA * m + q]);
         } else {
           uint4 lo, hi;
           if (W == kFp8) widen16(a[NA * m + q], lo, hi);
           else widen16_fp4(make_uint2(a[NA * m + q].x, a[NA * m + q].y), s[NA * m + q], lo, hi);
-          uint4* d = reinterpret_cast<uint4*>(&As[m][row][(tid % TW) * 16]);
-          d[0] = lo;
-          d[1] = hi;
+          st16(&As[m][row][(tid % TW) * 16], lo);
+          st16(&As[m][row][(tid % TW) * 16 + 8], hi);
         }
       }
     }
 #pragma unroll
-    for (int q = 0; q < NB; ++q) *reinterpret_cast<uint4*>(&Bs[tid / TB + RBT * q][(tid % TB) * 8]) = b[q];
+    for (int q = 0; q < NB; ++q) st16(&Bs[tid / TB + RBT * q][(tid % TB) * 8], b[q]);
   }
 };
 
@@ -1306,7 +1315,7 @@ bool ffn_reads_through(const moe_offload* h, int T) {
 // once per 8-token group of a record, the grouped GEMM once per 64-pair tile,
 // so with many pairs per record the GEMM streams fewer bytes; the crossover
 // was measured per weight format (FFN time per pair of both pairs on the same
-// calls, every expert resident): bf16 between 11 and 12 pairs per record
+// calls, every expert resident): bf16 between 4 and 6 pairs per record
 // (Mixtral shape), MXFP4 between 2 and 3 depending on the shape, fp8 below 1.3
 // (its decode kernels widen every code once per token group); fp8 switches at
 // 2 all the same, so decode batches below that keep read-through.  The rule
@@ -1318,7 +1327,7 @@ bool ffn_uses_gemm(const moe_offload* h, int T) {
   if (h->dtype == MOE_F32 || T == 1) return false;
   if (T > kDecodeMaxT || h->ffn_path == MOE_FFN_GEMM) return true;
   if (h->ffn_path == MOE_FFN_DECODE) return false;
-  const int per_record = h->dtype == MOE_FP8_E4M3_B128 ? 2 : (h->dtype == MOE_MXFP4 ? 3 : 12);
+  const int per_record = h->dtype == MOE_FP8_E4M3_B128 ? 2 : (h->dtype == MOE_MXFP4 ? 3 : 5);
   return T * h->k >= per_record * h->E;
 }
 
