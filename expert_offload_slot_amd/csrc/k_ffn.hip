@@ -442,15 +442,23 @@ __global__ __launch_bounds__(256) void k_gemm_gu(FfnArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     Slice<W, 2, R> sl;
+    // fp8: each slice's two block scales are loaded one slice ahead, before that slice's
+    // weights, so the MFMAs never wait on the loads of the slice in flight
+    float s2[2] = {W == kFp8 ? sc[0] : 1.f, W == kFp8 ? sc[nsc] : 1.f};
     sl.load(w0, mat, sr0, sstride, H, 0, bp);
     for (int kb = 0; kb < nk; ++kb) {
       __syncthreads();  // the previous slice (or item) is no longer read
       sl.store(As, Bs);
       __syncthreads();
+      float s2n[2] = {1.f, 1.f};
+      if (W == kFp8 && kb + 1 < nk) {
+        s2n[0] = sc[((kb + 1) * kGemmK) / 128];
+        s2n[1] = sc[nsc + ((kb + 1) * kGemmK) / 128];
+      }
       if (kb + 1 < nk) sl.load(w0, mat, sr0, sstride, H, (kb + 1) * kGemmK, bp);
-      const float s2[2] = {W == kFp8 ? sc[(kb * kGemmK) / 128] : 1.f,
-                           W == kFp8 ? sc[nsc + (kb * kGemmK) / 128] : 1.f};
       gemm_slice<W == kFp8, 2, R>(As, Bs, s2, acc);
+      s2[0] = s2n[0];
+      s2[1] = s2n[1];
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -500,14 +508,16 @@ __global__ __launch_bounds__(256) void k_gemm_dn(FfnArgs a) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[0][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     Slice<W, 1, R> sl;
+    float s1[1] = {W == kFp8 ? sc[0] : 1.f};  // one slice ahead, as in k_gemm_gu
     sl.load(w0, mat, sr0, 0, F, 0, bp);
     for (int kb = 0; kb < nk; ++kb) {
       __syncthreads();
       sl.store(As, Bs);
       __syncthreads();
+      const float s1n = W == kFp8 && kb + 1 < nk ? sc[((kb + 1) * kGemmK) / 128] : 1.f;
       if (kb + 1 < nk) sl.load(w0, mat, sr0, 0, F, (kb + 1) * kGemmK, bp);
-      const float s1[1] = {W == kFp8 ? sc[(kb * kGemmK) / 128] : 1.f};
       gemm_slice<W == kFp8, 1, R>(As, Bs, s1, acc);
+      s1[0] = s1n;
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
