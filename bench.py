@@ -83,10 +83,11 @@ def measured_traffic():
 
 
 def traced_avg_us(path, kernel):
-    """Average duration of `kernel` over the eager profile pass, from the committed rocprofv3 summary."""
+    """Average duration of `kernel` over all its dispatches in the committed rocprofv3 summary of this command
+    (the copy-kernel chain's graph replays and the eager profile pass run the same kernel on the same calls)."""
     if not os.path.exists(path):
         return None
-    m_ = re.search(r"^eager_pass_avg_us\[%s\]:\s*(\S+)\s*$" % re.escape(kernel), open(path).read(), re.M)
+    m_ = re.search(r"^trace_avg_us\[%s\]:\s*(\S+)\s*$" % re.escape(kernel), open(path).read(), re.M)
     return float(m_.group(1)) if m_ else None
 
 
@@ -105,6 +106,10 @@ def main():
     ap.add_argument("--cpu-rates", action="store_true", help="also the CPU oracle's own rates on all threads and one")
     ap.add_argument("--prefetch-only", action="store_true",
                     help="only the lookahead-prefetch comparison on the 48-layer workload (its own JSON line)")
+    ap.add_argument("--counters-only", action="store_true",
+                    help="only eager passes of the copy-kernel chain at batch 1 (no graph), --prof-steps steps from "
+                         "an empty cache, and the 256 MiB device copy: the workload of the FETCH_SIZE / WRITE_SIZE "
+                         "counter passes (its own JSON line)")
     ap.add_argument("--mixtral-only", action="store_true",
                     help="only the Mixtral-8x7B-shaped layer (its own JSON line)")
     ap.add_argument("--split-only", action="store_true",
@@ -274,6 +279,25 @@ def main():
             m.moe_offload_destroy(h)
         return
 
+    if args.counters_only:
+        c = m.moe_chain_create(handles, wr_d, b_d, T0, 0)
+        m.moe_chain_set_read_through(c, 0)
+        bufs = m.moe_chain_get_buffers(c)
+        xs_c = token_stream(T0, args.prof_steps)
+        for s in range(args.prof_steps):
+            hip.hipMemcpyAsync(bufs["x"], xs_c[s].data_ptr(), T0 * H * 2, 3, stream.cuda_stream)
+            m.moe_chain_run_eager(c, stream)
+        torch.cuda.synchronize()
+        st = stats_sum()
+        assert st["error"] == 0
+        m.moe_chain_destroy(c)
+        print(json.dumps({"workload": "qwen3-30b-a3b-shaped offloaded MoE decode, 48 layers, batch %d: eager passes "
+                                      "of the copy-kernel chain from an empty cache" % T0,
+                          "eager_steps": args.prof_steps, "calls": st["calls"], "misses": st["misses"]}), flush=True)
+        for h in reversed(handles):
+            m.moe_offload_destroy(h)
+        return
+
     if args.split_only:
         print(json.dumps({"workload": "qwen3-30b-a3b-shaped offloaded MoE decode, 48 layers, batch 32, eager "
                                       "entry-point calls: staged misses over the link, split with the host CPU, "
@@ -397,7 +421,9 @@ def main():
                      os.path.relpath(COUNTERS, ROOT),
                      "rocprof": None if traced is None else
                      {"avg_launch_us": traced, "frac": round(gu_alg / (traced * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-                      "source": "%s (rocprofv3 kernel trace of this command's eager pass)" % os.path.relpath(TRACE, ROOT)}},
+                      "source": "%s (rocprofv3 --kernel-trace --stats of this command: every dispatch of the "
+                                "kernel, the copy-kernel chain's graph replays and the eager pass)" %
+                                os.path.relpath(TRACE, ROOT)}},
         "roofline_down": {"bound": "hbm", "kernel": "k_down_one<bf16, 6, false>", "achieved": round(dn_gbps, 1),
                           "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dn_gbps / HBM_PEAK_GBPS, 4),
                           "avg_launch_us": round(dn_ms * 1e3 / dn_n, 3),
