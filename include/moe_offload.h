@@ -497,9 +497,11 @@ int moe_offload_kernel_times(moe_offload* h, moe_kernel_times* out);
  * predicted experts into layer l (every slot-table writer stays on the compute
  * stream).  The installed records move on a separate copy stream, started
  * once layer l-1's own missed records are in hand (after its copy launch; with
- * read-through, after its control step, since its FFN launches fetch them
- * themselves); nothing of layer l that reads slots starts before that copy has
- * finished.  All streams have the default priority.
+ * read-through, after its control step, so it shares the link with that
+ * layer's FFN launches, which fetch its misses themselves; starting it after
+ * those launches instead was measured slower on the same tokens); nothing of
+ * layer l that reads slots starts before that copy has finished.  All streams
+ * have the default priority.
  *
  * The chain owns its activation buffers (device):
  *   x      [L+1][T][H]  x[0] is the step input (caller writes it before run), x[l+1] = x[l] + y[l]
