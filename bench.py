@@ -103,7 +103,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--quick", action="store_true",
                     help="only the batch-1 window, its steady state, the eager profile and the host link")
-    ap.add_argument("--cpu-rates", action="store_true", help="also the CPU oracle's own rates on all threads and one")
+    ap.add_argument("--no-cpu-rates", action="store_true",
+                    help="skip the CPU oracle's own rates on all threads and one (about 15 s)")
     ap.add_argument("--prefetch-only", action="store_true",
                     help="only the lookahead-prefetch comparison on the 48-layer workload (its own JSON line)")
     ap.add_argument("--counters-only", action="store_true",
@@ -512,7 +513,7 @@ def main():
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args, handles, routers, stride, T0)
-        if args.cpu_rates:
+        if not args.no_cpu_rates and not args.quick:
             result["cpu_oracle"] = cpu_oracle_rates(args)
 
     for h in reversed(handles):
@@ -798,11 +799,11 @@ def deepseek_layer(args, m, torch):
     b_d = torch.from_numpy(b).to(dev)
     sh_d = torch.from_numpy(synth.records(seed, 0, 1, H, F, synth.FP8, shared=True)[0]).to(dev)
     out = {}
-    xs = synth.tokens(seed, 60, 16, H, 24, 0.0, synth.BF16)
+    xs = synth.tokens(seed, 60, 16, H, 72, 0.0, synth.BF16)
     xs_d = torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16).to(dev)
-    out["decode_T16"] = layer_steps(m, torch, h, wr_d, b_d, sh_d, xs_d, 16, 8, 4)
+    out["decode_T16"] = layer_steps(m, torch, h, wr_d, b_d, sh_d, xs_d, 16, 64, 8)
     log("deepseek decode T=16: %.1f tok/s, %d/%d calls staged" % (out["decode_T16"]["tokens_per_s"],
-                                                                  out["decode_T16"]["staged_calls"], 8))
+                                                                  out["decode_T16"]["staged_calls"], 64))
     T = 2048
     x = synth.tokens(seed, 70, T, H, 1, 0.0, synth.BF16)[0]
     out["prefill_T2048"] = prefill_ffn(m, torch, h, wr_d, b_d, sh_d, x, "bf16 (fp8 codes widened exactly)")
