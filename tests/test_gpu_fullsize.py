@@ -294,3 +294,80 @@ def test_qwen3_slot_fractions_bitwise_identical_full_size(qwen3):
     # over these 48 steps 26 slots may already hold every expert the 4 layers use: then only the
     # compulsory misses remain from 26 slots up
     assert misses[13] > misses[26] >= misses[52] >= misses[128]
+
+
+def test_qwen3_split_mode_full_size(qwen3):
+    """Split mode at full size: the first 8 layers of the Qwen3 shape at batch 32 (nearly every call wider than
+    its 26 slots), entry-point calls per layer with the share q measured per layer (MOE_COLD_SPLIT), teacher-
+    forced: block inputs, ids, slot ids, copy lists (staged records at S + e, host-computed ones at S + E + e),
+    slot tables and counters bit-exact against the oracle's split rule; sampled output rows within 2e-2 of the
+    plain definition from the host records; the residual stream bitwise."""
+    mo = qwen3
+    L, T, steps = 8, 32, 6
+    caches = mo.reset()
+    st = torch.cuda.current_stream()
+    dev = torch.device("cuda", 0)
+    x = [torch.empty((T, mo.H), dtype=torch.bfloat16, device=dev) for _ in range(L + 1)]
+    xn = [torch.empty_like(x[0]) for _ in range(L)]
+    y = [torch.empty_like(x[0]) for _ in range(L)]
+    ids = torch.empty((T, mo.k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, mo.k), dtype=torch.float32, device=dev)
+    sid = torch.empty_like(ids)
+    xs = synth.tokens(mo.seed, 321, T, mo.H, steps, 0.9, BF16)
+    host_seen = 0
+    try:
+        for l in range(L):
+            q, cpu_us, link_us = m.moe_offload_set_cold(mo.handles[l], m.COLD_SPLIT, st)
+            caches[l].set_split(q)
+            log("layer %d: host %.1f us, link %.1f us per record -> q %d" % (l, cpu_us, link_us, q))
+        worst = 0.0
+        for s in range(steps):
+            log("qwen3 split T=%d step %d" % (T, s))
+            x[0].copy_(to_dev(np.ascontiguousarray(xs[s])))
+            for l in range(L):
+                h = mo.handles[l]
+                m.moe_rmsnorm(x[l], xn[l], T, mo.H, BF16, stream=st)
+                m.moe_route_topk(h, xn[l], mo.wr[l], mo.b[l], T, ids, w, st)
+                m.moe_slot_ensure(h, ids, T, sid, st)
+                m.moe_copy_misses(h, st)
+                m.moe_slot_ffn_host_cold(h, xn[l], sid, w, T, None, y[l], x[l], x[l + 1], st)
+                torch.cuda.synchronize()
+                # teacher-forced oracle for this layer
+                gx = d2h(x[l].data_ptr(), T * mo.H * 2, np.uint16).reshape(T, mo.H)
+                gxn = d2h(xn[l].data_ptr(), T * mo.H * 2, np.uint16).reshape(T, mo.H)
+                assert np.array_equal(gxn, oracle.rmsnorm(gx, BF16)), (s, l)
+                wr, b = mo.routers[l]
+                oids, ow, _ = oracle.route(gxn, wr, b, mo.k, BF16)
+                assert np.array_equal(oids, d2h(ids.data_ptr(), T * mo.k * 4, np.int32).reshape(T, mo.k)), (s, l)
+                assert np.abs(d2h(w.data_ptr(), T * mo.k * 4, np.float32).reshape(T, mo.k) - ow).max() <= 1e-5
+                osid, mode, pairs = caches[l].ensure(oids)
+                assert np.array_equal(osid, d2h(sid.data_ptr(), T * mo.k * 4, np.int32).reshape(T, mo.k)), (s, l)
+                (gmode, gpairs), _, (so, eo, lu, sc) = layer_lists(mo, l)
+                assert gmode == mode and np.array_equal(gpairs, pairs), (s, l, gmode, mode)
+                host_seen += int((pairs[:, 1] >= mo.S + mo.E).sum()) if len(pairs) else 0
+                oso, oeo, olu, _ = caches[l].state()
+                assert np.array_equal(so, oso) and np.array_equal(eo, oeo) and np.array_equal(lu, olu), (s, l)
+                gy = d2h(y[l].data_ptr(), T * mo.H * 2, np.uint16).reshape(T, mo.H)
+                if l in (0, 5):
+                    toks = sorted({(t + 5 * s) % T for t in (0, 11, 31)})
+                    _, y64 = oracle.ffn(gxn[toks], BF16, mo.H, mo.F, oracle.host_records(mo.hosts[l], oids[toks]),
+                                        ow[toks], want_f64=True)
+                    err = row_rel_err(gy[toks], y64, BF16)
+                    assert err <= 2e-2, (s, l, err)
+                    worst = max(worst, err)
+                gx1 = d2h(x[l + 1].data_ptr(), T * mo.H * 2, np.uint16).reshape(T, mo.H)
+                assert np.array_equal(gx1, oracle.residual(gx, gy, BF16)), (s, l)
+        for l in range(L):
+            stt = m.moe_offload_stats(mo.handles[l])
+            c = caches[l].counters()
+            assert stt["error"] == 0
+            for key in ("calls", "hits", "misses", "staged_calls", "staged_copies"):
+                assert stt[key] == c[key], (l, key)
+            assert stt["cold_misses"] == c["cold"], l
+        assert host_seen > 0
+        log("qwen3 split: %d steps x %d layers bit-exact, %d host-computed records, sampled rows within %.2e" %
+            (steps, L, host_seen, worst))
+    finally:
+        for l in range(L):
+            m.moe_offload_set_cold(mo.handles[l], m.COLD_OFF, st)
+        mo.reset()
