@@ -11,8 +11,9 @@
 //   phase 1: (cold expert, block of F rows)  gate/up dot products, h = silu(g) * u
 //   phase 2: (cold expert, block of H rows)  down dot products into the output rows
 // Dot products accumulate in fp32 over 16 interleaved lanes: with AVX-512 (picked
-// when the library loads) one register per token, fused multiply-adds, codes
-// widened in registers; otherwise the same sums in portable C++.  A persistent
+// when the library loads) two weight rows at a time, one register per (row,
+// token), fused multiply-adds, codes widened in registers; otherwise the same sums
+// in portable C++.  A persistent
 // pool of worker threads claims blocks from an atomic counter.
 #include <immintrin.h>
 #include <math.h>
@@ -22,6 +23,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <condition_variable>
 #include <functional>
 #include <mutex>
@@ -146,99 +148,152 @@ MOE_AVX512 inline __m512 ld_e2m1(const uint8_t* w, __m512 table, __m512 s) {
   return _mm512_mul_ps(_mm512_permutexvar_ps(codes, table), s);
 }
 
-template <int NT, typename Load>
-MOE_AVX512 inline void dot_blocks(const Load& ld, int C, int block, const float* sc, const float* const* a,
+// NR weight rows (ld(r, c): 16 weights of row r from column c) against NT activation
+// rows: each activation chunk is loaded once for the NR rows, so with two rows the
+// loop issues 10 loads per 16 fused multiply-adds instead of 9 per 8.  Every (row,
+// token) sum keeps its own register and the same order as one row at a time.
+template <int NR, int NT, typename Load, typename Scale>
+MOE_AVX512 inline void dot_blocks(const Load& ld, const Scale& scale, int C, int block, const float* const* a,
                                   float* acc) {
-  float out[NT] = {};
+  float out[NR][NT] = {};
   for (int c0 = 0; c0 < C; c0 += block) {
-    __m512 l[NT];
-    for (int t = 0; t < NT; ++t) l[t] = _mm512_setzero_ps();
+    __m512 l[NR][NT];
+    for (int r = 0; r < NR; ++r)
+      for (int t = 0; t < NT; ++t) l[r][t] = _mm512_setzero_ps();
     for (int c = c0; c < c0 + block; c += kLanes) {
-      const __m512 wv = ld(c);
-      for (int t = 0; t < NT; ++t) l[t] = _mm512_fmadd_ps(wv, _mm512_loadu_ps(a[t] + c), l[t]);
+      __m512 av[NT];
+      for (int t = 0; t < NT; ++t) av[t] = _mm512_loadu_ps(a[t] + c);
+      for (int r = 0; r < NR; ++r) {
+        const __m512 wv = ld(r, c);
+        for (int t = 0; t < NT; ++t) l[r][t] = _mm512_fmadd_ps(wv, av[t], l[r][t]);
+      }
     }
-    const float s = sc ? sc[c0 / block] : 1.0f;
-    for (int t = 0; t < NT; ++t) out[t] += s * hsum(l[t]);
+    for (int r = 0; r < NR; ++r) {
+      const float sc = scale(r, c0);
+      for (int t = 0; t < NT; ++t) out[r][t] += sc * hsum(l[r][t]);
+    }
   }
-  for (int t = 0; t < NT; ++t) acc[t] = out[t];
+  for (int r = 0; r < NR; ++r)
+    for (int t = 0; t < NT; ++t) acc[r * kMaxTok + t] = out[r][t];
 }
 
-template <typename Load>
-MOE_AVX512 void dot_any(const Load& ld, int C, int block, const float* sc, const float* const* a, int nt,
+template <int NR, typename Load, typename Scale>
+MOE_AVX512 void dot_any(const Load& ld, const Scale& scale, int C, int block, const float* const* a, int nt,
                         float* acc) {
   switch (nt) {
-    case 1: dot_blocks<1>(ld, C, block, sc, a, acc); return;
-    case 2: dot_blocks<2>(ld, C, block, sc, a, acc); return;
-    case 3: dot_blocks<3>(ld, C, block, sc, a, acc); return;
-    case 4: dot_blocks<4>(ld, C, block, sc, a, acc); return;
-    case 5: dot_blocks<5>(ld, C, block, sc, a, acc); return;
-    case 6: dot_blocks<6>(ld, C, block, sc, a, acc); return;
-    case 7: dot_blocks<7>(ld, C, block, sc, a, acc); return;
-    default: dot_blocks<8>(ld, C, block, sc, a, acc); return;
+    case 1: dot_blocks<NR, 1>(ld, scale, C, block, a, acc); return;
+    case 2: dot_blocks<NR, 2>(ld, scale, C, block, a, acc); return;
+    case 3: dot_blocks<NR, 3>(ld, scale, C, block, a, acc); return;
+    case 4: dot_blocks<NR, 4>(ld, scale, C, block, a, acc); return;
+    case 5: dot_blocks<NR, 5>(ld, scale, C, block, a, acc); return;
+    case 6: dot_blocks<NR, 6>(ld, scale, C, block, a, acc); return;
+    case 7: dot_blocks<NR, 7>(ld, scale, C, block, a, acc); return;
+    default: dot_blocks<NR, 8>(ld, scale, C, block, a, acc); return;
   }
 }
 
-MOE_AVX512 void dot_f32_v(const float* w, int C, const float* const* a, int nt, float* acc) {
-  dot_any([&](int c) MOE_AVX512 { return _mm512_loadu_ps(w + c); }, C, C, nullptr, a, nt, acc);
-}
-MOE_AVX512 void dot_bf16_v(const uint16_t* w, int C, const float* const* a, int nt, float* acc) {
-  dot_any([&](int c) MOE_AVX512 { return ld_bf16(w + c); }, C, C, nullptr, a, nt, acc);
-}
-MOE_AVX512 void dot_fp8_v(const uint8_t* w, const float* sc, int C, const float* const* a, int nt, float* acc) {
-  dot_any([&](int c) MOE_AVX512 { return ld_e4m3(w + c); }, C, 128, sc, a, nt, acc);
-}
-MOE_AVX512 void dot_mx4_v(const uint8_t* w, const uint8_t* sc, int C, const float* const* a, int nt, float* acc) {
-  const __m512 table = _mm512_loadu_ps(g_tab.e2m1);
-  dot_any([&](int c) MOE_AVX512 { return ld_e2m1(w + c / 2, table, _mm512_set1_ps(e8m0_to_f32(sc[c / 32]))); },
-          C, C, nullptr, a, nt, acc);
+// nr (1 or 2) consecutive rows, row stride C weights; acc[r * kMaxTok + t]
+template <int NR>
+MOE_AVX512 void dot_rows_v(const uint8_t* w, int dtype, const void* sc, int C, const float* const* a, int nt,
+                           float* acc) {
+  const auto one = [](int, int) MOE_AVX512 { return 1.0f; };
+  switch (dtype) {
+    case MOE_F32: {
+      const float* wf = reinterpret_cast<const float*>(w);
+      dot_any<NR>([&](int r, int c) MOE_AVX512 { return _mm512_loadu_ps(wf + (size_t)r * C + c); }, one, C, C, a,
+                  nt, acc);
+      return;
+    }
+    case MOE_BF16: {
+      const uint16_t* wb = reinterpret_cast<const uint16_t*>(w);
+      dot_any<NR>([&](int r, int c) MOE_AVX512 { return ld_bf16(wb + (size_t)r * C + c); }, one, C, C, a, nt, acc);
+      return;
+    }
+    case MOE_FP8_E4M3_B128: {  // the rows share their 128-row block's scales
+      const float* s = reinterpret_cast<const float*>(sc);
+      dot_any<NR>([&](int r, int c) MOE_AVX512 { return ld_e4m3(w + (size_t)r * C + c); },
+                  [&](int, int c0) MOE_AVX512 { return s[c0 / 128]; }, C, 128, a, nt, acc);
+      return;
+    }
+    default: {  // MXFP4: E8M0 bytes per 32 columns of each row
+      const uint8_t* s = reinterpret_cast<const uint8_t*>(sc);
+      const __m512 table = _mm512_loadu_ps(g_tab.e2m1);
+      dot_any<NR>([&](int r, int c) MOE_AVX512 {
+                    return ld_e2m1(w + ((size_t)r * C + c) / 2, table,
+                                   _mm512_set1_ps(e8m0_to_f32(s[(size_t)r * (C / 32) + c / 32])));
+                  },
+                  one, C, C, a, nt, acc);
+      return;
+    }
+  }
 }
 
 const bool g_avx512 = __builtin_cpu_supports("avx512f");
 
-void dot_f32(const float* w, int C, const float* const* a, int nt, float* acc) {
-  if (g_avx512) return dot_f32_v(w, C, a, nt, acc);
-  dot_f32_p(w, C, a, nt, acc);
-}
+void dot_f32(const float* w, int C, const float* const* a, int nt, float* acc) { dot_f32_p(w, C, a, nt, acc); }
 void dot_bf16(const uint16_t* w, int C, const float* const* a, int nt, float* acc) {
-  if (g_avx512) return dot_bf16_v(w, C, a, nt, acc);
   dot_dec_p([&](int c) { return bf16_to_f32(w[c]); }, C, C, nullptr, a, nt, acc);
 }
 void dot_fp8(const uint8_t* w, const float* sc, int C, const float* const* a, int nt, float* acc) {
-  if (g_avx512) return dot_fp8_v(w, sc, C, a, nt, acc);
   dot_dec_p([&](int c) { return g_tab.e4m3[w[c]]; }, C, 128, sc, a, nt, acc);
 }
 void dot_mx4(const uint8_t* w, const uint8_t* sc, int C, const float* const* a, int nt, float* acc) {
-  if (g_avx512) return dot_mx4_v(w, sc, C, a, nt, acc);
   dot_dec_p([&](int c) { return g_tab.e2m1[(w[c / 2] >> (4 * (c & 1))) & 15] * e8m0_to_f32(sc[c / 32]); }, C, C,
             nullptr, a, nt, acc);
 }
 
-// row r of matrix m (0 gate, 1 up: [F][H]; 2 down: [H][F]) of a record against nt rows
-void dot_row(const uint8_t* rec, int dtype, int H, int F, int m, int r, const float* const* a, int nt, float* acc) {
+// rows r .. r + nr - 1 (nr 1 or 2; r even when nr is 2) of matrix m (0 gate, 1 up: [F][H];
+// 2 down: [H][F]) of a record against nt activation rows; acc[i * kMaxTok + t]
+void dot_rows(const uint8_t* rec, int dtype, int H, int F, int m, int r, int nr, const float* const* a, int nt,
+              float* acc) {
   const uint64_t n = (uint64_t)F * H;
   const int C = m == 2 ? F : H;
+  const uint8_t* w;
+  const void* sc = nullptr;
   switch (dtype) {
-    case MOE_F32:
-      dot_f32(reinterpret_cast<const float*>(rec) + m * n + (uint64_t)r * C, C, a, nt, acc);
-      return;
-    case MOE_BF16:
-      dot_bf16(reinterpret_cast<const uint16_t*>(rec) + m * n + (uint64_t)r * C, C, a, nt, acc);
-      return;
+    case MOE_F32: w = rec + 4 * (m * n + (uint64_t)r * C); break;
+    case MOE_BF16: w = rec + 2 * (m * n + (uint64_t)r * C); break;
     case MOE_FP8_E4M3_B128: {
       const float* scales = reinterpret_cast<const float*>(rec + 3 * n);
       const uint64_t per = (uint64_t)(F / 128) * (H / 128);
-      dot_fp8(rec + m * n + (uint64_t)r * C, scales + m * per + (uint64_t)(r / 128) * (C / 128), C, a, nt, acc);
-      return;
+      w = rec + m * n + (uint64_t)r * C;
+      sc = scales + m * per + (uint64_t)(r / 128) * (C / 128);
+      break;
     }
     default: {  // MOE_MXFP4
       const uint8_t* scales = rec + 3 * n / 2;
-      dot_mx4(rec + m * n / 2 + (uint64_t)r * C / 2, scales + m * (n / 32) + (uint64_t)r * (C / 32), C, a, nt, acc);
-      return;
+      w = rec + (m * n + (uint64_t)r * C) / 2;
+      sc = scales + m * (n / 32) + (uint64_t)r * (C / 32);
+      break;
+    }
+  }
+  if (g_avx512) {
+    if (nr == 2) dot_rows_v<2>(w, dtype, sc, C, a, nt, acc);
+    else dot_rows_v<1>(w, dtype, sc, C, a, nt, acc);
+    return;
+  }
+  for (int i = 0; i < nr; ++i) {
+    float* o = acc + i * kMaxTok;
+    switch (dtype) {
+      case MOE_F32: dot_f32(reinterpret_cast<const float*>(w) + (uint64_t)i * C, C, a, nt, o); break;
+      case MOE_BF16: dot_bf16(reinterpret_cast<const uint16_t*>(w) + (uint64_t)i * C, C, a, nt, o); break;
+      case MOE_FP8_E4M3_B128: dot_fp8(w + (uint64_t)i * C, reinterpret_cast<const float*>(sc), C, a, nt, o); break;
+      default:
+        dot_mx4(w + (uint64_t)i * C / 2, reinterpret_cast<const uint8_t*>(sc) + (uint64_t)i * (C / 32), C, a, nt,
+                o);
+        break;
     }
   }
 }
 
 // ---------------------------------------------------------------- worker pool
+// A call is one parallel region (both phases, ordered per expert by counters),
+// issued once per layer and lasting a few hundred microseconds, so waking
+// sleeping threads for it (futex round trips, one thread after another) would
+// cost as much as the work.  Workers therefore poll a generation counter for a
+// while after each region, yielding the CPU between polls so that a busy host
+// loses nothing to them, and only then sleep on a condition variable.  The
+// caller works too and waits for the region's last item the same way.
 class Pool {
  public:
   Pool() {
@@ -252,8 +307,8 @@ class Pool {
   ~Pool() {
     {
       std::lock_guard<std::mutex> lk(mu_);
-      stop_ = true;
-      ++gen_;
+      stop_.store(true);
+      gen_.fetch_add(1);
     }
     cv_.notify_all();
     for (auto& t : workers_) t.join();
@@ -264,50 +319,58 @@ class Pool {
   void run(int n, const std::function<void(int)>& fn) {
     if (n <= 0) return;
     std::unique_lock<std::mutex> call(call_mu_);  // one parallel region at a time
-    {
+    fn_ = &fn;
+    n_ = n;
+    next_.store(0);
+    pending_.store((int)workers_.size());
+    gen_.fetch_add(1);  // sequentially consistent: ordered before the sleeper count is read
+    if (sleepers_.load() > 0) {
       std::lock_guard<std::mutex> lk(mu_);
-      fn_ = &fn;
-      n_ = n;
-      next_.store(0);
-      busy_ = (int)workers_.size();
-      ++gen_;
+      cv_.notify_all();
     }
-    cv_.notify_all();
     work();
-    std::unique_lock<std::mutex> lk(mu_);
-    done_cv_.wait(lk, [this] { return busy_ == 0; });
+    while (pending_.load(std::memory_order_acquire) > 0) sched_yield();
     fn_ = nullptr;
   }
 
  private:
+  static constexpr int64_t kPollNs = 2000000;  // poll this long after a region before sleeping
+
   void work() {
     for (int i = next_.fetch_add(1); i < n_; i = next_.fetch_add(1)) (*fn_)(i);
   }
   void loop() {
-    uint64_t seen = 0;
+    uint64_t seen = 0;  // the generation at construction: a region may start before this thread runs
     for (;;) {
-      {
-        std::unique_lock<std::mutex> lk(mu_);
-        cv_.wait(lk, [&] { return gen_ != seen; });
-        seen = gen_;
-        if (stop_) return;
+      const auto t0 = std::chrono::steady_clock::now();
+      uint32_t polls = 0;
+      while (gen_.load(std::memory_order_acquire) == seen) {
+        sched_yield();
+        if ((++polls & 63) == 0 &&
+            std::chrono::duration_cast<std::chrono::nanoseconds>(std::chrono::steady_clock::now() - t0).count() >
+                kPollNs) {
+          std::unique_lock<std::mutex> lk(mu_);
+          sleepers_.fetch_add(1);  // sequentially consistent: ordered before gen_ is read again
+          cv_.wait(lk, [&] { return gen_.load() != seen; });
+          sleepers_.fetch_sub(1);
+          break;
+        }
       }
+      seen = gen_.load(std::memory_order_acquire);
+      if (stop_.load()) return;
       work();
-      {
-        std::lock_guard<std::mutex> lk(mu_);
-        if (--busy_ == 0) done_cv_.notify_one();
-      }
+      pending_.fetch_sub(1, std::memory_order_acq_rel);
     }
   }
   int nthreads_ = 1;
   std::vector<std::thread> workers_;
   std::mutex mu_, call_mu_;
-  std::condition_variable cv_, done_cv_;
+  std::condition_variable cv_;
   const std::function<void(int)>* fn_ = nullptr;
-  int n_ = 0, busy_ = 0;
-  std::atomic<int> next_{0};
-  uint64_t gen_ = 0;
-  bool stop_ = false;
+  int n_ = 0;
+  std::atomic<int> next_{0}, pending_{0}, sleepers_{0};
+  std::atomic<uint64_t> gen_{0};
+  std::atomic<bool> stop_{false};
 };
 
 Pool& pool() {
@@ -353,12 +416,15 @@ void host_cold_ffn(const HostFfnJob& j) {
       const int nt = std::min(kMaxTok, g.count - t0);
       const float* a[kMaxTok];
       for (int t = 0; t < nt; ++t) a[t] = xf.data() + (size_t)(order[g.first + t0 + t] / j.k) * H;
-      for (int f = f0; f < f0 + kRowsF; ++f) {
-        float gv[kMaxTok], uv[kMaxTok];
-        dot_row(rec, j.dtype, H, F, 0, f, a, nt, gv);
-        dot_row(rec, j.dtype, H, F, 1, f, a, nt, uv);
-        for (int t = 0; t < nt; ++t)
-          hbuf[(size_t)(g.first + t0 + t) * F + f] = gv[t] / (1.0f + expf(-gv[t])) * uv[t];
+      for (int f = f0; f < f0 + kRowsF; f += 2) {  // two rows at a time (kRowsF is even)
+        float gv[2 * kMaxTok], uv[2 * kMaxTok];
+        dot_rows(rec, j.dtype, H, F, 0, f, 2, a, nt, gv);
+        dot_rows(rec, j.dtype, H, F, 1, f, 2, a, nt, uv);
+        for (int i = 0; i < 2; ++i)
+          for (int t = 0; t < nt; ++t) {
+            const float gg = gv[i * kMaxTok + t], uu = uv[i * kMaxTok + t];
+            hbuf[(size_t)(g.first + t0 + t) * F + f + i] = gg / (1.0f + expf(-gg)) * uu;
+          }
       }
     }
   });
@@ -371,10 +437,12 @@ void host_cold_ffn(const HostFfnJob& j) {
       const int nt = std::min(kMaxTok, g.count - t0);
       const float* a[kMaxTok];
       for (int t = 0; t < nt; ++t) a[t] = hbuf.data() + (size_t)(g.first + t0 + t) * F;
-      for (int r = r0; r < r1; ++r) {
-        float o[kMaxTok];
-        dot_row(rec, j.dtype, H, F, 2, r, a, nt, o);
-        for (int t = 0; t < nt; ++t) j.out[(size_t)order[g.first + t0 + t] * H + r] = o[t];
+      for (int r = r0; r < r1; r += 2) {  // two rows at a time (H, r0 and r1 are even)
+        const int nr = std::min(2, r1 - r);
+        float o[2 * kMaxTok];
+        dot_rows(rec, j.dtype, H, F, 2, r, nr, a, nt, o);
+        for (int i = 0; i < nr; ++i)
+          for (int t = 0; t < nt; ++t) j.out[(size_t)order[g.first + t0 + t] * H + r + i] = o[i * kMaxTok + t];
       }
     }
   });
