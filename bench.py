@@ -114,7 +114,7 @@ def main():
     ap.add_argument("--mixtral-only", action="store_true",
                     help="only the Mixtral-8x7B-shaped layer (its own JSON line)")
     ap.add_argument("--split-only", action="store_true",
-                    help="only the batch-32 eager comparison of the link, split and host-cold modes (its own JSON line)")
+                    help="only the eager comparison of the link, split and host-cold modes at batch 1, 8 and 32 (its own JSON line)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--mxfp4-only", action="store_true",
                     help="only the same decode chain with MXFP4 expert records (prints its own JSON line)")
@@ -300,9 +300,9 @@ def main():
         return
 
     if args.split_only:
-        print(json.dumps({"workload": "qwen3-30b-a3b-shaped offloaded MoE decode, 48 layers, batch 32, eager "
-                                      "entry-point calls: staged misses over the link, split with the host CPU, "
-                                      "or all on the host",
+        print(json.dumps({"workload": "qwen3-30b-a3b-shaped offloaded MoE decode, 48 layers, batch 1, 8 and 32, eager "
+                                      "entry-point calls: misses over the link, split with the host CPU, or on "
+                                      "the host (from an empty cache, or after a warm-up over the link)",
                           "host_split": host_split_compare(args, m, torch, handles, wr_d, b_d, token_stream)}),
               flush=True)
         for h in reversed(handles):
@@ -819,77 +819,88 @@ def deepseek_layer(args, m, torch):
     return out
 
 
-def host_split_compare(args, m, torch, handles, wr_d, b_d, token_stream, T=32, warm=4, steps=8):
-    """Batch-32 eager decode over the layers with entry-point calls (route, ensure, copy, FFN per layer; at
-    this batch nearly every call needs more experts than its 26 slots): the staged misses all over the host
-    link; split between the link and the host CPU at the share measured per layer (MOE_COLD_SPLIT); and every
-    miss computed on the host (cold mode).  Wall-clock tok/s over `steps` steps after `warm` untimed ones,
-    each mode from empty caches."""
+def host_split_compare(args, m, torch, handles, wr_d, b_d, token_stream, batches=(1, 8, 32), warm=24, steps=8):
+    """Eager decode over the layers with entry-point calls (norm, route, ensure, copy, FFN per layer) at
+    batch 1, 8 and 32, the same `steps` timed steps of one token stream after `warm` untimed ones, each mode
+    from empty caches:
+      link       every miss over the host link (the method as it stands);
+      split      calls wider than the cache send the share of their staged misses measured per layer
+                 (MOE_COLD_SPLIT) to the host CPU;
+      cold       every miss computed on the host from the start (nothing is ever loaded);
+      cold_warm  the warm-up steps with the link (the cache learns), then every miss on the host.
+    Wall-clock tok/s."""
     import numpy as np
     dev = torch.device("cuda", 0)
     st = torch.cuda.current_stream()
-    L = len(handles)
-    ids = torch.empty((T, K_TOP), dtype=torch.int32, device=dev)
-    w = torch.empty((T, K_TOP), dtype=torch.float32, device=dev)
-    sid = torch.empty_like(ids)
-    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    xa, xb, xn = torch.empty_like(y), torch.empty_like(y), torch.empty_like(y)
-    xs = token_stream(T, warm + steps)
     out = {}
-    qs = []
-    try:
-        for mode in ("link", "split", "cold"):
+    for T in batches:
+        ids = torch.empty((T, K_TOP), dtype=torch.int32, device=dev)
+        w = torch.empty((T, K_TOP), dtype=torch.float32, device=dev)
+        sid = torch.empty_like(ids)
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        xa, xb, xn = torch.empty_like(y), torch.empty_like(y), torch.empty_like(y)
+        xs = token_stream(T, warm + steps)
+        res = {}
+        qs = []
+        try:
+            for mode in ("link", "split", "cold", "cold_warm"):
+                for h in handles:
+                    m.moe_offload_set_cold(h, m.COLD_OFF, st)
+                    m.moe_offload_reset(h, st)
+                if mode == "split":
+                    qs = [m.moe_offload_set_cold(h, m.COLD_SPLIT, st) for h in handles]
+                elif mode == "cold":
+                    for h in handles:
+                        m.moe_offload_set_cold(h, m.COLD_ON, st)
+                cold_ffn = [mode in ("split", "cold")]
+
+                def step(s):
+                    a, b = xa, xb
+                    a.copy_(xs[s])
+                    ffn = m.moe_slot_ffn_host_cold if cold_ffn[0] else m.moe_slot_ffn
+                    for l, h in enumerate(handles):  # the decode chain's block: pre-norm, MoE, residual
+                        m.moe_rmsnorm(a, xn, T, H, m.BF16, stream=st)
+                        m.moe_route_topk(h, xn, wr_d[l], b_d[l], T, ids, w, st)
+                        m.moe_slot_ensure(h, ids, T, sid, st)
+                        m.moe_copy_misses(h, st)
+                        ffn(h, xn, sid, w, T, None, y, a, b, st)
+                        a, b = b, a
+
+                for s in range(warm):
+                    step(s)
+                torch.cuda.synchronize()
+                if mode == "cold_warm":
+                    for h in handles:
+                        m.moe_offload_set_cold(h, m.COLD_ON, st)
+                    cold_ffn[0] = True
+                before = [m.moe_offload_stats(h) for h in handles]
+                t0 = time.perf_counter()
+                for s in range(warm, warm + steps):
+                    step(s)
+                torch.cuda.synchronize()
+                dt = time.perf_counter() - t0
+                after = [m.moe_offload_stats(h) for h in handles]
+                assert all(a_["error"] == 0 for a_ in after), [a_["error"] for a_ in after]
+                d = {kk: sum(a_[kk] - b_[kk] for a_, b_ in zip(after, before)) for kk in after[0]}
+                res[mode] = {"tokens_per_s": round(T * steps / dt, 2), "ms_per_step": round(dt * 1e3 / steps, 3),
+                             "link_records_per_token": round((d["misses"] + d["staged_copies"]) / (T * steps), 3),
+                             "host_records_per_token": round(d["cold_misses"] / (T * steps), 3),
+                             "staged_calls": d["staged_calls"], "calls": d["calls"]}
+                log("host-offload b%d %s: %.1f tok/s, %.2f records/token over the link, %.2f on the host" %
+                    (T, mode, res[mode]["tokens_per_s"], res[mode]["link_records_per_token"],
+                     res[mode]["host_records_per_token"]))
+        finally:
             for h in handles:
                 m.moe_offload_set_cold(h, m.COLD_OFF, st)
                 m.moe_offload_reset(h, st)
-            if mode == "split":
-                qs = [m.moe_offload_set_cold(h, m.COLD_SPLIT, st) for h in handles]
-            elif mode == "cold":
-                for h in handles:
-                    m.moe_offload_set_cold(h, m.COLD_ON, st)
-            ffn = m.moe_slot_ffn if mode == "link" else m.moe_slot_ffn_host_cold
-
-            def step(s):
-                a, b = xa, xb
-                a.copy_(xs[s])
-                for l, h in enumerate(handles):  # the decode chain's block: pre-norm, MoE, residual
-                    m.moe_rmsnorm(a, xn, T, H, m.BF16, stream=st)
-                    m.moe_route_topk(h, xn, wr_d[l], b_d[l], T, ids, w, st)
-                    m.moe_slot_ensure(h, ids, T, sid, st)
-                    m.moe_copy_misses(h, st)
-                    ffn(h, xn, sid, w, T, None, y, a, b, st)
-                    a, b = b, a
-
-            for s in range(warm):
-                step(s)
             torch.cuda.synchronize()
-            before = [m.moe_offload_stats(h) for h in handles]
-            t0 = time.perf_counter()
-            for s in range(warm, warm + steps):
-                step(s)
-            torch.cuda.synchronize()
-            dt = time.perf_counter() - t0
-            after = [m.moe_offload_stats(h) for h in handles]
-            assert all(a_["error"] == 0 for a_ in after), [a_["error"] for a_ in after]
-            d = {kk: sum(a_[kk] - b_[kk] for a_, b_ in zip(after, before)) for kk in after[0]}
-            out[mode] = {"tokens_per_s": round(T * steps / dt, 2), "ms_per_step": round(dt * 1e3 / steps, 3),
-                         "link_records_per_token": round((d["misses"] + d["staged_copies"]) / (T * steps), 3),
-                         "host_records_per_token": round(d["cold_misses"] / (T * steps), 3),
-                         "staged_calls": d["staged_calls"], "calls": d["calls"]}
-            log("host-split %s: batch %d, %.1f tok/s, %.2f records/token over the link, %.2f on the host" %
-                (mode, T, out[mode]["tokens_per_s"], out[mode]["link_records_per_token"],
-                 out[mode]["host_records_per_token"]))
-    finally:
-        for h in handles:
-            m.moe_offload_set_cold(h, m.COLD_OFF, st)
-            m.moe_offload_reset(h, st)
-        torch.cuda.synchronize()
-    if qs:
-        q = sorted(x[0] for x in qs)
-        out["split_share_q256"] = {"median": q[len(q) // 2], "min": q[0], "max": q[-1],
-                                   "host_us_per_record_median": round(float(np.median([x[1] for x in qs])), 1),
-                                   "link_us_per_record_median": round(float(np.median([x[2] for x in qs])), 1)}
-    out["split_speedup_vs_link"] = round(out["split"]["tokens_per_s"] / out["link"]["tokens_per_s"], 3)
+        if qs:
+            q = sorted(x[0] for x in qs)
+            res["split_share_q256"] = {"median": q[len(q) // 2], "min": q[0], "max": q[-1],
+                                       "host_us_per_record_median": round(float(np.median([x[1] for x in qs])), 1),
+                                       "link_us_per_record_median": round(float(np.median([x[2] for x in qs])), 1)}
+        res["steps"] = "%d-%d after %d untimed" % (warm, warm + steps - 1, warm)
+        out["batch%d" % T] = res
     return out
 
 
