@@ -297,13 +297,14 @@ def test_qwen3_slot_fractions_bitwise_identical_full_size(qwen3):
 
 
 def test_qwen3_split_mode_full_size(qwen3):
-    """Split mode at full size: the first 8 layers of the Qwen3 shape at batch 32 (nearly every call wider than
-    its 26 slots), entry-point calls per layer with the share q measured per layer (MOE_COLD_SPLIT), teacher-
-    forced: block inputs, ids, slot ids, copy lists (staged records at S + e, host-computed ones at S + E + e),
-    slot tables and counters bit-exact against the oracle's split rule; sampled output rows within 2e-2 of the
-    plain definition from the host records; the residual stream bitwise."""
+    """Split and cold mode at full size: the first 8 layers of the Qwen3 shape at batch 32 (nearly every call
+    wider than its 26 slots), entry-point calls per layer; 6 steps with the share q measured per layer
+    (MOE_COLD_SPLIT), then 3 steps with the warmed cache frozen and every miss on the host (MOE_COLD_ON).
+    Teacher-forced: block inputs, ids, slot ids, copy lists (staged records at S + e, host-computed ones at
+    S + E + e), slot tables and counters bit-exact against the oracle's split and cold rules; sampled output
+    rows within 2e-2 of the plain definition from the host records; the residual stream bitwise."""
     mo = qwen3
-    L, T, steps = 8, 32, 6
+    L, T, steps, split_steps = 8, 32, 9, 6
     caches = mo.reset()
     st = torch.cuda.current_stream()
     dev = torch.device("cuda", 0)
@@ -322,6 +323,10 @@ def test_qwen3_split_mode_full_size(qwen3):
             log("layer %d: host %.1f us, link %.1f us per record -> q %d" % (l, cpu_us, link_us, q))
         worst = 0.0
         for s in range(steps):
+            if s == split_steps:  # freeze the warmed cache: every miss on the host from here on
+                for l in range(L):
+                    assert m.moe_offload_set_cold(mo.handles[l], m.COLD_ON, st)[0] == 1
+                    caches[l].set_cold(True)
             log("qwen3 split T=%d step %d" % (T, s))
             x[0].copy_(to_dev(np.ascontiguousarray(xs[s])))
             for l in range(L):
@@ -365,8 +370,8 @@ def test_qwen3_split_mode_full_size(qwen3):
                 assert stt[key] == c[key], (l, key)
             assert stt["cold_misses"] == c["cold"], l
         assert host_seen > 0
-        log("qwen3 split: %d steps x %d layers bit-exact, %d host-computed records, sampled rows within %.2e" %
-            (steps, L, host_seen, worst))
+        log("qwen3 split/cold: %d steps x %d layers bit-exact, %d host-computed records, sampled rows within %.2e"
+            % (steps, L, host_seen, worst))
     finally:
         for l in range(L):
             m.moe_offload_set_cold(mo.handles[l], m.COLD_OFF, st)
