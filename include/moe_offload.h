@@ -318,6 +318,9 @@ int moe_offload_set_ffn_path(moe_offload* h, int32_t path);
  *         the share q in [0, 256];
  *   cpu_us, link_us (may be NULL): the two measured times per record (AUTO and
  *         SPLIT; 0 otherwise).
+ * Cold mode freezes the resident set (nothing is loaded while it is on), so
+ * switch it on once the cache has warmed over the link or been pinned to a
+ * profiled hot set; from an empty cache every expert stays cold.
  * Host-synchronising on `stream`; the flag is written on the device in stream
  * order, so issue it on the compute stream between calls.  Switching on the
  * first time allocates the pinned host buffers the cold FFN uses (max_tokens
