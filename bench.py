@@ -123,7 +123,7 @@ def main():
                          "(prints its own JSON line)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (requested --gpus %d)" % args.gpus,
+        print("bench.py measures one GPU only: the library has no multi-GPU path (requested --gpus %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 

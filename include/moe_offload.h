@@ -93,7 +93,7 @@ enum {
   MOE_EINVAL = -1,        /* bad argument (shape, size, null pointer, S < k, ...) */
   MOE_ENOMEM = -2,        /* device or pinned host allocation failed */
   MOE_EHIP = -3,          /* a HIP runtime call failed */
-  MOE_EUNSUPPORTED = -4,  /* a dtype or shape this build does not handle */
+  MOE_EUNSUPPORTED = -4,  /* a dtype or shape the library does not handle */
   MOE_EDEVICE = -5        /* a sticky device-side error is set (see stats.error) */
 };
 
@@ -382,7 +382,7 @@ int moe_slot_ffn_noalloc(moe_offload* h, const void* x, const int32_t* slot_ids,
 
 /* Per-token RMS normalisation, out = round(x / sqrt(mean(x^2) + eps)) (fp32 arithmetic,
  * no learned scale): the input of each MoE block in the decode-step chain.  The pages
- * describe no norm; it is this build's reading of the inter-layer glue (a 48-layer
+ * describe no norm; it is the library's reading of the inter-layer glue (a 48-layer
  * residual chain of gated FFNs without one overflows).
  *   x, out: device [T, H], fp32 (MOE_F32) or bf16 (otherwise); H a multiple of 8.
  * Asynchronous, capture-safe. */

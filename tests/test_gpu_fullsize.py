@@ -164,7 +164,7 @@ def check_slot_bytes(mo, layers):
 
 def test_qwen3_mxfp4_chain_full_size():
     """The same 48-layer chain with MXFP4 expert records (2.5 MB each, 15 GB host store), batch 1.  It runs
-    before the module's bf16 model exists and frees its own: both host stores at once exceed what the box
+    before the module's bf16 model exists and frees its own: both host stores at once exceed what the host
     lets a process pin."""
     mo = Qwen3Model(seed=1, wdt=MXFP4)
     try:
