@@ -276,8 +276,8 @@ class Cache:
         lib().orc_cache_set_cold(self._c, 1 if on else 0)
 
     def set_split(self, q):
-        """Split mode: of the misses a call wider than the cache stages for itself, the last
-        round(n * q / 256) (ascending id) are read from their host records instead."""
+        """Split mode: a call wider than the cache reads min(n_staged, round(n_misses * q / 256)) of its staged
+        misses, the last in ascending id, from their host records instead."""
         lib().orc_cache_set_split(self._c, int(q))
 
     def state(self):

@@ -508,12 +508,14 @@ int orc_ensure(orc_cache* c, const int32_t* ids, int n, int k, int32_t* slot_ids
     }
   for (int e = 0; e < E; ++e) /* every routed expert, resident or staged, was activated by this call */
     if (inD[e] && c->act[e] < ORC_SCORE_MAX) c->act[e] += 1;
-  /* split mode: the last n_host of the staged misses (ascending id) are computed on the host */
+  /* split mode (READING): the host takes its share q/256 of the call's whole link work, every miss
+   * (slot claims included), but only from the staged ones, the last n_host in ascending id */
   unsigned char* host_e = (unsigned char*)calloc((size_t)E, 1);
   int n_host = 0;
   if (over && c->cold == 2) {
     int n_staged = nm - ns;
-    n_host = (n_staged * c->cold_q + 128) / 256;
+    n_host = (nm * c->cold_q + 128) / 256;
+    if (n_host > n_staged) n_host = n_staged;
     int seen = 0;
     for (int e = 0; e < E; ++e) {
       if (!miss[e] || c->slot_of[e] >= 0) continue; /* a staged miss */

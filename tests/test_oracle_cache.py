@@ -124,9 +124,9 @@ class BruteCache:
                 self.uses[self.home[e]] = min(self.uses[self.home[e]] + 1, self.cap)
             self.fired[e] = min(self.fired[e] + 1, self.cap)
         host = set()
-        if over and self.split is not None:  # the last share of the staged misses go to the host
+        if over and self.split is not None:  # the host's share of all misses, from the last staged ones
             staged = sorted(e for e in miss if e not in self.home)
-            n_host = (len(staged) * self.split + 128) // 256
+            n_host = min(len(staged), (len(miss) * self.split + 128) // 256)
             host = set(staged[len(staged) - n_host:])
         rec = lambda e: self.home.get(e, self.S + self.E + e if e in host else self.S + e)
         return [rec(e) for e in ids], int(over), [(e, rec(e)) for e in miss]
@@ -502,14 +502,17 @@ def test_split_mode_matches_brute_force(orc, seed):
 def test_split_mode_hand_example(orc):
     # 3 slots hold experts 1, 2, 3; a call needs 1, 4, 5, 6, 7 (|D| = 5 > 3): experts 2 and 3 are the two
     # eligible victims; the misses 4..7 are routed once each at positions 1, 2 (token 0) and 0, 1 (token 1)
-    # after 1, so 6 (position 0) and 4 (position 1, lower id than 7) claim slots 1 and 2; 5 and 7 are staged,
-    # and with q = 128 (half) the last of them, 7, goes to the host
-    c = orc.Cache(8, 3)
-    c.ensure(np.array([[1, 2, 3]], np.int32))
-    c.set_split(128)
-    sid, mode, pairs = c.ensure(np.array([[1, 4, 5], [6, 7, 1]], np.int32))
-    assert mode == orc.STAGED
-    assert pairs.tolist() == [[4, 2], [5, 8], [6, 1], [7, 18]]  # S + 5 = 8 staged, S + E + 7 = 18 host
-    assert sid.tolist() == [[0, 2, 8], [1, 18, 0]]
-    cnt = c.counters()
-    assert (cnt["staged_copies"], cnt["cold"]) == (1, 1)
+    # after 1, so 6 (position 0) and 4 (position 1, lower id than 7) claim slots 1 and 2; 5 and 7 are staged.
+    # The host's share counts all 4 misses: q = 64 (a quarter) is one of them, the last staged one, 7;
+    # q = 128 (half) is two, both staged ones; q = 256 would be four, capped at the two staged.
+    for q, host in ((64, {7}), (128, {5, 7}), (256, {5, 7})):
+        c = orc.Cache(8, 3)
+        c.ensure(np.array([[1, 2, 3]], np.int32))
+        c.set_split(q)
+        sid, mode, pairs = c.ensure(np.array([[1, 4, 5], [6, 7, 1]], np.int32))
+        assert mode == orc.STAGED
+        rec = {e: (3 + 8 + e if e in host else 3 + e) for e in (5, 7)}  # host S + E + e, staged S + e
+        assert pairs.tolist() == [[4, 2], [5, rec[5]], [6, 1], [7, rec[7]]], q
+        assert sid.tolist() == [[0, 2, rec[5]], [1, rec[7], 0]], q
+        cnt = c.counters()
+        assert (cnt["staged_copies"], cnt["cold"]) == (2 - len(host), len(host)), q
