@@ -826,6 +826,8 @@ def host_split_compare(args, m, torch, handles, wr_d, b_d, token_stream, batches
       link       every miss over the host link (the method as it stands);
       split      calls wider than the cache send the share of their staged misses measured per layer
                  (MOE_COLD_SPLIT) to the host CPU;
+      split_all  the same with every staged miss on the host (share 256/256): the misses that claim
+                 slots still cross the link, so the cache keeps learning;
       cold       every miss computed on the host from the start (nothing is ever loaded);
       cold_warm  the warm-up steps with the link (the cache learns), then every miss on the host.
     Wall-clock tok/s."""
@@ -843,16 +845,19 @@ def host_split_compare(args, m, torch, handles, wr_d, b_d, token_stream, batches
         res = {}
         qs = []
         try:
-            for mode in ("link", "split", "cold", "cold_warm"):
+            for mode in ("link", "split", "split_all", "cold", "cold_warm"):
                 for h in handles:
                     m.moe_offload_set_cold(h, m.COLD_OFF, st)
                     m.moe_offload_reset(h, st)
                 if mode == "split":
                     qs = [m.moe_offload_set_cold(h, m.COLD_SPLIT, st) for h in handles]
+                elif mode == "split_all":
+                    for h in handles:
+                        m.moe_offload_set_split(h, 256, st)
                 elif mode == "cold":
                     for h in handles:
                         m.moe_offload_set_cold(h, m.COLD_ON, st)
-                cold_ffn = [mode in ("split", "cold")]
+                cold_ffn = [mode in ("split", "split_all", "cold")]
 
                 def step(s):
                     a, b = xa, xb

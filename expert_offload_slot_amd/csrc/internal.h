@@ -20,8 +20,8 @@ constexpr int kF32Rows = 64;        // rows per work item on the fp32 path
 // victim orders of the slot table (table.h victim_key)
 constexpr int kPolicyLru = 0, kPolicyScored = 1, kPolicyFreq = 2;
 // the layer's cold-mode word: 0 off; kColdAll: every miss is computed on the host;
-// kColdSplit | q << 8: of an overflowing call's staged misses, the last share q/256
-// (ascending id) is computed on the host, the rest crosses the link
+// kColdSplit | q << 8: an overflowing call computes min(staged, round(misses * q / 256))
+// of its staged misses (the last in ascending id) on the host, the rest crosses the link
 constexpr int kColdAll = 1, kColdSplit = 2;
 
 // counters[] layout (device, uint64)

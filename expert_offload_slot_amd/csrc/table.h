@@ -298,10 +298,10 @@ __device__ __forceinline__ void ensure_body(const CacheDev& c, SharedTable& t, c
       staged = crank >= ns;
     }
     if (over && (t.cold & 0xff) == kColdSplit) {  // block-uniform
-      // the last share q/256 of the staged misses (ascending id) are computed on the host
+      // the host's share q/256 of all the call's misses, from the staged ones (the last in ascending id)
       int nst;
       const int srank = block_rank(staged, t.wave, &nst);
-      n_host = (nst * (t.cold >> 8) + 128) >> 8;
+      n_host = min(nst, (nm * (t.cold >> 8) + 128) >> 8);
       if (staged && srank >= nst - n_host) {
         v = S + E + tid;
         t.flag[tid] = 2;

@@ -336,12 +336,13 @@ int moe_offload_set_cold(moe_offload* h, int32_t mode, void* stream, int32_t* ch
  * both).  Calls that fit the cache are unchanged (mode SLOTS).  In a call that
  * overflows (mode STAGED), slot claims, victims, usage updates and copy-list
  * order are unchanged; of the n staged misses (those that got no slot), the
- * last h = floor((n * q + 128) / 256) in ascending id are computed on the host:
+ * last h = min(n, floor((m * q + 128) / 256)) in ascending id, m being all the
+ * call's misses (the link's whole work), are computed on the host:
  * their record index is S + E + e in slot_ids and in the copy list, the copy
  * kernel skips them, stats.staged_copies counts the other n - h and
  * stats.cold_misses the h.
- *   q: the host's share in 1/256, in [0, 256] (0: every staged miss crosses the
- *      link, as with the mode off; 256: none does).
+ *   q: the host's share of the call's misses in 1/256, in [0, 256] (0: every
+ *      staged miss crosses the link, as with the mode off; 256: none does).
  * While split mode is on the FFN must be moe_slot_ffn_host_cold, and the
  * activations x it receives must already be final when the call's
  * moe_slot_ensure is enqueued (they are whenever x fed moe_route_topk before
