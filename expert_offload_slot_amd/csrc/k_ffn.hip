@@ -789,6 +789,9 @@ __device__ __forceinline__ void one_pass(const uint8_t* row0, const uint8_t* row
       s0[i] = load_sr<W>(sr0, k0 + i, c);
       s1[i] = load_sr<W>(sr1, k0 + i, c);
     }
+    // every load of the pass is issued before the first dot (the compiler otherwise sinks them
+    // next to their uses and keeps about nine in flight per lane); no operands, no outputs
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       if constexpr (FILL) {
