@@ -1,7 +1,7 @@
 // Grouping of a call's (token, choice) pairs by record for the expert FFN:
 // one workgroup counting-sorts the n = T*k record indices into the group
 // descriptor (internal.h, GroupLayout) that the FFN work items read, with each
-// record's first prefill-GEMM tile (a prefix sum of ceil(count / kGemmTok)).
+// record's first prefill-GEMM tile (a prefix sum of gemm_tile_count(count)).
 #pragma once
 
 #include "blockops.h"
@@ -41,7 +41,7 @@ __device__ __forceinline__ void group_body(const int32_t* rec, int n, int nb, in
   int tot_pairs, nr;
   const int pre = block_excl_sum(c0 + c1, g.wave, &tot_pairs);
   const int pre_nz = block_excl_sum((c0 > 0) + (c1 > 0), g.wave, &nr);
-  const int t0 = (c0 + kGemmTok - 1) / kGemmTok, t1 = (c1 + kGemmTok - 1) / kGemmTok;
+  const int t0 = gemm_tile_count(c0), t1 = gemm_tile_count(c1);
   int tot_tiles;
   const int pre_t = block_excl_sum(t0 + t1, g.wave, &tot_tiles);
   int32_t* tiles = grp + off_tiles;

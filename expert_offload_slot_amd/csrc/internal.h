@@ -52,12 +52,19 @@ struct CacheDev {
 //     [0] record index, [1] token count n, [2] offset of its pair ids in the
 //     pair array, [3 .. 3 + kInline) its first kInline pair ids (t*k + j)
 //   pair array at kRecWords * (1 + max_recs): all pair ids grouped by record
-//   tile starts at off_tiles(): record r's first kGemmTok-pair tile, and the
+//   tile starts at off_tiles(): record r's first prefill-GEMM tile, and the
 //     total at index nr (the prefill GEMM's work list)
 // so a work item gets its record and (usually all) its tokens in one load trip.
 constexpr int kRecWords = 32;
 constexpr int kInline = kRecWords - 3;
-constexpr int kGemmTok = 64;  // pairs per prefill GEMM tile
+// A record's n pairs form prefill-GEMM tiles of kGemmTok pairs, except the last,
+// which takes up to kGemmTail: a record of 65 to 80 pairs is one tile, not a
+// full one and a nearly empty one that reads all its weights again.
+constexpr int kGemmTok = 64;
+constexpr int kGemmTail = 80;
+__host__ __device__ constexpr inline int gemm_tile_count(int n) {
+  return n <= 0 ? 0 : (n <= kGemmTail ? 1 : 1 + (n - kGemmTail + kGemmTok - 1) / kGemmTok);
+}
 struct GroupLayout {
   int max_recs;   // distinct records a call can touch
   int max_pairs;  // max_tokens * k

@@ -21,9 +21,10 @@
 //              weight-streaming (HBM) problem, not a matrix-core one.
 //              T = 1: k_gateup_one / k_down_one, the same rows per wavefront
 //              for one activation row, work item (choice j, rows).
-//     larger T (prefill), or many pairs per record: k_gemm_gu / k_gemm_dn, a grouped GEMM whose work
-//              items are (tile of 64 pairs of one record, 64 weight rows), K
-//              slices staged through LDS, bf16 MFMA 16x16x32 tiles.
+//     larger T (prefill), or many pairs per record: k_gemm<W, GU>, a grouped GEMM whose work
+//              items are (tile of up to 80 pairs of one record, weight rows):
+//              weights straight into registers, token rows through LDS, bf16
+//              MFMA 16x16x32 tiles.
 //     fp32 records: plain fp32 FMA kernels, work item (record, 64 rows).
 //   h is stored in bf16 (fp32 for fp32 records); down writes fp32 partial
 //   outputs per (t, j) to the workspace.
@@ -41,6 +42,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <map>
 #include <mutex>
 
 #include "grouping.h"
@@ -233,32 +235,38 @@ __device__ __forceinline__ void widen16_fp4(uint2 q, float s, uint4& lo, uint4& 
 
 // ------------------------------------------------------------------ prefill GEMMs (bf16, fp8, MXFP4)
 // Many tokens per record: a call becomes a grouped GEMM over record tiles.
-// Work item = (tile of kGemmTok pairs of one record, R weight rows: 64 for gate/up,
-// 128 for down);
-// the items of a call follow the tile starts of the group descriptor (routed
-// records, then the shared expert's ceil(T / kGemmTok) tiles).  A 256-thread
-// workgroup stages 128-wide K slices of its weight rows and of its gathered
-// token rows through LDS with coalesced loads (fp8 and MXFP4 codes widened
-// exactly to bf16 on the way in), loads the next slice into registers while
-// the current one feeds bf16 MFMA 16x16x32 tiles, and each wavefront owns an
-// (R/2) x 32 corner of the R x 64 output tile.  Down holds one weight matrix,
-// so it takes taller tiles (fewer loaded bytes per FLOP); gate/up holds two and
-// keeps 64 rows, which keeps its LDS and registers for more resident waves.
-// fp8: one scale per 128 x 128
-// block, so one per K slice and matrix (slices are 128-aligned), multiplies
-// the slice's partial sum.
-// MFMA operands: lane l supplies row (l & 15) and the 8 K values at
-// 8 * (l >> 4) of a 32-wide K step, for A (weight rows) and B (tokens) alike;
-// the result holds rows 4 * (l >> 4) + i and token column (l & 15).
-constexpr int kGemmRowsGu = 64;       // weight rows per gate/up tile (two matrices)
-constexpr int kGemmRowsDn = 128;      // weight rows per down tile (one matrix)
-constexpr int kGemmK = 128;           // K per LDS slice
+// Work item = (tile of a record's pairs, row tile: 64 rows of gate and of up,
+// or 128 rows of down); a record's pairs form tiles of kGemmTok, the last one
+// taking up to kGemmTail (gemm_tile_count), and the items of a call follow
+// the tile starts of the group descriptor (routed records, then the shared
+// expert's tiles).  A 256-thread workgroup runs an item: wavefront w owns 16
+// rows of gate and of up (32 rows of down) and every pair of the tile, so
+// its weight fragments are loaded straight from memory into registers in the
+// MFMA operand layout (fp8 and MXFP4 codes widened exactly to bf16 there) and
+// are read by no other wavefront; only the gathered token rows go through
+// LDS, in 128-wide K slices, double-buffered.  Weights are loaded two slices
+// ahead and token rows one slice ahead.  bf16 MFMA 16x16x32, fp32
+// accumulation; fp8: one scale per 128 x 128 block, so one per K slice and
+// matrix, multiplies the slice's partial sum.  The grid is the number of
+// workgroups the device holds at once (gemm_grid_cap).
+// MFMA operands: lane l supplies row (l & 15) (token l & 15 for B) and 8 K
+// values of a 32-wide step; the result holds rows 4 * (l >> 4) + i and token
+// l & 15.  Which 8 K values lane group g = l >> 4 supplies at step s is
+// gemm_kmap(g, s), chosen per weight format so that a lane's codes for a
+// slice come in whole 16-byte loads and each load instruction covers 64
+// contiguous bytes of each of its 16 rows; A and B use the same map, and a
+// slice's four steps cover its 128 K values once.
+constexpr int kGemmRowsGu = 64;       // weight rows per gate/up tile (each matrix)
+constexpr int kGemmRowsDn = 128;      // weight rows per down tile
+constexpr int kGemmK = 128;           // K per slice
+constexpr int kGemmNJ = kGemmTail / 16;
 constexpr int kLdsRow = kGemmK + 8;   // LDS row stride in bf16: rows start on different banks
 
 struct GemmItem {
   Item it;
   int r;   // record block (nr = the shared expert)
   int n0;  // first pair of the tile within the record
+  int w;   // pairs in the tile
   int rt;  // row tile
 };
 
@@ -266,6 +274,7 @@ __device__ __forceinline__ GemmItem gemm_item(const FfnArgs& a, int nr, int rout
   GemmItem g;
   const int ti = item / row_tiles;
   g.rt = item - ti * row_tiles;
+  int j, nt;
   if (ti < routed_tiles) {
     const int32_t* tiles = a.grp + a.off_tiles;  // strictly increasing: every record has a pair
     int lo = 0, hi = nr - 1;
@@ -275,262 +284,242 @@ __device__ __forceinline__ GemmItem gemm_item(const FfnArgs& a, int nr, int rout
       else hi = mid - 1;
     }
     g.r = lo;
-    g.n0 = (ti - tiles[lo]) * kGemmTok;
+    j = ti - tiles[lo];
+    nt = tiles[lo + 1] - tiles[lo];
   } else {
     g.r = nr;
-    g.n0 = (ti - routed_tiles) * kGemmTok;
+    j = ti - routed_tiles;
+    nt = gemm_tile_count(a.T);
   }
   g.it = item_record(a, nr, g.r);
+  g.n0 = j * kGemmTok;
+  g.w = j == nt - 1 ? g.it.n - g.n0 : kGemmTok;
   return g;
 }
 
 __device__ __forceinline__ int gemm_tiles(const FfnArgs& a, int nr, int* routed) {
   *routed = a.grp[a.off_tiles + nr];
-  return *routed + (a.shared ? (a.T + kGemmTok - 1) / kGemmTok : 0);
+  return *routed + (a.shared ? gemm_tile_count(a.T) : 0);
 }
 
-// one K slice of NM weight matrices (R rows each, row stride K weights) and of
-// the tile's token rows, from memory into registers.  TW threads share a
-// weight row: bf16 8 weights (16 bytes) each, fp8 and MXFP4 16 codes each (16
-// or 8 bytes, MXFP4 with the scale of their 32-group); TB threads share a
-// token row, 8 activations each.
-template <int W, int NM, int R>
-struct Slice {
-  static constexpr int TW = W == kBf16 ? kGemmK / 8 : kGemmK / 16;  // threads per weight row
-  static constexpr int RW = 256 / TW;                                // weight rows per pass
-  static constexpr int NA = R / RW;
-  static constexpr int TB = kGemmK / 8;                              // threads per token row
-  static constexpr int RBT = 256 / TB;                               // token rows per pass
-  static constexpr int NB = kGemmTok / RBT;
-  uint4 a[NA * NM];  // MXFP4 uses .x, .y
-  float s[NA * NM];
-  uint4 b[NB];
+// Waits until every global load the wavefront has issued has returned (s_waitcnt vmcnt(0),
+// the export and LDS counters left alone).  The GEMM loop issues a slice's loads, computes the
+// previous slice, and only then needs them: placed where the loop stores them, this keeps any load
+// in flight across the back edge, which would make the compiler wait on the loads just issued
+// inside the compute on every iteration.
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-  // w0: row 0 of the tile in matrix 0, matrices mat bytes apart; sr0: for
-  // MXFP4, the scale bytes of row 0 of the tile in matrix 0, matrices sstride apart
-  __device__ __forceinline__ void load(const uint8_t* w0, uint64_t mat, const uint8_t* sr0, uint64_t sstride, int K,
-                                       int k0, const uint16_t* const bp[NB]) {
-    const int tid = threadIdx.x;
+template <int W>
+__device__ __forceinline__ int gemm_kmap(int g, int s) {
+  if (W == kBf16) return 32 * s + 8 * g;                        // 4 x 16 bytes: K 32s + 8g
+  if (W == kFp8) return (s & 2) * 32 + 16 * g + 8 * (s & 1);    // 2 x 16 bytes: K 16g and 64 + 16g
+  return 32 * g + 8 * s;                                        // MXFP4, 16 bytes: K 32g (one scale group)
+}
+
+// one lane's codes of one 16-row weight fragment over a K slice
+template <int W>
+struct AFrag {
+  static constexpr int N = W == kBf16 ? 4 : (W == kFp8 ? 2 : 1);
+  u32x4 q[N];
+  uint32_t e;  // MXFP4: the E8M0 scale byte of the lane's 32 weights
+  float s;     // ... decoded by prep()
+
+  // row: the lane's weight row (codes at K = 0); rs: MXFP4, its scale bytes
+  __device__ __forceinline__ void load(const uint8_t* row, const uint8_t* rs, int k0, int g) {
+    if (W == kBf16) {
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-#pragma unroll
-      for (int q = 0; q < NA; ++q) {
-        const int row = tid / TW + RW * q;
-        if (W == kBf16) {
-          a[NA * m + q] = ld16(w0 + m * mat + ((uint64_t)row * K + k0 + (tid % TW) * 8) * 2);
-        } else if (W == kFp8) {
-          a[NA * m + q] = ld16(w0 + m * mat + (uint64_t)row * K + k0 + (tid % TW) * 16);
-        } else {
-          const uint2 v =
-              *reinterpret_cast<const uint2*>(w0 + m * mat + ((uint64_t)row * K + k0) / 2 + (tid % TW) * 8);
-          a[NA * m + q].x = v.x;
-          a[NA * m + q].y = v.y;
-          s[NA * m + q] = e8m0_scale(sr0[m * sstride + (uint64_t)row * (K / 32) + (k0 + (tid % TW) * 16) / 32]);
-        }
-      }
+      for (int i = 0; i < 4; ++i) q[i] = *reinterpret_cast<const u32x4*>(row + 2 * (k0 + gemm_kmap<W>(g, i)));
+    } else if (W == kFp8) {
+      q[0] = *reinterpret_cast<const u32x4*>(row + k0 + 16 * g);
+      q[1] = *reinterpret_cast<const u32x4*>(row + k0 + 64 + 16 * g);
+    } else {
+      q[0] = *reinterpret_cast<const u32x4*>(row + (k0 + 32 * g) / 2);
+      e = rs[(k0 + 32 * g) / 32];
     }
-#pragma unroll
-    for (int q = 0; q < NB; ++q) b[q] = bp[q] ? ld16(bp[q] + k0) : make_uint4(0, 0, 0, 0);
   }
 
-  __device__ __forceinline__ void store(uint16_t (*As)[R][kLdsRow], uint16_t (*Bs)[kLdsRow]) const {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-#pragma unroll
-      for (int q = 0; q < NA; ++q) {
-        const int row = tid / TW + RW * q;
-        if (W == kBf16) {
-          st16(&As[m][row][(tid % TW) * 8], a[NA * m + q]);
-        } else {
-          uint4 lo, hi;
-          if (W == kFp8) widen16(a[NA * m + q], lo, hi);
-          else widen16_fp4(make_uint2(a[NA * m + q].x, a[NA * m + q].y), s[NA * m + q], lo, hi);
-          st16(&As[m][row][(tid % TW) * 16], lo);
-          st16(&As[m][row][(tid % TW) * 16 + 8], hi);
-        }
-      }
+  // MXFP4: decodes the scale where the slice is computed.  The empty asm makes the byte opaque up
+  // to here, so the decode (and the wait for its load) is not hoisted to where the load is issued,
+  // two slices earlier.
+  __device__ __forceinline__ void prep() {
+    if (W == kMx4) {
+      asm volatile("" : "+v"(e));
+      s = e8m0_scale(e);
     }
-#pragma unroll
-    for (int q = 0; q < NB; ++q) st16(&Bs[tid / TB + RBT * q][(tid % TB) * 8], b[q]);
+  }
+
+  // the bf16 operand of step st
+  __device__ __forceinline__ bf16x8 op(int st) const {
+    u32x4 v;
+    if (W == kBf16) {
+      v = q[st];
+    } else if (W == kFp8) {
+      const u32x4 c = q[st >> 1];
+      const uint32_t d0 = (st & 1) ? c.z : c.x, d1 = (st & 1) ? c.w : c.y;
+      v = u32x4{cvt2<false>(d0), cvt2<true>(d0), cvt2<false>(d1), cvt2<true>(d1)};
+    } else {
+      const uint32_t d = q[0][st];
+      v = u32x4{cvt2_fp4<0>(d, s), cvt2_fp4<1>(d, s), cvt2_fp4<2>(d, s), cvt2_fp4<3>(d, s)};
+    }
+    return __builtin_bit_cast(bf16x8, v);
   }
 };
 
-// token rows of the tile's pairs for Slice::load (null: past the tile's last pair)
-template <int NB>
-__device__ __forceinline__ void tile_rows(const uint16_t* base, uint64_t stride, const FfnArgs& a, const GemmItem& g,
-                                          int n_here, bool by_token, const uint16_t* bp[NB]) {
-  constexpr int TB = kGemmK / 8, RBT = 256 / TB;
-  const int tid = threadIdx.x;
+// One work item of NJ 16-pair blocks.  GU: gate/up over x (rows by token) into
+// h = silu(gate) * up in bf16; else down over h (rows by pair) into fp32 partial outputs.
+template <int W, bool GU, int NJ>
+__device__ __forceinline__ void gemm_run(const FfnArgs& a, const GemmItem& g, uint16_t (*Bs)[kGemmTail][kLdsRow]) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, lg = lane >> 4, lr = lane & 15;
+  const int K = GU ? a.H : a.F, nk = K / kGemmK;
+  const int m0 = g.rt * (GU ? kGemmRowsGu : kGemmRowsDn);
+  const uint64_t mat = code_bytes<W>((uint64_t)a.F * a.H);
+  // the wavefront's two fragments: gate and up rows m0 + 16 wv + lr, or down rows m0 + 32 wv + 16 f + lr
+  const uint8_t* row[2];
+  const uint8_t* rs[2];
+  const float* sc[2];  // fp8: the row block's scales of the fragment's matrix, one per K slice
 #pragma unroll
-  for (int q = 0; q < NB; ++q) {
-    const int idx = tid / TB + RBT * q;
-    if (idx < n_here) {
+  for (int f = 0; f < 2; ++f) {
+    const int m = GU ? f : 2;
+    const int r = GU ? m0 + 16 * wv + lr : m0 + 32 * wv + 16 * f + lr;
+    row[f] = g.it.rec + m * mat + code_bytes<W>((uint64_t)r * K);
+    rs[f] = scale_row<W>(g.it.rec, mat, a.F, a.H, m, r, K);
+    sc[f] = reinterpret_cast<const float*>(scale_row<W>(g.it.rec, mat, a.F, a.H, m, m0, K));
+  }
+  // the tile's token rows: 16 threads per row, 8 activations each, rows tid / 16 + 16 q.  Rows
+  // past the tile's last pair repeat that pair's row: every load is issued unconditionally (the
+  // wait counts stay static), and those columns' results are never stored.
+  const uint16_t* bp[NJ];
+  {
+    const uint16_t* base = GU ? (const uint16_t*)a.x : (const uint16_t*)a.hbuf;
+#pragma unroll
+    for (int q = 0; q < NJ; ++q) {
+      const int p = item_pair(a, g.it, g.r, g.n0 + min(tid / 16 + 16 * q, g.w - 1));
+      bp[q] = base + (uint64_t)(GU ? pair_token(a, p) : p) * K + (tid % 16) * 8;
+    }
+  }
+  u32x4 bst[NJ];
+  auto load_b = [&](int kb) {
+#pragma unroll
+    for (int q = 0; q < NJ; ++q) bst[q] = *reinterpret_cast<const u32x4*>(bp[q] + kb * kGemmK);
+  };
+  auto store_b = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < NJ; ++q) *reinterpret_cast<u32x4*>(&Bs[buf][tid / 16 + 16 * q][(tid % 16) * 8]) = bst[q];
+  };
+  f32x4 acc[2][NJ];
+#pragma unroll
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[f][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Weights run two slices ahead in three register sets whose roles rotate (the loop is unrolled
+  // by three, so no set is copied while its loads are in flight); token rows run one slice ahead
+  // in registers and are stored to the other LDS buffer at the end of each slice.  Every slice
+  // issues the same loads (past the last slice they repeat it), so the compiler's wait counts are
+  // exact: a slice's MFMAs never wait on global memory.
+  AFrag<W> AX[2], AY[2], AZ[2];
+  float sX[2] = {1.f, 1.f}, sY[2] = {1.f, 1.f}, sZ[2] = {1.f, 1.f};
+  auto load_a = [&](AFrag<W>(&A)[2], float(&sc_)[2], int kb) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f) A[f].load(row[f], rs[f], kb * kGemmK, lg);
+    if (W == kFp8) {
+      sc_[0] = sc[0][kb];
+      sc_[1] = sc[1][kb];
+    }
+  };
+  load_a(AX, sX, 0);
+  load_a(AY, sY, min(1, nk - 1));
+  load_b(0);
+  wait_loads();
+  __syncthreads();  // the previous item no longer reads either buffer
+  store_b(0);
+  __syncthreads();
+  // one slice: issue slice kb + 1's token rows, then slice kb + 2's weights (into ld), run slice kb
+  // from A and LDS, then store slice kb + 1's token rows into the other buffer (the one read in
+  // slice kb - 1, before the last barrier)
+  auto step = [&](int kb, AFrag<W>(&A)[2], const float(&s_)[2], AFrag<W>(&ld)[2], float(&sl)[2]) {
+    load_b(min(kb + 1, nk - 1));
+    load_a(ld, sl, min(kb + 2, nk - 1));
+    // keep the scheduler from pulling the next slice's widening into this one: that would wait on
+    // loads issued a slice ago, and in order behind them on this slice's own
+    __builtin_amdgcn_sched_barrier(0);
+    A[0].prep();
+    A[1].prep();
+    const uint16_t (*B)[kLdsRow] = Bs[kb & 1];
+    f32x4 part[2][NJ];
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) part[f][j] = W == kFp8 ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[f][j];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int kc = gemm_kmap<W>(lg, st);
+      bf16x8 bf[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) bf[j] = *reinterpret_cast<const bf16x8*>(&B[16 * j + lr][kc]);
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const bf16x8 af = A[f].op(st);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) part[f][j] = mfma(af, bf[j], part[f][j]);
+      }
+    }
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[f][j] = W == kFp8 ? fma4(s_[f], part[f][j], acc[f][j]) : part[f][j];
+    store_b((kb + 1) & 1);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int kb = 0;
+  for (; kb + 3 <= nk; kb += 3) {
+    step(kb, AX, sX, AZ, sZ);
+    step(kb + 1, AY, sY, AX, sX);
+    step(kb + 2, AZ, sZ, AY, sY);
+  }
+  if (kb < nk) step(kb, AX, sX, AZ, sZ);
+  if (kb + 1 < nk) step(kb + 1, AY, sY, AX, sX);
+  wait_loads();  // the repeated loads of the last slices, before the next item reuses the registers
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int idx = 16 * j + lr;
+    if (idx < g.w) {
       const int p = item_pair(a, g.it, g.r, g.n0 + idx);
-      bp[q] = base + (uint64_t)(by_token ? pair_token(a, p) : p) * stride + (tid % TB) * 8;
-    } else {
-      bp[q] = nullptr;
+      if (GU) {
+        uint16_t hv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hv[e] = f32_to_bf16(silu_mul(acc[0][j][e], acc[1][j][e]));
+        uint2 st;
+        st.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
+        st.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
+        *reinterpret_cast<uint2*>((uint16_t*)a.hbuf + (uint64_t)p * a.F + m0 + 16 * wv + 4 * lg) = st;
+      } else {
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+          *reinterpret_cast<float4*>(a.part + (uint64_t)p * a.H + m0 + 32 * wv + 16 * f + 4 * lg) =
+              make_float4(acc[f][j][0], acc[f][j][1], acc[f][j][2], acc[f][j][3]);
+      }
     }
   }
 }
 
-// acc[m][i][j] += the wavefront's (R/2) x 32 corner (row tiles i, token tiles j)
-// of matrix m over the LDS slice; SC (fp8): the slice's sum is scaled by sc[m] first
-template <bool SC, int NM, int R>
-__device__ __forceinline__ void gemm_slice(const uint16_t (*As)[R][kLdsRow], const uint16_t (*Bs)[kLdsRow],
-                                           const float* sc, f32x4 acc[NM][R / 32][2]) {
-  constexpr int RI = R / 32;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int r0 = (R / 2) * (wv >> 1) + (lane & 15), c0 = 32 * (wv & 1) + (lane & 15), kq = 8 * (lane >> 4);
-  f32x4 part[NM][RI][2];
-#pragma unroll
-  for (int m = 0; m < NM; ++m)
-#pragma unroll
-    for (int i = 0; i < RI; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) part[m][i][j] = SC ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[m][i][j];
-#pragma unroll
-  for (int ks = 0; ks < kGemmK; ks += 32) {
-    bf16x8 bf[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) bf[j] = *reinterpret_cast<const bf16x8*>(&Bs[c0 + 16 * j][ks + kq]);
-#pragma unroll
-    for (int m = 0; m < NM; ++m)
-#pragma unroll
-      for (int i = 0; i < RI; ++i) {
-        const bf16x8 af = *reinterpret_cast<const bf16x8*>(&As[m][r0 + 16 * i][ks + kq]);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) part[m][i][j] = mfma(af, bf[j], part[m][i][j]);
-      }
-  }
-#pragma unroll
-  for (int m = 0; m < NM; ++m)
-#pragma unroll
-    for (int i = 0; i < RI; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[m][i][j] = SC ? fma4(sc[m], part[m][i][j], acc[m][i][j]) : part[m][i][j];
-}
-
-// gate/up: C[f][p] = W[f] . x[token(p)] for gate and up, h = silu(gate) * up in bf16
-template <int W, int R = kGemmRowsGu>
-__global__ __launch_bounds__(256) void k_gemm_gu(FfnArgs a) {
-  __shared__ uint16_t As[2][R][kLdsRow];
-  __shared__ uint16_t Bs[kGemmTok][kLdsRow];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+// gate/up (GU: C[f][p] = W[f] . x[token(p)] for gate and up, h = silu(gate) * up in bf16)
+// or down (part[p][r] = Wd[r] . h[p], fp32 partial outputs)
+template <int W, bool GU>
+__global__ __launch_bounds__(256) void k_gemm(FfnArgs a) {
+  __shared__ uint16_t Bs[2][kGemmTail][kLdsRow];
   const int nr = a.grp[0];
   int routed;
   const int ntiles = gemm_tiles(a, nr, &routed);
-  const int H = a.H, F = a.F, RT = F / R, nk = H / kGemmK;
-  const uint64_t mat = code_bytes<W>((uint64_t)F * H);
-  const uint64_t sstride = (uint64_t)F * H / 32;  // MXFP4 scale bytes per matrix
-  const int nsc = (F / 128) * (H / 128);
-  const uint16_t* __restrict__ x = (const uint16_t*)a.x;
-  uint16_t* __restrict__ hb = (uint16_t*)a.hbuf;
+  const int RT = GU ? a.F / kGemmRowsGu : a.H / kGemmRowsDn;
   for (int item = blockIdx.x; item < ntiles * RT; item += gridDim.x) {
     const GemmItem g = gemm_item(a, nr, routed, RT, item);
-    const int m0 = g.rt * R, n_here = min(kGemmTok, g.it.n - g.n0);
-    const uint16_t* bp[Slice<W, 2, R>::NB];
-    tile_rows<Slice<W, 2, R>::NB>(x, H, a, g, n_here, true, bp);
-    const uint8_t* w0 = g.it.rec + code_bytes<W>((uint64_t)m0 * H);
-    const uint8_t* sr0 = scale_row<W>(g.it.rec, mat, F, H, 0, m0, H);
-    const float* sc = reinterpret_cast<const float*>(sr0);  // fp8: this row block's scales of gate
-    f32x4 acc[2][R / 32][2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int i = 0; i < R / 32; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    Slice<W, 2, R> sl;
-    // fp8: each slice's two block scales are loaded one slice ahead, before that slice's
-    // weights, so the MFMAs never wait on the loads of the slice in flight
-    float s2[2] = {W == kFp8 ? sc[0] : 1.f, W == kFp8 ? sc[nsc] : 1.f};
-    sl.load(w0, mat, sr0, sstride, H, 0, bp);
-    for (int kb = 0; kb < nk; ++kb) {
-      __syncthreads();  // the previous slice (or item) is no longer read
-      sl.store(As, Bs);
-      __syncthreads();
-      float s2n[2] = {1.f, 1.f};
-      if (W == kFp8 && kb + 1 < nk) {
-        s2n[0] = sc[((kb + 1) * kGemmK) / 128];
-        s2n[1] = sc[nsc + ((kb + 1) * kGemmK) / 128];
-      }
-      if (kb + 1 < nk) sl.load(w0, mat, sr0, sstride, H, (kb + 1) * kGemmK, bp);
-      gemm_slice<W == kFp8, 2, R>(As, Bs, s2, acc);
-      s2[0] = s2n[0];
-      s2[1] = s2n[1];
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int idx = 32 * (wv & 1) + 16 * j + (lane & 15);
-      if (idx < n_here) {
-        const int p = item_pair(a, g.it, g.r, g.n0 + idx);
-#pragma unroll
-        for (int i = 0; i < R / 32; ++i) {
-          const int f = m0 + (R / 2) * (wv >> 1) + 16 * i + 4 * (lane >> 4);
-          uint16_t hv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) hv[e] = f32_to_bf16(silu_mul(acc[0][i][j][e], acc[1][i][j][e]));
-          uint2 st;
-          st.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
-          st.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
-          *reinterpret_cast<uint2*>(hb + (uint64_t)p * F + f) = st;
-        }
-      }
-    }
-  }
-}
-
-// down: part[p][r] = Wd[r] . h[p] (fp32 partial outputs)
-template <int W, int R = kGemmRowsDn>
-__global__ __launch_bounds__(256) void k_gemm_dn(FfnArgs a) {
-  __shared__ uint16_t As[1][R][kLdsRow];
-  __shared__ uint16_t Bs[kGemmTok][kLdsRow];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int nr = a.grp[0];
-  int routed;
-  const int ntiles = gemm_tiles(a, nr, &routed);
-  const int H = a.H, F = a.F, RT = H / R, nk = F / kGemmK;
-  const uint64_t mat = code_bytes<W>((uint64_t)F * H);
-  const uint16_t* __restrict__ hb = (const uint16_t*)a.hbuf;
-  float* __restrict__ part = a.part;
-  for (int item = blockIdx.x; item < ntiles * RT; item += gridDim.x) {
-    const GemmItem g = gemm_item(a, nr, routed, RT, item);
-    const int m0 = g.rt * R, n_here = min(kGemmTok, g.it.n - g.n0);
-    const uint16_t* bp[Slice<W, 1, R>::NB];
-    tile_rows<Slice<W, 1, R>::NB>(hb, F, a, g, n_here, false, bp);
-    const uint8_t* w0 = g.it.rec + 2 * mat + code_bytes<W>((uint64_t)m0 * F);
-    const uint8_t* sr0 = scale_row<W>(g.it.rec, mat, F, H, 2, m0, F);
-    const float* sc = reinterpret_cast<const float*>(sr0);
-    f32x4 acc[1][R / 32][2];
-#pragma unroll
-    for (int i = 0; i < R / 32; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[0][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    Slice<W, 1, R> sl;
-    float s1[1] = {W == kFp8 ? sc[0] : 1.f};  // one slice ahead, as in k_gemm_gu
-    sl.load(w0, mat, sr0, 0, F, 0, bp);
-    for (int kb = 0; kb < nk; ++kb) {
-      __syncthreads();
-      sl.store(As, Bs);
-      __syncthreads();
-      const float s1n = W == kFp8 && kb + 1 < nk ? sc[((kb + 1) * kGemmK) / 128] : 1.f;
-      if (kb + 1 < nk) sl.load(w0, mat, sr0, 0, F, (kb + 1) * kGemmK, bp);
-      gemm_slice<W == kFp8, 1, R>(As, Bs, s1, acc);
-      s1[0] = s1n;
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int idx = 32 * (wv & 1) + 16 * j + (lane & 15);
-      if (idx < n_here) {
-        const int p = item_pair(a, g.it, g.r, g.n0 + idx);
-#pragma unroll
-        for (int i = 0; i < R / 32; ++i) {
-          const int r = m0 + (R / 2) * (wv >> 1) + 16 * i + 4 * (lane >> 4);
-          *reinterpret_cast<float4*>(part + (uint64_t)p * H + r) =
-              make_float4(acc[0][i][j][0], acc[0][i][j][1], acc[0][i][j][2], acc[0][i][j][3]);
-        }
-      }
+    switch ((g.w + 15) >> 4) {
+      case 1: gemm_run<W, GU, 1>(a, g, Bs); break;
+      case 2: gemm_run<W, GU, 2>(a, g, Bs); break;
+      case 3: gemm_run<W, GU, 3>(a, g, Bs); break;
+      case 4: gemm_run<W, GU, 4>(a, g, Bs); break;
+      default: gemm_run<W, GU, kGemmNJ>(a, g, Bs); break;
     }
   }
 }
@@ -1378,6 +1367,28 @@ void* scratch_ptr(int device) {
   return g_scratch[device];
 }
 
+// Workgroups of GEMM kernel k the device holds at once (CUs x resident workgroups per CU).  The
+// GEMM's grid is no larger: every workgroup then starts at once and strides over the work list
+// in step with the others, so the token tiles of one record and row tile (a multiple of 8 items
+// apart, so on one XCD: workgroup w runs on XCD w mod 8) run together and fetch the weight rows
+// into that XCD's L2 once.
+template <typename Kern>
+int gemm_grid_cap(Kern k, int device) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;
+  std::lock_guard<std::mutex> lk(mu);
+  const auto key = std::make_pair(reinterpret_cast<const void*>(k), device);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k, 256, 0) != hipSuccess || cus <= 0 || per <= 0) {
+    (void)hipGetLastError();
+    return 2048;  // not cached: the query is repeated on the next call
+  }
+  return cache[key] = cus * per;
+}
+
 FfnWork ffn_work_in(const moe_offload* h, int T, void* base, size_t* bytes) {
   FfnWork w;
   w.gl.max_pairs = T * h->k;
@@ -1458,13 +1469,14 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
       b1 = b2 = dim3(256);
     }
   } else {  // grouped GEMM over (record tile, 64 rows) work items; the grid strides over the call's list
-    gu = wf == kFp8 ? k_gemm_gu<kFp8> : (wf == kMx4 ? k_gemm_gu<kMx4> : k_gemm_gu<kBf16>);
-    dn = wf == kFp8 ? k_gemm_dn<kFp8> : (wf == kMx4 ? k_gemm_dn<kMx4> : k_gemm_dn<kBf16>);
-    // tiles of a call: at most one partial tile per record on top of the full ones
+    gu = wf == kFp8 ? k_gemm<kFp8, true> : (wf == kMx4 ? k_gemm<kMx4, true> : k_gemm<kBf16, true>);
+    dn = wf == kFp8 ? k_gemm<kFp8, false> : (wf == kMx4 ? k_gemm<kMx4, false> : k_gemm<kBf16, false>);
+    // tiles of a call: gemm_tile_count(n) <= ceil(n / kGemmTok), so at most one partial tile per
+    // record on top of the full ones
     const int tiles = (T * h->k) / kGemmTok + std::min(T * h->k, h->S + h->E) +
-                      (shared ? (T + kGemmTok - 1) / kGemmTok : 0);
-    g1 = dim3(std::min(tiles * (h->F / kGemmRowsGu), 2048));
-    g2 = dim3(std::min(tiles * (h->H / kGemmRowsDn), 2048));
+                      (shared ? gemm_tile_count(T) : 0);
+    g1 = dim3(std::min(tiles * (h->F / kGemmRowsGu), gemm_grid_cap(gu, h->device)));
+    g2 = dim3(std::min(tiles * (h->H / kGemmRowsDn), gemm_grid_cap(dn, h->device)));
     b1 = b2 = dim3(256);
   }
   {

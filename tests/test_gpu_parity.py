@@ -137,8 +137,43 @@ def test_mxfp4_decode_batches_with_shared_expert(S):
 
 
 def test_mxfp4_prefill_gemm_ragged_tiles():
-    # > 64 tokens per call: the grouped GEMM with E2M1 codes widened (scale folded in) into LDS
+    # > 64 tokens per call: the grouped GEMM with E2M1 codes widened (scale folded in) into registers
     run_sequence(12, 6, 3, 256, 512, 3, 1.2, 62, 3, [100, 130, 65], shared=True)
+
+
+@pytest.mark.parametrize("wdt", [1, 2, 3])
+def test_prefill_gemm_tile_boundaries(wdt):
+    """Records whose pair counts sit on every GEMM tile boundary: a record's pairs form 64-pair tiles
+    and a last tile of up to 80 (1 to 5 blocks of 16), so the counts 1, 15, 16, 17, 63 to 65, 79 to 81,
+    96, 144, 145, 160 and 161 reach one-tile records of every width, the first count that splits, and
+    two-tile records with the widest and narrowest last tile.  Choice 0 of each token names the record;
+    choice 1 names expert 15, a record of every token (19 tiles, a 35-pair last one).  Tokens are
+    shuffled, so every tile gathers rows from all over the call."""
+    counts = [1, 15, 16, 17, 63, 64, 65, 79, 80, 81, 96, 144, 145, 160, 161]
+    E, k, H, F = 16, 2, 256, 512  # MXFP4 needs multiples of 256
+    T = sum(counts)
+    rng = np.random.default_rng(70 + wdt)
+    first = rng.permutation(np.repeat(np.arange(len(counts)), counts)).astype(np.int32)
+    ids = np.stack([first, np.full(T, E - 1, np.int32)], axis=1)
+    w = rng.uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    shared = wdt == 2
+    print("tile boundaries wdt=%d T=%d" % (wdt, T), flush=True)
+    host, wr, b, sh = make_layer_inputs(71, 0, E, H, F, wdt, 0.0, shared)
+    x = np.ascontiguousarray(synth.tokens(72, 0, T, H, 1, 0.0, wdt)[0])
+    gl = GpuLayer(E, E, k, H, F, wdt, T, host, wr, b, shared=sh)
+    try:
+        m.moe_offload_set_ffn_path(gl.h, m.FFN_GEMM)
+        gl.w[:T].copy_(torch.from_numpy(w))
+        gl.ensure(T, ids=to_dev(ids))
+        gl.copy()
+        gl.ffn(to_dev(x), T)
+        y = to_np(gl.y[:T])
+        _, y64 = oracle.ffn(x, wdt, H, F, oracle.host_records(host, ids), w.astype(np.float64), shared=sh,
+                            want_f64=True)
+        assert row_rel_err(y, y64, wdt) <= TOL[wdt]
+        assert gl.stats()["error"] == 0
+    finally:
+        gl.close()
 
 
 @pytest.mark.parametrize("E,S,k,Ts", [(16, 6, 4, [1, 2, 3]), (32, 10, 4, [1, 4, 9]), (64, 12, 8, [1, 2])])
