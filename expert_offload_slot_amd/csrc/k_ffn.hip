@@ -1314,23 +1314,24 @@ bool ffn_reads_through(const moe_offload* h, int T) {
 }
 
 // Kernel pair of a multi-token call.  The decode kernels meet each weight row
-// once per 8-token group of a record, the grouped GEMM once per 64-pair tile,
-// so with many pairs per record the GEMM streams fewer bytes; the crossover
-// was measured per weight format (FFN time per pair of both pairs on the same
-// calls, every expert resident): bf16 between 4 and 6 pairs per record
-// (Mixtral shape), MXFP4 between 2 and 3 depending on the shape, fp8 below 1.3
-// (its decode kernels widen every code once per token group); fp8 switches at
-// 2 all the same, so decode batches below that keep read-through.  The rule
-// reads T * k / E, the fewest pairs per record a call can have on average, so
-// it depends only on the layer's shape and the call's token count (never on S
-// or on which experts are resident): every output bit stays independent of the
-// slot count.
+// once per 8-token group of a record, the grouped GEMM once per tile of up to
+// 80 pairs, so with many pairs per record the GEMM streams fewer bytes; the
+// crossover was measured per weight format (FFN time per pair of both pairs on
+// the same calls, every expert resident), in T * k / E, the fewest pairs per
+// record a call can average: bf16 between 4 and 6 (Mixtral shape; Qwen3 shape
+// even at 4); MXFP4 about 1 (the GEMM wins from 0.5 on the Qwen3 shape, the
+// decode kernels up to 1 on a 32-expert top-4 layer); fp8 below every size
+// measured, down to 0.125 (its decode kernels widen every code once per token
+// group).  So the GEMM takes a call when 8 * T * k >= c8 * E with c8 = 40, 8
+// and 1.  The rule reads only the layer's shape and the call's token count
+// (never S or which experts are resident): every output bit stays independent
+// of the slot count.
 bool ffn_uses_gemm(const moe_offload* h, int T) {
   if (h->dtype == MOE_F32 || T == 1) return false;
   if (T > kDecodeMaxT || h->ffn_path == MOE_FFN_GEMM) return true;
   if (h->ffn_path == MOE_FFN_DECODE) return false;
-  const int per_record = h->dtype == MOE_FP8_E4M3_B128 ? 2 : (h->dtype == MOE_MXFP4 ? 3 : 5);
-  return T * h->k >= per_record * h->E;
+  const int c8 = h->dtype == MOE_FP8_E4M3_B128 ? 1 : (h->dtype == MOE_MXFP4 ? 8 : 40);
+  return 8 * T * h->k >= c8 * h->E;
 }
 
 // ------------------------------------------------------------------ scratch workspace

@@ -283,9 +283,10 @@ int moe_slot_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const f
  * "How it works": decode and prefill are the same grouped FFN; which kernels
  * run is an implementation choice that never changes which experts are used).
  *   MOE_FFN_AUTO (the default): the grouped MFMA GEMM when T * k >= c * E, with
- *     c = 5 for bf16, 2 for fp8 and 3 for MXFP4 (the measured crossovers: the
+ *     c = 5 for bf16, 1 for MXFP4 and 1/8 for fp8 (the measured crossovers: the
  *     decode kernels read each weight row once per 8-token group of a record,
- *     the GEMM once per 64-pair tile), else the pair-dot decode kernels;
+ *     the GEMM once per tile of up to 80 pairs), else the pair-dot decode
+ *     kernels;
  *   MOE_FFN_DECODE: always the decode kernels;  MOE_FFN_GEMM: always the GEMM.
  * Calls of one token always take the single-token kernels, calls above 64
  * tokens the GEMM, fp32 layers their fp32 kernels.  The choice depends on T

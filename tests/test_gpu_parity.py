@@ -661,8 +661,8 @@ def test_split_mode_parity(wdt, E, S, k, H, F, Ts, shared, q):
 
 @pytest.mark.parametrize("wdt,E,S,k,H,F,Ts,shared", [
     (1, 8, 4, 2, 512, 256, [8, 16, 20, 48], False),   # bf16: the automatic rule takes the GEMM from 5 pairs per expert
-    (2, 16, 6, 4, 256, 256, [4, 8, 16], True),        # fp8 + shared: from 2
-    (3, 16, 8, 4, 256, 512, [8, 12, 32], False),      # MXFP4: from 3
+    (2, 64, 12, 2, 256, 256, [2, 3, 4, 16], True),    # fp8 + shared: from 1/8
+    (3, 16, 8, 4, 256, 512, [2, 3, 4, 12], False),    # MXFP4: from 1
 ])
 def test_ffn_path_choice_parity(wdt, E, S, k, H, F, Ts, shared):
     """The same calls through the decode kernels, the grouped GEMM and the automatic choice: each within
@@ -674,7 +674,7 @@ def test_ffn_path_choice_parity(wdt, E, S, k, H, F, Ts, shared):
     layers = [GpuLayer(E, S_, k, H, F, wdt, max(Ts), host, wr, b, shared=sh) for S_ in (S, E)]
     ol = oracle.Layer(E, E, k, H, F, wdt, host, wr, b, shared=sh)
     xs = synth.tokens(57, 3, max(Ts), H, len(Ts), 0.0, wdt)
-    per = {1: 5, 2: 2, 3: 3}[wdt]
+    c8 = {1: 40, 2: 1, 3: 8}[wdt]  # the GEMM from c8 / 8 pairs per expert
     try:
         for s, T in enumerate(Ts):
             x = np.ascontiguousarray(xs[s][:T])
@@ -691,7 +691,7 @@ def test_ffn_path_choice_parity(wdt, E, S, k, H, F, Ts, shared):
                     y = to_np(gl.y[:T])
                     assert row_rel_err(y, r["y64"], wdt) <= TOL[wdt], (T, li, path)
                     outs[(li, path)] = y
-            want = m.FFN_GEMM if T * k >= per * E else m.FFN_DECODE
+            want = m.FFN_GEMM if 8 * T * k >= c8 * E else m.FFN_DECODE
             assert np.array_equal(outs[(0, m.FFN_AUTO)], outs[(0, want)]), T
             for path in (m.FFN_DECODE, m.FFN_GEMM, m.FFN_AUTO):  # slot-count invariance on every path
                 assert np.array_equal(outs[(0, path)], outs[(1, path)]), (T, path)

@@ -16,8 +16,8 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("wdt,E,S,k,H,F,Ts,shared", [
     (1, 32, 10, 4, 512, 256, [24, 1], False),    # batch kernels, then the single-token kernels
-    (2, 16, 6, 4, 256, 256, [80, 9, 3], True),   # fp8 grouped GEMM (> 64 tokens; 9 tokens: 2.25 pairs per
-                                                 # expert, the GEMM too), then a 3-token decode batch
+    (2, 64, 12, 2, 256, 256, [80, 9, 3], True),  # fp8 grouped GEMM (> 64 tokens; 9 tokens: 0.28 pairs per
+                                                 # expert, the GEMM too), then a 3-token decode batch (0.09)
     (0, 8, 4, 2, 64, 128, [6, 3], False),        # fp32 kernels
     (3, 16, 8, 4, 256, 512, [40, 2], True),      # MXFP4: 40 tokens take the GEMM, 2 the decode kernels
 ])
