@@ -1,8 +1,8 @@
 // Grouped expert FFN over the slot tensor, with the top-k weighted combine.
 //
 // xinfer-ai 0.14.6 docs/moe_offload.md, "How it works": the expert GEMMs read a
-// [num_slots, N, K] slot tensor instead of [num_experts, N, K]; placement never
-// changes precision.  Per (token t, choice j) with record r = slot_ids[t][j]:
+// [num_slots, N, K] slot tensor instead of [num_experts, N, K]; which slot an
+// expert sits in leaves the arithmetic unchanged.  Per (token t, choice j) with record r = slot_ids[t][j]:
 //     h = silu(Wg x_t) * (Wu x_t),  o = Wd h,  y_t = sum_j w[t][j] o  (+ shared expert)
 //
 // Kernels (one launch each, fixed grids, no communication between workgroups):

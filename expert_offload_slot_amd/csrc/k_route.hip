@@ -1,8 +1,9 @@
 // Router: logits, top-k, renormalised softmax weights.
 //
 // The pages only say experts are "routed" (xinfer-ai 0.14.6 docs/moe_offload.md,
-// opening paragraph: placement never changes routing).  The logit is taken in
-// binary32 in one fixed order so the integer top-k decision is reproducible:
+// opening paragraph: where experts sit does not alter which ones are chosen).
+// The logit is taken in binary32 in one fixed order so the integer top-k
+// decision is reproducible:
 // a wavefront's 64 lanes each own every 64th chunk of 8 inputs and run an FMA
 // chain over them, then an xor-butterfly (offsets 32..1) combines the lanes,
 // then the bias is added.  This maps one (token, expert) dot product onto one

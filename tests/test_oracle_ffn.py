@@ -8,8 +8,8 @@
     weight is a bf16 value) give bitwise identical oracle outputs;
   * placement invariance: outputs through the oracle's own slot copies are
     bitwise identical at every slot count S = k..E and with every call
-    staged, and equal the cache-free result (the pages' statement that
-    placement never changes routing or precision);
+    staged, and equal the cache-free result (the pages' point that which
+    slot an expert occupies affects neither the routing nor the arithmetic);
   * special cases: x = 0 gives y = 0; k = 1 gives one expert's output;
     zero down-projection gives 0.
 """
