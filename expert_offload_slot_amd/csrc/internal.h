@@ -101,11 +101,13 @@ struct moe_offload {
   int32_t* pinned_i32;       // small pinned host scratch
   moe::Prof* prof;           // per-kernel timing, created on first enable
   int ffn_path;              // MOE_FFN_AUTO / DECODE / GEMM (moe_offload_set_ffn_path)
+  int n_pinned;              // size of the pinned set (moe_offload_pin)
   // host-computed cold experts (allocated when the cold mode is first switched on)
   bool cold_on;              // host mirror of the device word: nonzero
   bool cold_split;           // ... and in split mode (the copies run beside the host's share)
   hipStream_t cold_stream;   // split mode: the call's indices and activations go to the host on it
-  hipEvent_t ens_ev;         // split mode: recorded after each ensure (the indices are final)
+  hipEvent_t ens_ev;         // split mode: recorded after an ensure whose call may overflow (the indices are final)
+  bool ens_recorded;         // ... and the last ensure did record it (the FFN's host path then waits on it)
   int32_t* cold_sid;         // pinned host [max_tokens * k]: the call's record indices
   void* cold_x;              // pinned host [max_tokens * H]: the call's activations
   float* cold_out;           // pinned, mapped, coherent host [max_tokens * k][H]: cold pairs' outputs

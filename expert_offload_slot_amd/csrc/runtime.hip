@@ -344,13 +344,27 @@ int moe_route_topk(moe_offload* h, const void* x, const void* w_router, const fl
   return MOE_OK;
 }
 
+// Split mode: a call of at most S - (pinned experts) pairs has at most that many distinct experts,
+// never more than the slots it may claim, so it cannot overflow and none of its misses goes to the
+// host; moe_slot_ffn_host_cold runs it as the plain FFN.
+static bool split_call_fits(const moe_offload* h, int T) {
+  return (int64_t)T * h->k <= h->S - h->n_pinned;
+}
+
+// split mode, after a call's ensure: a call that may overflow records the event its FFN's host
+// path waits on before reading the call's indices (on the side stream)
+static hipError_t record_split_ensure(moe_offload* h, int T, hipStream_t s) {
+  h->ens_recorded = h->cold_split && !split_call_fits(h, T);
+  return h->ens_recorded ? hipEventRecord(h->ens_ev, s) : hipSuccess;
+}
+
 int moe_slot_ensure(moe_offload* h, const int32_t* ids, int32_t T, int32_t* slot_ids, void* stream) {
   if (int rc = check_handle(h)) return rc;
   if (int rc = check_T(h, T)) return rc;
   if (!ids || !slot_ids) return fail(MOE_EINVAL, "moe_slot_ensure: null pointer");
   DeviceGuard g(h->device);
   HIP_TRY(moe::launch_ensure(h, ids, T * h->k, slot_ids, (hipStream_t)stream));
-  if (h->cold_split) HIP_TRY(hipEventRecord(h->ens_ev, (hipStream_t)stream));
+  HIP_TRY(record_split_ensure(h, T, (hipStream_t)stream));
   return MOE_OK;
 }
 
@@ -381,11 +395,19 @@ int moe_slot_ffn_host_cold(moe_offload* h, const void* x, const int32_t* slot_id
   if (!h->cold_out) return fail(MOE_EINVAL, "moe_slot_ffn_host_cold: the cold mode was never switched on");
   DeviceGuard g(h->device);
   hipStream_t s = (hipStream_t)stream;
+  // split mode, a call that cannot overflow: the plain FFN, with no host round trip (the same
+  // kernels as moe_slot_ffn)
+  if (h->cold_split && split_call_fits(h, T)) {
+    HIP_TRY(moe::launch_ffn(h, x, slot_ids, w, T, shared_record, y, residual, x_next, nullptr, 0.f, s));
+    return MOE_OK;
+  }
   const size_t es = h->dtype == MOE_F32 ? 4 : 2;
   // the call's record indices and activations to the host, then the GPU's share of the FFN; in split
   // mode on a stream of their own from the ensure on, so the host's share runs beside the copy kernel
-  hipStream_t ds = h->cold_split ? h->cold_stream : s;
-  if (h->cold_split) HIP_TRY(hipStreamWaitEvent(ds, h->ens_ev, 0));
+  // (on the side stream only after an ensure that recorded its event; otherwise in stream order)
+  hipStream_t ds = h->cold_split && h->ens_recorded ? h->cold_stream : s;
+  if (ds != s) HIP_TRY(hipStreamWaitEvent(ds, h->ens_ev, 0));
+  h->ens_recorded = false;
   HIP_TRY(hipMemcpyAsync(h->cold_sid, slot_ids, 4 * (size_t)T * h->k, hipMemcpyDeviceToHost, ds));
   HIP_TRY(hipMemcpyAsync(h->cold_x, x, es * (size_t)T * h->H, hipMemcpyDeviceToHost, ds));
   HIP_TRY(hipEventRecord(h->cold_ev, ds));
@@ -460,7 +482,7 @@ int moe_prefill_stage(moe_offload* h, const int32_t* ids, int32_t T, int32_t* sl
     HIP_TRY(moe::launch_copy(h, h->cache.copy_list, s));
     if (staged_out) *staged_out = 0;
   }
-  if (h->cold_split) HIP_TRY(hipEventRecord(h->ens_ev, s));  // the indices are final
+  HIP_TRY(record_split_ensure(h, T, s));  // the indices are final
   return MOE_OK;
 }
 
@@ -481,6 +503,7 @@ int moe_offload_pin(moe_offload* h, const int32_t* experts, int32_t n, void* str
   DeviceGuard g(h->device);
   HIP_TRY(moe::launch_pin(h, experts, n, (hipStream_t)stream));
   HIP_TRY(moe::launch_copy(h, h->cache.copy_list, (hipStream_t)stream));
+  h->n_pinned = n;
   return MOE_OK;
 }
 

@@ -349,6 +349,9 @@ int moe_offload_set_cold(moe_offload* h, int32_t mode, void* stream, int32_t* ch
  * moe_slot_ensure is enqueued (they are whenever x fed moe_route_topk before
  * it): the host reads the call's indices and activations on a stream of its
  * own as soon as the ensure has run, so its share overlaps the copy kernel.
+ * A call of at most S - P pairs (P: the size of the pinned set) cannot
+ * overflow: moe_slot_ffn_host_cold runs it as moe_slot_ffn would, with no host
+ * round trip, and its outputs are those of moe_slot_ffn bit for bit.
  * Host-synchronising on `stream`; MOE_COLD_OFF (moe_offload_set_cold) ends it.
  * Errors: MOE_EINVAL (q outside [0, 256]), MOE_ENOMEM, MOE_EHIP. */
 int moe_offload_set_split(moe_offload* h, int32_t q, void* stream);

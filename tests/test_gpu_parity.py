@@ -659,6 +659,47 @@ def test_split_mode_parity(wdt, E, S, k, H, F, Ts, shared, q):
         gl.close()
 
 
+def test_split_mode_small_calls_take_the_plain_ffn():
+    """Split mode: a call of at most S - P pairs (P pinned experts) cannot overflow, so
+    moe_slot_ffn_host_cold runs it with no host round trip: outputs bit for bit those of a twin layer
+    with the mode off, tables and lists bit-exact against the oracle's split rule.  With P = 3 pinned,
+    3-token calls (6 pairs > S - P = 5) take the host path again and stay within tolerance."""
+    E, S, k, H, F, wdt = 16, 8, 2, 256, 512, 1
+    host, wr, b, _ = make_layer_inputs(58, 0, E, H, F, wdt, 1.2)
+    split = GpuLayer(E, S, k, H, F, wdt, 4, host, wr, b)
+    plain = GpuLayer(E, S, k, H, F, wdt, 4, host, wr, b)
+    ol = oracle.Layer(E, S, k, H, F, wdt, host, wr, b)
+    st = torch.cuda.current_stream()
+    Ts = [1, 2, 4, 1, 3, 4, 2, 3, 2, 3]
+    xs = synth.tokens(58, 2, 4, H, len(Ts), 0.0, wdt)
+    try:
+        m.moe_offload_set_split(split.h, 128, st)
+        ol.cache.set_split(128)
+        for s, T in enumerate(Ts):
+            if s == 6:  # pin 3 experts on both layers and in the oracle: S - P = 5
+                P = np.array([0, 5, 9], np.int32)
+                for gl in (split, plain):
+                    m.moe_offload_pin(gl.h, to_dev(P), len(P), st)
+                ol.cache.copy(0, ol.cache.pin(P))
+            x = np.ascontiguousarray(xs[s][:T])
+            xd = to_dev(x)
+            for gl in (split, plain):
+                gl.route(xd, T)
+                gl.ensure(T)
+                gl.copy()
+            m.moe_slot_ffn_host_cold(split.h, xd, split.slot_ids, split.w, T, None, split.y, None, split.xn, st)
+            plain.ffn(xd, T)
+            r = ol.step(x)
+            compare_call(split, r, T, r["y64"], oracle_cache=ol.cache)
+            if T * k <= S - (3 if s >= 6 else 0):
+                assert np.array_equal(to_np(split.y[:T]), to_np(plain.y[:T])), (s, T)
+                assert np.array_equal(to_np(split.xn[:T]), to_np(plain.xn[:T])), (s, T)
+        assert split.stats()["error"] == 0
+    finally:
+        split.close()
+        plain.close()
+
+
 @pytest.mark.parametrize("wdt,E,S,k,H,F,Ts,shared", [
     (1, 8, 4, 2, 512, 256, [8, 16, 20, 48], False),   # bf16: the automatic rule takes the GEMM from 5 pairs per expert
     (2, 64, 12, 2, 256, 256, [2, 3, 4, 16], True),    # fp8 + shared: from 1/8
