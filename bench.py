@@ -26,6 +26,9 @@ replays, from empty caches.  The same line carries, measured in the same run:
   * router-lookahead prefetch against none, LRU against scored eviction and
     pinned placement, decode at 10/20/40/100 % slots (outputs bitwise
     identical at every fraction);
+  * misses computed on the host CPU (split and cold mode) at batch 1, 8 and
+    32, through the entry points and inside the graph (the chain's host
+    thread);
   * the MXFP4 records, the Mixtral-8x7B-shaped layer at 2/4/6 slots and the
     DeepSeek-V3-shaped fp8 layer (decode at batch 16, the 2048-token prefill:
     staging copy, FFN TFLOP/s and the fraction of its attainable roofline);
@@ -303,7 +306,8 @@ def main():
         print(json.dumps({"workload": "qwen3-30b-a3b-shaped offloaded MoE decode, 48 layers, batch 1, 8 and 32, eager "
                                       "entry-point calls: misses over the link, split with the host CPU, or on "
                                       "the host (from an empty cache, or after a warm-up over the link)",
-                          "host_split": host_split_compare(args, m, torch, handles, wr_d, b_d, token_stream)}),
+                          "host_split": host_split_compare(args, m, torch, handles, wr_d, b_d, token_stream),
+                          "host_chain": host_chain_compare(args, m, torch, hip, handles, wr_d, b_d, token_stream)}),
               flush=True)
         for h in reversed(handles):
             m.moe_offload_destroy(h)
@@ -510,6 +514,7 @@ def main():
         result["eviction"] = eviction_compare(args, m, hip, torch, handles, wr_d, b_d, run_decode, token_stream)
         result["slot_fractions"] = slot_fraction_compare(args, m, hip, handles, run_decode, token_stream)
         result["host_split"] = host_split_compare(args, m, torch, handles, wr_d, b_d, token_stream)
+        result["host_chain"] = host_chain_compare(args, m, torch, hip, handles, wr_d, b_d, token_stream)
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args, handles, routers, stride, T0)
@@ -905,6 +910,71 @@ def host_split_compare(args, m, torch, handles, wr_d, b_d, token_stream, batches
                                        "host_us_per_record_median": round(float(np.median([x[1] for x in qs])), 1),
                                        "link_us_per_record_median": round(float(np.median([x[2] for x in qs])), 1)}
         res["steps"] = "%d-%d after %d untimed" % (warm, warm + steps - 1, warm)
+        out["batch%d" % T] = res
+    return out
+
+
+def host_chain_compare(args, m, torch, hip, handles, wr_d, b_d, token_stream, batches=(1, 8, 32), warm=24, steps=8):
+    """The same comparison inside the decode chain (one HIP graph per step; the host's share runs on the
+    chain's host thread, with no host synchronisation): batch 1, 8 and 32, each mode from empty caches,
+    `warm` untimed steps, one more untimed step after a mode switch (the graph is captured again), then
+    `steps` timed ones, waited for with a blocking event (the calling thread sleeps rather than spins, so
+    the host FFN has every core):
+      link       every miss over the host link (read-through);
+      split      calls wider than the cache send the measured share of their staged misses to the host;
+      cold_warm  the warm-up over the link (the cache learns), then every miss on the host.
+    Wall-clock tok/s."""
+    out = {}
+    st = torch.cuda.current_stream()
+    for T in batches:
+        xs = token_stream(T, warm + steps + 1)
+        res = {}
+        for mode in ("link", "split", "cold_warm"):
+            for h in handles:
+                m.moe_offload_set_cold(h, m.COLD_OFF, st)
+                m.moe_offload_reset(h, st)
+            if mode == "split":
+                for h in handles:
+                    m.moe_offload_set_cold(h, m.COLD_SPLIT, st)
+            c = m.moe_chain_create(handles, wr_d, b_d, T, 0)
+            bufs = m.moe_chain_get_buffers(c)
+            try:
+                def step(s_):
+                    assert hip.hipMemcpyAsync(bufs["x"], xs[s_].data_ptr(), T * H * 2, 3, st.cuda_stream) == 0
+                    m.moe_chain_run(c, st)
+
+                for s_ in range(warm):
+                    step(s_)
+                torch.cuda.synchronize()
+                if mode == "cold_warm":
+                    for h in handles:
+                        m.moe_offload_set_cold(h, m.COLD_ON, st)
+                step(warm)  # untimed: a switched mode captures the graph again
+                torch.cuda.synchronize()
+                before = [m.moe_offload_stats(h) for h in handles]
+                done = torch.cuda.Event(blocking=True)  # this thread sleeps: every core is left to the host FFN
+                t0 = time.perf_counter()
+                for s_ in range(warm + 1, warm + 1 + steps):
+                    step(s_)
+                done.record(st)
+                done.synchronize()
+                dt = time.perf_counter() - t0
+                after = [m.moe_offload_stats(h) for h in handles]
+            finally:
+                m.moe_chain_destroy(c)
+            assert all(a_["error"] == 0 for a_ in after), [a_["error"] for a_ in after]
+            d = {kk: sum(a_[kk] - b_[kk] for a_, b_ in zip(after, before)) for kk in after[0]}
+            res[mode] = {"tokens_per_s": round(T * steps / dt, 2), "ms_per_step": round(dt * 1e3 / steps, 3),
+                         "link_records_per_token": round((d["misses"] + d["staged_copies"]) / (T * steps), 3),
+                         "host_records_per_token": round(d["cold_misses"] / (T * steps), 3)}
+            log("host-offload chain b%d %s: %.1f tok/s, %.2f records/token over the link, %.2f on the host" %
+                (T, mode, res[mode]["tokens_per_s"], res[mode]["link_records_per_token"],
+                 res[mode]["host_records_per_token"]))
+        for h in handles:
+            m.moe_offload_set_cold(h, m.COLD_OFF, st)
+            m.moe_offload_reset(h, st)
+        torch.cuda.synchronize()
+        res["steps"] = "%d-%d after %d untimed (+1 after a mode switch)" % (warm + 1, warm + steps, warm)
         out["batch%d" % T] = res
     return out
 

@@ -20,7 +20,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe_offload.h")
 F32, BF16, FP8, MXFP4 = 0, 1, 2, 3
 MODE_SLOTS, MODE_STAGED, MODE_STAGED_ALL = 0, 1, 2
 FLAG_AUDIT, FLAG_HOST_COHERENT, FLAG_SCORED, FLAG_FREQ = 1, 2, 4, 8
-DEV_ERR_BAD_ID, DEV_ERR_NAN, DEV_ERR_AUDIT = 1, 2, 4
+DEV_ERR_BAD_ID, DEV_ERR_NAN, DEV_ERR_AUDIT, DEV_ERR_HOST_TIMEOUT = 1, 2, 4, 8
 EINVAL, ENOMEM, EHIP, EUNSUPPORTED, EDEVICE = -1, -2, -3, -4, -5
 
 

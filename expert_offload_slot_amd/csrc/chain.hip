@@ -11,15 +11,31 @@
 // only the prefetch copy runs on a side stream.  (Calls with more than
 // kDecideMaxPairs (t, j) pairs use the separate kernels and a predictor stream.)
 //
+// Layers in cold or split mode join the chain too (npu-offload README,
+// "Architecture": per layer the accelerator computes the resident experts while
+// the host CPU computes the cold ones from host DRAM): after the control step a
+// one-workgroup kernel publishes the call's record indices and activations into
+// pinned host memory and bumps the layer's request number; a host server thread
+// (host_ffn.cpp) computes the pairs whose record index is S + E + e into the
+// layer's host rows and stores the request number as the layer's done number;
+// after the GPU's own FFN launches, a one-workgroup kernel waits for that number
+// (bounded: past half a second or so it sets MOE_DEV_ERR_HOST_TIMEOUT and goes on)
+// and a workgroup per host-computed pair copies its row into the layer's fp32
+// outputs before the combine.
+// A call without such pairs publishes nothing and waits for nothing.
+//
 // xinfer-ai 0.14.6 docs/moe_offload.md, "How it works", Decode (the step stays
 // inside a captured graph, no host sync); FreeToken issue #677, "Proposal"
 // (Lookahead, Install, Correctness constraint: every slot-table writer on the
 // compute stream, only reads and byte copies on the other streams).
 #include <string.h>
 
+#include <algorithm>
 #include <new>
+#include <string>
 #include <vector>
 
+#include "host_ffn.h"
 #include "internal.h"
 
 struct moe_chain {
@@ -44,6 +60,22 @@ struct moe_chain {
   hipEvent_t ev_sp_done = nullptr, ev_sf_done = nullptr;
   hipGraph_t graph = nullptr;
   hipGraphExec_t exec = nullptr;
+  // host-computed experts: per layer, whether the issued step publishes its calls to the host
+  // (the state the graph was captured with); the pinned buffers shared with the server thread
+  std::vector<char> cold;
+  void* cold_block = nullptr;  // pinned, mapped, coherent host memory
+  int32_t* pub_sid = nullptr;  // [L][T*k] (device addresses of the same bytes: *_d)
+  uint8_t* pub_x = nullptr;    // [L][T][H]
+  float* cold_out = nullptr;   // [L][T*k][H]
+  uint32_t* req = nullptr;     // [L]
+  uint32_t* done = nullptr;    // [L]
+  int32_t* pub_sid_d = nullptr;
+  uint8_t* pub_x_d = nullptr;
+  float* cold_out_d = nullptr;
+  uint32_t* req_d = nullptr;
+  uint32_t* done_d = nullptr;
+  uint32_t* seq = nullptr;     // device [L]: each layer's last request number
+  moe::ColdServer* server = nullptr;
 };
 
 namespace {
@@ -55,6 +87,86 @@ int cfail(int code, const char* msg) { return moe::set_error(code, msg); }
     hipError_t e_ = (call);                            \
     if (e_ != hipSuccess) return e_;                   \
   } while (0)
+
+// ------------------------------------------------------------------ host-computed experts
+constexpr uint32_t kColdMaxPolls = 1u << 19;  // half a second or more of polls of the done number
+
+__device__ __forceinline__ bool is_cold(int r, int S, int E) { return r >= S + E && r < S + 2 * E; }
+
+// One workgroup: when the call has a host-computed pair, copies its record indices, and the
+// activation rows of the tokens that have such a pair, into the pinned host buffers, then (after a
+// system-scope fence by every thread) stores the next request number, also kept in seq for the wait.
+__global__ __launch_bounds__(1024) void k_cold_publish(const int32_t* __restrict__ sid, int T, int k, int S, int E,
+                                                       const uint4* __restrict__ x, int row16, int32_t* pub_sid,
+                                                       uint4* pub_x, uint32_t* req, uint32_t* seq) {
+  const int n = T * k;
+  bool mine = false;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int r = sid[i];
+    mine |= is_cold(r, S, E);
+    pub_sid[i] = r;
+  }
+  if (!__syncthreads_or(mine)) return;  // workgroup-uniform: nothing for the host, nothing published
+  for (int t = 0; t < T; ++t) {
+    bool row = false;
+    for (int j = 0; j < k; ++j) row |= is_cold(sid[t * k + j], S, E);  // uniform
+    if (!row) continue;
+    for (int i = threadIdx.x; i < row16; i += blockDim.x) pub_x[(size_t)t * row16 + i] = x[(size_t)t * row16 + i];
+  }
+  __threadfence_system();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t r = *seq + 1;
+    *seq = r;
+    __hip_atomic_store(req, r, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
+
+// One workgroup: when the call has a host-computed pair, waits until the host's done number equals
+// the request number (bounded).  The polls are relaxed system-scope loads, which read memory
+// without invalidating the caches each time.
+__global__ __launch_bounds__(256) void k_cold_wait(const int32_t* __restrict__ sid, int n, int S, int E,
+                                                   const uint32_t* done, const uint32_t* __restrict__ seq,
+                                                   int32_t* err) {
+  bool mine = false;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) mine |= is_cold(sid[i], S, E);
+  if (!__syncthreads_or(mine) || threadIdx.x != 0) return;
+  const uint32_t r = *seq;
+  uint32_t polls = 0;
+  while (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != r) {
+    if (++polls == kColdMaxPolls) {
+      atomicOr(err, MOE_DEV_ERR_HOST_TIMEOUT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(8);
+  }
+}
+
+// 16 bytes of host memory with two relaxed system-scope loads: read from memory, past any cached copy
+__device__ __forceinline__ float4 load_host16(const float4* p) {
+  const uint64_t* q = reinterpret_cast<const uint64_t*>(p);
+  const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  return make_float4(__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                     __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32)));
+}
+
+// After k_cold_wait (stream order: the host's rows were stored before its done number): a workgroup
+// per host-computed pair copies its host row into part.
+__global__ __launch_bounds__(256) void k_cold_rows(const int32_t* __restrict__ sid, int n, int S, int E, int H,
+                                                   const float4* rows, float4* __restrict__ part) {
+  const int h4 = H / 4;
+  for (int p = blockIdx.x; p < n; p += gridDim.x) {
+    if (!is_cold(sid[p], S, E)) continue;  // workgroup-uniform
+    for (int i = threadIdx.x; i < h4; i += blockDim.x) part[(size_t)p * h4 + i] = load_host16(rows + (size_t)p * h4 + i);
+  }
+}
+
+// whether layer h's calls of T tokens may have host-computed pairs: cold mode, or split mode for calls
+// that can overflow (more pairs than the slots they may claim)
+bool needs_host(const moe_offload* h, int T) {
+  return h->cold_on && !(h->cold_split && (int64_t)T * h->k <= h->S - h->n_pinned);
+}
 
 uint8_t* X(moe_chain* c, int l) { return c->x + (size_t)l * c->T * c->H * c->act; }
 uint8_t* XN(moe_chain* c, int l) { return c->xn + (size_t)l * c->T * c->H * c->act; }
@@ -116,6 +228,14 @@ hipError_t issue(moe_chain* c, hipStream_t cs) {
         CHK(moe::launch_install(hn, c->pred + R(c, l + 1), T, c->prefetch_n, cs));
       }
     }
+    const bool cold = c->cold[l] != 0;
+    if (cold) {  // the call's host-computed pairs go to the server thread
+      const size_t xrow = (size_t)c->H * c->act;
+      hipLaunchKernelGGL(k_cold_publish, dim3(1), dim3(1024), 0, cs, (const int32_t*)(c->sid + R(c, l)), T, c->k,
+                         h->S, h->E, (const uint4*)XN(c, l), (int)(xrow / 16), c->pub_sid_d + R(c, l),
+                         (uint4*)(c->pub_x_d + (size_t)l * T * xrow), c->req_d + l, c->seq + l);
+      CHK(hipGetLastError());
+    }
     if (pf && l >= 1) CHK(hipStreamWaitEvent(cs, c->ev_pf[l], 0));  // this layer's prefetch copy first
     // a decode step's misses are read through by its FFN launches instead of a copy launch
     const bool fill = c->read_through && moe::ffn_reads_through(h, T);
@@ -126,9 +246,21 @@ hipError_t issue(moe_chain* c, hipStream_t cs) {
       CHK(moe::launch_copy(hn, hn->cache.pf_list, c->sf));
       CHK(hipEventRecord(c->ev_pf[l + 1], c->sf));
     }
+    const bool combine = !(fuse_cl && l + 1 < c->L);
+    void* xn_next = l + 1 < c->L ? XN(c, l + 1) : nullptr;
     CHK(moe::launch_ffn(h, XN(c, l), c->sid + R(c, l), c->w + R(c, l), T, c->shared[l], Y(c, l), X(c, l), X(c, l + 1),
-                        l + 1 < c->L ? XN(c, l + 1) : nullptr, kRmsEps, cs, fused, !(fuse_cl && l + 1 < c->L),
-                        fill));
+                        xn_next, kRmsEps, cs, fused, combine && !cold, fill));
+    if (cold) {  // the host's rows join the GPU's before the combine
+      hipLaunchKernelGGL(k_cold_wait, dim3(1), dim3(256), 0, cs, (const int32_t*)(c->sid + R(c, l)), n, h->S, h->E,
+                         (const uint32_t*)(c->done_d + l), (const uint32_t*)(c->seq + l), h->cache.err);
+      CHK(hipGetLastError());
+      hipLaunchKernelGGL(k_cold_rows, dim3(std::min(n, 256)), dim3(256), 0, cs, (const int32_t*)(c->sid + R(c, l)), n,
+                         h->S, h->E, c->H, (const float4*)(c->cold_out_d + R(c, l) * c->H), (float4*)h->part);
+      CHK(hipGetLastError());
+      if (combine)
+        CHK(moe::launch_combine(h, XN(c, l), c->w + R(c, l), T, c->shared[l], Y(c, l), X(c, l), X(c, l + 1), xn_next,
+                                kRmsEps, cs));
+    }
   }
   if (pf && c->L > 1) {  // rejoin the side streams (the predictor stream is used only without fusion)
     if (!fused) {
@@ -142,6 +274,9 @@ hipError_t issue(moe_chain* c, hipStream_t cs) {
 }
 
 void release(moe_chain* c) {
+  if (c->server) moe::cold_server_stop(c->server);  // after the device drained (the callers synchronise first)
+  c->server = nullptr;
+  if (c->cold_block) (void)hipHostFree(c->cold_block);
   if (c->exec) (void)hipGraphExecDestroy(c->exec);
   if (c->graph) (void)hipGraphDestroy(c->graph);
   for (auto* v : {&c->ev_x, &c->ev_pred, &c->ev_demand, &c->ev_pf})
@@ -187,13 +322,14 @@ int moe_chain_create(moe_offload* const* layers, int32_t L, const void* const* w
   c->prefetch_n = prefetch_n;
   c->device = l0->device;
   c->act = l0->dtype == MOE_F32 ? 4 : 2;
+  c->cold.assign(L, 0);
   int prev = 0;
   (void)hipGetDevice(&prev);
   (void)hipSetDevice(c->device);
   const size_t xa = (size_t)(L + 1) * T * c->H * c->act, ya = (size_t)L * T * c->H * c->act;
   const size_t ra = (size_t)L * T * c->k * 4;
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
-  const size_t total = al(xa) + 2 * al(ya) + 5 * al(ra);
+  const size_t total = al(xa) + 2 * al(ya) + 5 * al(ra) + al(4 * (size_t)L);
   hipError_t e = hipMalloc(&c->block, total);
   if (e == hipSuccess) e = hipMemset(c->block, 0, total);
   if (e == hipSuccess) {
@@ -207,6 +343,7 @@ int moe_chain_create(moe_offload* const* layers, int32_t L, const void* const* w
     c->sid = (int32_t*)(r + 2 * al(ra));
     c->pred = (int32_t*)(r + 3 * al(ra));
     c->wpred = (float*)(r + 4 * al(ra));
+    c->seq = (uint32_t*)(r + 5 * al(ra));
     e = hipStreamCreateWithFlags(&c->cs, hipStreamNonBlocking);
   }
   if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->sp, hipStreamNonBlocking);
@@ -241,21 +378,90 @@ int moe_chain_get_buffers(const moe_chain* c, moe_chain_buffers* out) {
   return MOE_OK;
 }
 
-// the decode chain runs without a host round trip: a layer in cold mode cannot join it
-static bool any_cold(const moe_chain* c) {
-  for (const moe_offload* h : c->layers)
-    if (h->cold_on) return true;
-  return false;
+// Which layers publish their calls to the host now (cold mode, or split mode with calls that can
+// overflow); on the first such layer, the pinned buffers and the server thread.  *changed: the
+// set differs from the one the chain was last issued with (a captured graph is then stale).
+static int prepare_cold(moe_chain* c, const char* who, bool* changed) {
+  std::vector<char> now(c->L, 0);
+  bool any = false;
+  for (int l = 0; l < c->L; ++l) {
+    now[l] = needs_host(c->layers[l], c->T);
+    any = any || now[l];
+  }
+  if (any && c->prefetch_n > 0)
+    return moe::set_error(MOE_EINVAL, (std::string(who) + ": lookahead prefetch with a layer in cold or split mode")
+                                          .c_str());
+  *changed = now != c->cold;
+  if (any && !c->cold_block) {
+    const size_t L = c->L, n = (size_t)c->T * c->k;
+    auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+    const size_t flags = al(8 * L), sid = al(4 * L * n), xb = al(L * c->T * c->H * c->act), ob = 4 * L * n * c->H;
+    hipError_t e = hipHostMalloc(&c->cold_block, flags + sid + xb + ob, hipHostMallocMapped | hipHostMallocCoherent);
+    uint8_t* d = nullptr;
+    if (e == hipSuccess) {
+      memset(c->cold_block, 0, flags + sid + xb + ob);
+      e = hipHostGetDevicePointer((void**)&d, c->cold_block, 0);
+    }
+    if (e != hipSuccess) {
+      if (c->cold_block) (void)hipHostFree(c->cold_block);
+      c->cold_block = nullptr;
+      return moe::set_error(e == hipErrorOutOfMemory ? MOE_ENOMEM : MOE_EHIP, hipGetErrorString(e));
+    }
+    uint8_t* b = (uint8_t*)c->cold_block;
+    c->req = (uint32_t*)b;
+    c->done = c->req + L;
+    c->pub_sid = (int32_t*)(b + flags);
+    c->pub_x = b + flags + sid;
+    c->cold_out = (float*)(b + flags + sid + xb);
+    c->req_d = (uint32_t*)d;
+    c->done_d = c->req_d + L;
+    c->pub_sid_d = (int32_t*)(d + flags);
+    c->pub_x_d = d + flags + sid;
+    c->cold_out_d = (float*)(d + flags + sid + xb);
+  }
+  if (any && !c->server) {
+    // the device request counters restart with the host's numbers
+    hipError_t e = hipMemset(c->seq, 0, 4 * (size_t)c->L);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return moe::set_error(MOE_EHIP, hipGetErrorString(e));
+    memset(c->cold_block, 0, 8 * (size_t)c->L);
+    std::vector<moe::ColdChainLayer> ls(c->L);
+    for (int l = 0; l < c->L; ++l) {
+      const moe_offload* h = c->layers[l];
+      ls[l] = {h->host, (uint64_t)h->record_stride, h->dtype, h->H, h->F, h->k, h->S, h->E};
+    }
+    moe::ColdChainIo io;
+    io.sid = c->pub_sid;
+    io.x = c->pub_x;
+    io.out = c->cold_out;
+    io.req = c->req;
+    io.done = c->done;
+    c->server = moe::cold_server_start(ls.data(), c->L, c->T, (uint64_t)c->H * c->act, io);
+    if (!c->server) return moe::set_error(MOE_ENOMEM, (std::string(who) + ": cannot start the host thread").c_str());
+  }
+  c->cold = now;
+  return MOE_OK;
 }
 
 int moe_chain_run(moe_chain* c, void* stream) {
   if (!c) return cfail(MOE_EINVAL, "moe_chain_run: null chain");
-  if (any_cold(c)) return cfail(MOE_EINVAL, "moe_chain_run: a layer is in cold mode (host-computed experts)");
   int prev = 0;
   (void)hipGetDevice(&prev);
   (void)hipSetDevice(c->device);
+  bool changed = false;
+  if (int rc = prepare_cold(c, "moe_chain_run", &changed)) {
+    (void)hipSetDevice(prev);
+    return rc;
+  }
   hipError_t e = hipSuccess;
-  if (!c->exec) {
+  if (changed && c->exec) {  // the graph was captured with another set of host-computed layers
+    e = hipDeviceSynchronize();
+    (void)hipGraphExecDestroy(c->exec);
+    (void)hipGraphDestroy(c->graph);
+    c->exec = nullptr;
+    c->graph = nullptr;
+  }
+  if (e == hipSuccess && !c->exec) {
     e = hipStreamBeginCapture(c->cs, hipStreamCaptureModeThreadLocal);
     if (e == hipSuccess) {
       hipError_t ei = issue(c, c->cs);
@@ -289,10 +495,21 @@ int moe_chain_set_read_through(moe_chain* c, int on) {
 
 int moe_chain_run_eager(moe_chain* c, void* stream) {
   if (!c) return cfail(MOE_EINVAL, "moe_chain_run_eager: null chain");
-  if (any_cold(c)) return cfail(MOE_EINVAL, "moe_chain_run_eager: a layer is in cold mode (host-computed experts)");
   int prev = 0;
   (void)hipGetDevice(&prev);
   (void)hipSetDevice(c->device);
+  bool changed = false;
+  if (int rc = prepare_cold(c, "moe_chain_run_eager", &changed)) {
+    (void)hipSetDevice(prev);
+    return rc;
+  }
+  if (changed && c->exec) {  // the captured graph is stale: it is recaptured at the next moe_chain_run
+    (void)hipDeviceSynchronize();
+    (void)hipGraphExecDestroy(c->exec);
+    (void)hipGraphDestroy(c->graph);
+    c->exec = nullptr;
+    c->graph = nullptr;
+  }
   hipError_t e = issue(c, (hipStream_t)stream);
   (void)hipSetDevice(prev);
   if (e != hipSuccess) return cfail(MOE_EHIP, hipGetErrorString(e));

@@ -448,4 +448,76 @@ void host_cold_ffn(const HostFfnJob& j) {
   });
 }
 
+// ---------------------------------------------------------------- decode-chain server
+class ColdServer {
+ public:
+  ColdServer(const ColdChainLayer* layers, int L, int T, uint64_t xrow, const ColdChainIo& io)
+      : layers_(layers, layers + L), L_(L), T_(T), xrow_(xrow), io_(io), last_(L) {
+    for (int l = 0; l < L; ++l) last_[l] = __atomic_load_n(&io_.req[l], __ATOMIC_ACQUIRE);
+    thread_ = std::thread([this] { loop(); });
+  }
+  ~ColdServer() {
+    stop_.store(true);
+    thread_.join();
+  }
+
+ private:
+  void loop() {
+    using clk = std::chrono::steady_clock;
+    auto idle_since = clk::now();
+    while (!stop_.load(std::memory_order_relaxed)) {
+      bool did = false;
+      for (int l = 0; l < L_; ++l) {
+        const uint32_t r = __atomic_load_n(&io_.req[l], __ATOMIC_ACQUIRE);
+        if (r == last_[l]) continue;
+        // request r of layer l: its indices and activations were stored before r was
+        const ColdChainLayer& c = layers_[l];
+        HostFfnJob j;
+        j.host = c.host;
+        j.stride = c.stride;
+        j.dtype = c.dtype;
+        j.H = c.H;
+        j.F = c.F;
+        j.x = io_.x + (size_t)l * T_ * xrow_;
+        j.T = T_;
+        j.k = c.k;
+        j.sid = io_.sid + (size_t)l * T_ * c.k;
+        j.S = c.S;
+        j.E = c.E;
+        j.out = io_.out + (size_t)l * T_ * c.k * c.H;
+        host_cold_ffn(j);
+        __atomic_store_n(&io_.done[l], r, __ATOMIC_RELEASE);  // after the rows
+        last_[l] = r;
+        did = true;
+      }
+      const auto now = clk::now();
+      if (did) {
+        idle_since = now;
+      } else if (now - idle_since > std::chrono::milliseconds(50)) {
+        std::this_thread::sleep_for(std::chrono::microseconds(100));
+      } else {
+        _mm_pause();
+      }
+    }
+  }
+
+  std::vector<ColdChainLayer> layers_;
+  int L_, T_;
+  uint64_t xrow_;
+  ColdChainIo io_;
+  std::vector<uint32_t> last_;
+  std::atomic<bool> stop_{false};
+  std::thread thread_;
+};
+
+ColdServer* cold_server_start(const ColdChainLayer* layers, int L, int T, uint64_t xrow, const ColdChainIo& io) {
+  try {
+    return new ColdServer(layers, L, T, xrow, io);
+  } catch (...) {
+    return nullptr;
+  }
+}
+
+void cold_server_stop(ColdServer* s) { delete s; }
+
 }  // namespace moe

@@ -197,5 +197,9 @@ hipError_t launch_set_cold(moe_offload* h, int word, hipStream_t s);
 // part rows of the call's cold pairs (record index >= S + E) from h->cold_out, then the combine
 hipError_t launch_cold_combine(moe_offload* h, const void* x, const int32_t* slot_ids, const float* w, int T,
                                const void* shared, void* y, const void* residual, void* x_next, hipStream_t s);
+// the top-k weighted combine of h->part alone (residual, and the next norm when xn_next is given),
+// as launch_ffn ends it
+hipError_t launch_combine(moe_offload* h, const void* x, const float* w, int T, const void* shared, void* y,
+                          const void* residual, void* x_next, void* xn_next, float eps, hipStream_t s);
 
 }  // namespace moe

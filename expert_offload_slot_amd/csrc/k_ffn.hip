@@ -1286,6 +1286,11 @@ hipError_t launch_cold_combine(moe_offload* h, const void* x, const int32_t* slo
   const int n = T * h->k;
   launch_k(h, MOE_K_COMBINE, k_cold_scatter, dim3(std::min(n, 1024)), dim3(256), 0, s, slot_ids, n, h->S, h->E, h->H,
            (const float*)h->cold_out_dev, h->part);
+  return launch_combine(h, x, w, T, shared, y, residual, x_next, nullptr, 0.f, s);
+}
+
+hipError_t launch_combine(moe_offload* h, const void* x, const float* w, int T, const void* shared, void* y,
+                          const void* residual, void* x_next, void* xn_next, float eps, hipStream_t s) {
   FfnArgs a;
   memset(&a, 0, sizeof a);
   a.x = x;
@@ -1300,9 +1305,9 @@ hipError_t launch_cold_combine(moe_offload* h, const void* x, const int32_t* slo
   a.H = h->H;
   a.F = h->F;
   if (h->dtype == MOE_F32)
-    launch_k(h, MOE_K_COMBINE, k_combine<true>, dim3(T), dim3(kRowThreads), 0, s, a, (void*)nullptr, 0.f);
+    launch_k(h, MOE_K_COMBINE, k_combine<true>, dim3(T), dim3(kRowThreads), 0, s, a, xn_next, eps);
   else
-    launch_k(h, MOE_K_COMBINE, k_combine<false>, dim3(T), dim3(kRowThreads), 0, s, a, (void*)nullptr, 0.f);
+    launch_k(h, MOE_K_COMBINE, k_combine<false>, dim3(T), dim3(kRowThreads), 0, s, a, xn_next, eps);
   return hipGetLastError();
 }
 

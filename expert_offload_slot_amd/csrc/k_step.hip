@@ -65,7 +65,8 @@ __global__ __launch_bounds__(kBlock) void k_decide(CacheDev c, const float* __re
   __syncthreads();
   ensure_body(c, t, ids_l, n, k, slot_ids, rec_l, audit, u.keys);
   __syncthreads();
-  if (do_group) group_body(rec_l, n, c.S + c.E, grp, off_pairs, off_tiles, c.err, u.g);
+  // host-computed pairs (index S + E + e, cold and split mode) stay out of every record list
+  if (do_group) group_body(rec_l, n, c.S + c.E, grp, off_pairs, off_tiles, c.err, u.g, c.S + 2 * c.E);
   for (int i = threadIdx.x; i < n; i += kBlock) {
     ids[i] = ids_l[i];
     w[i] = w_l[i];

@@ -101,7 +101,9 @@ enum {
 enum {
   MOE_DEV_ERR_BAD_ID = 1,     /* a routed or predicted id outside [0, E) */
   MOE_DEV_ERR_NAN = 2,        /* a NaN router logit (selection then treats it as -inf) */
-  MOE_DEV_ERR_AUDIT = 4       /* audit mode: slot maps not mutually inverse, or a needed expert not resident */
+  MOE_DEV_ERR_AUDIT = 4,      /* audit mode: slot maps not mutually inverse, or a needed expert not resident */
+  MOE_DEV_ERR_HOST_TIMEOUT = 8 /* a decode chain gave up waiting (half a second or more) for the host's rows of a
+                                  cold-mode layer; that call's host-computed outputs are stale */
 };
 /* (A call with more pairs than max_tokens * top_k cannot reach the device: every
  * entry point rejects T > max_tokens with MOE_EINVAL before it launches.) */
@@ -325,8 +327,9 @@ int moe_offload_set_ffn_path(moe_offload* h, int32_t path);
  * Host-synchronising on `stream`; the flag is written on the device in stream
  * order, so issue it on the compute stream between calls.  Switching on the
  * first time allocates the pinned host buffers the cold FFN uses (max_tokens
- * rows).  While the mode is on, the FFN must be moe_slot_ffn_host_cold:
- * moe_slot_ffn and the decode chain refuse the handle (MOE_EINVAL).
+ * rows).  While the mode is on, the FFN must be moe_slot_ffn_host_cold
+ * (moe_slot_ffn refuses the handle with MOE_EINVAL) or a decode chain, which
+ * computes the host's share on a thread of its own (moe_chain_run).
  * Errors: MOE_EINVAL, MOE_ENOMEM, MOE_EHIP. */
 enum { MOE_COLD_OFF = 0, MOE_COLD_ON = 1, MOE_COLD_AUTO = 2, MOE_COLD_SPLIT = 3 };
 int moe_offload_set_cold(moe_offload* h, int32_t mode, void* stream, int32_t* chosen, double* cpu_us,
@@ -542,11 +545,26 @@ int moe_chain_create(moe_offload* const* layers, int32_t L, const void* const* w
 int moe_chain_get_buffers(const moe_chain* c, moe_chain_buffers* out);
 
 /* One decode step: launch the captured graph on `stream` (captured on the
- * first call; later calls only launch).  Asynchronous. */
+ * first call; later calls only launch).  Asynchronous.
+ * Layers in cold or split mode (moe_offload_set_cold) join the step: the
+ * graph publishes each call that has host-computed pairs (record index
+ * S + E + e) into pinned host memory, a host thread of the chain computes
+ * those pairs (the host FFN of moe_slot_ffn_host_cold), and the graph waits
+ * for its rows before the layer's combine, with no host synchronisation.
+ * Which layers take part is fixed when the graph is captured (cold mode, or
+ * split mode with calls of more than S - P pairs); a run that finds another
+ * set synchronises the device and captures again.  The host thread starts
+ * with the first such run and polls until moe_chain_destroy (every 100 us
+ * after 50 ms without work).  If the host does not answer within half a
+ * second or so, the step goes on with stale rows and sets
+ * MOE_DEV_ERR_HOST_TIMEOUT.
+ * Errors: MOE_EINVAL (null chain; a layer in cold or split mode together
+ * with the lookahead prefetch), MOE_ENOMEM, MOE_EHIP. */
 int moe_chain_run(moe_chain* c, void* stream);
 
 /* The same step issued call by call on `stream` (no graph), for profiling
- * and for checking the graph against eager execution. */
+ * and for checking the graph against eager execution (cold and split layers
+ * as in moe_chain_run). */
 int moe_chain_run_eager(moe_chain* c, void* stream);
 
 /* Read-through of decode misses (default on).  The pages move a missed

@@ -204,6 +204,58 @@ def test_chain_variants_match_eager_and_oracle(case):
         ce.close()
 
 
+@pytest.mark.parametrize("wdt,T,mode", [(1, 1, "cold"), (1, 4, "cold"), (2, 2, "cold"), (3, 1, "cold"),
+                                         (1, 8, "split"), (1, 1, "split")])
+def test_chain_with_host_computed_layers(wdt, T, mode):
+    """Layers in cold or split mode inside the decode chain: the graph publishes each call with
+    host-computed pairs to the chain's host thread and waits for its rows.  Steps 0-2 run over the link,
+    steps 3-5 with every layer in the mode, steps 6-8 with layer 1 switched back (the graph is captured
+    again each time the set changes).  Graph and eager runs bitwise identical; ids, slot ids (index
+    S + E + e for the host's pairs), tables and counters bit-exact against the oracle teacher-forced, its
+    outputs within tolerance.  Split mode at one token (4 pairs <= S) never involves the host."""
+    L, E, S, k, H, F = 3, 16, 6, 4, 256, 512
+    print("chain host-computed wdt=%d T=%d mode=%s" % (wdt, T, mode), flush=True)
+    cg = ChainModel(L, E, S, k, H, F, wdt, T, 86)
+    ce = ChainModel(L, E, S, k, H, F, wdt, T, 86)
+    rb = oracle.record_bytes(wdt, H, F)
+    caches = [oracle.Cache(E, S, cg.hosts[l], rb) for l in range(L)]
+    st = torch.cuda.current_stream()
+    cold_seen = 0
+    try:
+        for s in range(9):
+            if s in (3, 6):
+                for l in (range(L) if s == 3 else [1]):
+                    for cm in (cg, ce):
+                        if s == 6:
+                            assert m.moe_offload_set_cold(cm.handles[l], m.COLD_OFF, st)[0] == 0
+                        elif mode == "cold":
+                            assert m.moe_offload_set_cold(cm.handles[l], m.COLD_ON, st)[0] == 1
+                        else:
+                            m.moe_offload_set_split(cm.handles[l], 128, st)
+                    if s == 6:
+                        caches[l].set_cold(False)
+                    elif mode == "cold":
+                        caches[l].set_cold(True)
+                    else:
+                        caches[l].set_split(128)
+            cg.run(s, graph=True)
+            ce.run(s, graph=False)
+            sg, se = cg.snapshot(), ce.snapshot()
+            for key in sg:
+                assert np.array_equal(sg[key], se[key]), (s, key)
+            cold_seen += int((sg["sid"] >= S + E).sum())
+            oracle_replay_step(cg, caches, sg, 0)
+        for cm in (cg, ce):
+            assert all(m.moe_offload_stats(h)["error"] == 0 for h in cm.handles)
+        if mode == "cold" or T * k > S:
+            assert cold_seen > 0
+        else:
+            assert cold_seen == 0
+    finally:
+        cg.close()
+        ce.close()
+
+
 @pytest.mark.parametrize("prefetch_n,T", [(0, 1), (3, 2)])
 def test_chain_scored_eviction(prefetch_n, T):
     """Scored eviction in the decode chain, with and without lookahead installs (usage 0, first out)."""
