@@ -920,22 +920,34 @@ def host_chain_compare(args, m, torch, hip, handles, wr_d, b_d, token_stream, ba
     `warm` untimed steps, one more untimed step after a mode switch (the graph is captured again), then
     `steps` timed ones, waited for with a blocking event (the calling thread sleeps rather than spins, so
     the host FFN has every core):
-      link       every miss over the host link (read-through);
-      split      calls wider than the cache send the measured share of their staged misses to the host;
-      cold_warm  the warm-up over the link (the cache learns), then every miss on the host.
+      link          every miss over the host link (read-through);
+      split         calls wider than the cache send the measured share of their staged misses to the host;
+      cold_warm     the warm-up over the link (the cache learns), then every miss on the host;
+      cold_profile  a profile-guided hot set (npu-offload's placement from a routing profile): each layer
+                    pins its S - k most routed experts of a separate 32-step profiling stream, the warm-up
+                    fills the other k slots over the link, then every miss on the host.
     Wall-clock tok/s."""
+    import numpy as np
     out = {}
     st = torch.cuda.current_stream()
     for T in batches:
         xs = token_stream(T, warm + steps + 1)
         res = {}
-        for mode in ("link", "split", "cold_warm"):
+        for mode in ("link", "split", "cold_warm", "cold_profile"):
             for h in handles:
                 m.moe_offload_set_cold(h, m.COLD_OFF, st)
+                m.moe_offload_pin(h, None, 0, st)
                 m.moe_offload_reset(h, st)
             if mode == "split":
                 for h in handles:
                     m.moe_offload_set_cold(h, m.COLD_SPLIT, st)
+            if mode == "cold_profile":
+                cnt = routing_profile(args, m, hip, torch, handles, wr_d, b_d, T, 32)
+                for l, h in enumerate(handles):
+                    m.moe_offload_reset(h, st)
+                    top = np.ascontiguousarray(np.argsort(-cnt[l], kind="stable")[:SLOTS - K_TOP].astype(np.int32))
+                    m.moe_offload_pin(h, torch.from_numpy(top).to(st.device), len(top), st)
+                torch.cuda.synchronize()
             c = m.moe_chain_create(handles, wr_d, b_d, T, 0)
             bufs = m.moe_chain_get_buffers(c)
             try:
@@ -946,7 +958,7 @@ def host_chain_compare(args, m, torch, hip, handles, wr_d, b_d, token_stream, ba
                 for s_ in range(warm):
                     step(s_)
                 torch.cuda.synchronize()
-                if mode == "cold_warm":
+                if mode in ("cold_warm", "cold_profile"):
                     for h in handles:
                         m.moe_offload_set_cold(h, m.COLD_ON, st)
                 step(warm)  # untimed: a switched mode captures the graph again
@@ -972,6 +984,7 @@ def host_chain_compare(args, m, torch, hip, handles, wr_d, b_d, token_stream, ba
                  res[mode]["host_records_per_token"]))
         for h in handles:
             m.moe_offload_set_cold(h, m.COLD_OFF, st)
+            m.moe_offload_pin(h, None, 0, st)
             m.moe_offload_reset(h, st)
         torch.cuda.synchronize()
         res["steps"] = "%d-%d after %d untimed (+1 after a mode switch)" % (warm + 1, warm + steps, warm)

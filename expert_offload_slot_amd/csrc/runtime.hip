@@ -662,6 +662,7 @@ int moe_offload_reset(moe_offload* h, void* stream) {
   if (int rc = check_handle(h)) return rc;
   DeviceGuard g(h->device);
   HIP_TRY(moe::launch_reset(h, (hipStream_t)stream));
+  h->n_pinned = 0;  // the reset unpins every slot
   return MOE_OK;
 }
 

@@ -445,8 +445,8 @@ int moe_copy_prefetch(moe_offload* h, void* stream);
 /* Synchronise the device and read the counters and the sticky error word. */
 int moe_offload_stats(moe_offload* h, moe_stats* out);
 
-/* Empty the cache (all slots free, tick 0), zero the counters and the
- * sticky error word, on `stream`. */
+/* Empty the cache (all slots free and unpinned, tick 0), zero the counters
+ * and the sticky error word, on `stream`. */
 int moe_offload_reset(moe_offload* h, void* stream);
 
 /* Fill `out` with the device addresses and sizes of the handle's state. */
