@@ -219,6 +219,45 @@ def test_qwen3_chain_full_size_batches_1_8_32(qwen3):
     check_slot_bytes(mo, (0, 47))
 
 
+def test_qwen3_chain_host_computed_full_size(qwen3):
+    """The 48-layer chain with every layer in cold mode (the cache warmed over the link for 8 steps, then
+    frozen; the chain's host thread computes every miss): batch 1 and 8, ids, slot ids (S + E + e for the
+    host's pairs), copy lists, tables and counters bit-exact against the oracle's cold rule, sampled
+    output rows within tolerance, the graph captured again when the mode switches."""
+    mo = qwen3
+    st = torch.cuda.current_stream()
+    for T, toks in ((1, (0,)), (8, (0, 7))):
+        caches = mo.reset()
+        for cache in caches:
+            cache.set_cold(False)
+        ch = Chain(mo, T, 0, 400 + T)
+        host_pairs = 0
+        try:
+            worst = 0.0
+            for s in range(14):
+                if s == 8:
+                    for l, h in enumerate(mo.handles):
+                        assert m.moe_offload_set_cold(h, m.COLD_ON, st)[0] == 1
+                        caches[l].set_cold(True)
+                log("qwen3 chain host-computed T=%d step %d" % (T, s))
+                ch.run(s)
+                snap = ch.snapshot()
+                host_pairs += int((snap["sid"] >= mo.S + mo.E).sum())
+                rows = tuple(sorted({(t + s) % T for t in toks}))
+                worst = max(worst, replay_step(mo, caches, snap, T, 0, (0, 23, 47) if s >= 8 else (), rows))
+            for l, h in enumerate(mo.handles):
+                stt = m.moe_offload_stats(h)
+                assert stt["cold_misses"] == caches[l].counters()["cold"], l
+            check_counters(mo, caches)
+            assert host_pairs > 0
+            log("qwen3 chain host-computed T=%d: 14 steps bit-exact, %d host pairs, sampled rows within %.2e" %
+                (T, host_pairs, worst))
+        finally:
+            for l, h in enumerate(mo.handles):
+                m.moe_offload_set_cold(h, m.COLD_OFF, st)
+            ch.close()
+
+
 def test_qwen3_lookahead_prefetch_full_size(qwen3):
     mo = qwen3
     T, steps = 1, 16
