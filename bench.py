@@ -924,8 +924,9 @@ def host_chain_compare(args, m, torch, hip, handles, wr_d, b_d, token_stream, ba
       split         calls wider than the cache send the measured share of their staged misses to the host;
       cold_warm     the warm-up over the link (the cache learns), then every miss on the host;
       cold_profile  a profile-guided hot set (npu-offload's placement from a routing profile): each layer
-                    pins its S - k most routed experts of a separate 32-step profiling stream, the warm-up
-                    fills the other k slots over the link, then every miss on the host.
+                    pins its S - k most routed experts of a separate profiling stream (256 tokens, at
+                    least 16 steps), the warm-up fills the other k slots over the link, then every miss
+                    on the host.
     Wall-clock tok/s."""
     import numpy as np
     out = {}
@@ -942,7 +943,7 @@ def host_chain_compare(args, m, torch, hip, handles, wr_d, b_d, token_stream, ba
                 for h in handles:
                     m.moe_offload_set_cold(h, m.COLD_SPLIT, st)
             if mode == "cold_profile":
-                cnt = routing_profile(args, m, hip, torch, handles, wr_d, b_d, T, 32)
+                cnt = routing_profile(args, m, hip, torch, handles, wr_d, b_d, T, max(16, 256 // T))
                 for l, h in enumerate(handles):
                     m.moe_offload_reset(h, st)
                     top = np.ascontiguousarray(np.argsort(-cnt[l], kind="stable")[:SLOTS - K_TOP].astype(np.int32))
