@@ -86,8 +86,8 @@ def measured_traffic():
 
 
 def traced_avg_us(path, kernel):
-    """Average duration of `kernel` over all its dispatches in the committed rocprofv3 summary of this command
-    (the copy-kernel chain's graph replays and the eager profile pass run the same kernel on the same calls)."""
+    """Average duration of `kernel` in the committed rocprofv3 summary of this command: its dispatches in the
+    eager profile pass (the ones this run times with HIP events), from the trace's start and end timestamps."""
     if not os.path.exists(path):
         return None
     m_ = re.search(r"^trace_avg_us\[%s\]:\s*(\S+)\s*$" % re.escape(kernel), open(path).read(), re.M)
@@ -426,8 +426,8 @@ def main():
                      os.path.relpath(COUNTERS, ROOT),
                      "rocprof": None if traced is None else
                      {"avg_launch_us": traced, "frac": round(gu_alg / (traced * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-                      "source": "%s (rocprofv3 --kernel-trace --stats of this command: every dispatch of the "
-                                "kernel, the copy-kernel chain's graph replays and the eager pass)" %
+                      "source": "%s (rocprofv3 --kernel-trace --stats of this command: the kernel's dispatches "
+                                "in the eager pass, from the trace's own start and end timestamps)" %
                                 os.path.relpath(TRACE, ROOT)}},
         "roofline_down": {"bound": "hbm", "kernel": "k_down_one<bf16, 6, false>", "achieved": round(dn_gbps, 1),
                           "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(dn_gbps / HBM_PEAK_GBPS, 4),
