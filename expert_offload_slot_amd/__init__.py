@@ -94,6 +94,7 @@ def lib():
             "moe_offload_set_cold": ([vp, i32, vp, P(ctypes.c_int32), P(ctypes.c_double), P(ctypes.c_double)], i32),
             "moe_offload_set_split": ([vp, i32, vp], i32),
             "moe_offload_set_ffn_path": ([vp, i32], i32),
+            "moe_offload_set_gemm_waves": ([vp, i32], i32),
             "moe_rmsnorm": ([vp, vp, i32, i32, i32, ctypes.c_float, vp], i32),
             "moe_prefill_stage": ([vp, vp, i32, vp, P(ctypes.c_int32), vp], i32),
             "moe_prefetch_install": ([vp, vp, i32, i32, vp], i32),
@@ -226,6 +227,10 @@ FFN_AUTO, FFN_DECODE, FFN_GEMM = 0, 1, 2
 
 def moe_offload_set_ffn_path(h, path):
     return _check(lib().moe_offload_set_ffn_path(h, path))
+
+
+def moe_offload_set_gemm_waves(h, waves):
+    return _check(lib().moe_offload_set_gemm_waves(h, waves))
 
 
 def moe_offload_set_split(h, q, stream=None):

@@ -101,6 +101,7 @@ struct moe_offload {
   int32_t* pinned_i32;       // small pinned host scratch
   moe::Prof* prof;           // per-kernel timing, created on first enable
   int ffn_path;              // MOE_FFN_AUTO / DECODE / GEMM (moe_offload_set_ffn_path)
+  int gemm_waves;            // 0 (by the call's size), 4 or 8 (moe_offload_set_gemm_waves)
   int n_pinned;              // size of the pinned set (moe_offload_pin)
   // host-computed cold experts (allocated when the cold mode is first switched on)
   bool cold_on;              // host mirror of the device word: nonzero

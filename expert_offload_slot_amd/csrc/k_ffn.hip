@@ -235,16 +235,19 @@ __device__ __forceinline__ void widen16_fp4(uint2 q, float s, uint4& lo, uint4& 
 
 // ------------------------------------------------------------------ prefill GEMMs (bf16, fp8, MXFP4)
 // Many tokens per record: a call becomes a grouped GEMM over record tiles.
-// Work item = (tile of a record's pairs, row tile: 64 rows of gate and of up,
-// or 128 rows of down); a record's pairs form tiles of kGemmTok, the last one
-// taking up to kGemmTail (gemm_tile_count), and the items of a call follow
-// the tile starts of the group descriptor (routed records, then the shared
-// expert's tiles).  A 256-thread workgroup runs an item: wavefront w owns 16
-// rows of gate and of up (32 rows of down) and every pair of the tile, so
-// its weight fragments are loaded straight from memory into registers in the
-// MFMA operand layout (fp8 and MXFP4 codes widened exactly to bf16 there) and
-// are read by no other wavefront; only the gathered token rows go through
-// LDS, in 128-wide K slices, double-buffered.  Weights are loaded two slices
+// Work item = (tile of a record's pairs, row tile: 16 WV rows of gate and of
+// up, or 32 WV rows of down, for WV wavefronts per workgroup); a record's pairs
+// form tiles of kGemmTok, the last one taking up to kGemmTail
+// (gemm_tile_count), and the items of a call follow the tile starts of the
+// group descriptor (routed records, then the shared expert's tiles).  A
+// workgroup of WV wavefronts runs an item: wavefront w owns 16 rows of gate and
+// of up (32 rows of down) and every pair of the tile, so its weight fragments
+// are loaded straight from memory into registers in the MFMA operand layout
+// (fp8 and MXFP4 codes widened exactly to bf16 there) and are read by no other
+// wavefront; only the gathered token rows go through LDS, in 128-wide K
+// slices, double-buffered, and every wavefront of the workgroup reads them, so
+// the more wavefronts share a tile, the fewer times its token rows are fetched
+// (once per row tile).  Weights are loaded two slices
 // ahead and token rows one slice ahead.  bf16 MFMA 16x16x32, fp32
 // accumulation; fp8: one scale per 128 x 128 block, so one per K slice and
 // matrix, multiplies the slice's partial sum.  The grid is the number of
@@ -256,11 +259,14 @@ __device__ __forceinline__ void widen16_fp4(uint2 q, float s, uint4& lo, uint4& 
 // slice come in whole 16-byte loads and each load instruction covers 64
 // contiguous bytes of each of its 16 rows; A and B use the same map, and a
 // slice's four steps cover its 128 K values once.
-constexpr int kGemmRowsGu = 64;       // weight rows per gate/up tile (each matrix)
-constexpr int kGemmRowsDn = 128;      // weight rows per down tile
 constexpr int kGemmK = 128;           // K per slice
 constexpr int kGemmNJ = kGemmTail / 16;
 constexpr int kLdsRow = kGemmK + 8;   // LDS row stride in bf16: rows start on different banks
+// weight rows per row tile (gate/up: each matrix) with WV wavefronts per workgroup
+__host__ __device__ constexpr int gemm_rows(bool gu, int wv) { return gu ? 16 * wv : 32 * wv; }
+// LDS rows of a token slice: WV wavefronts stage 4 WV rows per load, so up to 16 rows past the
+// tile's last 16-pair block are written (and never read)
+constexpr int gemm_lds_rows(int wv) { return kGemmTail + 4 * wv - 16 > kGemmTail ? kGemmTail + 4 * wv - 16 : kGemmTail; }
 
 struct GemmItem {
   Item it;
@@ -367,11 +373,11 @@ struct AFrag {
 
 // One work item of NJ 16-pair blocks.  GU: gate/up over x (rows by token) into
 // h = silu(gate) * up in bf16; else down over h (rows by pair) into fp32 partial outputs.
-template <int W, bool GU, int NJ>
-__device__ __forceinline__ void gemm_run(const FfnArgs& a, const GemmItem& g, uint16_t (*Bs)[kGemmTail][kLdsRow]) {
+template <int W, bool GU, int WV, int NJ, bool B2 = (WV == 8)>
+__device__ __forceinline__ void gemm_run(const FfnArgs& a, const GemmItem& g, uint16_t (*Bs)[gemm_lds_rows(WV)][kLdsRow]) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, lg = lane >> 4, lr = lane & 15;
   const int K = GU ? a.H : a.F, nk = K / kGemmK;
-  const int m0 = g.rt * (GU ? kGemmRowsGu : kGemmRowsDn);
+  const int m0 = g.rt * gemm_rows(GU, WV);
   const uint64_t mat = code_bytes<W>((uint64_t)a.F * a.H);
   // the wavefront's two fragments: gate and up rows m0 + 16 wv + lr, or down rows m0 + 32 wv + 16 f + lr
   const uint8_t* row[2];
@@ -383,28 +389,32 @@ __device__ __forceinline__ void gemm_run(const FfnArgs& a, const GemmItem& g, ui
     const int r = GU ? m0 + 16 * wv + lr : m0 + 32 * wv + 16 * f + lr;
     row[f] = g.it.rec + m * mat + code_bytes<W>((uint64_t)r * K);
     rs[f] = scale_row<W>(g.it.rec, mat, a.F, a.H, m, r, K);
-    sc[f] = reinterpret_cast<const float*>(scale_row<W>(g.it.rec, mat, a.F, a.H, m, m0, K));
+    // the wavefront's rows lie in one 128-row scale block; so do the tile's, unless it is taller
+    const int rw = gemm_rows(GU, WV) <= 128 ? m0 : __builtin_amdgcn_readfirstlane(m0 + (GU ? 16 : 32) * wv);
+    sc[f] = reinterpret_cast<const float*>(scale_row<W>(g.it.rec, mat, a.F, a.H, m, rw, K));
   }
-  // the tile's token rows: 16 threads per row, 8 activations each, rows tid / 16 + 16 q.  Rows
-  // past the tile's last pair repeat that pair's row: every load is issued unconditionally (the
-  // wait counts stay static), and those columns' results are never stored.
-  const uint16_t* bp[NJ];
+  // the tile's token rows: 16 threads per row, 8 activations each, rows tid / 16 + RQ q for
+  // the NJ 16-pair blocks.  Rows past the tile's last pair repeat that pair's row: every load is
+  // issued unconditionally (the wait counts stay static), and those columns' results are never
+  // stored; rows past the last block are staged and never read.
+  constexpr int RQ = 4 * WV, NQ = (16 * NJ + RQ - 1) / RQ;
+  static_assert(RQ * NQ <= gemm_lds_rows(WV), "token slice rows exceed the LDS buffer");
+  const uint16_t* bp[NQ];
   {
     const uint16_t* base = GU ? (const uint16_t*)a.x : (const uint16_t*)a.hbuf;
 #pragma unroll
-    for (int q = 0; q < NJ; ++q) {
-      const int p = item_pair(a, g.it, g.r, g.n0 + min(tid / 16 + 16 * q, g.w - 1));
+    for (int q = 0; q < NQ; ++q) {
+      const int p = item_pair(a, g.it, g.r, g.n0 + min(tid / 16 + RQ * q, g.w - 1));
       bp[q] = base + (uint64_t)(GU ? pair_token(a, p) : p) * K + (tid % 16) * 8;
     }
   }
-  u32x4 bst[NJ];
-  auto load_b = [&](int kb) {
+  auto load_b = [&](u32x4(&b)[NQ], int kb) {
 #pragma unroll
-    for (int q = 0; q < NJ; ++q) bst[q] = *reinterpret_cast<const u32x4*>(bp[q] + kb * kGemmK);
+    for (int q = 0; q < NQ; ++q) b[q] = *reinterpret_cast<const u32x4*>(bp[q] + kb * kGemmK);
   };
-  auto store_b = [&](int buf) {
+  auto store_b = [&](const u32x4(&b)[NQ], int buf) {
 #pragma unroll
-    for (int q = 0; q < NJ; ++q) *reinterpret_cast<u32x4*>(&Bs[buf][tid / 16 + 16 * q][(tid % 16) * 8]) = bst[q];
+    for (int q = 0; q < NQ; ++q) *reinterpret_cast<u32x4*>(&Bs[buf][tid / 16 + RQ * q][(tid % 16) * 8]) = b[q];
   };
   f32x4 acc[2][NJ];
 #pragma unroll
@@ -426,18 +436,24 @@ __device__ __forceinline__ void gemm_run(const FfnArgs& a, const GemmItem& g, ui
       sc_[1] = sc[1][kb];
     }
   };
+  // Token rows: with B2, two slices ahead like the weights, in three register sets that rotate
+  // with them (BX holds the slice that goes to LDS first); else one slice ahead in one set.
+  u32x4 BX[NQ], BY[NQ], BZ[NQ];
   load_a(AX, sX, 0);
   load_a(AY, sY, min(1, nk - 1));
-  load_b(0);
+  load_b(BX, 0);
+  if (B2) load_b(BY, min(1, nk - 1));
   wait_loads();
   __syncthreads();  // the previous item no longer reads either buffer
-  store_b(0);
+  store_b(BX, 0);
   __syncthreads();
-  // one slice: issue slice kb + 1's token rows, then slice kb + 2's weights (into ld), run slice kb
-  // from A and LDS, then store slice kb + 1's token rows into the other buffer (the one read in
-  // slice kb - 1, before the last barrier)
-  auto step = [&](int kb, AFrag<W>(&A)[2], const float(&s_)[2], AFrag<W>(&ld)[2], float(&sl)[2]) {
-    load_b(min(kb + 1, nk - 1));
+  // one slice: issue the token rows of slice kb + 2 (B2; else kb + 1) into bl, then slice kb + 2's
+  // weights (into ld), run slice kb from A and LDS, then store slice kb + 1's token rows (bs; with
+  // B2 loaded a slice ago, else bl) into the other buffer (the one read in slice kb - 1, before the
+  // last barrier)
+  auto step = [&](int kb, AFrag<W>(&A)[2], const float(&s_)[2], AFrag<W>(&ld)[2], float(&sl)[2],
+                  const u32x4(&bs)[NQ], u32x4(&bl)[NQ]) {
+    load_b(bl, min(kb + (B2 ? 2 : 1), nk - 1));
     load_a(ld, sl, min(kb + 2, nk - 1));
     // keep the scheduler from pulling the next slice's widening into this one: that would wait on
     // loads issued a slice ago, and in order behind them on this slice's own
@@ -467,18 +483,21 @@ __device__ __forceinline__ void gemm_run(const FfnArgs& a, const GemmItem& g, ui
     for (int f = 0; f < 2; ++f)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[f][j] = W == kFp8 ? fma4(s_[f], part[f][j], acc[f][j]) : part[f][j];
-    store_b((kb + 1) & 1);
+    store_b(B2 ? bs : bl, (kb + 1) & 1);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
+  // without B2 every slice loads and stores the one set BX
+  u32x4(&B1)[NQ] = B2 ? BY : BX;
+  u32x4(&B2s)[NQ] = B2 ? BZ : BX;
   int kb = 0;
   for (; kb + 3 <= nk; kb += 3) {
-    step(kb, AX, sX, AZ, sZ);
-    step(kb + 1, AY, sY, AX, sX);
-    step(kb + 2, AZ, sZ, AY, sY);
+    step(kb, AX, sX, AZ, sZ, B1, B2s);
+    step(kb + 1, AY, sY, AX, sX, B2s, BX);
+    step(kb + 2, AZ, sZ, AY, sY, BX, B1);
   }
-  if (kb < nk) step(kb, AX, sX, AZ, sZ);
-  if (kb + 1 < nk) step(kb + 1, AY, sY, AX, sX);
+  if (kb < nk) step(kb, AX, sX, AZ, sZ, B1, B2s);
+  if (kb + 1 < nk) step(kb + 1, AY, sY, AX, sX, B2s, BX);
   wait_loads();  // the repeated loads of the last slices, before the next item reuses the registers
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
@@ -505,21 +524,21 @@ __device__ __forceinline__ void gemm_run(const FfnArgs& a, const GemmItem& g, ui
 
 // gate/up (GU: C[f][p] = W[f] . x[token(p)] for gate and up, h = silu(gate) * up in bf16)
 // or down (part[p][r] = Wd[r] . h[p], fp32 partial outputs)
-template <int W, bool GU>
-__global__ __launch_bounds__(256) void k_gemm(FfnArgs a) {
-  __shared__ uint16_t Bs[2][kGemmTail][kLdsRow];
+template <int W, bool GU, int WV>
+__global__ __launch_bounds__(64 * WV) void k_gemm(FfnArgs a) {
+  __shared__ uint16_t Bs[2][gemm_lds_rows(WV)][kLdsRow];
   const int nr = a.grp[0];
   int routed;
   const int ntiles = gemm_tiles(a, nr, &routed);
-  const int RT = GU ? a.F / kGemmRowsGu : a.H / kGemmRowsDn;
+  const int RT = (GU ? a.F : a.H) / gemm_rows(GU, WV);
   for (int item = blockIdx.x; item < ntiles * RT; item += gridDim.x) {
     const GemmItem g = gemm_item(a, nr, routed, RT, item);
     switch ((g.w + 15) >> 4) {
-      case 1: gemm_run<W, GU, 1>(a, g, Bs); break;
-      case 2: gemm_run<W, GU, 2>(a, g, Bs); break;
-      case 3: gemm_run<W, GU, 3>(a, g, Bs); break;
-      case 4: gemm_run<W, GU, 4>(a, g, Bs); break;
-      default: gemm_run<W, GU, kGemmNJ>(a, g, Bs); break;
+      case 1: gemm_run<W, GU, WV, 1>(a, g, Bs); break;
+      case 2: gemm_run<W, GU, WV, 2>(a, g, Bs); break;
+      case 3: gemm_run<W, GU, WV, 3>(a, g, Bs); break;
+      case 4: gemm_run<W, GU, WV, 4>(a, g, Bs); break;
+      default: gemm_run<W, GU, WV, kGemmNJ>(a, g, Bs); break;
     }
   }
 }
@@ -1373,13 +1392,13 @@ void* scratch_ptr(int device) {
   return g_scratch[device];
 }
 
-// Workgroups of GEMM kernel k the device holds at once (CUs x resident workgroups per CU).  The
-// GEMM's grid is no larger: every workgroup then starts at once and strides over the work list
-// in step with the others, so the token tiles of one record and row tile (a multiple of 8 items
-// apart, so on one XCD: workgroup w runs on XCD w mod 8) run together and fetch the weight rows
-// into that XCD's L2 once.
+// Workgroups of GEMM kernel k the device holds at once (CUs x resident workgroups per CU of
+// `block` threads).  The GEMM's grid is no larger: every workgroup then starts at once and strides
+// over the work list in step with the others, so the token tiles of one record and row tile (the
+// row-tile count apart: on one XCD when that count is a multiple of 8, as workgroup w runs on XCD
+// w mod 8) run together and fetch the weight rows into that XCD's L2 once.
 template <typename Kern>
-int gemm_grid_cap(Kern k, int device) {
+int gemm_grid_cap(Kern k, int block, int device) {
   static std::mutex mu;
   static std::map<std::pair<const void*, int>, int> cache;
   std::lock_guard<std::mutex> lk(mu);
@@ -1388,11 +1407,24 @@ int gemm_grid_cap(Kern k, int device) {
   if (it != cache.end()) return it->second;
   int cus = 0, per = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k, 256, 0) != hipSuccess || cus <= 0 || per <= 0) {
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k, block, 0) != hipSuccess || cus <= 0 || per <= 0) {
     (void)hipGetLastError();
     return 2048;  // not cached: the query is repeated on the next call
   }
   return cache[key] = cus * per;
+}
+
+// Wavefronts per grouped-GEMM workgroup for gate/up (gu) or down.  Eight share each token slice
+// in LDS across twice the weight rows and load it two slices ahead, but a compute unit holds one
+// such workgroup: the call needs at least 1024 of their work items (about four per compute unit),
+// counted at T * k / kGemmTok token tiles.  Eight need the rows to divide into their tiles (F and
+// H are multiples of 128: gate/up always; down when H is a multiple of 256).  Reads the layer's
+// shape, T and the handle's setting only; the outputs are the same bits either way.
+int gemm_waves(const moe_offload* h, int T, bool gu) {
+  const int rows = gu ? h->F : h->H;
+  if (rows % gemm_rows(gu, 8)) return 4;
+  if (h->gemm_waves) return h->gemm_waves;
+  return (int64_t)(T * h->k / kGemmTok) * (rows / gemm_rows(gu, 8)) >= 1024 ? 8 : 4;
 }
 
 FfnWork ffn_work_in(const moe_offload* h, int T, void* base, size_t* bytes) {
@@ -1475,15 +1507,23 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
       b1 = b2 = dim3(256);
     }
   } else {  // grouped GEMM over (record tile, 64 rows) work items; the grid strides over the call's list
-    gu = wf == kFp8 ? k_gemm<kFp8, true> : (wf == kMx4 ? k_gemm<kMx4, true> : k_gemm<kBf16, true>);
-    dn = wf == kFp8 ? k_gemm<kFp8, false> : (wf == kMx4 ? k_gemm<kMx4, false> : k_gemm<kBf16, false>);
+    const int wg = gemm_waves(h, T, true), wd = gemm_waves(h, T, false);
+    if (wg == 8)
+      gu = wf == kFp8 ? k_gemm<kFp8, true, 8> : (wf == kMx4 ? k_gemm<kMx4, true, 8> : k_gemm<kBf16, true, 8>);
+    else
+      gu = wf == kFp8 ? k_gemm<kFp8, true, 4> : (wf == kMx4 ? k_gemm<kMx4, true, 4> : k_gemm<kBf16, true, 4>);
+    if (wd == 8)
+      dn = wf == kFp8 ? k_gemm<kFp8, false, 8> : (wf == kMx4 ? k_gemm<kMx4, false, 8> : k_gemm<kBf16, false, 8>);
+    else
+      dn = wf == kFp8 ? k_gemm<kFp8, false, 4> : (wf == kMx4 ? k_gemm<kMx4, false, 4> : k_gemm<kBf16, false, 4>);
     // tiles of a call: gemm_tile_count(n) <= ceil(n / kGemmTok), so at most one partial tile per
     // record on top of the full ones
     const int tiles = (T * h->k) / kGemmTok + std::min(T * h->k, h->S + h->E) +
                       (shared ? gemm_tile_count(T) : 0);
-    g1 = dim3(std::min(tiles * (h->F / kGemmRowsGu), gemm_grid_cap(gu, h->device)));
-    g2 = dim3(std::min(tiles * (h->H / kGemmRowsDn), gemm_grid_cap(dn, h->device)));
-    b1 = b2 = dim3(256);
+    b1 = dim3(64 * wg);
+    b2 = dim3(64 * wd);
+    g1 = dim3(std::min(tiles * (h->F / gemm_rows(true, wg)), gemm_grid_cap(gu, 64 * wg, h->device)));
+    g2 = dim3(std::min(tiles * (h->H / gemm_rows(false, wd)), gemm_grid_cap(dn, 64 * wd, h->device)));
   }
   {
     launch_k(h, MOE_K_GATEUP, gu, g1, b1, 0, s, a);

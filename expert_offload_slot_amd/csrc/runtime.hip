@@ -522,6 +522,14 @@ int moe_offload_set_ffn_path(moe_offload* h, int32_t path) {
   return MOE_OK;
 }
 
+int moe_offload_set_gemm_waves(moe_offload* h, int32_t waves) {
+  if (int rc = check_handle(h)) return rc;
+  if (waves != 0 && waves != 4 && waves != 8)
+    return fail(MOE_EINVAL, "moe_offload_set_gemm_waves: waves %d (0, 4 or 8)", waves);
+  h->gemm_waves = waves;
+  return MOE_OK;
+}
+
 // the host side's buffers and the split mode's stream and events, once (the device must be current)
 static int cold_buffers(moe_offload* h) {
   if (h->cold_stream) return MOE_OK;

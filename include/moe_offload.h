@@ -301,6 +301,24 @@ int moe_slot_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, const f
 enum { MOE_FFN_AUTO = 0, MOE_FFN_DECODE = 1, MOE_FFN_GEMM = 2 };
 int moe_offload_set_ffn_path(moe_offload* h, int32_t path);
 
+/* Workgroup size of the grouped GEMM (the kernels of prefill-sized calls,
+ * xinfer-ai docs, "How it works", Prefill; an implementation choice).  Each
+ * wavefront owns 16 rows of gate and of up (32 of down) and every pair of a
+ * token tile, so a workgroup of 8 wavefronts fetches each tile's token rows
+ * once per 128 rows of gate and up (256 of down) instead of once per 64 (128),
+ * and has the registers to load them two K slices ahead, but holds one
+ * workgroup per compute unit, too few for small calls.
+ *   0 (the default): 8 wavefronts when the call has at least 1024 work items
+ *     of theirs, counted as (T * k / 64) token tiles times (F / 128) row tiles
+ *     for gate/up, (H / 256) for down (about four per compute unit), else 4
+ *     (measured: DeepSeek-V3- and Mixtral-shaped 2048-token calls 10 to 20 %
+ *     faster, 64-token calls 7 to 45 % slower);
+ *   4 or 8: always that many (down keeps 4 when H is not a multiple of 256).
+ * Every output element sums the same products in the same order either way:
+ * outputs are bitwise identical.  Host-side setting.
+ * Errors: MOE_EINVAL (waves not 0, 4 or 8). */
+int moe_offload_set_gemm_waves(moe_offload* h, int32_t waves);
+
 /* Host-computed cold experts (npu-offload README, intro and "Architecture":
  * hot experts stay in accelerator memory, the host CPU computes the cold ones
  * from host DRAM in parallel, only activations cross the link; "Results", where

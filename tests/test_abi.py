@@ -69,6 +69,7 @@ def test_null_handles_are_rejected_before_any_device_call():
         "moe_offload_set_cold": (None, 1, None, None, None, None),
         "moe_offload_set_split": (None, 128, None),
         "moe_offload_set_ffn_path": (None, 0),
+        "moe_offload_set_gemm_waves": (None, 0),
     }
     for name, args in calls.items():
         rc = getattr(L, name)(*args)

@@ -20,12 +20,14 @@ from gpu_harness import (TOL, GpuLayer, compare_call, d2h, h2d, make_layer_input
 pytestmark = pytest.mark.gpu
 
 
-def run_sequence(E, S, k, H, F, wdt, zipf, seed, steps, Ts, shared=False, flags=m.FLAG_AUDIT, pins=None):
+def run_sequence(E, S, k, H, F, wdt, zipf, seed, steps, Ts, shared=False, flags=m.FLAG_AUDIT, pins=None,
+                 gemm_waves=0):
     print("case E=%d S=%d k=%d H=%d F=%d wdt=%d zipf=%s seed=%d Ts=%s shared=%s" %
           (E, S, k, H, F, wdt, zipf, seed, Ts, shared), flush=True)
     host, wr, b, sh = make_layer_inputs(seed, 0, E, H, F, wdt, zipf, shared)
     maxT = max(Ts)
     gl = GpuLayer(E, S, k, H, F, wdt, maxT, host, wr, b, flags=flags, shared=sh)
+    m.moe_offload_set_gemm_waves(gl.h, gemm_waves)
     ol = oracle.Layer(E, S, k, H, F, wdt, host, wr, b, shared=sh,
                       policy=oracle_policy(flags))
     xs = synth.tokens(seed, 7, maxT, H, steps, 0.0, wdt)
@@ -102,10 +104,19 @@ def test_fp8_prefill_gemm_ragged_tiles():
 
 
 @pytest.mark.parametrize("wdt", [1, 2, 3])
-def test_prefill_gemm_several_tiles_per_record(wdt):
-    # the grouped GEMM at H = F = 512 (8 row tiles each way) in bf16, fp8 and MXFP4; Zipf routing gives
-    # records several 64-pair token tiles and a ragged last one
-    run_sequence(8, 8, 2, 512, 512, wdt, 1.2, 80 + wdt, 3, [300, 129, 70], shared=(wdt != 1))
+@pytest.mark.parametrize("waves", [4, 8])
+def test_prefill_gemm_several_tiles_per_record(wdt, waves):
+    # the grouped GEMM at H = F = 512 (8 row tiles each way with 4 wavefronts per workgroup, 4 and 2
+    # with 8) in bf16, fp8 and MXFP4; Zipf routing gives records several 64-pair token tiles and a
+    # ragged last one
+    run_sequence(8, 8, 2, 512, 512, wdt, 1.2, 80 + wdt, 3, [300, 129, 70], shared=(wdt != 1), gemm_waves=waves)
+
+
+@pytest.mark.parametrize("wdt", [1, 2])
+def test_prefill_gemm_down_rows_not_a_multiple_of_256(wdt):
+    # H = 640 with 8-wavefront workgroups forced: gate/up row tiles of 128 rows (F = 384, three per
+    # matrix), down keeps 4 wavefronts (five tiles of 128 rows); fp8 with the shared expert
+    run_sequence(8, 8, 2, 640, 384, wdt, 1.2, 90 + wdt, 3, [300, 129, 70], shared=(wdt == 2), gemm_waves=8)
 
 
 def test_bf16_prefill_gemm_one_hot_record():
@@ -166,11 +177,17 @@ def test_prefill_gemm_tile_boundaries(wdt):
         gl.w[:T].copy_(torch.from_numpy(w))
         gl.ensure(T, ids=to_dev(ids))
         gl.copy()
-        gl.ffn(to_dev(x), T)
-        y = to_np(gl.y[:T])
         _, y64 = oracle.ffn(x, wdt, H, F, oracle.host_records(host, ids), w.astype(np.float64), shared=sh,
                             want_f64=True)
-        assert row_rel_err(y, y64, wdt) <= TOL[wdt]
+        # workgroups of 4 wavefronts, and of 8 (token rows two K slices ahead; down's single
+        # 256-row tile spans two fp8 scale blocks): the same bits
+        ys = []
+        for waves in (4, 8):
+            m.moe_offload_set_gemm_waves(gl.h, waves)
+            gl.ffn(to_dev(x), T)
+            ys.append(to_np(gl.y[:T]))
+            assert row_rel_err(ys[-1], y64, wdt) <= TOL[wdt], waves
+        assert np.array_equal(ys[0], ys[1])
         assert gl.stats()["error"] == 0
     finally:
         gl.close()
