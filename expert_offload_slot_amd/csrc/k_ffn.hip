@@ -21,10 +21,11 @@
 //              weight-streaming (HBM) problem, not a matrix-core one.
 //              T = 1: k_gateup_one / k_down_one, the same rows per wavefront
 //              for one activation row, work item (choice j, rows).
-//     larger T (prefill), or many pairs per record: k_gemm<W, GU>, a grouped GEMM whose work
-//              items are (tile of up to 80 pairs of one record, weight rows):
-//              weights straight into registers, token rows through LDS, bf16
-//              MFMA 16x16x32 tiles.
+//     larger T (prefill), or many pairs per record: k_gemm<W, GU, WV>, a grouped GEMM whose
+//              work items are (tile of up to 80 pairs of one record, weight
+//              rows): weights straight into registers, token rows through LDS
+//              shared by the workgroup's WV = 4 or 8 wavefronts (gemm_waves),
+//              bf16 MFMA 16x16x32 tiles.
 //     fp32 records: plain fp32 FMA kernels, work item (record, 64 rows).
 //   h is stored in bf16 (fp32 for fp32 records); down writes fp32 partial
 //   outputs per (t, j) to the workspace.
@@ -1506,7 +1507,7 @@ hipError_t launch_ffn(moe_offload* h, const void* x, const int32_t* slot_ids, co
       g2 = dim3(std::min((max_items_r * (h->H / 8) + 3) / 4, 8192));
       b1 = b2 = dim3(256);
     }
-  } else {  // grouped GEMM over (record tile, 64 rows) work items; the grid strides over the call's list
+  } else {  // grouped GEMM over (record tile, row tile) work items; the grid strides over the call's list
     const int wg = gemm_waves(h, T, true), wd = gemm_waves(h, T, false);
     if (wg == 8)
       gu = wf == kFp8 ? k_gemm<kFp8, true, 8> : (wf == kMx4 ? k_gemm<kMx4, true, 8> : k_gemm<kBf16, true, 8>);
