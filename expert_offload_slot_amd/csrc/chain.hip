@@ -74,7 +74,7 @@ struct moe_chain {
   float* cold_out_d = nullptr;
   uint32_t* req_d = nullptr;
   uint32_t* done_d = nullptr;
-  uint32_t* seq = nullptr;     // device [L]: each layer's last request number
+  uint32_t* seq = nullptr;     // device [L + 1]: each layer's last request number, then the publish count
   moe::ColdServer* server = nullptr;
 };
 
@@ -93,32 +93,35 @@ constexpr uint32_t kColdMaxPolls = 1u << 19;  // half a second or more of polls 
 
 __device__ __forceinline__ bool is_cold(int r, int S, int E) { return r >= S + E && r < S + 2 * E; }
 
-// One workgroup: when the call has a host-computed pair, copies its record indices, and the
-// activation rows of the tokens that have such a pair, into the pinned host buffers, then (after a
-// system-scope fence by every thread) stores the next request number, also kept in seq for the wait.
-__global__ __launch_bounds__(1024) void k_cold_publish(const int32_t* __restrict__ sid, int T, int k, int S, int E,
-                                                       const uint4* __restrict__ x, int row16, int32_t* pub_sid,
-                                                       uint4* pub_x, uint32_t* req, uint32_t* seq) {
-  const int n = T * k;
+// A workgroup per token: when the call has a host-computed pair, copies the activation row of its
+// token if that token has such a pair (workgroup 0 also the call's record indices) into the pinned
+// host buffers.  Every thread then fences at system scope, and the last workgroup to count itself
+// in (an acquire-release count at system scope in device memory) stores the next request number,
+// also kept in seq for the wait, and clears the count for the next launch.  The rows cross the
+// host link from T workgroups at once: a single workgroup wrote them at about 4 GB/s.
+__global__ __launch_bounds__(256) void k_cold_publish(const int32_t* __restrict__ sid, int T, int k, int S, int E,
+                                                      const uint4* __restrict__ x, int row16, int32_t* pub_sid,
+                                                      uint4* pub_x, uint32_t* req, uint32_t* seq, uint32_t* arrive) {
+  const int n = T * k, t = blockIdx.x;
   bool mine = false;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const int r = sid[i];
-    mine |= is_cold(r, S, E);
-    pub_sid[i] = r;
-  }
-  if (!__syncthreads_or(mine)) return;  // workgroup-uniform: nothing for the host, nothing published
-  for (int t = 0; t < T; ++t) {
-    bool row = false;
-    for (int j = 0; j < k; ++j) row |= is_cold(sid[t * k + j], S, E);  // uniform
-    if (!row) continue;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) mine |= is_cold(sid[i], S, E);
+  if (!__syncthreads_or(mine)) return;  // the same in every workgroup: nothing for the host, nothing published
+  if (t == 0)
+    for (int i = threadIdx.x; i < n; i += blockDim.x) pub_sid[i] = sid[i];
+  bool row = false;
+  for (int j = 0; j < k; ++j) row |= is_cold(sid[t * k + j], S, E);  // uniform
+  if (row)
     for (int i = threadIdx.x; i < row16; i += blockDim.x) pub_x[(size_t)t * row16 + i] = x[(size_t)t * row16 + i];
-  }
   __threadfence_system();
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t r = *seq + 1;
-    *seq = r;
-    __hip_atomic_store(req, r, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    const uint32_t a = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_SYSTEM);
+    if (a == gridDim.x - 1) {  // every workgroup's rows are out
+      __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t r = *seq + 1;
+      *seq = r;
+      __hip_atomic_store(req, r, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
   }
 }
 
@@ -231,9 +234,9 @@ hipError_t issue(moe_chain* c, hipStream_t cs) {
     const bool cold = c->cold[l] != 0;
     if (cold) {  // the call's host-computed pairs go to the server thread
       const size_t xrow = (size_t)c->H * c->act;
-      hipLaunchKernelGGL(k_cold_publish, dim3(1), dim3(1024), 0, cs, (const int32_t*)(c->sid + R(c, l)), T, c->k,
+      hipLaunchKernelGGL(k_cold_publish, dim3(T), dim3(256), 0, cs, (const int32_t*)(c->sid + R(c, l)), T, c->k,
                          h->S, h->E, (const uint4*)XN(c, l), (int)(xrow / 16), c->pub_sid_d + R(c, l),
-                         (uint4*)(c->pub_x_d + (size_t)l * T * xrow), c->req_d + l, c->seq + l);
+                         (uint4*)(c->pub_x_d + (size_t)l * T * xrow), c->req_d + l, c->seq + l, c->seq + c->L);
       CHK(hipGetLastError());
     }
     if (pf && l >= 1) CHK(hipStreamWaitEvent(cs, c->ev_pf[l], 0));  // this layer's prefetch copy first
@@ -329,7 +332,7 @@ int moe_chain_create(moe_offload* const* layers, int32_t L, const void* const* w
   const size_t xa = (size_t)(L + 1) * T * c->H * c->act, ya = (size_t)L * T * c->H * c->act;
   const size_t ra = (size_t)L * T * c->k * 4;
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
-  const size_t total = al(xa) + 2 * al(ya) + 5 * al(ra) + al(4 * (size_t)L);
+  const size_t total = al(xa) + 2 * al(ya) + 5 * al(ra) + al(4 * ((size_t)L + 1));
   hipError_t e = hipMalloc(&c->block, total);
   if (e == hipSuccess) e = hipMemset(c->block, 0, total);
   if (e == hipSuccess) {
@@ -421,7 +424,7 @@ static int prepare_cold(moe_chain* c, const char* who, bool* changed) {
   }
   if (any && !c->server) {
     // the device request counters restart with the host's numbers
-    hipError_t e = hipMemset(c->seq, 0, 4 * (size_t)c->L);
+    hipError_t e = hipMemset(c->seq, 0, 4 * ((size_t)c->L + 1));
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) return moe::set_error(MOE_EHIP, hipGetErrorString(e));
     memset(c->cold_block, 0, 8 * (size_t)c->L);
