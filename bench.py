@@ -643,9 +643,11 @@ def qwen3_mxfp4(args, m, torch, hip, wr_d, b_d):
     return out
 
 
-def layer_steps(m, torch, h, wr, b, shared, xs, T, steps, warm):
+def layer_steps(m, torch, h, wr, b, shared, xs, T, steps, warm, split=False):
     """Entry-point decode calls (route, ensure, copy, FFN) of one layer: tok/s over the timed calls, and the
-    per-kernel event averages of the same calls."""
+    per-kernel event averages of the same calls.  split: the layer in split mode (MOE_COLD_SPLIT, the share
+    measured when it is switched on), the FFN through moe_slot_ffn_host_cold, so calls wider than the cache
+    send that share of their staged misses to the host CPU; the cache starts empty."""
     dev = torch.device("cuda", 0)
     st = torch.cuda.current_stream()
     H = xs.shape[-1]
@@ -654,13 +656,18 @@ def layer_steps(m, torch, h, wr, b, shared, xs, T, steps, warm):
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
     sid = torch.empty_like(ids)
     y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    q = None
+    if split:
+        m.moe_offload_reset(h, st)
+        q = m.moe_offload_set_cold(h, m.COLD_SPLIT, st)
+    ffn = m.moe_slot_ffn_host_cold if split else m.moe_slot_ffn
 
     def call(s):
         x = xs[s]
         m.moe_route_topk(h, x, wr, b, T, ids, w, st)
         m.moe_slot_ensure(h, ids, T, sid, st)
         m.moe_copy_misses(h, st)
-        m.moe_slot_ffn(h, x, sid, w, T, shared, y, None, None, st)
+        ffn(h, x, sid, w, T, shared, y, None, None, st)
 
     for s in range(warm):
         call(s)
@@ -678,7 +685,14 @@ def layer_steps(m, torch, h, wr, b, shared, xs, T, steps, warm):
     after = m.moe_offload_stats(h)
     ms = a.elapsed_time(b_)
     d = {kk: after[kk] - before[kk] for kk in after}
-    return {"tokens_per_s": round(T * steps * 1e3 / ms, 2), "ms_per_call": round(ms / steps, 3), "calls": steps,
+    extra = {}
+    if split:
+        m.moe_offload_set_cold(h, m.COLD_OFF, st)
+        m.moe_offload_reset(h, st)
+        torch.cuda.synchronize()
+        extra = {"host_share_of_256": q[0], "host_us_per_record": round(q[1], 1), "link_us_per_record": round(q[2], 1),
+                 "host_records_per_call": round(d["cold_misses"] / steps, 3)}
+    return {**extra, "tokens_per_s": round(T * steps * 1e3 / ms, 2), "ms_per_call": round(ms / steps, 3), "calls": steps,
             "misses_per_call": round(d["misses"] / steps, 3), "staged_calls": d["staged_calls"],
             "staged_copies_per_call": round(d["staged_copies"] / steps, 3),
             "copy_GBps": round(d["bytes_copied"] / (kt["copy"][0] * 1e-3) / 1e9, 2) if kt["copy"][0] > 0 else None,
@@ -809,6 +823,12 @@ def deepseek_layer(args, m, torch):
     out["decode_T16"] = layer_steps(m, torch, h, wr_d, b_d, sh_d, xs_d, 16, 64, 8)
     log("deepseek decode T=16: %.1f tok/s, %d/%d calls staged" % (out["decode_T16"]["tokens_per_s"],
                                                                   out["decode_T16"]["staged_calls"], 64))
+    # the same calls from an empty cache in split mode: the measured share of each call's staged misses is
+    # computed by the host CPU from host memory while the rest cross the link
+    out["decode_T16_split"] = layer_steps(m, torch, h, wr_d, b_d, sh_d, xs_d, 16, 64, 8, split=True)
+    log("deepseek decode T=16, split with the host: %.1f tok/s, %.2f records per call on the host (share %s/256)" %
+        (out["decode_T16_split"]["tokens_per_s"], out["decode_T16_split"]["host_records_per_call"],
+         out["decode_T16_split"]["host_share_of_256"]))
     T = 2048
     x = synth.tokens(seed, 70, T, H, 1, 0.0, synth.BF16)[0]
     out["prefill_T2048"] = prefill_ffn(m, torch, h, wr_d, b_d, sh_d, x, "bf16 (fp8 codes widened exactly)")
