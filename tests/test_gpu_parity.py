@@ -757,6 +757,9 @@ def test_ffn_path_choice_parity(wdt, E, S, k, H, F, Ts, shared):
             assert gl.stats()["error"] == 0
         with pytest.raises(m.MoeError):
             m.moe_offload_set_ffn_path(layers[0].h, 3)
+        for bad in (-1, 1, 2, 5, 16):
+            with pytest.raises(m.MoeError):
+                m.moe_offload_set_gemm_waves(layers[0].h, bad)
     finally:
         for gl in layers:
             gl.close()
