@@ -488,17 +488,17 @@ __device__ __forceinline__ void gemm_run(const FfnArgs& a, const GemmItem& g, ui
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
-  // without B2 every slice loads and stores the one set BX
-  u32x4(&B1)[NQ] = B2 ? BY : BX;
-  u32x4(&B2s)[NQ] = B2 ? BZ : BX;
+  // the token-row sets in rotation (RY, RZ); without B2 every slice loads and stores the one set BX
+  u32x4(&RY)[NQ] = B2 ? BY : BX;
+  u32x4(&RZ)[NQ] = B2 ? BZ : BX;
   int kb = 0;
   for (; kb + 3 <= nk; kb += 3) {
-    step(kb, AX, sX, AZ, sZ, B1, B2s);
-    step(kb + 1, AY, sY, AX, sX, B2s, BX);
-    step(kb + 2, AZ, sZ, AY, sY, BX, B1);
+    step(kb, AX, sX, AZ, sZ, RY, RZ);
+    step(kb + 1, AY, sY, AX, sX, RZ, BX);
+    step(kb + 2, AZ, sZ, AY, sY, BX, RY);
   }
-  if (kb < nk) step(kb, AX, sX, AZ, sZ, B1, B2s);
-  if (kb + 1 < nk) step(kb + 1, AY, sY, AX, sX, B2s, BX);
+  if (kb < nk) step(kb, AX, sX, AZ, sZ, RY, RZ);
+  if (kb + 1 < nk) step(kb + 1, AY, sY, AX, sX, RZ, BX);
   wait_loads();  // the repeated loads of the last slices, before the next item reuses the registers
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
