@@ -5,8 +5,10 @@ entry points (route, ensure or prefill stage, copy, FFN).
   expert), slots 2, 4 and 6, decode batches 1 to 64 plus one call above 64
   tokens (the matrix-core FFN kernels), uniform router.
 * DeepSeek-V3 shape: fp8 e4m3 with 128x128 block scales, 256 experts plus a
-  shared expert, top-8, hidden 7168, ffn 2048, 26 slots; decode batch 16 and a
-  2048-token prefill that stages the whole layer.
+  shared expert, top-8, hidden 7168, ffn 2048, 26 slots; decode batch 16, a
+  2048-token prefill that stages the whole layer, then decode batch 16 again
+  from an empty cache in split mode (a measured share of the staged misses
+  computed by the host CPU).
 
 Every call is checked bit for bit on ids, slot ids, the copy list and the slot
 table (weights within 1e-5); a few token rows per call are computed one by one
@@ -112,5 +114,38 @@ def test_deepseek_shape_fp8_decode_and_prefill():
             assert np.array_equal(got, host[e, :gl.info["record_bytes"]])
         assert m.moe_offload_stats(gl.h)["error"] == 0
         log("deepseek: decode + prefill bit-exact routing/slots, sampled rows within %.2e" % worst)
+        # split mode from an empty cache: the share q measured on this machine; each overflowing call sends
+        # that share of its staged misses to the host CPU (records listed at S + E + e) and copies the rest
+        st = torch.cuda.current_stream()
+        m.moe_offload_reset(gl.h, st)
+        cache = oracle.Cache(E, S)
+        q, cpu_us, link_us = m.moe_offload_set_cold(gl.h, m.COLD_SPLIT, st)
+        cache.set_split(q)
+        log("deepseek split: host %.1f us, link %.1f us per record -> q %d" % (cpu_us, link_us, q))
+        before = m.moe_offload_stats(gl.h)
+        host_seen = 0
+        try:
+            for s in range(8):
+                log("deepseek split decode step %d (T=16)" % s)
+                x = np.ascontiguousarray(synth.tokens(seed, 50 + s, 16, H, 1, 0.0, BF16)[0])
+                xd = to_dev(x)
+                gl.route(xd, 16)
+                gl.ensure(16)
+                gl.copy()
+                m.moe_slot_ffn_host_cold(gl.h, xd, gl.slot_ids, gl.w, 16, gl.shared, gl.y, None, None, st)
+                torch.cuda.synchronize()
+                _, err = check_call(gl, cache, x, 16, wr, b, wdt, H, F, host, (s % 16, 15 - s % 16), shared)
+                worst = max(worst, err)
+                _, pairs = gl.copy_list()
+                host_seen += int((pairs[:, 1] >= S + E).sum()) if len(pairs) else 0
+        finally:
+            m.moe_offload_set_cold(gl.h, m.COLD_OFF, st)
+        after = m.moe_offload_stats(gl.h)
+        c = cache.counters()
+        assert after["error"] == 0
+        for key in ("calls", "hits", "misses", "staged_calls", "staged_copies"):
+            assert after[key] - before[key] == c[key], key
+        assert after["cold_misses"] - before["cold_misses"] == c["cold"] == host_seen > 0
+        log("deepseek split: 8 calls bit-exact, %d host-computed records, sampled rows within %.2e" % (host_seen, worst))
     finally:
         gl.close()
