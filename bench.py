@@ -620,6 +620,46 @@ def qwen3_mxfp4(args, m, torch, hip, wr_d, b_d):
         m.moe_offload_profile(h, 0)
     copy_bytes = stats()["bytes_copied"] - cb0
     m.moe_chain_destroy(c)
+    # host-computed misses with MXFP4 records (the host FFN widens E2M1 codes): each layer pins its S - k most
+    # routed experts of a separate profiling stream, the warm-up fills the other k slots over the link, then
+    # every miss is computed on the host inside the graph (as the bf16 chain's cold_profile mode)
+    cnt = routing_profile(args, m, hip, torch, hs, wr_d, b_d, T, 256)
+    for l, h in enumerate(hs):
+        m.moe_offload_reset(h, stream)
+        top = np.ascontiguousarray(np.argsort(-cnt[l], kind="stable")[:SLOTS - K_TOP].astype(np.int32))
+        m.moe_offload_pin(h, torch.from_numpy(top).to(dev), len(top), stream)
+    c = m.moe_chain_create(hs, wr_d, b_d, T, 0)
+    bufs = m.moe_chain_get_buffers(c)
+    try:
+        for s in range(warm):
+            step(s, m.moe_chain_run)
+        torch.cuda.synchronize()
+        for h in hs:
+            m.moe_offload_set_cold(h, m.COLD_ON, stream)
+        step(warm, m.moe_chain_run)  # untimed: the graph is captured again
+        torch.cuda.synchronize()
+        before_c = stats()
+        done = torch.cuda.Event(blocking=True)
+        tc = time.perf_counter()
+        for s in range(warm + 1, warm + 1 + steps):
+            step(s, m.moe_chain_run)
+        done.record(stream)
+        done.synchronize()
+        dt_cold = time.perf_counter() - tc
+        dc = {kk: v - before_c[kk] for kk, v in stats().items()}
+        assert dc["error"] == 0
+    finally:
+        m.moe_chain_destroy(c)
+        for h in hs:
+            m.moe_offload_set_cold(h, m.COLD_OFF, stream)
+            m.moe_offload_pin(h, None, 0, stream)
+    cold_profile = {"tokens_per_s": round(T * steps / dt_cold, 2), "ms_per_step": round(dt_cold * 1e3 / steps, 4),
+                    "host_records_per_token": round(dc["cold_misses"] / (T * steps), 3),
+                    "link_records_per_token": round((dc["misses"] + dc["staged_copies"]) / (T * steps), 3),
+                    "steps": "%d-%d after %d untimed (+1 after the mode switch), wall clock" %
+                             (warm + 1, warm + steps, warm)}
+    log("qwen3 mxfp4 decode, profile-guided hot set, misses on the host: %.1f tok/s, %.2f host records/token" %
+        (cold_profile["tokens_per_s"], cold_profile["host_records_per_token"]))
     for h in reversed(hs):
         m.moe_offload_destroy(h)
     (gu_ms, gu_n), (dn_ms, dn_n), (cp_ms, cp_n) = kt["gateup"], kt["down"], kt["copy"]
@@ -636,7 +676,8 @@ def qwen3_mxfp4(args, m, torch, hip, wr_d, b_d):
                              "algorithmic_bytes_per_launch": int(dn_bytes // dn_n),
                              "achieved": round(dn_bytes / (dn_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
                              "unit": "GB/s", "frac": round(dn_bytes / (dn_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
-           "kernels_us": {kind: round(v * 1e3 / n, 3) for kind, (v, n) in kt.items() if n}}
+           "kernels_us": {kind: round(v * 1e3 / n, 3) for kind, (v, n) in kt.items() if n},
+           "host_cold_profile": cold_profile}
     log("qwen3 mxfp4 decode: %.1f tok/s (copy kernel: %.1f), %.2f copies/token of %.2f MB, gateup %.2f us, "
         "down %.2f us" % (out["tokens_per_s"], out["copy_kernel_tokens_per_s"], out["copies_per_token"], rb / 1e6,
                           out["roofline_gateup"]["avg_launch_us"], out["roofline_down"]["avg_launch_us"]))
