@@ -112,6 +112,37 @@ def test_prefill_gemm_several_tiles_per_record(wdt, waves):
     run_sequence(8, 8, 2, 512, 512, wdt, 1.2, 80 + wdt, 3, [300, 129, 70], shared=(wdt != 1), gemm_waves=waves)
 
 
+@pytest.mark.parametrize("wdt", [1, 2, 3])
+def test_prefill_gemm_automatic_workgroup_size(wdt):
+    """A call just large enough for the automatic rule to give gate/up 8-wavefront workgroups: T * k / 64 =
+    32 token tiles times F / 128 = 32 row tiles = 1024 items (down, H / 256 = 1 row tile, keeps 4).  The
+    automatic choice, 4 forced and 8 forced give the same bits, within tolerance of the oracle."""
+    E, k, H, F, T = 16, 2, 256, 4096, 1024
+    print("gemm automatic workgroup size wdt=%d T=%d" % (wdt, T), flush=True)
+    host, wr, b, sh = make_layer_inputs(75, 0, E, H, F, wdt, 0.0, wdt == 2)
+    x = np.ascontiguousarray(synth.tokens(76, 0, T, H, 1, 0.0, wdt)[0])
+    gl = GpuLayer(E, E, k, H, F, wdt, T, host, wr, b, shared=sh)
+    try:
+        xd = to_dev(x)
+        gl.route(xd, T)
+        gl.ensure(T)
+        gl.copy()
+        ids, w = to_np(gl.ids[:T]), to_np(gl.w[:T])
+        toks = [0, 1, 63, 64, 500, 777, 1022, 1023]  # sampled rows: the oracle's plain sums, one by one
+        _, y64 = oracle.ffn(x[toks], wdt, H, F, oracle.host_records(host, ids[toks]), w[toks].astype(np.float64),
+                            shared=sh, want_f64=True)
+        ys = []
+        for waves in (0, 4, 8):
+            m.moe_offload_set_gemm_waves(gl.h, waves)
+            gl.ffn(xd, T)
+            ys.append(to_np(gl.y[:T]))
+            assert row_rel_err(ys[-1][toks], y64, wdt) <= TOL[wdt], waves
+        assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[0], ys[2])
+        assert gl.stats()["error"] == 0
+    finally:
+        gl.close()
+
+
 @pytest.mark.parametrize("wdt", [1, 2])
 def test_prefill_gemm_down_rows_not_a_multiple_of_256(wdt):
     # H = 640 with 8-wavefront workgroups forced: gate/up row tiles of 128 rows (F = 384, three per
