@@ -29,9 +29,11 @@ replays, from empty caches.  The same line carries, measured in the same run:
   * misses computed on the host CPU (split and cold mode) at batch 1, 8 and
     32, through the entry points and inside the graph (the chain's host
     thread);
-  * the MXFP4 records, the Mixtral-8x7B-shaped layer at 2/4/6 slots and the
-    DeepSeek-V3-shaped fp8 layer (decode at batch 16, the 2048-token prefill:
-    staging copy, FFN TFLOP/s and the fraction of its attainable roofline);
+  * the MXFP4 records (over the link, and with a profile-guided hot set and
+    every miss on the host), the Mixtral-8x7B-shaped layer at 2/4/6 slots and
+    the DeepSeek-V3-shaped fp8 layer (decode at batch 16 over the link and in
+    split mode, the 2048-token prefill: staging copy, FFN TFLOP/s and the
+    fraction of its attainable roofline);
   * the CPU oracle on a bounded sample of the same workload.
 --quick keeps only the batch-1 window, its steady state, the eager profile
 and the host link.
