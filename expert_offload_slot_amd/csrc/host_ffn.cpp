@@ -138,16 +138,6 @@ MOE_AVX512 inline __m512 ld_e4m3(const uint8_t* w) {
   return _mm512_castsi512_ps(_mm512_or_si512(bits, sign));
 }
 
-// 16 E2M1 codes (8 bytes, element 2i in the low nibble) -> 16 fp32, times s
-MOE_AVX512 inline __m512 ld_e2m1(const uint8_t* w, __m512 table, __m512 s) {
-  const __m512i b = _mm512_cvtepu8_epi32(_mm_loadl_epi64(reinterpret_cast<const __m128i*>(w)));
-  const __m512i lo = _mm512_and_si512(b, _mm512_set1_epi32(15));
-  const __m512i hi = _mm512_srli_epi32(b, 4);
-  const __m512i idx = _mm512_set_epi32(23, 7, 22, 6, 21, 5, 20, 4, 19, 3, 18, 2, 17, 1, 16, 0);
-  const __m512i codes = _mm512_permutex2var_epi32(lo, idx, hi);
-  return _mm512_mul_ps(_mm512_permutexvar_ps(codes, table), s);
-}
-
 // NR weight rows (ld(r, c): 16 weights of row r from column c) against NT activation
 // rows: each activation chunk is loaded once for the NR rows, so with two rows the
 // loop issues 10 loads per 16 fused multiply-adds instead of 9 per 8.  Every (row,
@@ -175,6 +165,54 @@ MOE_AVX512 inline void dot_blocks(const Load& ld, const Scale& scale, int C, int
   }
   for (int r = 0; r < NR; ++r)
     for (int t = 0; t < NT; ++t) acc[r * kMaxTok + t] = out[r][t];
+}
+
+// MXFP4 rows: 32 weights (16 code bytes, one E8M0 block) per step.  The nibbles are split and
+// interleaved as bytes, widened once, and looked up in the E2M1 table times the block's scale (a power
+// of two, so each entry is exact and equal to the value times the scale); the same products summed in
+// the same order as 16 weights at a time with the scale applied after the lookup.
+template <int NR, int NT>
+MOE_AVX512 inline void dot_blocks_mx4(const uint8_t* w, const uint8_t* sc, int C, const float* const* a,
+                                      float* acc) {
+  const __m512 table = _mm512_loadu_ps(g_tab.e2m1);
+  const __m128i m4 = _mm_set1_epi8(15);
+  __m512 l[NR][NT];
+  for (int r = 0; r < NR; ++r)
+    for (int t = 0; t < NT; ++t) l[r][t] = _mm512_setzero_ps();
+  for (int c = 0; c < C; c += 2 * kLanes) {
+    __m512 av0[NT], av1[NT];
+    for (int t = 0; t < NT; ++t) {
+      av0[t] = _mm512_loadu_ps(a[t] + c);
+      av1[t] = _mm512_loadu_ps(a[t] + c + kLanes);
+    }
+    for (int r = 0; r < NR; ++r) {
+      const __m128i b = _mm_loadu_si128(reinterpret_cast<const __m128i*>(w + ((size_t)r * C + c) / 2));
+      const __m128i lo = _mm_and_si128(b, m4), hi = _mm_and_si128(_mm_srli_epi16(b, 4), m4);
+      const __m512 ts = _mm512_mul_ps(table, _mm512_set1_ps(e8m0_to_f32(sc[(size_t)r * (C / 32) + c / 32])));
+      const __m512 w0 = _mm512_permutexvar_ps(_mm512_cvtepu8_epi32(_mm_unpacklo_epi8(lo, hi)), ts);
+      const __m512 w1 = _mm512_permutexvar_ps(_mm512_cvtepu8_epi32(_mm_unpackhi_epi8(lo, hi)), ts);
+      for (int t = 0; t < NT; ++t) {
+        l[r][t] = _mm512_fmadd_ps(w0, av0[t], l[r][t]);
+        l[r][t] = _mm512_fmadd_ps(w1, av1[t], l[r][t]);
+      }
+    }
+  }
+  for (int r = 0; r < NR; ++r)
+    for (int t = 0; t < NT; ++t) acc[r * kMaxTok + t] = 0.0f + hsum(l[r][t]);
+}
+
+template <int NR>
+MOE_AVX512 void dot_mx4_any(const uint8_t* w, const uint8_t* sc, int C, const float* const* a, int nt, float* acc) {
+  switch (nt) {
+    case 1: dot_blocks_mx4<NR, 1>(w, sc, C, a, acc); return;
+    case 2: dot_blocks_mx4<NR, 2>(w, sc, C, a, acc); return;
+    case 3: dot_blocks_mx4<NR, 3>(w, sc, C, a, acc); return;
+    case 4: dot_blocks_mx4<NR, 4>(w, sc, C, a, acc); return;
+    case 5: dot_blocks_mx4<NR, 5>(w, sc, C, a, acc); return;
+    case 6: dot_blocks_mx4<NR, 6>(w, sc, C, a, acc); return;
+    case 7: dot_blocks_mx4<NR, 7>(w, sc, C, a, acc); return;
+    default: dot_blocks_mx4<NR, 8>(w, sc, C, a, acc); return;
+  }
 }
 
 template <int NR, typename Load, typename Scale>
@@ -215,16 +253,9 @@ MOE_AVX512 void dot_rows_v(const uint8_t* w, int dtype, const void* sc, int C, c
                   [&](int, int c0) MOE_AVX512 { return s[c0 / 128]; }, C, 128, a, nt, acc);
       return;
     }
-    default: {  // MXFP4: E8M0 bytes per 32 columns of each row
-      const uint8_t* s = reinterpret_cast<const uint8_t*>(sc);
-      const __m512 table = _mm512_loadu_ps(g_tab.e2m1);
-      dot_any<NR>([&](int r, int c) MOE_AVX512 {
-                    return ld_e2m1(w + ((size_t)r * C + c) / 2, table,
-                                   _mm512_set1_ps(e8m0_to_f32(s[(size_t)r * (C / 32) + c / 32])));
-                  },
-                  one, C, C, a, nt, acc);
+    default:  // MXFP4: E8M0 bytes per 32 columns of each row
+      dot_mx4_any<NR>(w, reinterpret_cast<const uint8_t*>(sc), C, a, nt, acc);
       return;
-    }
   }
 }
 
