@@ -43,6 +43,9 @@ namespace {
 struct Tables {
   float e4m3[256];
   float e2m1[16];
+  // the bf16 bits of the 128 e4m3 magnitudes (every e4m3 value is a bf16 value: 3 mantissa bits, exponents
+  // 2^-9 .. 2^8); the NaN code's entry is the quiet NaN
+  alignas(64) uint16_t e4m3_bf16[128];
   Tables() {
     for (int c = 0; c < 256; ++c) {
       const int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
@@ -51,6 +54,11 @@ struct Tables {
       else if (e == 0) v = ldexpf((float)m / 8.0f, -6);
       else v = ldexpf(1.0f + (float)m / 8.0f, e - 7);
       e4m3[c] = s ? -v : v;
+    }
+    for (int c = 0; c < 128; ++c) {
+      uint32_t u;
+      memcpy(&u, &e4m3[c], 4);
+      e4m3_bf16[c] = (uint16_t)(u >> 16);
     }
     for (int c = 0; c < 16; ++c) {
       const int s = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
@@ -114,6 +122,8 @@ void dot_dec_p(const Dec& dec, int C, int block, const float* sc, const float* c
 
 // ---- AVX-512
 #define MOE_AVX512 __attribute__((target("avx512f")))
+#define MOE_AVX512BW __attribute__((target("avx512f,avx512bw")))
+const bool g_avx512bw = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw");
 
 MOE_AVX512 inline float hsum(__m512 v) { return _mm512_reduce_add_ps(v); }
 
@@ -201,6 +211,69 @@ MOE_AVX512 inline void dot_blocks_mx4(const uint8_t* w, const uint8_t* sc, int C
     for (int t = 0; t < NT; ++t) acc[r * kMaxTok + t] = 0.0f + hsum(l[r][t]);
 }
 
+// 32 e4m3 codes -> 32 fp32 (v0: the first 16): the magnitudes looked up as bf16 bits in two 64-entry
+// halves of the 128-entry table (vpermi2w), the sign bit put in place, then widened; the same values as
+// ld_e4m3, exactly
+MOE_AVX512BW inline void ld_e4m3_32(const uint8_t* w, const __m512i (&t)[4], __m512& v0, __m512& v1) {
+  const __m512i u = _mm512_cvtepu8_epi16(_mm256_loadu_si256(reinterpret_cast<const __m256i*>(w)));
+  const __m512i em = _mm512_and_si512(u, _mm512_set1_epi16(0x7f));
+  const __m512i r0 = _mm512_permutex2var_epi16(t[0], em, t[1]);  // magnitudes 0..63 (index bits 0-5)
+  const __m512i r1 = _mm512_permutex2var_epi16(t[2], em, t[3]);  // 64..127
+  __m512i b = _mm512_mask_blend_epi16(_mm512_test_epi16_mask(em, _mm512_set1_epi16(64)), r0, r1);
+  b = _mm512_or_si512(b, _mm512_slli_epi16(_mm512_and_si512(u, _mm512_set1_epi16(0x80)), 8));
+  v0 = _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(_mm512_castsi512_si256(b)), 16));
+  v1 = _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(_mm512_extracti64x4_epi64(b, 1)), 16));
+}
+
+// fp8 rows with 128 x 128 block scales, 32 weights per step: the same products, sums and scaling, in the
+// same order, as dot_blocks with ld_e4m3 (16 at a time, one scale per 128 columns)
+template <int NR, int NT>
+MOE_AVX512BW inline void dot_blocks_fp8(const uint8_t* w, const float* sc, int C, const float* const* a, float* acc) {
+  __m512i t[4];
+  for (int i = 0; i < 4; ++i) t[i] = _mm512_load_si512(g_tab.e4m3_bf16 + 32 * i);
+  float out[NR][NT] = {};
+  for (int c0 = 0; c0 < C; c0 += 128) {
+    __m512 l[NR][NT];
+    for (int r = 0; r < NR; ++r)
+      for (int t_ = 0; t_ < NT; ++t_) l[r][t_] = _mm512_setzero_ps();
+    for (int c = c0; c < c0 + 128; c += 2 * kLanes) {
+      __m512 av0[NT], av1[NT];
+      for (int t_ = 0; t_ < NT; ++t_) {
+        av0[t_] = _mm512_loadu_ps(a[t_] + c);
+        av1[t_] = _mm512_loadu_ps(a[t_] + c + kLanes);
+      }
+      for (int r = 0; r < NR; ++r) {
+        __m512 w0, w1;
+        ld_e4m3_32(w + (size_t)r * C + c, t, w0, w1);
+        for (int t_ = 0; t_ < NT; ++t_) {
+          l[r][t_] = _mm512_fmadd_ps(w0, av0[t_], l[r][t_]);
+          l[r][t_] = _mm512_fmadd_ps(w1, av1[t_], l[r][t_]);
+        }
+      }
+    }
+    for (int r = 0; r < NR; ++r) {
+      const float s = sc[c0 / 128];
+      for (int t_ = 0; t_ < NT; ++t_) out[r][t_] += s * hsum(l[r][t_]);
+    }
+  }
+  for (int r = 0; r < NR; ++r)
+    for (int t_ = 0; t_ < NT; ++t_) acc[r * kMaxTok + t_] = out[r][t_];
+}
+
+template <int NR>
+MOE_AVX512BW void dot_fp8_any(const uint8_t* w, const float* sc, int C, const float* const* a, int nt, float* acc) {
+  switch (nt) {
+    case 1: dot_blocks_fp8<NR, 1>(w, sc, C, a, acc); return;
+    case 2: dot_blocks_fp8<NR, 2>(w, sc, C, a, acc); return;
+    case 3: dot_blocks_fp8<NR, 3>(w, sc, C, a, acc); return;
+    case 4: dot_blocks_fp8<NR, 4>(w, sc, C, a, acc); return;
+    case 5: dot_blocks_fp8<NR, 5>(w, sc, C, a, acc); return;
+    case 6: dot_blocks_fp8<NR, 6>(w, sc, C, a, acc); return;
+    case 7: dot_blocks_fp8<NR, 7>(w, sc, C, a, acc); return;
+    default: dot_blocks_fp8<NR, 8>(w, sc, C, a, acc); return;
+  }
+}
+
 template <int NR>
 MOE_AVX512 void dot_mx4_any(const uint8_t* w, const uint8_t* sc, int C, const float* const* a, int nt, float* acc) {
   switch (nt) {
@@ -249,6 +322,10 @@ MOE_AVX512 void dot_rows_v(const uint8_t* w, int dtype, const void* sc, int C, c
     }
     case MOE_FP8_E4M3_B128: {  // the rows share their 128-row block's scales
       const float* s = reinterpret_cast<const float*>(sc);
+      if (g_avx512bw) {
+        dot_fp8_any<NR>(w, s, C, a, nt, acc);
+        return;
+      }
       dot_any<NR>([&](int r, int c) MOE_AVX512 { return ld_e4m3(w + (size_t)r * C + c); },
                   [&](int, int c0) MOE_AVX512 { return s[c0 / 128]; }, C, 128, a, nt, acc);
       return;
